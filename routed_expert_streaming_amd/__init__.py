@@ -1,0 +1,292 @@
+"""MI355X-native routed-expert MoE decode path.
+
+Python face of libmoe (include/moe.h): torch supplies device memory and
+streams; every computation runs in the library's HIP kernels.  Names follow
+the C ABI: route_topk, expert_ffn_rvq, layer_forward, decode_forward,
+layer_forward_grouped, ExpertCache (expert_cache_*), layer_forward_streamed.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_NO_KEY, MOE_SCORE_SIGMOID,
+                   MOE_SCORE_SOFTMAX, MoeError, MoeLayer, MoeRecordLayout, MoeRouter,
+                   MoeTraceRec, check, lib)
+
+SCORE = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return MOE_DTYPE_F32
+    if x.dtype == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def rvq_record_layout(H: int, I: int) -> MoeRecordLayout:
+    out = MoeRecordLayout()
+    check(lib().moe_rvq_record_layout(H, I, ctypes.byref(out)), "moe_rvq_record_layout")
+    return out
+
+
+# ------------------------------------------------------------------ layers
+@dataclass
+class Router:
+    weight: torch.Tensor                 # [E, H] fp32 device
+    k: int
+    score: str = "softmax"
+    bias: Optional[torch.Tensor] = None  # [E] fp32 device
+
+    def struct(self) -> MoeRouter:
+        E = self.weight.shape[0]
+        return MoeRouter(self.weight.data_ptr(), None if self.bias is None else self.bias.data_ptr(),
+                         E, self.k, SCORE[self.score])
+
+
+@dataclass
+class Layer:
+    """One MoE layer: router, expert records resident in HBM (any device
+    tensors, 256-byte aligned), optional dense bf16 shared expert."""
+    H: int
+    I: int
+    router: Router
+    records: Sequence[torch.Tensor] = ()            # E uint8 device tensors (resident path)
+    shared: Optional[torch.Tensor] = None           # bf16/int16 device tensor, 3*H*I elements
+    record_ptrs: Optional[torch.Tensor] = field(default=None, repr=False)
+
+    def __post_init__(self):
+        if self.records and self.record_ptrs is None:
+            self.set_records(self.records)
+
+    def set_records(self, records: Sequence[torch.Tensor] = (), ptrs: Optional[Sequence[int]] = None):
+        if ptrs is None:
+            ptrs = [r.data_ptr() for r in records]
+        self.records = records
+        dev = self.router.weight.device
+        self.record_ptrs = torch.tensor(list(ptrs), dtype=torch.int64).to(dev)
+
+    def struct(self) -> MoeLayer:
+        return MoeLayer(self.H, self.I, self.router.struct(),
+                        None if self.record_ptrs is None else self.record_ptrs.data_ptr(),
+                        None if self.shared is None else self.shared.data_ptr())
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ routing
+def route_topk(router: Router, x: torch.Tensor, stream=None, ws: Optional[torch.Tensor] = None):
+    """idx [T, k] int32 and w [T, k] fp32 for x [T, H] (fp32 or bf16)."""
+    _need(x.dim() == 2 and x.is_contiguous(), "x must be a contiguous [T, H] tensor")
+    T, H = x.shape
+    E = router.weight.shape[0]
+    idx = torch.empty((T, router.k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, router.k), dtype=torch.float32, device=x.device)
+    need = lib().moe_route_workspace_bytes(E, T)
+    ws = ws if ws is not None else _ws(need, x.device)
+    r = router.struct()
+    check(lib().moe_route_topk(ctypes.byref(r), _ptr(x), _dtype_code(x), T, H, _ptr(idx), _ptr(w),
+                               _ptr(ws), ws.numel(), _stream(stream)), "moe_route_topk")
+    return idx, w
+
+
+# --------------------------------------------------------------- expert FFN
+def expert_ffn_rvq(record: torch.Tensor, H: int, I: int, x: torch.Tensor,
+                   gate_w: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                   accumulate: bool = False, stream=None, ws: Optional[torch.Tensor] = None):
+    """y [T, H] (+)= gate_w[t] * expert(x_t) for one RVQ expert record."""
+    _need(x.dim() == 2 and x.dtype == torch.float32 and x.is_contiguous(), "x must be contiguous fp32 [T, H]")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+        accumulate = False
+    need = lib().moe_expert_ffn_workspace_bytes(H, I, T)
+    ws = ws if ws is not None else _ws(need, x.device)
+    check(lib().moe_expert_ffn_rvq(_ptr(record), H, I, _ptr(x), T, _ptr(gate_w), _ptr(y), int(accumulate),
+                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_expert_ffn_rvq")
+    return y
+
+
+# ------------------------------------------------------------------- layer
+def layer_workspace_bytes(layer: Layer, T: int) -> int:
+    s = layer.struct()
+    return lib().moe_layer_workspace_bytes(ctypes.byref(s), T)
+
+
+def layer_forward(layer: Layer, x: torch.Tensor, stream=None, ws: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, want_routing: bool = True):
+    """out [T, H] fp32, idx [T, k], w [T, k] for x [T, H] (fp32 or bf16)."""
+    _need(x.dim() == 2 and x.is_contiguous(), "x must be a contiguous [T, H] tensor")
+    T = x.shape[0]
+    k = layer.router.k
+    out = out if out is not None else torch.empty((T, layer.H), dtype=torch.float32, device=x.device)
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device) if want_routing else None
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if want_routing else None
+    s = layer.struct()
+    need = lib().moe_layer_workspace_bytes(ctypes.byref(s), T)
+    ws = ws if ws is not None else _ws(need, x.device)
+    check(lib().moe_layer_forward(ctypes.byref(s), _ptr(x), _dtype_code(x), T, _ptr(out), _ptr(idx), _ptr(w),
+                                  _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward")
+    return out, idx, w
+
+
+def _layer_array(layers: Sequence[Layer]):
+    arr = (MoeLayer * len(layers))()
+    for i, l in enumerate(layers):
+        arr[i] = l.struct()
+    return arr
+
+
+def decode_workspace_bytes(layers: Sequence[Layer]) -> int:
+    arr = _layer_array(layers)
+    return lib().moe_decode_workspace_bytes(arr, len(layers))
+
+
+def decode_forward(layers: Sequence[Layer], x: torch.Tensor, stream=None, ws: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None, want_idx: bool = True):
+    """x [T, L, H] fp32 -> out [T, L, H] fp32, idx [T, L, k] (token-major decode)."""
+    _need(x.dim() == 3 and x.dtype == torch.float32 and x.is_contiguous(), "x must be contiguous fp32 [T, L, H]")
+    T, nL, H = x.shape
+    _need(nL == len(layers), "x's layer dimension must match len(layers)")
+    arr = _layer_array(layers)
+    k = layers[0].router.k
+    out = out if out is not None else torch.empty_like(x)
+    if want_idx and idx is None:
+        idx = torch.empty((T, nL, k), dtype=torch.int32, device=x.device)
+    need = lib().moe_decode_workspace_bytes(arr, nL)
+    ws = ws if ws is not None else _ws(need, x.device)
+    check(lib().moe_decode_forward(arr, nL, _ptr(x), T, _ptr(out), _ptr(idx if want_idx else None),
+                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_decode_forward")
+    return out, (idx if want_idx else None)
+
+
+def grouped_workspace_bytes(layer: Layer, T: int) -> int:
+    s = layer.struct()
+    return lib().moe_grouped_workspace_bytes(ctypes.byref(s), T)
+
+
+def layer_forward_grouped(layer: Layer, x: torch.Tensor, stream=None, ws: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None):
+    """Batched layer on matrix cores: out [T, H] fp32, idx [T, k], w [T, k]."""
+    _need(x.dim() == 2 and x.is_contiguous(), "x must be a contiguous [T, H] tensor")
+    T = x.shape[0]
+    k = layer.router.k
+    out = out if out is not None else torch.empty((T, layer.H), dtype=torch.float32, device=x.device)
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    s = layer.struct()
+    need = lib().moe_grouped_workspace_bytes(ctypes.byref(s), T)
+    ws = ws if ws is not None else _ws(need, x.device)
+    check(lib().moe_layer_forward_grouped(ctypes.byref(s), _ptr(x), _dtype_code(x), T, _ptr(out), _ptr(idx),
+                                          _ptr(w), _ptr(ws), ws.numel(), _stream(stream)),
+          "moe_layer_forward_grouped")
+    return out, idx, w
+
+
+# ------------------------------------------------------------------- cache
+class ExpertCache:
+    """HBM expert-slot LRU cache over a caller-owned device pool."""
+
+    def __init__(self, capacity: int, slot_bytes: int, pool: torch.Tensor):
+        _need(pool.numel() * pool.element_size() >= capacity * slot_bytes, "pool too small")
+        self.capacity, self.slot_bytes, self.pool = capacity, slot_bytes, pool
+        h = ctypes.c_void_p()
+        check(lib().expert_cache_create(capacity, slot_bytes, _ptr(pool), ctypes.byref(h)), "expert_cache_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            lib().expert_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def lookup(self, key: int) -> int:
+        slot = ctypes.c_int32()
+        check(lib().expert_cache_lookup(self.handle, key, ctypes.byref(slot)), "expert_cache_lookup")
+        return slot.value
+
+    def insert(self, key: int, host_src: int, copy_stream=None):
+        slot, ev = ctypes.c_int32(), ctypes.c_uint32()
+        check(lib().expert_cache_insert(self.handle, key, ctypes.c_void_p(host_src), _stream(copy_stream),
+                                        ctypes.byref(slot), ctypes.byref(ev)), "expert_cache_insert")
+        return slot.value, (None if ev.value == MOE_NO_KEY else ev.value)
+
+    def wait(self, slot: int, stream=None):
+        check(lib().expert_cache_wait(self.handle, slot, _stream(stream)), "expert_cache_wait")
+
+    def release(self, slot: int, stream=None):
+        check(lib().expert_cache_release(self.handle, slot, _stream(stream)), "expert_cache_release")
+
+    def slot_ptr(self, slot: int) -> int:
+        p = ctypes.c_void_p()
+        check(lib().expert_cache_slot_ptr(self.handle, slot, ctypes.byref(p)), "expert_cache_slot_ptr")
+        return p.value
+
+    def trace(self):
+        """List of (key, hit, slot, evicted or None)."""
+        n = ctypes.c_int64()
+        lib().expert_cache_trace(self.handle, None, 0, ctypes.byref(n))
+        buf = (MoeTraceRec * max(n.value, 1))()
+        check(lib().expert_cache_trace(self.handle, buf, n.value, ctypes.byref(n)), "expert_cache_trace")
+        return [(r.key, r.hit, r.slot, None if r.evicted == MOE_NO_KEY else r.evicted) for r in buf[:n.value]]
+
+    def trace_reset(self):
+        check(lib().expert_cache_trace_reset(self.handle), "expert_cache_trace_reset")
+
+    def stats(self):
+        v = [ctypes.c_int64() for _ in range(4)]
+        check(lib().expert_cache_stats(self.handle, *[ctypes.byref(x) for x in v]), "expert_cache_stats")
+        return dict(zip(("lookups", "hits", "inserts", "evictions"), [x.value for x in v]))
+
+
+def streamed_workspace_bytes(layer: Layer, T: int = 1) -> int:
+    s = layer.struct()
+    return lib().moe_streamed_workspace_bytes(ctypes.byref(s), T)
+
+
+def layer_forward_streamed(layer: Layer, cache: ExpertCache, layer_id: int, experts_host: Sequence[int],
+                           x: torch.Tensor, copy_stream: torch.cuda.Stream, stream=None,
+                           ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                           idx: Optional[torch.Tensor] = None, host_table=None):
+    """One decode step of one layer fed from the slot cache.  experts_host:
+    E pinned host addresses of the layer's records (or a prebuilt ctypes array)."""
+    _need(x.dim() == 2 and x.shape[0] == 1 and x.dtype == torch.float32, "x must be fp32 [1, H]")
+    out = out if out is not None else torch.empty((1, layer.H), dtype=torch.float32, device=x.device)
+    s = layer.struct()
+    table = host_table if host_table is not None else (ctypes.c_void_p * len(experts_host))(*experts_host)
+    need = lib().moe_streamed_workspace_bytes(ctypes.byref(s), 1)
+    ws = ws if ws is not None else _ws(need, x.device)
+    check(lib().moe_layer_forward_streamed(ctypes.byref(s), cache.handle, layer_id, table, _ptr(x), 1, _ptr(out),
+                                           _ptr(idx), _ptr(ws), ws.numel(), _stream(stream), _stream(copy_stream)),
+          "moe_layer_forward_streamed")
+    return out

@@ -1,0 +1,80 @@
+// Host-only LRU core of the HBM expert-slot cache (see expert_cache_core.h).
+#include "expert_cache_core.h"
+
+namespace moe {
+
+LruCore::LruCore(int capacity)
+    : capacity_(capacity), key_of_(capacity, kNoKey), prev_(capacity, -1), next_(capacity, -1) {
+    map_.reserve((size_t)capacity * 2);
+    for (int s = 0; s < capacity; s++) free_.insert(s);
+}
+
+void LruCore::unlink(int s) {
+    if (prev_[s] != -1) next_[prev_[s]] = next_[s];
+    else head_ = next_[s];
+    if (next_[s] != -1) prev_[next_[s]] = prev_[s];
+    else tail_ = prev_[s];
+    prev_[s] = next_[s] = -1;
+}
+
+void LruCore::push_front(int s) {
+    prev_[s] = -1;
+    next_[s] = head_;
+    if (head_ != -1) prev_[head_] = s;
+    head_ = s;
+    if (tail_ == -1) tail_ = s;
+}
+
+int LruCore::lookup(uint32_t key) {
+    lookups++;
+    auto it = map_.find(key);
+    if (it == map_.end()) return -1;
+    const int s = it->second;
+    hits++;
+    unlink(s);
+    push_front(s);
+    trace_.push_back({key, 1, s, kNoKey});
+    return s;
+}
+
+int LruCore::plan_insert(uint32_t key, uint32_t *victim) const {
+    if (map_.count(key)) return -1;
+    if (!free_.empty()) {
+        *victim = kNoKey;
+        return *free_.begin();
+    }
+    *victim = key_of_[tail_];
+    return tail_;
+}
+
+void LruCore::commit_insert(uint32_t key, int slot, uint32_t victim) {
+    if (victim != kNoKey) {
+        map_.erase(victim);
+        unlink(slot);
+        evictions++;
+    } else {
+        free_.erase(slot);
+    }
+    key_of_[slot] = key;
+    map_[key] = slot;
+    push_front(slot);
+    inserts++;
+    trace_.push_back({key, 0, slot, victim});
+}
+
+void LruCore::drop_slot(int slot) {
+    const uint32_t k = key_of_[slot];
+    if (k == kNoKey) return;
+    map_.erase(k);
+    unlink(slot);
+    key_of_[slot] = kNoKey;
+    free_.insert(slot);
+}
+
+std::vector<uint32_t> LruCore::order() const {
+    std::vector<uint32_t> v;
+    for (int s = head_; s != -1; s = next_[s]) v.push_back(key_of_[s]);
+    return v;
+}
+
+}  // namespace moe

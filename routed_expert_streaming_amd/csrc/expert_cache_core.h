@@ -1,0 +1,75 @@
+// Host-only LRU core of the HBM expert-slot cache: O(1) lookup and insert
+// (hash map + intrusive doubly linked list over slots), lowest-free-slot
+// allocation, a lookup trace and counters.  No HIP dependency, so it can be
+// built and tested on its own.
+//
+// Policy (WISP launch post, section "통찰": an LRU cache promotes the experts
+// the router keeps choosing): a hit moves the key to most-recently-used; a
+// new key takes the lowest-numbered free slot, else the least recently used
+// key is evicted and its slot reused; the new key becomes most-recently-used.
+#pragma once
+
+#include <cstdint>
+#include <set>
+#include <unordered_map>
+#include <vector>
+
+namespace moe {
+
+constexpr uint32_t kNoKey = 0xFFFFFFFFu;
+
+struct CacheTraceRec {
+    uint32_t key;
+    int32_t hit;
+    int32_t slot;
+    uint32_t evicted;   // kNoKey if none
+};
+
+class LruCore {
+public:
+    explicit LruCore(int capacity);
+
+    int capacity() const { return capacity_; }
+    int size() const { return (int)map_.size(); }
+    bool contains(uint32_t key) const { return map_.count(key) != 0; }
+
+    // Hit: returns the slot, moves the key to MRU and appends a hit record.
+    // Miss: returns -1 and changes nothing but the lookup counter.
+    int lookup(uint32_t key);
+
+    // Slot a new key would take and the key it would evict (kNoKey if a slot
+    // is free).  Returns -1 if the key is already cached.  Changes nothing.
+    int plan_insert(uint32_t key, uint32_t *victim) const;
+
+    // Apply a planned insert: evict the victim (if any), map key -> slot at
+    // MRU and append a miss record.
+    void commit_insert(uint32_t key, int slot, uint32_t victim);
+
+    // Forget whatever key a slot holds (the slot becomes free).
+    void drop_slot(int slot);
+
+    // Key held by a slot, or kNoKey.
+    uint32_t key_of(int slot) const { return key_of_[slot]; }
+
+    // Keys from most to least recently used.
+    std::vector<uint32_t> order() const;
+
+    const std::vector<CacheTraceRec> &trace() const { return trace_; }
+    void trace_reset() { trace_.clear(); }
+
+    int64_t lookups = 0, hits = 0, inserts = 0, evictions = 0;
+
+private:
+    void unlink(int s);
+    void push_front(int s);
+
+    int capacity_;
+    std::unordered_map<uint32_t, int> map_;
+    std::vector<uint32_t> key_of_;
+    std::vector<int> prev_, next_;
+    int head_ = -1, tail_ = -1;
+    std::set<int> free_;
+    std::vector<CacheTraceRec> trace_;
+};
+
+}  // namespace moe

@@ -1,0 +1,543 @@
+// HIP kernels for gfx950 (CDNA4): router logits, wavefront top-k, RVQ
+// gate/up and down GEMVs on packed 24-bit code pairs, dense bf16 shared
+// expert, fixed-order combine.
+//
+// Sources (pages on routed expert streaming):
+//  "WISP -- 실행될 수 없는 것을 스트리밍하다", section "통찰": the model's own
+//    router picks each token's experts (route + top-k below);
+//  "2.78조 파라미터 모델을 노트북에서: NVMe 스트리밍 추론 엔진 WASTE", section
+//    "유휴 가중치는 메모리가 아니라 제때 닿기만 하면 된다": experts are residual
+//    vector quantised at 3.00 bits per weight and never expanded (the GEMVs
+//    below decode codes on the fly; no weight matrix is ever written out).
+//
+// Numerics: logits, accumulation and the combine are fp32.  The RVQ GEMVs
+// multiply the exact fp16 codebook entries by the input rounded to fp16
+// (v_dot2_f32_f16: exact products, fp32 accumulation); the SwiGLU
+// intermediate is rounded to fp16 before the down GEMV.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Local item -> (global item, record).
+__device__ __forceinline__ const uint8_t *resolve_record(const RecSrc &s, int local, int &item) {
+    const int t = local / s.n_local, l = local % s.n_local;
+    if (s.table) {
+        item = t * s.k + l;
+        return (const uint8_t *)s.table[s.idx[item]];
+    }
+    item = t * s.k + s.rank[l];
+    return (const uint8_t *)s.list[l];
+}
+
+// Byte address in an LDS codebook of the stage-1 (a) and stage-2 (b) rows of
+// group g (0..15) of a 48-byte strip held in 12 dwords d[].
+template <int G>
+__device__ __forceinline__ void group_addr(const uint32_t (&d)[12], uint32_t &aa, uint32_t &ba) {
+    constexpr int bit = 24 * G, i = bit / 32, s = bit % 32;
+    uint32_t v;
+    if constexpr (s <= 8) v = d[i] >> s;
+    else v = __builtin_amdgcn_alignbit(d[i + 1], d[i], s);
+    aa = (v << 4) & 0xFFF0u;        // a * 16
+    ba = (v >> 8) & 0xFFF0u;        // b * 16
+}
+
+// acc[g%4] += sum over the 16 groups of (C[a] + C[b]) . x_group
+template <int G>
+__device__ __forceinline__ void strip_dot(const uint32_t (&d)[12], const char *cb, const uint32_t *xp,
+                                          float (&acc)[4]) {
+    if constexpr (G < 16) {
+        uint32_t aa, ba;
+        group_addr<G>(d, aa, ba);
+        const u32x4 ca = *(const u32x4 *)(cb + aa);
+        const u32x4 cbv = *(const u32x4 *)(cb + ba);
+        const uint32_t x0 = xp[4 * G + 0], x1 = xp[4 * G + 1], x2 = xp[4 * G + 2], x3 = xp[4 * G + 3];
+        float a = acc[G & 3];
+        a = dot2(ca.x, x0, a);
+        a = dot2(ca.y, x1, a);
+        a = dot2(ca.z, x2, a);
+        a = dot2(ca.w, x3, a);
+        a = dot2(cbv.x, x0, a);
+        a = dot2(cbv.y, x1, a);
+        a = dot2(cbv.z, x2, a);
+        a = dot2(cbv.w, x3, a);
+        acc[G & 3] = a;
+        strip_dot<G + 1>(d, cb, xp, acc);
+    }
+}
+
+__device__ __forceinline__ void load_strip(const u32x4 *tile, int lane, uint32_t (&d)[12]) {
+    const u32x4 w0 = __builtin_nontemporal_load(tile + lane);
+    const u32x4 w1 = __builtin_nontemporal_load(tile + 64 + lane);
+    const u32x4 w2 = __builtin_nontemporal_load(tile + 128 + lane);
+    d[0] = w0.x; d[1] = w0.y; d[2] = w0.z; d[3] = w0.w;
+    d[4] = w1.x; d[5] = w1.y; d[6] = w1.z; d[7] = w1.w;
+    d[8] = w2.x; d[9] = w2.y; d[10] = w2.z; d[11] = w2.w;
+}
+
+// ---------------------------------------------------------------- routing
+// z[t, e] = W[e] . x[t] + b[e].  One wave per expert row, 8 tokens per block.
+constexpr int kRouteTok = 8;
+
+__global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ W, const float *__restrict__ bias,
+                                                      int E, int H, const void *__restrict__ x, int x_dtype, int T,
+                                                      float *__restrict__ z) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + wave;
+    const int t0 = blockIdx.y * kRouteTok;
+    if (e >= E) return;
+    const int nt = min(kRouteTok, T - t0);
+    float acc[kRouteTok];
+#pragma unroll
+    for (int i = 0; i < kRouteTok; i++) acc[i] = 0.f;
+    const float *wr = W + (size_t)e * H;
+    for (int c = lane * 4; c < H; c += 256) {
+        const float4 wv = *(const float4 *)(wr + c);
+#pragma unroll
+        for (int i = 0; i < kRouteTok; i++) {
+            if (i < nt) {
+                float4 xv;
+                if (x_dtype == MOE_DTYPE_F32) {
+                    xv = *(const float4 *)((const float *)x + (size_t)(t0 + i) * H + c);
+                } else {
+                    const uint2 b = *(const uint2 *)((const uint16_t *)x + (size_t)(t0 + i) * H + c);
+                    xv = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                                     __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+                }
+                acc[i] = fmaf(wv.x, xv.x, acc[i]);
+                acc[i] = fmaf(wv.y, xv.y, acc[i]);
+                acc[i] = fmaf(wv.z, xv.z, acc[i]);
+                acc[i] = fmaf(wv.w, xv.w, acc[i]);
+            }
+        }
+    }
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kRouteTok; i++) {
+        const float s = wave_sum(acc[i]);
+        if (lane == 0 && i < nt) z[(size_t)(t0 + i) * E + e] = s + b;
+    }
+}
+
+// Top-k per token: one wave per token; k rounds of a wave-wide argmax on
+// (z desc, expert id asc); then softmax- or sigmoid-renormalised weights.
+constexpr int kMaxPerLane = MOE_MAX_E / 64;
+
+__global__ __launch_bounds__(64) void k_topk(const float *__restrict__ z, int E, int k, int score_fn,
+                                             int32_t *__restrict__ idx, float *__restrict__ w) {
+    const int t = blockIdx.x, lane = threadIdx.x;
+    float v[kMaxPerLane];
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; i++) {
+        const int e = lane + 64 * i;
+        const float zz = e < E ? z[(size_t)t * E + e] : -INFINITY;
+        v[i] = zz == zz ? zz : -INFINITY;          // NaN ranks last
+    }
+    uint32_t taken = 0;                            // bit i: v[i] already selected
+    float zsel = 0.f, zmax = 0.f, sum = 0.f;
+    int esel = 0;
+    for (int j = 0; j < k; j++) {
+        // lane-local best among untaken experts: largest value, lowest id on ties
+        float bv = -INFINITY;
+        int be = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; i++) {
+            const int e = lane + 64 * i;
+            if (e < E && !(taken >> i & 1u) && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oe = __shfl_xor(be, o, 64);
+            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        }
+        // k <= E, so an untaken expert always exists and be < E
+        if (j == 0) zmax = bv;
+        const float s = score_fn == MOE_SCORE_SOFTMAX ? __expf(bv - zmax) : 1.f / (1.f + __expf(-bv));
+        sum += s;
+        if (lane == j) { zsel = s; esel = be; }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    }
+    if (lane < k) {
+        idx[(size_t)t * k + lane] = esel;
+        w[(size_t)t * k + lane] = zsel / sum;
+    }
+}
+
+// x -> fp16 pairs (one dword per two consecutive elements)
+__global__ __launch_bounds__(256) void k_pack_x(const void *__restrict__ x, int x_dtype, int T, int H,
+                                                int64_t x_stride, uint32_t *__restrict__ xh) {
+    const int hp = H / 2;
+    const size_t n = (size_t)T * hp;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const size_t t = i / hp, c = (i % hp) * 2;
+        float a, b;
+        if (x_dtype == MOE_DTYPE_F32) {
+            const float *xr = (const float *)x + t * x_stride;
+            a = xr[c]; b = xr[c + 1];
+        } else {
+            const uint16_t *xr = (const uint16_t *)x + t * x_stride;
+            a = bf16_to_f32(xr[c]); b = bf16_to_f32(xr[c + 1]);
+        }
+        xh[i] = pack_f16x2(a, b);
+    }
+}
+
+// ------------------------------------------------------------- RVQ GEMVs
+// Gate/up: one workgroup per (item, 64-row tile); both codebooks staged in
+// LDS (128 KiB); lane = row, waves split the 128-column chunks; the input's
+// fp16 pairs are wave-uniform (scalar loads).  Output: fp16 SiLU(g) * u.
+constexpr int kGuWaves = 8;
+
+__global__ __launch_bounds__(kGuWaves * 64) void k_rvq_gateup(RecSrc src, RecOffsets off, int H, int I,
+                                                              const uint32_t *__restrict__ xh,
+                                                              uint16_t *__restrict__ hh) {
+    extern __shared__ __align__(16) char lds[];
+    char *cbg = lds, *cbu = lds + kCbRows * 16;
+    float *red = (float *)(lds + 2 * kCbRows * 16);      // [kGuWaves][2][64]
+    const int tiles = I / kTileRows;
+    const int local = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    int item;
+    const uint8_t *rec = resolve_record(src, local, item);
+    const int t = item / src.k;
+    {
+        const u32x4 *g = (const u32x4 *)(rec + off.cb[0]);
+        const u32x4 *u = (const u32x4 *)(rec + off.cb[1]);
+        for (int i = threadIdx.x; i < kCbRows; i += kGuWaves * 64) {
+            ((u32x4 *)cbg)[i] = g[i];
+            ((u32x4 *)cbu)[i] = u[i];
+        }
+    }
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int cpr = H / kChunkCols;
+    const u32x4 *gcodes = (const u32x4 *)(rec + off.codes[0]) + (size_t)tile * cpr * kTileVec;
+    const u32x4 *ucodes = (const u32x4 *)(rec + off.codes[1]) + (size_t)tile * cpr * kTileVec;
+    const uint32_t *x = xh + (size_t)t * (H / 2);
+    float ag[4] = {0.f, 0.f, 0.f, 0.f}, au[4] = {0.f, 0.f, 0.f, 0.f};
+    int c = wave;
+    uint32_t dg[12], du[12];
+    if (c < cpr) {
+        load_strip(gcodes + (size_t)c * kTileVec, lane, dg);
+        load_strip(ucodes + (size_t)c * kTileVec, lane, du);
+    }
+    while (c < cpr) {
+        const int cn = c + kGuWaves;
+        uint32_t ng[12], nu[12];
+        if (cn < cpr) {
+            load_strip(gcodes + (size_t)cn * kTileVec, lane, ng);
+            load_strip(ucodes + (size_t)cn * kTileVec, lane, nu);
+        }
+        const uint32_t *xp = x + c * 64;
+        strip_dot<0>(dg, cbg, xp, ag);
+        strip_dot<0>(du, cbu, xp, au);
+        if (cn < cpr) {
+#pragma unroll
+            for (int i = 0; i < 12; i++) { dg[i] = ng[i]; du[i] = nu[i]; }
+        }
+        c = cn;
+    }
+    red[(wave * 2 + 0) * 64 + lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
+    red[(wave * 2 + 1) * 64 + lane] = (au[0] + au[1]) + (au[2] + au[3]);
+    __syncthreads();
+    if (wave == 0) {
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kGuWaves; wv++) {
+            g += red[(wv * 2 + 0) * 64 + lane];
+            u += red[(wv * 2 + 1) * 64 + lane];
+        }
+        const int r = tile * kTileRows + lane;
+        const _Float16 sg = ((const _Float16 *)(rec + off.scales[0]))[r];
+        const _Float16 su = ((const _Float16 *)(rec + off.scales[1]))[r];
+        g *= (float)sg;
+        u *= (float)su;
+        const float h = g / (1.f + __expf(-g)) * u;
+        const _Float16 hf = (_Float16)h;
+        hh[(size_t)item * I + r] = __builtin_bit_cast(uint16_t, hf);
+    }
+}
+
+// Down: one workgroup per (item, 64-row tile of H, K-slice); down codebook in
+// LDS (64 KiB); writes s_d[r] * partial dot into ypart[item][ks][r].
+constexpr int kDnWaves = 4;
+
+__global__ __launch_bounds__(kDnWaves * 64) void k_rvq_down(RecSrc src, RecOffsets off, int H, int I, int KS,
+                                                            const uint16_t *__restrict__ hh,
+                                                            float *__restrict__ ypart) {
+    extern __shared__ __align__(16) char lds[];
+    char *cbd = lds;
+    float *red = (float *)(lds + kCbRows * 16);           // [kDnWaves][64]
+    const int tiles = H / kTileRows;
+    const int ks = blockIdx.x % KS;
+    const int tile = (blockIdx.x / KS) % tiles;
+    const int local = blockIdx.x / (KS * tiles);
+    int item;
+    const uint8_t *rec = resolve_record(src, local, item);
+    {
+        const u32x4 *d = (const u32x4 *)(rec + off.cb[2]);
+        for (int i = threadIdx.x; i < kCbRows; i += kDnWaves * 64) ((u32x4 *)cbd)[i] = d[i];
+    }
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int cpr = I / kChunkCols;
+    const int c0 = (int)((int64_t)cpr * ks / KS), c1 = (int)((int64_t)cpr * (ks + 1) / KS);
+    const u32x4 *codes = (const u32x4 *)(rec + off.codes[2]) + (size_t)tile * cpr * kTileVec;
+    const uint32_t *x = (const uint32_t *)(hh + (size_t)item * I);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int c = c0 + wave;
+    uint32_t d[12];
+    if (c < c1) load_strip(codes + (size_t)c * kTileVec, lane, d);
+    while (c < c1) {
+        const int cn = c + kDnWaves;
+        uint32_t nd[12];
+        if (cn < c1) load_strip(codes + (size_t)cn * kTileVec, lane, nd);
+        strip_dot<0>(d, cbd, x + c * 64, acc);
+        if (cn < c1) {
+#pragma unroll
+            for (int i = 0; i < 12; i++) d[i] = nd[i];
+        }
+        c = cn;
+    }
+    red[wave * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    __syncthreads();
+    if (wave == 0) {
+        float y = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kDnWaves; wv++) y += red[wv * 64 + lane];
+        const int r = tile * kTileRows + lane;
+        const _Float16 sd = ((const _Float16 *)(rec + off.scales[2]))[r];
+        ypart[((size_t)item * KS + ks) * H + r] = y * (float)sd;
+    }
+}
+
+// out[t, c] = (acc ? out : 0) + sum_j w[t, j] * sum_ks ypart[t*k+j][ks][c] + ysh[t, c]
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ypart, int k, int KS, int H,
+                                                 const float *__restrict__ w, const float *__restrict__ ysh,
+                                                 float *__restrict__ out, int64_t out_stride, int T,
+                                                 int accumulate) {
+    const size_t n = (size_t)T * H;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const size_t t = i / H, c = i % H;
+        float acc = 0.f;
+        for (int j = 0; j < k; j++) {
+            const size_t item = t * k + j;
+            float y = 0.f;
+            for (int s = 0; s < KS; s++) y += ypart[(item * KS + s) * H + c];
+            acc = fmaf(w ? w[item] : 1.f, y, acc);
+        }
+        if (ysh) acc += ysh[t * H + c];
+        float *o = out + t * out_stride + c;
+        *o = accumulate ? *o + acc : acc;
+    }
+}
+
+// ------------------------------------------------------ dense shared expert
+// hs[t, r] = SiLU(Wg[r] . x_t) * (Wu[r] . x_t); one wave per row, all tokens.
+constexpr int kDenseTok = 4;
+
+__global__ __launch_bounds__(256) void k_dense_gateup(const uint16_t *__restrict__ Wsh, int H, int I,
+                                                      const void *__restrict__ x, int x_dtype, int64_t x_stride,
+                                                      int T, float *__restrict__ hs) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + wave;
+    if (r >= I) return;
+    const uint16_t *wg = Wsh + (size_t)r * H;
+    const uint16_t *wu = Wsh + (size_t)I * H + (size_t)r * H;
+    for (int t0 = 0; t0 < T; t0 += kDenseTok) {
+        float ag[kDenseTok] = {}, au[kDenseTok] = {};
+        const int nt = min(kDenseTok, T - t0);
+        for (int c = lane * 8; c < H; c += 512) {
+            const uint4 gv = *(const uint4 *)(wg + c);
+            const uint4 uv = *(const uint4 *)(wu + c);
+            float gw[8], uw[8];
+            const uint32_t gq[4] = {gv.x, gv.y, gv.z, gv.w}, uq[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                gw[2 * i] = __uint_as_float(gq[i] << 16); gw[2 * i + 1] = __uint_as_float(gq[i] & 0xFFFF0000u);
+                uw[2 * i] = __uint_as_float(uq[i] << 16); uw[2 * i + 1] = __uint_as_float(uq[i] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int tt = 0; tt < kDenseTok; tt++) {
+                if (tt < nt) {
+                    float xv[8];
+                    if (x_dtype == MOE_DTYPE_F32) {
+                        const float *xr = (const float *)x + (size_t)(t0 + tt) * x_stride + c;
+                        const float4 a = *(const float4 *)xr, b = *(const float4 *)(xr + 4);
+                        xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+                        xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+                    } else {
+                        const uint4 b = *(const uint4 *)((const uint16_t *)x + (size_t)(t0 + tt) * x_stride + c);
+                        const uint32_t q[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            xv[2 * i] = __uint_as_float(q[i] << 16);
+                            xv[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        ag[tt] = fmaf(gw[i], xv[i], ag[tt]);
+                        au[tt] = fmaf(uw[i], xv[i], au[tt]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < kDenseTok; tt++) {
+            const float g = wave_sum(ag[tt]), u = wave_sum(au[tt]);
+            if (lane == 0 && tt < nt) hs[(size_t)(t0 + tt) * I + r] = g / (1.f + __expf(-g)) * u;
+        }
+    }
+}
+
+// ysh[t, c] = Wd[c] . hs_t; one wave per row.
+__global__ __launch_bounds__(256) void k_dense_down(const uint16_t *__restrict__ Wsh, int H, int I,
+                                                    const float *__restrict__ hs, int T, float *__restrict__ ysh) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + wave;
+    if (r >= H) return;
+    const uint16_t *wd = Wsh + 2 * (size_t)I * H + (size_t)r * I;
+    for (int t0 = 0; t0 < T; t0 += kDenseTok) {
+        float acc[kDenseTok] = {};
+        const int nt = min(kDenseTok, T - t0);
+        for (int c = lane * 8; c < I; c += 512) {
+            const uint4 dv = *(const uint4 *)(wd + c);
+            const uint32_t q[4] = {dv.x, dv.y, dv.z, dv.w};
+            float wv[8];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                wv[2 * i] = __uint_as_float(q[i] << 16);
+                wv[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int tt = 0; tt < kDenseTok; tt++) {
+                if (tt < nt) {
+                    const float *h = hs + (size_t)(t0 + tt) * I + c;
+                    const float4 a = *(const float4 *)h, b = *(const float4 *)(h + 4);
+                    acc[tt] = fmaf(wv[0], a.x, acc[tt]); acc[tt] = fmaf(wv[1], a.y, acc[tt]);
+                    acc[tt] = fmaf(wv[2], a.z, acc[tt]); acc[tt] = fmaf(wv[3], a.w, acc[tt]);
+                    acc[tt] = fmaf(wv[4], b.x, acc[tt]); acc[tt] = fmaf(wv[5], b.y, acc[tt]);
+                    acc[tt] = fmaf(wv[6], b.z, acc[tt]); acc[tt] = fmaf(wv[7], b.w, acc[tt]);
+                }
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < kDenseTok; tt++) {
+            const float s = wave_sum(acc[tt]);
+            if (lane == 0 && tt < nt) ysh[(size_t)(t0 + tt) * H + r] = s;
+        }
+    }
+}
+
+size_t gateup_lds() { return 2 * kCbRows * 16 + kGuWaves * 2 * 64 * sizeof(float); }
+size_t down_lds() { return kCbRows * 16 + kDnWaves * 64 * sizeof(float); }
+
+}  // namespace
+
+// ----------------------------------------------------------------- launchers
+hipError_t launch_route_logits(const float *W, const float *bias, int E, int H, const void *x, int x_dtype,
+                               int T, float *z, hipStream_t s) {
+    dim3 grid((E + 3) / 4, (T + kRouteTok - 1) / kRouteTok);
+    k_route_logits<<<grid, 256, 0, s>>>(W, bias, E, H, x, x_dtype, T, z);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float *z, int E, int k, int score_fn, int T, int32_t *idx, float *w,
+                       hipStream_t s) {
+    k_topk<<<T, 64, 0, s>>>(z, E, k, score_fn, idx, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_x(const void *x, int x_dtype, int T, int H, int64_t x_stride, uint32_t *xh,
+                         hipStream_t s) {
+    const size_t n = (size_t)T * H / 2;
+    const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
+    k_pack_x<<<grid, 256, 0, s>>>(x, x_dtype, T, H, x_stride, xh);
+    return hipGetLastError();
+}
+
+hipError_t launch_rvq_gateup(const RecSrc &src, const RecOffsets &off, int H, int I, int n_items,
+                             const uint32_t *xh, uint16_t *hh, hipStream_t s) {
+    if (n_items == 0) return hipSuccess;
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_rvq_gateup, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)gateup_lds());
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int grid = n_items * (I / kTileRows);
+    k_rvq_gateup<<<grid, kGuWaves * 64, gateup_lds(), s>>>(src, off, H, I, xh, hh);
+    return hipGetLastError();
+}
+
+int down_splits(int H, int I, int n_items) {
+    // enough workgroups to cover the chip twice (two 64 KiB workgroups per CU)
+    const int tiles = n_items * (H / kTileRows);
+    const int cpr = I / kChunkCols;
+    int ks = 1;
+    while (tiles * ks < 512 && ks * 2 <= cpr / 4) ks *= 2;
+    return ks;
+}
+
+hipError_t launch_rvq_down(const RecSrc &src, const RecOffsets &off, int H, int I, int n_items, int KS,
+                           const uint16_t *hh, float *ypart, hipStream_t s) {
+    if (n_items == 0) return hipSuccess;
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_rvq_down, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)down_lds());
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int grid = n_items * (H / kTileRows) * KS;
+    k_rvq_down<<<grid, kDnWaves * 64, down_lds(), s>>>(src, off, H, I, KS, hh, ypart);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float *ypart, int k, int KS, int H, const float *w, const float *ysh,
+                          float *out, int64_t out_stride, int T, int accumulate, hipStream_t s) {
+    const size_t n = (size_t)T * H;
+    const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
+    k_combine<<<grid, 256, 0, s>>>(ypart, k, KS, H, w, ysh, out, out_stride, T, accumulate);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_gateup(const uint16_t *shared, int H, int I, const void *x, int x_dtype,
+                               int64_t x_stride, int T, float *hs, hipStream_t s) {
+    k_dense_gateup<<<(I + 3) / 4, 256, 0, s>>>(shared, H, I, x, x_dtype, x_stride, T, hs);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_down(const uint16_t *shared, int H, int I, const float *hs, int T, float *ysh,
+                             hipStream_t s) {
+    k_dense_down<<<(H + 3) / 4, 256, 0, s>>>(shared, H, I, hs, T, ysh);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,391 @@
+// C ABI of libmoe: argument validation, workspace carving and the launch
+// sequences of the routed-expert MoE path.  Declarations and the meaning of
+// every argument are in include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "expert_cache.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace moe {
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(MOE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+}  // namespace moe
+
+#define HIPCHK(expr, what)                           \
+    do {                                             \
+        hipError_t e_ = (expr);                      \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+namespace {
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool dims_ok(int32_t H, int32_t I) { return H > 0 && I > 0 && H % 128 == 0 && I % 128 == 0; }
+
+void layout_of(int32_t H, int32_t I, moe_record_layout *L) {
+    const int64_t s[9] = {(int64_t)I * (H / 8) * 3, (int64_t)I * (H / 8) * 3, (int64_t)H * (I / 8) * 3,
+                          2 * (int64_t)I, 2 * (int64_t)I, 2 * (int64_t)H,
+                          (int64_t)kCbRows * 16, (int64_t)kCbRows * 16, (int64_t)kCbRows * 16};
+    int64_t pos = 0;
+    for (int i = 0; i < 9; i++) {
+        pos = align_up(pos, 256);
+        L->offset[i] = pos;
+        L->size[i] = s[i];
+        pos += s[i];
+    }
+    L->nbytes = pos;
+    L->padded = align_up(pos, 4096);
+}
+
+RecOffsets offsets_of(int32_t H, int32_t I) {
+    moe_record_layout L;
+    layout_of(H, I, &L);
+    RecOffsets o;
+    for (int m = 0; m < 3; m++) {
+        o.codes[m] = L.offset[m];
+        o.scales[m] = L.offset[3 + m];
+        o.cb[m] = L.offset[6 + m];
+    }
+    return o;
+}
+
+// Sequential carving of a workspace into 256-byte aligned pieces.
+struct Carver {
+    char *base;
+    size_t pos = 0;
+    explicit Carver(void *b) : base((char *)b) {}
+    template <class T>
+    T *take(size_t n) {
+        pos = (size_t)align_up((int64_t)pos, 256);
+        T *p = base ? (T *)(base + pos) : nullptr;
+        pos += n * sizeof(T);
+        return p;
+    }
+};
+
+LayerWs carve_layer(void *ws, int H, int I, int E, int k, int T, bool shared) {
+    Carver c(ws);
+    LayerWs L;
+    const int items = T * k;
+    const int KS = down_splits(H, I, items);
+    L.z = c.take<float>((size_t)T * E);
+    L.idx = c.take<int32_t>((size_t)T * k);
+    L.w = c.take<float>((size_t)T * k);
+    L.xh = c.take<uint32_t>((size_t)T * H / 2);
+    L.hh = c.take<uint16_t>((size_t)items * I);
+    L.ypart = c.take<float>((size_t)items * KS * H);
+    L.hs = shared ? c.take<float>((size_t)T * I) : nullptr;
+    L.ysh = shared ? c.take<float>((size_t)T * H) : nullptr;
+    L.bytes = (size_t)align_up((int64_t)c.pos, 256);
+    return L;
+}
+
+int check_router(const moe_router *r, int32_t H) {
+    if (!r) return fail(MOE_E_INVAL, "router is NULL");
+    if (!r->weight) return fail(MOE_E_INVAL, "router weight is NULL");
+    if (r->E < 1 || r->E > MOE_MAX_E) return fail(MOE_E_INVAL, "E=%d outside [1, %d]", r->E, MOE_MAX_E);
+    if (r->k < 1 || r->k > r->E || r->k > MOE_MAX_K)
+        return fail(MOE_E_INVAL, "k=%d outside [1, min(E=%d, %d)]", r->k, r->E, MOE_MAX_K);
+    if (r->score_fn != MOE_SCORE_SOFTMAX && r->score_fn != MOE_SCORE_SIGMOID)
+        return fail(MOE_E_INVAL, "unknown score_fn %d", r->score_fn);
+    if (H <= 0 || H % 128) return fail(MOE_E_INVAL, "H=%d is not a positive multiple of 128", H);
+    return MOE_OK;
+}
+
+int check_layer(const moe_layer *L, bool need_records) {
+    if (!L) return fail(MOE_E_INVAL, "layer is NULL");
+    if (!dims_ok(L->H, L->I))
+        return fail(MOE_E_INVAL, "H=%d, I=%d must be positive multiples of 128", L->H, L->I);
+    int rc = check_router(&L->router, L->H);
+    if (rc) return rc;
+    if (need_records && !L->records) return fail(MOE_E_INVAL, "records table is NULL");
+    return MOE_OK;
+}
+
+bool dtype_ok(int32_t d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16; }
+
+// route -> pack -> gate/up -> down (+ shared) -> combine for T tokens whose
+// experts come from `src` (table mode: idx filled by the router).
+int run_experts(const moe_layer *L, const LayerWs &ws, const RecSrc &src, const void *x, int32_t x_dtype,
+                int32_t T, int k, const float *w, float *out, hipStream_t s) {
+    const int H = L->H, I = L->I, items = T * k;
+    const RecOffsets off = offsets_of(H, I);
+    const int KS = down_splits(H, I, items);
+    HIPCHK(launch_pack_x(x, x_dtype, T, H, H, ws.xh, s), "pack_x launch");
+    if (L->shared) HIPCHK(launch_dense_gateup(L->shared, H, I, x, x_dtype, H, T, ws.hs, s), "shared gate/up launch");
+    HIPCHK(launch_rvq_gateup(src, off, H, I, items, ws.xh, ws.hh, s), "rvq gate/up launch");
+    HIPCHK(launch_rvq_down(src, off, H, I, items, KS, ws.hh, ws.ypart, s), "rvq down launch");
+    if (L->shared) HIPCHK(launch_dense_down(L->shared, H, I, ws.hs, T, ws.ysh, s), "shared down launch");
+    HIPCHK(launch_combine(ws.ypart, k, KS, H, w, L->shared ? ws.ysh : nullptr, out, H, T, 0, s), "combine launch");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+int moe_rvq_record_layout(int32_t H, int32_t I, moe_record_layout *out) {
+    if (!out) return fail(MOE_E_INVAL, "out is NULL");
+    if (!dims_ok(H, I)) return fail(MOE_E_INVAL, "H=%d, I=%d must be positive multiples of 128", H, I);
+    layout_of(H, I, out);
+    return MOE_OK;
+}
+
+size_t moe_route_workspace_bytes(int32_t E, int32_t T) {
+    if (E < 1 || T < 0) return 0;
+    return (size_t)align_up((int64_t)E * T * 4, 256);
+}
+
+int moe_route_topk(const moe_router *r, const void *x, int32_t x_dtype, int32_t T, int32_t H, int32_t *idx,
+                   float *w, void *ws, size_t ws_bytes, void *hip_stream) {
+    int rc = check_router(r, H);
+    if (rc) return rc;
+    if (T < 0) return fail(MOE_E_INVAL, "T=%d < 0", T);
+    if (!dtype_ok(x_dtype)) return fail(MOE_E_INVAL, "unknown x dtype %d", x_dtype);
+    if (T == 0) return MOE_OK;
+    if (!x || !idx || !w || !ws) return fail(MOE_E_INVAL, "x, idx, w and ws must be non-NULL");
+    if (ws_bytes < moe_route_workspace_bytes(r->E, T))
+        return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, moe_route_workspace_bytes(r->E, T));
+    hipStream_t s = (hipStream_t)hip_stream;
+    HIPCHK(launch_route_logits(r->weight, r->bias, r->E, H, x, x_dtype, T, (float *)ws, s), "route logits launch");
+    HIPCHK(launch_topk((const float *)ws, r->E, r->k, r->score_fn, T, idx, w, s), "top-k launch");
+    return MOE_OK;
+}
+
+size_t moe_expert_ffn_workspace_bytes(int32_t H, int32_t I, int32_t T) {
+    if (!dims_ok(H, I) || T < 0) return 0;
+    return carve_layer(nullptr, H, I, 1, 1, std::max(T, 1), false).bytes;
+}
+
+int moe_expert_ffn_rvq(const void *record, int32_t H, int32_t I, const float *x, int32_t T, const float *gate_w,
+                       float *y, int32_t accumulate, void *ws, size_t ws_bytes, void *hip_stream) {
+    if (!dims_ok(H, I)) return fail(MOE_E_INVAL, "H=%d, I=%d must be positive multiples of 128", H, I);
+    if (T < 0) return fail(MOE_E_INVAL, "T=%d < 0", T);
+    if (T == 0) return MOE_OK;
+    if (!record || !x || !y || !ws) return fail(MOE_E_INVAL, "record, x, y and ws must be non-NULL");
+    if ((uintptr_t)record % 256) return fail(MOE_E_INVAL, "record must be 256-byte aligned");
+    const size_t need = moe_expert_ffn_workspace_bytes(H, I, T);
+    if (ws_bytes < need) return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    hipStream_t s = (hipStream_t)hip_stream;
+    const LayerWs L = carve_layer(ws, H, I, 1, 1, T, false);
+    RecSrc src{};
+    src.list[0] = record;
+    src.rank[0] = 0;
+    src.k = 1;
+    src.n_local = 1;
+    const RecOffsets off = offsets_of(H, I);
+    const int KS = down_splits(H, I, T);
+    HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, T, H, H, L.xh, s), "pack_x launch");
+    HIPCHK(launch_rvq_gateup(src, off, H, I, T, L.xh, L.hh, s), "rvq gate/up launch");
+    HIPCHK(launch_rvq_down(src, off, H, I, T, KS, L.hh, L.ypart, s), "rvq down launch");
+    HIPCHK(launch_combine(L.ypart, 1, KS, H, gate_w, nullptr, y, H, T, accumulate, s), "combine launch");
+    return MOE_OK;
+}
+
+size_t moe_layer_workspace_bytes(const moe_layer *L, int32_t T) {
+    if (!L || !dims_ok(L->H, L->I) || L->router.E < 1 || L->router.k < 1 || T < 0) return 0;
+    return carve_layer(nullptr, L->H, L->I, L->router.E, L->router.k, std::max(T, 1), L->shared != nullptr).bytes;
+}
+
+int moe_layer_forward(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T, float *out, int32_t *idx_out,
+                      float *w_out, void *ws, size_t ws_bytes, void *hip_stream) {
+    int rc = check_layer(L, true);
+    if (rc) return rc;
+    if (T < 0) return fail(MOE_E_INVAL, "T=%d < 0", T);
+    if (!dtype_ok(x_dtype)) return fail(MOE_E_INVAL, "unknown x dtype %d", x_dtype);
+    if (T == 0) return MOE_OK;
+    if (!x || !out || !ws) return fail(MOE_E_INVAL, "x, out and ws must be non-NULL");
+    const size_t need = moe_layer_workspace_bytes(L, T);
+    if (ws_bytes < need) return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int E = L->router.E, k = L->router.k;
+    const LayerWs W = carve_layer(ws, L->H, L->I, E, k, T, L->shared != nullptr);
+    int32_t *idx = idx_out ? idx_out : W.idx;
+    float *w = w_out ? w_out : W.w;
+    HIPCHK(launch_route_logits(L->router.weight, L->router.bias, E, L->H, x, x_dtype, T, W.z, s),
+           "route logits launch");
+    HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, T, idx, w, s), "top-k launch");
+    RecSrc src{};
+    src.table = L->records;
+    src.idx = idx;
+    src.k = k;
+    src.n_local = k;
+    return run_experts(L, W, src, x, x_dtype, T, k, w, out, s);
+}
+
+size_t moe_decode_workspace_bytes(const moe_layer *layers, int32_t n_layers) {
+    if (!layers || n_layers < 1) return 0;
+    size_t m = 0;
+    for (int i = 0; i < n_layers; i++) m = std::max(m, moe_layer_workspace_bytes(&layers[i], 1));
+    return m;
+}
+
+int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x, int32_t T, float *out,
+                       int32_t *idx_out, void *ws, size_t ws_bytes, void *hip_stream) {
+    if (!layers || n_layers < 1) return fail(MOE_E_INVAL, "layers is NULL or n_layers < 1");
+    for (int l = 0; l < n_layers; l++) {
+        int rc = check_layer(&layers[l], true);
+        if (rc) return rc;
+        if (layers[l].H != layers[0].H || layers[l].I != layers[0].I || layers[l].router.k != layers[0].router.k)
+            return fail(MOE_E_INVAL, "layer %d differs from layer 0 in H, I or k", l);
+    }
+    if (T < 0) return fail(MOE_E_INVAL, "T=%d < 0", T);
+    if (T == 0) return MOE_OK;
+    if (!x || !out || !ws) return fail(MOE_E_INVAL, "x, out and ws must be non-NULL");
+    const size_t need = moe_decode_workspace_bytes(layers, n_layers);
+    if (ws_bytes < need) return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    const int H = layers[0].H, k = layers[0].router.k;
+    for (int t = 0; t < T; t++) {
+        for (int l = 0; l < n_layers; l++) {
+            const size_t step = (size_t)t * n_layers + l;
+            int rc = moe_layer_forward(&layers[l], x + step * H, MOE_DTYPE_F32, 1, out + step * H,
+                                       idx_out ? idx_out + step * k : nullptr, nullptr, ws, ws_bytes, hip_stream);
+            if (rc) return rc;
+        }
+    }
+    return MOE_OK;
+}
+
+
+size_t moe_streamed_workspace_bytes(const moe_layer *L, int32_t T) {
+    return moe_layer_workspace_bytes(L, T);
+}
+
+int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_id, const void *const *experts_host,
+                               const float *x, int32_t T, float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
+                               void *compute_stream, void *copy_stream) {
+    int rc = check_layer(L, false);
+    if (rc) return rc;
+    if (!c) return fail(MOE_E_INVAL, "cache is NULL");
+    if (T < 0 || T > 1) return fail(MOE_E_INVAL, "streamed decode takes T = 1 token (got %d)", T);
+    if (T == 0) return MOE_OK;
+    if (!experts_host || !x || !out || !ws) return fail(MOE_E_INVAL, "experts_host, x, out and ws must be non-NULL");
+    const int H = L->H, I = L->I, E = L->router.E, k = L->router.k;
+    if (c->core.capacity() < k)
+        return fail(MOE_E_INVAL, "cache capacity %d is below k = %d: the layer cannot hold one token's experts",
+                    c->core.capacity(), k);
+    moe_record_layout lay;
+    layout_of(H, I, &lay);
+    if ((int64_t)c->slot_bytes < lay.nbytes)
+        return fail(MOE_E_INVAL, "slot size %llu is below the record size %lld", (unsigned long long)c->slot_bytes,
+                    (long long)lay.nbytes);
+    if ((uint64_t)layer_id * (uint64_t)E + (uint64_t)E - 1 >= (uint64_t)MOE_NO_KEY)
+        return fail(MOE_E_INVAL, "layer_id * E overflows the 32-bit key");
+    const size_t need = moe_streamed_workspace_bytes(L, T);
+    if (ws_bytes < need) return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
+    const LayerWs W = carve_layer(ws, H, I, E, k, 1, L->shared != nullptr);
+    int32_t *idx = idx_out ? idx_out : W.idx;
+    const RecOffsets off = offsets_of(H, I);
+    const int KS = down_splits(H, I, k);
+
+    // route, then everything that does not depend on the choice
+    HIPCHK(launch_route_logits(L->router.weight, L->router.bias, E, H, x, MOE_DTYPE_F32, 1, W.z, cs), "route logits");
+    HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, 1, idx, W.w, cs), "top-k");
+    HIPCHK(hipMemcpyAsync(c->h_idx, idx, k * sizeof(int32_t), hipMemcpyDeviceToHost, cs), "idx to host");
+    HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, 1, H, H, W.xh, cs), "pack_x");
+    if (L->shared) {
+        HIPCHK(launch_dense_gateup(L->shared, H, I, x, MOE_DTYPE_F32, H, 1, W.hs, cs), "shared gate/up");
+        HIPCHK(launch_dense_down(L->shared, H, I, W.hs, 1, W.ysh, cs), "shared down");
+    }
+    HIPCHK(hipStreamSynchronize(cs), "wait for routing");
+
+    // lookups in ascending expert id; misses start their copies at once
+    int order[MOE_MAX_K];
+    for (int j = 0; j < k; j++) {
+        order[j] = j;
+        if (c->h_idx[j] < 0 || c->h_idx[j] >= E) return fail(MOE_E_HIP, "router produced expert id %d", c->h_idx[j]);
+    }
+    std::sort(order, order + k, [&](int a, int b) { return c->h_idx[a] < c->h_idx[b]; });
+    int32_t slot_of[MOE_MAX_K];
+    bool hit[MOE_MAX_K];
+    for (int n = 0; n < k; n++) {
+        const int j = order[n];
+        const int e = c->h_idx[j];
+        const uint32_t key = layer_id * (uint32_t)E + (uint32_t)e;
+        int32_t s = c->core.lookup(key);
+        hit[j] = s >= 0;
+        if (s < 0) {
+            uint32_t ev;
+            if (!experts_host[e]) return fail(MOE_E_INVAL, "experts_host[%d] is NULL", e);
+            rc = expert_cache_insert(c, key, experts_host[e], ps, &s, &ev);
+            if (rc) return rc;
+        }
+        slot_of[j] = s;
+    }
+
+    // hit experts run at once; each miss expert after its copy lands
+    RecSrc hits{};
+    hits.k = k;
+    for (int n = 0; n < k; n++) {
+        const int j = order[n];
+        if (!hit[j]) continue;
+        rc = cache_wait(c, slot_of[j], cs);
+        if (rc) return rc;
+        hits.list[hits.n_local] = c->pool + (size_t)slot_of[j] * c->slot_bytes;
+        hits.rank[hits.n_local] = (uint8_t)j;
+        hits.n_local++;
+    }
+    if (hits.n_local) {
+        HIPCHK(launch_rvq_gateup(hits, off, H, I, hits.n_local, W.xh, W.hh, cs), "rvq gate/up (hits)");
+        HIPCHK(launch_rvq_down(hits, off, H, I, hits.n_local, KS, W.hh, W.ypart, cs), "rvq down (hits)");
+    }
+    for (int n = 0; n < k; n++) {
+        const int j = order[n];
+        if (hit[j]) continue;
+        rc = cache_wait(c, slot_of[j], cs);
+        if (rc) return rc;
+        RecSrc one{};
+        one.k = k;
+        one.n_local = 1;
+        one.list[0] = c->pool + (size_t)slot_of[j] * c->slot_bytes;
+        one.rank[0] = (uint8_t)j;
+        HIPCHK(launch_rvq_gateup(one, off, H, I, 1, W.xh, W.hh, cs), "rvq gate/up (miss)");
+        HIPCHK(launch_rvq_down(one, off, H, I, 1, KS, W.hh, W.ypart, cs), "rvq down (miss)");
+    }
+    HIPCHK(launch_combine(W.ypart, k, KS, H, W.w, L->shared ? W.ysh : nullptr, out, H, 1, 0, cs), "combine");
+    for (int j = 0; j < k; j++) {
+        rc = cache_release(c, slot_of[j], cs);
+        if (rc) return rc;
+    }
+    return MOE_OK;
+}
+
+size_t moe_grouped_workspace_bytes(const moe_layer *L, int32_t T) {
+    return moe_layer_workspace_bytes(L, T);
+}
+
+int moe_layer_forward_grouped(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T, float *out,
+                              int32_t *idx_out, float *w_out, void *ws, size_t ws_bytes, void *hip_stream) {
+    (void)L; (void)x; (void)x_dtype; (void)T; (void)out; (void)idx_out; (void)w_out; (void)ws; (void)ws_bytes;
+    (void)hip_stream;
+    return fail(MOE_E_INVAL, "grouped path not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal declarations shared by the HIP kernels and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kCbRows = MOE_CODEBOOK_ROWS;   // codebook rows (12-bit indices)
+constexpr int kTileRows = 64;                // rows per code tile = lanes per wave
+constexpr int kChunkCols = 128;              // columns per code tile (16 groups)
+constexpr int kTileBytes = 3072;             // 64 rows x 48 bytes
+constexpr int kTileVec = kTileBytes / 16;    // 16-byte words per tile
+
+// How a work item finds its expert record.  A launch covers T tokens x
+// n_local items per token; local item l of token t is global item t*k + rank,
+// where rank = l (table mode) or rank[l] (list mode).  Global items index the
+// SwiGLU intermediate and the down partial sums, so any grouping of ranks
+// into launches produces the same bytes.
+struct RecSrc {
+    const void *const *table;      // [dev] record pointer per expert, or nullptr
+    const int32_t *idx;            // [dev] expert id per global item (table mode)
+    const void *list[MOE_MAX_K];   // list mode: record pointer of local item l
+    uint8_t rank[MOE_MAX_K];       // list mode: rank of local item l
+    int32_t k;                     // ranks per token
+    int32_t n_local;               // local items per token in this launch
+};
+
+// Section offsets of one record (bytes).
+struct RecOffsets {
+    int64_t codes[3];   // gate, up, down
+    int64_t scales[3];
+    int64_t cb[3];
+};
+
+// Workspace carving for one layer call.
+struct LayerWs {
+    float *z;          // [T, E] router logits
+    int32_t *idx;      // [T, k]
+    float *w;          // [T, k]
+    uint32_t *xh;      // [T, H/2] x as fp16 pairs
+    uint16_t *hh;      // [T*k, I] SwiGLU intermediate as fp16
+    float *ypart;      // [T*k, KS, H] down partial sums (scaled)
+    float *hs;         // [T, I] shared-expert intermediate (fp32)
+    float *ysh;        // [T, H] shared-expert output
+    size_t bytes;
+};
+
+// ---- launchers (kernels.hip) ------------------------------------------------
+hipError_t launch_route_logits(const float *W, const float *bias, int E, int H, const void *x,
+                               int x_dtype, int T, float *z, hipStream_t s);
+hipError_t launch_topk(const float *z, int E, int k, int score_fn, int T, int32_t *idx, float *w,
+                       hipStream_t s);
+hipError_t launch_pack_x(const void *x, int x_dtype, int T, int H, int64_t x_stride, uint32_t *xh,
+                         hipStream_t s);
+// n_local_total = T * src.n_local local items in the launch
+hipError_t launch_rvq_gateup(const RecSrc &src, const RecOffsets &off, int H, int I, int n_local_total,
+                             const uint32_t *xh, uint16_t *hh, hipStream_t s);
+hipError_t launch_rvq_down(const RecSrc &src, const RecOffsets &off, int H, int I, int n_local_total,
+                           int KS, const uint16_t *hh, float *ypart, hipStream_t s);
+hipError_t launch_combine(const float *ypart, int k, int KS, int H, const float *w, const float *ysh,
+                          float *out, int64_t out_stride, int T, int accumulate, hipStream_t s);
+hipError_t launch_dense_gateup(const uint16_t *shared, int H, int I, const void *x, int x_dtype,
+                               int64_t x_stride, int T, float *hs, hipStream_t s);
+hipError_t launch_dense_down(const uint16_t *shared, int H, int I, const float *hs, int T,
+                             float *ysh, hipStream_t s);
+
+int down_splits(int H, int I, int n_items);
+
+}  // namespace moe

@@ -1,0 +1,211 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Expert indices and cache traces are compared bit for bit; outputs by
+relative L2 per layer call (<= 1e-3).  Inputs are the seeded synthetic
+workloads shared by both sides.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import RTOL_F32_PATH, log, rel_l2, same_sets, weights_by_expert
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import routed_expert_streaming_amd as m
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def tiny(moe):
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    return DeviceWorkload(synth.CONFIGS["tiny"])
+
+
+def _oracle_layer(dw, L, x64):
+    """Oracle layer output.  Only the experts the oracle's own router selects
+    are read, so the others get a placeholder instead of a generated record."""
+    cfg, wl = dw.cfg, dw.wl
+    ridx, _, _ = oracle.route(wl.router(L), wl.bias(L), x64, cfg.k, cfg.score)
+    needed = set(int(e) for e in ridx.reshape(-1))
+    empty = np.zeros(1, np.uint8)
+    recs = [wl.record(L, e) if e in needed else empty for e in range(cfg.E)]
+    return oracle.layer(wl.router(L), wl.bias(L), cfg.k, cfg.score, recs, wl.shared(L), cfg.H, cfg.I, x64)
+
+
+def test_tiny_route_bit_exact(moe, tiny):
+    cfg = tiny.cfg
+    x = tiny.inputs()[:, 0, :].contiguous()
+    idx, w = moe.route_topk(tiny.layers[0].router, x)
+    ridx, rw, z = oracle.route(tiny.wl.router(0), None, x.cpu().numpy().astype(np.float64), cfg.k, cfg.score)
+    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    assert np.array_equal(idx, ridx)      # margins >= 1e-3 everywhere: order is unique too
+    np.testing.assert_allclose(w, rw, rtol=2e-6, atol=1e-7)
+    assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-6)
+
+
+def test_tiny_layer_parity(moe, tiny):
+    x = tiny.inputs()[:, 0, :].contiguous()
+    out, idx, w = moe.layer_forward(tiny.layers[0], x)
+    ref, ridx, rw = _oracle_layer(tiny, 0, x.cpu().numpy().astype(np.float64))
+    assert same_sets(idx.cpu().numpy(), ridx)
+    r = rel_l2(out.cpu().numpy(), ref)
+    log(f"tiny layer rel_l2={r:.3e}")
+    assert r <= RTOL_F32_PATH
+
+
+def test_tiny_zero_tokens_is_noop(moe, tiny):
+    x = torch.empty((0, tiny.cfg.H), device="cuda")
+    out, idx, w = moe.layer_forward(tiny.layers[0], x)
+    assert out.shape == (0, tiny.cfg.H)
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_expert_ffn_parity(moe, tiny, T):
+    cfg = tiny.cfg
+    rec_np = tiny.wl.record(0, 6)
+    rec = torch.from_numpy(rec_np).cuda()
+    rng = np.random.default_rng(T)
+    x = rng.standard_normal((T, cfg.H)).astype(np.float32)
+    g = rng.uniform(0.1, 1.0, T).astype(np.float32)
+    y0 = rng.standard_normal((T, cfg.H)).astype(np.float32)
+    y = torch.from_numpy(y0).cuda()
+    moe.expert_ffn_rvq(rec, cfg.H, cfg.I, torch.from_numpy(x).cuda(), gate_w=torch.from_numpy(g).cuda(), y=y,
+                       accumulate=True)
+    ffn = oracle.expert_ffn(rec_np, cfg.H, cfg.I, x.astype(np.float64))
+    ref = y0 + g[:, None] * ffn
+    r = rel_l2(y.cpu().numpy() - y0, g[:, None] * ffn)
+    log(f"expert ffn T={T} rel_l2={r:.3e}")
+    assert r <= RTOL_F32_PATH
+    np.testing.assert_allclose(y.cpu().numpy(), ref, rtol=1e-3, atol=1e-3)
+
+
+def test_expert_ffn_onehot_exact_codebook(moe):
+    # integer one-hot codebook, power-of-two scales, fp16-exact inputs: every
+    # product is exact and the sums are small integers, so fp32 equals fp64
+    H, I = 256, 256
+    rng = np.random.default_rng(3)
+    cb = np.zeros((4096, 8), np.float16)
+    c = np.arange(4096)
+    cb[c, c % 8] = ((c // 8) % 8).astype(np.float16)
+    codes = [rng.integers(0, 1 << 24, (n, kk // 8)).astype(np.uint32) for n, kk in ((I, H), (I, H), (H, I))]
+    sc = (np.full(I, 2.0 ** -6, np.float16), np.full(I, 2.0 ** -6, np.float16), np.full(H, 2.0 ** -6, np.float16))
+    rec_np = synth.build_record(H, I, *codes, sc, np.stack([cb, cb, cb]))
+    x = rng.integers(-2, 3, (2, H)).astype(np.float32)
+    y = moe.expert_ffn_rvq(torch.from_numpy(rec_np).cuda(), H, I, torch.from_numpy(x).cuda())
+    ref = oracle.expert_ffn(rec_np, H, I, x.astype(np.float64))
+    assert rel_l2(y.cpu().numpy(), ref) <= RTOL_F32_PATH
+
+
+@pytest.mark.parametrize("name,T", [("kimi_linear", 6), ("mixtral", 2), ("k3_slice", 2), ("batched", 3)])
+def test_layer_parity_real_shapes(moe, name, T):
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    cfg = synth.get_config(name, tokens=T, layers=1, batched=False)
+    log(f"layer parity {name} T={T}: uploading")
+    dw = DeviceWorkload(cfg, layers=[0])
+    x = dw.inputs()
+    x = (x[:, 0, :] if x.dim() == 3 else x).contiguous()
+    if cfg.x_dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    oracle.set_threads(16)
+    out, idx, w = moe.layer_forward(dw.layers[0], x)
+    ref, ridx, rw = _oracle_layer(dw, 0, x.float().cpu().numpy().astype(np.float64))
+    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    assert same_sets(idx, ridx)
+    np.testing.assert_allclose(weights_by_expert(idx, w), weights_by_expert(ridx, rw), rtol=1e-5, atol=1e-7)
+    for t in range(T):
+        r = rel_l2(out[t].cpu().numpy(), ref[t])
+        log(f"  {name} token {t} rel_l2={r:.3e}")
+        assert r <= RTOL_F32_PATH
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_decode_forward_two_layers(moe):
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    cfg = synth.get_config("kimi_linear", tokens=3, layers=2)
+    dw = DeviceWorkload(cfg)
+    x = dw.inputs()
+    out, idx = moe.decode_forward(dw.layers, x)
+    oracle.set_threads(16)
+    x64 = x.cpu().numpy().astype(np.float64)
+    for t in range(cfg.tokens):
+        for L in range(cfg.layers):
+            ref, ridx, _ = _oracle_layer(dw, L, x64[t, L][None])
+            assert same_sets(idx[t, L].cpu().numpy()[None], ridx)
+            r = rel_l2(out[t, L].cpu().numpy(), ref[0])
+            log(f"decode t={t} L={L} rel_l2={r:.3e}")
+            assert r <= RTOL_F32_PATH
+
+
+def _streamed_setup(moe, cfg, capacity):
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload, HostRecordPool
+    dw = DeviceWorkload(cfg)                       # resident copy: the reference for transparency
+    hp = HostRecordPool(cfg, list(range(cfg.layers)))
+    pool = torch.empty(capacity * hp.stride, dtype=torch.uint8, device="cuda")
+    cache = moe.ExpertCache(capacity, hp.stride, pool)
+    return dw, hp, cache
+
+
+@pytest.mark.parametrize("capacity", [16, 23, 40])
+def test_streamed_trace_and_transparency(moe, capacity):
+    # K3 structure with fewer experts so that a few tokens exercise hits,
+    # misses and evictions at capacity == k and above
+    cfg = synth.get_config("k3_slice", tokens=5, layers=2, E=48)
+    dw, hp, cache = _streamed_setup(moe, cfg, capacity)
+    x = dw.inputs()
+    copy_stream = torch.cuda.Stream()
+    outs, idxs = [], []
+    tables = [hp.table(L) for L in range(cfg.layers)]
+    ws = torch.empty(moe.streamed_workspace_bytes(dw.layers[0]), dtype=torch.uint8, device="cuda")
+    for t in range(cfg.tokens):
+        for L in range(cfg.layers):
+            idx = torch.empty((1, cfg.k), dtype=torch.int32, device="cuda")
+            o = moe.layer_forward_streamed(dw.layers[L], cache, L, None, x[t, L][None].contiguous(), copy_stream,
+                                           ws=ws, idx=idx, host_table=tables[L])
+            outs.append(o.clone())
+            idxs.append(idx.clone())
+    torch.cuda.synchronize()
+    # transparency: identical bits to the resident path
+    res, ridx = moe.decode_forward(dw.layers, x)
+    for n, (o, i) in enumerate(zip(outs, idxs)):
+        t, L = divmod(n, cfg.layers)
+        assert torch.equal(o[0], res[t, L]), f"streamed != resident at token {t} layer {L}"
+        assert torch.equal(i[0], ridx[t, L])
+    # trace: bit-exact against the oracle's LRU over the oracle's own routing
+    x64 = x.cpu().numpy().astype(np.float64)
+    oidx = np.zeros((cfg.tokens * cfg.layers, cfg.k), np.int32)
+    for t in range(cfg.tokens):
+        for L in range(cfg.layers):
+            oidx[t * cfg.layers + L] = oracle.route(dw.wl.router(L), dw.wl.bias(L), x64[t, L][None], cfg.k,
+                                                    cfg.score)[0][0]
+    key, hit, slot, ev = oracle.stream_trace(oidx, cfg.layers, cfg.E, capacity)
+    tr = cache.trace()
+    assert [r[0] for r in tr] == key.tolist()
+    assert [r[1] for r in tr] == hit.tolist()
+    assert [r[2] for r in tr] == slot.tolist()
+    assert [(-1 if r[3] is None else r[3]) for r in tr] == ev.tolist()
+    st = cache.stats()
+    log(f"streamed capacity={capacity}: hits {st['hits']}/{st['lookups']} evictions {st['evictions']}")
+    cache.close()
+
+
+def test_streamed_rejects_capacity_below_k(moe):
+    cfg = synth.get_config("k3_slice", tokens=1, layers=1, E=32)
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    dw = DeviceWorkload(cfg, with_records=False)
+    pool = torch.empty(8 * 12013568, dtype=torch.uint8, device="cuda")
+    cache = moe.ExpertCache(8, 12013568, pool)
+    with pytest.raises(moe.MoeError) as e:
+        moe.layer_forward_streamed(dw.layers[0], cache, 0, [1] * cfg.E, dw.inputs()[0, 0][None].contiguous(),
+                                   torch.cuda.Stream())
+    assert e.value.code == -1
+    cache.close()
