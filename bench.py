@@ -1,0 +1,169 @@
+#!/usr/bin/env python3
+"""MoE decode benchmark on one MI355X.
+
+Workload (default): Mixtral-8x7B-shaped decode -- 32 MoE layers, hidden 4096,
+expert intermediate 14336, 8 experts per layer with 3.00-bit RVQ records
+(66,322,432 bytes each, all 256 resident in HBM), softmax top-2 with
+renormalisation, batch 1 token, seeded fp32 layer inputs.  One step = one
+token through all 32 layers (route -> top-k -> RVQ SwiGLU experts ->
+combine), issued by the library's decode driver.
+
+Prints one JSON line: tok/s, expert-weight HBM GB/s against the 8 TB/s peak
+(the decode step, timed with HIP events on the stream it runs on), and the
+CPU oracle timed on this host's cores on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def git_commit() -> str:
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                              text=True, timeout=10).stdout.strip() or "unknown"
+    except Exception:
+        return "unknown"
+
+
+def cpu_baseline(cfg, x_np, sample_tokens: int):
+    """The fp64 oracle on `sample_tokens` tokens x all layers of the workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+    threads = min(16, len(os.sched_getaffinity(0)))
+    oracle.set_threads(threads)
+    wl = synth.Workload(cfg)
+    # inputs of the oracle: records of the experts its own router selects
+    # (generation is not timed)
+    jobs = []
+    for t in range(sample_tokens):
+        for L in range(cfg.layers):
+            x64 = x_np[t, L][None].astype(np.float64)
+            ridx, _, _ = oracle.route(wl.router(L), wl.bias(L), x64, cfg.k, cfg.score)
+            jobs.append((L, x64, set(int(e) for e in ridx.reshape(-1))))
+    empty = np.zeros(1, np.uint8)
+    t_total = 0.0
+    for L, x64, needed in jobs:
+        recs = [wl.record(L, e) if e in needed else empty for e in range(cfg.E)]
+        sh = wl.shared(L)
+        t0 = time.perf_counter()
+        oracle.layer(wl.router(L), wl.bias(L), cfg.k, cfg.score, recs, sh, cfg.H, cfg.I, x64)
+        t_total += time.perf_counter() - t0
+    return {"value": round(sample_tokens / t_total, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sample_tokens} tokens x {cfg.layers} layers of the {cfg.name} decode (fp64, "
+                      f"{threads} threads); {t_total:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64, help="timed decode tokens")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed decode tokens")
+    ap.add_argument("--config", default="mixtral", choices=["mixtral", "kimi_linear"])
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "see the sharding design notes.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import routed_expert_streaming_amd as moe
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+
+    moe.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    cfg = synth.get_config(args.config)
+    n_tok = args.warmup + args.steps
+    if n_tok > cfg.tokens:
+        cfg = cfg.replace(tokens=n_tok)
+    t0 = time.time()
+    dw = DeviceWorkload(cfg)
+    x = dw.inputs()
+    log(f"workload {cfg.name}: {cfg.layers} layers x {cfg.E} experts uploaded in {time.time() - t0:.1f} s "
+        f"(input redraws {dw.wl.redraws})")
+    layers = dw.layers
+    ws = torch.empty(moe.decode_workspace_bytes(layers), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def step(t):
+        moe.decode_forward(layers, x[t:t + 1], ws=ws, out=out[t:t + 1], want_idx=False)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+    tok_s = args.steps / elapsed
+    bytes_tok = synth.expert_bytes_per_token(cfg)
+    mean_step_s = float(np.mean(step_ms)) / 1e3
+    achieved = bytes_tok / mean_step_s / 1e9
+    record = {
+        "metric": "MoE decode tok/s on 1 MI355X; expert-weight HBM GB/s as % of peak",
+        "value": round(tok_s, 3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 accumulate, fp16 x RVQ-3bit weights",
+        "data": "synthetic (seeded; random RVQ records and router weights)",
+        "config": {"workload": f"{cfg.name} decode: {cfg.layers} layers, H {cfg.H}, I {cfg.I}, "
+                               f"{cfg.E} experts, top-{cfg.k} {cfg.score}, batch 1",
+                   "tokens": args.steps, "expert_bytes_per_token": bytes_tok},
+        "expert_gbs": round(bytes_tok * tok_s / 1e9, 1),
+        "expert_hbm_frac": round(bytes_tok * tok_s / 1e9 / HBM_PEAK_GBS, 4),
+        "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode step (route, RVQ gate/up, RVQ down, combine over all layers)",
+                     "algorithmic_bytes_per_launch": bytes_tok},
+        "device": torch.cuda.get_device_name(0),
+        "commit": git_commit(),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        record["cpu_baseline"] = cpu_baseline(cfg, x.cpu().numpy(), args.cpu_sample_tokens)
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
