@@ -102,6 +102,35 @@ LayerWs carve_layer(void *ws, int H, int I, int E, int k, int T, bool shared) {
     return L;
 }
 
+struct GroupedWs {
+    float *z;
+    int32_t *idx, *perm, *inv, *counts, *offsets;
+    float *w;
+    uint16_t *xb, *hbuf, *hs;
+    float *ybuf, *ysh;
+    size_t bytes;
+};
+
+GroupedWs carve_grouped(void *ws, int H, int I, int E, int k, int T, bool shared) {
+    Carver c(ws);
+    GroupedWs G;
+    const size_t pairs = (size_t)T * k;
+    G.z = c.take<float>((size_t)T * E);
+    G.idx = c.take<int32_t>(pairs);
+    G.w = c.take<float>(pairs);
+    G.perm = c.take<int32_t>(pairs);
+    G.inv = c.take<int32_t>(pairs);
+    G.counts = c.take<int32_t>((size_t)E);
+    G.offsets = c.take<int32_t>((size_t)E + 1);
+    G.xb = c.take<uint16_t>((size_t)T * H);
+    G.hbuf = c.take<uint16_t>(pairs * I);
+    G.ybuf = c.take<float>(pairs * H);
+    G.hs = shared ? c.take<uint16_t>((size_t)T * I) : nullptr;
+    G.ysh = shared ? c.take<float>((size_t)T * H) : nullptr;
+    G.bytes = (size_t)align_up((int64_t)c.pos, 256);
+    return G;
+}
+
 int check_router(const moe_router *r, int32_t H) {
     if (!r) return fail(MOE_E_INVAL, "router is NULL");
     if (!r->weight) return fail(MOE_E_INVAL, "router weight is NULL");
@@ -378,14 +407,34 @@ int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_
 }
 
 size_t moe_grouped_workspace_bytes(const moe_layer *L, int32_t T) {
-    return moe_layer_workspace_bytes(L, T);
+    if (!L || !dims_ok(L->H, L->I) || L->router.E < 1 || L->router.k < 1 || T < 0) return 0;
+    return carve_grouped(nullptr, L->H, L->I, L->router.E, L->router.k, std::max(T, 1), L->shared != nullptr).bytes;
 }
 
 int moe_layer_forward_grouped(const moe_layer *L, const void *x, int32_t x_dtype, int32_t T, float *out,
                               int32_t *idx_out, float *w_out, void *ws, size_t ws_bytes, void *hip_stream) {
-    (void)L; (void)x; (void)x_dtype; (void)T; (void)out; (void)idx_out; (void)w_out; (void)ws; (void)ws_bytes;
-    (void)hip_stream;
-    return fail(MOE_E_INVAL, "grouped path not built yet");
+    int rc = check_layer(L, true);
+    if (rc) return rc;
+    if (T < 0) return fail(MOE_E_INVAL, "T=%d < 0", T);
+    if (!dtype_ok(x_dtype)) return fail(MOE_E_INVAL, "unknown x dtype %d", x_dtype);
+    if (T == 0) return MOE_OK;
+    if (!x || !out || !ws) return fail(MOE_E_INVAL, "x, out and ws must be non-NULL");
+    const size_t need = moe_grouped_workspace_bytes(L, T);
+    if (ws_bytes < need) return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int H = L->H, I = L->I, E = L->router.E, k = L->router.k;
+    const GroupedWs W = carve_grouped(ws, H, I, E, k, T, L->shared != nullptr);
+    int32_t *idx = idx_out ? idx_out : W.idx;
+    float *w = w_out ? w_out : W.w;
+    HIPCHK(launch_route_logits(L->router.weight, L->router.bias, E, H, x, x_dtype, T, W.z, s), "route logits");
+    HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, T, idx, w, s), "top-k");
+    HIPCHK(launch_group(idx, T * k, E, W.perm, W.inv, W.counts, W.offsets, s), "group");
+    HIPCHK(launch_to_bf16(x, x_dtype, (size_t)T * H, W.xb, s), "x to bf16");
+    if (L->shared) HIPCHK(launch_grouped_dense(L->shared, H, I, T, W.xb, W.hs, W.ysh, s), "shared expert");
+    HIPCHK(launch_grouped_rvq(L->records, offsets_of(H, I), E, H, I, W.counts, W.offsets, W.perm, k, W.xb, W.hbuf,
+                              W.ybuf, s), "grouped RVQ GEMMs");
+    HIPCHK(launch_grouped_combine(W.ybuf, W.inv, w, k, H, T, L->shared ? W.ysh : nullptr, out, s), "combine");
+    return MOE_OK;
 }
 
 }  // extern "C"

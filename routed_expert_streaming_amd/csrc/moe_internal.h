@@ -70,4 +70,16 @@ hipError_t launch_dense_down(const uint16_t *shared, int H, int I, const float *
 
 int down_splits(int H, int I, int n_items);
 
+// ---- batched path (kernels_grouped.hip) --------------------------------------
+hipError_t launch_group(const int32_t *idx, int n_pairs, int E, int32_t *perm, int32_t *inv, int32_t *counts,
+                        int32_t *offsets, hipStream_t s);
+hipError_t launch_to_bf16(const void *x, int x_dtype, size_t n, uint16_t *xb, hipStream_t s);
+hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, int E, int H, int I,
+                              const int32_t *counts, const int32_t *offsets, const int32_t *perm, int k,
+                              const uint16_t *xb, uint16_t *hbuf, float *ybuf, hipStream_t s);
+hipError_t launch_grouped_dense(const uint16_t *shared, int H, int I, int T, const uint16_t *xb, uint16_t *hs,
+                                float *ysh, hipStream_t s);
+hipError_t launch_grouped_combine(const float *ybuf, const int32_t *inv, const float *w, int k, int H, int T,
+                                  const float *ysh, float *out, hipStream_t s);
+
 }  // namespace moe
