@@ -76,8 +76,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64, help="timed decode tokens")
     ap.add_argument("--warmup", type=int, default=2, help="untimed decode tokens")
-    ap.add_argument("--config", default="mixtral", choices=["mixtral", "kimi_linear"])
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2)
+    ap.add_argument("--config", default="mixtral", choices=["mixtral", "kimi_linear", "batched", "k3_slice"],
+                    help="mixtral / kimi_linear: resident decode; batched: one 256-token grouped layer call "
+                         "per step; k3_slice: streamed decode through the HBM slot cache (cold start)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -97,6 +99,10 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     cfg = synth.get_config(args.config)
+    if args.config == "batched":
+        return bench_batched(args, cfg)
+    if args.config == "k3_slice":
+        return bench_streamed(args, cfg)
     n_tok = args.warmup + args.steps
     if n_tok > cfg.tokens:
         cfg = cfg.replace(tokens=n_tok)
@@ -162,6 +168,124 @@ def main() -> int:
         log("timing the CPU oracle on a sample ...")
         record["cpu_baseline"] = cpu_baseline(cfg, x.cpu().numpy(), args.cpu_sample_tokens)
     print(json.dumps(record), flush=True)
+    return 0
+
+
+def bench_batched(args, cfg) -> int:
+    """One step = one 256-token batched layer call on the grouped matrix-core path."""
+    import numpy as np
+    import torch
+
+    import synth
+    import routed_expert_streaming_amd as moe
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    t0 = time.time()
+    dw = DeviceWorkload(cfg)
+    x = dw.inputs().to(torch.bfloat16).contiguous()
+    log(f"workload {cfg.name}: {cfg.E} experts uploaded in {time.time() - t0:.1f} s")
+    layer = dw.layers[0]
+    ws = torch.empty(moe.grouped_workspace_bytes(layer, cfg.tokens), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.tokens, cfg.H), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        moe.layer_forward_grouped(layer, x, ws=ws, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        moe.layer_forward_grouped(layer, x, ws=ws, out=out)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    step_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    # every expert is touched (P(unused) ~ 2e-5): bytes = all records + shared
+    nbytes = cfg.E * synth.expert_bytes(cfg) + synth.shared_record_bytes(cfg.H, cfg.I)
+    flops = 2.0 * cfg.tokens * (cfg.k + 1) * 3 * cfg.H * cfg.I + 2.0 * cfg.tokens * cfg.E * cfg.H
+    mean_s = float(np.mean(step_ms)) / 1e3
+    rec = {"metric": "batched MoE layer tokens/s on 1 MI355X (grouped bf16 MFMA)",
+           "value": round(cfg.tokens * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 MFMA, fp32 accumulate",
+           "data": "synthetic", "config": {"workload": f"batched layer: T {cfg.tokens}, H {cfg.H}, I {cfg.I}, "
+                                                        f"{cfg.E} experts, top-{cfg.k} + shared"},
+           "roofline": {"bound": "hbm", "achieved": round(nbytes / mean_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(nbytes / mean_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "batched layer call", "algorithmic_bytes_per_launch": nbytes},
+           "mfma": {"flops_per_call": flops, "achieved_tflops": round(flops / mean_s / 1e12, 2),
+                    "peak_tflops": 2500.0, "utilisation": round(flops / mean_s / 1e12 / 2500.0, 4)},
+           "commit": git_commit()}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def bench_streamed(args, cfg) -> int:
+    """K3-scale slice: 8 layers x 768 experts in pinned host memory, a 25%
+    HBM slot cache (1536 slots) starting cold; one step = one token."""
+    import numpy as np
+    import torch
+
+    import synth
+    import routed_expert_streaming_amd as moe
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload, HostRecordPool
+    n_tok = args.warmup + args.steps
+    if n_tok > cfg.tokens:
+        cfg = cfg.replace(tokens=n_tok)
+    t0 = time.time()
+    dw = DeviceWorkload(cfg, with_records=False)
+    x = dw.inputs()
+    hp = HostRecordPool(cfg, list(range(cfg.layers)))
+    log(f"host pool {len(hp.chunks)} chunks, {cfg.layers * cfg.E} records ready in {time.time() - t0:.1f} s")
+    cap = cfg.cache_capacity
+    pool = torch.empty(cap * hp.stride, dtype=torch.uint8, device="cuda")
+    cache = moe.ExpertCache(cap, hp.stride, pool)
+    tables = [hp.table(L) for L in range(cfg.layers)]
+    ws = torch.empty(moe.streamed_workspace_bytes(dw.layers[0]), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.tokens, cfg.layers, cfg.H), dtype=torch.float32, device="cuda")
+    copy_stream = torch.cuda.Stream()
+
+    def token(t):
+        for L in range(cfg.layers):
+            moe.layer_forward_streamed(dw.layers[L], cache, L, None, x[t, L][None], copy_stream, ws=ws,
+                                       out=out[t, L][None], host_table=tables[L])
+
+    # the cold start is part of the workload: warm-up tokens are decoded (and
+    # counted in the cache) but not timed
+    for t in range(args.warmup):
+        token(t)
+    torch.cuda.synchronize()
+    st0 = cache.stats()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        token(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    st = cache.stats()
+    tr = cache.trace()
+    hits = np.array([r[1] for r in tr])
+    per_tok = cfg.layers * cfg.k
+    half = (cfg.tokens // 2) * per_tok
+    misses_timed = (st["lookups"] - st0["lookups"]) - (st["hits"] - st0["hits"])
+    tok_s = args.steps / elapsed
+    hbm_bytes = synth.expert_bytes_per_token(cfg)
+    rec = {"metric": "streamed MoE decode tok/s on 1 MI355X (HBM LRU slot cache, misses over PCIe)",
+           "value": round(tok_s, 3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(elapsed * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32 accumulate, fp16 x RVQ-3bit weights", "data": "synthetic",
+           "config": {"workload": f"k3_slice streamed decode: {cfg.layers} layers x {cfg.E} experts, H {cfg.H}, "
+                                  f"I {cfg.I}, top-{cfg.k} sigmoid + shared, Zipf bias, cache {cap} slots",
+                      "tokens": cfg.tokens},
+           "hit_rate_all": round(float(hits.mean()), 4),
+           "hit_rate_second_half": round(float(hits[half:].mean()), 4) if len(hits) > half else None,
+           "misses_per_token_timed": round(misses_timed / args.steps, 2),
+           "h2d_gbs": round(misses_timed * hp.stride / elapsed / 1e9, 2),
+           "hbm_expert_gbs": round(hbm_bytes * tok_s / 1e9, 1),
+           "cold_tier": {"records": cfg.layers * cfg.E, "pinned_records": hp.pinned_records,
+                         "note": "the rest in pageable host memory (this host page-locks at most ~59 GiB)"},
+           "commit": git_commit()}
+    cache.close()
+    print(json.dumps(rec), flush=True)
     return 0
 
 

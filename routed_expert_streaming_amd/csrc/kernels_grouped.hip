@@ -30,7 +30,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGWaves = 8;          // waves per workgroup
-constexpr int kTokBlocks = 4;       // 16-token blocks per pass (64 tokens)
+constexpr int kTokBlocks = 2;
+constexpr int kTwGateUp = 2;        // 16-row tiles per wave unit (gate/up)
+constexpr int kTwDown = 5;          // 16-row tiles per wave unit (down)       // 16-token blocks per pass (32 tokens)
 
 __device__ __forceinline__ uint32_t bf16_pair_from_f16_sum(uint32_t a, uint32_t b) {
     const f16x2 s = __builtin_bit_cast(f16x2, a) + __builtin_bit_cast(f16x2, b);   // v_pk_add_f16
@@ -150,7 +152,10 @@ struct GroupedArgs {
     int mat;                    // RVQ matrix: 0 = gate (+up), 2 = down
 };
 
-template <bool GATEUP, bool DENSE>
+// Work unit of a wave: TW 16-row tiles x one pass of up to 16*kTokBlocks
+// tokens, swept over all 128-column chunks.  The codes (or dense weights) and
+// the A fragments of chunk j+1 are loaded while chunk j is computed.
+template <bool GATEUP, bool DENSE, int TW>
 __global__ __launch_bounds__(kGWaves * 64) void k_grouped(GroupedArgs g) {
     extern __shared__ __align__(16) char lds[];
     const int slot = DENSE ? 0 : blockIdx.x / g.splits, split = DENSE ? 0 : blockIdx.x % g.splits;
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped(GroupedArgs g) {
     char *cb0 = lds, *cb1 = lds + kCbRows * 16;
     if constexpr (!DENSE) {
         const u32x4 *s0 = (const u32x4 *)(rec + g.off.cb[g.mat]);
-        const u32x4 *s1 = (const u32x4 *)(rec + g.off.cb[GATEUP ? 1 : 2]);
+        const u32x4 *s1 = (const u32x4 *)(rec + g.off.cb[1]);
         for (int i = threadIdx.x; i < kCbRows; i += kGWaves * 64) {
             ((u32x4 *)cb0)[i] = s0[i];
             if constexpr (GATEUP) ((u32x4 *)cb1)[i] = s1[i];
@@ -180,6 +185,7 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped(GroupedArgs g) {
     const int rows_per_split = g.N / g.splits;          // multiple of 16
     const int r_begin = split * rows_per_split;
     const int tiles = rows_per_split / 16;
+    const int tgroups = (tiles + TW - 1) / TW;
     const int cpr = g.K / kChunkCols;
     const uint8_t *codes0 = nullptr, *codes1 = nullptr;
     const _Float16 *sc0 = nullptr, *sc1 = nullptr;
@@ -189,79 +195,129 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped(GroupedArgs g) {
         sc0 = (const _Float16 *)(rec + g.off.scales[g.mat]);
         sc1 = (const _Float16 *)(rec + g.off.scales[1]);
     }
-    // work units: (16-row tile, 64-token pass); RVQ experts spread the units of
-    // their row range over the workgroup's waves, the dense matrix over the grid
     const int passes = (cnt + 16 * kTokBlocks - 1) / (16 * kTokBlocks);
-    const int units = tiles * passes;
+    const int units = tgroups * passes;
     const int u_first = DENSE ? blockIdx.x * kGWaves + wave : wave;
     const int u_step = DENSE ? gridDim.x * kGWaves : kGWaves;
     for (int u = u_first; u < units; u += u_step) {
-        const int tile = u % tiles, pass = u / tiles;
-        const int n = r_begin + tile * 16 + col;         // this lane's weight row
-        const uint8_t *t0 = nullptr, *t1 = nullptr;
-        if constexpr (!DENSE) {
-            t0 = codes0 + (size_t)(n >> 6) * cpr * kTileBytes;
-            t1 = codes1 + (size_t)(n >> 6) * cpr * kTileBytes;
+        const int tg = u % tgroups, pass = u / tgroups;
+        const int ntw = min(TW, tiles - tg * TW);             // tiles in this unit (wave-uniform)
+        int n[TW];
+        const uint8_t *t0[TW], *t1[TW];
+#pragma unroll
+        for (int t = 0; t < TW; t++) {
+            n[t] = r_begin + (tg * TW + min(t, ntw - 1)) * 16 + col;
+            if constexpr (!DENSE) {
+                t0[t] = codes0 + (size_t)(n[t] >> 6) * cpr * kTileBytes;
+                t1[t] = codes1 + (size_t)(n[t] >> 6) * cpr * kTileBytes;
+            }
         }
-        {
-            const int m_base = pass * 16 * kTokBlocks;
-            f32x4 acc0[kTokBlocks], acc1[kTokBlocks];
-            // A row pointers of this lane's token (row col) in each block
-            const uint16_t *arow[kTokBlocks];
+        const int m_base = pass * 16 * kTokBlocks;
+        const int nblk = min(kTokBlocks, (cnt - m_base + 15) / 16);
+        const uint16_t *arow[kTokBlocks];
+#pragma unroll
+        for (int b = 0; b < kTokBlocks; b++) {
+            const int m = m_base + b * 16 + col;
+            arow[b] = nullptr;
+            if (b < nblk && m < cnt) {
+                const int p = pos0 + m;
+                const int row = DENSE ? p : (g.a_by_token ? g.perm[p] / g.k : p);
+                arow[b] = g.a + (size_t)row * g.K;
+            }
+        }
+        f32x4 acc0[TW][kTokBlocks], acc1[TW][kTokBlocks];
+#pragma unroll
+        for (int t = 0; t < TW; t++)
 #pragma unroll
             for (int b = 0; b < kTokBlocks; b++) {
-                acc0[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                acc1[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                const int m = m_base + b * 16 + col;
-                arow[b] = nullptr;
-                if (m < cnt) {
-                    const int p = pos0 + m;
-                    const int row = DENSE ? p : (g.a_by_token ? g.perm[p] / g.k : p);
-                    arow[b] = g.a + (size_t)row * g.K;
-                }
+                acc0[t][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                acc1[t][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
             }
-            const int nblk = min(kTokBlocks, (cnt - m_base + 15) / 16);
-            for (int j = 0; j < cpr; j++) {
-                uint32_t e0 = 0, e1 = 0, e2 = 0, f0 = 0, f1 = 0, f2 = 0;
-                if constexpr (!DENSE) {
-                    load_quad(t0 + (size_t)j * kTileBytes, n & 63, g4, e0, e1, e2);
-                    if constexpr (GATEUP) load_quad(t1 + (size_t)j * kTileBytes, n & 63, g4, f0, f1, f2);
-                }
+        // operand staging for one chunk
+        struct Stage {
+            uint32_t c0[TW][3], c1[TW][3];          // RVQ codes (4 groups) per tile
+            bf16x8 w0[TW][4], w1[TW][4];            // dense weights per tile and K-step
+            bf16x8 a[4][kTokBlocks];                // A fragments per K-step and block
+        };
+        auto load_stage = [&](int j, Stage &st) {
 #pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    const int q = 4 * g4 + s;                   // group within the chunk
-                    const int kc = j * kChunkCols + q * 8;      // first K column of the group
-                    bf16x8 B0, B1;
-                    if constexpr (DENSE) {
-                        B0 = *(const bf16x8 *)(g.dense + (size_t)n * g.K + kc);
-                        if constexpr (GATEUP) B1 = *(const bf16x8 *)(g.dense2 + (size_t)n * g.K + kc);
+            for (int t = 0; t < TW; t++) {
+                if (t < ntw) {
+                    if constexpr (!DENSE) {
+                        load_quad(t0[t] + (size_t)j * kTileBytes, n[t] & 63, g4, st.c0[t][0], st.c0[t][1], st.c0[t][2]);
+                        if constexpr (GATEUP)
+                            load_quad(t1[t] + (size_t)j * kTileBytes, n[t] & 63, g4, st.c1[t][0], st.c1[t][1],
+                                      st.c1[t][2]);
                     } else {
-                        const uint32_t v0 = s == 0 ? quad_code<0>(e0, e1, e2) : s == 1 ? quad_code<1>(e0, e1, e2)
-                                          : s == 2 ? quad_code<2>(e0, e1, e2) : quad_code<3>(e0, e1, e2);
-                        B0 = decode_group(cb0, v0);
-                        if constexpr (GATEUP) {
-                            const uint32_t v1 = s == 0 ? quad_code<0>(f0, f1, f2) : s == 1 ? quad_code<1>(f0, f1, f2)
-                                              : s == 2 ? quad_code<2>(f0, f1, f2) : quad_code<3>(f0, f1, f2);
-                            B1 = decode_group(cb1, v1);
-                        }
-                    }
 #pragma unroll
-                    for (int b = 0; b < kTokBlocks; b++) {
-                        if (b < nblk) {
-                            bf16x8 A = (bf16x8){};
-                            if (arow[b]) A = *(const bf16x8 *)(arow[b] + kc);
-                            acc0[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc0[b], 0, 0, 0);
-                            if constexpr (GATEUP)
-                                acc1[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc1[b], 0, 0, 0);
+                        for (int s = 0; s < 4; s++) {
+                            const int kc = j * kChunkCols + (4 * g4 + s) * 8;
+                            st.w0[t][s] = *(const bf16x8 *)(g.dense + (size_t)n[t] * g.K + kc);
+                            if constexpr (GATEUP) st.w1[t][s] = *(const bf16x8 *)(g.dense2 + (size_t)n[t] * g.K + kc);
                         }
                     }
                 }
             }
-            // epilogue: lane holds D[4*g4 + i][col] of each block
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const int kc = j * kChunkCols + (4 * g4 + s) * 8;
+#pragma unroll
+                for (int b = 0; b < kTokBlocks; b++) {
+                    st.a[s][b] = (bf16x8){};
+                    if (b < nblk && arow[b]) st.a[s][b] = *(const bf16x8 *)(arow[b] + kc);
+                }
+            }
+        };
+        Stage cur, nxt;
+        load_stage(0, cur);
+        for (int j = 0; j < cpr; j++) {
+            if (j + 1 < cpr) load_stage(j + 1, nxt);
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+#pragma unroll
+                for (int t = 0; t < TW; t++) {
+                    if (t < ntw) {
+                        bf16x8 B0, B1;
+                        if constexpr (DENSE) {
+                            B0 = cur.w0[t][s];
+                            if constexpr (GATEUP) B1 = cur.w1[t][s];
+                        } else {
+                            const uint32_t *c0 = cur.c0[t], *c1 = cur.c1[t];
+                            const uint32_t v0 = s == 0 ? quad_code<0>(c0[0], c0[1], c0[2])
+                                              : s == 1 ? quad_code<1>(c0[0], c0[1], c0[2])
+                                              : s == 2 ? quad_code<2>(c0[0], c0[1], c0[2])
+                                                       : quad_code<3>(c0[0], c0[1], c0[2]);
+                            B0 = decode_group(cb0, v0);
+                            if constexpr (GATEUP) {
+                                const uint32_t v1 = s == 0 ? quad_code<0>(c1[0], c1[1], c1[2])
+                                                  : s == 1 ? quad_code<1>(c1[0], c1[1], c1[2])
+                                                  : s == 2 ? quad_code<2>(c1[0], c1[1], c1[2])
+                                                           : quad_code<3>(c1[0], c1[1], c1[2]);
+                                B1 = decode_group(cb1, v1);
+                            }
+                        }
+#pragma unroll
+                        for (int b = 0; b < kTokBlocks; b++) {
+                            if (b < nblk) {
+                                acc0[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B0, acc0[t][b], 0, 0, 0);
+                                if constexpr (GATEUP)
+                                    acc1[t][b] =
+                                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B1, acc1[t][b], 0, 0, 0);
+                            }
+                        }
+                    }
+                }
+            }
+            if (j + 1 < cpr) cur = nxt;
+        }
+        // epilogue: lane holds D[4*g4 + i][col] of each (tile, block)
+#pragma unroll
+        for (int t = 0; t < TW; t++) {
+            if (t >= ntw) continue;
             float s0v = 1.f, s1v = 1.f;
             if constexpr (!DENSE) {
-                s0v = (float)sc0[n];
-                if constexpr (GATEUP) s1v = (float)sc1[n];
+                s0v = (float)sc0[n[t]];
+                if constexpr (GATEUP) s1v = (float)sc1[n[t]];
             }
 #pragma unroll
             for (int b = 0; b < kTokBlocks; b++) {
@@ -271,11 +327,11 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped(GroupedArgs g) {
                     if (b < nblk && m < cnt) {
                         const size_t p = (size_t)(pos0 + m);
                         if constexpr (GATEUP) {
-                            const float gg = acc0[b][i] * s0v, uu = acc1[b][i] * s1v;
+                            const float gg = acc0[t][b][i] * s0v, uu = acc1[t][b][i] * s1v;
                             const __bf16 h = (__bf16)(gg / (1.f + __expf(-gg)) * uu);
-                            g.hout[p * g.N + n] = __builtin_bit_cast(uint16_t, h);
+                            g.hout[p * g.N + n[t]] = __builtin_bit_cast(uint16_t, h);
                         } else {
-                            g.yout[p * g.N + n] = acc0[b][i] * s0v;
+                            g.yout[p * g.N + n[t]] = acc0[t][b][i] * s0v;
                         }
                     }
                 }
@@ -341,15 +397,15 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
     g.mat = 0;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_grouped<true, false>,
+        hipError_t e = hipFuncSetAttribute((const void *)k_grouped<true, false, kTwGateUp>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kCbRows * 16);
         if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void *)k_grouped<false, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+            e = hipFuncSetAttribute((const void *)k_grouped<false, false, kTwDown>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     kCbRows * 16);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    k_grouped<true, false><<<E * g.splits, kGWaves * 64, 2 * kCbRows * 16, s>>>(g);
+    k_grouped<true, false, kTwGateUp><<<E * g.splits, kGWaves * 64, 2 * kCbRows * 16, s>>>(g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // down: N = H rows, K = I; A = h rows by position
@@ -361,7 +417,7 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
     g.K = I;
     g.splits = pick_splits(H);
     g.mat = 2;
-    k_grouped<false, false><<<E * g.splits, kGWaves * 64, kCbRows * 16, s>>>(g);
+    k_grouped<false, false, kTwDown><<<E * g.splits, kGWaves * 64, kCbRows * 16, s>>>(g);
     return hipGetLastError();
 }
 
@@ -379,7 +435,7 @@ hipError_t launch_grouped_dense(const uint16_t *shared, int H, int I, int T, con
     g.K = H;
     g.splits = 1;
     const int passes = (T + 16 * kTokBlocks - 1) / (16 * kTokBlocks);
-    k_grouped<true, true><<<std::max(1, (I / 16) * passes / kGWaves), kGWaves * 64, 0, s>>>(g);
+    k_grouped<true, true, 1><<<std::max(1, (I / 16) * passes / kGWaves), kGWaves * 64, 0, s>>>(g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     g.a = hs;
@@ -389,7 +445,7 @@ hipError_t launch_grouped_dense(const uint16_t *shared, int H, int I, int T, con
     g.yout = ysh;
     g.N = H;
     g.K = I;
-    k_grouped<false, true><<<std::max(1, (H / 16) * passes / kGWaves), kGWaves * 64, 0, s>>>(g);
+    k_grouped<false, true, 1><<<std::max(1, (H / 16) * passes / kGWaves), kGWaves * 64, 0, s>>>(g);
     return hipGetLastError();
 }
 

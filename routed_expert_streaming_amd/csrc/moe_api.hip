@@ -345,31 +345,34 @@ int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_
     }
     HIPCHK(hipStreamSynchronize(cs), "wait for routing");
 
-    // lookups in ascending expert id; misses start their copies at once
+    // cache bookkeeping in ascending expert id (get-or-insert, the LRU order
+    // the trace records); the copies of misses are enqueued after the hit
+    // experts have been launched, so those compute while the copies run (and
+    // while the host is held by copies from pageable memory)
     int order[MOE_MAX_K];
     for (int j = 0; j < k; j++) {
         order[j] = j;
         if (c->h_idx[j] < 0 || c->h_idx[j] >= E) return fail(MOE_E_HIP, "router produced expert id %d", c->h_idx[j]);
+        if (!experts_host[c->h_idx[j]]) return fail(MOE_E_INVAL, "experts_host[%d] is NULL", c->h_idx[j]);
     }
     std::sort(order, order + k, [&](int a, int b) { return c->h_idx[a] < c->h_idx[b]; });
     int32_t slot_of[MOE_MAX_K];
     bool hit[MOE_MAX_K];
     for (int n = 0; n < k; n++) {
         const int j = order[n];
-        const int e = c->h_idx[j];
-        const uint32_t key = layer_id * (uint32_t)E + (uint32_t)e;
+        const uint32_t key = layer_id * (uint32_t)E + (uint32_t)c->h_idx[j];
         int32_t s = c->core.lookup(key);
         hit[j] = s >= 0;
         if (s < 0) {
-            uint32_t ev;
-            if (!experts_host[e]) return fail(MOE_E_INVAL, "experts_host[%d] is NULL", e);
-            rc = expert_cache_insert(c, key, experts_host[e], ps, &s, &ev);
-            if (rc) return rc;
+            uint32_t victim = kNoKey;
+            s = c->core.plan_insert(key, &victim);
+            c->core.commit_insert(key, s, victim);
+            c->filled[s] = 0;                 // until its copy is enqueued below
         }
         slot_of[j] = s;
     }
 
-    // hit experts run at once; each miss expert after its copy lands
+    // hit experts run at once
     RecSrc hits{};
     hits.k = k;
     for (int n = 0; n < k; n++) {
@@ -385,15 +388,27 @@ int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_
         HIPCHK(launch_rvq_gateup(hits, off, H, I, hits.n_local, W.xh, W.hh, cs), "rvq gate/up (hits)");
         HIPCHK(launch_rvq_down(hits, off, H, I, hits.n_local, KS, W.hh, W.ypart, cs), "rvq down (hits)");
     }
+    // each miss: copy into its slot after the slot's previous readers, then
+    // its expert after the copy lands
     for (int n = 0; n < k; n++) {
         const int j = order[n];
         if (hit[j]) continue;
-        rc = cache_wait(c, slot_of[j], cs);
+        const int32_t s = slot_of[j];
+        if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "copy waits for slot readers");
+        hipError_t e = hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, experts_host[c->h_idx[j]], c->slot_bytes,
+                                      hipMemcpyHostToDevice, ps);
+        if (e == hipSuccess) e = hipEventRecord(c->ready[s], ps);
+        if (e != hipSuccess) {
+            c->core.drop_slot(s);             // the slot's contents are unknown now
+            return hip_fail(e, "expert copy");
+        }
+        c->filled[s] = 1;
+        rc = cache_wait(c, s, cs);
         if (rc) return rc;
         RecSrc one{};
         one.k = k;
         one.n_local = 1;
-        one.list[0] = c->pool + (size_t)slot_of[j] * c->slot_bytes;
+        one.list[0] = c->pool + (size_t)s * c->slot_bytes;
         one.rank[0] = (uint8_t)j;
         HIPCHK(launch_rvq_gateup(one, off, H, I, 1, W.xh, W.hh, cs), "rvq gate/up (miss)");
         HIPCHK(launch_rvq_down(one, off, H, I, 1, KS, W.hh, W.ypart, cs), "rvq down (miss)");

@@ -78,22 +78,36 @@ class DeviceWorkload:
 
 
 class HostRecordPool:
-    """Expert records of several layers in pinned host memory (the cold tier
-    of streamed decode), allocated in chunks of at most ``chunk_bytes``."""
+    """Expert records of several layers in host memory (the cold tier of
+    streamed decode): page-locked chunks of at most ``chunk_bytes`` up to
+    ``pin_limit`` bytes in total, the remainder (if any) in pageable memory.
+    ``pinned_records`` says how many records are page-locked."""
 
     def __init__(self, cfg: synth.MoEConfig, layers: Sequence[int], experts: Optional[int] = None,
-                 chunk_bytes: int = 8 << 30):
+                 chunk_bytes: int = 4 << 30, pin_limit: int = 52 << 30):
         self.cfg = cfg
         wl = synth.Workload(cfg)
         self.stride = wl.layout.padded
         E = cfg.E if experts is None else experts
         per_chunk = max(1, chunk_bytes // self.stride)
         keys = [(L, e) for L in layers for e in range(E)]
-        self.chunks: List[torch.Tensor] = []
+        self.chunks: List = []
         self.addr = {}
+        self.pinned_records = 0
+        pinned_bytes = 0
         for c0 in range(0, len(keys), per_chunk):
             ck = keys[c0:c0 + per_chunk]
-            t = torch.empty((len(ck), self.stride), dtype=torch.uint8, pin_memory=True)
+            nbytes = len(ck) * self.stride
+            t = None
+            if pinned_bytes + nbytes <= pin_limit:
+                try:
+                    t = torch.empty((len(ck), self.stride), dtype=torch.uint8, pin_memory=True)
+                    pinned_bytes += nbytes
+                    self.pinned_records += len(ck)
+                except Exception:             # page-locked memory exhausted
+                    t = None
+            if t is None:
+                t = torch.empty((len(ck), self.stride), dtype=torch.uint8)
             arr = t.numpy()
             wl.fill_records(ck, [arr[j] for j in range(len(ck))], _threads())
             base = t.data_ptr()
@@ -104,5 +118,5 @@ class HostRecordPool:
         self.E = E
 
     def table(self, L: int):
-        """ctypes array of the E pinned record addresses of layer L."""
+        """ctypes array of the E host record addresses of layer L."""
         return (ctypes.c_void_p * self.cfg.E)(*[self.addr.get((L, e), 0) for e in range(self.cfg.E)])
