@@ -187,7 +187,11 @@ size_t moe_decode_workspace_bytes(const moe_layer *layers, int32_t n_layers);
 /* Decode driver: T tokens one at a time, each through n_layers resident
  * layers in order (WISP "통찰": token -> router -> experts -> next layer).
  * Layer inputs are given per (token, layer); token t's layer L runs only
- * after its layer L-1 has finished.
+ * after its layer L-1 has finished.  All layers must share H, I, E and k.
+ * Runs as one cooperative persistent kernel (one workgroup per CU) for up to
+ * 40 layers; the combine order is fixed, so results are run-to-run
+ * identical (they may differ in the last bits from moe_layer_forward, whose
+ * partial sums are split differently).
  *   layers  [host] array of n_layers layers (all with the same H, I)
  *   x       [dev] [T, n_layers, H] fp32;  out [dev] [T, n_layers, H] fp32
  *   idx_out [dev] [T, n_layers, k] int32 or NULL (k of each layer must agree)
@@ -195,6 +199,13 @@ size_t moe_decode_workspace_bytes(const moe_layer *layers, int32_t n_layers);
 int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x,
                        int32_t T, float *out, int32_t *idx_out, void *ws,
                        size_t ws_bytes, void *hip_stream);
+
+/* Whether the last moe_decode_forward that used this workspace hit its
+ * device-side wait limit (a dependency between workgroups did not resolve
+ * within a few seconds; every wave then leaves the kernel and the outputs of
+ * that call are invalid).  Synchronises with the device (reads one word).
+ *   ws [dev] the workspace passed to moe_decode_forward;  timed_out: 0 or 1 */
+int moe_decode_status(const void *ws, int32_t *timed_out);
 
 /* Workspace bytes that moe_layer_forward_grouped needs for T tokens. */
 size_t moe_grouped_workspace_bytes(const moe_layer *L, int32_t T);

@@ -185,6 +185,14 @@ def decode_forward(layers: Sequence[Layer], x: torch.Tensor, stream=None, ws: Op
     return out, (idx if want_idx else None)
 
 
+def decode_status(ws: torch.Tensor) -> bool:
+    """True if the last decode_forward on this workspace hit its device-side
+    wait limit (its outputs are then invalid).  Synchronises."""
+    flag = ctypes.c_int32()
+    check(lib().moe_decode_status(_ptr(ws), ctypes.byref(flag)), "moe_decode_status")
+    return bool(flag.value)
+
+
 def grouped_workspace_bytes(layer: Layer, T: int) -> int:
     s = layer.struct()
     return lib().moe_grouped_workspace_bytes(ctypes.byref(s), T)

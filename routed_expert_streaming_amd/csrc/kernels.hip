@@ -17,87 +17,10 @@
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
+#include "rvq_device.h"
 
 namespace moe {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-    return __uint_as_float((uint32_t)b << 16);
-}
-
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-// Local item -> (global item, record).
-__device__ __forceinline__ const uint8_t *resolve_record(const RecSrc &s, int local, int &item) {
-    const int t = local / s.n_local, l = local % s.n_local;
-    if (s.table) {
-        item = t * s.k + l;
-        return (const uint8_t *)s.table[s.idx[item]];
-    }
-    item = t * s.k + s.rank[l];
-    return (const uint8_t *)s.list[l];
-}
-
-// Byte address in an LDS codebook of the stage-1 (a) and stage-2 (b) rows of
-// group g (0..15) of a 48-byte strip held in 12 dwords d[].
-template <int G>
-__device__ __forceinline__ void group_addr(const uint32_t (&d)[12], uint32_t &aa, uint32_t &ba) {
-    constexpr int bit = 24 * G, i = bit / 32, s = bit % 32;
-    uint32_t v;
-    if constexpr (s <= 8) v = d[i] >> s;
-    else v = __builtin_amdgcn_alignbit(d[i + 1], d[i], s);
-    aa = (v << 4) & 0xFFF0u;        // a * 16
-    ba = (v >> 8) & 0xFFF0u;        // b * 16
-}
-
-// acc[g%4] += sum over the 16 groups of (C[a] + C[b]) . x_group
-template <int G>
-__device__ __forceinline__ void strip_dot(const uint32_t (&d)[12], const char *cb, const uint32_t *xp,
-                                          float (&acc)[4]) {
-    if constexpr (G < 16) {
-        uint32_t aa, ba;
-        group_addr<G>(d, aa, ba);
-        const u32x4 ca = *(const u32x4 *)(cb + aa);
-        const u32x4 cbv = *(const u32x4 *)(cb + ba);
-        const uint32_t x0 = xp[4 * G + 0], x1 = xp[4 * G + 1], x2 = xp[4 * G + 2], x3 = xp[4 * G + 3];
-        float a = acc[G & 3];
-        a = dot2(ca.x, x0, a);
-        a = dot2(ca.y, x1, a);
-        a = dot2(ca.z, x2, a);
-        a = dot2(ca.w, x3, a);
-        a = dot2(cbv.x, x0, a);
-        a = dot2(cbv.y, x1, a);
-        a = dot2(cbv.z, x2, a);
-        a = dot2(cbv.w, x3, a);
-        acc[G & 3] = a;
-        strip_dot<G + 1>(d, cb, xp, acc);
-    }
-}
-
-__device__ __forceinline__ void load_strip(const u32x4 *tile, int lane, uint32_t (&d)[12]) {
-    const u32x4 w0 = __builtin_nontemporal_load(tile + lane);
-    const u32x4 w1 = __builtin_nontemporal_load(tile + 64 + lane);
-    const u32x4 w2 = __builtin_nontemporal_load(tile + 128 + lane);
-    d[0] = w0.x; d[1] = w0.y; d[2] = w0.z; d[3] = w0.w;
-    d[4] = w1.x; d[5] = w1.y; d[6] = w1.z; d[7] = w1.w;
-    d[8] = w2.x; d[9] = w2.y; d[10] = w2.z; d[11] = w2.w;
-}
 
 // ---------------------------------------------------------------- routing
 // z[t, e] = W[e] . x[t] + b[e].  One wave per expert row, 8 tokens per block.

@@ -1,0 +1,799 @@
+// Persistent decode kernel: a whole decode (T tokens x n_layers resident MoE
+// layers, token-major) in one cooperative launch, one workgroup per CU.
+//
+// Sources: WISP launch post, section "통찰" (token -> the model's router ->
+// the selected experts -> next layer); WASTE article, section "유휴 가중치는
+// 메모리가 아니라 제때 닿기만 하면 된다" (RVQ experts, 3.00 bits per weight,
+// never expanded).
+//
+// Per (token, layer) step:
+//   shared gate/up   rows split evenly over the workgroups (does not wait for
+//                    routing); fp32 h of the shared expert
+//   route            logit rows split over min(E, G) workgroups; then every
+//                    workgroup recomputes the top-k itself from the logits
+//   gate/up          the (rank, 64-row tile, 128-column chunk) space is split
+//                    into G equal contiguous ranges; partial sums per
+//                    (tile, contributor) are joined by the last contributor
+//                    (per-tile counter), which writes fp16 SiLU(g) * u
+//   shared down      rows split evenly; counted as contributions to the
+//                    output tiles they touch
+//   down             the (rank, 64-row tile of H, chunk) space likewise,
+//                    after the rank's h is complete; the last contributor of
+//                    an output tile combines sum_j w_j y_j + shared in fixed
+//                    (rank, contributor) order and counts the tile as done
+// The next step's routing starts when every output tile of this step is done.
+// Counters only grow within a launch (targets are multiples of the step
+// index), are zeroed before the launch, and every wait is bounded: on
+// timeout the kernel sets an error flag and all waves leave.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+#include "rvq_device.h"
+
+namespace moe {
+namespace {
+
+constexpr int kPW = 8;                 // waves per workgroup
+constexpr long kSpinLimit = 1L << 24;  // x ~0.1 us per poll: a few seconds
+constexpr int kDecLdsBytes = 160 * 1024;
+
+enum SyncIdx { kErr = 0, kRoute = 1, kLayerDone = 2, kHReady = 3 };   // h_ready[k+1] follows
+
+// Cross-workgroup data (logits, packed x, partial sums, h, shared-expert
+// vectors) is written and read with agent-scope relaxed atomic accesses,
+// which are coherent across the chip's XCDs without writing back or
+// invalidating whole L2 caches.  A producer waits until its stores have
+// completed (vmcnt 0), then bumps a counter; a consumer that has seen the
+// counter reach its target issues its loads afterwards.
+template <class T>
+__device__ __forceinline__ void st_x(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <class T>
+__device__ __forceinline__ T ld_x(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+__device__ __forceinline__ unsigned ld_cnt(const unsigned *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup-wide wait until *p >= target.  Returns false (error flag set)
+// on timeout or if another workgroup already failed.
+__device__ __forceinline__ bool wg_wait(unsigned *sync, const unsigned *p, unsigned target, int *bcast) {
+    if (threadIdx.x == 0) {
+        long spins = 0;
+        int ok = 1;
+        while (ld_cnt(p) < target) {
+            if (ld_cnt(sync + kErr)) { ok = 0; break; }
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > kSpinLimit) {
+                __hip_atomic_store(sync + kErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+        }
+        *bcast = ok;
+    }
+    __syncthreads();
+    const bool ok = *bcast != 0;
+    __syncthreads();
+    return ok;
+}
+
+// Workgroup-wide: wait for this workgroup's stores to complete, then add 1
+// to a counter.  Returns the counter's previous value (to every thread).
+__device__ __forceinline__ unsigned wg_signal(unsigned *p, int *bcast) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this thread's stores are done
+    __syncthreads();
+    if (threadIdx.x == 0) *bcast = (int)__hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const unsigned old = (unsigned)*bcast;
+    __syncthreads();
+    return old;
+}
+
+// A space of n units is split over Ga = min(G, n) active workgroups into
+// contiguous, non-empty ranges [start(w), start(w+1)); workgroups w >= Ga get
+// nothing.  Non-empty ranges keep the contributors of any unit interval
+// contiguous in w.
+__device__ __forceinline__ int active_of(long n, int G) { return (int)(n < G ? n : G); }
+__device__ __forceinline__ long range_start(long n, int G, int w) {
+    const int Ga = active_of(n, G);
+    return w >= Ga ? n : n * w / Ga;
+}
+// workgroup owning unit u
+__device__ __forceinline__ int range_owner(long n, int G, long u) {
+    const int Ga = active_of(n, G);
+    return (int)(((u + 1) * Ga + n - 1) / n - 1);
+}
+
+// dot of one 48-byte code strip with x pairs read from LDS at a wave-uniform
+// address (a broadcast read: all lanes get the same 16 bytes)
+template <int G>
+__device__ __forceinline__ void strip_dot_lx(const uint32_t (&d)[12], const char *cb, const uint32_t *xl,
+                                             float (&acc)[4]) {
+    if constexpr (G < 16) {
+        uint32_t aa, ba;
+        group_addr<G>(d, aa, ba);
+        const u32x4 ca = *(const u32x4 *)(cb + aa);
+        const u32x4 cbv = *(const u32x4 *)(cb + ba);
+        const u32x4 xq = *(const u32x4 *)(xl + 4 * G);
+        float a = acc[G & 3];
+        a = dot2(ca.x, xq.x, a);
+        a = dot2(ca.y, xq.y, a);
+        a = dot2(ca.z, xq.z, a);
+        a = dot2(ca.w, xq.w, a);
+        a = dot2(cbv.x, xq.x, a);
+        a = dot2(cbv.y, xq.y, a);
+        a = dot2(cbv.z, xq.z, a);
+        a = dot2(cbv.w, xq.w, a);
+        acc[G & 3] = a;
+        strip_dot_lx<G + 1>(d, cb, xl, acc);
+    }
+}
+
+// gate and up together, two groups per batch: the batch's 8 codebook
+// gathers and 2 broadcast reads of x pairs are issued before its 32 dot
+// products
+template <int B>
+__device__ __forceinline__ void strip_dot2_lx(const uint32_t (&dg)[12], const uint32_t (&du)[12], const char *cbg,
+                                              const char *cbu, const uint32_t *xl, float (&ag)[4], float (&au)[4]) {
+    if constexpr (B < 8) {
+        u32x4 g0[2], g1[2], u0[2], u1[2], xq[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            uint32_t ga, gb, ua, ub;
+            if (i == 0) { group_addr<2 * B>(dg, ga, gb); group_addr<2 * B>(du, ua, ub); }
+            else { group_addr<2 * B + 1>(dg, ga, gb); group_addr<2 * B + 1>(du, ua, ub); }
+            g0[i] = *(const u32x4 *)(cbg + ga);
+            g1[i] = *(const u32x4 *)(cbg + gb);
+            u0[i] = *(const u32x4 *)(cbu + ua);
+            u1[i] = *(const u32x4 *)(cbu + ub);
+            xq[i] = *(const u32x4 *)(xl + 4 * (2 * B + i));
+        }
+        // every read of the batch is issued before any of its values is used
+        asm volatile("" : "+v"(g0[0]), "+v"(g0[1]), "+v"(g1[0]), "+v"(g1[1]), "+v"(u0[0]), "+v"(u0[1]), "+v"(u1[0]),
+                     "+v"(u1[1]), "+v"(xq[0]), "+v"(xq[1]));
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            float a = ag[(2 * B + i) & 3], b = au[(2 * B + i) & 3];
+            a = dot2(g0[i].x, xq[i].x, a); b = dot2(u0[i].x, xq[i].x, b);
+            a = dot2(g0[i].y, xq[i].y, a); b = dot2(u0[i].y, xq[i].y, b);
+            a = dot2(g0[i].z, xq[i].z, a); b = dot2(u0[i].z, xq[i].z, b);
+            a = dot2(g0[i].w, xq[i].w, a); b = dot2(u0[i].w, xq[i].w, b);
+            a = dot2(g1[i].x, xq[i].x, a); b = dot2(u1[i].x, xq[i].x, b);
+            a = dot2(g1[i].y, xq[i].y, a); b = dot2(u1[i].y, xq[i].y, b);
+            a = dot2(g1[i].z, xq[i].z, a); b = dot2(u1[i].z, xq[i].z, b);
+            a = dot2(g1[i].w, xq[i].w, a); b = dot2(u1[i].w, xq[i].w, b);
+            ag[(2 * B + i) & 3] = a;
+            au[(2 * B + i) & 3] = b;
+        }
+        strip_dot2_lx<B + 1>(dg, du, cbg, cbu, xl, ag, au);
+    }
+}
+
+// one matrix, four groups per batch: 8 gathers + 4 broadcast reads in flight
+template <int B>
+__device__ __forceinline__ void strip_dot_lx4(const uint32_t (&d)[12], const char *cb, const uint32_t *xl,
+                                              float (&acc)[4]) {
+    if constexpr (B < 4) {
+        u32x4 c0[4], c1[4], xq[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint32_t aa, ba;
+            switch (i) {
+                case 0: group_addr<4 * B + 0>(d, aa, ba); break;
+                case 1: group_addr<4 * B + 1>(d, aa, ba); break;
+                case 2: group_addr<4 * B + 2>(d, aa, ba); break;
+                default: group_addr<4 * B + 3>(d, aa, ba); break;
+            }
+            c0[i] = *(const u32x4 *)(cb + aa);
+            c1[i] = *(const u32x4 *)(cb + ba);
+            xq[i] = *(const u32x4 *)(xl + 4 * (4 * B + i));
+        }
+        asm volatile("" : "+v"(c0[0]), "+v"(c0[1]), "+v"(c0[2]), "+v"(c0[3]), "+v"(c1[0]), "+v"(c1[1]), "+v"(c1[2]),
+                     "+v"(c1[3]), "+v"(xq[0]), "+v"(xq[1]), "+v"(xq[2]), "+v"(xq[3]));
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float a = acc[i];
+            a = dot2(c0[i].x, xq[i].x, a);
+            a = dot2(c0[i].y, xq[i].y, a);
+            a = dot2(c0[i].z, xq[i].z, a);
+            a = dot2(c0[i].w, xq[i].w, a);
+            a = dot2(c1[i].x, xq[i].x, a);
+            a = dot2(c1[i].y, xq[i].y, a);
+            a = dot2(c1[i].z, xq[i].z, a);
+            a = dot2(c1[i].w, xq[i].w, a);
+            acc[i] = a;
+        }
+        strip_dot_lx4<B + 1>(d, cb, xl, acc);
+    }
+}
+
+// The streaming GEMV loops live in functions of their own so that each gets
+// its own register allocation (inlined together with the rest they spill).
+// They address the kernel's dynamic LDS directly.
+extern __shared__ __align__(16) char dec_lds[];
+
+// LDS layout (bytes).  Gate/up: [gate cb 64K][up cb 64K][x pairs][sums];
+// down: [down cb 64K][h pairs][sums]; a small tail holds routing results.
+struct DecLds {
+    int x_gu, red_gu, x_d, red_d;
+};
+__device__ __forceinline__ DecLds dec_lds_layout(int H, int I) {
+    DecLds L;
+    L.x_gu = 2 * kCbRows * 16;
+    L.red_gu = L.x_gu + ((H * 2 + 255) & ~255);
+    L.x_d = kCbRows * 16;
+    L.red_d = L.x_d + ((I * 2 + 255) & ~255);
+    return L;
+}
+constexpr int kDecTail = kDecLdsBytes - 1024;     // sidx, sw, broadcast words, router partials
+
+constexpr int kRingGU = 3;      // code buffers per wave (2 units in flight ahead)
+constexpr int kRingD = 4;       // (3 ahead)
+
+__device__ __forceinline__ void load_codes(gu32x4 *base, long u, int lane, uint32_t (&d)[12]) {
+    load_strip((const u32x4 *)(base + u * kTileVec), lane, d);
+}
+
+// Gate and up of one expert: units [la, lb) (unit u = tile u / cpr, chunk
+// u % cpr; its codes are 3072 bytes at base + u * 3072).  Wave v takes units
+// la + v, la + v + kPW, ...; tile sums go to LDS slot (tile - t0).  The first
+// loads are issued before the codebooks (and, if stage_x, the x pairs) are
+// staged into LDS.
+__device__ __noinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *usec, const u32x4 *cbg_src,
+                                           const u32x4 *cbu_src, const uint32_t *xh_src, int stage_x, int H, int I,
+                                           int cpr, long la, long lb, long t0, int nslots, int wave, int lane) {
+    const DecLds L = dec_lds_layout(H, I);
+    char *cbg = dec_lds, *cbu = dec_lds + kCbRows * 16;
+    uint32_t *xl = (uint32_t *)(dec_lds + L.x_gu);
+    float *red = (float *)(dec_lds + L.red_gu);
+    gu32x4 *gb = (gu32x4 *)gsec, *ub = (gu32x4 *)usec;
+    const long first = la + wave;
+    const int n = first < lb ? (int)((lb - first + kPW - 1) / kPW) : 0;
+    uint32_t bg[kRingGU][12], bu[kRingGU][12];
+#pragma unroll
+    for (int r = 0; r < kRingGU - 1; r++)
+        if (r < n) {
+            load_codes(gb, first + (long)r * kPW, lane, bg[r]);
+            load_codes(ub, first + (long)r * kPW, lane, bu[r]);
+        }
+    // stage codebooks (+ x), clear this segment's sum slots
+    for (int i = threadIdx.x; i < kCbRows; i += kPW * 64) {
+        ((u32x4 *)cbg)[i] = cbg_src[i];
+        ((u32x4 *)cbu)[i] = cbu_src[i];
+    }
+    if (stage_x)
+        for (int i = threadIdx.x; i < H / 2; i += kPW * 64) xl[i] = ld_x(xh_src + i);
+    for (int i = threadIdx.x; i < nslots * kPW * 128; i += kPW * 64) red[i] = 0.f;
+    __syncthreads();
+    float ag[4] = {0.f, 0.f, 0.f, 0.f}, au[4] = {0.f, 0.f, 0.f, 0.f};
+    long cur_t = n ? first / cpr : -1;
+    for (int i0 = 0; i0 < n; i0 += kRingGU) {
+#pragma unroll
+        for (int r = 0; r < kRingGU; r++) {
+            const int i = i0 + r;
+            if (i < n) {
+                const int nxt = i + kRingGU - 1;
+                if (nxt < n) {
+                    load_codes(gb, first + (long)nxt * kPW, lane, bg[(r + kRingGU - 1) % kRingGU]);
+                    load_codes(ub, first + (long)nxt * kPW, lane, bu[(r + kRingGU - 1) % kRingGU]);
+                }
+                const long u = first + (long)i * kPW;
+                const long t = u / cpr;
+                if (t != cur_t) {
+                    float *p = red + ((int)(cur_t - t0) * kPW + wave) * 128;
+                    p[lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
+                    p[64 + lane] = (au[0] + au[1]) + (au[2] + au[3]);
+                    ag[0] = ag[1] = ag[2] = ag[3] = 0.f;
+                    au[0] = au[1] = au[2] = au[3] = 0.f;
+                    cur_t = t;
+                }
+                strip_dot2_lx<0>(bg[r], bu[r], cbg, cbu, xl + (int)(u % cpr) * 64, ag, au);
+            }
+        }
+    }
+    if (n) {
+        float *p = red + ((int)(cur_t - t0) * kPW + wave) * 128;
+        p[lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
+        p[64 + lane] = (au[0] + au[1]) + (au[2] + au[3]);
+    }
+}
+
+// Down of one expert: units [la, lb) over tiles of H, like stream_gateup.
+// The first loads are issued before waiting for the expert's h (counter
+// h_ready >= h_target) and staging it with the codebook.  Returns 0 if the
+// wait failed.
+__device__ __noinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_src, const uint32_t *h_src, unsigned *sync,
+                                        const unsigned *h_ready, unsigned h_target, int *bcast, int H, int I, int cpr,
+                                        long la, long lb, long t0, int nslots, int wave, int lane) {
+    const DecLds L = dec_lds_layout(H, I);
+    char *cb = dec_lds;
+    uint32_t *xl = (uint32_t *)(dec_lds + L.x_d);
+    float *red = (float *)(dec_lds + L.red_d);
+    gu32x4 *db = (gu32x4 *)dsec;
+    const long first = la + wave;
+    const int n = first < lb ? (int)((lb - first + kPW - 1) / kPW) : 0;
+    uint32_t bd[kRingD][12];
+#pragma unroll
+    for (int r = 0; r < kRingD - 1; r++)
+        if (r < n) load_codes(db, first + (long)r * kPW, lane, bd[r]);
+    if (!wg_wait(sync, h_ready, h_target, bcast)) return 0;
+    for (int i = threadIdx.x; i < kCbRows; i += kPW * 64) ((u32x4 *)cb)[i] = cbd_src[i];
+    for (int i = threadIdx.x; i < I / 2; i += kPW * 64) xl[i] = ld_x(h_src + i);
+    for (int i = threadIdx.x; i < nslots * kPW * 64; i += kPW * 64) red[i] = 0.f;
+    __syncthreads();
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    long cur_t = n ? first / cpr : -1;
+    for (int i0 = 0; i0 < n; i0 += kRingD) {
+#pragma unroll
+        for (int r = 0; r < kRingD; r++) {
+            const int i = i0 + r;
+            if (i < n) {
+                const int nxt = i + kRingD - 1;
+                if (nxt < n) load_codes(db, first + (long)nxt * kPW, lane, bd[(r + kRingD - 1) % kRingD]);
+                const long u = first + (long)i * kPW;
+                const long t = u / cpr;
+                if (t != cur_t) {
+                    red[((int)(cur_t - t0) * kPW + wave) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                    acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+                    cur_t = t;
+                }
+                strip_dot_lx4<0>(bd[r], cb, xl + (int)(u % cpr) * 64, acc);
+            }
+        }
+    }
+    if (n) red[((int)(cur_t - t0) * kPW + wave) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    return 1;
+}
+
+// number of contributions an output tile of H receives per step
+__device__ __forceinline__ unsigned tile_target(int td, int k, int tilesH, int cprI, long nD, int G, int H, bool shared_on) {
+    unsigned n = 0;
+    for (int j = 0; j < k; j++) {
+        const long tau = (long)j * tilesH + td;
+        n += range_owner(nD, G, (tau + 1) * cprI - 1) - range_owner(nD, G, tau * cprI) + 1;
+    }
+    if (shared_on)
+        n += range_owner(H, G, (long)td * kTileRows + kTileRows - 1) - range_owner(H, G, (long)td * kTileRows) + 1;
+    return n;
+}
+
+// last contributor of output tile td: fixed-order combine
+// out = sum_j w_j * sum_slots y_j + shared
+__device__ __forceinline__ void combine_tile(int td, int s, int k, int tilesH, int cprI, long nD, int G, int H, bool shared_on,
+                             const float *part_d, int slots_d, const float *ysh, float *out, const float *sw,
+                             unsigned *sync, int wave, int lane, int *bcast) {
+    if (wave == 0) {
+        const int r = td * kTileRows + lane;
+        float o = 0.f;
+        for (int j = 0; j < k; j++) {
+            const long tau = (long)j * tilesH + td;
+            const int first = range_owner(nD, G, tau * cprI);
+            const int last = range_owner(nD, G, (tau + 1) * cprI - 1);
+            float y = 0.f;
+            for (int sl = 0; sl <= last - first; sl++)
+                y += ld_x(part_d + ((size_t)tau * slots_d + sl) * 64 + lane);
+            o = fmaf(sw[j], y, o);
+        }
+        if (shared_on) o += ld_x(ysh + r);
+        out[(size_t)s * H + r] = o;
+    }
+    wg_signal(sync + kLayerDone, bcast);
+}
+
+struct DecArgs {
+    const DecLayer *layers;  // [nL] in device memory
+    int nL, T, H, I, k, E_max, G;
+    int has_shared;
+    const float *x;          // [T, nL, H]
+    float *out;              // [T, nL, H]
+    int32_t *idx_out;        // [T, nL, k] or null
+    RecOffsets off;
+    unsigned *sync;          // counters
+    float *z;                // [E_max]
+    uint32_t *xh;            // [H/2]
+    uint16_t *hh;            // [k][I] fp16 h per rank
+    float *hs;               // [I] shared h
+    float *ysh;              // [H] shared y
+    float *part_gu;          // [k*tilesI][slots_gu][128]
+    float *part_d;           // [k*tilesH][slots_d][64]
+    int slots_gu, slots_d;
+    int slots_red_gu, slots_red_d;   // tiles one workgroup's range can touch (LDS sum slots)
+    unsigned long long *stamps;   // optional phase timestamps [steps][G][6], or null
+    int stamp_steps;
+};
+
+__global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_decode_persistent(DecArgs a) {
+    char *lds = dec_lds;
+    const DecLds LL = dec_lds_layout(a.H, a.I);
+    const float *red_gu = (const float *)(lds + LL.red_gu);     // [slot][kPW][2][64]
+    const float *red_d = (const float *)(lds + LL.red_d);       // [slot][kPW][64]
+    int *sidx = (int *)(lds + kDecTail);                        // [MOE_MAX_K]
+    float *sw = (float *)(sidx + MOE_MAX_K);                    // [MOE_MAX_K]
+    int *bcast = (int *)(sw + MOE_MAX_K);                       // [4]
+    float *red = (float *)(bcast + 4);                          // [kPW] router partials
+
+    const int G = a.G, w = blockIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int H = a.H, I = a.I, k = a.k;
+    const int tilesI = I / kTileRows, tilesH = H / kTileRows;
+    const int cprH = H / kChunkCols, cprI = I / kChunkCols;
+    const long nGU = (long)k * tilesI * cprH, nD = (long)k * tilesH * cprI;
+    const long gu0 = range_start(nGU, G, w), gu1 = range_start(nGU, G, w + 1);
+    const long d0 = range_start(nD, G, w), d1 = range_start(nD, G, w + 1);
+    unsigned *sync = a.sync;
+    unsigned *h_ready = sync + kHReady;                          // [k+1]
+    unsigned *cnt_gu = h_ready + (k + 1);                        // [k*tilesI]
+    unsigned *cnt_d = cnt_gu + k * tilesI;                       // [tilesH]
+    const int steps = a.T * a.nL;
+    // shared-expert row ranges
+    const int shI0 = (int)range_start(I, G, w), shI1 = (int)range_start(I, G, w + 1);
+    const int shH0 = (int)range_start(H, G, w), shH1 = (int)range_start(H, G, w + 1);
+    const unsigned sh_gu_contrib = (unsigned)min(G, I);          // workgroups with shared gate/up rows
+
+    unsigned long long *stamp = nullptr;
+    auto mark = [&](int i) {
+        if (stamp && threadIdx.x == 0) stamp[i] = wall_clock64();
+    };
+    for (int s = 0; s < steps; s++) {
+        stamp = (a.stamps && s < a.stamp_steps) ? a.stamps + ((size_t)s * G + w) * 6 : nullptr;
+        mark(0);
+        const int t = s / a.nL, L = s % a.nL;
+        const DecLayer lay = a.layers[L];   // device memory, uniform
+        const float *xs = a.x + ((size_t)t * a.nL + L) * H;
+        const int E = lay.E, nE = min(E, G);
+        const bool shared_on = a.has_shared && lay.shared;
+        if (s > 0 && !wg_wait(sync, sync + kLayerDone, (unsigned)s * tilesH, bcast)) return;
+        mark(1);
+
+        // ---- shared gate/up (independent of routing)
+        if (shared_on) {
+            for (int r = shI0 + wave; r < shI1; r += kPW) {
+                const uint16_t *wg = lay.shared + (size_t)r * H, *wu = lay.shared + (size_t)I * H + (size_t)r * H;
+                float g = 0.f, u = 0.f;
+                for (int c = lane * 8; c < H; c += 512) {
+                    const uint4 gv = *(const uint4 *)(wg + c), uv = *(const uint4 *)(wu + c);
+                    const float4 xa = *(const float4 *)(xs + c), xb = *(const float4 *)(xs + c + 4);
+                    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+                    const uint32_t gq[4] = {gv.x, gv.y, gv.z, gv.w}, uq[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        g = fmaf(__uint_as_float(gq[i] << 16), xv[2 * i], g);
+                        g = fmaf(__uint_as_float(gq[i] & 0xFFFF0000u), xv[2 * i + 1], g);
+                        u = fmaf(__uint_as_float(uq[i] << 16), xv[2 * i], u);
+                        u = fmaf(__uint_as_float(uq[i] & 0xFFFF0000u), xv[2 * i + 1], u);
+                    }
+                }
+                g = wave_sum(g);
+                u = wave_sum(u);
+                if (lane == 0) st_x(a.hs + r, g / (1.f + __expf(-g)) * u);
+            }
+            if (shI1 > shI0) wg_signal(h_ready + k, bcast);
+        }
+
+        // ---- route: logits of rows e = w, w + G, ... ; workgroup 0 also packs x
+        if (w < nE) {
+            for (int e = w; e < E; e += G) {
+                const float *wr = lay.W + (size_t)e * H;
+                float acc = 0.f;
+                for (int c = threadIdx.x * 4; c < H; c += kPW * 64 * 4) {
+                    const float4 wv = *(const float4 *)(wr + c), xv = *(const float4 *)(xs + c);
+                    acc = fmaf(wv.x, xv.x, acc);
+                    acc = fmaf(wv.y, xv.y, acc);
+                    acc = fmaf(wv.z, xv.z, acc);
+                    acc = fmaf(wv.w, xv.w, acc);
+                }
+                acc = wave_sum(acc);
+                __syncthreads();
+                if (lane == 0) red[wave] = acc;
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    float z = 0.f;
+                    for (int v = 0; v < kPW; v++) z += red[v];
+                    st_x(a.z + e, z + (lay.bias ? lay.bias[e] : 0.f));
+                }
+            }
+            if (w == 0)
+                for (int i = threadIdx.x; i < H / 2; i += kPW * 64) st_x(a.xh + i, pack_f16x2(xs[2 * i], xs[2 * i + 1]));
+            wg_signal(sync + kRoute, bcast);
+        }
+        if (!wg_wait(sync, sync + kRoute, (unsigned)(s + 1) * nE, bcast)) return;
+        mark(2);
+
+        // ---- top-k (every workgroup, wave 0): k rounds of a wave argmax over
+        // (logit desc, expert id asc)
+        if (wave == 0) {
+            float v[MOE_MAX_E / 64];
+#pragma unroll
+            for (int i = 0; i < MOE_MAX_E / 64; i++) {
+                const int e = lane + 64 * i;
+                const float zz = e < E ? ld_x(a.z + e) : -INFINITY;
+                v[i] = zz == zz ? zz : -INFINITY;
+            }
+            uint32_t taken = 0;
+            float zmax = 0.f, sum = 0.f, mine = 0.f;
+            int emine = 0;
+            for (int j = 0; j < lay.k; j++) {
+                float bv = -INFINITY;
+                int be = 0x7FFFFFFF;
+#pragma unroll
+                for (int i = 0; i < MOE_MAX_E / 64; i++) {
+                    const int e = lane + 64 * i;
+                    if (e < E && !(taken >> i & 1u) && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    const float ov = __shfl_xor(bv, o, 64);
+                    const int oe = __shfl_xor(be, o, 64);
+                    if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+                }
+                if (j == 0) zmax = bv;
+                const float sc = lay.score_fn == MOE_SCORE_SOFTMAX ? __expf(bv - zmax) : 1.f / (1.f + __expf(-bv));
+                sum += sc;
+                if (lane == j) { mine = sc; emine = be; }
+                if ((be & 63) == lane) taken |= 1u << (be >> 6);
+            }
+            if (lane < lay.k) {
+                sidx[lane] = emine;
+                sw[lane] = mine / sum;
+                if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = emine;
+            }
+        }
+        __syncthreads();
+
+        // ---- gate/up over this workgroup's range of (rank, tile, chunk), one
+        // expert segment at a time (a range spans at most two experts)
+        {
+            bool x_staged = false;
+            const long t_first = gu0 / cprH;
+            for (long ea = gu0; ea < gu1;) {
+                const int j = (int)(ea / ((long)tilesI * cprH));
+                const long eb = min(gu1, (long)(j + 1) * tilesI * cprH);
+                const uint8_t *rec = (const uint8_t *)lay.records[sidx[j]];
+                const long base = (long)j * tilesI * cprH;       // expert-local units
+                stream_gateup((const u32x4 *)(rec + a.off.codes[0]), (const u32x4 *)(rec + a.off.codes[1]),
+                              (const u32x4 *)(rec + a.off.cb[0]), (const u32x4 *)(rec + a.off.cb[1]), a.xh,
+                              x_staged ? 0 : 1, H, I, cprH, ea - base, eb - base, ea / cprH - base / cprH,
+                              a.slots_red_gu, wave, lane);
+                x_staged = true;
+                __syncthreads();
+                // one partial per touched tile, then the join by its last contributor
+                for (long tau = ea / cprH; tau <= (eb - 1) / cprH; tau++) {
+                    const int tile = (int)(tau % tilesI);
+                    const int first = range_owner(nGU, G, tau * cprH);
+                    const int last = range_owner(nGU, G, (tau + 1) * cprH - 1);
+                    const int slot = w - first, ncontrib = last - first + 1;
+                    const int rs = (int)(tau - ea / cprH);
+                    if (wave == 0) {
+                        float g = 0.f, uu = 0.f;
+#pragma unroll
+                        for (int v = 0; v < kPW; v++) {
+                            g += red_gu[((rs * kPW) + v) * 128 + lane];
+                            uu += red_gu[((rs * kPW) + v) * 128 + 64 + lane];
+                        }
+                        float *p = a.part_gu + ((size_t)tau * a.slots_gu + slot) * 128;
+                        st_x(p + lane, g);
+                        st_x(p + 64 + lane, uu);
+                    }
+                    const unsigned old = wg_signal(cnt_gu + tau, bcast);
+                    if ((old + 1) % (unsigned)ncontrib == 0) {
+                        if (wave == 0) {
+                            float g = 0.f, uu = 0.f;
+                            for (int sl = 0; sl < ncontrib; sl++) {
+                                const float *p = a.part_gu + ((size_t)tau * a.slots_gu + sl) * 128;
+                                g += ld_x(p + lane);
+                                uu += ld_x(p + 64 + lane);
+                            }
+                            const int r = tile * kTileRows + lane;
+                            g *= (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
+                            uu *= (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
+                            const _Float16 hf = (_Float16)(g / (1.f + __expf(-g)) * uu);
+                            st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
+                        }
+                        wg_signal(h_ready + j, bcast);
+                    }
+                }
+                ea = eb;
+            }
+            (void)t_first;
+        }
+
+        mark(3);
+        // ---- shared down rows (after the whole shared h is ready)
+        if (shared_on && shH1 > shH0) {
+            if (!wg_wait(sync, h_ready + k, (unsigned)(s + 1) * sh_gu_contrib, bcast)) return;
+            for (int r = shH0 + wave; r < shH1; r += kPW) {
+                const uint16_t *wd = lay.shared + 2 * (size_t)I * H + (size_t)r * I;
+                float acc = 0.f;
+                for (int c = lane * 8; c < I; c += 512) {
+                    const uint4 dv = *(const uint4 *)(wd + c);
+                    float hv[8];
+#pragma unroll
+                    for (int i = 0; i < 8; i++) hv[i] = ld_x(a.hs + c + i);
+                    const uint32_t q[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        acc = fmaf(__uint_as_float(q[i] << 16), hv[2 * i], acc);
+                        acc = fmaf(__uint_as_float(q[i] & 0xFFFF0000u), hv[2 * i + 1], acc);
+                    }
+                }
+                acc = wave_sum(acc);
+                if (lane == 0) st_x(a.ysh + r, acc);
+            }
+            for (int td = shH0 / kTileRows; td <= (shH1 - 1) / kTileRows; td++) {
+                const unsigned old = wg_signal(cnt_d + td, bcast);
+                if ((old + 1) % tile_target(td, k, tilesH, cprI, nD, G, H, shared_on) == 0)
+                    combine_tile(td, s, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d, a.ysh, a.out, sw, sync, wave, lane, bcast);
+            }
+        }
+
+        mark(4);
+        // ---- down over this workgroup's range of (rank, tile of H, chunk),
+        // one expert segment at a time
+        for (long ea = d0; ea < d1;) {
+            const int j = (int)(ea / ((long)tilesH * cprI));
+            const long eb = min(d1, (long)(j + 1) * tilesH * cprI);
+            const uint8_t *rec = (const uint8_t *)lay.records[sidx[j]];
+            const long base = (long)j * tilesH * cprI;
+            if (!stream_down((const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]),
+                             (const uint32_t *)(a.hh + (size_t)j * I), sync, h_ready + j, (unsigned)(s + 1) * tilesI,
+                             bcast, H, I, cprI, ea - base, eb - base, ea / cprI - base / cprI, a.slots_red_d, wave,
+                             lane))
+                return;
+            __syncthreads();
+            for (long tau = ea / cprI; tau <= (eb - 1) / cprI; tau++) {
+                const int td = (int)(tau % tilesH);
+                const int first = range_owner(nD, G, tau * cprI);
+                const int rs = (int)(tau - ea / cprI);
+                if (wave == 0) {
+                    float y = 0.f;
+#pragma unroll
+                    for (int v = 0; v < kPW; v++) y += red_d[(rs * kPW + v) * 64 + lane];
+                    const int r = td * kTileRows + lane;
+                    y *= (float)((const _Float16 *)(rec + a.off.scales[2]))[r];
+                    st_x(a.part_d + ((size_t)tau * a.slots_d + (w - first)) * 64 + lane, y);
+                }
+                const unsigned old = wg_signal(cnt_d + td, bcast);
+                if ((old + 1) % tile_target(td, k, tilesH, cprI, nD, G, H, shared_on) == 0)
+                    combine_tile(td, s, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d, a.ysh, a.out, sw,
+                                 sync, wave, lane, bcast);
+            }
+            ea = eb;
+        }
+        mark(5);
+    }
+}
+
+struct LayerPack {
+    DecLayer layers[kDecMaxLayers];
+    int n;
+};
+
+// copies the layer descriptors into device memory (indices are compile-time
+// after unrolling, so the argument block is never indexed at run time)
+__global__ void k_store_layers(LayerPack pack, DecLayer *dst) {
+    if (threadIdx.x != 0) return;
+#pragma unroll
+    for (int l = 0; l < kDecMaxLayers; l++)
+        if (l < pack.n) dst[l] = pack.layers[l];
+}
+
+__global__ void k_fill_u32(unsigned *p, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+size_t decode_lds() { return kDecLdsBytes; }
+
+}  // namespace
+
+// ---------------------------------------------------------------- host side
+struct DecodePlan {
+    int G;
+    int slots_gu, slots_d;
+    size_t sync_words;
+};
+
+static long h_range_start(long n, int G, int w) {
+    const int Ga = (int)std::min<long>(n, G);
+    return w >= Ga ? n : n * w / Ga;
+}
+static int h_range_owner(long n, int G, long u) {
+    const int Ga = (int)std::min<long>(n, G);
+    return (int)(((u + 1) * Ga + n - 1) / n - 1);
+}
+
+static int max_contributors(long n_tiles, int cpr, int G) {
+    const long n = n_tiles * cpr;
+    int m = 1;
+    for (long tau = 0; tau < n_tiles; tau++)
+        m = std::max(m, h_range_owner(n, G, (tau + 1) * cpr - 1) - h_range_owner(n, G, tau * cpr) + 1);
+    return m;
+}
+
+// most tiles (of cpr units each) that one workgroup's range of an n-unit space touches
+static int max_tiles_per_range(long n_tiles, int cpr, int G) {
+    const long n = n_tiles * cpr;
+    int m = 1;
+    for (int w = 0; w < G; w++) {
+        const long a = h_range_start(n, G, w), b = h_range_start(n, G, w + 1);
+        if (b > a) m = std::max(m, (int)((b - 1) / cpr - a / cpr + 1));
+    }
+    return m;
+}
+
+hipError_t decode_plan(int H, int I, int k, DecodePlanOut *o) {
+    static int G = 0;
+    if (G == 0) {
+        int dev = 0, cus = 0, per = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)k_decode_persistent, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)decode_lds());
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void *)k_decode_persistent, kPW * 64,
+                                                             decode_lds());
+        if (e != hipSuccess) return e;
+        if (per < 1) return hipErrorInvalidConfiguration;
+        G = cus * per;
+    }
+    const int tilesI = I / kTileRows, tilesH = H / kTileRows, cprH = H / kChunkCols, cprI = I / kChunkCols;
+    o->G = G;
+    o->slots_gu = max_contributors((long)k * tilesI, cprH, G);
+    o->slots_d = max_contributors((long)k * tilesH, cprI, G);
+    o->slots_red_gu = max_tiles_per_range((long)k * tilesI, cprH, G);
+    o->slots_red_d = max_tiles_per_range((long)k * tilesH, cprI, G);
+    o->sync_words = 3 + (size_t)(k + 1) + (size_t)k * tilesI + tilesH;
+    // LDS: both phases' layouts must fit below the routing tail
+    const long red_gu = 2L * kCbRows * 16 + ((H * 2 + 255) & ~255) + (long)o->slots_red_gu * kPW * 128 * 4;
+    const long red_d = (long)kCbRows * 16 + ((I * 2 + 255) & ~255) + (long)o->slots_red_d * kPW * 64 * 4;
+    o->lds_ok = red_gu <= kDecTail && red_d <= kDecTail;
+    return hipSuccess;
+}
+
+hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s) {
+    const int tilesI = d.I / kTileRows, tilesH = d.H / kTileRows;
+    k_fill_u32<<<1, 256, 0, s>>>(d.sync, d.sync_words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    DecArgs a{};
+    LayerPack pack;
+    for (int l = 0; l < kDecMaxLayers; l++) pack.layers[l] = l < d.nL ? d.layers[l] : DecLayer{};
+    pack.n = d.nL;
+    k_store_layers<<<1, 64, 0, s>>>(pack, d.layer_buf);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.layers = d.layer_buf;
+    a.nL = d.nL;
+    a.T = d.T;
+    a.H = d.H;
+    a.I = d.I;
+    a.k = d.k;
+    a.E_max = d.E_max;
+    a.G = d.G;
+    a.has_shared = d.has_shared;
+    a.x = d.x;
+    a.out = d.out;
+    a.idx_out = d.idx_out;
+    a.off = d.off;
+    a.sync = d.sync;
+    a.z = d.z;
+    a.xh = d.xh;
+    a.hh = d.hh;
+    a.hs = d.hs;
+    a.ysh = d.ysh;
+    a.part_gu = d.part_gu;
+    a.part_d = d.part_d;
+    a.slots_gu = d.slots_gu;
+    a.slots_d = d.slots_d;
+    a.slots_red_gu = d.slots_red_gu;
+    a.slots_red_d = d.slots_red_d;
+    a.stamps = d.stamps;
+    a.stamp_steps = d.stamp_steps;
+    (void)tilesI;
+    (void)tilesH;
+    void *args[] = {&a};
+    return hipLaunchCooperativeKernel((const void *)k_decode_persistent, dim3(d.G), dim3(kPW * 64), args,
+                                      (unsigned)decode_lds(), s);
+}
+
+}  // namespace moe

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -268,11 +269,69 @@ int moe_layer_forward(const moe_layer *L, const void *x, int32_t x_dtype, int32_
     return run_experts(L, W, src, x, x_dtype, T, k, w, out, s);
 }
 
+namespace {
+struct DecodeWs {
+    unsigned *sync;
+    DecLayer *layers;
+    float *z;
+    uint32_t *xh;
+    uint16_t *hh;
+    float *hs, *ysh, *part_gu, *part_d;
+    unsigned long long *stamps;
+    int stamp_steps;
+    int G, slots_gu, slots_d, slots_red_gu, slots_red_d;
+    size_t sync_words, bytes;
+};
+
+// Profiling aid: MOE_DECODE_STAMPS=<n> makes the decode workspace end with
+// n steps x G workgroups x 6 wall-clock stamps (step start, previous layer
+// done, routing done, gate/up done, shared down done, down done).
+int decode_stamp_steps() {
+    const char *e = getenv("MOE_DECODE_STAMPS");
+    return e ? std::max(0, atoi(e)) : 0;
+}
+
+int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *D) {
+    const int H = layers[0].H, I = layers[0].I, k = layers[0].router.k;
+    int E_max = 1;
+    bool shared = false;
+    for (int l = 0; l < n_layers; l++) {
+        E_max = std::max(E_max, layers[l].router.E);
+        shared = shared || layers[l].shared;
+    }
+    DecodePlanOut P;
+    hipError_t e = decode_plan(H, I, k, &P);
+    if (e != hipSuccess) return hip_fail(e, "decode plan");
+    if (!P.lds_ok) return fail(MOE_E_INVAL, "decode kernel: H=%d, I=%d do not fit its LDS layout", H, I);
+    D->G = P.G;
+    D->slots_gu = P.slots_gu;
+    D->slots_d = P.slots_d;
+    D->slots_red_gu = P.slots_red_gu;
+    D->slots_red_d = P.slots_red_d;
+    D->sync_words = P.sync_words;
+    Carver c(ws);
+    D->sync = c.take<unsigned>(D->sync_words);
+    D->layers = c.take<DecLayer>(kDecMaxLayers);
+    D->z = c.take<float>((size_t)E_max);
+    D->xh = c.take<uint32_t>((size_t)H / 2);
+    D->hh = c.take<uint16_t>((size_t)k * I);
+    D->hs = c.take<float>((size_t)I);
+    D->ysh = c.take<float>((size_t)H);
+    D->part_gu = c.take<float>((size_t)k * (I / 64) * D->slots_gu * 128);
+    D->part_d = c.take<float>((size_t)k * (H / 64) * D->slots_d * 64);
+    D->stamp_steps = decode_stamp_steps();
+    D->stamps = D->stamp_steps ? c.take<unsigned long long>((size_t)D->stamp_steps * D->G * 6) : nullptr;
+    D->bytes = (size_t)align_up((int64_t)c.pos, 256);
+    (void)shared;
+    return MOE_OK;
+}
+}  // namespace
+
 size_t moe_decode_workspace_bytes(const moe_layer *layers, int32_t n_layers) {
-    if (!layers || n_layers < 1) return 0;
-    size_t m = 0;
-    for (int i = 0; i < n_layers; i++) m = std::max(m, moe_layer_workspace_bytes(&layers[i], 1));
-    return m;
+    if (!layers || n_layers < 1 || !dims_ok(layers[0].H, layers[0].I) || layers[0].router.k < 1) return 0;
+    DecodeWs D;
+    if (carve_decode(nullptr, layers, n_layers, &D)) return 0;
+    return D.bytes;
 }
 
 int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x, int32_t T, float *out,
@@ -281,26 +340,84 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
     for (int l = 0; l < n_layers; l++) {
         int rc = check_layer(&layers[l], true);
         if (rc) return rc;
-        if (layers[l].H != layers[0].H || layers[l].I != layers[0].I || layers[l].router.k != layers[0].router.k)
-            return fail(MOE_E_INVAL, "layer %d differs from layer 0 in H, I or k", l);
+        if (layers[l].H != layers[0].H || layers[l].I != layers[0].I || layers[l].router.k != layers[0].router.k ||
+            layers[l].router.E != layers[0].router.E)
+            return fail(MOE_E_INVAL, "layer %d differs from layer 0 in H, I, E or k", l);
     }
     if (T < 0) return fail(MOE_E_INVAL, "T=%d < 0", T);
     if (T == 0) return MOE_OK;
     if (!x || !out || !ws) return fail(MOE_E_INVAL, "x, out and ws must be non-NULL");
-    const size_t need = moe_decode_workspace_bytes(layers, n_layers);
-    if (ws_bytes < need) return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-    const int H = layers[0].H, k = layers[0].router.k;
+    DecodeWs D;
+    int rc = carve_decode(ws, layers, n_layers, &D);
+    if (rc) return rc;
+    if (ws_bytes < D.bytes) return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, D.bytes);
+    const int H = layers[0].H, I = layers[0].I, k = layers[0].router.k;
+    hipStream_t s = (hipStream_t)hip_stream;
+    DecodeLaunch d{};
+    d.H = H;
+    d.I = I;
+    d.k = k;
+    d.E_max = layers[0].router.E;
+    d.G = D.G;
+    d.off = offsets_of(H, I);
+    d.sync = D.sync;
+    d.sync_words = D.sync_words;
+    d.layer_buf = D.layers;
+    d.z = D.z;
+    d.xh = D.xh;
+    d.hh = D.hh;
+    d.hs = D.hs;
+    d.ysh = D.ysh;
+    d.part_gu = D.part_gu;
+    d.part_d = D.part_d;
+    d.slots_gu = D.slots_gu;
+    d.slots_d = D.slots_d;
+    d.slots_red_gu = D.slots_red_gu;
+    d.slots_red_d = D.slots_red_d;
+    d.stamps = D.stamps;
+    d.stamp_steps = D.stamp_steps;
+    auto set_layers = [&](int l0, int nl) {
+        d.nL = nl;
+        d.has_shared = 0;
+        for (int l = 0; l < nl; l++) {
+            const moe_layer &L = layers[l0 + l];
+            d.layers[l] = DecLayer{L.router.weight, L.router.bias, L.records, L.shared, L.router.E, L.router.k,
+                                   L.router.score_fn, 0};
+            d.has_shared |= L.shared != nullptr;
+        }
+    };
+    if (n_layers <= kDecMaxLayers) {
+        // the whole decode in one launch
+        set_layers(0, n_layers);
+        d.T = T;
+        d.x = x;
+        d.out = out;
+        d.idx_out = idx_out;
+        HIPCHK(launch_decode_persistent(d, s), "persistent decode launch");
+        return MOE_OK;
+    }
+    // more layers than one launch carries: one launch per (token, layer group)
     for (int t = 0; t < T; t++) {
-        for (int l = 0; l < n_layers; l++) {
-            const size_t step = (size_t)t * n_layers + l;
-            int rc = moe_layer_forward(&layers[l], x + step * H, MOE_DTYPE_F32, 1, out + step * H,
-                                       idx_out ? idx_out + step * k : nullptr, nullptr, ws, ws_bytes, hip_stream);
-            if (rc) return rc;
+        for (int l0 = 0; l0 < n_layers; l0 += kDecMaxLayers) {
+            const int nl = std::min(kDecMaxLayers, n_layers - l0);
+            set_layers(l0, nl);
+            d.T = 1;
+            d.x = x + ((size_t)t * n_layers + l0) * H;
+            d.out = out + ((size_t)t * n_layers + l0) * H;
+            d.idx_out = idx_out ? idx_out + ((size_t)t * n_layers + l0) * k : nullptr;
+            HIPCHK(launch_decode_persistent(d, s), "persistent decode launch");
         }
     }
     return MOE_OK;
 }
 
+int moe_decode_status(const void *ws, int32_t *timed_out) {
+    if (!ws || !timed_out) return fail(MOE_E_INVAL, "ws and timed_out must be non-NULL");
+    unsigned flag = 0;
+    HIPCHK(hipMemcpy(&flag, ws, sizeof flag, hipMemcpyDeviceToHost), "read decode status");
+    *timed_out = flag != 0;
+    return MOE_OK;
+}
 
 size_t moe_streamed_workspace_bytes(const moe_layer *L, int32_t T) {
     return moe_layer_workspace_bytes(L, T);

@@ -70,6 +70,47 @@ hipError_t launch_dense_down(const uint16_t *shared, int H, int I, const float *
 
 int down_splits(int H, int I, int n_items);
 
+// ---- persistent decode (kernels_decode.hip) ----------------------------------
+constexpr int kDecMaxLayers = 40;   // layer descriptors carried in one launch's arguments
+
+struct DecLayer {
+    const float *W;
+    const float *bias;
+    const void *const *records;
+    const uint16_t *shared;
+    int32_t E, k, score_fn, pad;
+};
+
+struct DecodeLaunch {
+    DecLayer layers[kDecMaxLayers];
+    int nL, T, H, I, k, E_max, G, has_shared;
+    const float *x;
+    float *out;
+    int32_t *idx_out;
+    RecOffsets off;
+    unsigned *sync;
+    size_t sync_words;
+    DecLayer *layer_buf;     // [kDecMaxLayers] device copy of the descriptors
+    float *z;
+    uint32_t *xh;
+    uint16_t *hh;
+    float *hs, *ysh, *part_gu, *part_d;
+    int slots_gu, slots_d;
+    int slots_red_gu, slots_red_d;
+    unsigned long long *stamps;   // phase timestamps (profiling aid), or null
+    int stamp_steps;
+};
+
+struct DecodePlanOut {
+    int G;                        // persistent workgroups (one per CU)
+    int slots_gu, slots_d;        // most contributors to one tile's partial sums
+    int slots_red_gu, slots_red_d;   // most tiles one workgroup touches per phase
+    size_t sync_words;
+    bool lds_ok;
+};
+hipError_t decode_plan(int H, int I, int k, DecodePlanOut *o);
+hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s);
+
 // ---- batched path (kernels_grouped.hip) --------------------------------------
 hipError_t launch_group(const int32_t *idx, int n_pairs, int E, int32_t *perm, int32_t *inv, int32_t *counts,
                         int32_t *offsets, hipStream_t s);
