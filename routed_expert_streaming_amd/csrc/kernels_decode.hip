@@ -54,6 +54,40 @@ __device__ __forceinline__ unsigned ld_cnt(const unsigned *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Direct global -> LDS copies (global_load_lds_dwordx4): each lane moves 16
+// bytes into LDS at the wave-uniform base + 16 * lane, without passing
+// through registers, so a workgroup's whole staging is in flight at once.
+// Wave v moves 1 KB blocks v, v + kPW, ...  The cache policy is kLdsPlain for
+// record data (immutable during the launch) and kLdsCoherent (sc1, the
+// policy of an agent-scope load) for data other workgroups wrote.  The caller
+// waits for vmcnt 0 and synchronises the workgroup before reading.
+typedef __attribute__((address_space(1))) const void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+constexpr int kLdsPlain = 0, kLdsCoherent = 16;
+template <int AUX>
+__device__ __forceinline__ void stage_lds(char *dst, const void *src, int nbytes, int wave, int lane) {
+    const int nblk = (nbytes + 1023) >> 10;
+    for (int b = wave; b < nblk; b += kPW) {
+        const int off = (b << 10) + lane * 16;
+        if (off < nbytes)
+            __builtin_amdgcn_global_load_lds((gvoid *)((const char *)src + off), (lvoid *)(dst + (b << 10)), 16, 0, AUX);
+    }
+}
+
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// Wait until all but this wave's N most recent vector memory operations
+// (and all its LDS operations) are done, then a plain workgroup barrier.
+// For LDS data only: __syncthreads() would also wait for the N loads still
+// in flight.  The asm's memory clobber keeps the compiler from moving memory
+// accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void wait_lds_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+constexpr int kStripLoads = 3;   // 128-bit loads per 48-byte code strip
+
 // Workgroup-wide wait until *p >= target.  Returns false (error flag set)
 // on timeout or if another workgroup already failed.
 __device__ __forceinline__ bool wg_wait(unsigned *sync, const unsigned *p, unsigned target, int *bcast) {
@@ -77,16 +111,12 @@ __device__ __forceinline__ bool wg_wait(unsigned *sync, const unsigned *p, unsig
     return ok;
 }
 
-// Workgroup-wide: wait for this workgroup's stores to complete, then add 1
-// to a counter.  Returns the counter's previous value (to every thread).
-__device__ __forceinline__ unsigned wg_signal(unsigned *p, int *bcast) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this thread's stores are done
+// Workgroup-wide release: wait until this workgroup's stores have completed,
+// then add 1 to a counter.  The add returns nothing, so nothing waits for it.
+__device__ __forceinline__ void wg_signal(unsigned *p) {
+    wait_vm_all();
     __syncthreads();
-    if (threadIdx.x == 0) *bcast = (int)__hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const unsigned old = (unsigned)*bcast;
-    __syncthreads();
-    return old;
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // A space of n units is split over Ga = min(G, n) active workgroups into
@@ -104,112 +134,132 @@ __device__ __forceinline__ int range_owner(long n, int G, long u) {
     return (int)(((u + 1) * Ga + n - 1) / n - 1);
 }
 
-// dot of one 48-byte code strip with x pairs read from LDS at a wave-uniform
-// address (a broadcast read: all lanes get the same 16 bytes)
-template <int G>
-__device__ __forceinline__ void strip_dot_lx(const uint32_t (&d)[12], const char *cb, const uint32_t *xl,
-                                             float (&acc)[4]) {
-    if constexpr (G < 16) {
-        uint32_t aa, ba;
-        group_addr<G>(d, aa, ba);
-        const u32x4 ca = *(const u32x4 *)(cb + aa);
-        const u32x4 cbv = *(const u32x4 *)(cb + ba);
-        const u32x4 xq = *(const u32x4 *)(xl + 4 * G);
-        float a = acc[G & 3];
-        a = dot2(ca.x, xq.x, a);
-        a = dot2(ca.y, xq.y, a);
-        a = dot2(ca.z, xq.z, a);
-        a = dot2(ca.w, xq.w, a);
-        a = dot2(cbv.x, xq.x, a);
-        a = dot2(cbv.y, xq.y, a);
-        a = dot2(cbv.z, xq.z, a);
-        a = dot2(cbv.w, xq.w, a);
-        acc[G & 3] = a;
-        strip_dot_lx<G + 1>(d, cb, xl, acc);
+// One strip (64 rows x 128 columns, 16 groups of 8 columns) of codes against
+// x pairs in LDS.  Each lane owns one row; a group costs two codebook-row
+// gathers (codes a and b) and a broadcast read of the group's x pairs (a
+// wave-uniform address).  Groups are processed in batches whose reads are
+// software-pipelined: batch B+1's gathers are issued before batch B's dot
+// products, so a wave always has LDS work queued while it computes.
+// sched_barrier fences keep the compiler from hoisting further batches
+// (which would hold every gathered row in registers at once).
+
+// gate and up together, two groups per batch (8 gathers + 2 x reads)
+struct GuBatch {
+    u32x4 g0[2], g1[2], u0[2], u1[2], xq[2];
+};
+template <int B>
+__device__ __forceinline__ void gu_read(GuBatch &d, const uint32_t (&dg)[12], const uint32_t (&du)[12], const char *cbg,
+                                        const char *cbu, const uint32_t *xl) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        uint32_t ga, gb, ua, ub;
+        if (i == 0) { group_addr<2 * B>(dg, ga, gb); group_addr<2 * B>(du, ua, ub); }
+        else { group_addr<2 * B + 1>(dg, ga, gb); group_addr<2 * B + 1>(du, ua, ub); }
+        d.g0[i] = *(const u32x4 *)(cbg + ga);
+        d.g1[i] = *(const u32x4 *)(cbg + gb);
+        d.u0[i] = *(const u32x4 *)(cbu + ua);
+        d.u1[i] = *(const u32x4 *)(cbu + ub);
+        d.xq[i] = *(const u32x4 *)(xl + 4 * (2 * B + i));
     }
 }
-
-// gate and up together, two groups per batch: the batch's 8 codebook
-// gathers and 2 broadcast reads of x pairs are issued before its 32 dot
-// products
 template <int B>
-__device__ __forceinline__ void strip_dot2_lx(const uint32_t (&dg)[12], const uint32_t (&du)[12], const char *cbg,
-                                              const char *cbu, const uint32_t *xl, float (&ag)[4], float (&au)[4]) {
+__device__ __forceinline__ void gu_dots(GuBatch &d, float (&ag)[4], float (&au)[4]) {
+    // the batch's values are complete here (waits only for this batch)
+    asm volatile("" : "+v"(d.g0[0]), "+v"(d.g0[1]), "+v"(d.g1[0]), "+v"(d.g1[1]), "+v"(d.u0[0]), "+v"(d.u0[1]),
+                 "+v"(d.u1[0]), "+v"(d.u1[1]), "+v"(d.xq[0]), "+v"(d.xq[1]));
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        float a = ag[(2 * B + i) & 3], b = au[(2 * B + i) & 3];
+        a = dot2(d.g0[i].x, d.xq[i].x, a); b = dot2(d.u0[i].x, d.xq[i].x, b);
+        a = dot2(d.g0[i].y, d.xq[i].y, a); b = dot2(d.u0[i].y, d.xq[i].y, b);
+        a = dot2(d.g0[i].z, d.xq[i].z, a); b = dot2(d.u0[i].z, d.xq[i].z, b);
+        a = dot2(d.g0[i].w, d.xq[i].w, a); b = dot2(d.u0[i].w, d.xq[i].w, b);
+        a = dot2(d.g1[i].x, d.xq[i].x, a); b = dot2(d.u1[i].x, d.xq[i].x, b);
+        a = dot2(d.g1[i].y, d.xq[i].y, a); b = dot2(d.u1[i].y, d.xq[i].y, b);
+        a = dot2(d.g1[i].z, d.xq[i].z, a); b = dot2(d.u1[i].z, d.xq[i].z, b);
+        a = dot2(d.g1[i].w, d.xq[i].w, a); b = dot2(d.u1[i].w, d.xq[i].w, b);
+        ag[(2 * B + i) & 3] = a;
+        au[(2 * B + i) & 3] = b;
+    }
+}
+template <int B>
+__device__ __forceinline__ void gu_pipe(const uint32_t (&dg)[12], const uint32_t (&du)[12], const char *cbg,
+                                        const char *cbu, const uint32_t *xl, GuBatch &cur, GuBatch &nxt,
+                                        float (&ag)[4], float (&au)[4]) {
     if constexpr (B < 8) {
-        u32x4 g0[2], g1[2], u0[2], u1[2], xq[2];
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            uint32_t ga, gb, ua, ub;
-            if (i == 0) { group_addr<2 * B>(dg, ga, gb); group_addr<2 * B>(du, ua, ub); }
-            else { group_addr<2 * B + 1>(dg, ga, gb); group_addr<2 * B + 1>(du, ua, ub); }
-            g0[i] = *(const u32x4 *)(cbg + ga);
-            g1[i] = *(const u32x4 *)(cbg + gb);
-            u0[i] = *(const u32x4 *)(cbu + ua);
-            u1[i] = *(const u32x4 *)(cbu + ub);
-            xq[i] = *(const u32x4 *)(xl + 4 * (2 * B + i));
-        }
-        // every read of the batch is issued before any of its values is used
-        asm volatile("" : "+v"(g0[0]), "+v"(g0[1]), "+v"(g1[0]), "+v"(g1[1]), "+v"(u0[0]), "+v"(u0[1]), "+v"(u1[0]),
-                     "+v"(u1[1]), "+v"(xq[0]), "+v"(xq[1]));
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            float a = ag[(2 * B + i) & 3], b = au[(2 * B + i) & 3];
-            a = dot2(g0[i].x, xq[i].x, a); b = dot2(u0[i].x, xq[i].x, b);
-            a = dot2(g0[i].y, xq[i].y, a); b = dot2(u0[i].y, xq[i].y, b);
-            a = dot2(g0[i].z, xq[i].z, a); b = dot2(u0[i].z, xq[i].z, b);
-            a = dot2(g0[i].w, xq[i].w, a); b = dot2(u0[i].w, xq[i].w, b);
-            a = dot2(g1[i].x, xq[i].x, a); b = dot2(u1[i].x, xq[i].x, b);
-            a = dot2(g1[i].y, xq[i].y, a); b = dot2(u1[i].y, xq[i].y, b);
-            a = dot2(g1[i].z, xq[i].z, a); b = dot2(u1[i].z, xq[i].z, b);
-            a = dot2(g1[i].w, xq[i].w, a); b = dot2(u1[i].w, xq[i].w, b);
-            ag[(2 * B + i) & 3] = a;
-            au[(2 * B + i) & 3] = b;
-        }
-        strip_dot2_lx<B + 1>(dg, du, cbg, cbu, xl, ag, au);
+        if constexpr (B + 1 < 8) gu_read<B + 1>(nxt, dg, du, cbg, cbu, xl);
+        __builtin_amdgcn_sched_barrier(0);
+        gu_dots<B>(cur, ag, au);
+        __builtin_amdgcn_sched_barrier(0);
+        gu_pipe<B + 1>(dg, du, cbg, cbu, xl, nxt, cur, ag, au);
     }
 }
+__device__ __forceinline__ void strip_gateup(const uint32_t (&dg)[12], const uint32_t (&du)[12], const char *cbg,
+                                             const char *cbu, const uint32_t *xl, float (&ag)[4], float (&au)[4]) {
+    GuBatch p, q;
+    gu_read<0>(p, dg, du, cbg, cbu, xl);
+    gu_pipe<0>(dg, du, cbg, cbu, xl, p, q, ag, au);
+}
 
-// one matrix, four groups per batch: 8 gathers + 4 broadcast reads in flight
+// one matrix, four groups per batch (8 gathers + 4 x reads)
+struct DBatch {
+    u32x4 c0[4], c1[4], xq[4];
+};
 template <int B>
-__device__ __forceinline__ void strip_dot_lx4(const uint32_t (&d)[12], const char *cb, const uint32_t *xl,
-                                              float (&acc)[4]) {
-    if constexpr (B < 4) {
-        u32x4 c0[4], c1[4], xq[4];
+__device__ __forceinline__ void d_read(DBatch &d, const uint32_t (&c)[12], const char *cb, const uint32_t *xl) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            uint32_t aa, ba;
-            switch (i) {
-                case 0: group_addr<4 * B + 0>(d, aa, ba); break;
-                case 1: group_addr<4 * B + 1>(d, aa, ba); break;
-                case 2: group_addr<4 * B + 2>(d, aa, ba); break;
-                default: group_addr<4 * B + 3>(d, aa, ba); break;
-            }
-            c0[i] = *(const u32x4 *)(cb + aa);
-            c1[i] = *(const u32x4 *)(cb + ba);
-            xq[i] = *(const u32x4 *)(xl + 4 * (4 * B + i));
+    for (int i = 0; i < 4; i++) {
+        uint32_t aa, ba;
+        switch (i) {
+            case 0: group_addr<4 * B + 0>(c, aa, ba); break;
+            case 1: group_addr<4 * B + 1>(c, aa, ba); break;
+            case 2: group_addr<4 * B + 2>(c, aa, ba); break;
+            default: group_addr<4 * B + 3>(c, aa, ba); break;
         }
-        asm volatile("" : "+v"(c0[0]), "+v"(c0[1]), "+v"(c0[2]), "+v"(c0[3]), "+v"(c1[0]), "+v"(c1[1]), "+v"(c1[2]),
-                     "+v"(c1[3]), "+v"(xq[0]), "+v"(xq[1]), "+v"(xq[2]), "+v"(xq[3]));
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            float a = acc[i];
-            a = dot2(c0[i].x, xq[i].x, a);
-            a = dot2(c0[i].y, xq[i].y, a);
-            a = dot2(c0[i].z, xq[i].z, a);
-            a = dot2(c0[i].w, xq[i].w, a);
-            a = dot2(c1[i].x, xq[i].x, a);
-            a = dot2(c1[i].y, xq[i].y, a);
-            a = dot2(c1[i].z, xq[i].z, a);
-            a = dot2(c1[i].w, xq[i].w, a);
-            acc[i] = a;
-        }
-        strip_dot_lx4<B + 1>(d, cb, xl, acc);
+        d.c0[i] = *(const u32x4 *)(cb + aa);
+        d.c1[i] = *(const u32x4 *)(cb + ba);
+        d.xq[i] = *(const u32x4 *)(xl + 4 * (4 * B + i));
     }
 }
+__device__ __forceinline__ void d_dots(DBatch &d, float (&acc)[4]) {
+    asm volatile("" : "+v"(d.c0[0]), "+v"(d.c0[1]), "+v"(d.c0[2]), "+v"(d.c0[3]), "+v"(d.c1[0]), "+v"(d.c1[1]),
+                 "+v"(d.c1[2]), "+v"(d.c1[3]), "+v"(d.xq[0]), "+v"(d.xq[1]), "+v"(d.xq[2]), "+v"(d.xq[3]));
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        float a = acc[i];
+        a = dot2(d.c0[i].x, d.xq[i].x, a);
+        a = dot2(d.c0[i].y, d.xq[i].y, a);
+        a = dot2(d.c0[i].z, d.xq[i].z, a);
+        a = dot2(d.c0[i].w, d.xq[i].w, a);
+        a = dot2(d.c1[i].x, d.xq[i].x, a);
+        a = dot2(d.c1[i].y, d.xq[i].y, a);
+        a = dot2(d.c1[i].z, d.xq[i].z, a);
+        a = dot2(d.c1[i].w, d.xq[i].w, a);
+        acc[i] = a;
+    }
+}
+template <int B>
+__device__ __forceinline__ void d_pipe(const uint32_t (&c)[12], const char *cb, const uint32_t *xl, DBatch &cur,
+                                       DBatch &nxt, float (&acc)[4]) {
+    if constexpr (B < 4) {
+        if constexpr (B + 1 < 4) d_read<B + 1>(nxt, c, cb, xl);
+        __builtin_amdgcn_sched_barrier(0);
+        d_dots(cur, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        d_pipe<B + 1>(c, cb, xl, nxt, cur, acc);
+    }
+}
+__device__ __forceinline__ void strip_down(const uint32_t (&c)[12], const char *cb, const uint32_t *xl,
+                                           float (&acc)[4]) {
+    DBatch p, q;
+    d_read<0>(p, c, cb, xl);
+    d_pipe<0>(c, cb, xl, p, q, acc);
+}
 
-// The streaming GEMV loops live in functions of their own so that each gets
-// its own register allocation (inlined together with the rest they spill).
-// They address the kernel's dynamic LDS directly.
+// The streaming GEMV loops are inlined into the kernel: as separate
+// functions, the call convention makes each call save and restore most of
+// the register file through scratch memory.  They address the kernel's
+// dynamic LDS directly.
 extern __shared__ __align__(16) char dec_lds[];
 
 // LDS layout (bytes).  Gate/up: [gate cb 64K][up cb 64K][x pairs][sums];
@@ -230,118 +280,156 @@ constexpr int kDecTail = kDecLdsBytes - 1024;     // sidx, sw, broadcast words, 
 constexpr int kRingGU = 3;      // code buffers per wave (2 units in flight ahead)
 constexpr int kRingD = 4;       // (3 ahead)
 
-__device__ __forceinline__ void load_codes(gu32x4 *base, long u, int lane, uint32_t (&d)[12]) {
-    load_strip((const u32x4 *)(base + u * kTileVec), lane, d);
+__device__ __forceinline__ void load_codes(gu32x4 *base, int u, int lane, uint32_t (&d)[12]) {
+    load_strip((const u32x4 *)(base + (long)u * kTileVec), lane, d);
+}
+
+// A wave's position in its units: tile t, chunk c; it advances kPW units at
+// a time.  Tile sums accumulate in registers and are flushed to the LDS slot
+// (tile - t0) when the tile changes.
+struct UnitPos {
+    int t, c, cur_t;
+    float rcp;    // 1 / cpr
+};
+// Branch-free advance (a loop here lets the compiler sink the unit's dot
+// products past it, keeping every gathered row live): the float quotient of
+// c < cpr + kPW by cpr is exact or one low, and one select corrects it.
+__device__ __forceinline__ void next_unit(UnitPos &p, int cpr) {
+    const int c = p.c + kPW;
+    int q = (int)((float)c * p.rcp);
+    int r = c - q * cpr;
+    const bool hi = r >= cpr;
+    q += hi ? 1 : 0;
+    r -= hi ? cpr : 0;
+    p.t += q;
+    p.c = r;
+}
+
+__device__ __forceinline__ void gu_unit(const uint32_t (&dg)[12], const uint32_t (&du)[12], const char *cbg,
+                                        const char *cbu, const uint32_t *xl, float *red, int t0, int cpr, int wave,
+                                        int lane, UnitPos &p, float (&ag)[4], float (&au)[4]) {
+    if (p.t != p.cur_t) {
+        float *s = red + ((p.cur_t - t0) * kPW + wave) * 128;
+        s[lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
+        s[64 + lane] = (au[0] + au[1]) + (au[2] + au[3]);
+        ag[0] = ag[1] = ag[2] = ag[3] = 0.f;
+        au[0] = au[1] = au[2] = au[3] = 0.f;
+        p.cur_t = p.t;
+    }
+    strip_gateup(dg, du, cbg, cbu, xl + p.c * 64, ag, au);
+    next_unit(p, cpr);
+}
+
+__device__ __forceinline__ void d_unit(const uint32_t (&d)[12], const char *cb, const uint32_t *xl, float *red, int t0,
+                                       int cpr, int wave, int lane, UnitPos &p, float (&acc)[4]) {
+    if (p.t != p.cur_t) {
+        red[((p.cur_t - t0) * kPW + wave) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+        p.cur_t = p.t;
+    }
+    strip_down(d, cb, xl + p.c * 64, acc);
+    next_unit(p, cpr);
 }
 
 // Gate and up of one expert: units [la, lb) (unit u = tile u / cpr, chunk
 // u % cpr; its codes are 3072 bytes at base + u * 3072).  Wave v takes units
 // la + v, la + v + kPW, ...; tile sums go to LDS slot (tile - t0).  The first
 // loads are issued before the codebooks (and, if stage_x, the x pairs) are
-// staged into LDS.
-__device__ __noinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *usec, const u32x4 *cbg_src,
+// staged into LDS.  The steady-state loop has no branches around its loads:
+// loads past the wave's last unit re-read that unit (their buffers are never
+// consumed), so every load of the ring stays in flight while older units are
+// computed.
+__device__ __forceinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *usec, const u32x4 *cbg_src,
                                            const u32x4 *cbu_src, const uint32_t *xh_src, int stage_x, int H, int I,
-                                           int cpr, long la, long lb, long t0, int nslots, int wave, int lane) {
+                                           int cpr, int la, int lb, int t0, int nslots, int wave, int lane) {
     const DecLds L = dec_lds_layout(H, I);
     char *cbg = dec_lds, *cbu = dec_lds + kCbRows * 16;
     uint32_t *xl = (uint32_t *)(dec_lds + L.x_gu);
     float *red = (float *)(dec_lds + L.red_gu);
     gu32x4 *gb = (gu32x4 *)gsec, *ub = (gu32x4 *)usec;
-    const long first = la + wave;
-    const int n = first < lb ? (int)((lb - first + kPW - 1) / kPW) : 0;
+    const int first = __builtin_amdgcn_readfirstlane(la + wave);
+    const int n = __builtin_amdgcn_readfirstlane(first < lb ? (lb - first + kPW - 1) / kPW : 0);
+    // stage codebooks (+ x) and clear this segment's sum slots, with the
+    // first code loads in flight
+    stage_lds<kLdsPlain>(cbg, cbg_src, kCbRows * 16, wave, lane);
+    stage_lds<kLdsPlain>(cbu, cbu_src, kCbRows * 16, wave, lane);
+    if (stage_x) stage_lds<kLdsCoherent>((char *)xl, xh_src, H * 2, wave, lane);
+    // the code loads are issued after every staging copy (the fence keeps
+    // that order), so waiting until only they are outstanding is enough to
+    // see the staged data: the loop starts without waiting for them
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t bg[kRingGU][12], bu[kRingGU][12];
-#pragma unroll
-    for (int r = 0; r < kRingGU - 1; r++)
-        if (r < n) {
-            load_codes(gb, first + (long)r * kPW, lane, bg[r]);
-            load_codes(ub, first + (long)r * kPW, lane, bu[r]);
-        }
-    // stage codebooks (+ x), clear this segment's sum slots
-    for (int i = threadIdx.x; i < kCbRows; i += kPW * 64) {
-        ((u32x4 *)cbg)[i] = cbg_src[i];
-        ((u32x4 *)cbu)[i] = cbu_src[i];
-    }
-    if (stage_x)
-        for (int i = threadIdx.x; i < H / 2; i += kPW * 64) xl[i] = ld_x(xh_src + i);
     for (int i = threadIdx.x; i < nslots * kPW * 128; i += kPW * 64) red[i] = 0.f;
-    __syncthreads();
+    // first ring stages; a wave without units loads the segment's first unit
+    // (never consumed), so every wave has the same loads in flight
+#pragma unroll
+    for (int r = 0; r < kRingGU - 1; r++) {
+        const int u = n ? first + min(r, n - 1) * kPW : la;
+        load_codes(gb, u, lane, bg[r]);
+        load_codes(ub, u, lane, bu[r]);
+    }
+    wait_lds_barrier<(kRingGU - 1) * 2 * kStripLoads>();
+    lds_barrier();
+    if (!n) return;
     float ag[4] = {0.f, 0.f, 0.f, 0.f}, au[4] = {0.f, 0.f, 0.f, 0.f};
-    long cur_t = n ? first / cpr : -1;
-    for (int i0 = 0; i0 < n; i0 += kRingGU) {
+    UnitPos p{first / cpr, first % cpr, first / cpr, 1.f / (float)cpr};
+    int i = 0;
+    for (; i + kRingGU <= n; i += kRingGU) {
 #pragma unroll
         for (int r = 0; r < kRingGU; r++) {
-            const int i = i0 + r;
-            if (i < n) {
-                const int nxt = i + kRingGU - 1;
-                if (nxt < n) {
-                    load_codes(gb, first + (long)nxt * kPW, lane, bg[(r + kRingGU - 1) % kRingGU]);
-                    load_codes(ub, first + (long)nxt * kPW, lane, bu[(r + kRingGU - 1) % kRingGU]);
-                }
-                const long u = first + (long)i * kPW;
-                const long t = u / cpr;
-                if (t != cur_t) {
-                    float *p = red + ((int)(cur_t - t0) * kPW + wave) * 128;
-                    p[lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
-                    p[64 + lane] = (au[0] + au[1]) + (au[2] + au[3]);
-                    ag[0] = ag[1] = ag[2] = ag[3] = 0.f;
-                    au[0] = au[1] = au[2] = au[3] = 0.f;
-                    cur_t = t;
-                }
-                strip_dot2_lx<0>(bg[r], bu[r], cbg, cbu, xl + (int)(u % cpr) * 64, ag, au);
-            }
+            const int u = first + min(i + r + kRingGU - 1, n - 1) * kPW;
+            load_codes(gb, u, lane, bg[(r + kRingGU - 1) % kRingGU]);
+            load_codes(ub, u, lane, bu[(r + kRingGU - 1) % kRingGU]);
+            gu_unit(bg[r], bu[r], cbg, cbu, xl, red, t0, cpr, wave, lane, p, ag, au);
         }
     }
-    if (n) {
-        float *p = red + ((int)(cur_t - t0) * kPW + wave) * 128;
-        p[lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
-        p[64 + lane] = (au[0] + au[1]) + (au[2] + au[3]);
-    }
+    // the last n - i (< kRingGU) units are already in buffers 0, 1, ...
+#pragma unroll
+    for (int r = 0; r < kRingGU - 1; r++)
+        if (i + r < n) gu_unit(bg[r], bu[r], cbg, cbu, xl, red, t0, cpr, wave, lane, p, ag, au);
+    float *s = red + ((p.cur_t - t0) * kPW + wave) * 128;
+    s[lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
+    s[64 + lane] = (au[0] + au[1]) + (au[2] + au[3]);
 }
 
 // Down of one expert: units [la, lb) over tiles of H, like stream_gateup.
 // The first loads are issued before waiting for the expert's h (counter
 // h_ready >= h_target) and staging it with the codebook.  Returns 0 if the
 // wait failed.
-__device__ __noinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_src, const uint32_t *h_src, unsigned *sync,
+__device__ __forceinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_src, const uint32_t *h_src, unsigned *sync,
                                         const unsigned *h_ready, unsigned h_target, int *bcast, int H, int I, int cpr,
-                                        long la, long lb, long t0, int nslots, int wave, int lane) {
+                                        int la, int lb, int t0, int nslots, int wave, int lane) {
     const DecLds L = dec_lds_layout(H, I);
     char *cb = dec_lds;
     uint32_t *xl = (uint32_t *)(dec_lds + L.x_d);
     float *red = (float *)(dec_lds + L.red_d);
     gu32x4 *db = (gu32x4 *)dsec;
-    const long first = la + wave;
-    const int n = first < lb ? (int)((lb - first + kPW - 1) / kPW) : 0;
+    const int first = __builtin_amdgcn_readfirstlane(la + wave);
+    const int n = __builtin_amdgcn_readfirstlane(first < lb ? (lb - first + kPW - 1) / kPW : 0);
     uint32_t bd[kRingD][12];
 #pragma unroll
-    for (int r = 0; r < kRingD - 1; r++)
-        if (r < n) load_codes(db, first + (long)r * kPW, lane, bd[r]);
-    if (!wg_wait(sync, h_ready, h_target, bcast)) return 0;
-    for (int i = threadIdx.x; i < kCbRows; i += kPW * 64) ((u32x4 *)cb)[i] = cbd_src[i];
-    for (int i = threadIdx.x; i < I / 2; i += kPW * 64) xl[i] = ld_x(h_src + i);
+    for (int r = 0; r < kRingD - 1; r++) load_codes(db, n ? first + min(r, n - 1) * kPW : la, lane, bd[r]);
+    stage_lds<kLdsPlain>(cb, cbd_src, kCbRows * 16, wave, lane);
     for (int i = threadIdx.x; i < nslots * kPW * 64; i += kPW * 64) red[i] = 0.f;
+    if (!wg_wait(sync, h_ready, h_target, bcast)) return 0;
+    stage_lds<kLdsCoherent>((char *)xl, h_src, I * 2, wave, lane);
+    wait_vm_all();
     __syncthreads();
+    if (!n) return 1;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    long cur_t = n ? first / cpr : -1;
-    for (int i0 = 0; i0 < n; i0 += kRingD) {
+    UnitPos p{first / cpr, first % cpr, first / cpr, 1.f / (float)cpr};
+    int i = 0;
+    for (; i + kRingD <= n; i += kRingD) {
 #pragma unroll
         for (int r = 0; r < kRingD; r++) {
-            const int i = i0 + r;
-            if (i < n) {
-                const int nxt = i + kRingD - 1;
-                if (nxt < n) load_codes(db, first + (long)nxt * kPW, lane, bd[(r + kRingD - 1) % kRingD]);
-                const long u = first + (long)i * kPW;
-                const long t = u / cpr;
-                if (t != cur_t) {
-                    red[((int)(cur_t - t0) * kPW + wave) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                    acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
-                    cur_t = t;
-                }
-                strip_dot_lx4<0>(bd[r], cb, xl + (int)(u % cpr) * 64, acc);
-            }
+            load_codes(db, first + min(i + r + kRingD - 1, n - 1) * kPW, lane, bd[(r + kRingD - 1) % kRingD]);
+            d_unit(bd[r], cb, xl, red, t0, cpr, wave, lane, p, acc);
         }
     }
-    if (n) red[((int)(cur_t - t0) * kPW + wave) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+    for (int r = 0; r < kRingD - 1; r++)
+        if (i + r < n) d_unit(bd[r], cb, xl, red, t0, cpr, wave, lane, p, acc);
+    red[((p.cur_t - t0) * kPW + wave) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     return 1;
 }
 
@@ -357,27 +445,53 @@ __device__ __forceinline__ unsigned tile_target(int td, int k, int tilesH, int c
     return n;
 }
 
-// last contributor of output tile td: fixed-order combine
-// out = sum_j w_j * sum_slots y_j + shared
-__device__ __forceinline__ void combine_tile(int td, int s, int k, int tilesH, int cprI, long nD, int G, int H, bool shared_on,
-                             const float *part_d, int slots_d, const float *ysh, float *out, const float *sw,
-                             unsigned *sync, int wave, int lane, int *bcast) {
-    if (wave == 0) {
-        const int r = td * kTileRows + lane;
-        float o = 0.f;
-        for (int j = 0; j < k; j++) {
-            const long tau = (long)j * tilesH + td;
-            const int first = range_owner(nD, G, tau * cprI);
-            const int last = range_owner(nD, G, (tau + 1) * cprI - 1);
-            float y = 0.f;
-            for (int sl = 0; sl <= last - first; sl++)
-                y += ld_x(part_d + ((size_t)tau * slots_d + sl) * 64 + lane);
-            o = fmaf(sw[j], y, o);
-        }
-        if (shared_on) o += ld_x(ysh + r);
-        out[(size_t)s * H + r] = o;
+// Output tile td, by one wave of the workgroup that made its last
+// contribution: out = sum_j w_j * sum_slots y_j + shared, in fixed (rank,
+// contributor) order.
+__device__ __forceinline__ void combine_rows(int td, int s, int k, int tilesH, int cprI, long nD, int G, int H,
+                                             bool shared_on, const float *part_d, int slots_d, const float *ysh,
+                                             float *out, const float *sw, int lane) {
+    const int r = td * kTileRows + lane;
+    float o = 0.f;
+    for (int j = 0; j < k; j++) {
+        const long tau = (long)j * tilesH + td;
+        const int first = range_owner(nD, G, tau * cprI);
+        const int last = range_owner(nD, G, (tau + 1) * cprI - 1);
+        float y = 0.f;
+        for (int sl = 0; sl <= last - first; sl++) y += ld_x(part_d + ((size_t)tau * slots_d + sl) * 64 + lane);
+        o = fmaf(sw[j], y, o);
     }
-    wg_signal(sync + kLayerDone, bcast);
+    if (shared_on) o += ld_x(ysh + r);
+    out[(size_t)s * H + r] = o;
+}
+
+// Counts this workgroup's contribution to each output tile in [tdA, tdA + nt)
+// (its data stored and waited for, the workgroup synchronised), then
+// combines the tiles it completed, one wave per tile, and adds their number
+// to the layer-done counter.  All counter updates of the call are issued
+// together, so the call costs a few memory round trips whatever nt is.
+// flag: LDS scratch of nt ints.
+__device__ __forceinline__ void down_tiles_done(int tdA, int nt, int s, int k, int tilesH, int cprI, long nD, int G,
+                                                int H, bool shared_on, const float *part_d, int slots_d,
+                                                const float *ysh, float *out, const float *sw, unsigned *sync,
+                                                unsigned *cnt_d, int *flag, int wave, int lane) {
+    for (int v = threadIdx.x; v < nt; v += kPW * 64) {
+        const int td = tdA + v;
+        const unsigned old = __hip_atomic_fetch_add(cnt_d + td, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        flag[v] = (old + 1) % tile_target(td, k, tilesH, cprI, nD, G, H, shared_on) == 0;
+    }
+    __syncthreads();
+    int nc = 0;
+    for (int v = 0; v < nt; v++) {
+        if (!flag[v]) continue;
+        if (v % kPW == wave)
+            combine_rows(tdA + v, s, k, tilesH, cprI, nD, G, H, shared_on, part_d, slots_d, ysh, out, sw, lane);
+        ++nc;
+    }
+    wait_vm_all();
+    __syncthreads();
+    if (threadIdx.x == 0 && nc)
+        __hip_atomic_fetch_add(sync + kLayerDone, (unsigned)nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 struct DecArgs {
@@ -467,7 +581,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 u = wave_sum(u);
                 if (lane == 0) st_x(a.hs + r, g / (1.f + __expf(-g)) * u);
             }
-            if (shI1 > shI0) wg_signal(h_ready + k, bcast);
+            if (shI1 > shI0) wg_signal(h_ready + k);
         }
 
         // ---- route: logits of rows e = w, w + G, ... ; workgroup 0 also packs x
@@ -494,7 +608,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             }
             if (w == 0)
                 for (int i = threadIdx.x; i < H / 2; i += kPW * 64) st_x(a.xh + i, pack_f16x2(xs[2 * i], xs[2 * i + 1]));
-            wg_signal(sync + kRoute, bcast);
+            wg_signal(sync + kRoute);
         }
         if (!wg_wait(sync, sync + kRoute, (unsigned)(s + 1) * nE, bcast)) return;
         mark(2);
@@ -544,7 +658,6 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // expert segment at a time (a range spans at most two experts)
         {
             bool x_staged = false;
-            const long t_first = gu0 / cprH;
             for (long ea = gu0; ea < gu1;) {
                 const int j = (int)(ea / ((long)tilesI * cprH));
                 const long eb = min(gu1, (long)(j + 1) * tilesI * cprH);
@@ -552,49 +665,66 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 const long base = (long)j * tilesI * cprH;       // expert-local units
                 stream_gateup((const u32x4 *)(rec + a.off.codes[0]), (const u32x4 *)(rec + a.off.codes[1]),
                               (const u32x4 *)(rec + a.off.cb[0]), (const u32x4 *)(rec + a.off.cb[1]), a.xh,
-                              x_staged ? 0 : 1, H, I, cprH, ea - base, eb - base, ea / cprH - base / cprH,
+                              x_staged ? 0 : 1, H, I, cprH, (int)(ea - base), (int)(eb - base), (int)(ea / cprH - base / cprH),
                               a.slots_red_gu, wave, lane);
                 x_staged = true;
                 __syncthreads();
-                // one partial per touched tile, then the join by its last contributor
-                for (long tau = ea / cprH; tau <= (eb - 1) / cprH; tau++) {
-                    const int tile = (int)(tau % tilesI);
-                    const int first = range_owner(nGU, G, tau * cprH);
-                    const int last = range_owner(nGU, G, (tau + 1) * cprH - 1);
-                    const int slot = w - first, ncontrib = last - first + 1;
-                    const int rs = (int)(tau - ea / cprH);
-                    if (wave == 0) {
-                        float g = 0.f, uu = 0.f;
+                // one partial per touched tile (wave v: tiles v, v + kPW, ...);
+                // then every tile's counter at once; the tiles this workgroup
+                // completed are joined (one wave each) into fp16 SiLU(g) * u
+                const long tA = ea / cprH;
+                const int nt = (int)((eb - 1) / cprH - tA) + 1;
+                for (int v = wave; v < nt; v += kPW) {
+                    const long tau = tA + v;
+                    const int slot = w - range_owner(nGU, G, tau * cprH);
+                    float g = 0.f, uu = 0.f;
 #pragma unroll
-                        for (int v = 0; v < kPW; v++) {
-                            g += red_gu[((rs * kPW) + v) * 128 + lane];
-                            uu += red_gu[((rs * kPW) + v) * 128 + 64 + lane];
-                        }
-                        float *p = a.part_gu + ((size_t)tau * a.slots_gu + slot) * 128;
-                        st_x(p + lane, g);
-                        st_x(p + 64 + lane, uu);
+                    for (int q = 0; q < kPW; q++) {
+                        g += red_gu[(v * kPW + q) * 128 + lane];
+                        uu += red_gu[(v * kPW + q) * 128 + 64 + lane];
                     }
-                    const unsigned old = wg_signal(cnt_gu + tau, bcast);
-                    if ((old + 1) % (unsigned)ncontrib == 0) {
-                        if (wave == 0) {
-                            float g = 0.f, uu = 0.f;
-                            for (int sl = 0; sl < ncontrib; sl++) {
-                                const float *p = a.part_gu + ((size_t)tau * a.slots_gu + sl) * 128;
-                                g += ld_x(p + lane);
-                                uu += ld_x(p + 64 + lane);
-                            }
-                            const int r = tile * kTileRows + lane;
-                            g *= (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
-                            uu *= (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
-                            const _Float16 hf = (_Float16)(g / (1.f + __expf(-g)) * uu);
-                            st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
-                        }
-                        wg_signal(h_ready + j, bcast);
-                    }
+                    float *p = a.part_gu + ((size_t)tau * a.slots_gu + slot) * 128;
+                    st_x(p + lane, g);
+                    st_x(p + 64 + lane, uu);
                 }
+                wait_vm_all();
+                __syncthreads();
+                int *flag = (int *)(lds + LL.red_gu);
+                for (int v = threadIdx.x; v < nt; v += kPW * 64) {
+                    const long tau = tA + v;
+                    const int ncontrib =
+                        range_owner(nGU, G, (tau + 1) * cprH - 1) - range_owner(nGU, G, tau * cprH) + 1;
+                    const unsigned old =
+                        __hip_atomic_fetch_add(cnt_gu + tau, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    flag[v] = (old + 1) % (unsigned)ncontrib == 0;
+                }
+                __syncthreads();
+                int nj = 0;
+                for (int v = 0; v < nt; v++) {
+                    if (!flag[v]) continue;
+                    ++nj;
+                    if (v % kPW != wave) continue;
+                    const long tau = tA + v;
+                    const int ncontrib =
+                        range_owner(nGU, G, (tau + 1) * cprH - 1) - range_owner(nGU, G, tau * cprH) + 1;
+                    float g = 0.f, uu = 0.f;
+                    for (int sl = 0; sl < ncontrib; sl++) {
+                        const float *pp = a.part_gu + ((size_t)tau * a.slots_gu + sl) * 128;
+                        g += ld_x(pp + lane);
+                        uu += ld_x(pp + 64 + lane);
+                    }
+                    const int r = (int)(tau % tilesI) * kTileRows + lane;
+                    g *= (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
+                    uu *= (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
+                    const _Float16 hf = (_Float16)(g / (1.f + __expf(-g)) * uu);
+                    st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
+                }
+                wait_vm_all();
+                __syncthreads();
+                if (threadIdx.x == 0 && nj)
+                    __hip_atomic_fetch_add(h_ready + j, (unsigned)nj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ea = eb;
             }
-            (void)t_first;
         }
 
         mark(3);
@@ -619,11 +749,11 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 acc = wave_sum(acc);
                 if (lane == 0) st_x(a.ysh + r, acc);
             }
-            for (int td = shH0 / kTileRows; td <= (shH1 - 1) / kTileRows; td++) {
-                const unsigned old = wg_signal(cnt_d + td, bcast);
-                if ((old + 1) % tile_target(td, k, tilesH, cprI, nD, G, H, shared_on) == 0)
-                    combine_tile(td, s, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d, a.ysh, a.out, sw, sync, wave, lane, bcast);
-            }
+            wait_vm_all();
+            __syncthreads();
+            const int tdA = shH0 / kTileRows;
+            down_tiles_done(tdA, (shH1 - 1) / kTileRows - tdA + 1, s, k, tilesH, cprI, nD, G, H, shared_on, a.part_d,
+                            a.slots_d, a.ysh, a.out, sw, sync, cnt_d, (int *)(lds + LL.red_d), wave, lane);
         }
 
         mark(4);
@@ -636,27 +766,25 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             const long base = (long)j * tilesH * cprI;
             if (!stream_down((const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]),
                              (const uint32_t *)(a.hh + (size_t)j * I), sync, h_ready + j, (unsigned)(s + 1) * tilesI,
-                             bcast, H, I, cprI, ea - base, eb - base, ea / cprI - base / cprI, a.slots_red_d, wave,
+                             bcast, H, I, cprI, (int)(ea - base), (int)(eb - base), (int)(ea / cprI - base / cprI), a.slots_red_d, wave,
                              lane))
                 return;
             __syncthreads();
-            for (long tau = ea / cprI; tau <= (eb - 1) / cprI; tau++) {
-                const int td = (int)(tau % tilesH);
-                const int first = range_owner(nD, G, tau * cprI);
-                const int rs = (int)(tau - ea / cprI);
-                if (wave == 0) {
-                    float y = 0.f;
+            const long tA = ea / cprI;
+            const int nt = (int)((eb - 1) / cprI - tA) + 1;
+            for (int v = wave; v < nt; v += kPW) {
+                const long tau = tA + v;
+                float y = 0.f;
 #pragma unroll
-                    for (int v = 0; v < kPW; v++) y += red_d[(rs * kPW + v) * 64 + lane];
-                    const int r = td * kTileRows + lane;
-                    y *= (float)((const _Float16 *)(rec + a.off.scales[2]))[r];
-                    st_x(a.part_d + ((size_t)tau * a.slots_d + (w - first)) * 64 + lane, y);
-                }
-                const unsigned old = wg_signal(cnt_d + td, bcast);
-                if ((old + 1) % tile_target(td, k, tilesH, cprI, nD, G, H, shared_on) == 0)
-                    combine_tile(td, s, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d, a.ysh, a.out, sw,
-                                 sync, wave, lane, bcast);
+                for (int q = 0; q < kPW; q++) y += red_d[(v * kPW + q) * 64 + lane];
+                const int r = (int)(tau % tilesH) * kTileRows + lane;
+                y *= (float)((const _Float16 *)(rec + a.off.scales[2]))[r];
+                st_x(a.part_d + ((size_t)tau * a.slots_d + (w - range_owner(nD, G, tau * cprI))) * 64 + lane, y);
             }
+            wait_vm_all();
+            __syncthreads();
+            down_tiles_done((int)(tA % tilesH), nt, s, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d,
+                            a.ysh, a.out, sw, sync, cnt_d, (int *)(lds + LL.red_d), wave, lane);
             ea = eb;
         }
         mark(5);
