@@ -37,7 +37,7 @@ constexpr int kPW = 8;                 // waves per workgroup
 constexpr long kSpinLimit = 1L << 24;  // x ~0.1 us per poll: a few seconds
 constexpr int kDecLdsBytes = 160 * 1024;
 
-enum SyncIdx { kErr = 0, kRoute = 1, kLayerDone = 2, kHReady = 3 };   // h_ready[k+1] follows
+enum SyncIdx { kErr = 0, kLayerDone = 1, kHReady = 2 };   // h_ready[k+1] follows
 
 // Cross-workgroup data (logits, packed x, partial sums, h, shared-expert
 // vectors) is written and read with agent-scope relaxed atomic accesses,
@@ -75,6 +75,12 @@ __device__ __forceinline__ void stage_lds(char *dst, const void *src, int nbytes
 }
 
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// Wave-level coherent copy of one 64-float block (lane l: src[l]) into LDS at
+// dst (wave-uniform), written by other workgroups in this launch.
+__device__ __forceinline__ void dma_block(float *dst, const float *src, int lane) {
+    __builtin_amdgcn_global_load_lds((gvoid *)(src + lane), (lvoid *)dst, 4, 0, kLdsCoherent);
+}
 // Wait until all but this wave's N most recent vector memory operations
 // (and all its LDS operations) are done, then a plain workgroup barrier.
 // For LDS data only: __syncthreads() would also wait for the N loads still
@@ -94,9 +100,12 @@ __device__ __forceinline__ bool wg_wait(unsigned *sync, const unsigned *p, unsig
     if (threadIdx.x == 0) {
         long spins = 0;
         int ok = 1;
-        while (ld_cnt(p) < target) {
-            if (ld_cnt(sync + kErr)) { ok = 0; break; }
-            __builtin_amdgcn_s_sleep(2);
+        for (;;) {
+            // both loads in flight together: one memory round trip per poll
+            const unsigned c = ld_cnt(p), err = ld_cnt(sync + kErr);
+            if (c >= target) break;
+            if (err) { ok = 0; break; }
+            __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
                 __hip_atomic_store(sync + kErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
@@ -117,6 +126,35 @@ __device__ __forceinline__ void wg_signal(unsigned *p) {
     wait_vm_all();
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Values exchanged between workgroups inside a step carry the step: value
+// in the low and (step + 1) in the high half of one 64-bit word, stored and
+// loaded as a single atomic access.  A writer needs no wait and no counter;
+// a reader polls until every word it needs carries the current step, and has
+// the data in the same load.  (Buffers start zeroed, so tag 0 never matches;
+// the layer-done barrier keeps the next step from rewriting a word that a
+// reader of this step still polls.)
+__device__ __forceinline__ void st_tagged(uint64_t *p, float v, unsigned tag) {
+    __hip_atomic_store(p, (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_ok(uint64_t v, unsigned tag) { return (unsigned)(v >> 32) == tag; }
+__device__ __forceinline__ float tag_val(uint64_t v) { return __uint_as_float((unsigned)v); }
+
+// Wave-level bound on a poll loop: false (and the error flag set) after too
+// many polls, or once another workgroup has failed.
+__device__ __forceinline__ bool poll_more(unsigned *sync, long &spins) {
+    if (++spins > kSpinLimit) {
+        __hip_atomic_store(sync + kErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+    if ((spins & 31) == 0 && ld_cnt(sync + kErr)) return false;
+    __builtin_amdgcn_s_sleep(1);
+    return true;
 }
 
 // A space of n units is split over Ga = min(G, n) active workgroups into
@@ -276,6 +314,7 @@ __device__ __forceinline__ DecLds dec_lds_layout(int H, int I) {
     return L;
 }
 constexpr int kDecTail = kDecLdsBytes - 1024;     // sidx, sw, broadcast words, router partials
+constexpr int kDecRecs = kDecTail - 8 * MOE_MAX_E;   // the layer's record pointers, until top-k
 
 constexpr int kRingGU = 3;      // code buffers per wave (2 units in flight ahead)
 constexpr int kRingD = 4;       // (3 ahead)
@@ -332,16 +371,17 @@ __device__ __forceinline__ void d_unit(const uint32_t (&d)[12], const char *cb, 
 }
 
 // Gate and up of one expert: units [la, lb) (unit u = tile u / cpr, chunk
-// u % cpr; its codes are 3072 bytes at base + u * 3072).  Wave v takes units
-// la + v, la + v + kPW, ...; tile sums go to LDS slot (tile - t0).  The first
-// loads are issued before the codebooks (and, if stage_x, the x pairs) are
-// staged into LDS.  The steady-state loop has no branches around its loads:
+// u % cpr; its codes are 3072 bytes at base + u * 3072), against the x pairs
+// already in LDS.  Wave v takes units la + v, la + v + kPW, ...; tile sums go
+// to LDS slot (tile - t0).  The first code loads are issued together with
+// the staging of the codebooks.  The steady-state loop has no branches around its loads:
 // loads past the wave's last unit re-read that unit (their buffers are never
 // consumed), so every load of the ring stays in flight while older units are
 // computed.
 __device__ __forceinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *usec, const u32x4 *cbg_src,
-                                           const u32x4 *cbu_src, const uint32_t *xh_src, int stage_x, int H, int I,
-                                           int cpr, int la, int lb, int t0, int nslots, int wave, int lane) {
+                                           const u32x4 *cbu_src, int H, int I,
+                                           int cpr, int la, int lb, int t0, int nslots, int wave, int lane,
+                                           unsigned long long *stamp) {
     const DecLds L = dec_lds_layout(H, I);
     char *cbg = dec_lds, *cbu = dec_lds + kCbRows * 16;
     uint32_t *xl = (uint32_t *)(dec_lds + L.x_gu);
@@ -353,7 +393,6 @@ __device__ __forceinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *us
     // first code loads in flight
     stage_lds<kLdsPlain>(cbg, cbg_src, kCbRows * 16, wave, lane);
     stage_lds<kLdsPlain>(cbu, cbu_src, kCbRows * 16, wave, lane);
-    if (stage_x) stage_lds<kLdsCoherent>((char *)xl, xh_src, H * 2, wave, lane);
     // the code loads are issued after every staging copy (the fence keeps
     // that order), so waiting until only they are outstanding is enough to
     // see the staged data: the loop starts without waiting for them
@@ -370,6 +409,7 @@ __device__ __forceinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *us
     }
     wait_lds_barrier<(kRingGU - 1) * 2 * kStripLoads>();
     lds_barrier();
+    if (stamp && threadIdx.x == 0) stamp[kStampGuStaged] = wall_clock64();
     if (!n) return;
     float ag[4] = {0.f, 0.f, 0.f, 0.f}, au[4] = {0.f, 0.f, 0.f, 0.f};
     UnitPos p{first / cpr, first % cpr, first / cpr, 1.f / (float)cpr};
@@ -398,7 +438,8 @@ __device__ __forceinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *us
 // wait failed.
 __device__ __forceinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_src, const uint32_t *h_src, unsigned *sync,
                                         const unsigned *h_ready, unsigned h_target, int *bcast, int H, int I, int cpr,
-                                        int la, int lb, int t0, int nslots, int wave, int lane) {
+                                        int la, int lb, int t0, int nslots, int wave, int lane,
+                                        unsigned long long *stamp) {
     const DecLds L = dec_lds_layout(H, I);
     char *cb = dec_lds;
     uint32_t *xl = (uint32_t *)(dec_lds + L.x_d);
@@ -415,6 +456,7 @@ __device__ __forceinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_s
     stage_lds<kLdsCoherent>((char *)xl, h_src, I * 2, wave, lane);
     wait_vm_all();
     __syncthreads();
+    if (stamp && threadIdx.x == 0) stamp[kStampDownStaged] = wall_clock64();
     if (!n) return 1;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     UnitPos p{first / cpr, first % cpr, first / cpr, 1.f / (float)cpr};
@@ -433,65 +475,56 @@ __device__ __forceinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_s
     return 1;
 }
 
-// number of contributions an output tile of H receives per step
-__device__ __forceinline__ unsigned tile_target(int td, int k, int tilesH, int cprI, long nD, int G, int H, bool shared_on) {
-    unsigned n = 0;
-    for (int j = 0; j < k; j++) {
-        const long tau = (long)j * tilesH + td;
-        n += range_owner(nD, G, (tau + 1) * cprI - 1) - range_owner(nD, G, tau * cprI) + 1;
-    }
-    if (shared_on)
-        n += range_owner(H, G, (long)td * kTileRows + kTileRows - 1) - range_owner(H, G, (long)td * kTileRows) + 1;
-    return n;
+// Workgroup whose down range holds the last unit of output tile td in the
+// last rank: it combines the tile.
+__device__ __forceinline__ int combiner_of(int td, int k, int tilesH, int cprI, long nD, int G) {
+    return range_owner(nD, G, ((long)(k - 1) * tilesH + td + 1) * cprI - 1);
 }
 
-// Output tile td, by one wave of the workgroup that made its last
-// contribution: out = sum_j w_j * sum_slots y_j + shared, in fixed (rank,
-// contributor) order.
-__device__ __forceinline__ void combine_rows(int td, int s, int k, int tilesH, int cprI, long nD, int G, int H,
-                                             bool shared_on, const float *part_d, int slots_d, const float *ysh,
-                                             float *out, const float *sw, int lane) {
+// Output tile td, by one wave: out = sum_j w_j * sum_slots y_j + shared, in
+// fixed (rank, contributor) order, from tagged partials (polled until every
+// contribution of this step is there).  Returns false on a failed wait.
+__device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k, int tilesH, int cprI, long nD,
+                                             int G, int H, bool shared_on, const uint64_t *part_d, int slots_d,
+                                             const uint64_t *ysh, float *out, const float *sw, unsigned *sync,
+                                             int lane) {
     const int r = td * kTileRows + lane;
     float o = 0.f;
+    long spins = 0;
     for (int j = 0; j < k; j++) {
         const long tau = (long)j * tilesH + td;
-        const int first = range_owner(nD, G, tau * cprI);
-        const int last = range_owner(nD, G, (tau + 1) * cprI - 1);
+        const int cnt = range_owner(nD, G, (tau + 1) * cprI - 1) - range_owner(nD, G, tau * cprI) + 1;
+        const uint64_t *pp = part_d + (size_t)tau * slots_d * 64 + lane;
         float y = 0.f;
-        for (int sl = 0; sl <= last - first; sl++) y += ld_x(part_d + ((size_t)tau * slots_d + sl) * 64 + lane);
+        for (int s0 = 0; s0 < cnt; s0 += 4) {
+            uint64_t v[4];
+            for (;;) {
+                bool ok = true;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    v[q] = ld_tagged(pp + (size_t)min(s0 + q, cnt - 1) * 64);
+                    ok = ok && tag_ok(v[q], tag);
+                }
+                if (__all(ok)) break;
+                if (!poll_more(sync, spins)) return false;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                if (s0 + q < cnt) y += tag_val(v[q]);
+        }
         o = fmaf(sw[j], y, o);
     }
-    if (shared_on) o += ld_x(ysh + r);
+    if (shared_on) {
+        uint64_t v;
+        for (;;) {
+            v = ld_tagged(ysh + r);
+            if (__all(tag_ok(v, tag))) break;
+            if (!poll_more(sync, spins)) return false;
+        }
+        o += tag_val(v);
+    }
     out[(size_t)s * H + r] = o;
-}
-
-// Counts this workgroup's contribution to each output tile in [tdA, tdA + nt)
-// (its data stored and waited for, the workgroup synchronised), then
-// combines the tiles it completed, one wave per tile, and adds their number
-// to the layer-done counter.  All counter updates of the call are issued
-// together, so the call costs a few memory round trips whatever nt is.
-// flag: LDS scratch of nt ints.
-__device__ __forceinline__ void down_tiles_done(int tdA, int nt, int s, int k, int tilesH, int cprI, long nD, int G,
-                                                int H, bool shared_on, const float *part_d, int slots_d,
-                                                const float *ysh, float *out, const float *sw, unsigned *sync,
-                                                unsigned *cnt_d, int *flag, int wave, int lane) {
-    for (int v = threadIdx.x; v < nt; v += kPW * 64) {
-        const int td = tdA + v;
-        const unsigned old = __hip_atomic_fetch_add(cnt_d + td, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        flag[v] = (old + 1) % tile_target(td, k, tilesH, cprI, nD, G, H, shared_on) == 0;
-    }
-    __syncthreads();
-    int nc = 0;
-    for (int v = 0; v < nt; v++) {
-        if (!flag[v]) continue;
-        if (v % kPW == wave)
-            combine_rows(tdA + v, s, k, tilesH, cprI, nD, G, H, shared_on, part_d, slots_d, ysh, out, sw, lane);
-        ++nc;
-    }
-    wait_vm_all();
-    __syncthreads();
-    if (threadIdx.x == 0 && nc)
-        __hip_atomic_fetch_add(sync + kLayerDone, (unsigned)nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
 }
 
 struct DecArgs {
@@ -503,16 +536,15 @@ struct DecArgs {
     int32_t *idx_out;        // [T, nL, k] or null
     RecOffsets off;
     unsigned *sync;          // counters
-    float *z;                // [E_max]
-    uint32_t *xh;            // [H/2]
+    uint64_t *z;             // [E_max] tagged logits
     uint16_t *hh;            // [k][I] fp16 h per rank
     float *hs;               // [I] shared h
-    float *ysh;              // [H] shared y
-    float *part_gu;          // [k*tilesI][slots_gu][128]
-    float *part_d;           // [k*tilesH][slots_d][64]
+    uint64_t *ysh;           // [H] tagged shared y
+    uint64_t *part_gu;       // [k*tilesI][slots_gu][128] tagged
+    uint64_t *part_d;        // [k*tilesH][slots_d][64] tagged
     int slots_gu, slots_d;
     int slots_red_gu, slots_red_d;   // tiles one workgroup's range can touch (LDS sum slots)
-    unsigned long long *stamps;   // optional phase timestamps [steps][G][6], or null
+    unsigned long long *stamps;   // optional phase timestamps [steps][G][kDecStamps], or null
     int stamp_steps;
 };
 
@@ -525,6 +557,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
     float *sw = (float *)(sidx + MOE_MAX_K);                    // [MOE_MAX_K]
     int *bcast = (int *)(sw + MOE_MAX_K);                       // [4]
     float *red = (float *)(bcast + 4);                          // [kPW] router partials
+    uint64_t *recs = (uint64_t *)(red + kPW);                   // [MOE_MAX_K] records of the chosen experts
+    uint64_t *recs_all = (uint64_t *)(lds + kDecRecs);          // [E] until top-k
 
     const int G = a.G, w = blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -536,8 +570,6 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
     const long d0 = range_start(nD, G, w), d1 = range_start(nD, G, w + 1);
     unsigned *sync = a.sync;
     unsigned *h_ready = sync + kHReady;                          // [k+1]
-    unsigned *cnt_gu = h_ready + (k + 1);                        // [k*tilesI]
-    unsigned *cnt_d = cnt_gu + k * tilesI;                       // [tilesH]
     const int steps = a.T * a.nL;
     // shared-expert row ranges
     const int shI0 = (int)range_start(I, G, w), shI1 = (int)range_start(I, G, w + 1);
@@ -549,15 +581,20 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         if (stamp && threadIdx.x == 0) stamp[i] = wall_clock64();
     };
     for (int s = 0; s < steps; s++) {
-        stamp = (a.stamps && s < a.stamp_steps) ? a.stamps + ((size_t)s * G + w) * 6 : nullptr;
-        mark(0);
+        stamp = (a.stamps && s < a.stamp_steps) ? a.stamps + ((size_t)s * G + w) * kDecStamps : nullptr;
+        mark(kStampStart);
         const int t = s / a.nL, L = s % a.nL;
         const DecLayer lay = a.layers[L];   // device memory, uniform
         const float *xs = a.x + ((size_t)t * a.nL + L) * H;
         const int E = lay.E, nE = min(E, G);
         const bool shared_on = a.has_shared && lay.shared;
+        // the layer's record pointers, loaded while waiting (the table is
+        // fixed during the launch): the chosen experts' loads can start right
+        // after top-k
+        for (int e = threadIdx.x; e < E; e += kPW * 64) recs_all[e] = (uint64_t)lay.records[e];
         if (s > 0 && !wg_wait(sync, sync + kLayerDone, (unsigned)s * tilesH, bcast)) return;
-        mark(1);
+        if (s == 0) __syncthreads();
+        mark(kStampLayerWait);
 
         // ---- shared gate/up (independent of routing)
         if (shared_on) {
@@ -584,17 +621,37 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             if (shI1 > shI0) wg_signal(h_ready + k);
         }
 
-        // ---- route: logits of rows e = w, w + G, ... ; workgroup 0 also packs x
+        const unsigned tag = (unsigned)s + 1;
+
+        // ---- x as fp16 pairs into LDS (every workgroup, for gate/up)
+        {
+            uint32_t *xl = (uint32_t *)(lds + LL.x_gu);
+            for (int i = threadIdx.x; i < H / 2; i += kPW * 64) {
+                const float2 xv = *(const float2 *)(xs + 2 * i);
+                xl[i] = pack_f16x2(xv.x, xv.y);
+            }
+        }
+
+        // ---- route: logits of rows e = w, w + G, ... (tagged, no counter)
         if (w < nE) {
             for (int e = w; e < E; e += G) {
                 const float *wr = lay.W + (size_t)e * H;
                 float acc = 0.f;
-                for (int c = threadIdx.x * 4; c < H; c += kPW * 64 * 4) {
-                    const float4 wv = *(const float4 *)(wr + c), xv = *(const float4 *)(xs + c);
-                    acc = fmaf(wv.x, xv.x, acc);
-                    acc = fmaf(wv.y, xv.y, acc);
-                    acc = fmaf(wv.z, xv.z, acc);
-                    acc = fmaf(wv.w, xv.w, acc);
+                for (int c0 = threadIdx.x * 4; c0 < H; c0 += 2 * kPW * 64 * 4) {
+                    // two chunks' loads in flight together
+                    const int c1 = c0 + kPW * 64 * 4;
+                    const float4 w0 = *(const float4 *)(wr + c0), x0 = *(const float4 *)(xs + c0);
+                    const bool two = c1 < H;
+                    const float4 w1 = two ? *(const float4 *)(wr + c1) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const float4 x1 = two ? *(const float4 *)(xs + c1) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    acc = fmaf(w0.x, x0.x, acc);
+                    acc = fmaf(w0.y, x0.y, acc);
+                    acc = fmaf(w0.z, x0.z, acc);
+                    acc = fmaf(w0.w, x0.w, acc);
+                    acc = fmaf(w1.x, x1.x, acc);
+                    acc = fmaf(w1.y, x1.y, acc);
+                    acc = fmaf(w1.z, x1.z, acc);
+                    acc = fmaf(w1.w, x1.w, acc);
                 }
                 acc = wave_sum(acc);
                 __syncthreads();
@@ -603,134 +660,159 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 if (threadIdx.x == 0) {
                     float z = 0.f;
                     for (int v = 0; v < kPW; v++) z += red[v];
-                    st_x(a.z + e, z + (lay.bias ? lay.bias[e] : 0.f));
+                    st_tagged(a.z + e, z + (lay.bias ? lay.bias[e] : 0.f), tag);
                 }
             }
-            if (w == 0)
-                for (int i = threadIdx.x; i < H / 2; i += kPW * 64) st_x(a.xh + i, pack_f16x2(xs[2 * i], xs[2 * i + 1]));
-            wg_signal(sync + kRoute);
         }
-        if (!wg_wait(sync, sync + kRoute, (unsigned)(s + 1) * nE, bcast)) return;
-        mark(2);
 
-        // ---- top-k (every workgroup, wave 0): k rounds of a wave argmax over
-        // (logit desc, expert id asc)
+        // ---- top-k (every workgroup, wave 0): poll the tagged logits, then k
+        // rounds of a wave argmax over (logit desc, expert id asc)
         if (wave == 0) {
             float v[MOE_MAX_E / 64];
-#pragma unroll
-            for (int i = 0; i < MOE_MAX_E / 64; i++) {
-                const int e = lane + 64 * i;
-                const float zz = e < E ? ld_x(a.z + e) : -INFINITY;
-                v[i] = zz == zz ? zz : -INFINITY;
-            }
-            uint32_t taken = 0;
-            float zmax = 0.f, sum = 0.f, mine = 0.f;
-            int emine = 0;
-            for (int j = 0; j < lay.k; j++) {
-                float bv = -INFINITY;
-                int be = 0x7FFFFFFF;
+            long spins = 0;
+            bool okw = true;
+            for (;;) {
+                bool ok = true;
 #pragma unroll
                 for (int i = 0; i < MOE_MAX_E / 64; i++) {
                     const int e = lane + 64 * i;
-                    if (e < E && !(taken >> i & 1u) && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
+                    if (e < E) {
+                        const uint64_t zz = ld_tagged(a.z + e);
+                        ok = ok && tag_ok(zz, tag);
+                        const float f = tag_val(zz);
+                        v[i] = f == f ? f : -INFINITY;
+                    } else {
+                        v[i] = -INFINITY;
+                    }
                 }
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) {
-                    const float ov = __shfl_xor(bv, o, 64);
-                    const int oe = __shfl_xor(be, o, 64);
-                    if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-                }
-                if (j == 0) zmax = bv;
-                const float sc = lay.score_fn == MOE_SCORE_SOFTMAX ? __expf(bv - zmax) : 1.f / (1.f + __expf(-bv));
-                sum += sc;
-                if (lane == j) { mine = sc; emine = be; }
-                if ((be & 63) == lane) taken |= 1u << (be >> 6);
+                if (__all(ok)) break;
+                if (!poll_more(sync, spins)) { okw = false; break; }
             }
-            if (lane < lay.k) {
-                sidx[lane] = emine;
-                sw[lane] = mine / sum;
-                if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = emine;
+            if (lane == 0) *bcast = okw;
+            if (okw) {
+                uint32_t taken = 0;
+                float zmax = 0.f, sum = 0.f, mine = 0.f;
+                int emine = 0;
+                for (int j = 0; j < lay.k; j++) {
+                    float bv = -INFINITY;
+                    int be = 0x7FFFFFFF;
+#pragma unroll
+                    for (int i = 0; i < MOE_MAX_E / 64; i++) {
+                        const int e = lane + 64 * i;
+                        if (e < E && !(taken >> i & 1u) && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
+                    }
+#pragma unroll
+                    for (int o = 32; o > 0; o >>= 1) {
+                        const float ov = __shfl_xor(bv, o, 64);
+                        const int oe = __shfl_xor(be, o, 64);
+                        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+                    }
+                    if (j == 0) zmax = bv;
+                    const float sc = lay.score_fn == MOE_SCORE_SOFTMAX ? __expf(bv - zmax) : 1.f / (1.f + __expf(-bv));
+                    sum += sc;
+                    if (lane == j) { mine = sc; emine = be; }
+                    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+                }
+                if (lane < lay.k) {
+                    sidx[lane] = emine;
+                    sw[lane] = mine / sum;
+                    recs[lane] = recs_all[emine];
+                    if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = emine;
+                }
             }
         }
         __syncthreads();
+        if (!*bcast) return;
+        mark(kStampRouted);
 
         // ---- gate/up over this workgroup's range of (rank, tile, chunk), one
         // expert segment at a time (a range spans at most two experts)
-        {
-            bool x_staged = false;
-            for (long ea = gu0; ea < gu1;) {
-                const int j = (int)(ea / ((long)tilesI * cprH));
-                const long eb = min(gu1, (long)(j + 1) * tilesI * cprH);
-                const uint8_t *rec = (const uint8_t *)lay.records[sidx[j]];
-                const long base = (long)j * tilesI * cprH;       // expert-local units
-                stream_gateup((const u32x4 *)(rec + a.off.codes[0]), (const u32x4 *)(rec + a.off.codes[1]),
-                              (const u32x4 *)(rec + a.off.cb[0]), (const u32x4 *)(rec + a.off.cb[1]), a.xh,
-                              x_staged ? 0 : 1, H, I, cprH, (int)(ea - base), (int)(eb - base), (int)(ea / cprH - base / cprH),
-                              a.slots_red_gu, wave, lane);
-                x_staged = true;
-                __syncthreads();
-                // one partial per touched tile (wave v: tiles v, v + kPW, ...);
-                // then every tile's counter at once; the tiles this workgroup
-                // completed are joined (one wave each) into fp16 SiLU(g) * u
-                const long tA = ea / cprH;
-                const int nt = (int)((eb - 1) / cprH - tA) + 1;
-                for (int v = wave; v < nt; v += kPW) {
-                    const long tau = tA + v;
-                    const int slot = w - range_owner(nGU, G, tau * cprH);
-                    float g = 0.f, uu = 0.f;
+        for (long ea = gu0; ea < gu1;) {
+            const int j = (int)(ea / ((long)tilesI * cprH));
+            const long eb = min(gu1, (long)(j + 1) * tilesI * cprH);
+            const uint8_t *rec = (const uint8_t *)recs[j];
+            const long base = (long)j * tilesI * cprH;       // expert-local units
+            stream_gateup((const u32x4 *)(rec + a.off.codes[0]), (const u32x4 *)(rec + a.off.codes[1]),
+                          (const u32x4 *)(rec + a.off.cb[0]), (const u32x4 *)(rec + a.off.cb[1]), H, I, cprH,
+                          (int)(ea - base), (int)(eb - base), (int)(ea / cprH - base / cprH), a.slots_red_gu, wave,
+                          lane, stamp);
+            __syncthreads();
+            mark(kStampGuLoop);
+            // one tagged partial per touched tile (wave v: tiles v, v + kPW,
+            // ...); the workgroup owning a tile's last unit joins it (one
+            // wave per tile) into fp16 SiLU(g) * u once every contributor's
+            // partial of this step is there
+            const long tA = ea / cprH;
+            const int nt = (int)((eb - 1) / cprH - tA) + 1;
+            for (int v = wave; v < nt; v += kPW) {
+                const long tau = tA + v;
+                const int slot = w - range_owner(nGU, G, tau * cprH);
+                float g = 0.f, uu = 0.f;
 #pragma unroll
-                    for (int q = 0; q < kPW; q++) {
-                        g += red_gu[(v * kPW + q) * 128 + lane];
-                        uu += red_gu[(v * kPW + q) * 128 + 64 + lane];
-                    }
-                    float *p = a.part_gu + ((size_t)tau * a.slots_gu + slot) * 128;
-                    st_x(p + lane, g);
-                    st_x(p + 64 + lane, uu);
+                for (int q = 0; q < kPW; q++) {
+                    g += red_gu[(v * kPW + q) * 128 + lane];
+                    uu += red_gu[(v * kPW + q) * 128 + 64 + lane];
                 }
-                wait_vm_all();
-                __syncthreads();
-                int *flag = (int *)(lds + LL.red_gu);
-                for (int v = threadIdx.x; v < nt; v += kPW * 64) {
-                    const long tau = tA + v;
-                    const int ncontrib =
-                        range_owner(nGU, G, (tau + 1) * cprH - 1) - range_owner(nGU, G, tau * cprH) + 1;
-                    const unsigned old =
-                        __hip_atomic_fetch_add(cnt_gu + tau, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    flag[v] = (old + 1) % (unsigned)ncontrib == 0;
-                }
-                __syncthreads();
-                int nj = 0;
-                for (int v = 0; v < nt; v++) {
-                    if (!flag[v]) continue;
-                    ++nj;
-                    if (v % kPW != wave) continue;
-                    const long tau = tA + v;
-                    const int ncontrib =
-                        range_owner(nGU, G, (tau + 1) * cprH - 1) - range_owner(nGU, G, tau * cprH) + 1;
-                    float g = 0.f, uu = 0.f;
-                    for (int sl = 0; sl < ncontrib; sl++) {
-                        const float *pp = a.part_gu + ((size_t)tau * a.slots_gu + sl) * 128;
-                        g += ld_x(pp + lane);
-                        uu += ld_x(pp + 64 + lane);
-                    }
-                    const int r = (int)(tau % tilesI) * kTileRows + lane;
-                    g *= (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
-                    uu *= (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
-                    const _Float16 hf = (_Float16)(g / (1.f + __expf(-g)) * uu);
-                    st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
-                }
-                wait_vm_all();
-                __syncthreads();
-                if (threadIdx.x == 0 && nj)
-                    __hip_atomic_fetch_add(h_ready + j, (unsigned)nj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ea = eb;
+                uint64_t *p = a.part_gu + ((size_t)tau * a.slots_gu + slot) * 128;
+                st_tagged(p + lane, g, tag);
+                st_tagged(p + 64 + lane, uu, tag);
             }
+            int nj = 0;
+            bool okj = true;
+            for (int v = 0; v < nt; v++) {
+                const long tau = tA + v;
+                if (range_owner(nGU, G, (tau + 1) * cprH - 1) != w) continue;
+                if (nj++ % kPW != wave) continue;
+                const int first = range_owner(nGU, G, tau * cprH), ncontrib = w - first + 1;
+                const int r = (int)(tau % tilesI) * kTileRows + lane;
+                const float sg = (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
+                const float su = (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
+                const uint64_t *pp = a.part_gu + (size_t)tau * a.slots_gu * 128 + lane;
+                float g = 0.f, uu = 0.f;
+                long spins = 0;
+                for (int s0 = 0; s0 < ncontrib && okj; s0 += 4) {
+                    uint64_t vg[4], vu[4];
+                    for (;;) {
+                        bool ok = true;
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            const size_t o = (size_t)min(s0 + q, ncontrib - 1) * 128;
+                            vg[q] = ld_tagged(pp + o);
+                            vu[q] = ld_tagged(pp + o + 64);
+                            ok = ok && tag_ok(vg[q], tag) && tag_ok(vu[q], tag);
+                        }
+                        if (__all(ok)) break;
+                        if (!poll_more(sync, spins)) { okj = false; break; }
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        if (s0 + q < ncontrib) {
+                            g += tag_val(vg[q]);
+                            uu += tag_val(vu[q]);
+                        }
+                }
+                g *= sg;
+                uu *= su;
+                const _Float16 hf = (_Float16)(g / (1.f + __expf(-g)) * uu);
+                st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
+            }
+            if (lane == 0 && !okj) *bcast = 0;
+            wait_vm_all();
+            __syncthreads();
+            if (!*bcast) return;
+            if (threadIdx.x == 0 && nj)
+                __hip_atomic_fetch_add(h_ready + j, (unsigned)nj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ea = eb;
         }
 
-        mark(3);
-        // ---- shared down rows (after the whole shared h is ready)
+        mark(kStampGuDone);
+        // ---- shared down rows (after the whole shared h is ready), tagged
         if (shared_on && shH1 > shH0) {
             if (!wg_wait(sync, h_ready + k, (unsigned)(s + 1) * sh_gu_contrib, bcast)) return;
+            float *hl = (float *)lds;                                   // [I]
+            for (int b = wave; b * 64 < I; b += kPW) dma_block(hl + b * 64, a.hs + b * 64, lane);
+            wait_vm_all();
+            __syncthreads();
             for (int r = shH0 + wave; r < shH1; r += kPW) {
                 const uint16_t *wd = lay.shared + 2 * (size_t)I * H + (size_t)r * I;
                 float acc = 0.f;
@@ -738,7 +820,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     const uint4 dv = *(const uint4 *)(wd + c);
                     float hv[8];
 #pragma unroll
-                    for (int i = 0; i < 8; i++) hv[i] = ld_x(a.hs + c + i);
+                    for (int i = 0; i < 8; i++) hv[i] = hl[c + i];
                     const uint32_t q[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
@@ -747,29 +829,26 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     }
                 }
                 acc = wave_sum(acc);
-                if (lane == 0) st_x(a.ysh + r, acc);
+                if (lane == 0) st_tagged(a.ysh + r, acc, tag);
             }
-            wait_vm_all();
             __syncthreads();
-            const int tdA = shH0 / kTileRows;
-            down_tiles_done(tdA, (shH1 - 1) / kTileRows - tdA + 1, s, k, tilesH, cprI, nD, G, H, shared_on, a.part_d,
-                            a.slots_d, a.ysh, a.out, sw, sync, cnt_d, (int *)(lds + LL.red_d), wave, lane);
         }
 
-        mark(4);
+        mark(kStampSharedDown);
         // ---- down over this workgroup's range of (rank, tile of H, chunk),
-        // one expert segment at a time
+        // one expert segment at a time: tagged partials per touched tile
         for (long ea = d0; ea < d1;) {
             const int j = (int)(ea / ((long)tilesH * cprI));
             const long eb = min(d1, (long)(j + 1) * tilesH * cprI);
-            const uint8_t *rec = (const uint8_t *)lay.records[sidx[j]];
+            const uint8_t *rec = (const uint8_t *)recs[j];
             const long base = (long)j * tilesH * cprI;
             if (!stream_down((const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]),
                              (const uint32_t *)(a.hh + (size_t)j * I), sync, h_ready + j, (unsigned)(s + 1) * tilesI,
-                             bcast, H, I, cprI, (int)(ea - base), (int)(eb - base), (int)(ea / cprI - base / cprI), a.slots_red_d, wave,
-                             lane))
+                             bcast, H, I, cprI, (int)(ea - base), (int)(eb - base), (int)(ea / cprI - base / cprI),
+                             a.slots_red_d, wave, lane, stamp))
                 return;
             __syncthreads();
+            mark(kStampDownLoop);
             const long tA = ea / cprI;
             const int nt = (int)((eb - 1) / cprI - tA) + 1;
             for (int v = wave; v < nt; v += kPW) {
@@ -779,15 +858,36 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 for (int q = 0; q < kPW; q++) y += red_d[(v * kPW + q) * 64 + lane];
                 const int r = (int)(tau % tilesH) * kTileRows + lane;
                 y *= (float)((const _Float16 *)(rec + a.off.scales[2]))[r];
-                st_x(a.part_d + ((size_t)tau * a.slots_d + (w - range_owner(nD, G, tau * cprI))) * 64 + lane, y);
+                st_tagged(a.part_d + ((size_t)tau * a.slots_d + (w - range_owner(nD, G, tau * cprI))) * 64 + lane, y,
+                          tag);
             }
-            wait_vm_all();
             __syncthreads();
-            down_tiles_done((int)(tA % tilesH), nt, s, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d,
-                            a.ysh, a.out, sw, sync, cnt_d, (int *)(lds + LL.red_d), wave, lane);
             ea = eb;
         }
-        mark(5);
+
+        // ---- output tiles this workgroup combines (one wave each), then
+        // their count on the layer-done counter
+        {
+            int nc = 0;
+            bool okc = true;
+            // candidates: the last rank's tiles that this workgroup's range touches
+            const long lb0 = (long)(k - 1) * tilesH * cprI;
+            const int tdA = d1 > lb0 ? (int)((max(d0, lb0) - lb0) / cprI) : tilesH;
+            const int tdB = d1 > lb0 ? (int)((d1 - 1 - lb0) / cprI) : -1;
+            for (int td = tdA; td <= tdB; td++) {
+                if (combiner_of(td, k, tilesH, cprI, nD, G) != w) continue;
+                if (nc++ % kPW == wave && okc)
+                    okc = combine_tile(td, s, tag, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d, a.ysh,
+                                       a.out, sw, sync, lane);
+            }
+            if (lane == 0 && !okc) *bcast = 0;
+            wait_vm_all();
+            __syncthreads();
+            if (!*bcast) return;
+            if (threadIdx.x == 0 && nc)
+                __hip_atomic_fetch_add(sync + kLayerDone, (unsigned)nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        mark(kStampDownDone);
     }
 }
 
@@ -814,12 +914,6 @@ size_t decode_lds() { return kDecLdsBytes; }
 }  // namespace
 
 // ---------------------------------------------------------------- host side
-struct DecodePlan {
-    int G;
-    int slots_gu, slots_d;
-    size_t sync_words;
-};
-
 static long h_range_start(long n, int G, int w) {
     const int Ga = (int)std::min<long>(n, G);
     return w >= Ga ? n : n * w / Ga;
@@ -870,17 +964,19 @@ hipError_t decode_plan(int H, int I, int k, DecodePlanOut *o) {
     o->slots_d = max_contributors((long)k * tilesH, cprI, G);
     o->slots_red_gu = max_tiles_per_range((long)k * tilesI, cprH, G);
     o->slots_red_d = max_tiles_per_range((long)k * tilesH, cprI, G);
-    o->sync_words = 3 + (size_t)(k + 1) + (size_t)k * tilesI + tilesH;
+    o->sync_words = kHReady + (size_t)(k + 1);
     // LDS: both phases' layouts must fit below the routing tail
     const long red_gu = 2L * kCbRows * 16 + ((H * 2 + 255) & ~255) + (long)o->slots_red_gu * kPW * 128 * 4;
     const long red_d = (long)kCbRows * 16 + ((I * 2 + 255) & ~255) + (long)o->slots_red_d * kPW * 64 * 4;
-    o->lds_ok = red_gu <= kDecTail && red_d <= kDecTail;
+    // the shared expert's fp32 h is staged below the record pointers
+    o->lds_ok = red_gu <= kDecTail && red_d <= kDecTail && (long)I * 4 <= kDecRecs;
     return hipSuccess;
 }
 
 hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s) {
     const int tilesI = d.I / kTileRows, tilesH = d.H / kTileRows;
-    k_fill_u32<<<1, 256, 0, s>>>(d.sync, d.sync_words);
+    const unsigned fill_blocks = (unsigned)std::min<size_t>(1024, (d.clear_words + 255) / 256);
+    k_fill_u32<<<fill_blocks, 256, 0, s>>>(d.sync, d.clear_words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     DecArgs a{};
@@ -905,7 +1001,6 @@ hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s) {
     a.off = d.off;
     a.sync = d.sync;
     a.z = d.z;
-    a.xh = d.xh;
     a.hh = d.hh;
     a.hs = d.hs;
     a.ysh = d.ysh;

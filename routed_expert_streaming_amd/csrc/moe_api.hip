@@ -273,19 +273,17 @@ namespace {
 struct DecodeWs {
     unsigned *sync;
     DecLayer *layers;
-    float *z;
-    uint32_t *xh;
+    uint64_t *z, *ysh, *part_gu, *part_d;
     uint16_t *hh;
-    float *hs, *ysh, *part_gu, *part_d;
+    float *hs;
     unsigned long long *stamps;
     int stamp_steps;
     int G, slots_gu, slots_d, slots_red_gu, slots_red_d;
-    size_t sync_words, bytes;
+    size_t sync_words, clear_words, bytes;
 };
 
 // Profiling aid: MOE_DECODE_STAMPS=<n> makes the decode workspace end with
-// n steps x G workgroups x 6 wall-clock stamps (step start, previous layer
-// done, routing done, gate/up done, shared down done, down done).
+// n steps x G workgroups x kDecStamps wall-clock stamps (see DecStamp).
 int decode_stamp_steps() {
     const char *e = getenv("MOE_DECODE_STAMPS");
     return e ? std::max(0, atoi(e)) : 0;
@@ -310,17 +308,19 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
     D->slots_red_d = P.slots_red_d;
     D->sync_words = P.sync_words;
     Carver c(ws);
+    // zeroed before every launch: the counters (word 0 is the error flag
+    // that moe_decode_status reads), then the step-tagged buffers
     D->sync = c.take<unsigned>(D->sync_words);
+    D->z = c.take<uint64_t>((size_t)E_max);
+    D->ysh = c.take<uint64_t>((size_t)H);
+    D->part_gu = c.take<uint64_t>((size_t)k * (I / 64) * D->slots_gu * 128);
+    D->part_d = c.take<uint64_t>((size_t)k * (H / 64) * D->slots_d * 64);
+    D->clear_words = c.pos / 4;
     D->layers = c.take<DecLayer>(kDecMaxLayers);
-    D->z = c.take<float>((size_t)E_max);
-    D->xh = c.take<uint32_t>((size_t)H / 2);
     D->hh = c.take<uint16_t>((size_t)k * I);
     D->hs = c.take<float>((size_t)I);
-    D->ysh = c.take<float>((size_t)H);
-    D->part_gu = c.take<float>((size_t)k * (I / 64) * D->slots_gu * 128);
-    D->part_d = c.take<float>((size_t)k * (H / 64) * D->slots_d * 64);
     D->stamp_steps = decode_stamp_steps();
-    D->stamps = D->stamp_steps ? c.take<unsigned long long>((size_t)D->stamp_steps * D->G * 6) : nullptr;
+    D->stamps = D->stamp_steps ? c.take<unsigned long long>((size_t)D->stamp_steps * D->G * kDecStamps) : nullptr;
     D->bytes = (size_t)align_up((int64_t)c.pos, 256);
     (void)shared;
     return MOE_OK;
@@ -361,10 +361,9 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
     d.G = D.G;
     d.off = offsets_of(H, I);
     d.sync = D.sync;
-    d.sync_words = D.sync_words;
+    d.clear_words = D.clear_words;
     d.layer_buf = D.layers;
     d.z = D.z;
-    d.xh = D.xh;
     d.hh = D.hh;
     d.hs = D.hs;
     d.ysh = D.ysh;

@@ -72,6 +72,21 @@ int down_splits(int H, int I, int n_items);
 
 // ---- persistent decode (kernels_decode.hip) ----------------------------------
 constexpr int kDecMaxLayers = 40;   // layer descriptors carried in one launch's arguments
+// Optional per-(step, workgroup) wall-clock stamps of the decode kernel
+// (profiling aid), in this order:
+enum DecStamp {
+    kStampStart,        // step begins
+    kStampLayerWait,    // previous step's outputs all written
+    kStampRouted,       // top-k known
+    kStampGuStaged,     // gate/up codebooks and x in LDS (last segment)
+    kStampGuLoop,       // gate/up streaming done (last segment)
+    kStampGuDone,       // gate/up partials joined
+    kStampSharedDown,   // shared-expert down rows done
+    kStampDownStaged,   // h and the down codebook in LDS (last segment)
+    kStampDownLoop,     // down streaming done (last segment)
+    kStampDownDone,     // down partials and output tiles done
+    kDecStamps
+};
 
 struct DecLayer {
     const float *W;
@@ -89,12 +104,12 @@ struct DecodeLaunch {
     int32_t *idx_out;
     RecOffsets off;
     unsigned *sync;
-    size_t sync_words;
+    size_t clear_words;      // 32-bit words from sync on that are zeroed before the launch
+                             // (the counters and every step-tagged buffer)
     DecLayer *layer_buf;     // [kDecMaxLayers] device copy of the descriptors
-    float *z;
-    uint32_t *xh;
+    uint64_t *z, *ysh, *part_gu, *part_d;   // step-tagged exchange buffers
     uint16_t *hh;
-    float *hs, *ysh, *part_gu, *part_d;
+    float *hs;
     int slots_gu, slots_d;
     int slots_red_gu, slots_red_d;
     unsigned long long *stamps;   // phase timestamps (profiling aid), or null
