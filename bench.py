@@ -18,7 +18,6 @@ from __future__ import annotations
 import argparse
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -28,16 +27,45 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per decode launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# (each scaled by the same counter on a 1 GiB device copy; the runs and the
+# factors are in profiles/k_decode_persistent_mixtral_hbm_counters.txt),
+# valid for the kernel source they were taken on: reported as null once that
+# source has changed.
+DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
+                  "sha256_prefix": "4432cf8e0152a642", "bytes_per_launch": 4713669043}
+
+
+def measured_traffic():
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, DECODE_TRAFFIC["kernel_source"]), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return DECODE_TRAFFIC["bytes_per_launch"] if digest.startswith(DECODE_TRAFFIC["sha256_prefix"]) else None
+
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
 def git_commit() -> str:
+    """HEAD read from the .git directory (no child process: under a profiler a
+    child inherits the profiler's preloaded library)."""
     try:
-        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
-                              text=True, timeout=10).stdout.strip() or "unknown"
-    except Exception:
+        head = open(os.path.join(ROOT, ".git", "HEAD")).read().strip()
+        if head.startswith("ref: "):
+            ref = head[5:]
+            path = os.path.join(ROOT, ".git", ref)
+            if os.path.exists(path):
+                return open(path).read().strip()[:7]
+            for line in open(os.path.join(ROOT, ".git", "packed-refs")):
+                if line.rstrip().endswith(" " + ref):
+                    return line.split()[0][:7]
+            return "unknown"
+        return head[:7]
+    except OSError:
         return "unknown"
 
 
@@ -81,6 +109,9 @@ def main() -> int:
                          "per step; k3_slice: streamed decode through the HBM slot cache (cold start)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (reference for the HBM byte "
+                         "counters FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
@@ -98,6 +129,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "repeats": 3}))
+        return 0
     cfg = synth.get_config(args.config)
     if args.config == "batched":
         return bench_batched(args, cfg)
@@ -158,8 +198,10 @@ def main() -> int:
         "expert_hbm_frac": round(bytes_tok * tok_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode step (route, RVQ gate/up, RVQ down, combine over all layers)",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if cfg.name == "mixtral" else None,
+                     "kernel": "k_decode_persistent (route, top-k, RVQ gate/up, RVQ down, combine; all layers of "
+                               "one token per launch)",
                      "algorithmic_bytes_per_launch": bytes_tok},
         "device": torch.cuda.get_device_name(0),
         "commit": git_commit(),
@@ -290,4 +332,8 @@ def bench_streamed(args, cfg) -> int:
 
 
 if __name__ == "__main__":
-    sys.exit(main())
+    rc = main()
+    # a successful run ends normally: leaving through SystemExit reorders the
+    # runtime's teardown so that rocprofv3 loses its results
+    if rc:
+        sys.exit(rc)
