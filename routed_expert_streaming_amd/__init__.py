@@ -14,7 +14,7 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_NO_KEY, MOE_SCORE_SIGMOID,
+from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_E_INVAL, MOE_NO_KEY, MOE_SCORE_SIGMOID,
                    MOE_SCORE_SOFTMAX, MoeError, MoeLayer, MoeRecordLayout, MoeRouter,
                    MoeTraceRec, check, lib)
 
@@ -164,7 +164,10 @@ def _layer_array(layers: Sequence[Layer]):
 
 def decode_workspace_bytes(layers: Sequence[Layer]) -> int:
     arr = _layer_array(layers)
-    return lib().moe_decode_workspace_bytes(arr, len(layers))
+    n = lib().moe_decode_workspace_bytes(arr, len(layers))
+    if n == 0:
+        raise MoeError(MOE_E_INVAL, "moe_decode_workspace_bytes", lib().moe_last_error().decode(errors="replace"))
+    return n
 
 
 def decode_forward(layers: Sequence[Layer], x: torch.Tensor, stream=None, ws: Optional[torch.Tensor] = None,

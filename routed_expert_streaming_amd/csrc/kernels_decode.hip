@@ -482,47 +482,54 @@ __device__ __forceinline__ int combiner_of(int td, int k, int tilesH, int cprI, 
 }
 
 // Output tile td, by one wave: out = sum_j w_j * sum_slots y_j + shared, in
-// fixed (rank, contributor) order, from tagged partials (polled until every
-// contribution of this step is there).  Returns false on a failed wait.
+// fixed (rank, contributor) order, from tagged partials polled until every
+// contribution of this step is there.  Each poll loads two ranks' partials
+// (up to 4 contributors each) and, the first time, the shared output, so a
+// top-2 layer needs one round trip.  Returns false on a failed wait.
 __device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k, int tilesH, int cprI, long nD,
                                              int G, int H, bool shared_on, const uint64_t *part_d, int slots_d,
                                              const uint64_t *ysh, float *out, const float *sw, unsigned *sync,
                                              int lane) {
     const int r = td * kTileRows + lane;
-    float o = 0.f;
+    float o = 0.f, sh = 0.f;
     long spins = 0;
-    for (int j = 0; j < k; j++) {
-        const long tau = (long)j * tilesH + td;
-        const int cnt = range_owner(nD, G, (tau + 1) * cprI - 1) - range_owner(nD, G, tau * cprI) + 1;
-        const uint64_t *pp = part_d + (size_t)tau * slots_d * 64 + lane;
-        float y = 0.f;
-        for (int s0 = 0; s0 < cnt; s0 += 4) {
-            uint64_t v[4];
+    for (int j = 0; j < k; j += 2) {
+        const bool two = j + 1 < k;
+        const long ta = (long)j * tilesH + td, tb = two ? ta + tilesH : ta;
+        const int ca = range_owner(nD, G, (ta + 1) * cprI - 1) - range_owner(nD, G, ta * cprI) + 1;
+        const int cb = two ? range_owner(nD, G, (tb + 1) * cprI - 1) - range_owner(nD, G, tb * cprI) + 1 : ca;
+        const uint64_t *pa = part_d + (size_t)ta * slots_d * 64 + lane;
+        const uint64_t *pb = part_d + (size_t)tb * slots_d * 64 + lane;
+        const bool with_shared = shared_on && j == 0;
+        float ya = 0.f, yb = 0.f;
+        for (int s0 = 0; s0 < max(ca, cb); s0 += 4) {
+            uint64_t va[4], vb[4], vs = 0;
             for (;;) {
                 bool ok = true;
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    v[q] = ld_tagged(pp + (size_t)min(s0 + q, cnt - 1) * 64);
-                    ok = ok && tag_ok(v[q], tag);
+                    va[q] = ld_tagged(pa + (size_t)min(s0 + q, ca - 1) * 64);
+                    vb[q] = ld_tagged(pb + (size_t)min(s0 + q, cb - 1) * 64);
+                    ok = ok && tag_ok(va[q], tag) && tag_ok(vb[q], tag);
+                }
+                if (with_shared && s0 == 0) {
+                    vs = ld_tagged(ysh + r);
+                    ok = ok && tag_ok(vs, tag);
                 }
                 if (__all(ok)) break;
                 if (!poll_more(sync, spins)) return false;
             }
 #pragma unroll
-            for (int q = 0; q < 4; q++)
-                if (s0 + q < cnt) y += tag_val(v[q]);
+            for (int q = 0; q < 4; q++) {
+                if (s0 + q < ca) ya += tag_val(va[q]);
+                if (two && s0 + q < cb) yb += tag_val(vb[q]);
+            }
+            if (with_shared && s0 == 0) sh = tag_val(vs);
         }
-        o = fmaf(sw[j], y, o);
+        o = fmaf(sw[j], ya, o);
+        if (two) o = fmaf(sw[j + 1], yb, o);
     }
-    if (shared_on) {
-        uint64_t v;
-        for (;;) {
-            v = ld_tagged(ysh + r);
-            if (__all(tag_ok(v, tag))) break;
-            if (!poll_more(sync, spins)) return false;
-        }
-        o += tag_val(v);
-    }
+    if (shared_on) o += sh;
     out[(size_t)s * H + r] = o;
     return true;
 }

@@ -328,7 +328,10 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
 }  // namespace
 
 size_t moe_decode_workspace_bytes(const moe_layer *layers, int32_t n_layers) {
-    if (!layers || n_layers < 1 || !dims_ok(layers[0].H, layers[0].I) || layers[0].router.k < 1) return 0;
+    if (!layers || n_layers < 1 || !dims_ok(layers[0].H, layers[0].I) || layers[0].router.k < 1) {
+        fail(MOE_E_INVAL, "decode workspace: invalid layers, n_layers or shapes");
+        return 0;
+    }
     DecodeWs D;
     if (carve_decode(nullptr, layers, n_layers, &D)) return 0;
     return D.bytes;
