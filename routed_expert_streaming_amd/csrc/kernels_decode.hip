@@ -603,31 +603,6 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         if (s == 0) __syncthreads();
         mark(kStampLayerWait);
 
-        // ---- shared gate/up (independent of routing)
-        if (shared_on) {
-            for (int r = shI0 + wave; r < shI1; r += kPW) {
-                const uint16_t *wg = lay.shared + (size_t)r * H, *wu = lay.shared + (size_t)I * H + (size_t)r * H;
-                float g = 0.f, u = 0.f;
-                for (int c = lane * 8; c < H; c += 512) {
-                    const uint4 gv = *(const uint4 *)(wg + c), uv = *(const uint4 *)(wu + c);
-                    const float4 xa = *(const float4 *)(xs + c), xb = *(const float4 *)(xs + c + 4);
-                    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-                    const uint32_t gq[4] = {gv.x, gv.y, gv.z, gv.w}, uq[4] = {uv.x, uv.y, uv.z, uv.w};
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        g = fmaf(__uint_as_float(gq[i] << 16), xv[2 * i], g);
-                        g = fmaf(__uint_as_float(gq[i] & 0xFFFF0000u), xv[2 * i + 1], g);
-                        u = fmaf(__uint_as_float(uq[i] << 16), xv[2 * i], u);
-                        u = fmaf(__uint_as_float(uq[i] & 0xFFFF0000u), xv[2 * i + 1], u);
-                    }
-                }
-                g = wave_sum(g);
-                u = wave_sum(u);
-                if (lane == 0) st_x(a.hs + r, g / (1.f + __expf(-g)) * u);
-            }
-            if (shI1 > shI0) wg_signal(h_ready + k);
-        }
-
         const unsigned tag = (unsigned)s + 1;
 
         // ---- x as fp16 pairs into LDS (every workgroup, for gate/up)
@@ -670,6 +645,32 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     st_tagged(a.z + e, z + (lay.bias ? lay.bias[e] : 0.f), tag);
                 }
             }
+        }
+
+        // ---- shared gate/up (independent of routing; after the logits, so it
+        // overlaps their exchange instead of delaying it)
+        if (shared_on) {
+            for (int r = shI0 + wave; r < shI1; r += kPW) {
+                const uint16_t *wg = lay.shared + (size_t)r * H, *wu = lay.shared + (size_t)I * H + (size_t)r * H;
+                float g = 0.f, u = 0.f;
+                for (int c = lane * 8; c < H; c += 512) {
+                    const uint4 gv = *(const uint4 *)(wg + c), uv = *(const uint4 *)(wu + c);
+                    const float4 xa = *(const float4 *)(xs + c), xb = *(const float4 *)(xs + c + 4);
+                    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+                    const uint32_t gq[4] = {gv.x, gv.y, gv.z, gv.w}, uq[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        g = fmaf(__uint_as_float(gq[i] << 16), xv[2 * i], g);
+                        g = fmaf(__uint_as_float(gq[i] & 0xFFFF0000u), xv[2 * i + 1], g);
+                        u = fmaf(__uint_as_float(uq[i] << 16), xv[2 * i], u);
+                        u = fmaf(__uint_as_float(uq[i] & 0xFFFF0000u), xv[2 * i + 1], u);
+                    }
+                }
+                g = wave_sum(g);
+                u = wave_sum(u);
+                if (lane == 0) st_x(a.hs + r, g / (1.f + __expf(-g)) * u);
+            }
+            if (shI1 > shI0) wg_signal(h_ready + k);
         }
 
         // ---- top-k (every workgroup, wave 0): poll the tagged logits, then k
@@ -872,8 +873,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             ea = eb;
         }
 
-        // ---- output tiles this workgroup combines (one wave each), then
-        // their count on the layer-done counter
+        // ---- output tiles this workgroup combines (one wave each), each
+        // counted on the layer-done counter by its wave
         {
             int nc = 0;
             bool okc = true;
@@ -883,16 +884,17 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             const int tdB = d1 > lb0 ? (int)((d1 - 1 - lb0) / cprI) : -1;
             for (int td = tdA; td <= tdB; td++) {
                 if (combiner_of(td, k, tilesH, cprI, nD, G) != w) continue;
-                if (nc++ % kPW == wave && okc)
-                    okc = combine_tile(td, s, tag, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d, a.ysh,
-                                       a.out, sw, sync, lane);
+                if (nc++ % kPW != wave || !okc) continue;
+                okc = combine_tile(td, s, tag, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d, a.ysh,
+                                   a.out, sw, sync, lane);
+                // counted at once: nothing in this launch reads the outputs, and
+                // the partials it read are consumed (their values are used)
+                if (okc && lane == 0)
+                    __hip_atomic_fetch_add(sync + kLayerDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             if (lane == 0 && !okc) *bcast = 0;
-            wait_vm_all();
             __syncthreads();
             if (!*bcast) return;
-            if (threadIdx.x == 0 && nc)
-                __hip_atomic_fetch_add(sync + kLayerDone, (unsigned)nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         mark(kStampDownDone);
     }
