@@ -373,8 +373,7 @@ __device__ __forceinline__ void d_unit(const uint32_t (&d)[12], const char *cb, 
 // Gate and up of one expert: units [la, lb) (unit u = tile u / cpr, chunk
 // u % cpr; its codes are 3072 bytes at base + u * 3072), against the x pairs
 // already in LDS.  Wave v takes units la + v, la + v + kPW, ...; tile sums go
-// to LDS slot (tile - t0).  The first code loads are issued together with
-// the staging of the codebooks.  The steady-state loop has no branches around its loads:
+// to LDS slot (tile - t0).  The steady-state loop has no branches around its loads:
 // loads past the wave's last unit re-read that unit (their buffers are never
 // consumed), so every load of the ring stays in flight while older units are
 // computed.
@@ -389,26 +388,22 @@ __device__ __forceinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *us
     gu32x4 *gb = (gu32x4 *)gsec, *ub = (gu32x4 *)usec;
     const int first = __builtin_amdgcn_readfirstlane(la + wave);
     const int n = __builtin_amdgcn_readfirstlane(first < lb ? (lb - first + kPW - 1) / kPW : 0);
-    // stage codebooks (+ x) and clear this segment's sum slots, with the
-    // first code loads in flight
+    // stage the codebooks and clear this segment's sum slots
     stage_lds<kLdsPlain>(cbg, cbg_src, kCbRows * 16, wave, lane);
     stage_lds<kLdsPlain>(cbu, cbu_src, kCbRows * 16, wave, lane);
-    // the code loads are issued after every staging copy (the fence keeps
-    // that order), so waiting until only they are outstanding is enough to
-    // see the staged data: the loop starts without waiting for them
-    __builtin_amdgcn_sched_barrier(0);
     uint32_t bg[kRingGU][12], bu[kRingGU][12];
     for (int i = threadIdx.x; i < nslots * kPW * 128; i += kPW * 64) red[i] = 0.f;
-    // first ring stages; a wave without units loads the segment's first unit
-    // (never consumed), so every wave has the same loads in flight
+    wait_lds_barrier<0>();
+    lds_barrier();
+    // first ring stages, issued after the codebooks have landed (issued
+    // together, the chip-wide burst of code loads delays the codebooks); a
+    // wave without units loads the segment's first unit (never consumed)
 #pragma unroll
     for (int r = 0; r < kRingGU - 1; r++) {
         const int u = n ? first + min(r, n - 1) * kPW : la;
         load_codes(gb, u, lane, bg[r]);
         load_codes(ub, u, lane, bu[r]);
     }
-    wait_lds_barrier<(kRingGU - 1) * 2 * kStripLoads>();
-    lds_barrier();
     if (stamp && threadIdx.x == 0) stamp[kStampGuStaged] = wall_clock64();
     if (!n) return;
     float ag[4] = {0.f, 0.f, 0.f, 0.f}, au[4] = {0.f, 0.f, 0.f, 0.f};
