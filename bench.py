@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # valid for the kernel source they were taken on: reported as null once that
 # source has changed.
 DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
-                  "sha256_prefix": "4432cf8e0152a642", "bytes_per_launch": 4713669043}
+                  "sha256_prefix": "83d09abc5f859a2c", "bytes_per_launch": 4681542778}
 
 
 def measured_traffic():
