@@ -54,24 +54,9 @@ __device__ __forceinline__ unsigned ld_cnt(const unsigned *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Direct global -> LDS copies (global_load_lds_dwordx4): each lane moves 16
-// bytes into LDS at the wave-uniform base + 16 * lane, without passing
-// through registers, so a workgroup's whole staging is in flight at once.
-// Wave v moves 1 KB blocks v, v + kPW, ...  The cache policy is kLdsPlain for
-// record data (immutable during the launch) and kLdsCoherent (sc1, the
-// policy of an agent-scope load) for data other workgroups wrote.  The caller
-// waits for vmcnt 0 and synchronises the workgroup before reading.
-typedef __attribute__((address_space(1))) const void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
-constexpr int kLdsPlain = 0, kLdsCoherent = 16;
 template <int AUX>
 __device__ __forceinline__ void stage_lds(char *dst, const void *src, int nbytes, int wave, int lane) {
-    const int nblk = (nbytes + 1023) >> 10;
-    for (int b = wave; b < nblk; b += kPW) {
-        const int off = (b << 10) + lane * 16;
-        if (off < nbytes)
-            __builtin_amdgcn_global_load_lds((gvoid *)((const char *)src + off), (lvoid *)(dst + (b << 10)), 16, 0, AUX);
-    }
+    stage_lds_waves<AUX, kPW>(dst, src, nbytes, wave, lane);
 }
 
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)

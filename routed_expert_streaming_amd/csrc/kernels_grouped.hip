@@ -13,19 +13,22 @@
 // v_mfma_f32_16x16x32_bf16: A is 16 (tokens) x 32 (K), B is 32 (K) x 16
 // (weight rows); lane l holds A[l%16][8*(l/16)+0..7], B[8*(l/16)+0..7][l%16]
 // and D[4*(l/16)+0..3][l%16].  Eight consecutive K values of one weight row
-// are exactly one RVQ group, so each lane decodes bf16(C[a] + C[b]) of one
-// group into its B fragment.  Within a 128-column chunk, K-step s uses group
-// 4*(l/16)+s in lane block l/16 (a fixed permutation of K, applied to A and B
-// alike).  The weight row scale is applied to the fp32 accumulator.
+// are exactly one RVQ group, so one codebook row is one lane's B fragment.
+// The codebooks are converted to bf16 in LDS once; a group then costs two
+// gathers, C[a] and C[b], used as B fragments of two MFMAs that share the A
+// fragment and the accumulator (W x = C[a] x + C[b] x, summed in fp32): no
+// per-group arithmetic besides the addresses.  Within a 128-column chunk,
+// K-step s uses group 4*(l/16)+s in lane block l/16 (a fixed permutation of
+// K, applied to A and B alike).  The weight row scale is applied to the fp32
+// accumulator.
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
+#include "rvq_device.h"
 
 namespace moe {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -34,24 +37,32 @@ constexpr int kTokBlocks = 2;
 constexpr int kTwGateUp = 2;        // 16-row tiles per wave unit (gate/up)
 constexpr int kTwDown = 5;          // 16-row tiles per wave unit (down)       // 16-token blocks per pass (32 tokens)
 
-__device__ __forceinline__ uint32_t bf16_pair_from_f16_sum(uint32_t a, uint32_t b) {
-    const f16x2 s = __builtin_bit_cast(f16x2, a) + __builtin_bit_cast(f16x2, b);   // v_pk_add_f16
+__device__ __forceinline__ uint32_t bf16_pair_from_f16_pair(uint32_t a) {
+    const f16x2 h = __builtin_bit_cast(f16x2, a);
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     bf16x2 r;
-    r.x = (__bf16)(float)s.x;
-    r.y = (__bf16)(float)s.y;
+    r.x = (__bf16)(float)h.x;
+    r.y = (__bf16)(float)h.y;
     return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ bf16x8 decode_group(const char *cb, uint32_t v) {
-    const u32x4 ca = *(const u32x4 *)(cb + ((v << 4) & 0xFFF0u));
-    const u32x4 cv = *(const u32x4 *)(cb + ((v >> 8) & 0xFFF0u));
-    u32x4 r;
-    r.x = bf16_pair_from_f16_sum(ca.x, cv.x);
-    r.y = bf16_pair_from_f16_sum(ca.y, cv.y);
-    r.z = bf16_pair_from_f16_sum(ca.z, cv.z);
-    r.w = bf16_pair_from_f16_sum(ca.w, cv.w);
-    return __builtin_bit_cast(bf16x8, r);
+// fp16 codebook rows staged in LDS -> bf16 in place (each thread its rows)
+__device__ __forceinline__ void codebook_to_bf16(char *cb) {
+    for (int i = threadIdx.x; i < kCbRows; i += kGWaves * 64) {
+        u32x4 v = ((u32x4 *)cb)[i];
+        v.x = bf16_pair_from_f16_pair(v.x);
+        v.y = bf16_pair_from_f16_pair(v.y);
+        v.z = bf16_pair_from_f16_pair(v.z);
+        v.w = bf16_pair_from_f16_pair(v.w);
+        ((u32x4 *)cb)[i] = v;
+    }
+}
+
+// B fragments of the stage-1 and stage-2 codebook rows of a group (24-bit
+// code pair v) from a bf16 codebook in LDS
+__device__ __forceinline__ void group_rows(const char *cb, uint32_t v, bf16x8 &ba, bf16x8 &bb) {
+    ba = *(const bf16x8 *)(cb + ((v << 4) & 0xFFF0u));
+    bb = *(const bf16x8 *)(cb + ((v >> 8) & 0xFFF0u));
 }
 
 // The lane's 3 dwords (4 groups) of its row's 48-byte strip in a code tile.
@@ -150,6 +161,7 @@ struct GroupedArgs {
     int N, K;                   // weight matrix rows (outputs) and columns (reduction)
     int splits;                 // workgroups per expert (row ranges)
     int mat;                    // RVQ matrix: 0 = gate (+up), 2 = down
+    int xcd_group;              // 1: place each expert's workgroups on one XCD (expert count % 8 == 0)
 };
 
 // Work unit of a wave: TW 16-row tiles x one pass of up to 16*kTokBlocks
@@ -171,16 +183,17 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped(GroupedArgs g) {
         rec = (const uint8_t *)g.table[slot];
     }
     char *cb0 = lds, *cb1 = lds + kCbRows * 16;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if constexpr (!DENSE) {
-        const u32x4 *s0 = (const u32x4 *)(rec + g.off.cb[g.mat]);
-        const u32x4 *s1 = (const u32x4 *)(rec + g.off.cb[1]);
-        for (int i = threadIdx.x; i < kCbRows; i += kGWaves * 64) {
-            ((u32x4 *)cb0)[i] = s0[i];
-            if constexpr (GATEUP) ((u32x4 *)cb1)[i] = s1[i];
-        }
+        // codebooks into LDS with direct copies, all in flight at once
+        stage_lds_waves<kLdsPlain, kGWaves>(cb0, rec + g.off.cb[g.mat], kCbRows * 16, wave, lane);
+        if constexpr (GATEUP) stage_lds_waves<kLdsPlain, kGWaves>(cb1, rec + g.off.cb[1], kCbRows * 16, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+        codebook_to_bf16(cb0);
+        if constexpr (GATEUP) codebook_to_bf16(cb1);
         __syncthreads();
     }
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 15, g4 = lane >> 4;
     const int rows_per_split = g.N / g.splits;          // multiple of 16
     const int r_begin = split * rows_per_split;
@@ -277,32 +290,49 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped(GroupedArgs g) {
 #pragma unroll
                 for (int t = 0; t < TW; t++) {
                     if (t < ntw) {
-                        bf16x8 B0, B1;
                         if constexpr (DENSE) {
-                            B0 = cur.w0[t][s];
+                            const bf16x8 B0 = cur.w0[t][s];
+                            bf16x8 B1;
                             if constexpr (GATEUP) B1 = cur.w1[t][s];
+#pragma unroll
+                            for (int b = 0; b < kTokBlocks; b++) {
+                                if (b < nblk) {
+                                    acc0[t][b] =
+                                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B0, acc0[t][b], 0, 0, 0);
+                                    if constexpr (GATEUP)
+                                        acc1[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B1,
+                                                                                             acc1[t][b], 0, 0, 0);
+                                }
+                            }
                         } else {
                             const uint32_t *c0 = cur.c0[t], *c1 = cur.c1[t];
                             const uint32_t v0 = s == 0 ? quad_code<0>(c0[0], c0[1], c0[2])
                                               : s == 1 ? quad_code<1>(c0[0], c0[1], c0[2])
                                               : s == 2 ? quad_code<2>(c0[0], c0[1], c0[2])
                                                        : quad_code<3>(c0[0], c0[1], c0[2]);
-                            B0 = decode_group(cb0, v0);
+                            bf16x8 B0a, B0b, B1a, B1b;
+                            group_rows(cb0, v0, B0a, B0b);
                             if constexpr (GATEUP) {
                                 const uint32_t v1 = s == 0 ? quad_code<0>(c1[0], c1[1], c1[2])
                                                   : s == 1 ? quad_code<1>(c1[0], c1[1], c1[2])
                                                   : s == 2 ? quad_code<2>(c1[0], c1[1], c1[2])
                                                            : quad_code<3>(c1[0], c1[1], c1[2]);
-                                B1 = decode_group(cb1, v1);
+                                group_rows(cb1, v1, B1a, B1b);
                             }
-                        }
 #pragma unroll
-                        for (int b = 0; b < kTokBlocks; b++) {
-                            if (b < nblk) {
-                                acc0[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B0, acc0[t][b], 0, 0, 0);
-                                if constexpr (GATEUP)
-                                    acc1[t][b] =
-                                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B1, acc1[t][b], 0, 0, 0);
+                            for (int b = 0; b < kTokBlocks; b++) {
+                                if (b < nblk) {
+                                    acc0[t][b] =
+                                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B0a, acc0[t][b], 0, 0, 0);
+                                    acc0[t][b] =
+                                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B0b, acc0[t][b], 0, 0, 0);
+                                    if constexpr (GATEUP) {
+                                        acc1[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B1a,
+                                                                                             acc1[t][b], 0, 0, 0);
+                                        acc1[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B1b,
+                                                                                             acc1[t][b], 0, 0, 0);
+                                    }
+                                }
                             }
                         }
                     }
@@ -334,6 +364,286 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped(GroupedArgs g) {
                             g.yout[p * g.N + n[t]] = acc0[t][b][i] * s0v;
                         }
                     }
+                }
+            }
+        }
+    }
+}
+
+// RVQ experts: one 16-token block per pass (experts average 10.7 tokens in
+// the 256-token layer; the few with more take a second pass over their
+// codes).  All waves of a workgroup sweep the 128-column chunks together:
+//  - the A operand (16 token rows x 128 columns, 4 KB per chunk) goes
+//    through a 3-slot ring in LDS, copied once per workgroup instead of once
+//    per wave (each wave copies 1/8 of a chunk two chunks ahead), with one
+//    workgroup barrier per chunk;
+//  - each wave keeps its own codes in a 3-deep register ring (loads past the
+//    last chunk re-read it and tiles past the last row re-use the last tile,
+//    so the steady state has no branches around its loads);
+//  - the codebook gathers run one K-step ahead of the MFMAs that use them.
+// The epilogue writes real rows and tokens only.
+constexpr int kBufNt = 2;                     // buffer load cache policy: non-temporal
+constexpr int kBufWord3 = 0x00020000;         // buffer descriptor word 3 (32-bit data format)
+constexpr int kASlot = 16 * kChunkCols * 2;   // bytes of one A ring slot
+constexpr int kARing = 3;
+static_assert(kGWaves == 8, "the A copy assigns two tokens to each wave");
+
+template <int TW>
+struct RvqStage {
+    uint32_t c0[TW][3], c1[TW][3];   // codes of 4 groups per tile (gate or down; up)
+};
+
+// Codes of chunk j through buffer loads: rs0/rs1 describe the code sections
+// of the two matrices (reads past a section's end return zero), qoff[t][i]
+// is the lane's byte offset of dword i of its 4 groups of tile t in chunk 0,
+// and the chunk's offset goes in the scalar offset.  Streaming (nt) loads.
+template <bool GATEUP, int TW>
+__device__ __forceinline__ void rvq_load(RvqStage<TW> &st, __amdgpu_buffer_rsrc_t rs0, __amdgpu_buffer_rsrc_t rs1,
+                                         const uint32_t (&qoff)[TW][3], int j) {
+    const int soff = j * kTileBytes;
+#pragma unroll
+    for (int t = 0; t < TW; t++)
+#pragma unroll
+        for (int i = 0; i < 3; i++) {
+            st.c0[t][i] = __builtin_amdgcn_raw_buffer_load_b32(rs0, (int)qoff[t][i], soff, kBufNt);
+            if constexpr (GATEUP) st.c1[t][i] = __builtin_amdgcn_raw_buffer_load_b32(rs1, (int)qoff[t][i], soff, kBufNt);
+        }
+}
+
+// Gathered B fragments of one K-step: C[a] and C[b] per tile and matrix.
+template <bool GATEUP, int TW>
+struct RvqGather {
+    bf16x8 b[TW][GATEUP ? 2 : 1][2];
+};
+
+template <bool GATEUP, int TW, int S>
+__device__ __forceinline__ void rvq_gather(const RvqStage<TW> &st, const char *cb0, const char *cb1,
+                                           RvqGather<GATEUP, TW> &g) {
+#pragma unroll
+    for (int t = 0; t < TW; t++) {
+        group_rows(cb0, quad_code<S>(st.c0[t][0], st.c0[t][1], st.c0[t][2]), g.b[t][0][0], g.b[t][0][1]);
+        if constexpr (GATEUP)
+            group_rows(cb1, quad_code<S>(st.c1[t][0], st.c1[t][1], st.c1[t][2]), g.b[t][1][0], g.b[t][1][1]);
+    }
+}
+
+template <bool GATEUP, int TW>
+__device__ __forceinline__ void rvq_mfma(const bf16x8 &a, const RvqGather<GATEUP, TW> &g, f32x4 (&acc0)[TW],
+                                         f32x4 (&acc1)[TW]) {
+#pragma unroll
+    for (int t = 0; t < TW; t++) {
+        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][0][0], acc0[t], 0, 0, 0);
+        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][0][1], acc0[t], 0, 0, 0);
+        if constexpr (GATEUP) {
+            acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][1][0], acc1[t], 0, 0, 0);
+            acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][1][1], acc1[t], 0, 0, 0);
+        }
+    }
+}
+
+// Wait until at most N LDS operations of this wave are outstanding, then a
+// workgroup barrier; outstanding global loads are not waited for.
+template <int N>
+__device__ __forceinline__ void lds_wait_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));   // vmcnt(63) expcnt(7) lgkmcnt(N)
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// The A ring.  Token m's 16-byte piece q (columns 8q..8q+7 of the chunk)
+// sits at m*256 + (q ^ m)*16 of a slot, so the 16 lanes of one lane block
+// (16 tokens, one piece each) read 16 different bank groups.  Wave w copies
+// tokens 2w, 2w+1: lane i writes slot byte 512w + 16(i%32) (lanes i and
+// i+32 copy the same piece, which keeps the copy free of branches).
+struct ARing {
+    char *base;                 // slot 0
+    const uint16_t *src;        // the lane's token row + its piece (columns 8q..)
+    uint32_t wr;                // byte offset of the lane's piece in a slot
+    uint32_t rd[4];             // byte offset of the lane's A fragment of K-step s in a slot
+};
+
+__device__ __forceinline__ u32x4 a_fetch(const ARing &r, int j) {
+    return *(const u32x4 *)(r.src + (size_t)j * kChunkCols);
+}
+__device__ __forceinline__ void a_store(const ARing &r, int slot, const u32x4 &v) {
+    *(u32x4 *)(r.base + slot * kASlot + r.wr) = v;
+}
+
+// One chunk (ring slot R, codes in cur): on entry g holds K-step 0 of this
+// chunk's gathers and areg the A piece of chunk j+1 (copied here into the
+// ring); areg leaves with chunk j+2's piece, fill with chunk j+2's codes
+// and, with NEXT, g with K-step 0 of the next chunk (nxt).
+template <bool GATEUP, int TW, bool NEXT, int R>
+__device__ __forceinline__ void rvq_chunk(const RvqStage<TW> &cur, const RvqStage<TW> &nxt, RvqStage<TW> &fill,
+                                          __amdgpu_buffer_rsrc_t rs0, __amdgpu_buffer_rsrc_t rs1,
+                                          const uint32_t (&qoff)[TW][3],
+                                          int j, int cpr, const ARing &ar, u32x4 &areg,
+                                          const char *cb0, const char *cb1, RvqGather<GATEUP, TW> &g,
+                                          f32x4 (&acc0)[TW], f32x4 (&acc1)[TW]) {
+    constexpr int kG = TW * (GATEUP ? 2 : 1) * 2;   // gathers per K-step
+    static_assert(kG <= 15, "lgkmcnt range");
+    a_store(ar, (R + 1) % kARing, areg);
+    bf16x8 a[4];
+    const char *slot = ar.base + R * kASlot;
+#pragma unroll
+    for (int s = 0; s < 4; s++) a[s] = *(const bf16x8 *)(slot + ar.rd[s]);
+    areg = a_fetch(ar, min(j + 2, cpr - 1));
+    rvq_load<GATEUP, TW>(fill, rs0, rs1, qoff, min(j + 2, cpr - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    RvqGather<GATEUP, TW> g1, g2;
+    rvq_gather<GATEUP, TW, 1>(cur, cb0, cb1, g1);
+    __builtin_amdgcn_sched_barrier(0);
+    // the A copy of chunk j+1 (issued before the K-step 1 gathers) is done
+    lds_wait_barrier<kG>();
+    __builtin_amdgcn_sched_barrier(0);
+    rvq_mfma<GATEUP, TW>(a[0], g, acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    rvq_gather<GATEUP, TW, 2>(cur, cb0, cb1, g2);
+    __builtin_amdgcn_sched_barrier(0);
+    rvq_mfma<GATEUP, TW>(a[1], g1, acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    rvq_gather<GATEUP, TW, 3>(cur, cb0, cb1, g1);
+    __builtin_amdgcn_sched_barrier(0);
+    rvq_mfma<GATEUP, TW>(a[2], g2, acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) rvq_gather<GATEUP, TW, 0>(nxt, cb0, cb1, g);
+    __builtin_amdgcn_sched_barrier(0);
+    rvq_mfma<GATEUP, TW>(a[3], g1, acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool GATEUP, int TW>
+__global__ __launch_bounds__(kGWaves * 64) void k_grouped_rvq(GroupedArgs g) {
+    extern __shared__ __align__(16) char lds[];
+    // Workgroups are dealt to the 8 XCDs round-robin by index; when the
+    // expert count is a multiple of 8, the row ranges of one expert all go to
+    // one XCD (consecutive there), so its codebooks and A rows come from HBM
+    // once and from that XCD's L2 after.
+    int slot, split;
+    if (g.xcd_group) {
+        const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
+        slot = (idx / g.splits) * 8 + xcd;
+        split = idx % g.splits;
+    } else {
+        slot = blockIdx.x / g.splits;
+        split = blockIdx.x % g.splits;
+    }
+    const int cnt = g.counts[slot], pos0 = g.offsets[slot];
+    if (cnt == 0) return;                 // uniform across the workgroup
+    const uint8_t *rec = (const uint8_t *)g.table[slot];
+    char *cb0 = lds, *cb1 = lds + kCbRows * 16;
+    char *aring = lds + (GATEUP ? 2 : 1) * kCbRows * 16;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    // codebooks into LDS with direct copies (all in flight at once), then bf16
+    stage_lds_waves<kLdsPlain, kGWaves>(cb0, rec + g.off.cb[g.mat], kCbRows * 16, wave, lane);
+    if constexpr (GATEUP) stage_lds_waves<kLdsPlain, kGWaves>(cb1, rec + g.off.cb[1], kCbRows * 16, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    codebook_to_bf16(cb0);
+    if constexpr (GATEUP) codebook_to_bf16(cb1);
+    const int col = lane & 15, g4 = lane >> 4;
+    const int rows_per_split = g.N / g.splits;          // multiple of 16
+    const int r_begin = split * rows_per_split;
+    const int tiles = rows_per_split / 16;
+    const int tgroups = (tiles + TW - 1) / TW;
+    const int rounds = (tgroups + kGWaves - 1) / kGWaves;
+    const int cpr = g.K / kChunkCols;
+    const int code_bytes = g.N / 64 * cpr * kTileBytes;   // one matrix's code section
+    const __amdgpu_buffer_rsrc_t rs0 =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(rec + g.off.codes[g.mat]), 0, code_bytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rs1 =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(rec + g.off.codes[1]), 0, code_bytes, kBufWord3);
+    const _Float16 *sc0 = (const _Float16 *)(rec + g.off.scales[g.mat]);
+    const _Float16 *sc1 = (const _Float16 *)(rec + g.off.scales[1]);
+    const int passes = (cnt + 15) / 16;
+    ARing ar;
+    ar.base = aring;
+    ar.wr = wave * 512 + (lane & 31) * 16;
+#pragma unroll
+    for (int s = 0; s < 4; s++) ar.rd[s] = col * 256 + (((4 * g4 + s) ^ col) & 15) * 16;
+    // Every wave runs every (pass, round) so the barriers line up; a wave
+    // without a tile group in the last round repeats the last one and
+    // writes nothing.
+    for (int it = 0; it < passes * rounds; it++) {
+        const int pass = it / rounds, tg_raw = (it % rounds) * kGWaves + wave;
+        const bool active = tg_raw < tgroups;                  // wave-uniform
+        const int tg = min(tg_raw, tgroups - 1);
+        const int ntw = min(TW, tiles - tg * TW);             // tiles in this unit (wave-uniform)
+        int n[TW];
+        uint32_t qoff[TW][3];
+#pragma unroll
+        for (int t = 0; t < TW; t++) {
+            n[t] = r_begin + (tg * TW + min(t, ntw - 1)) * 16 + col;
+#pragma unroll
+            for (int i = 0; i < 3; i++) {
+                const int dw = 3 * g4 + i;   // strip dword: 16-byte part dw/4 of row n
+                qoff[t][i] = (uint32_t)((n[t] >> 6) * cpr) * kTileBytes + (dw >> 2) * 1024 + (n[t] & 63) * 16 +
+                             (dw & 3) * 4;
+            }
+        }
+        // the copying lanes' A rows: tokens past the pass's last real one
+        // copy the last real row (their products are never written)
+        {
+            const int mloc = 2 * wave + ((lane >> 4) & 1);
+            const int m = min(pass * 16 + mloc, cnt - 1);
+            const int p = pos0 + m;
+            const uint16_t *row = g.a + (size_t)(g.a_by_token ? g.perm[p] / g.k : p) * g.K;
+            ar.src = row + (((lane & 15) ^ mloc) & 15) * 8;
+        }
+        f32x4 acc0[TW], acc1[TW];
+#pragma unroll
+        for (int t = 0; t < TW; t++) {
+            acc0[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            acc1[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+        // prologue: every wave is past the previous unit's last A reads (and
+        // the codebook conversion) before slot 0 is rewritten
+        u32x4 areg = a_fetch(ar, 0);
+        lds_wait_barrier<0>();
+        a_store(ar, 0, areg);
+        areg = a_fetch(ar, min(1, cpr - 1));
+        RvqStage<TW> st[3];
+        rvq_load<GATEUP, TW>(st[0], rs0, rs1, qoff, 0);
+        rvq_load<GATEUP, TW>(st[1], rs0, rs1, qoff, min(1, cpr - 1));
+        RvqGather<GATEUP, TW> g0;
+        rvq_gather<GATEUP, TW, 0>(st[0], cb0, cb1, g0);
+        lds_wait_barrier<0>();
+        int j = 0;
+        for (; j + 3 <= cpr; j += 3) {
+            rvq_chunk<GATEUP, TW, true, 0>(st[0], st[1], st[2], rs0, rs1, qoff, j, cpr, ar, areg, cb0, cb1, g0,
+                                           acc0, acc1);
+            rvq_chunk<GATEUP, TW, true, 1>(st[1], st[2], st[0], rs0, rs1, qoff, j + 1, cpr, ar, areg, cb0, cb1,
+                                           g0, acc0, acc1);
+            rvq_chunk<GATEUP, TW, true, 2>(st[2], st[0], st[1], rs0, rs1, qoff, j + 2, cpr, ar, areg, cb0, cb1,
+                                           g0, acc0, acc1);
+        }
+        // the last cpr - j (< 3) chunks are already in st[0], st[1]
+        if (j + 2 == cpr) {
+            rvq_chunk<GATEUP, TW, true, 0>(st[0], st[1], st[2], rs0, rs1, qoff, j, cpr, ar, areg, cb0, cb1, g0,
+                                           acc0, acc1);
+            rvq_chunk<GATEUP, TW, false, 1>(st[1], st[2], st[0], rs0, rs1, qoff, j + 1, cpr, ar, areg, cb0, cb1,
+                                            g0, acc0, acc1);
+        } else if (j + 1 == cpr) {
+            rvq_chunk<GATEUP, TW, false, 0>(st[0], st[1], st[2], rs0, rs1, qoff, j, cpr, ar, areg, cb0, cb1, g0,
+                                            acc0, acc1);
+        }
+        if (!active) continue;
+        // epilogue: lane holds D[4*g4 + i][col] of each tile
+#pragma unroll
+        for (int t = 0; t < TW; t++) {
+            if (t >= ntw) continue;
+            const float s0v = (float)sc0[n[t]];
+            const float s1v = GATEUP ? (float)sc1[n[t]] : 1.f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int mm = pass * 16 + 4 * g4 + i;
+                if (mm >= cnt) continue;
+                const size_t p = (size_t)(pos0 + mm);
+                if constexpr (GATEUP) {
+                    const float gg = acc0[t][i] * s0v, uu = acc1[t][i] * s1v;
+                    const __bf16 h = (__bf16)(gg / (1.f + __expf(-gg)) * uu);
+                    g.hout[p * g.N + n[t]] = __builtin_bit_cast(uint16_t, h);
+                } else {
+                    g.yout[p * g.N + n[t]] = acc0[t][i] * s0v;
                 }
             }
         }
@@ -377,6 +687,9 @@ static int pick_splits(int N) {
     return splits;
 }
 
+constexpr int kLdsGateUp = 2 * kCbRows * 16 + kARing * kASlot;
+constexpr int kLdsDown = kCbRows * 16 + kARing * kASlot;
+
 hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, int E, int H, int I,
                               const int32_t *counts, const int32_t *offsets, const int32_t *perm, int k,
                               const uint16_t *xb, uint16_t *hbuf, float *ybuf, hipStream_t s) {
@@ -395,17 +708,18 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
     g.K = H;
     g.splits = pick_splits(I);
     g.mat = 0;
+    g.xcd_group = E % 8 == 0;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_grouped<true, false, kTwGateUp>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kCbRows * 16);
+        hipError_t e = hipFuncSetAttribute((const void *)k_grouped_rvq<true, kTwGateUp>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsGateUp);
         if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void *)k_grouped<false, false, kTwDown>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    kCbRows * 16);
+            e = hipFuncSetAttribute((const void *)k_grouped_rvq<false, kTwDown>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDown);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    k_grouped<true, false, kTwGateUp><<<E * g.splits, kGWaves * 64, 2 * kCbRows * 16, s>>>(g);
+    k_grouped_rvq<true, kTwGateUp><<<E * g.splits, kGWaves * 64, kLdsGateUp, s>>>(g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // down: N = H rows, K = I; A = h rows by position
@@ -417,7 +731,7 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
     g.K = I;
     g.splits = pick_splits(H);
     g.mat = 2;
-    k_grouped<false, false, kTwDown><<<E * g.splits, kGWaves * 64, kCbRows * 16, s>>>(g);
+    k_grouped_rvq<false, kTwDown><<<E * g.splits, kGWaves * 64, kLdsDown, s>>>(g);
     return hipGetLastError();
 }
 

@@ -80,6 +80,27 @@ __device__ __forceinline__ void strip_dot(const uint32_t (&d)[12], const char *c
 
 typedef __attribute__((address_space(1))) const u32x4 gu32x4;   // global memory
 
+// Direct global -> LDS copies (global_load_lds_dwordx4): each lane moves 16
+// bytes into LDS at the wave-uniform base + 16 * lane, without passing
+// through registers, so a workgroup's whole staging is in flight at once.
+// Wave v of WAVES moves 1 KB blocks v, v + WAVES, ...  The cache policy is
+// kLdsPlain for record data (immutable during a launch) and kLdsCoherent
+// (sc1, the policy of an agent-scope load) for data other workgroups of the
+// same launch wrote.  The caller waits for vmcnt 0 and synchronises the
+// workgroup before reading.
+typedef __attribute__((address_space(1))) const void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+constexpr int kLdsPlain = 0, kLdsCoherent = 16;
+template <int AUX, int WAVES>
+__device__ __forceinline__ void stage_lds_waves(char *dst, const void *src, int nbytes, int wave, int lane) {
+    const int nblk = (nbytes + 1023) >> 10;
+    for (int b = wave; b < nblk; b += WAVES) {
+        const int off = (b << 10) + lane * 16;
+        if (off < nbytes)
+            __builtin_amdgcn_global_load_lds((gvoid *)((const char *)src + off), (lvoid *)(dst + (b << 10)), 16, 0, AUX);
+    }
+}
+
 __device__ __forceinline__ void load_strip(const u32x4 *tile_generic, int lane, uint32_t (&d)[12]) {
     gu32x4 *tile = (gu32x4 *)tile_generic;      // codes live in global memory
     const u32x4 w0 = __builtin_nontemporal_load(tile + lane);
