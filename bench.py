@@ -107,6 +107,9 @@ def main() -> int:
     ap.add_argument("--config", default="mixtral", choices=["mixtral", "kimi_linear", "batched", "k3_slice"],
                     help="mixtral / kimi_linear: resident decode; batched: one 256-token grouped layer call "
                          "per step; k3_slice: streamed decode through the HBM slot cache (cold start)")
+    ap.add_argument("--sweep", choices=["capacity", "k"], default=None,
+                    help="k3_slice only: hit rate and tok/s against cache capacity (one stack-distance pass "
+                         "plus measured runs), or tok/s against experts per token")
     ap.add_argument("--cpu-sample-tokens", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -141,6 +144,13 @@ def main() -> int:
     cfg = synth.get_config(args.config)
     if args.config == "batched":
         return bench_batched(args, cfg)
+    if args.sweep and args.config != "k3_slice":
+        print("--sweep needs --config k3_slice", file=sys.stderr)
+        return 2
+    if args.sweep == "capacity":
+        return bench_sweep_capacity(args, cfg)
+    if args.sweep == "k":
+        return bench_sweep_k(args, cfg)
     if args.config == "k3_slice":
         return bench_streamed(args, cfg)
     n_tok = args.warmup + args.steps
@@ -262,9 +272,148 @@ def bench_batched(args, cfg) -> int:
     return 0
 
 
+def _streamed_run(moe, cfg, layers, x, hp, tables, cap, warmup, steps):
+    """Decode warmup + steps tokens through a cold cache of `cap` slots; the
+    first `warmup` tokens are decoded (and counted in the cache) untimed."""
+    import numpy as np
+    import torch
+    pool = torch.empty(cap * hp.stride, dtype=torch.uint8, device="cuda")
+    cache = moe.ExpertCache(cap, hp.stride, pool)
+    ws = torch.empty(moe.streamed_workspace_bytes(layers[0]), dtype=torch.uint8, device="cuda")
+    out = torch.empty((warmup + steps, cfg.layers, cfg.H), dtype=torch.float32, device="cuda")
+    copy_stream = torch.cuda.Stream()
+
+    def token(t):
+        for L in range(cfg.layers):
+            moe.layer_forward_streamed(layers[L], cache, L, None, x[t, L][None], copy_stream, ws=ws,
+                                       out=out[t, L][None], host_table=tables[L])
+
+    for t in range(warmup):
+        token(t)
+    torch.cuda.synchronize()
+    st0 = cache.stats()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        token(warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    st = cache.stats()
+    tr = cache.trace()
+    cache.close()
+    del pool
+    keys = np.array([r[0] for r in tr], dtype=np.uint32)
+    hits = np.array([r[1] for r in tr], dtype=np.int32)
+    misses_timed = (st["lookups"] - st0["lookups"]) - (st["hits"] - st0["hits"])
+    return {"elapsed": elapsed, "tok_s": steps / elapsed, "keys": keys, "hits": hits,
+            "timed_lookups": st["lookups"] - st0["lookups"], "timed_hits": st["hits"] - st0["hits"],
+            "misses_timed": misses_timed}
+
+
+def _streamed_setup(cfg):
+    import routed_expert_streaming_amd as moe
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload, HostRecordPool
+    t0 = time.time()
+    dw = DeviceWorkload(cfg, with_records=False)
+    x = dw.inputs()
+    hp = HostRecordPool(cfg, list(range(cfg.layers)))
+    log(f"host pool {len(hp.chunks)} chunks, {cfg.layers * cfg.E} records ready in {time.time() - t0:.1f} s")
+    return moe, dw, x, hp, [hp.table(L) for L in range(cfg.layers)]
+
+
+def _cold_tier(cfg, hp):
+    return {"records": cfg.layers * cfg.E, "pinned_records": hp.pinned_records,
+            "note": "the rest in pageable host memory (this host page-locks at most ~59 GiB)"}
+
+
 def bench_streamed(args, cfg) -> int:
     """K3-scale slice: 8 layers x 768 experts in pinned host memory, a 25%
     HBM slot cache (1536 slots) starting cold; one step = one token."""
+    import synth
+    n_tok = args.warmup + args.steps
+    if n_tok > cfg.tokens:
+        cfg = cfg.replace(tokens=n_tok)
+    moe, dw, x, hp, tables = _streamed_setup(cfg)
+    cap = cfg.cache_capacity
+    r = _streamed_run(moe, cfg, dw.layers, x, hp, tables, cap, args.warmup, args.steps)
+    hits = r["hits"]
+    per_tok = cfg.layers * cfg.k
+    half = (cfg.tokens // 2) * per_tok
+    tok_s = r["tok_s"]
+    hbm_bytes = synth.expert_bytes_per_token(cfg)
+    rec = {"metric": "streamed MoE decode tok/s on 1 MI355X (HBM LRU slot cache, misses over PCIe)",
+           "value": round(tok_s, 3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(r["elapsed"] * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32 accumulate, fp16 x RVQ-3bit weights", "data": "synthetic",
+           "config": {"workload": f"k3_slice streamed decode: {cfg.layers} layers x {cfg.E} experts, H {cfg.H}, "
+                                  f"I {cfg.I}, top-{cfg.k} sigmoid + shared, Zipf bias, cache {cap} slots",
+                      "tokens": cfg.tokens},
+           "hit_rate_all": round(float(hits.mean()), 4),
+           "hit_rate_second_half": round(float(hits[half:].mean()), 4) if len(hits) > half else None,
+           "misses_per_token_timed": round(r["misses_timed"] / args.steps, 2),
+           "h2d_gbs": round(r["misses_timed"] * hp.stride / r["elapsed"] / 1e9, 2),
+           "hbm_expert_gbs": round(hbm_bytes * tok_s / 1e9, 1),
+           "cold_tier": _cold_tier(cfg, hp),
+           "commit": git_commit()}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def bench_sweep_capacity(args, cfg) -> int:
+    """Hit rate against cache size (WARP's Table C shape) for every capacity in
+    one LRU stack-distance pass over the decode's key string, and measured
+    tok/s with cold caches of 1/16, 1/8, 1/4 and 1/2 of all records; each
+    measured hit count is checked against the one-pass prediction."""
+    n_tok = args.warmup + args.steps
+    if n_tok > cfg.tokens:
+        cfg = cfg.replace(tokens=n_tok)
+    moe, dw, x, hp, tables = _streamed_setup(cfg)
+    n_rec = cfg.layers * cfg.E
+    caps = [n_rec // 16, n_rec // 8, n_rec // 4, n_rec // 2]
+    runs, keys0, dist = [], None, None
+    for cap in caps:
+        r = _streamed_run(moe, cfg, dw.layers, x, hp, tables, cap, args.warmup, args.steps)
+        if keys0 is None:
+            keys0 = r["keys"]
+            dist = moe.lru_stack_distances(keys0)
+        if not (r["keys"].shape == keys0.shape and (r["keys"] == keys0).all()):
+            log("key strings differ between runs (routing is not deterministic)")
+            return 1
+        w0 = keys0.size - r["timed_lookups"]            # first reference of the timed window
+        pred_all = moe.lru_hits_at(dist, [cap])[0]
+        dt = dist[w0:]
+        pred_timed = int(((dt >= 0) & (dt < cap)).sum())
+        runs.append({"capacity": cap, "fraction": round(cap / n_rec, 4), "tok_s": round(r["tok_s"], 3),
+                     "hit_rate_all": round(float(r["hits"].mean()), 4),
+                     "hit_rate_timed": round(r["timed_hits"] / max(1, r["timed_lookups"]), 4),
+                     "predicted_hits_all": pred_all, "measured_hits_all": int(r["hits"].sum()),
+                     "predicted_hits_timed": pred_timed, "measured_hits_timed": int(r["timed_hits"]),
+                     "misses_per_token_timed": round(r["misses_timed"] / args.steps, 2),
+                     "h2d_gbs": round(r["misses_timed"] * hp.stride / r["elapsed"] / 1e9, 2)})
+        log(f"capacity {cap}: {runs[-1]}")
+    grid = sorted(set([cfg.k, 64, 128, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, n_rec]))
+    curve = [[c, round(h / keys0.size, 4)] for c, h in zip(grid, moe.lru_hits_at(dist, grid))]
+    ok = all(u["predicted_hits_all"] == u["measured_hits_all"] and u["predicted_hits_timed"] ==
+             u["measured_hits_timed"] for u in runs)
+    rec = {"metric": "streamed decode: hit rate and tok/s against HBM cache capacity (one MI355X)",
+           "value": runs[caps.index(cfg.cache_capacity)]["tok_s"] if cfg.cache_capacity in caps else None,
+           "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+           "data": "synthetic",
+           "config": {"workload": f"k3_slice streamed decode: {cfg.layers} layers x {cfg.E} experts, H {cfg.H}, "
+                                  f"I {cfg.I}, top-{cfg.k} sigmoid + shared, Zipf bias; cold caches",
+                      "tokens": n_tok, "references": int(keys0.size)},
+           "runs": runs, "hit_curve_all_tokens": curve, "prediction_matches": ok,
+           "cold_tier": _cold_tier(cfg, hp), "commit": git_commit()}
+    print(json.dumps(rec), flush=True)
+    return 0 if ok else 1
+
+
+def bench_sweep_k(args, cfg) -> int:
+    """Experts per token (WARP's num_experts_per_token) against decode speed:
+    k = 16, 8, 4 on the K3 slice, all records resident in HBM (the persistent
+    decode kernel) and streamed through a cold 25% cache.  Each k decodes the
+    inputs drawn for that k (same seeds, margin filter at that k)."""
+    import dataclasses
+
     import numpy as np
     import torch
 
@@ -272,61 +421,48 @@ def bench_streamed(args, cfg) -> int:
     import routed_expert_streaming_amd as moe
     from routed_expert_streaming_amd.device_workload import DeviceWorkload, HostRecordPool
     n_tok = args.warmup + args.steps
-    if n_tok > cfg.tokens:
-        cfg = cfg.replace(tokens=n_tok)
+    cfg = cfg.replace(tokens=max(cfg.tokens, n_tok))
     t0 = time.time()
-    dw = DeviceWorkload(cfg, with_records=False)
-    x = dw.inputs()
+    dw = DeviceWorkload(cfg)                         # records do not depend on k
     hp = HostRecordPool(cfg, list(range(cfg.layers)))
-    log(f"host pool {len(hp.chunks)} chunks, {cfg.layers * cfg.E} records ready in {time.time() - t0:.1f} s")
-    cap = cfg.cache_capacity
-    pool = torch.empty(cap * hp.stride, dtype=torch.uint8, device="cuda")
-    cache = moe.ExpertCache(cap, hp.stride, pool)
     tables = [hp.table(L) for L in range(cfg.layers)]
-    ws = torch.empty(moe.streamed_workspace_bytes(dw.layers[0]), dtype=torch.uint8, device="cuda")
-    out = torch.empty((cfg.tokens, cfg.layers, cfg.H), dtype=torch.float32, device="cuda")
-    copy_stream = torch.cuda.Stream()
-
-    def token(t):
-        for L in range(cfg.layers):
-            moe.layer_forward_streamed(dw.layers[L], cache, L, None, x[t, L][None], copy_stream, ws=ws,
-                                       out=out[t, L][None], host_table=tables[L])
-
-    # the cold start is part of the workload: warm-up tokens are decoded (and
-    # counted in the cache) but not timed
-    for t in range(args.warmup):
-        token(t)
-    torch.cuda.synchronize()
-    st0 = cache.stats()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        token(args.warmup + i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    st = cache.stats()
-    tr = cache.trace()
-    hits = np.array([r[1] for r in tr])
-    per_tok = cfg.layers * cfg.k
-    half = (cfg.tokens // 2) * per_tok
-    misses_timed = (st["lookups"] - st0["lookups"]) - (st["hits"] - st0["hits"])
-    tok_s = args.steps / elapsed
-    hbm_bytes = synth.expert_bytes_per_token(cfg)
-    rec = {"metric": "streamed MoE decode tok/s on 1 MI355X (HBM LRU slot cache, misses over PCIe)",
-           "value": round(tok_s, 3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(elapsed * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "f32 accumulate, fp16 x RVQ-3bit weights", "data": "synthetic",
-           "config": {"workload": f"k3_slice streamed decode: {cfg.layers} layers x {cfg.E} experts, H {cfg.H}, "
-                                  f"I {cfg.I}, top-{cfg.k} sigmoid + shared, Zipf bias, cache {cap} slots",
-                      "tokens": cfg.tokens},
-           "hit_rate_all": round(float(hits.mean()), 4),
-           "hit_rate_second_half": round(float(hits[half:].mean()), 4) if len(hits) > half else None,
-           "misses_per_token_timed": round(misses_timed / args.steps, 2),
-           "h2d_gbs": round(misses_timed * hp.stride / elapsed / 1e9, 2),
-           "hbm_expert_gbs": round(hbm_bytes * tok_s / 1e9, 1),
-           "cold_tier": {"records": cfg.layers * cfg.E, "pinned_records": hp.pinned_records,
-                         "note": "the rest in pageable host memory (this host page-locks at most ~59 GiB)"},
-           "commit": git_commit()}
-    cache.close()
+    log(f"resident and host records ready in {time.time() - t0:.1f} s")
+    runs = []
+    for kk in (16, 8, 4):
+        ck = cfg.replace(k=kk)
+        layers = [dataclasses.replace(l, router=dataclasses.replace(l.router, k=kk)) for l in dw.layers]
+        x = torch.from_numpy(np.ascontiguousarray(synth.Workload(ck).inputs())).to("cuda")
+        ws = torch.empty(moe.decode_workspace_bytes(layers), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(x)
+        for t in range(args.warmup):
+            moe.decode_forward(layers, x[t:t + 1], ws=ws, out=out[t:t + 1], want_idx=False)
+        torch.cuda.synchronize()
+        ts = time.perf_counter()
+        for i in range(args.steps):
+            t = args.warmup + i
+            moe.decode_forward(layers, x[t:t + 1], ws=ws, out=out[t:t + 1], want_idx=False)
+        torch.cuda.synchronize()
+        res_tok_s = args.steps / (time.perf_counter() - ts)
+        nbytes = synth.expert_bytes_per_token(ck)
+        r = _streamed_run(moe, ck, layers, x, hp, tables, cfg.cache_capacity, args.warmup, args.steps)
+        runs.append({"k": kk, "expert_bytes_per_token": nbytes,
+                     "resident_tok_s": round(res_tok_s, 2),
+                     "resident_expert_gbs": round(nbytes * res_tok_s / 1e9, 1),
+                     "streamed_tok_s": round(r["tok_s"], 3),
+                     "streamed_hit_rate_timed": round(r["timed_hits"] / max(1, r["timed_lookups"]), 4),
+                     "streamed_misses_per_token_timed": round(r["misses_timed"] / args.steps, 2)})
+        log(f"k={kk}: {runs[-1]}")
+    base = runs[0]
+    for u in runs:
+        u["resident_speedup_vs_k16"] = round(u["resident_tok_s"] / base["resident_tok_s"], 3)
+        u["streamed_speedup_vs_k16"] = round(u["streamed_tok_s"] / base["streamed_tok_s"], 3)
+    rec = {"metric": "decode tok/s against experts per token k (one MI355X)", "value": base["resident_tok_s"],
+           "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+           "data": "synthetic",
+           "config": {"workload": f"k3_slice decode: {cfg.layers} layers x {cfg.E} experts, H {cfg.H}, I {cfg.I}, "
+                                  f"sigmoid top-k + shared, Zipf bias; streamed runs use a cold "
+                                  f"{cfg.cache_capacity}-slot cache"},
+           "runs": runs, "cold_tier": _cold_tier(cfg, hp), "commit": git_commit()}
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -269,6 +269,20 @@ int expert_cache_trace_reset(moe_cache *c);
 int expert_cache_stats(moe_cache *c, int64_t *lookups, int64_t *hits, int64_t *inserts,
                        int64_t *evictions);
 
+/* LRU stack distances of a reference string of cache keys (hit rate against
+ * cache size, WARP "WARP의 캐시 설정에서 드러나는 역설", Table C), computed in
+ * one pass by the stack algorithm of Mattson et al. (1970): dist[i] = number
+ * of distinct keys referenced since the previous reference to keys[i] (0 =
+ * it was the most recent), or -1 for its first reference.  The expert cache's
+ * policy (hit -> MRU; miss -> insert at MRU, evict the LRU key when full) is
+ * LRU over the key sequence of its trace, so a cache of capacity C started
+ * empty hits exactly the references with 0 <= dist[i] < C: one pass gives
+ * the hit count at every capacity.  Host-only, O(n log n) time, O(n) memory.
+ *   keys [host] n keys;  dist [host] n int32 (caller-owned)
+ * MOE_E_INVAL if n < 0, n > INT32_MAX, or keys/dist NULL with n > 0;
+ * MOE_E_SPACE if host memory runs out. */
+int moe_lru_stack_distances(const uint32_t *keys, int64_t n, int32_t *dist);
+
 /* Workspace bytes that moe_layer_forward_streamed needs for T tokens. */
 size_t moe_streamed_workspace_bytes(const moe_layer *L, int32_t T);
 

@@ -3,7 +3,8 @@
 Python face of libmoe (include/moe.h): torch supplies device memory and
 streams; every computation runs in the library's HIP kernels.  Names follow
 the C ABI: route_topk, expert_ffn_rvq, layer_forward, decode_forward,
-layer_forward_grouped, ExpertCache (expert_cache_*), layer_forward_streamed.
+layer_forward_grouped, ExpertCache (expert_cache_*), layer_forward_streamed,
+lru_stack_distances.
 """
 from __future__ import annotations
 
@@ -278,6 +279,27 @@ class ExpertCache:
         v = [ctypes.c_int64() for _ in range(4)]
         check(lib().expert_cache_stats(self.handle, *[ctypes.byref(x) for x in v]), "expert_cache_stats")
         return dict(zip(("lookups", "hits", "inserts", "evictions"), [x.value for x in v]))
+
+
+def lru_stack_distances(keys) -> "numpy.ndarray":
+    """LRU stack distance of each reference in a sequence of cache keys
+    (moe_lru_stack_distances): -1 at a first reference, else the number of
+    distinct keys referenced since the previous reference to the same key."""
+    import numpy as np
+    k = np.ascontiguousarray(keys, dtype=np.uint32)
+    d = np.empty(k.shape[0], dtype=np.int32)
+    check(lib().moe_lru_stack_distances(k.ctypes.data if k.size else None, k.shape[0],
+                                        d.ctypes.data if d.size else None), "moe_lru_stack_distances")
+    return d
+
+
+def lru_hits_at(dist, capacities: Sequence[int]) -> List[int]:
+    """Hits of an LRU cache of each capacity, started empty, on the reference
+    string whose stack distances are dist (a reference hits iff 0 <= d < C)."""
+    import numpy as np
+    d = np.asarray(dist)
+    warm = np.sort(d[d >= 0])
+    return [int(np.searchsorted(warm, c, side="left")) for c in capacities]
 
 
 def streamed_workspace_bytes(layer: Layer, T: int = 1) -> int:

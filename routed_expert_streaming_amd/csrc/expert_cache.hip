@@ -9,6 +9,7 @@
 // aligned record per expert, so a miss costs exactly one transfer).
 #include "expert_cache.h"
 
+#include <climits>
 #include <new>
 
 namespace moe {
@@ -149,6 +150,18 @@ int expert_cache_trace(moe_cache *c, moe_trace_rec *buf, int64_t cap, int64_t *n
 int expert_cache_trace_reset(moe_cache *c) {
     if (!c) return fail(MOE_E_INVAL, "cache is NULL");
     c->core.trace_reset();
+    return MOE_OK;
+}
+
+int moe_lru_stack_distances(const uint32_t *keys, int64_t n, int32_t *dist) {
+    if (n < 0) return fail(MOE_E_INVAL, "n=%lld < 0", (long long)n);
+    if (n > 0 && (!keys || !dist)) return fail(MOE_E_INVAL, "keys and dist must be non-NULL");
+    if (n > INT32_MAX) return fail(MOE_E_INVAL, "n=%lld exceeds the 32-bit distance range", (long long)n);
+    try {
+        lru_stack_distances(keys, n, dist);
+    } catch (const std::bad_alloc &) {
+        return fail(MOE_E_SPACE, "out of host memory for %lld references", (long long)n);
+    }
     return MOE_OK;
 }
 

@@ -77,4 +77,35 @@ std::vector<uint32_t> LruCore::order() const {
     return v;
 }
 
+// LRU stack distances in one pass (Mattson, Gecsei, Slutz and Traiger,
+// "Evaluation techniques for storage hierarchies", 1970): a Fenwick tree over
+// reference times holds a 1 at each key's latest reference, so the distinct
+// keys referenced since key k's previous reference p are the ones in (p, i).
+void lru_stack_distances(const uint32_t *keys, int64_t n, int32_t *dist) {
+    std::vector<int32_t> tree((size_t)n + 1, 0);
+    auto add = [&](int64_t i, int32_t v) {
+        for (++i; i <= n; i += i & -i) tree[(size_t)i] += v;
+    };
+    auto prefix = [&](int64_t i) {   // sum over positions [0, i)
+        int64_t s = 0;
+        for (; i > 0; i -= i & -i) s += tree[(size_t)i];
+        return s;
+    };
+    std::unordered_map<uint32_t, int64_t> last;
+    last.reserve((size_t)n);
+    for (int64_t i = 0; i < n; i++) {
+        auto it = last.find(keys[i]);
+        if (it == last.end()) {
+            dist[i] = -1;
+            last.emplace(keys[i], i);
+        } else {
+            const int64_t p = it->second;
+            dist[i] = (int32_t)(prefix(i) - prefix(p + 1));
+            add(p, -1);
+            it->second = i;
+        }
+        add(i, 1);
+    }
+}
+
 }  // namespace moe

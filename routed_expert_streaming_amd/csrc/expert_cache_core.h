@@ -72,4 +72,9 @@ private:
     std::vector<CacheTraceRec> trace_;
 };
 
+// dist[i] = distinct keys referenced since the previous reference to
+// keys[i] (0: it was the most recent one), or -1 at a first reference.  An
+// LRU cache of capacity C hits exactly the references with 0 <= dist < C.
+void lru_stack_distances(const uint32_t *keys, int64_t n, int32_t *dist);
+
 }  // namespace moe

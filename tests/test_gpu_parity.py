@@ -171,6 +171,12 @@ def test_decode_forward_k3_shape_shared(moe):
     _check_decode(moe, synth.get_config("k3_slice", tokens=2, layers=2))
 
 
+@pytest.mark.parametrize("k", [4, 8])
+def test_decode_forward_k3_shape_fewer_experts_per_token(moe, k):
+    # num_experts_per_token below the K3 default of 16 (the k sweep's settings)
+    _check_decode(moe, synth.get_config("k3_slice", tokens=2, layers=2, k=k))
+
+
 def test_decode_forward_mixtral_full_size(moe):
     # the configuration bench.py times: all 32 layers, 8 resident experts each
     _check_decode(moe, synth.get_config("mixtral", tokens=2))
