@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # valid for the kernel source they were taken on: reported as null once that
 # source has changed.
 DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
-                  "sha256_prefix": "83d09abc5f859a2c", "bytes_per_launch": 4681542778}
+                  "sha256_prefix": "e59bda19a41ef11e", "bytes_per_launch": 4681107717}
 
 
 def measured_traffic():
