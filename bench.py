@@ -107,9 +107,10 @@ def main() -> int:
     ap.add_argument("--config", default="mixtral", choices=["mixtral", "kimi_linear", "batched", "k3_slice"],
                     help="mixtral / kimi_linear: resident decode; batched: one 256-token grouped layer call "
                          "per step; k3_slice: streamed decode through the HBM slot cache (cold start)")
-    ap.add_argument("--sweep", choices=["capacity", "k"], default=None,
+    ap.add_argument("--sweep", choices=["capacity", "k", "ahead"], default=None,
                     help="k3_slice only: hit rate and tok/s against cache capacity (one stack-distance pass "
-                         "plus measured runs), or tok/s against experts per token")
+                         "plus measured runs), tok/s against experts per token, or look-ahead reads on "
+                         "chained inputs")
     ap.add_argument("--cpu-sample-tokens", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -151,6 +152,8 @@ def main() -> int:
         return bench_sweep_capacity(args, cfg)
     if args.sweep == "k":
         return bench_sweep_k(args, cfg)
+    if args.sweep == "ahead":
+        return bench_sweep_ahead(args, cfg)
     if args.config == "k3_slice":
         return bench_streamed(args, cfg)
     n_tok = args.warmup + args.steps
@@ -403,6 +406,94 @@ def bench_sweep_capacity(args, cfg) -> int:
                       "tokens": n_tok, "references": int(keys0.size)},
            "runs": runs, "hit_curve_all_tokens": curve, "prediction_matches": ok,
            "cold_tier": _cold_tier(cfg, hp), "commit": git_commit()}
+    print(json.dumps(rec), flush=True)
+    return 0 if ok else 1
+
+
+def bench_sweep_ahead(args, cfg) -> int:
+    """Look-ahead reads (WARP's pre-read router) on the chained K3 slice: each
+    layer reads the rescaled residual stream of the previous layers' outputs,
+    so the next layer's router applied to this layer's input is a prediction.
+    Cold 25% cache; runs without look-ahead and with k_ahead = k and k/2;
+    outputs must be identical bit for bit."""
+    import numpy as np
+    import torch
+
+    from routed_expert_streaming_amd.device_workload import chain_next_input
+    n_tok = args.warmup + args.steps
+    if n_tok > cfg.tokens:
+        cfg = cfg.replace(tokens=n_tok)
+    moe, dw, x, hp, tables = _streamed_setup(cfg)
+    cap = cfg.cache_capacity
+    ws = torch.empty(moe.streamed_workspace_bytes(dw.layers[0]), dtype=torch.uint8, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    runs, ref_out = [], None
+    for k_ahead in (0, cfg.k, cfg.k // 2):
+        pool = torch.empty(cap * hp.stride, dtype=torch.uint8, device="cuda")
+        cache = moe.ExpertCache(cap, hp.stride, pool)
+        out = torch.empty((n_tok, cfg.layers, cfg.H), dtype=torch.float32, device="cuda")
+
+        def token(t):
+            h = x[t, 0].clone()
+            scale = h.pow(2).mean().sqrt()
+            xin = x[t, 0][None].contiguous()
+            for L in range(cfg.layers):
+                ahead = None
+                if k_ahead and L + 1 < cfg.layers:
+                    ahead = (dw.layers[L + 1], L + 1, tables[L + 1], k_ahead)
+                moe.layer_forward_streamed(dw.layers[L], cache, L, None, xin, copy_stream, ws=ws,
+                                           out=out[t, L][None], host_table=tables[L], ahead=ahead)
+                xin = chain_next_input(h, out[t, L], scale)
+
+        for t in range(args.warmup):
+            token(t)
+        torch.cuda.synchronize()
+        st0 = cache.stats()
+        ts = time.perf_counter()
+        for i in range(args.steps):
+            token(args.warmup + i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - ts
+        st = cache.stats()
+        tr = cache.trace()
+        cache.close()
+        del pool
+        # prediction quality from the operation string: per (t, L) k lookups,
+        # then k_ahead touches of layer L + 1 (not after the last layer)
+        pos, inter, npred = 0, 0, 0
+        pending = None
+        for t in range(n_tok):
+            for L in range(cfg.layers):
+                look = set(r[0] for r in tr[pos:pos + cfg.k])
+                pos += cfg.k
+                if pending is not None:
+                    inter += len(pending & look)
+                    npred += len(pending)
+                    pending = None
+                if k_ahead and L + 1 < cfg.layers:
+                    pending = set(r[0] for r in tr[pos:pos + k_ahead])
+                    pos += k_ahead
+        if ref_out is None:
+            ref_out = out
+        d = {k2: st[k2] - st0[k2] for k2 in st}
+        runs.append({"k_ahead": k_ahead, "tok_s": round(args.steps / elapsed, 3),
+                     "hit_rate_timed": round(d["hits"] / max(1, d["lookups"]), 4),
+                     "demand_misses_per_token": round((d["lookups"] - d["hits"]) / args.steps, 2),
+                     "ahead_copies_per_token": round(d["ahead_inserted"] / args.steps, 2),
+                     "ahead_copies_used_per_token": round(d["ahead_used"] / args.steps, 2),
+                     "wasted_copy_gb_per_token": round(d["ahead_wasted"] * hp.stride / args.steps / 1e9, 3),
+                     "h2d_gb_per_token": round((d["inserts"]) * hp.stride / args.steps / 1e9, 3),
+                     "prediction_precision": round(inter / npred, 4) if npred else None,
+                     "outputs_identical": bool(torch.equal(out, ref_out))})
+        log(f"k_ahead={k_ahead}: {runs[-1]}")
+    ok = all(u["outputs_identical"] for u in runs)
+    rec = {"metric": "chained streamed decode tok/s with and without look-ahead reads (one MI355X)",
+           "value": runs[1]["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "data": "synthetic; chained inputs (rescaled residual stream)",
+           "config": {"workload": f"k3_slice streamed decode, chained: {cfg.layers} layers x {cfg.E} experts, "
+                                  f"H {cfg.H}, I {cfg.I}, top-{cfg.k} sigmoid + shared, Zipf bias, cold cache "
+                                  f"of {cap} slots"},
+           "runs": runs, "outputs_identical": ok, "cold_tier": _cold_tier(cfg, hp), "commit": git_commit()}
     print(json.dumps(rec), flush=True)
     return 0 if ok else 1
 

@@ -124,7 +124,8 @@ typedef struct moe_cache moe_cache;
 /* One cache lookup of a streamed decode (expert_cache_trace). */
 typedef struct moe_trace_rec {
     uint32_t key;       /* layer_id * E + expert                                  */
-    int32_t hit;        /* 1 = hit, 0 = miss                                      */
+    int32_t hit;        /* 1 = hit, 0 = miss; look-ahead touches (not lookups):   */
+                        /* 2 = inserted ahead, 3 = already present (moved to MRU) */
     int32_t slot;       /* slot holding the key after the lookup                  */
     uint32_t evicted;   /* key evicted by this miss, or MOE_NO_KEY                */
 } moe_trace_rec;
@@ -265,6 +266,12 @@ int expert_cache_trace(moe_cache *c, moe_trace_rec *buf, int64_t cap, int64_t *n
 /* Clear the trace (the cache contents stay). */
 int expert_cache_trace_reset(moe_cache *c);
 
+/* Look-ahead counters since creation: keys inserted ahead (copies), keys
+ * found present, inserted keys later hit by a lookup, and inserted keys
+ * evicted before any lookup (wasted copies).  Any pointer may be NULL. */
+int expert_cache_stats_ahead(moe_cache *c, int64_t *inserted, int64_t *present, int64_t *used,
+                             int64_t *wasted);
+
 /* Counters since creation: lookups, hits, inserts (copies), evictions. */
 int expert_cache_stats(moe_cache *c, int64_t *lookups, int64_t *hits, int64_t *inserts,
                        int64_t *evictions);
@@ -302,6 +309,32 @@ int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_
                                const void *const *experts_host, const float *x, int32_t T,
                                float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
                                void *compute_stream, void *copy_stream);
+
+/* moe_layer_forward_streamed plus a look-ahead read (WARP "WARP가 모델을 램에
+ * 올리지 않는 방법": a pre-read router guesses the next layer's experts so their
+ * reads start early, while the real router still decides; WISP "더블 버퍼
+ * 비동기 파이프라인": loads for the next step overlap this step's compute).
+ * The next layer's router (next->router weights and bias, k_ahead experts) is
+ * applied to this layer's input x on compute_stream, with this layer's own
+ * routing and the same single host sync.  After this layer's work is queued
+ * (and its slots released), the predicted keys next_layer_id * E_next + e are
+ * touched in the cache in ascending e, like lookups that count as neither
+ * hit nor miss (trace kinds 2 and 3): an absent key is inserted (evicting the
+ * LRU key if full) and copied from next_experts_host[e] on copy_stream behind
+ * this layer's miss copies; its copy waits for the victim slot's last
+ * readers.  Outputs are those of moe_layer_forward_streamed bit for bit: the
+ * prediction changes only which copies happen and when.
+ *   next [host] the next layer (its records are not read; H must match)
+ *   next_experts_host [host] array of E_next [pinned] record pointers
+ *   k_ahead in 1..min(E_next, MOE_MAX_K, capacity)
+ * MOE_E_INVAL on a NULL next or bad arguments, as well as the conditions of
+ * moe_layer_forward_streamed.  ws: moe_streamed_workspace_bytes(L, T). */
+int moe_layer_forward_streamed_ahead(const moe_layer *L, moe_cache *c, uint32_t layer_id,
+                                     const void *const *experts_host, const float *x, int32_t T,
+                                     float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
+                                     void *compute_stream, void *copy_stream, const moe_layer *next,
+                                     uint32_t next_layer_id, const void *const *next_experts_host,
+                                     int32_t k_ahead);
 
 #ifdef __cplusplus
 }

@@ -276,9 +276,12 @@ class ExpertCache:
         check(lib().expert_cache_trace_reset(self.handle), "expert_cache_trace_reset")
 
     def stats(self):
-        v = [ctypes.c_int64() for _ in range(4)]
-        check(lib().expert_cache_stats(self.handle, *[ctypes.byref(x) for x in v]), "expert_cache_stats")
-        return dict(zip(("lookups", "hits", "inserts", "evictions"), [x.value for x in v]))
+        v = [ctypes.c_int64() for _ in range(8)]
+        check(lib().expert_cache_stats(self.handle, *[ctypes.byref(x) for x in v[:4]]), "expert_cache_stats")
+        check(lib().expert_cache_stats_ahead(self.handle, *[ctypes.byref(x) for x in v[4:]]),
+              "expert_cache_stats_ahead")
+        return dict(zip(("lookups", "hits", "inserts", "evictions", "ahead_inserted", "ahead_present",
+                         "ahead_used", "ahead_wasted"), [x.value for x in v]))
 
 
 def lru_stack_distances(keys) -> "numpy.ndarray":
@@ -310,16 +313,27 @@ def streamed_workspace_bytes(layer: Layer, T: int = 1) -> int:
 def layer_forward_streamed(layer: Layer, cache: ExpertCache, layer_id: int, experts_host: Sequence[int],
                            x: torch.Tensor, copy_stream: torch.cuda.Stream, stream=None,
                            ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                           idx: Optional[torch.Tensor] = None, host_table=None):
+                           idx: Optional[torch.Tensor] = None, host_table=None, ahead=None):
     """One decode step of one layer fed from the slot cache.  experts_host:
-    E pinned host addresses of the layer's records (or a prebuilt ctypes array)."""
+    E pinned host addresses of the layer's records (or a prebuilt ctypes
+    array).  ahead = (next_layer, next_layer_id, next_host_table, k_ahead)
+    adds the look-ahead read of moe_layer_forward_streamed_ahead."""
     _need(x.dim() == 2 and x.shape[0] == 1 and x.dtype == torch.float32, "x must be fp32 [1, H]")
     out = out if out is not None else torch.empty((1, layer.H), dtype=torch.float32, device=x.device)
     s = layer.struct()
     table = host_table if host_table is not None else (ctypes.c_void_p * len(experts_host))(*experts_host)
     need = lib().moe_streamed_workspace_bytes(ctypes.byref(s), 1)
     ws = ws if ws is not None else _ws(need, x.device)
-    check(lib().moe_layer_forward_streamed(ctypes.byref(s), cache.handle, layer_id, table, _ptr(x), 1, _ptr(out),
-                                           _ptr(idx), _ptr(ws), ws.numel(), _stream(stream), _stream(copy_stream)),
-          "moe_layer_forward_streamed")
+    if ahead is None:
+        check(lib().moe_layer_forward_streamed(ctypes.byref(s), cache.handle, layer_id, table, _ptr(x), 1, _ptr(out),
+                                               _ptr(idx), _ptr(ws), ws.numel(), _stream(stream),
+                                               _stream(copy_stream)), "moe_layer_forward_streamed")
+        return out
+    nxt, nxt_id, nxt_host, k_ahead = ahead
+    ns = nxt.struct()
+    ntable = nxt_host if not isinstance(nxt_host, (list, tuple)) else (ctypes.c_void_p * len(nxt_host))(*nxt_host)
+    check(lib().moe_layer_forward_streamed_ahead(ctypes.byref(s), cache.handle, layer_id, table, _ptr(x), 1,
+                                                 _ptr(out), _ptr(idx), _ptr(ws), ws.numel(), _stream(stream),
+                                                 _stream(copy_stream), ctypes.byref(ns), nxt_id, ntable, k_ahead),
+          "moe_layer_forward_streamed_ahead")
     return out

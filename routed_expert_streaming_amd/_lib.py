@@ -67,6 +67,10 @@ SIGNATURES = {
     "expert_cache_stats": (ctypes.c_int, [P, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                           ctypes.POINTER(I64), ctypes.POINTER(I64)]),
     "moe_lru_stack_distances": (ctypes.c_int, [P, I64, P]),
+    "expert_cache_stats_ahead": (ctypes.c_int, [P, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                                ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+    "moe_layer_forward_streamed_ahead": (ctypes.c_int, [ctypes.POINTER(MoeLayer), P, U32, P, P, I32, P, P,
+                                                        P, SZ, P, P, ctypes.POINTER(MoeLayer), U32, P, I32]),
     "moe_streamed_workspace_bytes": (SZ, [ctypes.POINTER(MoeLayer), I32]),
     "moe_layer_forward_streamed": (ctypes.c_int, [ctypes.POINTER(MoeLayer), P, U32, P, P, I32, P, P,
                                                   P, SZ, P, P]),

@@ -71,7 +71,7 @@ int expert_cache_create(int32_t capacity, uint64_t slot_bytes, void *pool_dev, m
         e = hipEventCreateWithFlags(&c->ready[s], hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&c->last_use[s], hipEventDisableTiming);
     }
-    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_idx, MOE_MAX_K * sizeof(int32_t), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_idx, 2 * MOE_MAX_K * sizeof(int32_t), hipHostMallocDefault);
     if (e != hipSuccess) {
         destroy_events(c);
         delete c;
@@ -162,6 +162,15 @@ int moe_lru_stack_distances(const uint32_t *keys, int64_t n, int32_t *dist) {
     } catch (const std::bad_alloc &) {
         return fail(MOE_E_SPACE, "out of host memory for %lld references", (long long)n);
     }
+    return MOE_OK;
+}
+
+int expert_cache_stats_ahead(moe_cache *c, int64_t *inserted, int64_t *present, int64_t *used, int64_t *wasted) {
+    if (!c) return fail(MOE_E_INVAL, "cache is NULL");
+    if (inserted) *inserted = c->core.ahead_inserts;
+    if (present) *present = c->core.ahead_present;
+    if (used) *used = c->core.ahead_used;
+    if (wasted) *wasted = c->core.ahead_wasted;
     return MOE_OK;
 }
 

@@ -4,7 +4,7 @@
 namespace moe {
 
 LruCore::LruCore(int capacity)
-    : capacity_(capacity), key_of_(capacity, kNoKey), prev_(capacity, -1), next_(capacity, -1) {
+    : capacity_(capacity), key_of_(capacity, kNoKey), ahead_(capacity, 0), prev_(capacity, -1), next_(capacity, -1) {
     map_.reserve((size_t)capacity * 2);
     for (int s = 0; s < capacity; s++) free_.insert(s);
 }
@@ -31,9 +31,13 @@ int LruCore::lookup(uint32_t key) {
     if (it == map_.end()) return -1;
     const int s = it->second;
     hits++;
+    if (ahead_[s]) {
+        ahead_used++;
+        ahead_[s] = 0;
+    }
     unlink(s);
     push_front(s);
-    trace_.push_back({key, 1, s, kNoKey});
+    trace_.push_back({key, kTraceHit, s, kNoKey});
     return s;
 }
 
@@ -47,24 +51,51 @@ int LruCore::plan_insert(uint32_t key, uint32_t *victim) const {
     return tail_;
 }
 
-void LruCore::commit_insert(uint32_t key, int slot, uint32_t victim) {
+void LruCore::insert_at(uint32_t key, int slot, uint32_t victim, int32_t kind) {
     if (victim != kNoKey) {
         map_.erase(victim);
         unlink(slot);
         evictions++;
+        if (ahead_[slot]) ahead_wasted++;
     } else {
         free_.erase(slot);
     }
     key_of_[slot] = key;
     map_[key] = slot;
+    ahead_[slot] = kind == kTraceAheadInsert;
     push_front(slot);
     inserts++;
-    trace_.push_back({key, 0, slot, victim});
+    trace_.push_back({key, kind, slot, victim});
+}
+
+void LruCore::commit_insert(uint32_t key, int slot, uint32_t victim) {
+    insert_at(key, slot, victim, kTraceMiss);
+}
+
+int LruCore::touch_ahead(uint32_t key, uint32_t *victim, bool *inserted) {
+    auto it = map_.find(key);
+    if (it != map_.end()) {
+        const int s = it->second;
+        unlink(s);
+        push_front(s);
+        ahead_present++;
+        trace_.push_back({key, kTraceAheadPresent, s, kNoKey});
+        *victim = kNoKey;
+        *inserted = false;
+        return s;
+    }
+    const int s = plan_insert(key, victim);
+    insert_at(key, s, *victim, kTraceAheadInsert);
+    ahead_inserts++;
+    *inserted = true;
+    return s;
 }
 
 void LruCore::drop_slot(int slot) {
     const uint32_t k = key_of_[slot];
     if (k == kNoKey) return;
+    if (ahead_[slot]) ahead_wasted++;
+    ahead_[slot] = 0;
     map_.erase(k);
     unlink(slot);
     key_of_[slot] = kNoKey;

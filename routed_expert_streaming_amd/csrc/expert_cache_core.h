@@ -9,6 +9,7 @@
 // key is evicted and its slot reused; the new key becomes most-recently-used.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 #include <set>
 #include <unordered_map>
@@ -18,9 +19,17 @@ namespace moe {
 
 constexpr uint32_t kNoKey = 0xFFFFFFFFu;
 
+// Trace record kinds (CacheTraceRec::hit).
+enum TraceKind : int32_t {
+    kTraceMiss = 0,          // lookup missed; the key was inserted
+    kTraceHit = 1,           // lookup hit; the key moved to MRU
+    kTraceAheadInsert = 2,   // look-ahead: key absent, inserted ahead of its lookup
+    kTraceAheadPresent = 3,  // look-ahead: key present, moved to MRU
+};
+
 struct CacheTraceRec {
     uint32_t key;
-    int32_t hit;
+    int32_t hit;        // TraceKind
     int32_t slot;
     uint32_t evicted;   // kNoKey if none
 };
@@ -45,6 +54,13 @@ public:
     // MRU and append a miss record.
     void commit_insert(uint32_t key, int slot, uint32_t victim);
 
+    // Look-ahead touch of a key predicted for a later lookup: present -> move
+    // to MRU (a kTraceAheadPresent record); absent -> insert exactly like a
+    // miss (kTraceAheadInsert record, *inserted = true).  Returns the slot.
+    // Either way the LRU order changes as it would for a lookup of the key,
+    // but the lookup and hit counters do not.
+    int touch_ahead(uint32_t key, uint32_t *victim, bool *inserted);
+
     // Forget whatever key a slot holds (the slot becomes free).
     void drop_slot(int slot);
 
@@ -58,6 +74,9 @@ public:
     void trace_reset() { trace_.clear(); }
 
     int64_t lookups = 0, hits = 0, inserts = 0, evictions = 0;
+    // look-ahead: keys inserted ahead, keys found present, inserted keys later
+    // hit by a lookup, inserted keys evicted (or dropped) before any lookup
+    int64_t ahead_inserts = 0, ahead_present = 0, ahead_used = 0, ahead_wasted = 0;
 
 private:
     void unlink(int s);
@@ -65,7 +84,10 @@ private:
 
     int capacity_;
     std::unordered_map<uint32_t, int> map_;
+    void insert_at(uint32_t key, int slot, uint32_t victim, int32_t kind);
+
     std::vector<uint32_t> key_of_;
+    std::vector<uint8_t> ahead_;     // slot holds a key inserted ahead and not looked up since
     std::vector<int> prev_, next_;
     int head_ = -1, tail_ = -1;
     std::set<int> free_;

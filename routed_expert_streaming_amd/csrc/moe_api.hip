@@ -421,13 +421,28 @@ int moe_decode_status(const void *ws, int32_t *timed_out) {
     return MOE_OK;
 }
 
+// Look-ahead region after the layer's own workspace: the next layer's
+// logits, predicted ids and (unused) weights.
+constexpr size_t kAheadBytes = MOE_MAX_E * sizeof(float) + 256 + 2 * MOE_MAX_K * sizeof(float) + 256;
+
 size_t moe_streamed_workspace_bytes(const moe_layer *L, int32_t T) {
-    return moe_layer_workspace_bytes(L, T);
+    const size_t b = moe_layer_workspace_bytes(L, T);
+    return b ? b + kAheadBytes : 0;
 }
 
-int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_id, const void *const *experts_host,
-                               const float *x, int32_t T, float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
-                               void *compute_stream, void *copy_stream) {
+}  // extern "C"
+
+namespace {
+struct Ahead {
+    const moe_layer *L = nullptr;          // next layer, or null: no look-ahead
+    uint32_t layer_id = 0;
+    const void *const *host = nullptr;
+    int k = 0;
+};
+
+int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const void *const *experts_host,
+                  const float *x, int32_t T, float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
+                  void *compute_stream, void *copy_stream, const Ahead &ah) {
     int rc = check_layer(L, false);
     if (rc) return rc;
     if (!c) return fail(MOE_E_INVAL, "cache is NULL");
@@ -447,8 +462,31 @@ int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_
         return fail(MOE_E_INVAL, "layer_id * E overflows the 32-bit key");
     const size_t need = moe_streamed_workspace_bytes(L, T);
     if (ws_bytes < need) return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (ah.L) {
+        rc = check_layer(ah.L, false);
+        if (rc) return rc;
+        if (ah.L->H != H) return fail(MOE_E_INVAL, "next layer H=%d differs from this layer's %d", ah.L->H, H);
+        if (ah.k < 1 || ah.k > ah.L->router.E || ah.k > MOE_MAX_K || ah.k > c->core.capacity())
+            return fail(MOE_E_INVAL, "look-ahead k=%d must be in 1..min(E, %d, capacity)", ah.k, MOE_MAX_K);
+        if (!ah.host) return fail(MOE_E_INVAL, "next layer's experts_host is NULL");
+        if ((uint64_t)ah.layer_id * (uint64_t)ah.L->router.E + (uint64_t)ah.L->router.E - 1 >= (uint64_t)MOE_NO_KEY)
+            return fail(MOE_E_INVAL, "next layer_id * E overflows the 32-bit key");
+        moe_record_layout nlay;
+        layout_of(ah.L->H, ah.L->I, &nlay);
+        if ((int64_t)c->slot_bytes < nlay.nbytes)
+            return fail(MOE_E_INVAL, "slot size is below the next layer's record size");
+    }
     hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
     const LayerWs W = carve_layer(ws, H, I, E, k, 1, L->shared != nullptr);
+    float *za = nullptr, *wa = nullptr;
+    int32_t *ia = nullptr;
+    {
+        Carver ca((char *)ws + moe_layer_workspace_bytes(L, T));
+        za = ca.take<float>(MOE_MAX_E);
+        ia = ca.take<int32_t>(MOE_MAX_K);
+        wa = ca.take<float>(MOE_MAX_K);
+    }
+    int32_t *h_ahead = c->h_idx + MOE_MAX_K;
     int32_t *idx = idx_out ? idx_out : W.idx;
     const RecOffsets off = offsets_of(H, I);
     const int KS = down_splits(H, I, k);
@@ -457,6 +495,13 @@ int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_
     HIPCHK(launch_route_logits(L->router.weight, L->router.bias, E, H, x, MOE_DTYPE_F32, 1, W.z, cs), "route logits");
     HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, 1, idx, W.w, cs), "top-k");
     HIPCHK(hipMemcpyAsync(c->h_idx, idx, k * sizeof(int32_t), hipMemcpyDeviceToHost, cs), "idx to host");
+    if (ah.L) {
+        // the next layer's router on this layer's input: a prediction only
+        HIPCHK(launch_route_logits(ah.L->router.weight, ah.L->router.bias, ah.L->router.E, H, x, MOE_DTYPE_F32, 1, za,
+                                   cs), "look-ahead logits");
+        HIPCHK(launch_topk(za, ah.L->router.E, ah.k, ah.L->router.score_fn, 1, ia, wa, cs), "look-ahead top-k");
+        HIPCHK(hipMemcpyAsync(h_ahead, ia, ah.k * sizeof(int32_t), hipMemcpyDeviceToHost, cs), "look-ahead ids");
+    }
     HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, 1, H, H, W.xh, cs), "pack_x");
     if (L->shared) {
         HIPCHK(launch_dense_gateup(L->shared, H, I, x, MOE_DTYPE_F32, H, 1, W.hs, cs), "shared gate/up");
@@ -537,7 +582,62 @@ int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_
         rc = cache_release(c, slot_of[j], cs);
         if (rc) return rc;
     }
+    if (!ah.L) return MOE_OK;
+    // look-ahead: the predicted keys of the next layer (ascending id) are
+    // touched in the LRU; the absent ones are copied now, behind this layer's
+    // misses on the copy stream, so they land while this layer computes.  A
+    // victim slot's copy still waits for that slot's last readers.
+    int pred[MOE_MAX_K];
+    const int En = ah.L->router.E;
+    for (int j = 0; j < ah.k; j++) {
+        pred[j] = h_ahead[j];
+        if (pred[j] < 0 || pred[j] >= En) return fail(MOE_E_HIP, "look-ahead router produced expert id %d", pred[j]);
+        if (!ah.host[pred[j]]) return fail(MOE_E_INVAL, "next layer's experts_host[%d] is NULL", pred[j]);
+    }
+    std::sort(pred, pred + ah.k);
+    for (int j = 0; j < ah.k; j++) {
+        const uint32_t key = ah.layer_id * (uint32_t)En + (uint32_t)pred[j];
+        uint32_t victim = kNoKey;
+        bool inserted = false;
+        const int32_t s = c->core.touch_ahead(key, &victim, &inserted);
+        if (!inserted) continue;
+        c->filled[s] = 0;
+        if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "look-ahead copy waits for slot readers");
+        hipError_t e = hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, ah.host[pred[j]], c->slot_bytes,
+                                      hipMemcpyHostToDevice, ps);
+        if (e == hipSuccess) e = hipEventRecord(c->ready[s], ps);
+        if (e != hipSuccess) {
+            c->core.drop_slot(s);
+            return hip_fail(e, "look-ahead copy");
+        }
+        c->filled[s] = 1;
+    }
     return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_id, const void *const *experts_host,
+                               const float *x, int32_t T, float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
+                               void *compute_stream, void *copy_stream) {
+    return streamed_impl(L, c, layer_id, experts_host, x, T, out, idx_out, ws, ws_bytes, compute_stream, copy_stream,
+                         Ahead{});
+}
+
+int moe_layer_forward_streamed_ahead(const moe_layer *L, moe_cache *c, uint32_t layer_id,
+                                     const void *const *experts_host, const float *x, int32_t T, float *out,
+                                     int32_t *idx_out, void *ws, size_t ws_bytes, void *compute_stream,
+                                     void *copy_stream, const moe_layer *next, uint32_t next_layer_id,
+                                     const void *const *next_experts_host, int32_t k_ahead) {
+    if (!next) return fail(MOE_E_INVAL, "next layer is NULL (use moe_layer_forward_streamed)");
+    Ahead ah;
+    ah.L = next;
+    ah.layer_id = next_layer_id;
+    ah.host = next_experts_host;
+    ah.k = k_ahead;
+    return streamed_impl(L, c, layer_id, experts_host, x, T, out, idx_out, ws, ws_bytes, compute_stream, copy_stream,
+                         ah);
 }
 
 size_t moe_grouped_workspace_bytes(const moe_layer *L, int32_t T) {

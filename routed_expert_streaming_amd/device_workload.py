@@ -77,6 +77,15 @@ class DeviceWorkload:
         return torch.from_numpy(np.ascontiguousarray(x)).to(self.device)
 
 
+def chain_next_input(h: torch.Tensor, out: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    """Chained (pre-norm) decode inputs, a stand-in for the trunk between MoE
+    layers, which is not modelled: the residual stream h [H] takes the layer's
+    output (h += out), and the next layer reads h rescaled to rms `scale`
+    (the seeded first input's rms).  Device tensor ops on the current stream."""
+    h.add_(out.reshape(h.shape))
+    return (h * (scale * torch.rsqrt(h.pow(2).mean()))).reshape(1, -1)
+
+
 class HostRecordPool:
     """Expert records of several layers in host memory (the cold tier of
     streamed decode): page-locked chunks of at most ``chunk_bytes`` up to

@@ -246,3 +246,90 @@ def test_streamed_rejects_capacity_below_k(moe):
                                    torch.cuda.Stream())
     assert e.value.code == -1
     cache.close()
+
+
+def test_streamed_lookahead_chained(moe):
+    # Chained decode (each layer reads the rescaled residual stream, so the
+    # next layer's router applied to this layer's input predicts something):
+    # the look-ahead changes which copies happen and when, never the outputs;
+    # the cache trace (lookups and look-ahead touches) replays exactly through
+    # the oracle's LRU; actual and predicted expert sets match the oracle's
+    # routers wherever the top-k boundary is not a near-tie.
+    from routed_expert_streaming_amd.device_workload import chain_next_input
+    cfg = synth.get_config("k3_slice", tokens=4, layers=3, E=48)
+    capacity, k_ahead = 40, cfg.k
+    dw, hp, cache = _streamed_setup(moe, cfg, capacity)
+    pool2 = torch.empty(capacity * hp.stride, dtype=torch.uint8, device="cuda")
+    cache_plain = moe.ExpertCache(capacity, hp.stride, pool2)
+    x = dw.inputs()
+    copy_stream = torch.cuda.Stream()
+    tables = [hp.table(L) for L in range(cfg.layers)]
+    ws = torch.empty(moe.streamed_workspace_bytes(dw.layers[0]), dtype=torch.uint8, device="cuda")
+
+    def run(mode):
+        outs, ins = [], []
+        for t in range(cfg.tokens):
+            h = x[t, 0].clone()
+            scale = h.pow(2).mean().sqrt()
+            xin = x[t, 0][None].contiguous()
+            for L in range(cfg.layers):
+                ins.append(xin.clone())
+                if mode == "resident":
+                    o, _, _ = moe.layer_forward(dw.layers[L], xin)
+                else:
+                    ahead = None
+                    if mode == "ahead" and L + 1 < cfg.layers:
+                        ahead = (dw.layers[L + 1], L + 1, tables[L + 1], k_ahead)
+                    c = cache if mode == "ahead" else cache_plain
+                    o = moe.layer_forward_streamed(dw.layers[L], c, L, None, xin, copy_stream, ws=ws,
+                                                   host_table=tables[L], ahead=ahead)
+                outs.append(o.clone())
+                xin = chain_next_input(h, o, scale)
+        torch.cuda.synchronize()
+        return outs, ins
+
+    out_a, in_a = run("ahead")
+    out_p, _ = run("plain")
+    out_r, _ = run("resident")
+    for n in range(len(out_a)):
+        assert torch.equal(out_a[n], out_p[n]), f"look-ahead changed output {n}"
+        assert torch.equal(out_a[n], out_r[n]), f"streamed != resident at {n}"
+    # replay of the cache's own operation string through the oracle's LRU
+    tr = cache.trace()
+    keys = np.array([r[0] for r in tr], np.int64)
+    hit, slot, ev = oracle.lru(keys, capacity)
+    assert [int(r[1] in (1, 3)) for r in tr] == hit.tolist()
+    assert [r[2] for r in tr] == slot.tolist()
+    assert [(-1 if r[3] is None else r[3]) for r in tr] == ev.tolist()
+    # operation string: per (t, L) k lookups, then k_ahead touches of L + 1
+    pos, checked = 0, 0
+    for t in range(cfg.tokens):
+        for L in range(cfg.layers):
+            n = t * cfg.layers + L
+            x64 = in_a[n].cpu().numpy().astype(np.float64)
+            look = tr[pos:pos + cfg.k]
+            pos += cfg.k
+            assert all(r[1] in (0, 1) for r in look)
+            ridx, _, z = oracle.route(dw.wl.router(L), dw.wl.bias(L), x64, cfg.k, cfg.score)
+            zs = np.sort(z[0])[::-1]
+            if zs[cfg.k - 1] - zs[cfg.k] > 1e-4:
+                assert sorted(r[0] - L * cfg.E for r in look) == sorted(ridx[0].tolist())
+                checked += 1
+            if L + 1 < cfg.layers:
+                pred = tr[pos:pos + k_ahead]
+                pos += k_ahead
+                assert all(r[1] in (2, 3) for r in pred)
+                pidx, _, zp = oracle.route(dw.wl.router(L + 1), dw.wl.bias(L + 1), x64, k_ahead, cfg.score)
+                zs = np.sort(zp[0])[::-1]
+                if zs[k_ahead - 1] - zs[k_ahead] > 1e-4:
+                    assert sorted(r[0] - (L + 1) * cfg.E for r in pred) == sorted(pidx[0].tolist())
+                    checked += 1
+    assert pos == len(tr) and checked >= len(out_a)
+    st = cache.stats()
+    assert st["ahead_inserted"] == sum(r[1] == 2 for r in tr)
+    assert st["ahead_present"] == sum(r[1] == 3 for r in tr)
+    assert st["ahead_used"] + st["ahead_wasted"] <= st["ahead_inserted"]
+    assert st["lookups"] == sum(r[1] in (0, 1) for r in tr)
+    log(f"look-ahead: {st}")
+    cache.close()
+    cache_plain.close()
