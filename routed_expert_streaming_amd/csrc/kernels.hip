@@ -66,6 +66,84 @@ __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ 
     }
 }
 
+// Router logits for many tokens (batched calls): a workgroup takes 64 tokens
+// x 64 experts x one slice of H, staged through LDS in 64-column steps; each
+// thread accumulates 4 tokens x 4 experts (tokens ty + 16i, experts tx + 16j,
+// so the 16 expert rows a wave reads sit in 16 different bank groups of the
+// 68-float padded rows).  Slices write fp32 partial sums; k_route_reduce adds
+// them in slice order plus the bias, so the result does not depend on timing.
+constexpr int kRbT = 64, kRbE = 64, kRbK = 64, kRbRow = 68;
+
+__global__ __launch_bounds__(256) void k_route_blocked(const float *__restrict__ W, int E, int H,
+                                                       const void *__restrict__ x, int x_dtype, int T, int kslice,
+                                                       float *__restrict__ part) {
+    __shared__ __align__(16) float xs[kRbT * kRbRow];
+    __shared__ __align__(16) float ws[kRbE * kRbRow];
+    const int t0 = blockIdx.x * kRbT, e0 = blockIdx.y * kRbE, ks = blockIdx.z;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int c_begin = ks * kslice, c_end = min(H, c_begin + kslice);
+    float acc[4][4] = {};
+    // loader: 64 rows x 64 columns = 1024 float4; four per thread
+    for (int c0 = c_begin; c0 < c_end; c0 += kRbK) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int q = tid + 256 * r, row = q >> 4, c4 = (q & 15) * 4;
+            const int t = min(t0 + row, T - 1), e = min(e0 + row, E - 1);
+            float4 xv;
+            if (x_dtype == MOE_DTYPE_F32) {
+                xv = *(const float4 *)((const float *)x + (size_t)t * H + c0 + c4);
+            } else {
+                const uint2 b = *(const uint2 *)((const uint16_t *)x + (size_t)t * H + c0 + c4);
+                xv = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                                 __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+            }
+            *(float4 *)(xs + row * kRbRow + c4) = xv;
+            *(float4 *)(ws + row * kRbRow + c4) = *(const float4 *)(W + (size_t)e * H + c0 + c4);
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int c = 0; c < kRbK; c += 4) {
+            float4 xv[4], wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) xv[i] = *(const float4 *)(xs + (ty + 16 * i) * kRbRow + c);
+#pragma unroll
+            for (int j = 0; j < 4; j++) wv[j] = *(const float4 *)(ws + (tx + 16 * j) * kRbRow + c);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    float a = acc[i][j];
+                    a = fmaf(xv[i].x, wv[j].x, a);
+                    a = fmaf(xv[i].y, wv[j].y, a);
+                    a = fmaf(xv[i].z, wv[j].z, a);
+                    a = fmaf(xv[i].w, wv[j].w, a);
+                    acc[i][j] = a;
+                }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int t = t0 + ty + 16 * i;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int e = e0 + tx + 16 * j;
+            if (e < E) part[((size_t)ks * T + t) * E + e] = acc[i][j];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_route_reduce(const float *__restrict__ part, const float *__restrict__ bias,
+                                                      int E, int T, int KS, float *__restrict__ z) {
+    const size_t n = (size_t)T * E;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        float s = 0.f;
+        for (int ks = 0; ks < KS; ks++) s += part[ks * n + i];
+        z[i] = s + (bias ? bias[i % E] : 0.f);
+    }
+}
+
 // Top-k per token: one wave per token; k rounds of a wave-wide argmax on
 // (z desc, expert id asc); then softmax- or sigmoid-renormalised weights.
 constexpr int kMaxPerLane = MOE_MAX_E / 64;
@@ -387,6 +465,29 @@ hipError_t launch_route_logits(const float *W, const float *bias, int E, int H, 
                                int T, float *z, hipStream_t s) {
     dim3 grid((E + 3) / 4, (T + kRouteTok - 1) / kRouteTok);
     k_route_logits<<<grid, 256, 0, s>>>(W, bias, E, H, x, x_dtype, T, z);
+    return hipGetLastError();
+}
+
+int route_blocked_slices(int E, int H, int T) {
+    const int tiles = ((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE);
+    const int steps = H / kRbK;
+    int ks = (256 + tiles - 1) / tiles;
+    return std::max(1, std::min(ks, std::min(steps, kRouteMaxSlices)));
+}
+
+hipError_t launch_route_blocked(const float *W, const float *bias, int E, int H, const void *x, int x_dtype, int T,
+                                float *part, float *z, hipStream_t s) {
+    if (H % kRbK) return hipErrorInvalidValue;
+    const int KS = route_blocked_slices(E, H, T);
+    const int steps = H / kRbK;
+    const int kslice = ((steps + KS - 1) / KS) * kRbK;
+    const int ks_used = (H + kslice - 1) / kslice;
+    dim3 grid((T + kRbT - 1) / kRbT, (E + kRbE - 1) / kRbE, ks_used);
+    k_route_blocked<<<grid, 256, 0, s>>>(W, E, H, x, x_dtype, T, kslice, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t n = (size_t)T * E;
+    k_route_reduce<<<(int)std::min<size_t>((n + 255) / 256, 4096), 256, 0, s>>>(part, bias, E, T, ks_used, z);
     return hipGetLastError();
 }
 

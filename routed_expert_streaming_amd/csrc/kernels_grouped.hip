@@ -33,9 +33,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGWaves = 8;          // waves per workgroup
-constexpr int kTokBlocks = 2;
 constexpr int kTwGateUp = 2;        // 16-row tiles per wave unit (gate/up)
-constexpr int kTwDown = 5;          // 16-row tiles per wave unit (down)       // 16-token blocks per pass (32 tokens)
+constexpr int kTwDown = 5;          // 16-row tiles per wave unit (down)
 
 __device__ __forceinline__ uint32_t bf16_pair_from_f16_pair(uint32_t a) {
     const f16x2 h = __builtin_bit_cast(f16x2, a);
@@ -63,18 +62,6 @@ __device__ __forceinline__ void codebook_to_bf16(char *cb) {
 __device__ __forceinline__ void group_rows(const char *cb, uint32_t v, bf16x8 &ba, bf16x8 &bb) {
     ba = *(const bf16x8 *)(cb + ((v << 4) & 0xFFF0u));
     bb = *(const bf16x8 *)(cb + ((v >> 8) & 0xFFF0u));
-}
-
-// The lane's 3 dwords (4 groups) of its row's 48-byte strip in a code tile.
-__device__ __forceinline__ void load_quad(const uint8_t *tile, int row_in_tile, int g4, uint32_t &d0, uint32_t &d1,
-                                          uint32_t &d2) {
-    const int d = 3 * g4;
-    auto at = [&](int dw) -> uint32_t {
-        return __builtin_nontemporal_load((const uint32_t *)(tile + (dw >> 2) * 1024 + row_in_tile * 16 + (dw & 3) * 4));
-    };
-    d0 = at(d);
-    d1 = at(d + 1);
-    d2 = at(d + 2);
 }
 
 template <int S>
@@ -145,14 +132,11 @@ struct GroupedArgs {
     // weights
     const void *const *table;   // [dev] expert record pointers (RVQ experts)
     RecOffsets off;
-    const uint16_t *dense;      // dense bf16 matrix rows [N, K] (shared expert), gate at dense, up at dense2
-    const uint16_t *dense2;
     // tokens
     const int32_t *counts;      // [E] pairs per expert
     const int32_t *offsets;     // [E] first position of each expert's segment
     const int32_t *perm;        // [positions] -> pair index
     int k;                      // ranks per token (pair -> token = pair / k)
-    int n_tokens;               // dense mode: number of tokens (positions = tokens)
     // operands
     const uint16_t *a;          // A rows: x bf16 [T, K] (gate/up) or h bf16 [positions, K] (down)
     int a_by_token;             // 1: A row of position p = token of p; 0: A row = p
@@ -164,207 +148,97 @@ struct GroupedArgs {
     int xcd_group;              // 1: place each expert's workgroups on one XCD (expert count % 8 == 0)
 };
 
-// Work unit of a wave: TW 16-row tiles x one pass of up to 16*kTokBlocks
-// tokens, swept over all 128-column chunks.  The codes (or dense weights) and
-// the A fragments of chunk j+1 are loaded while chunk j is computed.
-template <bool GATEUP, bool DENSE, int TW>
-__global__ __launch_bounds__(kGWaves * 64) void k_grouped(GroupedArgs g) {
-    extern __shared__ __align__(16) char lds[];
-    const int slot = DENSE ? 0 : blockIdx.x / g.splits, split = DENSE ? 0 : blockIdx.x % g.splits;
-    int cnt, pos0;
-    const uint8_t *rec = nullptr;
-    if constexpr (DENSE) {
-        cnt = g.n_tokens;
-        pos0 = 0;
-    } else {
-        cnt = g.counts[slot];
-        pos0 = g.offsets[slot];
-        if (cnt == 0) return;                 // uniform across the workgroup
-        rec = (const uint8_t *)g.table[slot];
-    }
-    char *cb0 = lds, *cb1 = lds + kCbRows * 16;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if constexpr (!DENSE) {
-        // codebooks into LDS with direct copies, all in flight at once
-        stage_lds_waves<kLdsPlain, kGWaves>(cb0, rec + g.off.cb[g.mat], kCbRows * 16, wave, lane);
-        if constexpr (GATEUP) stage_lds_waves<kLdsPlain, kGWaves>(cb1, rec + g.off.cb[1], kCbRows * 16, wave, lane);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        __syncthreads();
-        codebook_to_bf16(cb0);
-        if constexpr (GATEUP) codebook_to_bf16(cb1);
-        __syncthreads();
-    }
+// Dense bf16 GEMM for the shared expert over all T tokens: D[t][n] =
+// sum_k A[t][k] W[n][k] (A = x or h in bf16 rows of K, W = weight rows),
+// fp32 accumulation.  Workgroup tile: 64 weight rows x 32 tokens, 4 waves as
+// 2 x 2 (a wave: two 16-row MFMA tiles x 16 tokens, per matrix); K goes
+// through LDS in stages of 64 columns, double-buffered, the next stage's
+// operands loaded into registers while this stage is multiplied.  Rows are
+// padded to 144 bytes in LDS so the 16 lanes of a fragment read hit 16
+// different bank groups.  Gate/up: two weight matrices, epilogue
+// h = bf16(SiLU(g) * u); down: fp32 output.  Token rows past T are clamped
+// on load and never written.
+constexpr int kDnN = 64, kDnM = 32, kDnK = 64, kDnRow = 144;
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void k_dense_mm(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W0,
+                                                  const uint16_t *__restrict__ W1, int T, int N, int K,
+                                                  uint16_t *__restrict__ hout, float *__restrict__ yout) {
+    constexpr int NB = GATEUP ? 2 : 1;
+    constexpr int kStage = (kDnM + NB * kDnN) * kDnRow;
+    __shared__ __align__(16) char lds[2 * kStage];
+    const int n0 = blockIdx.x * kDnN, m0 = blockIdx.y * kDnM;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 15, g4 = lane >> 4;
-    const int rows_per_split = g.N / g.splits;          // multiple of 16
-    const int r_begin = split * rows_per_split;
-    const int tiles = rows_per_split / 16;
-    const int tgroups = (tiles + TW - 1) / TW;
-    const int cpr = g.K / kChunkCols;
-    const uint8_t *codes0 = nullptr, *codes1 = nullptr;
-    const _Float16 *sc0 = nullptr, *sc1 = nullptr;
-    if constexpr (!DENSE) {
-        codes0 = rec + g.off.codes[g.mat];
-        codes1 = rec + g.off.codes[1];
-        sc0 = (const _Float16 *)(rec + g.off.scales[g.mat]);
-        sc1 = (const _Float16 *)(rec + g.off.scales[1]);
+    const int wn = (wave & 1) * 32, wm = (wave >> 1) * 16;
+    // staging: A 32 rows x 128 B (one 16-byte piece per thread), each weight
+    // matrix 64 rows x 128 B (two pieces per thread)
+    const int ar = tid >> 3, ap = tid & 7;
+    const uint16_t *a_src = A + (size_t)min(m0 + ar, T - 1) * K + ap * 8;
+    const uint16_t *w_src[NB][2];
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+#pragma unroll
+        for (int h = 0; h < 2; h++) w_src[b][h] = (b ? W1 : W0) + (size_t)(n0 + ar + 32 * h) * K + ap * 8;
+    u32x4 ra, rw[NB][2];
+    auto fetch = [&](int k0) {
+        ra = *(const u32x4 *)(a_src + k0);
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+#pragma unroll
+            for (int h = 0; h < 2; h++) rw[b][h] = *(const u32x4 *)(w_src[b][h] + k0);
+    };
+    auto stash = [&](int buf) {
+        char *st = lds + buf * kStage;
+        *(u32x4 *)(st + ar * kDnRow + ap * 16) = ra;
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+                *(u32x4 *)(st + (kDnM + b * kDnN + ar + 32 * h) * kDnRow + ap * 16) = rw[b][h];
+    };
+    f32x4 acc[NB][2];
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[b][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const int stages = K / kDnK;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int st = 0; st < stages; st++) {
+        const int cur = st & 1;
+        if (st + 1 < stages) fetch((st + 1) * kDnK);
+        const char *L = lds + cur * kStage;
+#pragma unroll
+        for (int kk = 0; kk < kDnK / 32; kk++) {
+            const bf16x8 af = *(const bf16x8 *)(L + (wm + col) * kDnRow + kk * 64 + g4 * 16);
+#pragma unroll
+            for (int b = 0; b < NB; b++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const bf16x8 bfr =
+                        *(const bf16x8 *)(L + (kDnM + b * kDnN + wn + 16 * j + col) * kDnRow + kk * 64 + g4 * 16);
+                    acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[b][j], 0, 0, 0);
+                }
+        }
+        if (st + 1 < stages) stash(cur ^ 1);
+        __syncthreads();
     }
-    const int passes = (cnt + 16 * kTokBlocks - 1) / (16 * kTokBlocks);
-    const int units = tgroups * passes;
-    const int u_first = DENSE ? blockIdx.x * kGWaves + wave : wave;
-    const int u_step = DENSE ? gridDim.x * kGWaves : kGWaves;
-    for (int u = u_first; u < units; u += u_step) {
-        const int tg = u % tgroups, pass = u / tgroups;
-        const int ntw = min(TW, tiles - tg * TW);             // tiles in this unit (wave-uniform)
-        int n[TW];
-        const uint8_t *t0[TW], *t1[TW];
+    // lane holds D[token 4*g4 + i][row col] of each 16 x 16 tile
 #pragma unroll
-        for (int t = 0; t < TW; t++) {
-            n[t] = r_begin + (tg * TW + min(t, ntw - 1)) * 16 + col;
-            if constexpr (!DENSE) {
-                t0[t] = codes0 + (size_t)(n[t] >> 6) * cpr * kTileBytes;
-                t1[t] = codes1 + (size_t)(n[t] >> 6) * cpr * kTileBytes;
-            }
-        }
-        const int m_base = pass * 16 * kTokBlocks;
-        const int nblk = min(kTokBlocks, (cnt - m_base + 15) / 16);
-        const uint16_t *arow[kTokBlocks];
+    for (int j = 0; j < 2; j++) {
+        const int n = n0 + wn + 16 * j + col;
 #pragma unroll
-        for (int b = 0; b < kTokBlocks; b++) {
-            const int m = m_base + b * 16 + col;
-            arow[b] = nullptr;
-            if (b < nblk && m < cnt) {
-                const int p = pos0 + m;
-                const int row = DENSE ? p : (g.a_by_token ? g.perm[p] / g.k : p);
-                arow[b] = g.a + (size_t)row * g.K;
-            }
-        }
-        f32x4 acc0[TW][kTokBlocks], acc1[TW][kTokBlocks];
-#pragma unroll
-        for (int t = 0; t < TW; t++)
-#pragma unroll
-            for (int b = 0; b < kTokBlocks; b++) {
-                acc0[t][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                acc1[t][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            }
-        // operand staging for one chunk
-        struct Stage {
-            uint32_t c0[TW][3], c1[TW][3];          // RVQ codes (4 groups) per tile
-            bf16x8 w0[TW][4], w1[TW][4];            // dense weights per tile and K-step
-            bf16x8 a[4][kTokBlocks];                // A fragments per K-step and block
-        };
-        auto load_stage = [&](int j, Stage &st) {
-#pragma unroll
-            for (int t = 0; t < TW; t++) {
-                if (t < ntw) {
-                    if constexpr (!DENSE) {
-                        load_quad(t0[t] + (size_t)j * kTileBytes, n[t] & 63, g4, st.c0[t][0], st.c0[t][1], st.c0[t][2]);
-                        if constexpr (GATEUP)
-                            load_quad(t1[t] + (size_t)j * kTileBytes, n[t] & 63, g4, st.c1[t][0], st.c1[t][1],
-                                      st.c1[t][2]);
-                    } else {
-#pragma unroll
-                        for (int s = 0; s < 4; s++) {
-                            const int kc = j * kChunkCols + (4 * g4 + s) * 8;
-                            st.w0[t][s] = *(const bf16x8 *)(g.dense + (size_t)n[t] * g.K + kc);
-                            if constexpr (GATEUP) st.w1[t][s] = *(const bf16x8 *)(g.dense2 + (size_t)n[t] * g.K + kc);
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < 4; s++) {
-                const int kc = j * kChunkCols + (4 * g4 + s) * 8;
-#pragma unroll
-                for (int b = 0; b < kTokBlocks; b++) {
-                    st.a[s][b] = (bf16x8){};
-                    if (b < nblk && arow[b]) st.a[s][b] = *(const bf16x8 *)(arow[b] + kc);
-                }
-            }
-        };
-        Stage cur, nxt;
-        load_stage(0, cur);
-        for (int j = 0; j < cpr; j++) {
-            if (j + 1 < cpr) load_stage(j + 1, nxt);
-#pragma unroll
-            for (int s = 0; s < 4; s++) {
-#pragma unroll
-                for (int t = 0; t < TW; t++) {
-                    if (t < ntw) {
-                        if constexpr (DENSE) {
-                            const bf16x8 B0 = cur.w0[t][s];
-                            bf16x8 B1;
-                            if constexpr (GATEUP) B1 = cur.w1[t][s];
-#pragma unroll
-                            for (int b = 0; b < kTokBlocks; b++) {
-                                if (b < nblk) {
-                                    acc0[t][b] =
-                                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B0, acc0[t][b], 0, 0, 0);
-                                    if constexpr (GATEUP)
-                                        acc1[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B1,
-                                                                                             acc1[t][b], 0, 0, 0);
-                                }
-                            }
-                        } else {
-                            const uint32_t *c0 = cur.c0[t], *c1 = cur.c1[t];
-                            const uint32_t v0 = s == 0 ? quad_code<0>(c0[0], c0[1], c0[2])
-                                              : s == 1 ? quad_code<1>(c0[0], c0[1], c0[2])
-                                              : s == 2 ? quad_code<2>(c0[0], c0[1], c0[2])
-                                                       : quad_code<3>(c0[0], c0[1], c0[2]);
-                            bf16x8 B0a, B0b, B1a, B1b;
-                            group_rows(cb0, v0, B0a, B0b);
-                            if constexpr (GATEUP) {
-                                const uint32_t v1 = s == 0 ? quad_code<0>(c1[0], c1[1], c1[2])
-                                                  : s == 1 ? quad_code<1>(c1[0], c1[1], c1[2])
-                                                  : s == 2 ? quad_code<2>(c1[0], c1[1], c1[2])
-                                                           : quad_code<3>(c1[0], c1[1], c1[2]);
-                                group_rows(cb1, v1, B1a, B1b);
-                            }
-#pragma unroll
-                            for (int b = 0; b < kTokBlocks; b++) {
-                                if (b < nblk) {
-                                    acc0[t][b] =
-                                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B0a, acc0[t][b], 0, 0, 0);
-                                    acc0[t][b] =
-                                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B0b, acc0[t][b], 0, 0, 0);
-                                    if constexpr (GATEUP) {
-                                        acc1[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B1a,
-                                                                                             acc1[t][b], 0, 0, 0);
-                                        acc1[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[s][b], B1b,
-                                                                                             acc1[t][b], 0, 0, 0);
-                                    }
-                                }
-                            }
-                        }
-                    }
-                }
-            }
-            if (j + 1 < cpr) cur = nxt;
-        }
-        // epilogue: lane holds D[4*g4 + i][col] of each (tile, block)
-#pragma unroll
-        for (int t = 0; t < TW; t++) {
-            if (t >= ntw) continue;
-            float s0v = 1.f, s1v = 1.f;
-            if constexpr (!DENSE) {
-                s0v = (float)sc0[n[t]];
-                if constexpr (GATEUP) s1v = (float)sc1[n[t]];
-            }
-#pragma unroll
-            for (int b = 0; b < kTokBlocks; b++) {
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int m = m_base + b * 16 + 4 * g4 + i;
-                    if (b < nblk && m < cnt) {
-                        const size_t p = (size_t)(pos0 + m);
-                        if constexpr (GATEUP) {
-                            const float gg = acc0[t][b][i] * s0v, uu = acc1[t][b][i] * s1v;
-                            const __bf16 h = (__bf16)(gg / (1.f + __expf(-gg)) * uu);
-                            g.hout[p * g.N + n[t]] = __builtin_bit_cast(uint16_t, h);
-                        } else {
-                            g.yout[p * g.N + n[t]] = acc0[t][b][i] * s0v;
-                        }
-                    }
-                }
+        for (int i = 0; i < 4; i++) {
+            const int t = m0 + wm + 4 * g4 + i;
+            if (t >= T) continue;
+            if constexpr (GATEUP) {
+                const float g = acc[0][j][i], u = acc[NB - 1][j][i];
+                const __bf16 h = (__bf16)(g / (1.f + __expf(-g)) * u);
+                hout[(size_t)t * N + n] = __builtin_bit_cast(uint16_t, h);
+            } else {
+                yout[(size_t)t * N + n] = acc[0][j][i];
             }
         }
     }
@@ -664,7 +538,6 @@ __global__ __launch_bounds__(256) void k_grouped_combine(const float *__restrict
     }
 }
 
-// dense shared-expert down output is written per token as fp32 by k_grouped<false, true>
 
 }  // namespace
 
@@ -737,29 +610,14 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
 
 hipError_t launch_grouped_dense(const uint16_t *shared, int H, int I, int T, const uint16_t *xb, uint16_t *hs,
                                 float *ysh, hipStream_t s) {
-    GroupedArgs g{};
-    g.n_tokens = T;
-    g.k = 1;
-    g.a = xb;
-    g.a_by_token = 0;
-    g.dense = shared;
-    g.dense2 = shared + (size_t)I * H;
-    g.hout = hs;
-    g.N = I;
-    g.K = H;
-    g.splits = 1;
-    const int passes = (T + 16 * kTokBlocks - 1) / (16 * kTokBlocks);
-    k_grouped<true, true, 1><<<std::max(1, (I / 16) * passes / kGWaves), kGWaves * 64, 0, s>>>(g);
+    if (T <= 0) return hipSuccess;
+    if (I % kDnN || H % kDnN || H % kDnK || I % kDnK) return hipErrorInvalidValue;
+    const uint16_t *wg = shared, *wu = shared + (size_t)I * H, *wd = shared + 2 * (size_t)I * H;
+    const int mt = (T + kDnM - 1) / kDnM;
+    k_dense_mm<true><<<dim3(I / kDnN, mt), 256, 0, s>>>(xb, wg, wu, T, I, H, hs, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    g.a = hs;
-    g.dense = shared + 2 * (size_t)I * H;
-    g.dense2 = nullptr;
-    g.hout = nullptr;
-    g.yout = ysh;
-    g.N = H;
-    g.K = I;
-    k_grouped<false, true, 1><<<std::max(1, (H / 16) * passes / kGWaves), kGWaves * 64, 0, s>>>(g);
+    k_dense_mm<false><<<dim3(H / kDnN, mt), 256, 0, s>>>(hs, wd, nullptr, T, H, I, nullptr, ysh);
     return hipGetLastError();
 }
 

@@ -104,7 +104,7 @@ LayerWs carve_layer(void *ws, int H, int I, int E, int k, int T, bool shared) {
 }
 
 struct GroupedWs {
-    float *z;
+    float *z, *zpart;
     int32_t *idx, *perm, *inv, *counts, *offsets;
     float *w;
     uint16_t *xb, *hbuf, *hs;
@@ -117,6 +117,7 @@ GroupedWs carve_grouped(void *ws, int H, int I, int E, int k, int T, bool shared
     GroupedWs G;
     const size_t pairs = (size_t)T * k;
     G.z = c.take<float>((size_t)T * E);
+    G.zpart = c.take<float>((size_t)kRouteMaxSlices * T * E);
     G.idx = c.take<int32_t>(pairs);
     G.w = c.take<float>(pairs);
     G.perm = c.take<int32_t>(pairs);
@@ -660,7 +661,8 @@ int moe_layer_forward_grouped(const moe_layer *L, const void *x, int32_t x_dtype
     const GroupedWs W = carve_grouped(ws, H, I, E, k, T, L->shared != nullptr);
     int32_t *idx = idx_out ? idx_out : W.idx;
     float *w = w_out ? w_out : W.w;
-    HIPCHK(launch_route_logits(L->router.weight, L->router.bias, E, H, x, x_dtype, T, W.z, s), "route logits");
+    HIPCHK(launch_route_blocked(L->router.weight, L->router.bias, E, H, x, x_dtype, T, W.zpart, W.z, s),
+           "route logits");
     HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, T, idx, w, s), "top-k");
     HIPCHK(launch_group(idx, T * k, E, W.perm, W.inv, W.counts, W.offsets, s), "group");
     HIPCHK(launch_to_bf16(x, x_dtype, (size_t)T * H, W.xb, s), "x to bf16");

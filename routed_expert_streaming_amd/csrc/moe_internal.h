@@ -54,6 +54,12 @@ hipError_t launch_route_logits(const float *W, const float *bias, int E, int H, 
                                int x_dtype, int T, float *z, hipStream_t s);
 hipError_t launch_topk(const float *z, int E, int k, int score_fn, int T, int32_t *idx, float *w,
                        hipStream_t s);
+// Many-token router logits: H-sliced partial sums (part: route_blocked_slices
+// x T x E floats) reduced in slice order into z.  H % 64 == 0.
+constexpr int kRouteMaxSlices = 16;
+int route_blocked_slices(int E, int H, int T);
+hipError_t launch_route_blocked(const float *W, const float *bias, int E, int H, const void *x, int x_dtype, int T,
+                                float *part, float *z, hipStream_t s);
 hipError_t launch_pack_x(const void *x, int x_dtype, int T, int H, int64_t x_stride, uint32_t *xh,
                          hipStream_t s);
 // n_local_total = T * src.n_local local items in the launch
