@@ -32,9 +32,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGWaves = 8;          // waves per workgroup
-constexpr int kTwGateUp = 2;        // 16-row tiles per wave unit (gate/up)
-constexpr int kTwDown = 5;          // 16-row tiles per wave unit (down)
+constexpr int kNwGateUp = 16;       // waves per workgroup (gate/up)
+constexpr int kTwGateUp = 1;        // 16-row tiles per wave unit (gate/up)
+constexpr int kNwDown = 16;         // waves per workgroup (down)
+constexpr int kTwDown = 2;          // 16-row tiles per wave unit (down)
 
 __device__ __forceinline__ uint32_t bf16_pair_from_f16_pair(uint32_t a) {
     const f16x2 h = __builtin_bit_cast(f16x2, a);
@@ -47,7 +48,7 @@ __device__ __forceinline__ uint32_t bf16_pair_from_f16_pair(uint32_t a) {
 
 // fp16 codebook rows staged in LDS -> bf16 in place (each thread its rows)
 __device__ __forceinline__ void codebook_to_bf16(char *cb) {
-    for (int i = threadIdx.x; i < kCbRows; i += kGWaves * 64) {
+    for (int i = threadIdx.x; i < kCbRows; i += blockDim.x) {
         u32x4 v = ((u32x4 *)cb)[i];
         v.x = bf16_pair_from_f16_pair(v.x);
         v.y = bf16_pair_from_f16_pair(v.y);
@@ -260,7 +261,6 @@ constexpr int kBufNt = 2;                     // buffer load cache policy: non-t
 constexpr int kBufWord3 = 0x00020000;         // buffer descriptor word 3 (32-bit data format)
 constexpr int kASlot = 16 * kChunkCols * 2;   // bytes of one A ring slot
 constexpr int kARing = 3;
-static_assert(kGWaves == 8, "the A copy assigns two tokens to each wave");
 
 template <int TW>
 struct RvqStage {
@@ -325,9 +325,9 @@ __device__ __forceinline__ void lds_wait_barrier() {
 
 // The A ring.  Token m's 16-byte piece q (columns 8q..8q+7 of the chunk)
 // sits at m*256 + (q ^ m)*16 of a slot, so the 16 lanes of one lane block
-// (16 tokens, one piece each) read 16 different bank groups.  Wave w copies
-// tokens 2w, 2w+1: lane i writes slot byte 512w + 16(i%32) (lanes i and
-// i+32 copy the same piece, which keeps the copy free of branches).
+// (16 tokens, one piece each) read 16 different bank groups.  Thread i of
+// the workgroup copies piece (i % 256) to slot byte 16 (i % 256); beyond 256
+// threads the copies repeat, which keeps the copy free of branches.
 struct ARing {
     char *base;                 // slot 0
     const uint16_t *src;        // the lane's token row + its piece (columns 8q..)
@@ -385,8 +385,9 @@ __device__ __forceinline__ void rvq_chunk(const RvqStage<TW> &cur, const RvqStag
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool GATEUP, int TW>
-__global__ __launch_bounds__(kGWaves * 64) void k_grouped_rvq(GroupedArgs g) {
+template <bool GATEUP, int TW, int NW>
+__global__ __launch_bounds__(NW * 64) void k_grouped_rvq(GroupedArgs g) {
+    static_assert(NW >= 4, "the A copy needs 256 lanes");
     extern __shared__ __align__(16) char lds[];
     // Workgroups are dealt to the 8 XCDs round-robin by index; when the
     // expert count is a multiple of 8, the row ranges of one expert all go to
@@ -408,8 +409,8 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped_rvq(GroupedArgs g) {
     char *aring = lds + (GATEUP ? 2 : 1) * kCbRows * 16;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     // codebooks into LDS with direct copies (all in flight at once), then bf16
-    stage_lds_waves<kLdsPlain, kGWaves>(cb0, rec + g.off.cb[g.mat], kCbRows * 16, wave, lane);
-    if constexpr (GATEUP) stage_lds_waves<kLdsPlain, kGWaves>(cb1, rec + g.off.cb[1], kCbRows * 16, wave, lane);
+    stage_lds_waves<kLdsPlain, NW>(cb0, rec + g.off.cb[g.mat], kCbRows * 16, wave, lane);
+    if constexpr (GATEUP) stage_lds_waves<kLdsPlain, NW>(cb1, rec + g.off.cb[1], kCbRows * 16, wave, lane);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
     codebook_to_bf16(cb0);
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped_rvq(GroupedArgs g) {
     const int r_begin = split * rows_per_split;
     const int tiles = rows_per_split / 16;
     const int tgroups = (tiles + TW - 1) / TW;
-    const int rounds = (tgroups + kGWaves - 1) / kGWaves;
+    const int rounds = (tgroups + NW - 1) / NW;
     const int cpr = g.K / kChunkCols;
     const int code_bytes = g.N / 64 * cpr * kTileBytes;   // one matrix's code section
     const __amdgpu_buffer_rsrc_t rs0 =
@@ -431,14 +432,15 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped_rvq(GroupedArgs g) {
     const int passes = (cnt + 15) / 16;
     ARing ar;
     ar.base = aring;
-    ar.wr = wave * 512 + (lane & 31) * 16;
+    const int apiece = (wave * 64 + lane) & 255;   // A piece this lane copies: token apiece/16, piece apiece%16
+    ar.wr = apiece * 16;
 #pragma unroll
     for (int s = 0; s < 4; s++) ar.rd[s] = col * 256 + (((4 * g4 + s) ^ col) & 15) * 16;
     // Every wave runs every (pass, round) so the barriers line up; a wave
     // without a tile group in the last round repeats the last one and
     // writes nothing.
     for (int it = 0; it < passes * rounds; it++) {
-        const int pass = it / rounds, tg_raw = (it % rounds) * kGWaves + wave;
+        const int pass = it / rounds, tg_raw = (it % rounds) * NW + wave;
         const bool active = tg_raw < tgroups;                  // wave-uniform
         const int tg = min(tg_raw, tgroups - 1);
         const int ntw = min(TW, tiles - tg * TW);             // tiles in this unit (wave-uniform)
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(kGWaves * 64) void k_grouped_rvq(GroupedArgs g) {
         // the copying lanes' A rows: tokens past the pass's last real one
         // copy the last real row (their products are never written)
         {
-            const int mloc = 2 * wave + ((lane >> 4) & 1);
+            const int mloc = apiece >> 4;
             const int m = min(pass * 16 + mloc, cnt - 1);
             const int p = pos0 + m;
             const uint16_t *row = g.a + (size_t)(g.a_by_token ? g.perm[p] / g.k : p) * g.K;
@@ -553,11 +555,13 @@ hipError_t launch_to_bf16(const void *x, int x_dtype, size_t n, uint16_t *xb, hi
     return hipGetLastError();
 }
 
-static int pick_splits(int N) {
-    // row ranges per expert: whole 16-row tiles, about 8 tiles per wave
-    int splits = 1;
-    while ((N / (splits * 2)) % 64 == 0 && N / (splits * 2) >= 64 * kGWaves / 2 && splits < 8) splits *= 2;
-    return splits;
+// Row ranges per expert: the most (up to 16) that divide N into whole rounds
+// of the workgroup's tile groups (16 * TW * NW rows), else one range.
+static int pick_splits(int N, int TW, int NW) {
+    const int round_rows = 16 * TW * NW;
+    for (int s = 16; s > 1; s--)
+        if (N % s == 0 && (N / s) % round_rows == 0) return s;
+    return 1;
 }
 
 constexpr int kLdsGateUp = 2 * kCbRows * 16 + kARing * kASlot;
@@ -579,20 +583,20 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
     g.hout = hbuf;
     g.N = I;
     g.K = H;
-    g.splits = pick_splits(I);
+    g.splits = pick_splits(I, kTwGateUp, kNwGateUp);
     g.mat = 0;
     g.xcd_group = E % 8 == 0;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_grouped_rvq<true, kTwGateUp>,
+        hipError_t e = hipFuncSetAttribute((const void *)k_grouped_rvq<true, kTwGateUp, kNwGateUp>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsGateUp);
         if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void *)k_grouped_rvq<false, kTwDown>,
+            e = hipFuncSetAttribute((const void *)k_grouped_rvq<false, kTwDown, kNwDown>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDown);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    k_grouped_rvq<true, kTwGateUp><<<E * g.splits, kGWaves * 64, kLdsGateUp, s>>>(g);
+    k_grouped_rvq<true, kTwGateUp, kNwGateUp><<<E * g.splits, kNwGateUp * 64, kLdsGateUp, s>>>(g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // down: N = H rows, K = I; A = h rows by position
@@ -602,9 +606,9 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
     g.yout = ybuf;
     g.N = H;
     g.K = I;
-    g.splits = pick_splits(H);
+    g.splits = pick_splits(H, kTwDown, kNwDown);
     g.mat = 2;
-    k_grouped_rvq<false, kTwDown><<<E * g.splits, kGWaves * 64, kLdsDown, s>>>(g);
+    k_grouped_rvq<false, kTwDown, kNwDown><<<E * g.splits, kNwDown * 64, kLdsDown, s>>>(g);
     return hipGetLastError();
 }
 
