@@ -77,7 +77,13 @@ __device__ __forceinline__ void wait_lds_barrier() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-constexpr int kStripLoads = 3;   // 128-bit loads per 48-byte code strip
+// Workgroup barrier for LDS data: waits for this wave's LDS operations only,
+// so stores and loads to global memory stay in flight across it
+// (__syncthreads() would wait for all of them: a memory round trip).
+__device__ __forceinline__ void lds_sync() {
+    wait_lds_barrier<63>();
+    lds_barrier();
+}
 
 // Workgroup-wide wait until *p >= target.  Returns false (error flag set)
 // on timeout or if another workgroup already failed.
@@ -99,18 +105,10 @@ __device__ __forceinline__ bool wg_wait(unsigned *sync, const unsigned *p, unsig
         }
         *bcast = ok;
     }
-    __syncthreads();
+    lds_sync();
     const bool ok = *bcast != 0;
-    __syncthreads();
+    lds_sync();
     return ok;
-}
-
-// Workgroup-wide release: wait until this workgroup's stores have completed,
-// then add 1 to a counter.  The add returns nothing, so nothing waits for it.
-__device__ __forceinline__ void wg_signal(unsigned *p) {
-    wait_vm_all();
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Values exchanged between workgroups inside a step carry the step: value
@@ -302,6 +300,19 @@ constexpr int kDecTail = kDecLdsBytes - 1024;     // sidx, sw, broadcast words, 
 constexpr int kDecRecs = kDecTail - 8 * MOE_MAX_E;   // the layer's record pointers, until top-k
 
 constexpr int kRingGU = 3;      // code buffers per wave (2 units in flight ahead)
+constexpr int kShRows = 8;      // shared-expert rows per load group
+constexpr int kTopkScratch = 2048;   // LDS bytes (codebook area, free while routing): top-k staging
+
+// Order-preserving key of a float (larger float, larger key; -0 and +0 one
+// key, as they compare equal) and back.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 constexpr int kRingD = 4;       // (3 ahead)
 
 __device__ __forceinline__ void load_codes(gu32x4 *base, int u, int lane, uint32_t (&d)[12]) {
@@ -580,7 +591,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // after top-k
         for (int e = threadIdx.x; e < E; e += kPW * 64) recs_all[e] = (uint64_t)lay.records[e];
         if (s > 0 && !wg_wait(sync, sync + kLayerDone, (unsigned)s * tilesH, bcast)) return;
-        if (s == 0) __syncthreads();
+        if (s == 0) lds_sync();
         mark(kStampLayerWait);
 
         const unsigned tag = (unsigned)s + 1;
@@ -616,9 +627,9 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     acc = fmaf(w1.w, x1.w, acc);
                 }
                 acc = wave_sum(acc);
-                __syncthreads();
+                lds_sync();
                 if (lane == 0) red[wave] = acc;
-                __syncthreads();
+                lds_sync();
                 if (threadIdx.x == 0) {
                     float z = 0.f;
                     for (int v = 0; v < kPW; v++) z += red[v];
@@ -628,35 +639,83 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         }
 
         // ---- shared gate/up (independent of routing; after the logits, so it
-        // overlaps their exchange instead of delaying it)
-        if (shared_on) {
-            for (int r = shI0 + wave; r < shI1; r += kPW) {
-                const uint16_t *wg = lay.shared + (size_t)r * H, *wu = lay.shared + (size_t)I * H + (size_t)r * H;
-                float g = 0.f, u = 0.f;
-                for (int c = lane * 8; c < H; c += 512) {
-                    const uint4 gv = *(const uint4 *)(wg + c), uv = *(const uint4 *)(wu + c);
-                    const float4 xa = *(const float4 *)(xs + c), xb = *(const float4 *)(xs + c + 4);
-                    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-                    const uint32_t gq[4] = {gv.x, gv.y, gv.z, gv.w}, uq[4] = {uv.x, uv.y, uv.z, uv.w};
+        // overlaps their exchange instead of delaying it).  The workgroup's
+        // rows go kShRows at a time, each thread on 8 columns of every row of
+        // the group: all weight loads are in flight together (one memory
+        // round trip per group instead of one per 512 columns), then one
+        // workgroup reduction per group.
+        if (shared_on && shI1 > shI0) {
+            float *shred = (float *)lds;   // [kPW][2 * kShRows], codebook area (free until gate/up)
+            const uint16_t *wg0 = lay.shared, *wu0 = lay.shared + (size_t)I * H;
+            for (int r0 = shI0; r0 < shI1; r0 += kShRows) {
+                const int nr = min(kShRows, shI1 - r0);
+                float g[kShRows], u[kShRows];
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        g = fmaf(__uint_as_float(gq[i] << 16), xv[2 * i], g);
-                        g = fmaf(__uint_as_float(gq[i] & 0xFFFF0000u), xv[2 * i + 1], g);
-                        u = fmaf(__uint_as_float(uq[i] << 16), xv[2 * i], u);
-                        u = fmaf(__uint_as_float(uq[i] & 0xFFFF0000u), xv[2 * i + 1], u);
+                for (int q = 0; q < kShRows; q++) g[q] = u[q] = 0.f;
+                for (int c = threadIdx.x * 8; c < H; c += kPW * 64 * 8) {
+                    const float4 xa = *(const float4 *)(xs + c), xb = *(const float4 *)(xs + c + 4);
+                    uint4 gv[kShRows], uv[kShRows];
+#pragma unroll
+                    for (int q = 0; q < kShRows; q++) {
+                        const size_t o = (size_t)min(r0 + q, shI1 - 1) * H + c;
+                        gv[q] = *(const uint4 *)(wg0 + o);
+                        uv[q] = *(const uint4 *)(wu0 + o);
+                    }
+                    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                    for (int q = 0; q < kShRows; q++) {
+                        const uint32_t gq[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
+                        const uint32_t uq[4] = {uv[q].x, uv[q].y, uv[q].z, uv[q].w};
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            g[q] = fmaf(__uint_as_float(gq[i] << 16), xv[2 * i], g[q]);
+                            g[q] = fmaf(__uint_as_float(gq[i] & 0xFFFF0000u), xv[2 * i + 1], g[q]);
+                            u[q] = fmaf(__uint_as_float(uq[i] << 16), xv[2 * i], u[q]);
+                            u[q] = fmaf(__uint_as_float(uq[i] & 0xFFFF0000u), xv[2 * i + 1], u[q]);
+                        }
                     }
                 }
-                g = wave_sum(g);
-                u = wave_sum(u);
-                if (lane == 0) st_x(a.hs + r, g / (1.f + __expf(-g)) * u);
+#pragma unroll
+                for (int q = 0; q < kShRows; q++) {
+                    g[q] = wave_sum(g[q]);
+                    u[q] = wave_sum(u[q]);
+                }
+                if (lane == 0) {
+#pragma unroll
+                    for (int q = 0; q < kShRows; q++) {
+                        shred[wave * 2 * kShRows + q] = g[q];
+                        shred[wave * 2 * kShRows + kShRows + q] = u[q];
+                    }
+                }
+                lds_sync();
+                // wave 1 finishes the rows (wave 0 goes on to poll the logits)
+                if (wave == 1 && lane < nr) {
+                    float gg = 0.f, uu = 0.f;
+                    for (int v = 0; v < kPW; v++) {
+                        gg += shred[v * 2 * kShRows + lane];
+                        uu += shred[v * 2 * kShRows + kShRows + lane];
+                    }
+                    st_x(a.hs + r0 + lane, gg / (1.f + __expf(-gg)) * uu);
+                }
+                lds_sync();
             }
-            if (shI1 > shI0) wg_signal(h_ready + k);
+            // wave 1 wrote every row: once its stores are done, count them
+            if (wave == 1) {
+                wait_vm_all();
+                if (lane == 0) __hip_atomic_fetch_add(h_ready + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
 
-        // ---- top-k (every workgroup, wave 0): poll the tagged logits, then k
-        // rounds of a wave argmax over (logit desc, expert id asc)
+        // ---- top-k: wave 0 polls the tagged logits into LDS as
+        // order-preserving keys; then every thread ranks its experts by
+        // counting the ones ahead of it in (logit desc, expert id asc) order
+        // (no lane exchanges, no dependency chain); ranks below k land in
+        // rank order, and wave 0 computes the weights in that order.
+        // key of expert e: order_key(z) << 32 | (2^32 - 1 - e), so one 64-bit
+        // comparison orders by logit, then by lower id
+        uint64_t *zkey = (uint64_t *)(lds + kTopkScratch);    // [E rounded up to 32]
+        float *sz = (float *)(zkey + MOE_MAX_E);              // [MOE_MAX_K] logits in rank order
         if (wave == 0) {
-            float v[MOE_MAX_E / 64];
             long spins = 0;
             bool okw = true;
             for (;;) {
@@ -668,49 +727,58 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                         const uint64_t zz = ld_tagged(a.z + e);
                         ok = ok && tag_ok(zz, tag);
                         const float f = tag_val(zz);
-                        v[i] = f == f ? f : -INFINITY;
-                    } else {
-                        v[i] = -INFINITY;
+                        zkey[e] = (uint64_t)order_key(f == f ? f : -INFINITY) << 32 | (0xFFFFFFFFu - (uint32_t)e);
+                    } else if (e < ((E + 31) & ~31)) {
+                        zkey[e] = 0u;   // padding: below every real key
                     }
                 }
                 if (__all(ok)) break;
                 if (!poll_more(sync, spins)) { okw = false; break; }
             }
             if (lane == 0) *bcast = okw;
-            if (okw) {
-                uint32_t taken = 0;
-                float zmax = 0.f, sum = 0.f, mine = 0.f;
-                int emine = 0;
-                for (int j = 0; j < lay.k; j++) {
-                    float bv = -INFINITY;
-                    int be = 0x7FFFFFFF;
+        }
+        lds_sync();
+        if (!*bcast) return;
+        {
+            const int kk = __builtin_amdgcn_readfirstlane(lay.k);
+            for (int e = threadIdx.x; e < E; e += kPW * 64) {
+                const uint64_t ke = zkey[e];
+                // 32 keys per step (broadcast reads), four independent counts
+                int r[4] = {0, 0, 0, 0};
+                for (int q0 = 0; q0 < E && r[0] + r[1] + r[2] + r[3] < kk; q0 += 32) {
+                    uint64_t kv[32];
 #pragma unroll
-                    for (int i = 0; i < MOE_MAX_E / 64; i++) {
-                        const int e = lane + 64 * i;
-                        if (e < E && !(taken >> i & 1u) && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
+                    for (int i = 0; i < 16; i++) {
+                        const u32x4 two = *(const u32x4 *)(zkey + q0 + 2 * i);
+                        kv[2 * i] = (uint64_t)two.y << 32 | two.x;
+                        kv[2 * i + 1] = (uint64_t)two.w << 32 | two.z;
                     }
 #pragma unroll
-                    for (int o = 32; o > 0; o >>= 1) {
-                        const float ov = __shfl_xor(bv, o, 64);
-                        const int oe = __shfl_xor(be, o, 64);
-                        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-                    }
-                    if (j == 0) zmax = bv;
-                    const float sc = lay.score_fn == MOE_SCORE_SOFTMAX ? __expf(bv - zmax) : 1.f / (1.f + __expf(-bv));
-                    sum += sc;
-                    if (lane == j) { mine = sc; emine = be; }
-                    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+                    for (int i = 0; i < 32; i++) r[i & 3] += kv[i] > ke;
                 }
-                if (lane < lay.k) {
-                    sidx[lane] = emine;
-                    sw[lane] = mine / sum;
-                    recs[lane] = recs_all[emine];
-                    if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = emine;
+                const int rank = r[0] + r[1] + r[2] + r[3];
+                if (rank < kk) {
+                    sidx[rank] = e;
+                    sz[rank] = key_value((uint32_t)(ke >> 32));
                 }
             }
         }
-        __syncthreads();
-        if (!*bcast) return;
+        lds_sync();
+        if (wave == 0 && lane < lay.k) {
+            const float zmax = sz[0];
+            float sum = 0.f, mine = 0.f;
+            for (int r = 0; r < lay.k; r++) {
+                const float z = sz[r];
+                const float sc = lay.score_fn == MOE_SCORE_SOFTMAX ? __expf(z - zmax) : 1.f / (1.f + __expf(-z));
+                sum += sc;
+                if (r == lane) mine = sc;
+            }
+            const int e = sidx[lane];
+            sw[lane] = mine / sum;
+            recs[lane] = recs_all[e];
+            if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = e;
+        }
+        lds_sync();
         mark(kStampRouted);
 
         // ---- gate/up over this workgroup's range of (rank, tile, chunk), one
@@ -724,7 +792,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                           (const u32x4 *)(rec + a.off.cb[0]), (const u32x4 *)(rec + a.off.cb[1]), H, I, cprH,
                           (int)(ea - base), (int)(eb - base), (int)(ea / cprH - base / cprH), a.slots_red_gu, wave,
                           lane, stamp);
-            __syncthreads();
+            lds_sync();
             mark(kStampGuLoop);
             // one tagged partial per touched tile (wave v: tiles v, v + kPW,
             // ...); the workgroup owning a tile's last unit joins it (one
@@ -794,32 +862,54 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         }
 
         mark(kStampGuDone);
-        // ---- shared down rows (after the whole shared h is ready), tagged
+        // ---- shared down rows (after the whole shared h is ready), tagged;
+        // kShRows rows at a time with every thread on 8 columns of each, as
+        // for gate/up
         if (shared_on && shH1 > shH0) {
             if (!wg_wait(sync, h_ready + k, (unsigned)(s + 1) * sh_gu_contrib, bcast)) return;
             float *hl = (float *)lds;                                   // [I]
+            float *shred = hl + I;                                      // [kPW][kShRows]
             for (int b = wave; b * 64 < I; b += kPW) dma_block(hl + b * 64, a.hs + b * 64, lane);
             wait_vm_all();
             __syncthreads();
-            for (int r = shH0 + wave; r < shH1; r += kPW) {
-                const uint16_t *wd = lay.shared + 2 * (size_t)I * H + (size_t)r * I;
-                float acc = 0.f;
-                for (int c = lane * 8; c < I; c += 512) {
-                    const uint4 dv = *(const uint4 *)(wd + c);
+            const uint16_t *wd0 = lay.shared + 2 * (size_t)I * H;
+            for (int r0 = shH0; r0 < shH1; r0 += kShRows) {
+                const int nr = min(kShRows, shH1 - r0);
+                float acc[kShRows];
+#pragma unroll
+                for (int q = 0; q < kShRows; q++) acc[q] = 0.f;
+                for (int c = threadIdx.x * 8; c < I; c += kPW * 64 * 8) {
+                    uint4 dv[kShRows];
+#pragma unroll
+                    for (int q = 0; q < kShRows; q++)
+                        dv[q] = *(const uint4 *)(wd0 + (size_t)min(r0 + q, shH1 - 1) * I + c);
                     float hv[8];
 #pragma unroll
                     for (int i = 0; i < 8; i++) hv[i] = hl[c + i];
-                    const uint32_t q[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        acc = fmaf(__uint_as_float(q[i] << 16), hv[2 * i], acc);
-                        acc = fmaf(__uint_as_float(q[i] & 0xFFFF0000u), hv[2 * i + 1], acc);
+                    for (int q = 0; q < kShRows; q++) {
+                        const uint32_t dq[4] = {dv[q].x, dv[q].y, dv[q].z, dv[q].w};
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            acc[q] = fmaf(__uint_as_float(dq[i] << 16), hv[2 * i], acc[q]);
+                            acc[q] = fmaf(__uint_as_float(dq[i] & 0xFFFF0000u), hv[2 * i + 1], acc[q]);
+                        }
                     }
                 }
-                acc = wave_sum(acc);
-                if (lane == 0) st_tagged(a.ysh + r, acc, tag);
+#pragma unroll
+                for (int q = 0; q < kShRows; q++) acc[q] = wave_sum(acc[q]);
+                if (lane == 0) {
+#pragma unroll
+                    for (int q = 0; q < kShRows; q++) shred[wave * kShRows + q] = acc[q];
+                }
+                lds_sync();
+                if (threadIdx.x < nr) {
+                    float y = 0.f;
+                    for (int v = 0; v < kPW; v++) y += shred[v * kShRows + threadIdx.x];
+                    st_tagged(a.ysh + r0 + threadIdx.x, y, tag);
+                }
+                lds_sync();
             }
-            __syncthreads();
         }
 
         mark(kStampSharedDown);
@@ -835,7 +925,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                              bcast, H, I, cprI, (int)(ea - base), (int)(eb - base), (int)(ea / cprI - base / cprI),
                              a.slots_red_d, wave, lane, stamp))
                 return;
-            __syncthreads();
+            lds_sync();
             mark(kStampDownLoop);
             const long tA = ea / cprI;
             const int nt = (int)((eb - 1) / cprI - tA) + 1;
@@ -849,7 +939,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 st_tagged(a.part_d + ((size_t)tau * a.slots_d + (w - range_owner(nD, G, tau * cprI))) * 64 + lane, y,
                           tag);
             }
-            __syncthreads();
+            lds_sync();
             ea = eb;
         }
 
@@ -873,7 +963,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     __hip_atomic_fetch_add(sync + kLayerDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             if (lane == 0 && !okc) *bcast = 0;
-            __syncthreads();
+            lds_sync();
             if (!*bcast) return;
         }
         mark(kStampDownDone);
@@ -958,7 +1048,7 @@ hipError_t decode_plan(int H, int I, int k, DecodePlanOut *o) {
     const long red_gu = 2L * kCbRows * 16 + ((H * 2 + 255) & ~255) + (long)o->slots_red_gu * kPW * 128 * 4;
     const long red_d = (long)kCbRows * 16 + ((I * 2 + 255) & ~255) + (long)o->slots_red_d * kPW * 64 * 4;
     // the shared expert's fp32 h is staged below the record pointers
-    o->lds_ok = red_gu <= kDecTail && red_d <= kDecTail && (long)I * 4 <= kDecRecs;
+    o->lds_ok = red_gu <= kDecTail && red_d <= kDecTail && (long)I * 4 + kPW * kShRows * 4 <= kDecRecs;
     return hipSuccess;
 }
 
