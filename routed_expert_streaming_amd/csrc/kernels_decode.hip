@@ -474,9 +474,11 @@ __device__ __forceinline__ int combiner_of(int td, int k, int tilesH, int cprI, 
 
 // Output tile td, by one wave: out = sum_j w_j * sum_slots y_j + shared, in
 // fixed (rank, contributor) order, from tagged partials polled until every
-// contribution of this step is there.  Each poll loads two ranks' partials
-// (up to 4 contributors each) and, the first time, the shared output, so a
-// top-2 layer needs one round trip.  Returns false on a failed wait.
+// contribution of this step is there.  Each poll loads RG ranks' partials (up
+// to 4 contributors each) and, the first time, the shared output, so a layer
+// of up to RG ranks needs one round trip once the last partial lands.
+// Returns false on a failed wait.
+template <int RG>
 __device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k, int tilesH, int cprI, long nD,
                                              int G, int H, bool shared_on, const uint64_t *part_d, int slots_d,
                                              const uint64_t *ysh, float *out, const float *sw, unsigned *sync,
@@ -484,26 +486,34 @@ __device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k,
     const int r = td * kTileRows + lane;
     float o = 0.f, sh = 0.f;
     long spins = 0;
-    for (int j = 0; j < k; j += 2) {
-        const bool two = j + 1 < k;
-        const long ta = (long)j * tilesH + td, tb = two ? ta + tilesH : ta;
-        const int ca = range_owner(nD, G, (ta + 1) * cprI - 1) - range_owner(nD, G, ta * cprI) + 1;
-        const int cb = two ? range_owner(nD, G, (tb + 1) * cprI - 1) - range_owner(nD, G, tb * cprI) + 1 : ca;
-        const uint64_t *pa = part_d + (size_t)ta * slots_d * 64 + lane;
-        const uint64_t *pb = part_d + (size_t)tb * slots_d * 64 + lane;
-        const bool with_shared = shared_on && j == 0;
-        float ya = 0.f, yb = 0.f;
-        for (int s0 = 0; s0 < max(ca, cb); s0 += 4) {
-            uint64_t va[4], vb[4], vs = 0;
+    // ranks RG at a time, contributors 4 at a time: up to 4 RG partials (and
+    // the shared output) in flight per poll
+    for (int j0 = 0; j0 < k; j0 += RG) {
+        float ya[RG];
+        int cj[RG];
+        const uint64_t *pj[RG];
+        int cmax = 0;
+#pragma unroll
+        for (int jj = 0; jj < RG; jj++) {
+            const long t = (long)min(j0 + jj, k - 1) * tilesH + td;
+            cj[jj] = range_owner(nD, G, (t + 1) * cprI - 1) - range_owner(nD, G, t * cprI) + 1;
+            pj[jj] = part_d + (size_t)t * slots_d * 64 + lane;
+            cmax = max(cmax, cj[jj]);
+            ya[jj] = 0.f;
+        }
+        for (int q0 = 0; q0 < cmax; q0 += 4) {
+            const bool with_shared = shared_on && j0 == 0 && q0 == 0;
+            uint64_t v[RG][4], vs = 0;
             for (;;) {
                 bool ok = true;
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    va[q] = ld_tagged(pa + (size_t)min(s0 + q, ca - 1) * 64);
-                    vb[q] = ld_tagged(pb + (size_t)min(s0 + q, cb - 1) * 64);
-                    ok = ok && tag_ok(va[q], tag) && tag_ok(vb[q], tag);
-                }
-                if (with_shared && s0 == 0) {
+                for (int jj = 0; jj < RG; jj++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        v[jj][q] = ld_tagged(pj[jj] + (size_t)min(q0 + q, cj[jj] - 1) * 64);
+                        ok = ok && tag_ok(v[jj][q], tag);
+                    }
+                if (with_shared) {
                     vs = ld_tagged(ysh + r);
                     ok = ok && tag_ok(vs, tag);
                 }
@@ -511,14 +521,15 @@ __device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k,
                 if (!poll_more(sync, spins)) return false;
             }
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                if (s0 + q < ca) ya += tag_val(va[q]);
-                if (two && s0 + q < cb) yb += tag_val(vb[q]);
-            }
-            if (with_shared && s0 == 0) sh = tag_val(vs);
+            for (int jj = 0; jj < RG; jj++)
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    if (j0 + jj < k && q0 + q < cj[jj]) ya[jj] += tag_val(v[jj][q]);
+            if (with_shared) sh = tag_val(vs);
         }
-        o = fmaf(sw[j], ya, o);
-        if (two) o = fmaf(sw[j + 1], yb, o);
+#pragma unroll
+        for (int jj = 0; jj < RG; jj++)
+            if (j0 + jj < k) o = fmaf(sw[j0 + jj], ya[jj], o);
     }
     if (shared_on) o += sh;
     out[(size_t)s * H + r] = o;
@@ -955,8 +966,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             for (int td = tdA; td <= tdB; td++) {
                 if (combiner_of(td, k, tilesH, cprI, nD, G) != w) continue;
                 if (nc++ % kPW != wave || !okc) continue;
-                okc = combine_tile(td, s, tag, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d, a.ysh,
-                                   a.out, sw, sync, lane);
+                okc = k <= 2 ? combine_tile<2>(td, s, tag, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d,
+                                               a.ysh, a.out, sw, sync, lane)
+                             : combine_tile<8>(td, s, tag, k, tilesH, cprI, nD, G, H, shared_on, a.part_d, a.slots_d,
+                                               a.ysh, a.out, sw, sync, lane);
                 // counted at once: nothing in this launch reads the outputs, and
                 // the partials it read are consumed (their values are used)
                 if (okc && lane == 0)
