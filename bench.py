@@ -107,10 +107,12 @@ def main() -> int:
     ap.add_argument("--config", default="mixtral", choices=["mixtral", "kimi_linear", "batched", "k3_slice"],
                     help="mixtral / kimi_linear: resident decode; batched: one 256-token grouped layer call "
                          "per step; k3_slice: streamed decode through the HBM slot cache (cold start)")
-    ap.add_argument("--sweep", choices=["capacity", "k", "ahead"], default=None,
+    ap.add_argument("--sweep", choices=["capacity", "k", "ahead", "tiers"], default=None,
                     help="k3_slice only: hit rate and tok/s against cache capacity (one stack-distance pass "
                          "plus measured runs), tok/s against experts per token, or look-ahead reads on "
-                         "chained inputs")
+                         "chained inputs, or the three-tier path with a record file read with O_DIRECT")
+    ap.add_argument("--tier-dir", default="/tmp", help="directory for the record file of --sweep tiers")
+    ap.add_argument("--io-threads", type=int, default=8, help="file reader threads of --sweep tiers")
     ap.add_argument("--cpu-sample-tokens", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -154,6 +156,8 @@ def main() -> int:
         return bench_sweep_k(args, cfg)
     if args.sweep == "ahead":
         return bench_sweep_ahead(args, cfg)
+    if args.sweep == "tiers":
+        return bench_sweep_tiers(args, cfg)
     if args.config == "k3_slice":
         return bench_streamed(args, cfg)
     n_tok = args.warmup + args.steps
@@ -496,6 +500,86 @@ def bench_sweep_ahead(args, cfg) -> int:
            "runs": runs, "outputs_identical": ok, "cold_tier": _cold_tier(cfg, hp), "commit": git_commit()}
     print(json.dumps(rec), flush=True)
     return 0 if ok else 1
+
+
+def bench_sweep_tiers(args, cfg) -> int:
+    """Three tiers (WISP: VRAM, then RAM, then NVMe): the first two layers of
+    the K3 slice (1536 records, 18.5 GB) in a file read with O_DIRECT, behind
+    a pinned host pool and the HBM slot cache, both cold.  Runs: host pool of
+    25% of the records, and of only k records (nearly every HBM miss read
+    from the file).  The file is written, synced, used, and removed."""
+    import numpy as np
+    import torch
+
+    import synth
+    import routed_expert_streaming_amd as moe
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload, write_record_file
+    n_tok = args.warmup + args.steps
+    ck = cfg.replace(layers=2, tokens=max(n_tok, cfg.tokens))
+    path = os.path.join(args.tier_dir, f"moe_tier_records_{os.getpid()}.bin")
+    t0 = time.time()
+    def progress(n):
+        if n % 256 == 0:
+            log(f"  {n} records written ({time.time() - t0:.0f} s)")
+
+    stride = write_record_file(ck, path, list(range(ck.layers)), progress=progress)
+    with open(path, "rb+") as f:
+        os.fsync(f.fileno())
+    t_write = time.time() - t0
+    n_rec = ck.layers * ck.E
+    log(f"record file {n_rec * stride / 1e9:.1f} GB written and synced in {t_write:.1f} s")
+    try:
+        dw = DeviceWorkload(ck, with_records=False)
+        x = dw.inputs()
+        ws = torch.empty(moe.streamed_workspace_bytes(dw.layers[0]), dtype=torch.uint8, device="cuda")
+        copy_stream = torch.cuda.Stream()
+        hbm_slots = n_rec // 4
+        runs = []
+        for ram_slots in (n_rec // 4, ck.k):
+            pool = torch.empty(hbm_slots * stride, dtype=torch.uint8, device="cuda")
+            cache = moe.ExpertCache(hbm_slots, stride, pool)
+            tier = moe.HostTier(path, stride, n_rec, ram_slots, io_threads=args.io_threads)
+
+            def token(t):
+                for L in range(ck.layers):
+                    moe.layer_forward_streamed(dw.layers[L], cache, L, None, x[t, L][None], copy_stream, ws=ws,
+                                               tier=(tier, L * ck.E))
+
+            for t in range(args.warmup):
+                token(t)
+            torch.cuda.synchronize()
+            c0, s0 = cache.stats(), tier.stats()
+            ts = time.perf_counter()
+            for i in range(args.steps):
+                token(args.warmup + i)
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - ts
+            c1, s1 = cache.stats(), tier.stats()
+            dc = {q: c1[q] - c0[q] for q in c1}
+            dt = {q: s1[q] - s0[q] for q in s1}
+            runs.append({"hbm_slots": hbm_slots, "host_slots": ram_slots, "tok_s": round(args.steps / elapsed, 3),
+                         "layers_per_token": ck.layers,
+                         "hbm_hit_rate": round(dc["hits"] / max(1, dc["lookups"]), 4),
+                         "host_hit_rate": round(dt["hits"] / max(1, dt["lookups"]), 4),
+                         "file_reads_per_token": round(dt["reads"] / args.steps, 2),
+                         "file_read_gbs": round(dt["read_bytes"] / max(1, dt["read_ns"]), 2),
+                         "file_gb_per_token": round(dt["read_bytes"] / args.steps / 1e9, 3)})
+            log(f"host slots {ram_slots}: {runs[-1]}")
+            tier.close()
+            cache.close()
+            del pool
+    finally:
+        os.remove(path)
+    rec = {"metric": "three-tier streamed decode tok/s on 1 MI355X (HBM cache, pinned host pool, O_DIRECT file)",
+           "value": runs[0]["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "data": "synthetic",
+           "config": {"workload": f"k3_slice layers 0-1: {ck.E} experts x 2 layers, H {ck.H}, I {ck.I}, top-{ck.k} "
+                                  f"sigmoid + shared, Zipf bias; cold tiers",
+                      "file": f"{n_rec} records x {stride} B in {args.tier_dir}",
+                      "file_write_s": round(t_write, 1)},
+           "runs": runs, "commit": git_commit()}
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def bench_sweep_k(args, cfg) -> int:

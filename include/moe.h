@@ -336,6 +336,40 @@ int moe_layer_forward_streamed_ahead(const moe_layer *L, moe_cache *c, uint32_t 
                                      uint32_t next_layer_id, const void *const *next_experts_host,
                                      int32_t k_ahead);
 
+/* ---- third tier: expert records in a file ------------------------------- */
+typedef struct moe_host_tier moe_host_tier;
+
+/* A file of n_records records of record_bytes each (record i at byte
+ * i * record_bytes), read with O_DIRECT (WASTE "유휴 가중치는 …": one aligned
+ * read per expert, no OS page cache, so measured hit rates are real) into a
+ * caller-owned pinned host pool of `slots` records kept as LRU (WISP "통찰":
+ * VRAM, then RAM, then the disk).  io_threads host threads read the misses of
+ * one layer call in parallel.  MOE_E_INVAL if record_bytes is not a multiple
+ * of 4096, the pool is not 4096-aligned, the file cannot be opened with
+ * O_DIRECT or is shorter than n_records records. */
+int moe_host_tier_create(const char *path, uint64_t record_bytes, int64_t n_records, int32_t slots,
+                         void *pinned_pool, int32_t io_threads, moe_host_tier **out);
+/* Waits for the copies still reading the pool, closes the file. */
+void moe_host_tier_destroy(moe_host_tier *t);
+/* Counters since creation: lookups and hits of the host slots, records read
+ * from the file, their bytes, and the wall time spent in reads (ns). */
+int moe_host_tier_stats(moe_host_tier *t, int64_t *lookups, int64_t *hits, int64_t *reads,
+                        int64_t *read_bytes, int64_t *read_ns);
+/* The host tier's LRU trace (keys are record indices), as expert_cache_trace. */
+int moe_host_tier_trace(moe_host_tier *t, moe_trace_rec *buf, int64_t cap, int64_t *n);
+
+/* moe_layer_forward_streamed with the file tier behind the HBM cache: the
+ * records of the HBM misses (expert e is file record record0 + e) come from
+ * the host slots, the absent ones read from the file first (in parallel,
+ * while the hit experts compute); each copy then goes to the device as in
+ * moe_layer_forward_streamed.  Outputs are identical to it bit for bit.
+ * MOE_E_INVAL if the host tier has fewer slots than k, besides the
+ * conditions of moe_layer_forward_streamed. */
+int moe_layer_forward_streamed_tiered(const moe_layer *L, moe_cache *c, uint32_t layer_id,
+                                      moe_host_tier *tier, int64_t record0, const float *x, int32_t T,
+                                      float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
+                                      void *compute_stream, void *copy_stream);
+
 #ifdef __cplusplus
 }
 #endif

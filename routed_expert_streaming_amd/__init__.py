@@ -4,7 +4,7 @@ Python face of libmoe (include/moe.h): torch supplies device memory and
 streams; every computation runs in the library's HIP kernels.  Names follow
 the C ABI: route_topk, expert_ffn_rvq, layer_forward, decode_forward,
 layer_forward_grouped, ExpertCache (expert_cache_*), layer_forward_streamed,
-lru_stack_distances.
+lru_stack_distances, HostTier (moe_host_tier_*).
 """
 from __future__ import annotations
 
@@ -305,6 +305,44 @@ def lru_hits_at(dist, capacities: Sequence[int]) -> List[int]:
     return [int(np.searchsorted(warm, c, side="left")) for c in capacities]
 
 
+class HostTier:
+    """Expert records in a file (moe_host_tier_*): O_DIRECT reads into a
+    pinned pool of `slots` records kept as LRU, the source of the HBM
+    cache's misses in layer_forward_streamed(..., tier=(this, record0))."""
+
+    def __init__(self, path: str, record_bytes: int, n_records: int, slots: int, io_threads: int = 8):
+        self.pool = torch.empty(slots * record_bytes + 4096, dtype=torch.uint8, pin_memory=True)
+        base = (self.pool.data_ptr() + 4095) & ~4095
+        h = ctypes.c_void_p()
+        check(lib().moe_host_tier_create(path.encode(), record_bytes, n_records, slots, base, io_threads,
+                                         ctypes.byref(h)), "moe_host_tier_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            lib().moe_host_tier_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def stats(self):
+        v = [ctypes.c_int64() for _ in range(5)]
+        check(lib().moe_host_tier_stats(self.handle, *[ctypes.byref(x) for x in v]), "moe_host_tier_stats")
+        return dict(zip(("lookups", "hits", "reads", "read_bytes", "read_ns"), [x.value for x in v]))
+
+    def trace(self):
+        """List of (key, hit, slot, evicted or None); keys are record indices."""
+        n = ctypes.c_int64()
+        lib().moe_host_tier_trace(self.handle, None, 0, ctypes.byref(n))
+        buf = (MoeTraceRec * max(n.value, 1))()
+        check(lib().moe_host_tier_trace(self.handle, buf, n.value, ctypes.byref(n)), "moe_host_tier_trace")
+        return [(r.key, r.hit, r.slot, None if r.evicted == MOE_NO_KEY else r.evicted) for r in buf[:n.value]]
+
+
 def streamed_workspace_bytes(layer: Layer, T: int = 1) -> int:
     s = layer.struct()
     return lib().moe_streamed_workspace_bytes(ctypes.byref(s), T)
@@ -313,17 +351,28 @@ def streamed_workspace_bytes(layer: Layer, T: int = 1) -> int:
 def layer_forward_streamed(layer: Layer, cache: ExpertCache, layer_id: int, experts_host: Sequence[int],
                            x: torch.Tensor, copy_stream: torch.cuda.Stream, stream=None,
                            ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                           idx: Optional[torch.Tensor] = None, host_table=None, ahead=None):
+                           idx: Optional[torch.Tensor] = None, host_table=None, ahead=None, tier=None):
     """One decode step of one layer fed from the slot cache.  experts_host:
     E pinned host addresses of the layer's records (or a prebuilt ctypes
     array).  ahead = (next_layer, next_layer_id, next_host_table, k_ahead)
-    adds the look-ahead read of moe_layer_forward_streamed_ahead."""
+    adds the look-ahead read of moe_layer_forward_streamed_ahead; tier =
+    (HostTier, record0) takes the misses from the file tier instead
+    (moe_layer_forward_streamed_tiered)."""
     _need(x.dim() == 2 and x.shape[0] == 1 and x.dtype == torch.float32, "x must be fp32 [1, H]")
     out = out if out is not None else torch.empty((1, layer.H), dtype=torch.float32, device=x.device)
     s = layer.struct()
-    table = host_table if host_table is not None else (ctypes.c_void_p * len(experts_host))(*experts_host)
+    table = None
+    if tier is None:
+        table = host_table if host_table is not None else (ctypes.c_void_p * len(experts_host))(*experts_host)
     need = lib().moe_streamed_workspace_bytes(ctypes.byref(s), 1)
     ws = ws if ws is not None else _ws(need, x.device)
+    if tier is not None:
+        ht, record0 = tier
+        check(lib().moe_layer_forward_streamed_tiered(ctypes.byref(s), cache.handle, layer_id, ht.handle, record0,
+                                                      _ptr(x), 1, _ptr(out), _ptr(idx), _ptr(ws), ws.numel(),
+                                                      _stream(stream), _stream(copy_stream)),
+              "moe_layer_forward_streamed_tiered")
+        return out
     if ahead is None:
         check(lib().moe_layer_forward_streamed(ctypes.byref(s), cache.handle, layer_id, table, _ptr(x), 1, _ptr(out),
                                                _ptr(idx), _ptr(ws), ws.numel(), _stream(stream),

@@ -69,6 +69,13 @@ SIGNATURES = {
     "moe_lru_stack_distances": (ctypes.c_int, [P, I64, P]),
     "expert_cache_stats_ahead": (ctypes.c_int, [P, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                                 ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+    "moe_host_tier_create": (ctypes.c_int, [ctypes.c_char_p, U64, I64, I32, P, I32, ctypes.POINTER(P)]),
+    "moe_host_tier_destroy": (None, [P]),
+    "moe_host_tier_stats": (ctypes.c_int, [P, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                           ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+    "moe_host_tier_trace": (ctypes.c_int, [P, ctypes.POINTER(MoeTraceRec), I64, ctypes.POINTER(I64)]),
+    "moe_layer_forward_streamed_tiered": (ctypes.c_int, [ctypes.POINTER(MoeLayer), P, U32, P, I64, P, I32, P, P, P,
+                                                         SZ, P, P]),
     "moe_layer_forward_streamed_ahead": (ctypes.c_int, [ctypes.POINTER(MoeLayer), P, U32, P, P, I32, P, P,
                                                         P, SZ, P, P, ctypes.POINTER(MoeLayer), U32, P, I32]),
     "moe_streamed_workspace_bytes": (SZ, [ctypes.POINTER(MoeLayer), I32]),

@@ -11,6 +11,7 @@
 #include <string>
 
 #include "expert_cache.h"
+#include "host_tier.h"
 #include "moe_internal.h"
 
 using namespace moe;
@@ -440,16 +441,21 @@ struct Ahead {
     const void *const *host = nullptr;
     int k = 0;
 };
+struct Tier {
+    moe_host_tier *t = nullptr;            // file tier, or null: records from experts_host
+    int64_t record0 = 0;
+};
 
 int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const void *const *experts_host,
                   const float *x, int32_t T, float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
-                  void *compute_stream, void *copy_stream, const Ahead &ah) {
+                  void *compute_stream, void *copy_stream, const Ahead &ah, const Tier &tier = Tier{}) {
     int rc = check_layer(L, false);
     if (rc) return rc;
     if (!c) return fail(MOE_E_INVAL, "cache is NULL");
     if (T < 0 || T > 1) return fail(MOE_E_INVAL, "streamed decode takes T = 1 token (got %d)", T);
     if (T == 0) return MOE_OK;
-    if (!experts_host || !x || !out || !ws) return fail(MOE_E_INVAL, "experts_host, x, out and ws must be non-NULL");
+    if ((!experts_host && !tier.t) || !x || !out || !ws)
+        return fail(MOE_E_INVAL, "experts_host (or a tier), x, out and ws must be non-NULL");
     const int H = L->H, I = L->I, E = L->router.E, k = L->router.k;
     if (c->core.capacity() < k)
         return fail(MOE_E_INVAL, "cache capacity %d is below k = %d: the layer cannot hold one token's experts",
@@ -518,7 +524,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     for (int j = 0; j < k; j++) {
         order[j] = j;
         if (c->h_idx[j] < 0 || c->h_idx[j] >= E) return fail(MOE_E_HIP, "router produced expert id %d", c->h_idx[j]);
-        if (!experts_host[c->h_idx[j]]) return fail(MOE_E_INVAL, "experts_host[%d] is NULL", c->h_idx[j]);
+        if (!tier.t && !experts_host[c->h_idx[j]]) return fail(MOE_E_INVAL, "experts_host[%d] is NULL", c->h_idx[j]);
     }
     std::sort(order, order + k, [&](int a, int b) { return c->h_idx[a] < c->h_idx[b]; });
     int32_t slot_of[MOE_MAX_K];
@@ -553,6 +559,26 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         HIPCHK(launch_rvq_gateup(hits, off, H, I, hits.n_local, W.xh, W.hh, cs), "rvq gate/up (hits)");
         HIPCHK(launch_rvq_down(hits, off, H, I, hits.n_local, KS, W.hh, W.ypart, cs), "rvq down (hits)");
     }
+    // file tier: the misses' records into host slots (read while the hit
+    // experts compute)
+    const char *src_of[MOE_MAX_K] = {};
+    if (tier.t) {
+        int64_t recs[MOE_MAX_K];
+        int nm = 0, mj[MOE_MAX_K];
+        for (int n = 0; n < k; n++) {
+            const int j = order[n];
+            if (hit[j]) continue;
+            mj[nm] = j;
+            recs[nm++] = tier.record0 + c->h_idx[j];
+        }
+        const char *ptrs[MOE_MAX_K];
+        rc = tier_fetch(tier.t, recs, nm, ptrs);
+        if (rc) {
+            for (int q = 0; q < nm; q++) c->core.drop_slot(slot_of[mj[q]]);   // never filled
+            return rc;
+        }
+        for (int q = 0; q < nm; q++) src_of[mj[q]] = ptrs[q];
+    }
     // each miss: copy into its slot after the slot's previous readers, then
     // its expert after the copy lands
     for (int n = 0; n < k; n++) {
@@ -560,8 +586,16 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         if (hit[j]) continue;
         const int32_t s = slot_of[j];
         if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "copy waits for slot readers");
-        hipError_t e = hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, experts_host[c->h_idx[j]], c->slot_bytes,
+        const void *src = tier.t ? (const void *)src_of[j] : experts_host[c->h_idx[j]];
+        hipError_t e = hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, src, c->slot_bytes,
                                       hipMemcpyHostToDevice, ps);
+        if (e == hipSuccess && tier.t) {
+            const int trc = tier_copied(tier.t, src_of[j], ps);
+            if (trc) {
+                c->core.drop_slot(s);
+                return trc;
+            }
+        }
         if (e == hipSuccess) e = hipEventRecord(c->ready[s], ps);
         if (e != hipSuccess) {
             c->core.drop_slot(s);             // the slot's contents are unknown now
@@ -624,6 +658,23 @@ int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_
                                void *compute_stream, void *copy_stream) {
     return streamed_impl(L, c, layer_id, experts_host, x, T, out, idx_out, ws, ws_bytes, compute_stream, copy_stream,
                          Ahead{});
+}
+
+int moe_layer_forward_streamed_tiered(const moe_layer *L, moe_cache *c, uint32_t layer_id, moe_host_tier *tier,
+                                      int64_t record0, const float *x, int32_t T, float *out, int32_t *idx_out,
+                                      void *ws, size_t ws_bytes, void *compute_stream, void *copy_stream) {
+    if (!tier) return fail(MOE_E_INVAL, "host tier is NULL");
+    if (c && tier->record_bytes < c->slot_bytes)
+        return fail(MOE_E_INVAL, "host tier records (%llu bytes) are smaller than the cache slots (%llu)",
+                    (unsigned long long)tier->record_bytes, (unsigned long long)c->slot_bytes);
+    if (L && tier->core.capacity() < L->router.k)
+        return fail(MOE_E_INVAL, "host tier has %d slots, below k = %d", tier->core.capacity(), L->router.k);
+    if (record0 < 0) return fail(MOE_E_INVAL, "record0=%lld < 0", (long long)record0);
+    Tier tr;
+    tr.t = tier;
+    tr.record0 = record0;
+    return streamed_impl(L, c, layer_id, nullptr, x, T, out, idx_out, ws, ws_bytes, compute_stream, copy_stream,
+                         Ahead{}, tr);
 }
 
 int moe_layer_forward_streamed_ahead(const moe_layer *L, moe_cache *c, uint32_t layer_id,

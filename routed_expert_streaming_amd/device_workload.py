@@ -77,6 +77,27 @@ class DeviceWorkload:
         return torch.from_numpy(np.ascontiguousarray(x)).to(self.device)
 
 
+def write_record_file(cfg: synth.MoEConfig, path: str, layers: Sequence[int], batch: int = 64,
+                      progress=None) -> int:
+    """Write the records of `layers` (all E experts each) to `path`, record
+    (i, e) of the i-th listed layer at index i * E + e, each padded to the
+    4 KiB record stride (the file tier's layout).  Returns the stride.
+    progress(records_written) is called after every batch if given."""
+    wl = synth.Workload(cfg)
+    stride = wl.layout.padded
+    keys = [(L, e) for L in layers for e in range(cfg.E)]
+    buf = np.zeros((min(batch, len(keys)), stride), dtype=np.uint8)
+    with open(path, "wb") as f:
+        for k0 in range(0, len(keys), batch):
+            ck = keys[k0:k0 + batch]
+            buf[:len(ck)] = 0
+            wl.fill_records(ck, [buf[j] for j in range(len(ck))], _threads())
+            f.write(buf[:len(ck)].tobytes())
+            if progress:
+                progress(k0 + len(ck))
+    return stride
+
+
 def chain_next_input(h: torch.Tensor, out: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
     """Chained (pre-norm) decode inputs, a stand-in for the trunk between MoE
     layers, which is not modelled: the residual stream h [H] takes the layer's

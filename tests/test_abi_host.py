@@ -114,3 +114,21 @@ def test_cache_create_validation(L):
     assert L.expert_cache_create(4, 100, 1, ctypes.byref(h)) == _lib.MOE_E_INVAL
     assert L.expert_cache_create(4, 4096, None, ctypes.byref(h)) == _lib.MOE_E_INVAL
     assert L.expert_cache_lookup(None, 1, ctypes.byref(ctypes.c_int32())) == _lib.MOE_E_INVAL
+
+
+def test_host_tier_rejects_bad_arguments(L, tmp_path):
+    # argument checks that run before any HIP call (no GPU needed)
+    from routed_expert_streaming_amd._lib import MOE_E_INVAL
+    h = ctypes.c_void_p()
+    f = tmp_path / "r.bin"
+    f.write_bytes(b"\0" * 8192)
+    pool = ctypes.create_string_buffer(3 * 4096 + 4096)
+    aligned = (ctypes.addressof(pool) + 4095) & ~4095
+    assert L.moe_host_tier_create(str(f).encode(), 4000, 2, 1, aligned, 1, ctypes.byref(h)) == MOE_E_INVAL
+    assert L.moe_host_tier_create(str(f).encode(), 4096, 2, 1, aligned + 16, 1, ctypes.byref(h)) == MOE_E_INVAL
+    assert L.moe_host_tier_create(str(tmp_path / "none").encode(), 4096, 2, 1, aligned, 1, ctypes.byref(h)) == \
+        MOE_E_INVAL
+    assert L.moe_host_tier_create(str(f).encode(), 4096, 3, 1, aligned, 1, ctypes.byref(h)) == MOE_E_INVAL   # short
+    assert L.moe_host_tier_create(str(f).encode(), 4096, 2, 0, aligned, 1, ctypes.byref(h)) == MOE_E_INVAL
+    assert L.moe_host_tier_create(str(f).encode(), 4096, 2, 1, aligned, 0, ctypes.byref(h)) == MOE_E_INVAL
+    assert not h.value

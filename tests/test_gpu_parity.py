@@ -333,3 +333,46 @@ def test_streamed_lookahead_chained(moe):
     log(f"look-ahead: {st}")
     cache.close()
     cache_plain.close()
+
+
+def test_streamed_file_tier(moe, tmp_path):
+    # Third tier: records in a file read with O_DIRECT into a small pinned
+    # LRU pool behind a small HBM cache.  Outputs equal the resident path's
+    # bit for bit; the host tier's trace replays exactly through the oracle's
+    # LRU over the HBM misses in order; every tier miss is one record read.
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload, write_record_file
+    cfg = synth.get_config("tiny", tokens=6, layers=3, E=16)
+    path = str(tmp_path / "records.bin")
+    stride = write_record_file(cfg, path, list(range(cfg.layers)))
+    dw = DeviceWorkload(cfg)
+    x = dw.inputs()
+    hbm_slots, tier_slots = 4, 6
+    pool = torch.empty(hbm_slots * stride, dtype=torch.uint8, device="cuda")
+    cache = moe.ExpertCache(hbm_slots, stride, pool)
+    tier = moe.HostTier(path, stride, cfg.layers * cfg.E, tier_slots, io_threads=3)
+    copy_stream = torch.cuda.Stream()
+    ws = torch.empty(moe.streamed_workspace_bytes(dw.layers[0]), dtype=torch.uint8, device="cuda")
+    outs = []
+    for t in range(cfg.tokens):
+        for L in range(cfg.layers):
+            o = moe.layer_forward_streamed(dw.layers[L], cache, L, None, x[t, L][None].contiguous(), copy_stream,
+                                           ws=ws, tier=(tier, L * cfg.E))
+            outs.append(o.clone())
+    torch.cuda.synchronize()
+    for n, o in enumerate(outs):
+        t, L = divmod(n, cfg.layers)
+        ro, _, _ = moe.layer_forward(dw.layers[L], x[t, L][None].contiguous())
+        assert torch.equal(o[0], ro[0]), f"file tier != resident at token {t} layer {L}"
+    misses = np.array([r[0] for r in cache.trace() if r[1] == 0], np.int64)   # key = layer * E + e = record
+    tr = tier.trace()
+    assert [r[0] for r in tr] == misses.tolist()
+    hit, slot, ev = oracle.lru(misses, tier_slots)
+    assert [r[1] for r in tr] == hit.tolist()
+    assert [r[2] for r in tr] == slot.tolist()
+    assert [(-1 if r[3] is None else r[3]) for r in tr] == ev.tolist()
+    st = tier.stats()
+    assert st["lookups"] == len(misses) and st["reads"] == len(misses) - int(hit.sum())
+    assert st["read_bytes"] == st["reads"] * stride
+    log(f"file tier: {st}, HBM misses {len(misses)} of {len(cache.trace())}")
+    tier.close()
+    cache.close()
