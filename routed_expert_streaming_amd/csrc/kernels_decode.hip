@@ -37,7 +37,13 @@ constexpr int kPW = 8;                 // waves per workgroup
 constexpr long kSpinLimit = 1L << 24;  // x ~0.1 us per poll: a few seconds
 constexpr int kDecLdsBytes = 160 * 1024;
 
-enum SyncIdx { kErr = 0, kLayerDone = 1, kHReady = 2 };   // h_ready[k+1] follows
+// Counter words, each on its own 256-byte line (pollers of one counter do
+// not contend with adders of another): the error flag, kLayerCopies
+// layer-done counters (output tile td adds to copy td % kLayerCopies; a
+// waiter sums them), then h_ready[j] for j = 0..k (k: the shared expert).
+constexpr int kLine = 64;          // words per counter line
+constexpr int kLayerCopies = 8;
+enum SyncIdx { kErr = 0, kLayerDone = kLine, kHReady = kLine * (1 + kLayerCopies) };
 
 // Cross-workgroup data (logits, packed x, partial sums, h, shared-expert
 // vectors) is written and read with agent-scope relaxed atomic accesses,
@@ -85,15 +91,20 @@ __device__ __forceinline__ void lds_sync() {
     lds_barrier();
 }
 
-// Workgroup-wide wait until *p >= target.  Returns false (error flag set)
-// on timeout or if another workgroup already failed.
+// Workgroup-wide wait until the sum of the NC counters p[0], p[kLine], ...
+// reaches target.  Returns false (error flag set) on timeout or if another
+// workgroup already failed.
+template <int NC = 1>
 __device__ __forceinline__ bool wg_wait(unsigned *sync, const unsigned *p, unsigned target, int *bcast) {
     if (threadIdx.x == 0) {
         long spins = 0;
         int ok = 1;
         for (;;) {
-            // both loads in flight together: one memory round trip per poll
-            const unsigned c = ld_cnt(p), err = ld_cnt(sync + kErr);
+            // all loads in flight together: one memory round trip per poll
+            unsigned c = 0;
+#pragma unroll
+            for (int i = 0; i < NC; i++) c += ld_cnt(p + i * kLine);
+            const unsigned err = ld_cnt(sync + kErr);
             if (c >= target) break;
             if (err) { ok = 0; break; }
             __builtin_amdgcn_s_sleep(1);
@@ -578,7 +589,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
     const long gu0 = range_start(nGU, G, w), gu1 = range_start(nGU, G, w + 1);
     const long d0 = range_start(nD, G, w), d1 = range_start(nD, G, w + 1);
     unsigned *sync = a.sync;
-    unsigned *h_ready = sync + kHReady;                          // [k+1]
+    unsigned *h_ready = sync + kHReady;                          // [k+1], kLine apart
     const int steps = a.T * a.nL;
     // shared-expert row ranges
     const int shI0 = (int)range_start(I, G, w), shI1 = (int)range_start(I, G, w + 1);
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // fixed during the launch): the chosen experts' loads can start right
         // after top-k
         for (int e = threadIdx.x; e < E; e += kPW * 64) recs_all[e] = (uint64_t)lay.records[e];
-        if (s > 0 && !wg_wait(sync, sync + kLayerDone, (unsigned)s * tilesH, bcast)) return;
+        if (s > 0 && !wg_wait<kLayerCopies>(sync, sync + kLayerDone, (unsigned)s * tilesH, bcast)) return;
         if (s == 0) lds_sync();
         mark(kStampLayerWait);
 
@@ -713,7 +724,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // wave 1 wrote every row: once its stores are done, count them
             if (wave == 1) {
                 wait_vm_all();
-                if (lane == 0) __hip_atomic_fetch_add(h_ready + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane == 0)
+                    __hip_atomic_fetch_add(h_ready + k * kLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
 
@@ -868,7 +880,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             __syncthreads();
             if (!*bcast) return;
             if (threadIdx.x == 0 && nj)
-                __hip_atomic_fetch_add(h_ready + j, (unsigned)nj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(h_ready + j * kLine, (unsigned)nj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             ea = eb;
         }
 
@@ -877,7 +889,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // kShRows rows at a time with every thread on 8 columns of each, as
         // for gate/up
         if (shared_on && shH1 > shH0) {
-            if (!wg_wait(sync, h_ready + k, (unsigned)(s + 1) * sh_gu_contrib, bcast)) return;
+            if (!wg_wait(sync, h_ready + k * kLine, (unsigned)(s + 1) * sh_gu_contrib, bcast)) return;
             float *hl = (float *)lds;                                   // [I]
             float *shred = hl + I;                                      // [kPW][kShRows]
             for (int b = wave; b * 64 < I; b += kPW) dma_block(hl + b * 64, a.hs + b * 64, lane);
@@ -932,7 +944,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             const uint8_t *rec = (const uint8_t *)recs[j];
             const long base = (long)j * tilesH * cprI;
             if (!stream_down((const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]),
-                             (const uint32_t *)(a.hh + (size_t)j * I), sync, h_ready + j, (unsigned)(s + 1) * tilesI,
+                             (const uint32_t *)(a.hh + (size_t)j * I), sync, h_ready + j * kLine, (unsigned)(s + 1) * tilesI,
                              bcast, H, I, cprI, (int)(ea - base), (int)(eb - base), (int)(ea / cprI - base / cprI),
                              a.slots_red_d, wave, lane, stamp))
                 return;
@@ -973,7 +985,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 // counted at once: nothing in this launch reads the outputs, and
                 // the partials it read are consumed (their values are used)
                 if (okc && lane == 0)
-                    __hip_atomic_fetch_add(sync + kLayerDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_add(sync + kLayerDone + (td % kLayerCopies) * kLine, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
             }
             if (lane == 0 && !okc) *bcast = 0;
             lds_sync();
@@ -1056,7 +1069,7 @@ hipError_t decode_plan(int H, int I, int k, DecodePlanOut *o) {
     o->slots_d = max_contributors((long)k * tilesH, cprI, G);
     o->slots_red_gu = max_tiles_per_range((long)k * tilesI, cprH, G);
     o->slots_red_d = max_tiles_per_range((long)k * tilesH, cprI, G);
-    o->sync_words = kHReady + (size_t)(k + 1);
+    o->sync_words = kHReady + (size_t)(k + 1) * kLine;
     // LDS: both phases' layouts must fit below the routing tail
     const long red_gu = 2L * kCbRows * 16 + ((H * 2 + 255) & ~255) + (long)o->slots_red_gu * kPW * 128 * 4;
     const long red_d = (long)kCbRows * 16 + ((I * 2 + 255) & ~255) + (long)o->slots_red_d * kPW * 64 * 4;
