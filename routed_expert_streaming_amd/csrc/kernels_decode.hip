@@ -660,74 +660,67 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             }
         }
 
-        // ---- shared gate/up (independent of routing; after the logits, so it
-        // overlaps their exchange instead of delaying it).  The workgroup's
-        // rows go kShRows at a time, each thread on 8 columns of every row of
-        // the group: all weight loads are in flight together (one memory
-        // round trip per group instead of one per 512 columns), then one
-        // workgroup reduction per group.
-        if (shared_on && shI1 > shI0) {
-            float *shred = (float *)lds;   // [kPW][2 * kShRows], codebook area (free until gate/up)
+        // ---- shared gate/up (independent of routing) on waves 1..7 while
+        // wave 0 polls the logits.  The workgroup's rows go kShRows at a
+        // time, each thread on 8 columns of every row of the group: all
+        // weight loads are in flight together, then one reduction per group.
+        // A workgroup with more than kShRows rows (I > kShRows * G) does the
+        // further groups with all waves after the poll.
+        const bool sh_rows = shared_on && shI1 > shI0;
+        float *shred = (float *)lds;   // [kPW][2 * kShRows], codebook area (free until gate/up)
+        auto shared_partials = [&](int r0, int t, int nthr) {
             const uint16_t *wg0 = lay.shared, *wu0 = lay.shared + (size_t)I * H;
-            for (int r0 = shI0; r0 < shI1; r0 += kShRows) {
-                const int nr = min(kShRows, shI1 - r0);
-                float g[kShRows], u[kShRows];
+            float g[kShRows], u[kShRows];
 #pragma unroll
-                for (int q = 0; q < kShRows; q++) g[q] = u[q] = 0.f;
-                for (int c = threadIdx.x * 8; c < H; c += kPW * 64 * 8) {
-                    const float4 xa = *(const float4 *)(xs + c), xb = *(const float4 *)(xs + c + 4);
-                    uint4 gv[kShRows], uv[kShRows];
-#pragma unroll
-                    for (int q = 0; q < kShRows; q++) {
-                        const size_t o = (size_t)min(r0 + q, shI1 - 1) * H + c;
-                        gv[q] = *(const uint4 *)(wg0 + o);
-                        uv[q] = *(const uint4 *)(wu0 + o);
-                    }
-                    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-#pragma unroll
-                    for (int q = 0; q < kShRows; q++) {
-                        const uint32_t gq[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
-                        const uint32_t uq[4] = {uv[q].x, uv[q].y, uv[q].z, uv[q].w};
-#pragma unroll
-                        for (int i = 0; i < 4; i++) {
-                            g[q] = fmaf(__uint_as_float(gq[i] << 16), xv[2 * i], g[q]);
-                            g[q] = fmaf(__uint_as_float(gq[i] & 0xFFFF0000u), xv[2 * i + 1], g[q]);
-                            u[q] = fmaf(__uint_as_float(uq[i] << 16), xv[2 * i], u[q]);
-                            u[q] = fmaf(__uint_as_float(uq[i] & 0xFFFF0000u), xv[2 * i + 1], u[q]);
-                        }
-                    }
-                }
+            for (int q = 0; q < kShRows; q++) g[q] = u[q] = 0.f;
+            for (int c = t * 8; c < H; c += nthr * 8) {
+                const float4 xa = *(const float4 *)(xs + c), xb = *(const float4 *)(xs + c + 4);
+                uint4 gv[kShRows], uv[kShRows];
 #pragma unroll
                 for (int q = 0; q < kShRows; q++) {
-                    g[q] = wave_sum(g[q]);
-                    u[q] = wave_sum(u[q]);
+                    const size_t o = (size_t)min(r0 + q, shI1 - 1) * H + c;
+                    gv[q] = *(const uint4 *)(wg0 + o);
+                    uv[q] = *(const uint4 *)(wu0 + o);
                 }
-                if (lane == 0) {
+                const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-                    for (int q = 0; q < kShRows; q++) {
-                        shred[wave * 2 * kShRows + q] = g[q];
-                        shred[wave * 2 * kShRows + kShRows + q] = u[q];
+                for (int q = 0; q < kShRows; q++) {
+                    const uint32_t gq[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
+                    const uint32_t uq[4] = {uv[q].x, uv[q].y, uv[q].z, uv[q].w};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        g[q] = fmaf(__uint_as_float(gq[i] << 16), xv[2 * i], g[q]);
+                        g[q] = fmaf(__uint_as_float(gq[i] & 0xFFFF0000u), xv[2 * i + 1], g[q]);
+                        u[q] = fmaf(__uint_as_float(uq[i] << 16), xv[2 * i], u[q]);
+                        u[q] = fmaf(__uint_as_float(uq[i] & 0xFFFF0000u), xv[2 * i + 1], u[q]);
                     }
                 }
-                lds_sync();
-                // wave 1 finishes the rows (wave 0 goes on to poll the logits)
-                if (wave == 1 && lane < nr) {
-                    float gg = 0.f, uu = 0.f;
-                    for (int v = 0; v < kPW; v++) {
-                        gg += shred[v * 2 * kShRows + lane];
-                        uu += shred[v * 2 * kShRows + kShRows + lane];
-                    }
-                    st_x(a.hs + r0 + lane, gg / (1.f + __expf(-gg)) * uu);
+            }
+#pragma unroll
+            for (int q = 0; q < kShRows; q++) {
+                g[q] = wave_sum(g[q]);
+                u[q] = wave_sum(u[q]);
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int q = 0; q < kShRows; q++) {
+                    shred[wave * 2 * kShRows + q] = g[q];
+                    shred[wave * 2 * kShRows + kShRows + q] = u[q];
                 }
-                lds_sync();
             }
-            // wave 1 wrote every row: once its stores are done, count them
-            if (wave == 1) {
-                wait_vm_all();
-                if (lane == 0)
-                    __hip_atomic_fetch_add(h_ready + k * kLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        // wave 1 finishes a group from the waves' partials v0..kPW-1
+        auto shared_finish = [&](int r0, int v0) {
+            const int nr = min(kShRows, shI1 - r0);
+            if (wave == 1 && lane < nr) {
+                float gg = 0.f, uu = 0.f;
+                for (int v = v0; v < kPW; v++) {
+                    gg += shred[v * 2 * kShRows + lane];
+                    uu += shred[v * 2 * kShRows + kShRows + lane];
+                }
+                st_x(a.hs + r0 + lane, gg / (1.f + __expf(-gg)) * uu);
             }
-        }
+        };
 
         // ---- top-k: wave 0 polls the tagged logits into LDS as
         // order-preserving keys; then every thread ranks its experts by
@@ -759,9 +752,20 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 if (!poll_more(sync, spins)) { okw = false; break; }
             }
             if (lane == 0) *bcast = okw;
+        } else if (sh_rows) {
+            shared_partials(shI0, (int)threadIdx.x - 64, (kPW - 1) * 64);
         }
         lds_sync();
         if (!*bcast) return;
+        if (sh_rows) {
+            shared_finish(shI0, 1);
+            for (int r0 = shI0 + kShRows; r0 < shI1; r0 += kShRows) {
+                lds_sync();
+                shared_partials(r0, threadIdx.x, kPW * 64);
+                lds_sync();
+                shared_finish(r0, 0);
+            }
+        }
         {
             const int kk = __builtin_amdgcn_readfirstlane(lay.k);
             for (int e = threadIdx.x; e < E; e += kPW * 64) {
@@ -800,6 +804,12 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             sw[lane] = mine / sum;
             recs[lane] = recs_all[e];
             if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = e;
+        }
+        // wave 1 wrote every shared row: once its stores are done (long since,
+        // by now), count them
+        if (sh_rows && wave == 1) {
+            wait_vm_all();
+            if (lane == 0) __hip_atomic_fetch_add(h_ready + k * kLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         lds_sync();
         mark(kStampRouted);
