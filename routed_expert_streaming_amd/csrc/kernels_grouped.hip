@@ -262,26 +262,59 @@ constexpr int kBufWord3 = 0x00020000;         // buffer descriptor word 3 (32-bi
 constexpr int kASlot = 16 * kChunkCols * 2;   // bytes of one A ring slot
 constexpr int kARing = 3;
 
+// A lane's 4 groups are 12 bytes (dwords d0, d1, d2) of its row's 48-byte
+// strip, which the record splits into three 16-byte parts 1 KB apart.  They
+// come in one 8-byte and one 4-byte load: lane blocks 0 and 2 read (d0, d1)
+// and d2, blocks 1 and 3 (whose 12 bytes straddle a part boundary) read
+// (d1, d2) and d0.  Per wave and tile the two loads touch 10 cache lines
+// where three 4-byte loads touched 18.
+struct RvqQuadOff {
+    int part8, byte8, part4, byte4;   // the 8-byte and the 4-byte load: strip part and byte in it
+};
+__device__ __forceinline__ RvqQuadOff rvq_quad_off(int g4) {
+    switch (g4) {
+    case 0: return {0, 0, 0, 8};
+    case 1: return {1, 0, 0, 12};
+    case 2: return {1, 8, 2, 0};
+    default: return {2, 8, 2, 4};
+    }
+}
+
 template <int TW>
 struct RvqStage {
-    uint32_t c0[TW][3], c1[TW][3];   // codes of 4 groups per tile (gate or down; up)
+    // per tile (gate or down; up): the 8-byte load in [0], [1], the 4-byte one in [2]
+    uint32_t c0[TW][3], c1[TW][3];
 };
 
 // Codes of chunk j through buffer loads: rs0/rs1 describe the code sections
-// of the two matrices (reads past a section's end return zero), qoff[t][i]
-// is the lane's byte offset of dword i of its 4 groups of tile t in chunk 0,
-// and the chunk's offset goes in the scalar offset.  Streaming (nt) loads.
+// of the two matrices (reads past a section's end return zero), qoff[t] the
+// lane's byte offsets of its two loads of tile t in chunk 0, and the chunk's
+// offset goes in the scalar offset.  Streaming (nt) loads.
 template <bool GATEUP, int TW>
 __device__ __forceinline__ void rvq_load(RvqStage<TW> &st, __amdgpu_buffer_rsrc_t rs0, __amdgpu_buffer_rsrc_t rs1,
-                                         const uint32_t (&qoff)[TW][3], int j) {
+                                         const uint32_t (&qoff)[TW][2], int j) {
     const int soff = j * kTileBytes;
 #pragma unroll
-    for (int t = 0; t < TW; t++)
-#pragma unroll
-        for (int i = 0; i < 3; i++) {
-            st.c0[t][i] = __builtin_amdgcn_raw_buffer_load_b32(rs0, (int)qoff[t][i], soff, kBufNt);
-            if constexpr (GATEUP) st.c1[t][i] = __builtin_amdgcn_raw_buffer_load_b32(rs1, (int)qoff[t][i], soff, kBufNt);
+    for (int t = 0; t < TW; t++) {
+        const auto q0 = __builtin_amdgcn_raw_buffer_load_b64(rs0, (int)qoff[t][0], soff, kBufNt);
+        st.c0[t][0] = q0[0];
+        st.c0[t][1] = q0[1];
+        st.c0[t][2] = __builtin_amdgcn_raw_buffer_load_b32(rs0, (int)qoff[t][1], soff, kBufNt);
+        if constexpr (GATEUP) {
+            const auto q1 = __builtin_amdgcn_raw_buffer_load_b64(rs1, (int)qoff[t][0], soff, kBufNt);
+            st.c1[t][0] = q1[0];
+            st.c1[t][1] = q1[1];
+            st.c1[t][2] = __builtin_amdgcn_raw_buffer_load_b32(rs1, (int)qoff[t][1], soff, kBufNt);
         }
+    }
+}
+
+// (d0, d1, d2) from a tile's loads; odd: lane block 1 or 3
+__device__ __forceinline__ void rvq_dwords(const uint32_t (&c)[3], bool odd, uint32_t &d0, uint32_t &d1,
+                                           uint32_t &d2) {
+    d0 = odd ? c[2] : c[0];
+    d1 = odd ? c[0] : c[1];
+    d2 = odd ? c[1] : c[2];
 }
 
 // Gathered B fragments of one K-step: C[a] and C[b] per tile and matrix.
@@ -291,13 +324,17 @@ struct RvqGather {
 };
 
 template <bool GATEUP, int TW, int S>
-__device__ __forceinline__ void rvq_gather(const RvqStage<TW> &st, const char *cb0, const char *cb1,
+__device__ __forceinline__ void rvq_gather(const RvqStage<TW> &st, bool odd, const char *cb0, const char *cb1,
                                            RvqGather<GATEUP, TW> &g) {
 #pragma unroll
     for (int t = 0; t < TW; t++) {
-        group_rows(cb0, quad_code<S>(st.c0[t][0], st.c0[t][1], st.c0[t][2]), g.b[t][0][0], g.b[t][0][1]);
-        if constexpr (GATEUP)
-            group_rows(cb1, quad_code<S>(st.c1[t][0], st.c1[t][1], st.c1[t][2]), g.b[t][1][0], g.b[t][1][1]);
+        uint32_t d0, d1, d2;
+        rvq_dwords(st.c0[t], odd, d0, d1, d2);
+        group_rows(cb0, quad_code<S>(d0, d1, d2), g.b[t][0][0], g.b[t][0][1]);
+        if constexpr (GATEUP) {
+            rvq_dwords(st.c1[t], odd, d0, d1, d2);
+            group_rows(cb1, quad_code<S>(d0, d1, d2), g.b[t][1][0], g.b[t][1][1]);
+        }
     }
 }
 
@@ -349,7 +386,7 @@ __device__ __forceinline__ void a_store(const ARing &r, int slot, const u32x4 &v
 template <bool GATEUP, int TW, bool NEXT, int R>
 __device__ __forceinline__ void rvq_chunk(const RvqStage<TW> &cur, const RvqStage<TW> &nxt, RvqStage<TW> &fill,
                                           __amdgpu_buffer_rsrc_t rs0, __amdgpu_buffer_rsrc_t rs1,
-                                          const uint32_t (&qoff)[TW][3],
+                                          const uint32_t (&qoff)[TW][2], bool odd,
                                           int j, int cpr, const ARing &ar, u32x4 &areg,
                                           const char *cb0, const char *cb1, RvqGather<GATEUP, TW> &g,
                                           f32x4 (&acc0)[TW], f32x4 (&acc1)[TW]) {
@@ -364,22 +401,22 @@ __device__ __forceinline__ void rvq_chunk(const RvqStage<TW> &cur, const RvqStag
     rvq_load<GATEUP, TW>(fill, rs0, rs1, qoff, min(j + 2, cpr - 1));
     __builtin_amdgcn_sched_barrier(0);
     RvqGather<GATEUP, TW> g1, g2;
-    rvq_gather<GATEUP, TW, 1>(cur, cb0, cb1, g1);
+    rvq_gather<GATEUP, TW, 1>(cur, odd, cb0, cb1, g1);
     __builtin_amdgcn_sched_barrier(0);
     // the A copy of chunk j+1 (issued before the K-step 1 gathers) is done
     lds_wait_barrier<kG>();
     __builtin_amdgcn_sched_barrier(0);
     rvq_mfma<GATEUP, TW>(a[0], g, acc0, acc1);
     __builtin_amdgcn_sched_barrier(0);
-    rvq_gather<GATEUP, TW, 2>(cur, cb0, cb1, g2);
+    rvq_gather<GATEUP, TW, 2>(cur, odd, cb0, cb1, g2);
     __builtin_amdgcn_sched_barrier(0);
     rvq_mfma<GATEUP, TW>(a[1], g1, acc0, acc1);
     __builtin_amdgcn_sched_barrier(0);
-    rvq_gather<GATEUP, TW, 3>(cur, cb0, cb1, g1);
+    rvq_gather<GATEUP, TW, 3>(cur, odd, cb0, cb1, g1);
     __builtin_amdgcn_sched_barrier(0);
     rvq_mfma<GATEUP, TW>(a[2], g2, acc0, acc1);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) rvq_gather<GATEUP, TW, 0>(nxt, cb0, cb1, g);
+    if constexpr (NEXT) rvq_gather<GATEUP, TW, 0>(nxt, odd, cb0, cb1, g);
     __builtin_amdgcn_sched_barrier(0);
     rvq_mfma<GATEUP, TW>(a[3], g1, acc0, acc1);
     __builtin_amdgcn_sched_barrier(0);
@@ -416,6 +453,8 @@ __global__ __launch_bounds__(NW * 64) void k_grouped_rvq(GroupedArgs g) {
     codebook_to_bf16(cb0);
     if constexpr (GATEUP) codebook_to_bf16(cb1);
     const int col = lane & 15, g4 = lane >> 4;
+    const RvqQuadOff qo = rvq_quad_off(g4);
+    const bool odd = (g4 & 1) != 0;
     const int rows_per_split = g.N / g.splits;          // multiple of 16
     const int r_begin = split * rows_per_split;
     const int tiles = rows_per_split / 16;
@@ -445,16 +484,13 @@ __global__ __launch_bounds__(NW * 64) void k_grouped_rvq(GroupedArgs g) {
         const int tg = min(tg_raw, tgroups - 1);
         const int ntw = min(TW, tiles - tg * TW);             // tiles in this unit (wave-uniform)
         int n[TW];
-        uint32_t qoff[TW][3];
+        uint32_t qoff[TW][2];
 #pragma unroll
         for (int t = 0; t < TW; t++) {
             n[t] = r_begin + (tg * TW + min(t, ntw - 1)) * 16 + col;
-#pragma unroll
-            for (int i = 0; i < 3; i++) {
-                const int dw = 3 * g4 + i;   // strip dword: 16-byte part dw/4 of row n
-                qoff[t][i] = (uint32_t)((n[t] >> 6) * cpr) * kTileBytes + (dw >> 2) * 1024 + (n[t] & 63) * 16 +
-                             (dw & 3) * 4;
-            }
+            const uint32_t row0 = (uint32_t)((n[t] >> 6) * cpr) * kTileBytes + (n[t] & 63) * 16;
+            qoff[t][0] = row0 + qo.part8 * 1024 + qo.byte8;
+            qoff[t][1] = row0 + qo.part4 * 1024 + qo.byte4;
         }
         // the copying lanes' A rows: tokens past the pass's last real one
         // copy the last real row (their products are never written)
@@ -481,25 +517,25 @@ __global__ __launch_bounds__(NW * 64) void k_grouped_rvq(GroupedArgs g) {
         rvq_load<GATEUP, TW>(st[0], rs0, rs1, qoff, 0);
         rvq_load<GATEUP, TW>(st[1], rs0, rs1, qoff, min(1, cpr - 1));
         RvqGather<GATEUP, TW> g0;
-        rvq_gather<GATEUP, TW, 0>(st[0], cb0, cb1, g0);
+        rvq_gather<GATEUP, TW, 0>(st[0], odd, cb0, cb1, g0);
         lds_wait_barrier<0>();
         int j = 0;
         for (; j + 3 <= cpr; j += 3) {
-            rvq_chunk<GATEUP, TW, true, 0>(st[0], st[1], st[2], rs0, rs1, qoff, j, cpr, ar, areg, cb0, cb1, g0,
+            rvq_chunk<GATEUP, TW, true, 0>(st[0], st[1], st[2], rs0, rs1, qoff, odd, j, cpr, ar, areg, cb0, cb1, g0,
                                            acc0, acc1);
-            rvq_chunk<GATEUP, TW, true, 1>(st[1], st[2], st[0], rs0, rs1, qoff, j + 1, cpr, ar, areg, cb0, cb1,
+            rvq_chunk<GATEUP, TW, true, 1>(st[1], st[2], st[0], rs0, rs1, qoff, odd, j + 1, cpr, ar, areg, cb0, cb1,
                                            g0, acc0, acc1);
-            rvq_chunk<GATEUP, TW, true, 2>(st[2], st[0], st[1], rs0, rs1, qoff, j + 2, cpr, ar, areg, cb0, cb1,
+            rvq_chunk<GATEUP, TW, true, 2>(st[2], st[0], st[1], rs0, rs1, qoff, odd, j + 2, cpr, ar, areg, cb0, cb1,
                                            g0, acc0, acc1);
         }
         // the last cpr - j (< 3) chunks are already in st[0], st[1]
         if (j + 2 == cpr) {
-            rvq_chunk<GATEUP, TW, true, 0>(st[0], st[1], st[2], rs0, rs1, qoff, j, cpr, ar, areg, cb0, cb1, g0,
+            rvq_chunk<GATEUP, TW, true, 0>(st[0], st[1], st[2], rs0, rs1, qoff, odd, j, cpr, ar, areg, cb0, cb1, g0,
                                            acc0, acc1);
-            rvq_chunk<GATEUP, TW, false, 1>(st[1], st[2], st[0], rs0, rs1, qoff, j + 1, cpr, ar, areg, cb0, cb1,
+            rvq_chunk<GATEUP, TW, false, 1>(st[1], st[2], st[0], rs0, rs1, qoff, odd, j + 1, cpr, ar, areg, cb0, cb1,
                                             g0, acc0, acc1);
         } else if (j + 1 == cpr) {
-            rvq_chunk<GATEUP, TW, false, 0>(st[0], st[1], st[2], rs0, rs1, qoff, j, cpr, ar, areg, cb0, cb1, g0,
+            rvq_chunk<GATEUP, TW, false, 0>(st[0], st[1], st[2], rs0, rs1, qoff, odd, j, cpr, ar, areg, cb0, cb1, g0,
                                             acc0, acc1);
         }
         if (!active) continue;
