@@ -69,7 +69,53 @@ def git_commit() -> str:
         return "unknown"
 
 
-def cpu_baseline(cfg, x_np, sample_tokens: int):
+def read_ceiling(nbytes: int = 4 << 30, passes: int = 5):
+    """Plain streaming read of an nbytes device buffer (moe_hbm_read), timed
+    with HIP events on the launch stream: the rate the expert bytes are also
+    quoted against.  Median over passes."""
+    import numpy as np
+    import torch
+
+    import routed_expert_streaming_amd as moe
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(moe.HBM_READ_BLOCKS, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    moe.hbm_read(buf, sink)
+    ms = []
+    for _ in range(passes):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        moe.hbm_read(buf, sink)
+        b.record(stream)
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    del buf
+    gbs = nbytes / (float(np.median(ms)) / 1e3) / 1e9
+    return {"gbs": round(gbs, 1), "bytes": nbytes, "passes": passes, "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel": "k_hbm_read (16-byte nontemporal loads, XOR per load)"}
+
+
+def block_rates(step_ms, units_per_step: float, blocks: int = 5):
+    """The timed steps in `blocks` consecutive blocks: units/s of each block
+    from its GPU event times; median, min and max."""
+    import numpy as np
+    parts = [p for p in np.array_split(np.asarray(step_ms, dtype=np.float64), blocks) if len(p)]
+    rates = [units_per_step * len(p) / (p.sum() / 1e3) for p in parts]
+    return {"blocks": len(rates), "median": round(float(np.median(rates)), 3), "min": round(min(rates), 3),
+            "max": round(max(rates), 3)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, x_np, sample_tokens: int, one_thread_tokens: int = 1):
     """The fp64 oracle on `sample_tokens` tokens x all layers of the workload."""
     import numpy as np
 
@@ -87,16 +133,28 @@ def cpu_baseline(cfg, x_np, sample_tokens: int):
             ridx, _, _ = oracle.route(wl.router(L), wl.bias(L), x64, cfg.k, cfg.score)
             jobs.append((L, x64, set(int(e) for e in ridx.reshape(-1))))
     empty = np.zeros(1, np.uint8)
-    t_total = 0.0
-    for L, x64, needed in jobs:
-        recs = [wl.record(L, e) if e in needed else empty for e in range(cfg.E)]
-        sh = wl.shared(L)
-        t0 = time.perf_counter()
-        oracle.layer(wl.router(L), wl.bias(L), cfg.k, cfg.score, recs, sh, cfg.H, cfg.I, x64)
-        t_total += time.perf_counter() - t0
+
+    def run(jobs_):
+        t = 0.0
+        for L, x64, needed in jobs_:
+            recs = [wl.record(L, e) if e in needed else empty for e in range(cfg.E)]
+            sh = wl.shared(L)
+            t0 = time.perf_counter()
+            oracle.layer(wl.router(L), wl.bias(L), cfg.k, cfg.score, recs, sh, cfg.H, cfg.I, x64)
+            t += time.perf_counter() - t0
+        return t
+
+    t_total = run(jobs)
+    n1 = min(one_thread_tokens, sample_tokens)
+    oracle.set_threads(1)
+    t_one = run(jobs[:n1 * cfg.layers])
+    oracle.set_threads(threads)
     return {"value": round(sample_tokens / t_total, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": f"{sample_tokens} tokens x {cfg.layers} layers of the {cfg.name} decode (fp64, "
-                      f"{threads} threads); {t_total:.1f} s"}
+                      f"{threads} threads); {t_total:.1f} s",
+            "one_thread": {"value": round(n1 / t_one, 4), "unit": "tok/s",
+                           "sample": f"{n1} token(s) x {cfg.layers} layers, 1 thread; {t_one:.1f} s"},
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def main() -> int:
@@ -214,6 +272,7 @@ def main() -> int:
         "expert_gbs": round(bytes_tok * tok_s / 1e9, 1),
         "expert_hbm_frac": round(bytes_tok * tok_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
+        "tok_s_blocks": block_rates(step_ms, 1.0),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if cfg.name == "mixtral" else None,
@@ -223,6 +282,9 @@ def main() -> int:
         "device": torch.cuda.get_device_name(0),
         "commit": git_commit(),
     }
+    rc = read_ceiling()
+    rc["expert_frac_of_ceiling"] = round(achieved / rc["gbs"], 4)
+    record["read_ceiling"] = rc
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
         record["cpu_baseline"] = cpu_baseline(cfg, x.cpu().numpy(), args.cpu_sample_tokens)
@@ -274,7 +336,11 @@ def bench_batched(args, cfg) -> int:
                         "kernel": "batched layer call", "algorithmic_bytes_per_launch": nbytes},
            "mfma": {"flops_per_call": flops, "achieved_tflops": round(flops / mean_s / 1e12, 2),
                     "peak_tflops": 2500.0, "utilisation": round(flops / mean_s / 1e12 / 2500.0, 4)},
+           "tokens_s_blocks": block_rates(step_ms, float(cfg.tokens)),
            "commit": git_commit()}
+    rc = read_ceiling()
+    rc["expert_frac_of_ceiling"] = round(nbytes / mean_s / 1e9 / rc["gbs"], 4)
+    rec["read_ceiling"] = rc
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -327,6 +393,26 @@ def _streamed_setup(cfg):
     return moe, dw, x, hp, [hp.table(L) for L in range(cfg.layers)]
 
 
+def h2d_peak(nbytes: int = 1 << 30, passes: int = 3):
+    """Pinned host -> HBM copy of nbytes on a side stream (the link the cache
+    misses cross), timed with HIP events; best of passes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    best = 0.0
+    for _ in range(passes + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            a.record(s)
+            dst.copy_(src, non_blocking=True)
+            b.record(s)
+        b.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) / 1e3) / 1e9)
+    del src, dst
+    return round(best, 2)
+
+
 def _cold_tier(cfg, hp):
     return {"records": cfg.layers * cfg.E, "pinned_records": hp.pinned_records,
             "note": "the rest in pageable host memory (this host page-locks at most ~59 GiB)"}
@@ -347,6 +433,7 @@ def bench_streamed(args, cfg) -> int:
     half = (cfg.tokens // 2) * per_tok
     tok_s = r["tok_s"]
     hbm_bytes = synth.expert_bytes_per_token(cfg)
+    peak = h2d_peak()
     rec = {"metric": "streamed MoE decode tok/s on 1 MI355X (HBM LRU slot cache, misses over PCIe)",
            "value": round(tok_s, 3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(r["elapsed"] * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
@@ -360,6 +447,8 @@ def bench_streamed(args, cfg) -> int:
            "h2d_gbs": round(r["misses_timed"] * hp.stride / r["elapsed"] / 1e9, 2),
            "hbm_expert_gbs": round(hbm_bytes * tok_s / 1e9, 1),
            "cold_tier": _cold_tier(cfg, hp),
+           "h2d_pinned_peak_gbs": peak,
+           "h2d_frac_of_pinned_peak": round(r["misses_timed"] * hp.stride / r["elapsed"] / 1e9 / peak, 4),
            "commit": git_commit()}
     print(json.dumps(rec), flush=True)
     return 0

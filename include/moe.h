@@ -88,6 +88,7 @@ extern "C" {
 #define MOE_MAX_E 1024
 #define MOE_CODEBOOK_ROWS 4096
 #define MOE_NO_KEY 0xFFFFFFFFu
+#define MOE_HBM_READ_BLOCKS 2048   /* partial words moe_hbm_read writes        */
 
 /* Section offsets and sizes (bytes) of an expert record; index order:
  * 0 gate codes, 1 up codes, 2 down codes, 3 gate scales, 4 up scales,
@@ -369,6 +370,17 @@ int moe_layer_forward_streamed_tiered(const moe_layer *L, moe_cache *c, uint32_t
                                       moe_host_tier *tier, int64_t record0, const float *x, int32_t T,
                                       float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
                                       void *compute_stream, void *copy_stream);
+
+/* ---- measurement aid ---------------------------------------------------- */
+/* The plain-read reference for expert-weight bandwidth: one pass of 16-byte
+ * nontemporal loads over buf, with no arithmetic besides an XOR per load.
+ * The expert bytes a decode streams are quoted as a fraction of this rate as
+ * well as of the HBM peak.  sink [dev] receives MOE_HBM_READ_BLOCKS words
+ * whose XOR equals the XOR of buf's 32-bit words (so the reads are checked
+ * and never dead code).  Asynchronous on hip_stream.  MOE_E_INVAL if sink is
+ * NULL, buf is NULL with bytes > 0, buf is not 16-byte aligned or bytes is
+ * not a multiple of 16; bytes = 0 writes zero partials. */
+int moe_hbm_read(const void *buf, uint64_t bytes, uint32_t *sink, void *hip_stream);
 
 #ifdef __cplusplus
 }

@@ -4,7 +4,7 @@ Python face of libmoe (include/moe.h): torch supplies device memory and
 streams; every computation runs in the library's HIP kernels.  Names follow
 the C ABI: route_topk, expert_ffn_rvq, layer_forward, decode_forward,
 layer_forward_grouped, ExpertCache (expert_cache_*), layer_forward_streamed,
-lru_stack_distances, HostTier (moe_host_tier_*).
+lru_stack_distances, HostTier (moe_host_tier_*), hbm_read.
 """
 from __future__ import annotations
 
@@ -46,6 +46,22 @@ def _need(cond: bool, msg: str):
 
 def abi_version() -> int:
     return lib().moe_abi_version()
+
+
+HBM_READ_BLOCKS = 2048   # MOE_HBM_READ_BLOCKS
+
+
+def hbm_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One plain streaming read of buf's bytes (moe_hbm_read, the reference
+    rate for expert-weight bandwidth).  Returns the [HBM_READ_BLOCKS] int32
+    partials, whose XOR equals the XOR of buf's 32-bit words."""
+    _need(buf.is_contiguous(), "buf must be contiguous")
+    if sink is None:
+        sink = torch.empty(HBM_READ_BLOCKS, dtype=torch.int32, device=buf.device)
+    _need(sink.numel() >= HBM_READ_BLOCKS and sink.dtype == torch.int32, "sink must hold HBM_READ_BLOCKS int32")
+    nbytes = buf.numel() * buf.element_size()
+    check(lib().moe_hbm_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "moe_hbm_read")
+    return sink
 
 
 def rvq_record_layout(H: int, I: int) -> MoeRecordLayout:

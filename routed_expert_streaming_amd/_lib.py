@@ -43,6 +43,7 @@ class MoeTraceRec(ctypes.Structure):
 SIGNATURES = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_abi_version": (ctypes.c_int, []),
+    "moe_hbm_read": (ctypes.c_int, [P, ctypes.c_uint64, P, P]),
     "moe_rvq_record_layout": (ctypes.c_int, [I32, I32, ctypes.POINTER(MoeRecordLayout)]),
     "moe_route_workspace_bytes": (SZ, [I32, I32]),
     "moe_route_topk": (ctypes.c_int, [ctypes.POINTER(MoeRouter), P, I32, I32, I32, P, P, P, SZ, P]),

@@ -182,6 +182,15 @@ const char *moe_last_error(void) { return g_err.c_str(); }
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+int moe_hbm_read(const void *buf, uint64_t bytes, uint32_t *sink, void *hip_stream) {
+    if ((!buf && bytes) || !sink) return fail(MOE_E_INVAL, "buf (unless bytes = 0) and sink must be non-NULL");
+    if ((uintptr_t)buf % 16 || bytes % 16)
+        return fail(MOE_E_INVAL, "buf must be 16-byte aligned and bytes a multiple of 16 (bytes=%llu)",
+                    (unsigned long long)bytes);
+    HIPCHK(launch_hbm_read(buf, (size_t)bytes, sink, (hipStream_t)hip_stream), "hbm read launch");
+    return MOE_OK;
+}
+
 int moe_rvq_record_layout(int32_t H, int32_t I, moe_record_layout *out) {
     if (!out) return fail(MOE_E_INVAL, "out is NULL");
     if (!dims_ok(H, I)) return fail(MOE_E_INVAL, "H=%d, I=%d must be positive multiples of 128", H, I);

@@ -71,6 +71,7 @@ hipError_t launch_combine(const float *ypart, int k, int KS, int H, const float 
                           float *out, int64_t out_stride, int T, int accumulate, hipStream_t s);
 hipError_t launch_dense_gateup(const uint16_t *shared, int H, int I, const void *x, int x_dtype,
                                int64_t x_stride, int T, float *hs, hipStream_t s);
+hipError_t launch_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_dense_down(const uint16_t *shared, int H, int I, const float *hs, int T,
                              float *ysh, hipStream_t s);
 

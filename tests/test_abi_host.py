@@ -132,3 +132,13 @@ def test_host_tier_rejects_bad_arguments(L, tmp_path):
     assert L.moe_host_tier_create(str(f).encode(), 4096, 2, 0, aligned, 1, ctypes.byref(h)) == MOE_E_INVAL
     assert L.moe_host_tier_create(str(f).encode(), 4096, 2, 1, aligned, 0, ctypes.byref(h)) == MOE_E_INVAL
     assert not h.value
+
+
+def test_hbm_read_validation(L):
+    # rejected before any device call
+    from routed_expert_streaming_amd import _lib
+    sink = ctypes.c_void_p(4096)
+    assert L.moe_hbm_read(None, 16, sink, None) == _lib.MOE_E_INVAL
+    assert L.moe_hbm_read(ctypes.c_void_p(4096), 16, None, None) == _lib.MOE_E_INVAL
+    assert L.moe_hbm_read(ctypes.c_void_p(4104), 16, sink, None) == _lib.MOE_E_INVAL   # not 16-byte aligned
+    assert L.moe_hbm_read(ctypes.c_void_p(4096), 24, sink, None) == _lib.MOE_E_INVAL   # not a multiple of 16
