@@ -618,12 +618,39 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 
         const unsigned tag = (unsigned)s + 1;
 
-        // ---- x as fp16 pairs into LDS (every workgroup, for gate/up)
+        // ---- x as fp16 pairs into LDS (every workgroup, for gate/up), in
+        // one pass with this workgroup's first logit row (e = w, if w < E):
+        // thread t takes the float4 pieces c = 4t + 2048 m of x and of the
+        // row, up to four pieces' loads in flight together, and multiplies
+        // them in increasing m, the order of the row loop below (pieces past
+        // H add fma(0, 0), as there)
+        float acc_w = 0.f;
         {
             uint32_t *xl = (uint32_t *)(lds + LL.x_gu);
-            for (int i = threadIdx.x; i < H / 2; i += kPW * 64) {
-                const float2 xv = *(const float2 *)(xs + 2 * i);
-                xl[i] = pack_f16x2(xv.x, xv.y);
+            const bool row_w = w < nE;
+            const float *wr = lay.W + (size_t)(row_w ? w : 0) * H;
+            const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            constexpr int kPiece = kPW * 64 * 4;
+            for (int c = threadIdx.x * 4; c < H; c += 4 * kPiece) {
+                float4 xv[4], wv[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int cu = c + u * kPiece;
+                    xv[u] = cu < H ? *(const float4 *)(xs + cu) : zero4;
+                    wv[u] = cu < H && row_w ? *(const float4 *)(wr + cu) : zero4;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int cu = c + u * kPiece;
+                    if (cu < H) {
+                        xl[cu / 2] = pack_f16x2(xv[u].x, xv[u].y);
+                        xl[cu / 2 + 1] = pack_f16x2(xv[u].z, xv[u].w);
+                    }
+                    acc_w = fmaf(wv[u].x, xv[u].x, acc_w);
+                    acc_w = fmaf(wv[u].y, xv[u].y, acc_w);
+                    acc_w = fmaf(wv[u].z, xv[u].z, acc_w);
+                    acc_w = fmaf(wv[u].w, xv[u].w, acc_w);
+                }
             }
         }
 
@@ -631,8 +658,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         if (w < nE) {
             for (int e = w; e < E; e += G) {
                 const float *wr = lay.W + (size_t)e * H;
-                float acc = 0.f;
-                for (int c0 = threadIdx.x * 4; c0 < H; c0 += 2 * kPW * 64 * 4) {
+                float acc = e == w ? acc_w : 0.f;
+                for (int c0 = threadIdx.x * 4; c0 < H && e != w; c0 += 2 * kPW * 64 * 4) {
                     // two chunks' loads in flight together
                     const int c1 = c0 + kPW * 64 * 4;
                     const float4 w0 = *(const float4 *)(wr + c0), x0 = *(const float4 *)(xs + c0);
