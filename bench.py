@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # valid for the kernel source they were taken on: reported as null once that
 # source has changed.
 DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
-                  "sha256_prefix": "31a10d78e9f6d297", "bytes_per_launch": 4698946107}
+                  "sha256_prefix": "630163846a9ee153", "bytes_per_launch": 4696877553}
 
 
 def measured_traffic():
