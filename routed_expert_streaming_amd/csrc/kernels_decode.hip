@@ -477,6 +477,194 @@ __device__ __forceinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_s
     return 1;
 }
 
+// ---- Gate/up by table lookup (for experts with many rows per codebook).
+// Within a 128-column chunk, group q (8 columns) of every row contributes
+// C[a].x_q + C[b].x_q.  A table T[q][c] = C[c].x_q over all 4096 codebook
+// rows c and the chunk's 16 groups (128 KiB of fp16) turns each group into
+// two 2-byte LDS lookups in place of two 16-byte gathers; random 2-byte
+// reads sustain about twice the lanes per clock of random 16-byte reads.
+// Each table serves every row of the matrix that this workgroup streams for
+// that chunk.
+//
+// The table is a small dense contraction, built on matrix cores:
+// v_mfma_f32_16x16x16_f16, where lane l holds A[l%16][4(l/16)..+3],
+// B[4(l/16)..+3][l%16] and D[4(l/16)..+3][l%16].  K half h of A holds
+// codebook rows c0 + 16h + m; column n of B holds x of group n % 8 (of one
+// half chunk) in K half n / 8 and zero in the other, so
+// D[m][n] = C[c0 + 16(n/8) + m] . x_{n%8}: one instruction yields 32 rows x 8
+// groups.  x enters as an fp16 pair hi + lo (two MFMAs into one fp32
+// accumulator), so only the table entries themselves are rounded (to fp16).
+// A wave keeps the A fragments of its 512 codebook rows in registers for the
+// whole segment (the codebook never goes to LDS).
+//
+// LDS in this phase: the table, row q (group q) at kLutRowB q (the 64-byte
+// pad puts consecutive rows 16 banks apart, so a table store is 2-way at
+// worst), then the token's x (fp32, stored there by the routing pass).  The lookups address LDS
+// from byte 0 (the kernel has no static LDS, so its dynamic LDS starts there;
+// the host checks), with the row offset as the instruction's immediate
+// where it fits (rows 0..7).
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const _Float16 lds_f16;
+constexpr int kLutRowB = 2 * kCbRows + 64;                     // bytes per table row
+constexpr int kLutX = 16 * kLutRowB;                           // x offset (132,096)
+constexpr int kLutMaxH = (kDecRecs - kLutX) / 4;               // x must end below the routing tail
+constexpr int kLutRing = 4;                                    // code buffers per wave (3 units ahead)
+constexpr int kLutCbTiles = kCbRows / 32 / kPW;                // 32-row MFMA tiles each wave builds
+typedef __attribute__((address_space(1))) const f16x4 gf16x4;  // global memory
+
+// Group G's two lookups (row G of the table) as one fp16 pair.
+template <int G>
+__device__ __forceinline__ f16x2 lut_pair(const uint32_t (&d)[12]) {
+    constexpr int bit = 24 * G, i = bit / 32, s = bit % 32;
+    uint32_t v;
+    if constexpr (s <= 8) v = d[i] >> s;
+    else v = __builtin_amdgcn_alignbit(d[i + 1], d[i], s);
+    constexpr uint32_t off = G * kLutRowB;
+    const uint32_t aa = ((v << 1) & 0x1FFEu) + off;
+    const uint32_t ba = ((v >> 11) & 0x1FFEu) + off;
+    f16x2 p;
+    p.x = *(lds_f16 *)(uintptr_t)aa;
+    p.y = *(lds_f16 *)(uintptr_t)ba;
+    return p;
+}
+template <int HF>
+__device__ __forceinline__ void lut_read8(const uint32_t (&d)[12], f16x2 (&p)[8]) {
+    p[0] = lut_pair<8 * HF + 0>(d);
+    p[1] = lut_pair<8 * HF + 1>(d);
+    p[2] = lut_pair<8 * HF + 2>(d);
+    p[3] = lut_pair<8 * HF + 3>(d);
+    p[4] = lut_pair<8 * HF + 4>(d);
+    p[5] = lut_pair<8 * HF + 5>(d);
+    p[6] = lut_pair<8 * HF + 6>(d);
+    p[7] = lut_pair<8 * HF + 7>(d);
+}
+__device__ __forceinline__ float lut_sum8(f16x2 (&p)[8]) {
+    // the values are complete here (waits for these lookups only)
+    asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
+                 "+v"(p[7]));
+    const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; g += 2) {
+        a0 = __builtin_amdgcn_fdot2(p[g], one, a0, false);       // T[a] + T[b], exact in fp32
+        a1 = __builtin_amdgcn_fdot2(p[g + 1], one, a1, false);
+    }
+    return a0 + a1;
+}
+// One 48-byte strip (16 groups): the second half's lookups are issued
+// before the first half's sums.
+__device__ __forceinline__ float lut_strip(const uint32_t (&d)[12]) {
+    f16x2 p0[8], p1[8];
+    lut_read8<0>(d, p0);
+    lut_read8<1>(d, p1);
+    const float s0 = lut_sum8(p0);
+    return s0 + lut_sum8(p1);
+}
+
+// The lane id, computed afresh where it is used: left to the compiler, the
+// lane-dependent addresses of the table builds are kept across the whole
+// phase and spilled, and reloading a spill waits for every load in flight.
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// The table of chunk c (of the token's x in LDS) from the A fragments.
+__device__ __forceinline__ void lut_build(const f16x4 (&A)[kLutCbTiles], int c, int wave) {
+    const int lane = fresh_lane();
+    const int n = lane & 15, g = lane >> 4;
+    const bool valid = (g >> 1) == (n >> 3);
+    const f16x4 z4 = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+    f16x4 bh[2], bl[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+        const float4 xv =
+            *(const float4 *)(dec_lds + kLutX + 4 * (kChunkCols * c + 64 * hf + 8 * (n & 7) + 4 * (g & 1)));
+        bh[hf].x = (_Float16)xv.x; bh[hf].y = (_Float16)xv.y; bh[hf].z = (_Float16)xv.z; bh[hf].w = (_Float16)xv.w;
+        bl[hf].x = (_Float16)(xv.x - (float)bh[hf].x);
+        bl[hf].y = (_Float16)(xv.y - (float)bh[hf].y);
+        bl[hf].z = (_Float16)(xv.z - (float)bh[hf].z);
+        bl[hf].w = (_Float16)(xv.w - (float)bh[hf].w);
+        if (!valid) { bh[hf] = z4; bl[hf] = z4; }
+    }
+    // this lane's entries: rows 8 hf + n % 8, codebook rows c0 + 16 (n / 8) + 4 g + 0..3;
+    // two tiles (four independent accumulators) per step
+    char *dst = dec_lds + (n & 7) * kLutRowB + 2 * (wave * kLutCbTiles * 32 + 16 * (n >> 3) + 4 * g);
+#pragma unroll
+    for (int t = 0; t < kLutCbTiles; t += 2) {
+        f32x4 d[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+            for (int hf = 0; hf < 2; hf++) {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                d[u][hf] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[t + u], bh[hf], z, 0, 0, 0);
+            }
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+            for (int hf = 0; hf < 2; hf++)
+                d[u][hf] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[t + u], bl[hf], d[u][hf], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+            for (int hf = 0; hf < 2; hf++) {
+                f16x4 o;
+                o.x = (_Float16)d[u][hf].x; o.y = (_Float16)d[u][hf].y;
+                o.z = (_Float16)d[u][hf].z; o.w = (_Float16)d[u][hf].w;
+                *(f16x4 *)(dst + hf * 8 * kLutRowB + 64 * (t + u)) = o;
+            }
+    }
+}
+
+// One segment of the table-lookup gate/up space: matrix m (codes at codes,
+// codebook at cb) of one expert, chunk c, row tiles [ta, ta + nt).  One
+// table build, then wave v streams tiles ta + v, ta + v + kPW, ... through a
+// register ring (no barriers) and stores each tile's sum over the chunk as a
+// tagged partial at part + 128 * cprH * tile (slot c of the tile; the caller
+// adds the rank's base, the slot and the matrix's half).
+__device__ __forceinline__ void stream_gateup_lut(const u32x4 *codes, const u32x4 *cb, int cprH, int c, int ta,
+                                                  int nt, uint64_t *part, unsigned tag, int wave, int lane) {
+    gu32x4 *gb = (gu32x4 *)codes;
+    const int first = ta + wave;
+    const int n = __builtin_amdgcn_readfirstlane(wave < nt ? (nt - wave + kPW - 1) / kPW : 0);
+    // the A fragments first: the build waits for them alone, tile by tile,
+    // while the code ring's loads stay in flight
+    f16x4 A[kLutCbTiles];
+    {
+        const int nn = lane & 15, g = lane >> 4;
+        gf16x4 *src = (gf16x4 *)((const char *)cb + (size_t)(wave * kLutCbTiles * 32 + 16 * (g >> 1) + nn) * 16 +
+                                 8 * (g & 1));
+#pragma unroll
+        for (int t = 0; t < kLutCbTiles; t++) A[t] = src[t * 64];
+    }
+    // a wave without tiles loads the segment's first tile (never consumed)
+    auto unit_addr = [&](int i) { return (n ? first + kPW * min(i, n - 1) : ta) * cprH + c; };
+    uint32_t buf[kLutRing][12];
+#pragma unroll
+    for (int r = 0; r < kLutRing - 1; r++) load_codes(gb, unit_addr(r), lane, buf[r]);
+    lds_sync();                    // the previous table's readers are done
+    lut_build(A, c, wave);
+    lds_sync();
+    auto process = [&](int i, const uint32_t (&d)[12]) {
+        st_tagged(part + (size_t)(first + kPW * i) * 128 * cprH + lane, lut_strip(d), tag);
+    };
+    int i = 0;
+    for (; i + kLutRing <= n; i += kLutRing) {
+#pragma unroll
+        for (int r = 0; r < kLutRing; r++) {
+            load_codes(gb, unit_addr(i + r + kLutRing - 1), lane, buf[(r + kLutRing - 1) % kLutRing]);
+            process(i + r, buf[r]);
+        }
+    }
+    // the last n - i (< kLutRing) units are already in buffers 0, 1, ...
+#pragma unroll
+    for (int r = 0; r < kLutRing - 1; r++)
+        if (i + r < n) process(i + r, buf[r]);
+}
+
 // Workgroup whose down range holds the last unit of output tile td in the
 // last rank: it combines the tile.
 __device__ __forceinline__ int combiner_of(int td, int k, int tilesH, int cprI, long nD, int G) {
@@ -564,6 +752,8 @@ struct DecArgs {
     uint64_t *part_d;        // [k*tilesH][slots_d][64] tagged
     int slots_gu, slots_d;
     int slots_red_gu, slots_red_d;   // tiles one workgroup's range can touch (LDS sum slots)
+    int lut;                 // gate/up by table lookup: 1, else 0 (part_gu then has
+                             // H / 128 slots per tile, one per chunk)
     unsigned long long *stamps;   // optional phase timestamps [steps][G][kDecStamps], or null
     int stamp_steps;
 };
@@ -642,7 +832,9 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     const int cu = c + u * kPiece;
-                    if (cu < H) {
+                    if (cu < H && a.lut) {
+                        *(float4 *)(lds + kLutX + 4 * cu) = xv[u];   // fp32, for the table builds
+                    } else if (cu < H) {
                         xl[cu / 2] = pack_f16x2(xv[u].x, xv[u].y);
                         xl[cu / 2 + 1] = pack_f16x2(xv[u].z, xv[u].w);
                     }
@@ -841,9 +1033,105 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         lds_sync();
         mark(kStampRouted);
 
+        if (a.lut) {
+            // ---- gate/up by table lookup over this workgroup's range of the
+            // (rank, matrix, chunk, tile) space, one segment (fixed rank,
+            // matrix and chunk) at a time; each tile's sum over the chunk goes
+            // out as a tagged partial (slot = chunk; gate in words 0..63, up
+            // in 64..127)
+            const long nL = (long)k * 2 * cprH * tilesI;
+            const long l1 = range_start(nL, G, w + 1);
+            for (long ua = range_start(nL, G, w); ua < l1;) {
+                const long seg = ua / tilesI;
+                const long ub = min(l1, (seg + 1) * tilesI);
+                const int c = (int)(seg % cprH), m = (int)((seg / cprH) & 1), j = (int)(seg / (2 * cprH));
+                const uint8_t *rec = (const uint8_t *)recs[j];
+                const int ta = (int)(ua - seg * tilesI);
+                stream_gateup_lut((const u32x4 *)(rec + a.off.codes[m]), (const u32x4 *)(rec + a.off.cb[m]), cprH, c,
+                                  ta, (int)(ub - ua), a.part_gu + ((size_t)j * tilesI * cprH + c) * 128 + m * 64, tag,
+                                  wave, lane);
+                ua = ub;
+            }
+            lds_sync();
+            mark(kStampGuLoop);
+            // joins: tiles tau = w + G i of all ranks' k * tilesI tiles, two at
+            // a time.  Wave v polls slots v, v + kPW, ... of both tiles (all its
+            // loads in flight together: one round trip once the partials have
+            // landed) and sums them in slot order; the waves' sums meet in LDS,
+            // and wave tt adds them in wave order for tile tt, scales, and
+            // writes fp16 SiLU(g) * u.
+            bool okj = true;
+            const long nTau = (long)k * tilesI;
+            const int nT = w < nTau ? (int)((nTau - 1 - w) / G) + 1 : 0;
+            float *jred = (float *)lds;     // [2][kPW][128], table area (free now)
+            for (int p0 = 0; p0 < nT; p0 += 2) {
+                const int tn = min(2, nT - p0);
+                float gs[2] = {0.f, 0.f}, us[2] = {0.f, 0.f};
+                for (int s0 = wave; s0 < cprH && okj; s0 += 4 * kPW) {
+                    uint64_t vg[2][4], vu[2][4];
+                    long spins = 0;
+                    for (;;) {
+                        bool ok = true;
+#pragma unroll
+                        for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+                            for (int q = 0; q < 4; q++) {
+                                const long tau = w + (long)G * (p0 + min(tt, tn - 1));
+                                const int sl = min(s0 + q * kPW, cprH - 1);
+                                const uint64_t *pp = a.part_gu + ((size_t)tau * cprH + sl) * 128 + lane;
+                                vg[tt][q] = ld_tagged(pp);
+                                vu[tt][q] = ld_tagged(pp + 64);
+                                ok = ok && tag_ok(vg[tt][q], tag) && tag_ok(vu[tt][q], tag);
+                            }
+                        if (__all(ok)) break;
+                        if (!poll_more(sync, spins)) { okj = false; break; }
+                    }
+                    if (!okj) break;
+#pragma unroll
+                    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+                        for (int q = 0; q < 4; q++)
+                            if (s0 + q * kPW < cprH) {
+                                gs[tt] += tag_val(vg[tt][q]);
+                                us[tt] += tag_val(vu[tt][q]);
+                            }
+                }
+#pragma unroll
+                for (int tt = 0; tt < 2; tt++) {
+                    jred[(tt * kPW + wave) * 128 + lane] = gs[tt];
+                    jred[(tt * kPW + wave) * 128 + 64 + lane] = us[tt];
+                }
+                lds_sync();
+                if (wave < tn) {
+                    const long tau = w + (long)G * (p0 + wave);
+                    const int j = (int)(tau / tilesI);
+                    const uint8_t *rec = (const uint8_t *)recs[j];
+                    const int r = (int)(tau % tilesI) * kTileRows + lane;
+                    float g = 0.f, uu = 0.f;
+#pragma unroll
+                    for (int v = 0; v < kPW; v++) {
+                        g += jred[(wave * kPW + v) * 128 + lane];
+                        uu += jred[(wave * kPW + v) * 128 + 64 + lane];
+                    }
+                    g *= (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
+                    uu *= (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
+                    const _Float16 hf = (_Float16)(g / (1.f + __expf(-g)) * uu);
+                    st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
+                }
+                lds_sync();
+            }
+            if (lane == 0 && !okj) *bcast = 0;
+            wait_vm_all();
+            __syncthreads();
+            if (!*bcast) return;
+            if (threadIdx.x == 0)
+                for (long tau = w; tau < (long)k * tilesI; tau += G)
+                    __hip_atomic_fetch_add(h_ready + (tau / tilesI) * kLine, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        }
         // ---- gate/up over this workgroup's range of (rank, tile, chunk), one
         // expert segment at a time (a range spans at most two experts)
-        for (long ea = gu0; ea < gu1;) {
+        for (long ea = a.lut ? gu1 : gu0; ea < gu1;) {
             const int j = (int)(ea / ((long)tilesI * cprH));
             const long eb = min(gu1, (long)(j + 1) * tilesI * cprH);
             const uint8_t *rec = (const uint8_t *)recs[j];
@@ -1084,9 +1372,14 @@ static int max_tiles_per_range(long n_tiles, int cpr, int G) {
     return m;
 }
 
-hipError_t decode_plan(int H, int I, int k, DecodePlanOut *o) {
+hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
     static int G = 0;
+    static bool lds_at_zero = false;   // no static LDS: dynamic LDS starts at byte 0
     if (G == 0) {
+        hipFuncAttributes fa;
+        hipError_t ea = hipFuncGetAttributes(&fa, (const void *)k_decode_persistent);
+        if (ea != hipSuccess) return ea;
+        lds_at_zero = fa.sharedSizeBytes == 0;
         int dev = 0, cus = 0, per = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1106,6 +1399,13 @@ hipError_t decode_plan(int H, int I, int k, DecodePlanOut *o) {
     o->slots_d = max_contributors((long)k * tilesH, cprI, G);
     o->slots_red_gu = max_tiles_per_range((long)k * tilesI, cprH, G);
     o->slots_red_d = max_tiles_per_range((long)k * tilesH, cprI, G);
+    // Table lookup: a table costs about as much as streaming 4096 rows' groups
+    // by gathers, so it pays when every table serves many more rows than that
+    // (by default I >= 8192 rows per gate/up matrix); x (fp32) must fit in LDS
+    // beside the table.
+    const bool lut_fits = lds_at_zero && H <= kLutMaxH;
+    o->lut = lut_fits && (lut_mode == 1 || (lut_mode < 0 && I >= 2 * kCbRows)) ? 1 : 0;
+    if (o->lut) o->slots_gu = cprH;
     o->sync_words = kHReady + (size_t)(k + 1) * kLine;
     // LDS: both phases' layouts must fit below the routing tail
     const long red_gu = 2L * kCbRows * 16 + ((H * 2 + 255) & ~255) + (long)o->slots_red_gu * kPW * 128 * 4;
@@ -1152,6 +1452,7 @@ hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s) {
     a.slots_d = d.slots_d;
     a.slots_red_gu = d.slots_red_gu;
     a.slots_red_d = d.slots_red_d;
+    a.lut = d.lut;
     a.stamps = d.stamps;
     a.stamp_steps = d.stamp_steps;
     (void)tilesI;

@@ -289,7 +289,7 @@ struct DecodeWs {
     float *hs;
     unsigned long long *stamps;
     int stamp_steps;
-    int G, slots_gu, slots_d, slots_red_gu, slots_red_d;
+    int G, slots_gu, slots_d, slots_red_gu, slots_red_d, lut;
     size_t sync_words, clear_words, bytes;
 };
 
@@ -298,6 +298,13 @@ struct DecodeWs {
 int decode_stamp_steps() {
     const char *e = getenv("MOE_DECODE_STAMPS");
     return e ? std::max(0, atoi(e)) : 0;
+}
+
+// MOE_DECODE_LUT=0 or 1 forces the gate/up method of the decode kernel
+// (codebook gathers or table lookup); unset, the shape decides.
+int decode_lut_mode() {
+    const char *e = getenv("MOE_DECODE_LUT");
+    return e && *e ? (atoi(e) ? 1 : 0) : -1;
 }
 
 int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *D) {
@@ -309,7 +316,7 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
         shared = shared || layers[l].shared;
     }
     DecodePlanOut P;
-    hipError_t e = decode_plan(H, I, k, &P);
+    hipError_t e = decode_plan(H, I, k, decode_lut_mode(), &P);
     if (e != hipSuccess) return hip_fail(e, "decode plan");
     if (!P.lds_ok) return fail(MOE_E_INVAL, "decode kernel: H=%d, I=%d do not fit its LDS layout", H, I);
     D->G = P.G;
@@ -317,6 +324,7 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
     D->slots_d = P.slots_d;
     D->slots_red_gu = P.slots_red_gu;
     D->slots_red_d = P.slots_red_d;
+    D->lut = P.lut;
     D->sync_words = P.sync_words;
     Carver c(ws);
     // zeroed before every launch: the counters (word 0 is the error flag
@@ -387,6 +395,7 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
     d.slots_d = D.slots_d;
     d.slots_red_gu = D.slots_red_gu;
     d.slots_red_d = D.slots_red_d;
+    d.lut = D.lut;
     d.stamps = D.stamps;
     d.stamp_steps = D.stamp_steps;
     auto set_layers = [&](int l0, int nl) {

@@ -119,6 +119,7 @@ struct DecodeLaunch {
     float *hs;
     int slots_gu, slots_d;
     int slots_red_gu, slots_red_d;
+    int lut;                 // gate/up by table lookup (decode_plan decides)
     unsigned long long *stamps;   // phase timestamps (profiling aid), or null
     int stamp_steps;
 };
@@ -127,10 +128,13 @@ struct DecodePlanOut {
     int G;                        // persistent workgroups (one per CU)
     int slots_gu, slots_d;        // most contributors to one tile's partial sums
     int slots_red_gu, slots_red_d;   // most tiles one workgroup touches per phase
+    int lut;                      // gate/up by table lookup: 1, by codebook gathers: 0
     size_t sync_words;
     bool lds_ok;
 };
-hipError_t decode_plan(int H, int I, int k, DecodePlanOut *o);
+// lut_mode: -1 = choose by shape, 0 = codebook gathers, 1 = table lookup
+// (o->lut = 0 if the shape does not allow it).
+hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o);
 hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s);
 
 // ---- batched path (kernels_grouped.hip) --------------------------------------

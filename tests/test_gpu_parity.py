@@ -179,7 +179,28 @@ def test_decode_forward_k3_shape_fewer_experts_per_token(moe, k):
 
 def test_decode_forward_mixtral_full_size(moe):
     # the configuration bench.py times: all 32 layers, 8 resident experts each
+    # (gate/up by table lookup, the default at I = 14336)
     _check_decode(moe, synth.get_config("mixtral", tokens=2))
+
+
+def test_decode_forward_mixtral_gathers(moe, monkeypatch):
+    # the same shape with gate/up by codebook gathers
+    monkeypatch.setenv("MOE_DECODE_LUT", "0")
+    _check_decode(moe, synth.get_config("mixtral", tokens=1, layers=4))
+
+
+def test_decode_forward_lut_straddling_segments(moe, monkeypatch):
+    # gate/up by table lookup forced at a shape whose default is gathers:
+    # 4.5 tiles per workgroup, so ranges straddle segments (matrices, chunk
+    # groups, experts) and most waves have no tile
+    monkeypatch.setenv("MOE_DECODE_LUT", "1")
+    _check_decode(moe, synth.get_config("mixtral", H=2048, I=3072, k=3, tokens=2, layers=2))
+
+
+def test_decode_forward_lut_shared_sigmoid(moe, monkeypatch):
+    # forced table lookup with a shared expert, sigmoid top-8 and Zipf bias
+    monkeypatch.setenv("MOE_DECODE_LUT", "1")
+    _check_decode(moe, synth.get_config("kimi_linear", H=2048, I=2048, E=64, tokens=2, layers=2))
 
 
 def _streamed_setup(moe, cfg, capacity):
