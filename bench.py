@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # valid for the kernel source they were taken on: reported as null once that
 # source has changed.
 DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
-                  "sha256_prefix": "630163846a9ee153", "bytes_per_launch": 4696877553}
+                  "sha256_prefix": "e390e40f35a33d40", "bytes_per_launch": 5393606201}
 
 
 def measured_traffic():

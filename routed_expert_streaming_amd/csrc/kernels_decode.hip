@@ -310,6 +310,7 @@ __device__ __forceinline__ DecLds dec_lds_layout(int H, int I) {
 constexpr int kDecTail = kDecLdsBytes - 1024;     // sidx, sw, broadcast words, router partials
 constexpr int kDecRecs = kDecTail - 8 * MOE_MAX_E;   // the layer's record pointers, until top-k
 
+constexpr int kDecCtr = kDecLdsBytes - 4;   // the lookup phase's tile counter (unused end of the tail)
 constexpr int kRingGU = 3;      // code buffers per wave (2 units in flight ahead)
 constexpr int kShRows = 8;      // shared-expert rows per load group
 constexpr int kTopkScratch = 2048;   // LDS bytes (codebook area, free while routing): top-k staging
@@ -621,15 +622,22 @@ __device__ __forceinline__ void lut_build(const f16x4 (&A)[kLutCbTiles], int c, 
 
 // One segment of the table-lookup gate/up space: matrix m (codes at codes,
 // codebook at cb) of one expert, chunk c, row tiles [ta, ta + nt).  One
-// table build, then wave v streams tiles ta + v, ta + v + kPW, ... through a
-// register ring (no barriers) and stores each tile's sum over the chunk as a
-// tagged partial at part + 128 * cprH * tile (slot c of the tile; the caller
-// adds the rank's base, the slot and the matrix's half).
+// table build, then the waves stream the tiles through register rings (no
+// barriers) and store each tile's sum over the chunk as a tagged partial at
+// part + 128 * cprH * tile (slot c of the tile; the caller adds the rank's
+// base, the slot and the matrix's half).  Wave v's first kLutRing - 1 tiles
+// are v, v + kPW, ...; after that each wave takes the next tile from a
+// workgroup counter in LDS, so waves that run ahead take more tiles.  A tile
+// is always summed whole by one wave, so the result does not depend on which.
+__device__ __forceinline__ int lut_next_tile(unsigned *ctr, int lane) {
+    unsigned v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return (int)__builtin_amdgcn_readfirstlane(v);
+}
 __device__ __forceinline__ void stream_gateup_lut(const u32x4 *codes, const u32x4 *cb, int cprH, int c, int ta,
                                                   int nt, uint64_t *part, unsigned tag, int wave, int lane) {
     gu32x4 *gb = (gu32x4 *)codes;
-    const int first = ta + wave;
-    const int n = __builtin_amdgcn_readfirstlane(wave < nt ? (nt - wave + kPW - 1) / kPW : 0);
+    unsigned *ctr = (unsigned *)(dec_lds + kDecCtr);
     // the A fragments first: the build waits for them alone, tile by tile,
     // while the code ring's loads stay in flight
     f16x4 A[kLutCbTiles];
@@ -640,29 +648,30 @@ __device__ __forceinline__ void stream_gateup_lut(const u32x4 *codes, const u32x
 #pragma unroll
         for (int t = 0; t < kLutCbTiles; t++) A[t] = src[t * 64];
     }
-    // a wave without tiles loads the segment's first tile (never consumed)
-    auto unit_addr = [&](int i) { return (n ? first + kPW * min(i, n - 1) : ta) * cprH + c; };
+    // tiles past the segment load its last tile (never consumed)
+    auto unit_addr = [&](int t) { return (ta + min(t, nt - 1)) * cprH + c; };
     uint32_t buf[kLutRing][12];
+    int tile[kLutRing];
 #pragma unroll
-    for (int r = 0; r < kLutRing - 1; r++) load_codes(gb, unit_addr(r), lane, buf[r]);
-    lds_sync();                    // the previous table's readers are done
+    for (int r = 0; r < kLutRing - 1; r++) {
+        tile[r] = wave + kPW * r;
+        load_codes(gb, unit_addr(tile[r]), lane, buf[r]);
+    }
+    lds_sync();                    // the previous table's readers and counter users are done
+    if (threadIdx.x == 0) *ctr = kPW * (kLutRing - 1);
     lut_build(A, c, wave);
     lds_sync();
-    auto process = [&](int i, const uint32_t (&d)[12]) {
-        st_tagged(part + (size_t)(first + kPW * i) * 128 * cprH + lane, lut_strip(d), tag);
-    };
-    int i = 0;
-    for (; i + kLutRing <= n; i += kLutRing) {
+    // a wave's tiles only grow, so once one is past the segment, all later ones are
+    for (;;) {
 #pragma unroll
         for (int r = 0; r < kLutRing; r++) {
-            load_codes(gb, unit_addr(i + r + kLutRing - 1), lane, buf[(r + kLutRing - 1) % kLutRing]);
-            process(i + r, buf[r]);
+            const int nr = (r + kLutRing - 1) % kLutRing;
+            tile[nr] = lut_next_tile(ctr, lane);
+            load_codes(gb, unit_addr(tile[nr]), lane, buf[nr]);
+            if (tile[r] < nt) st_tagged(part + (size_t)(ta + tile[r]) * 128 * cprH + lane, lut_strip(buf[r]), tag);
         }
+        if (tile[kLutRing - 1] >= nt) break;
     }
-    // the last n - i (< kLutRing) units are already in buffers 0, 1, ...
-#pragma unroll
-    for (int r = 0; r < kLutRing - 1; r++)
-        if (i + r < n) process(i + r, buf[r]);
 }
 
 // Workgroup whose down range holds the last unit of output tile td in the
@@ -1039,17 +1048,20 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // matrix and chunk) at a time; each tile's sum over the chunk goes
             // out as a tagged partial (slot = chunk; gate in words 0..63, up
             // in 64..127)
-            const long nL = (long)k * 2 * cprH * tilesI;
-            const long l1 = range_start(nL, G, w + 1);
-            for (long ua = range_start(nL, G, w); ua < l1;) {
-                const long seg = ua / tilesI;
-                const long ub = min(l1, (seg + 1) * tilesI);
-                const int c = (int)(seg % cprH), m = (int)((seg / cprH) & 1), j = (int)(seg / (2 * cprH));
+            // (32-bit index math: the host allows this path only where
+            // nL * G fits an int)
+            const int nL = k * 2 * cprH * tilesI;
+            const int GaL = min(nL, G);
+            const int l1 = w + 1 >= GaL ? nL : nL * (w + 1) / GaL;
+            for (int ua = w >= GaL ? nL : nL * w / GaL; ua < l1;) {
+                const int seg = ua / tilesI;
+                const int ub = min(l1, (seg + 1) * tilesI);
+                const int c = seg % cprH, m = (seg / cprH) & 1, j = seg / (2 * cprH);
                 const uint8_t *rec = (const uint8_t *)recs[j];
-                const int ta = (int)(ua - seg * tilesI);
+                const int ta = ua - seg * tilesI;
                 stream_gateup_lut((const u32x4 *)(rec + a.off.codes[m]), (const u32x4 *)(rec + a.off.cb[m]), cprH, c,
-                                  ta, (int)(ub - ua), a.part_gu + ((size_t)j * tilesI * cprH + c) * 128 + m * 64, tag,
-                                  wave, lane);
+                                  ta, ub - ua, a.part_gu + ((size_t)j * tilesI * cprH + c) * 128 + m * 64, tag, wave,
+                                  lane);
                 ua = ub;
             }
             lds_sync();
@@ -1403,7 +1415,7 @@ hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
     // by gathers, so it pays when every table serves many more rows than that
     // (by default I >= 8192 rows per gate/up matrix); x (fp32) must fit in LDS
     // beside the table.
-    const bool lut_fits = lds_at_zero && H <= kLutMaxH;
+    const bool lut_fits = lds_at_zero && H <= kLutMaxH && (long)k * 2 * cprH * tilesI * G < (1L << 31);
     o->lut = lut_fits && (lut_mode == 1 || (lut_mode < 0 && I >= 2 * kCbRows)) ? 1 : 0;
     if (o->lut) o->slots_gu = cprH;
     o->sync_words = kHReady + (size_t)(k + 1) * kLine;
