@@ -314,6 +314,9 @@ constexpr int kDecCtr = kDecLdsBytes - 4;   // the lookup phase's tile counter (
 constexpr int kRingGU = 3;      // code buffers per wave (2 units in flight ahead)
 constexpr int kShRows = 8;      // shared-expert rows per load group
 constexpr int kTopkScratch = 2048;   // LDS bytes (codebook area, free while routing): top-k staging
+constexpr int kTopkGroups = 8;       // first-level groups of the top-k
+// zkey [MOE_MAX_E], candidates [kTopkGroups * MOE_MAX_K], logits in rank order [MOE_MAX_K], count
+constexpr int kTopkCount = kTopkScratch + 8 * (MOE_MAX_E + kTopkGroups * MOE_MAX_K) + 4 * MOE_MAX_K;
 
 // Order-preserving key of a float (larger float, larger key; -0 and +0 one
 // key, as they compare equal) and back.
@@ -816,6 +819,12 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         mark(kStampLayerWait);
 
         const unsigned tag = (unsigned)s + 1;
+        {
+            // the top-k's candidate list and count (LDS free since the last step ended)
+            uint64_t *cand0 = (uint64_t *)(lds + kTopkScratch) + MOE_MAX_E;
+            for (int i = threadIdx.x; i < kTopkGroups * MOE_MAX_K; i += kPW * 64) cand0[i] = 0u;
+            if (threadIdx.x == 0) *(unsigned *)(lds + kTopkCount) = 0u;
+        }
 
         // ---- x as fp16 pairs into LDS (every workgroup, for gate/up), in
         // one pass with this workgroup's first logit row (e = w, if w < E):
@@ -958,7 +967,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // key of expert e: order_key(z) << 32 | (2^32 - 1 - e), so one 64-bit
         // comparison orders by logit, then by lower id
         uint64_t *zkey = (uint64_t *)(lds + kTopkScratch);    // [E rounded up to 32]
-        float *sz = (float *)(zkey + MOE_MAX_E);              // [MOE_MAX_K] logits in rank order
+        float *sz = (float *)(zkey + MOE_MAX_E + kTopkGroups * MOE_MAX_K);   // [MOE_MAX_K] logits in rank order
         if (wave == 0) {
             long spins = 0;
             bool okw = true;
@@ -995,26 +1004,54 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             }
         }
         {
+            // Exact top-k by counting: a key's rank is the number of keys
+            // above it (keys are unique: logit bits above the inverted id).
+            // For E > 64 in two levels: each key is first ranked within its
+            // group (E split into kTopkGroups ranges of whole 32-key blocks);
+            // keys of local rank < k are candidates (every global top-k key is
+            // one) and are ranked among themselves, so the result does not
+            // depend on the order in which they were appended.
             const int kk = __builtin_amdgcn_readfirstlane(lay.k);
-            for (int e = threadIdx.x; e < E; e += kPW * 64) {
-                const uint64_t ke = zkey[e];
-                // 32 keys per step (broadcast reads), four independent counts
+            const bool two = E > 64;
+            const int gsz = two ? ((E + kTopkGroups - 1) / kTopkGroups + 31) & ~31 : (E + 31) & ~31;
+            uint64_t *cand = zkey + MOE_MAX_E;                  // [kTopkGroups * MOE_MAX_K], zeroed while routing began
+            unsigned *ncand = (unsigned *)(lds + kTopkCount);
+            // rank of key ke among the keys at list[q0, q1) (q0, q1 multiples of 32)
+            auto count_above = [&](const uint64_t *list, int q0, int q1, uint64_t ke) {
                 int r[4] = {0, 0, 0, 0};
-                for (int q0 = 0; q0 < E && r[0] + r[1] + r[2] + r[3] < kk; q0 += 32) {
+                for (; q0 < q1 && r[0] + r[1] + r[2] + r[3] < kk; q0 += 32) {
                     uint64_t kv[32];
 #pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const u32x4 two = *(const u32x4 *)(zkey + q0 + 2 * i);
-                        kv[2 * i] = (uint64_t)two.y << 32 | two.x;
-                        kv[2 * i + 1] = (uint64_t)two.w << 32 | two.z;
+                    for (int i = 0; i < 16; i++) {   // 32 keys per step (broadcast reads)
+                        const u32x4 tw = *(const u32x4 *)(list + q0 + 2 * i);
+                        kv[2 * i] = (uint64_t)tw.y << 32 | tw.x;
+                        kv[2 * i + 1] = (uint64_t)tw.w << 32 | tw.z;
                     }
 #pragma unroll
-                    for (int i = 0; i < 32; i++) r[i & 3] += kv[i] > ke;
+                    for (int i = 0; i < 32; i++) r[i & 3] += kv[i] > ke;   // four independent counts
                 }
-                const int rank = r[0] + r[1] + r[2] + r[3];
+                return r[0] + r[1] + r[2] + r[3];
+            };
+            auto place = [&](int rank, uint64_t ke) {
+                sidx[rank] = (int)(0xFFFFFFFFu - (uint32_t)ke);
+                sz[rank] = key_value((uint32_t)(ke >> 32));
+            };
+            for (int e = threadIdx.x; e < E; e += kPW * 64) {
+                const uint64_t ke = zkey[e];
+                const int g0 = e / gsz * gsz;
+                const int rank = count_above(zkey, g0, min((E + 31) & ~31, g0 + gsz), ke);
                 if (rank < kk) {
-                    sidx[rank] = e;
-                    sz[rank] = key_value((uint32_t)(ke >> 32));
+                    if (two) cand[__hip_atomic_fetch_add(ncand, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)] = ke;
+                    else place(rank, ke);
+                }
+            }
+            if (two) {
+                lds_sync();
+                const int nc = (int)*ncand;
+                for (int c = threadIdx.x; c < nc; c += kPW * 64) {
+                    const uint64_t ke = cand[c];
+                    const int rank = count_above(cand, 0, (nc + 31) & ~31, ke);
+                    if (rank < kk) place(rank, ke);
                 }
             }
         }
