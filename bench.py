@@ -276,8 +276,10 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if cfg.name == "mixtral" else None,
-                     "kernel": "k_decode_persistent (route, top-k, RVQ gate/up, RVQ down, combine; all layers of "
-                               "one token per launch)",
+                     "kernel": "k_decode_persistent (route, top-k, RVQ gate/up by %s, RVQ down, combine; all "
+                               "layers of one token per launch)" % (
+                                   "table lookup" if moe.decode_gate_up_method(dw.layers) == "lookup"
+                                   else "codebook gathers"),
                      "algorithmic_bytes_per_launch": bytes_tok},
         "device": torch.cuda.get_device_name(0),
         "commit": git_commit(),

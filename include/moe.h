@@ -202,6 +202,18 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
                        int32_t T, float *out, int32_t *idx_out, void *ws,
                        size_t ws_bytes, void *hip_stream);
 
+/* Which gate/up method moe_decode_forward uses for these layers on the
+ * current device: 0 = codebook-row gathers (two 16-byte LDS reads per group
+ * of 8 weights), 1 = table lookup (a per-chunk table of codebook-row x group
+ * dot products in LDS, two 2-byte reads per group).  Both compute the same
+ * products of the RVQ weights (WASTE article, section "유휴 가중치는 메모리가
+ * 아니라 제때 닿기만 하면 된다": weights never expanded); the kernel picks
+ * table lookup where each table serves many rows (I >= 8192), and the
+ * environment variable MOE_DECODE_LUT=0 or 1 overrides where the shape allows.
+ * Host-only query; needs a device (reads its compute-unit count).
+ *   layers [host] as for moe_decode_forward;  method: 0 or 1 */
+int moe_decode_gate_up_method(const moe_layer *layers, int32_t n_layers, int32_t *method);
+
 /* Whether the last moe_decode_forward that used this workspace hit its
  * device-side wait limit (a dependency between workgroups did not resolve
  * within a few seconds; every wave then leaves the kernel and the outputs of

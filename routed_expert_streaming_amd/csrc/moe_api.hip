@@ -433,6 +433,17 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
     return MOE_OK;
 }
 
+int moe_decode_gate_up_method(const moe_layer *layers, int32_t n_layers, int32_t *method) {
+    if (!layers || n_layers < 1 || !method) return fail(MOE_E_INVAL, "layers or method is NULL, or n_layers < 1");
+    if (!dims_ok(layers[0].H, layers[0].I) || layers[0].router.k < 1)
+        return fail(MOE_E_INVAL, "invalid layer shape");
+    DecodeWs D;
+    int rc = carve_decode(nullptr, layers, n_layers, &D);
+    if (rc) return rc;
+    *method = D.lut;
+    return MOE_OK;
+}
+
 int moe_decode_status(const void *ws, int32_t *timed_out) {
     if (!ws || !timed_out) return fail(MOE_E_INVAL, "ws and timed_out must be non-NULL");
     unsigned flag = 0;

@@ -129,13 +129,15 @@ def test_layer_parity_real_shapes(moe, name, T):
     torch.cuda.empty_cache()
 
 
-def _check_decode(moe, cfg, layers=None, sample=None):
+def _check_decode(moe, cfg, layers=None, sample=None, method=None):
     """Persistent decode kernel (one launch for all tokens x layers) against
-    the oracle, layer call by layer call; also run-to-run determinism and
-    the device-side wait flag."""
+    the oracle, layer call by layer call; also run-to-run determinism, the
+    device-side wait flag and (if given) the gate/up method in use."""
     from routed_expert_streaming_amd.device_workload import DeviceWorkload
     log(f"decode {cfg.name}: {cfg.tokens} tokens x {cfg.layers} layers, uploading")
     dw = DeviceWorkload(cfg)
+    if method is not None:
+        assert moe.decode_gate_up_method(dw.layers) == method
     x = dw.inputs()
     ws = torch.empty(moe.decode_workspace_bytes(dw.layers), dtype=torch.uint8, device="cuda")
     out, idx = moe.decode_forward(dw.layers, x, ws=ws)
@@ -168,7 +170,7 @@ def test_decode_forward_tiny(moe):
 
 
 def test_decode_forward_k3_shape_shared(moe):
-    _check_decode(moe, synth.get_config("k3_slice", tokens=2, layers=2))
+    _check_decode(moe, synth.get_config("k3_slice", tokens=2, layers=2), method="gathers")
 
 
 @pytest.mark.parametrize("k", [4, 8])
@@ -180,13 +182,13 @@ def test_decode_forward_k3_shape_fewer_experts_per_token(moe, k):
 def test_decode_forward_mixtral_full_size(moe):
     # the configuration bench.py times: all 32 layers, 8 resident experts each
     # (gate/up by table lookup, the default at I = 14336)
-    _check_decode(moe, synth.get_config("mixtral", tokens=2))
+    _check_decode(moe, synth.get_config("mixtral", tokens=2), method="lookup")
 
 
 def test_decode_forward_mixtral_gathers(moe, monkeypatch):
     # the same shape with gate/up by codebook gathers
     monkeypatch.setenv("MOE_DECODE_LUT", "0")
-    _check_decode(moe, synth.get_config("mixtral", tokens=1, layers=4))
+    _check_decode(moe, synth.get_config("mixtral", tokens=1, layers=4), method="gathers")
 
 
 def test_decode_forward_lut_straddling_segments(moe, monkeypatch):
@@ -194,13 +196,13 @@ def test_decode_forward_lut_straddling_segments(moe, monkeypatch):
     # 4.5 tiles per workgroup, so ranges straddle segments (matrices, chunk
     # groups, experts) and most waves have no tile
     monkeypatch.setenv("MOE_DECODE_LUT", "1")
-    _check_decode(moe, synth.get_config("mixtral", H=2048, I=3072, k=3, tokens=2, layers=2))
+    _check_decode(moe, synth.get_config("mixtral", H=2048, I=3072, k=3, tokens=2, layers=2), method="lookup")
 
 
 def test_decode_forward_lut_shared_sigmoid(moe, monkeypatch):
     # forced table lookup with a shared expert, sigmoid top-8 and Zipf bias
     monkeypatch.setenv("MOE_DECODE_LUT", "1")
-    _check_decode(moe, synth.get_config("kimi_linear", H=2048, I=2048, E=64, tokens=2, layers=2))
+    _check_decode(moe, synth.get_config("kimi_linear", H=2048, I=2048, E=64, tokens=2, layers=2), method="lookup")
 
 
 def _streamed_setup(moe, cfg, capacity):
