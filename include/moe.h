@@ -37,8 +37,16 @@
  *    void* (NULL = the default stream).
  *  - Ownership: the caller owns every device buffer, workspace, slot pool,
  *    pinned pool and stream.  The library never allocates device memory; it
- *    owns only host-side cache metadata and the hipEvents it creates, which
+ *    owns only host-side cache metadata, the hipEvents it creates and, once
+ *    a record is copied from pageable memory, the cache's four pinned bounce
+ *    buffers (slot_bytes each) and host copy threads, all of which
  *    expert_cache_destroy() frees.
+ *  - Expert records for the cache ([pinned] below) may also be in pageable
+ *    host memory: such a record is copied by host threads into the next
+ *    bounce buffer (after that buffer's previous transfer has completed,
+ *    which the calling thread waits for) and transferred from there, since
+ *    the runtime's own staging of pageable transfers runs well below the
+ *    link rate.
  *  - Kernels are asynchronous: argument and launch errors are returned at
  *    once, execution errors surface at the caller's next synchronisation.
  *  - T = 0 is a no-op returning MOE_OK.

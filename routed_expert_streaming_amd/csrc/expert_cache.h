@@ -4,10 +4,37 @@
 
 #include <hip/hip_runtime.h>
 
+#include <condition_variable>
+#include <mutex>
+#include <thread>
 #include <vector>
 
 #include "expert_cache_core.h"
 #include "moe.h"
+
+namespace moe {
+// Persistent host threads that split one memcpy between them (pageable
+// records into a pinned bounce buffer).
+class CopyPool {
+public:
+    explicit CopyPool(int n);
+    ~CopyPool();
+    void copy(void *dst, const void *src, size_t bytes);   // returns when all of it is copied
+private:
+    void worker(int i);
+    std::mutex m_;
+    std::condition_variable go_, done_;
+    std::vector<std::thread> th_;
+    size_t n_ = 0;                 // threads (fixed before any starts)
+    char *dst_ = nullptr;
+    const char *src_ = nullptr;
+    size_t bytes_ = 0;
+    unsigned gen_ = 0;
+    int pending_ = 0;
+    bool stop_ = false;
+};
+constexpr int kBounce = 4;   // pinned bounce buffers per cache
+}  // namespace moe
 
 struct moe_cache {
     moe::LruCore core;
@@ -19,6 +46,13 @@ struct moe_cache {
     std::vector<uint8_t> used;            // last_use has been recorded
     int32_t *h_idx = nullptr;             // pinned staging for the router's expert ids
     int device = 0;
+    // records in pageable host memory go through pinned bounce buffers
+    // (allocated on first use) filled by host threads
+    char *bounce[moe::kBounce] = {};
+    hipEvent_t bounce_done[moe::kBounce] = {};   // recorded on the copy stream after the buffer's copy
+    bool bounce_used[moe::kBounce] = {};
+    int bounce_next = 0;
+    moe::CopyPool *copier = nullptr;
 
     explicit moe_cache(int capacity) : core(capacity) {}
 };
@@ -26,4 +60,10 @@ struct moe_cache {
 namespace moe {
 int cache_wait(moe_cache *c, int32_t slot, hipStream_t s);
 int cache_release(moe_cache *c, int32_t slot, hipStream_t s);
+// Enqueue the copy of one record (slot_bytes at src, host memory) into slot
+// s on stream ps: straight from page-locked memory; from pageable memory
+// through the next bounce buffer, which host threads fill after its previous
+// copy has completed (the runtime's own staging of pageable copies reaches a
+// fraction of the link rate).
+hipError_t cache_copy_in(moe_cache *c, int32_t s, const void *src, hipStream_t ps);
 }  // namespace moe

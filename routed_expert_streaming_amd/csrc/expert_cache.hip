@@ -1,6 +1,7 @@
 // C ABI of the HBM expert-slot cache (include/moe.h): LRU metadata on the
-// host (expert_cache_core), one hipMemcpyAsync per miss from pinned host
-// memory into the slot on a copy stream, per-slot events for ordering.
+// host (expert_cache_core), one hipMemcpyAsync per miss from host memory into
+// the slot on a copy stream (pageable records through pinned bounce buffers
+// filled by host threads), per-slot events for ordering.
 //
 // Sources: WISP launch post, section "통찰" (lookups in the fastest tier
 // that holds the expert, LRU promotion) and section "더블 버퍼 비동기
@@ -9,7 +10,9 @@
 // aligned record per expert, so a miss costs exactly one transfer).
 #include "expert_cache.h"
 
+#include <algorithm>
 #include <climits>
+#include <cstring>
 #include <new>
 
 namespace moe {
@@ -47,8 +50,100 @@ void destroy_events(moe_cache *c) {
     c->last_use.clear();
     if (c->h_idx) (void)hipHostFree(c->h_idx);
     c->h_idx = nullptr;
+    for (int b = 0; b < moe::kBounce; b++) {
+        if (c->bounce_used[b]) (void)hipEventSynchronize(c->bounce_done[b]);
+        if (c->bounce_done[b]) (void)hipEventDestroy(c->bounce_done[b]);
+        if (c->bounce[b]) (void)hipHostFree(c->bounce[b]);
+        c->bounce_done[b] = nullptr;
+        c->bounce[b] = nullptr;
+        c->bounce_used[b] = false;
+    }
+    delete c->copier;
+    c->copier = nullptr;
+}
+
+bool page_locked(const void *p) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();          // pageable memory may be reported as an error
+        return false;
+    }
+    return at.type == hipMemoryTypeHost;
 }
 }  // namespace
+
+namespace moe {
+CopyPool::CopyPool(int n) : n_((size_t)n) {
+    th_.reserve(n_);
+    for (int i = 0; i < n; i++) th_.emplace_back(&CopyPool::worker, this, i);
+}
+CopyPool::~CopyPool() {
+    {
+        std::lock_guard<std::mutex> g(m_);
+        stop_ = true;
+    }
+    go_.notify_all();
+    for (auto &t : th_) t.join();
+}
+void CopyPool::worker(int i) {
+    unsigned seen = 0;
+    for (;;) {
+        char *dst;
+        const char *src;
+        size_t bytes;
+        {
+            std::unique_lock<std::mutex> l(m_);
+            go_.wait(l, [&] { return stop_ || gen_ != seen; });
+            if (stop_) return;
+            seen = gen_;
+            dst = dst_;
+            src = src_;
+            bytes = bytes_;
+        }
+        // slice i of n, on 4 KiB boundaries
+        const size_t n = n_, pages = (bytes + 4095) / 4096;
+        const size_t a = std::min(bytes, pages * i / n * 4096), b = std::min(bytes, pages * (i + 1) / n * 4096);
+        if (b > a) std::memcpy(dst + a, src + a, b - a);
+        std::lock_guard<std::mutex> g(m_);
+        if (--pending_ == 0) done_.notify_one();
+    }
+}
+void CopyPool::copy(void *dst, const void *src, size_t bytes) {
+    std::unique_lock<std::mutex> l(m_);
+    dst_ = (char *)dst;
+    src_ = (const char *)src;
+    bytes_ = bytes;
+    pending_ = (int)n_;
+    gen_++;
+    go_.notify_all();
+    done_.wait(l, [&] { return pending_ == 0; });
+}
+
+hipError_t cache_copy_in(moe_cache *c, int32_t s, const void *src, hipStream_t ps) {
+    char *dst = c->pool + (size_t)s * c->slot_bytes;
+    if (page_locked(src)) return hipMemcpyAsync(dst, src, c->slot_bytes, hipMemcpyHostToDevice, ps);
+    hipError_t e = hipSuccess;
+    if (!c->copier) {
+        for (int b = 0; e == hipSuccess && b < kBounce; b++) {
+            e = hipHostMalloc((void **)&c->bounce[b], c->slot_bytes, hipHostMallocDefault);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&c->bounce_done[b], hipEventDisableTiming);
+        }
+        if (e != hipSuccess) return e;
+        const unsigned hw = std::thread::hardware_concurrency();
+        c->copier = new (std::nothrow) CopyPool((int)std::max(1u, std::min(8u, hw ? hw : 1u)));
+        if (!c->copier) return hipErrorOutOfMemory;
+    }
+    const int b = c->bounce_next;
+    c->bounce_next = (b + 1) % kBounce;
+    if (c->bounce_used[b] && (e = hipEventSynchronize(c->bounce_done[b])) != hipSuccess) return e;
+    c->bounce_used[b] = false;
+    c->copier->copy(c->bounce[b], src, c->slot_bytes);
+    e = hipMemcpyAsync(dst, c->bounce[b], c->slot_bytes, hipMemcpyHostToDevice, ps);
+    if (e == hipSuccess) e = hipEventRecord(c->bounce_done[b], ps);
+    c->bounce_used[b] = e == hipSuccess;
+    return e;
+}
+}  // namespace moe
 
 extern "C" {
 
@@ -104,8 +199,8 @@ int expert_cache_insert(moe_cache *c, uint32_t key, const void *host_src, void *
     hipError_t e = hipSuccess;
     if (c->used[s]) e = hipStreamWaitEvent(cs, c->last_use[s], 0);      // readers of the victim first
     if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(last_use)");
-    e = hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, host_src, c->slot_bytes, hipMemcpyHostToDevice, cs);
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(slot)");    // nothing enqueued: cache unchanged
+    e = moe::cache_copy_in(c, s, host_src, cs);
+    if (e != hipSuccess) return hip_fail(e, "copy into slot");    // nothing enqueued: cache unchanged
     e = hipEventRecord(c->ready[s], cs);
     if (e != hipSuccess) {
         // the copy is in flight but cannot be waited on: the slot no longer

@@ -616,8 +616,9 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         const int32_t s = slot_of[j];
         if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "copy waits for slot readers");
         const void *src = tier.t ? (const void *)src_of[j] : experts_host[c->h_idx[j]];
-        hipError_t e = hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, src, c->slot_bytes,
-                                      hipMemcpyHostToDevice, ps);
+        hipError_t e = tier.t ? hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, src, c->slot_bytes,
+                                               hipMemcpyHostToDevice, ps)
+                              : cache_copy_in(c, s, src, ps);
         if (e == hipSuccess && tier.t) {
             const int trc = tier_copied(tier.t, src_of[j], ps);
             if (trc) {
@@ -667,8 +668,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         if (!inserted) continue;
         c->filled[s] = 0;
         if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "look-ahead copy waits for slot readers");
-        hipError_t e = hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, ah.host[pred[j]], c->slot_bytes,
-                                      hipMemcpyHostToDevice, ps);
+        hipError_t e = cache_copy_in(c, s, ah.host[pred[j]], ps);
         if (e == hipSuccess) e = hipEventRecord(c->ready[s], ps);
         if (e != hipSuccess) {
             c->core.drop_slot(s);

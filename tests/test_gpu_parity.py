@@ -205,21 +205,24 @@ def test_decode_forward_lut_shared_sigmoid(moe, monkeypatch):
     _check_decode(moe, synth.get_config("kimi_linear", H=2048, I=2048, E=64, tokens=2, layers=2), method="lookup")
 
 
-def _streamed_setup(moe, cfg, capacity):
+def _streamed_setup(moe, cfg, capacity, pageable=False):
     from routed_expert_streaming_amd.device_workload import DeviceWorkload, HostRecordPool
     dw = DeviceWorkload(cfg)                       # resident copy: the reference for transparency
-    hp = HostRecordPool(cfg, list(range(cfg.layers)))
+    hp = HostRecordPool(cfg, list(range(cfg.layers)), pin_limit=0 if pageable else 52 << 30)
+    assert hp.pinned_records == (0 if pageable else cfg.layers * cfg.E)
     pool = torch.empty(capacity * hp.stride, dtype=torch.uint8, device="cuda")
     cache = moe.ExpertCache(capacity, hp.stride, pool)
     return dw, hp, cache
 
 
-@pytest.mark.parametrize("capacity", [16, 23, 40])
-def test_streamed_trace_and_transparency(moe, capacity):
+@pytest.mark.parametrize("capacity,pageable", [(16, False), (23, False), (40, False), (23, True)])
+def test_streamed_trace_and_transparency(moe, capacity, pageable):
     # K3 structure with fewer experts so that a few tokens exercise hits,
-    # misses and evictions at capacity == k and above
+    # misses and evictions at capacity == k and above; pageable: every record
+    # in pageable host memory (copied through the cache's pinned bounce
+    # buffers)
     cfg = synth.get_config("k3_slice", tokens=5, layers=2, E=48)
-    dw, hp, cache = _streamed_setup(moe, cfg, capacity)
+    dw, hp, cache = _streamed_setup(moe, cfg, capacity, pageable)
     x = dw.inputs()
     copy_stream = torch.cuda.Stream()
     outs, idxs = [], []
