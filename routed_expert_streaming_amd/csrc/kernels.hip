@@ -23,46 +23,70 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------- routing
-// z[t, e] = W[e] . x[t] + b[e].  One wave per expert row, 8 tokens per block.
+// z[t, e] = W[e] . x[t] + b[e].  One workgroup per expert row and 8 tokens:
+// its four waves take interleaved 256-column pieces of the row, four per step
+// (loads in flight together), and their sums are added in wave order.
 constexpr int kRouteTok = 8;
 
 __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ W, const float *__restrict__ bias,
                                                       int E, int H, const void *__restrict__ x, int x_dtype, int T,
                                                       float *__restrict__ z) {
+    __shared__ float red[4][kRouteTok];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + wave;
+    const int e = blockIdx.x;
     const int t0 = blockIdx.y * kRouteTok;
-    if (e >= E) return;
     const int nt = min(kRouteTok, T - t0);
     float acc[kRouteTok];
 #pragma unroll
     for (int i = 0; i < kRouteTok; i++) acc[i] = 0.f;
     const float *wr = W + (size_t)e * H;
-    for (int c = lane * 4; c < H; c += 256) {
-        const float4 wv = *(const float4 *)(wr + c);
+    // wave v takes the 256-column pieces v, v + 4, ... of the row, four per
+    // step (their loads in flight together)
+    constexpr int kPieces = 4;
+    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = wave * 256 + lane * 4; c0 < H; c0 += kPieces * 1024) {
+        float4 wv[kPieces];
+#pragma unroll
+        for (int u = 0; u < kPieces; u++) {
+            const int c = c0 + u * 1024;
+            wv[u] = c < H ? *(const float4 *)(wr + c) : zero4;
+        }
 #pragma unroll
         for (int i = 0; i < kRouteTok; i++) {
             if (i < nt) {
-                float4 xv;
-                if (x_dtype == MOE_DTYPE_F32) {
-                    xv = *(const float4 *)((const float *)x + (size_t)(t0 + i) * H + c);
-                } else {
-                    const uint2 b = *(const uint2 *)((const uint16_t *)x + (size_t)(t0 + i) * H + c);
-                    xv = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
-                                     __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+                float4 xv[kPieces];
+#pragma unroll
+                for (int u = 0; u < kPieces; u++) {
+                    const int c = c0 + u * 1024;
+                    if (c >= H) {
+                        xv[u] = zero4;
+                    } else if (x_dtype == MOE_DTYPE_F32) {
+                        xv[u] = *(const float4 *)((const float *)x + (size_t)(t0 + i) * H + c);
+                    } else {
+                        const uint2 b = *(const uint2 *)((const uint16_t *)x + (size_t)(t0 + i) * H + c);
+                        xv[u] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                                            __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+                    }
                 }
-                acc[i] = fmaf(wv.x, xv.x, acc[i]);
-                acc[i] = fmaf(wv.y, xv.y, acc[i]);
-                acc[i] = fmaf(wv.z, xv.z, acc[i]);
-                acc[i] = fmaf(wv.w, xv.w, acc[i]);
+#pragma unroll
+                for (int u = 0; u < kPieces; u++) {
+                    acc[i] = fmaf(wv[u].x, xv[u].x, acc[i]);
+                    acc[i] = fmaf(wv[u].y, xv[u].y, acc[i]);
+                    acc[i] = fmaf(wv[u].z, xv[u].z, acc[i]);
+                    acc[i] = fmaf(wv[u].w, xv[u].w, acc[i]);
+                }
             }
         }
     }
-    const float b = bias ? bias[e] : 0.f;
 #pragma unroll
     for (int i = 0; i < kRouteTok; i++) {
         const float s = wave_sum(acc[i]);
-        if (lane == 0 && i < nt) z[(size_t)(t0 + i) * E + e] = s + b;
+        if (lane == 0) red[wave][i] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) {
+        const int i = threadIdx.x;
+        z[(size_t)(t0 + i) * E + e] = ((red[0][i] + red[1][i]) + (red[2][i] + red[3][i])) + (bias ? bias[e] : 0.f);
     }
 }
 
@@ -144,48 +168,87 @@ __global__ __launch_bounds__(256) void k_route_reduce(const float *__restrict__ 
     }
 }
 
-// Top-k per token: one wave per token; k rounds of a wave-wide argmax on
-// (z desc, expert id asc); then softmax- or sigmoid-renormalised weights.
-constexpr int kMaxPerLane = MOE_MAX_E / 64;
+// Top-k per token, one 256-thread workgroup per token, by counting: the
+// rank of an expert is the number of experts ahead of it in (z desc, id asc)
+// order.  Each logit becomes a 64-bit key (order-preserving logit bits above
+// the inverted id; NaN ranks last, -0 and +0 tie), so a rank is a count of
+// larger keys and all ranks differ.  For E > 64 in two levels: ranks within
+// eighths of the experts first (whole 32-key blocks); the keys of local rank
+// below k (every global top-k key is one) are then ranked among themselves.
+// Weights: softmax over the selected logits, or sigmoid scores renormalised,
+// summed in rank order.
+constexpr int kTopkThreads = 256, kTopkLvl = 8;
+__device__ __forceinline__ uint32_t topk_order_key(float f) {
+    f = f == f ? f : -INFINITY;
+    uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float topk_key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
-__global__ __launch_bounds__(64) void k_topk(const float *__restrict__ z, int E, int k, int score_fn,
-                                             int32_t *__restrict__ idx, float *__restrict__ w) {
-    const int t = blockIdx.x, lane = threadIdx.x;
-    float v[kMaxPerLane];
+__global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__ z, int E, int k, int score_fn,
+                                                       int32_t *__restrict__ idx, float *__restrict__ w) {
+    __shared__ __align__(16) uint64_t key[MOE_MAX_E];              // padded to a multiple of 32 with zeros
+    __shared__ __align__(16) uint64_t cand[kTopkLvl * MOE_MAX_K];  // zeros past the candidates
+    __shared__ int ncand;
+    __shared__ int sidx[MOE_MAX_K];
+    __shared__ float sz[MOE_MAX_K];
+    const int t = blockIdx.x;
+    const int Ep = (E + 31) & ~31;
+    for (int e = threadIdx.x; e < Ep; e += kTopkThreads)
+        key[e] = e < E ? (uint64_t)topk_order_key(z[(size_t)t * E + e]) << 32 | (0xFFFFFFFFu - (uint32_t)e) : 0u;
+    for (int i = threadIdx.x; i < kTopkLvl * MOE_MAX_K; i += kTopkThreads) cand[i] = 0u;
+    if (threadIdx.x == 0) ncand = 0;
+    __syncthreads();
+    const bool two = E > 64;
+    const int gsz = two ? ((E + kTopkLvl - 1) / kTopkLvl + 31) & ~31 : Ep;
+    // rank of ke among list[q0, q1), 32 keys per step; stops once it reaches k
+    auto count_above = [&](const uint64_t *list, int q0, int q1, uint64_t ke) {
+        int r[4] = {0, 0, 0, 0};
+        for (; q0 < q1 && r[0] + r[1] + r[2] + r[3] < k; q0 += 32) {
+            uint64_t kv[32];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; i++) {
-        const int e = lane + 64 * i;
-        const float zz = e < E ? z[(size_t)t * E + e] : -INFINITY;
-        v[i] = zz == zz ? zz : -INFINITY;          // NaN ranks last
-    }
-    uint32_t taken = 0;                            // bit i: v[i] already selected
-    float zsel = 0.f, zmax = 0.f, sum = 0.f;
-    int esel = 0;
-    for (int j = 0; j < k; j++) {
-        // lane-local best among untaken experts: largest value, lowest id on ties
-        float bv = -INFINITY;
-        int be = 0x7FFFFFFF;
+            for (int i = 0; i < 32; i++) kv[i] = list[q0 + i];
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; i++) {
-            const int e = lane + 64 * i;
-            if (e < E && !(taken >> i & 1u) && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
+            for (int i = 0; i < 32; i++) r[i & 3] += kv[i] > ke;
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oe = __shfl_xor(be, o, 64);
-            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        return r[0] + r[1] + r[2] + r[3];
+    };
+    auto place = [&](int rank, uint64_t ke) {
+        sidx[rank] = (int)(0xFFFFFFFFu - (uint32_t)ke);
+        sz[rank] = topk_key_value((uint32_t)(ke >> 32));
+    };
+    for (int e = threadIdx.x; e < E; e += kTopkThreads) {
+        const uint64_t ke = key[e];
+        const int g0 = e / gsz * gsz;
+        const int rank = count_above(key, g0, min(Ep, g0 + gsz), ke);
+        if (rank < k) {
+            if (two) cand[atomicAdd(&ncand, 1)] = ke;
+            else place(rank, ke);
         }
-        // k <= E, so an untaken expert always exists and be < E
-        if (j == 0) zmax = bv;
-        const float s = score_fn == MOE_SCORE_SOFTMAX ? __expf(bv - zmax) : 1.f / (1.f + __expf(-bv));
-        sum += s;
-        if (lane == j) { zsel = s; esel = be; }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
     }
-    if (lane < k) {
-        idx[(size_t)t * k + lane] = esel;
-        w[(size_t)t * k + lane] = zsel / sum;
+    if (two) {
+        __syncthreads();
+        const int nc = ncand;
+        for (int c = threadIdx.x; c < nc; c += kTopkThreads) {
+            const uint64_t ke = cand[c];
+            const int rank = count_above(cand, 0, (nc + 31) & ~31, ke);
+            if (rank < k) place(rank, ke);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < k) {
+        const float zmax = sz[0];
+        float sum = 0.f, mine = 0.f;
+        for (int r = 0; r < k; r++) {
+            const float s = score_fn == MOE_SCORE_SOFTMAX ? __expf(sz[r] - zmax) : 1.f / (1.f + __expf(-sz[r]));
+            sum += s;
+            if (r == (int)threadIdx.x) mine = s;
+        }
+        idx[(size_t)t * k + threadIdx.x] = sidx[threadIdx.x];
+        w[(size_t)t * k + threadIdx.x] = mine / sum;
     }
 }
 
@@ -463,7 +526,7 @@ size_t down_lds() { return kCbRows * 16 + kDnWaves * 64 * sizeof(float); }
 // ----------------------------------------------------------------- launchers
 hipError_t launch_route_logits(const float *W, const float *bias, int E, int H, const void *x, int x_dtype,
                                int T, float *z, hipStream_t s) {
-    dim3 grid((E + 3) / 4, (T + kRouteTok - 1) / kRouteTok);
+    dim3 grid(E, (T + kRouteTok - 1) / kRouteTok);
     k_route_logits<<<grid, 256, 0, s>>>(W, bias, E, H, x, x_dtype, T, z);
     return hipGetLastError();
 }
@@ -493,7 +556,7 @@ hipError_t launch_route_blocked(const float *W, const float *bias, int E, int H,
 
 hipError_t launch_topk(const float *z, int E, int k, int score_fn, int T, int32_t *idx, float *w,
                        hipStream_t s) {
-    k_topk<<<T, 64, 0, s>>>(z, E, k, score_fn, idx, w);
+    k_topk<<<T, kTopkThreads, 0, s>>>(z, E, k, score_fn, idx, w);
     return hipGetLastError();
 }
 
