@@ -191,6 +191,12 @@ def test_decode_forward_mixtral_gathers(moe, monkeypatch):
     _check_decode(moe, synth.get_config("mixtral", tokens=1, layers=4), method="gathers")
 
 
+def test_decode_forward_lut_default_small(moe):
+    # table lookup chosen by the shape (I = 8192), not forced: 16 tiles per
+    # workgroup, 8 workgroups per segment, several tokens and layers
+    _check_decode(moe, synth.get_config("mixtral", H=1024, I=8192, E=4, tokens=3, layers=3), method="lookup")
+
+
 def test_decode_forward_lut_straddling_segments(moe, monkeypatch):
     # gate/up by table lookup forced at a shape whose default is gathers:
     # 4.5 tiles per workgroup, so ranges straddle segments (matrices, chunk
