@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # valid for the kernel source they were taken on: reported as null once that
 # source has changed.
 DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
-                  "sha256_prefix": "dc3dfc96ef5beb13", "bytes_per_launch": 5396026436}
+                  "sha256_prefix": "d4194d45d460f156", "bytes_per_launch": 5924152519}
 
 
 def measured_traffic():
@@ -276,10 +276,10 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if cfg.name == "mixtral" else None,
-                     "kernel": "k_decode_persistent (route, top-k, RVQ gate/up by %s, RVQ down, combine; all "
-                               "layers of one token per launch)" % (
-                                   "table lookup" if moe.decode_gate_up_method(dw.layers) == "lookup"
-                                   else "codebook gathers"),
+                     "kernel": "k_decode_persistent (route, top-k, RVQ gate/up by %s, RVQ down by %s, combine; "
+                               "all layers of one token per launch)" % tuple(
+                                   "table lookup" if m == "lookup" else "codebook gathers"
+                                   for m in (moe.decode_gate_up_method(dw.layers), moe.decode_down_method(dw.layers))),
                      "algorithmic_bytes_per_launch": bytes_tok},
         "device": torch.cuda.get_device_name(0),
         "commit": git_commit(),

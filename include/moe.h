@@ -217,10 +217,18 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
  * products of the RVQ weights (WASTE article, section "유휴 가중치는 메모리가
  * 아니라 제때 닿기만 하면 된다": weights never expanded); the kernel picks
  * table lookup where each table serves many rows (I >= 8192), and the
- * environment variable MOE_DECODE_LUT=0 or 1 overrides where the shape allows.
+ * environment variable MOE_DECODE_LUT (0 gathers, 1 table lookup for gate/up
+ * and down, 2 table lookup for gate/up only) overrides where the shape allows.
  * Host-only query; needs a device (reads its compute-unit count).
  *   layers [host] as for moe_decode_forward;  method: 0 or 1 */
 int moe_decode_gate_up_method(const moe_layer *layers, int32_t n_layers, int32_t *method);
+
+/* The same for the down projection (same source): 0 = codebook-row gathers,
+ * 1 = table lookup, one table per (rank, 128-column chunk of I) built from
+ * that chunk of the SwiGLU intermediate h and serving all H rows.  Chosen
+ * with gate/up's table lookup by default (I >= 8192).
+ *   layers [host] as for moe_decode_forward;  method: 0 or 1 */
+int moe_decode_down_method(const moe_layer *layers, int32_t n_layers, int32_t *method);
 
 /* Whether the last moe_decode_forward that used this workspace hit its
  * device-side wait limit (a dependency between workgroups did not resolve

@@ -214,6 +214,15 @@ def decode_gate_up_method(layers: Sequence[Layer]) -> str:
     return "lookup" if m.value else "gathers"
 
 
+def decode_down_method(layers: Sequence[Layer]) -> str:
+    """"lookup" or "gathers": the down method decode_forward uses for these
+    layers on the current device."""
+    arr = _layer_array(layers)
+    m = ctypes.c_int32()
+    check(lib().moe_decode_down_method(arr, len(layers), ctypes.byref(m)), "moe_decode_down_method")
+    return "lookup" if m.value else "gathers"
+
+
 def decode_status(ws: torch.Tensor) -> bool:
     """True if the last decode_forward on this workspace hit its device-side
     wait limit (its outputs are then invalid).  Synchronises."""

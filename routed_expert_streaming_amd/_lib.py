@@ -55,6 +55,7 @@ SIGNATURES = {
     "moe_decode_forward": (ctypes.c_int, [ctypes.POINTER(MoeLayer), I32, P, I32, P, P, P, SZ, P]),
     "moe_decode_status": (ctypes.c_int, [P, ctypes.POINTER(I32)]),
     "moe_decode_gate_up_method": (ctypes.c_int, [P, I32, ctypes.POINTER(I32)]),
+    "moe_decode_down_method": (ctypes.c_int, [P, I32, ctypes.POINTER(I32)]),
     "moe_grouped_workspace_bytes": (SZ, [ctypes.POINTER(MoeLayer), I32]),
     "moe_layer_forward_grouped": (ctypes.c_int, [ctypes.POINTER(MoeLayer), P, I32, I32, P, P, P, P, SZ, P]),
     "expert_cache_create": (ctypes.c_int, [I32, U64, P, ctypes.POINTER(P)]),

@@ -575,8 +575,9 @@ __device__ __forceinline__ int fresh_lane() {
     return l;
 }
 
-// The table of chunk c (of the token's x in LDS) from the A fragments.
-__device__ __forceinline__ void lut_build(const f16x4 (&A)[kLutCbTiles], int c, int wave) {
+// The table of one chunk from the A fragments; the chunk's 128 x values
+// (fp32) are at LDS byte xo.
+__device__ __forceinline__ void lut_build(const f16x4 (&A)[kLutCbTiles], int xo, int wave) {
     const int lane = fresh_lane();
     const int n = lane & 15, g = lane >> 4;
     const bool valid = (g >> 1) == (n >> 3);
@@ -585,7 +586,7 @@ __device__ __forceinline__ void lut_build(const f16x4 (&A)[kLutCbTiles], int c, 
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
         const float4 xv =
-            *(const float4 *)(dec_lds + kLutX + 4 * (kChunkCols * c + 64 * hf + 8 * (n & 7) + 4 * (g & 1)));
+            *(const float4 *)(dec_lds + xo + 4 * (64 * hf + 8 * (n & 7) + 4 * (g & 1)));
         bh[hf].x = (_Float16)xv.x; bh[hf].y = (_Float16)xv.y; bh[hf].z = (_Float16)xv.z; bh[hf].w = (_Float16)xv.w;
         bl[hf].x = (_Float16)(xv.x - (float)bh[hf].x);
         bl[hf].y = (_Float16)(xv.y - (float)bh[hf].y);
@@ -623,22 +624,26 @@ __device__ __forceinline__ void lut_build(const f16x4 (&A)[kLutCbTiles], int c, 
     }
 }
 
-// One segment of the table-lookup gate/up space: matrix m (codes at codes,
-// codebook at cb) of one expert, chunk c, row tiles [ta, ta + nt).  One
-// table build, then the waves stream the tiles through register rings (no
-// barriers) and store each tile's sum over the chunk as a tagged partial at
-// part + 128 * cprH * tile (slot c of the tile; the caller adds the rank's
-// base, the slot and the matrix's half).  Wave v's first kLutRing - 1 tiles
-// are v, v + kPW, ...; after that each wave takes the next tile from a
-// workgroup counter in LDS, so waves that run ahead take more tiles.  A tile
-// is always summed whole by one wave, so the result does not depend on which.
+// One segment of a table-lookup space: one matrix (codes at codes, codebook
+// at cb, cpr chunks per row tile) of one expert, chunk c, row tiles
+// [ta, ta + nt).  One table build, then the waves stream the tiles through
+// register rings (no barriers) and store each tile's sum over the chunk as a
+// tagged partial at part + tstride * tile (the caller's part points at the
+// segment's slot).  Wave v's first kLutRing - 1 tiles are v, v + kPW, ...;
+// after that each wave takes the next tile from a workgroup counter in LDS,
+// so waves that run ahead take more tiles.  A tile is always summed whole by
+// one wave, so the result does not depend on which.  pre() runs once the
+// first code loads are in flight and before the build reads the chunk's x
+// at LDS byte xo (down waits for h and stages its chunk there); it returns
+// false if its wait failed, and so does the segment.
 __device__ __forceinline__ int lut_next_tile(unsigned *ctr, int lane) {
     unsigned v = 0;
     if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return (int)__builtin_amdgcn_readfirstlane(v);
 }
-__device__ __forceinline__ void stream_gateup_lut(const u32x4 *codes, const u32x4 *cb, int cprH, int c, int ta,
-                                                  int nt, uint64_t *part, unsigned tag, int wave, int lane) {
+template <class Pre>
+__device__ __forceinline__ bool stream_lut(const u32x4 *codes, const u32x4 *cb, int cpr, int c, int xo, int ta, int nt,
+                                           uint64_t *part, int tstride, unsigned tag, int wave, int lane, Pre pre) {
     gu32x4 *gb = (gu32x4 *)codes;
     unsigned *ctr = (unsigned *)(dec_lds + kDecCtr);
     // the A fragments first: the build waits for them alone, tile by tile,
@@ -652,7 +657,7 @@ __device__ __forceinline__ void stream_gateup_lut(const u32x4 *codes, const u32x
         for (int t = 0; t < kLutCbTiles; t++) A[t] = src[t * 64];
     }
     // tiles past the segment load its last tile (never consumed)
-    auto unit_addr = [&](int t) { return (ta + min(t, nt - 1)) * cprH + c; };
+    auto unit_addr = [&](int t) { return (ta + min(t, nt - 1)) * cpr + c; };
     uint32_t buf[kLutRing][12];
     int tile[kLutRing];
 #pragma unroll
@@ -660,9 +665,10 @@ __device__ __forceinline__ void stream_gateup_lut(const u32x4 *codes, const u32x
         tile[r] = wave + kPW * r;
         load_codes(gb, unit_addr(tile[r]), lane, buf[r]);
     }
+    if (!pre()) return false;
     lds_sync();                    // the previous table's readers and counter users are done
     if (threadIdx.x == 0) *ctr = kPW * (kLutRing - 1);
-    lut_build(A, c, wave);
+    lut_build(A, xo, wave);
     lds_sync();
     // a wave's tiles only grow, so once one is past the segment, all later ones are
     for (;;) {
@@ -671,10 +677,11 @@ __device__ __forceinline__ void stream_gateup_lut(const u32x4 *codes, const u32x
             const int nr = (r + kLutRing - 1) % kLutRing;
             tile[nr] = lut_next_tile(ctr, lane);
             load_codes(gb, unit_addr(tile[nr]), lane, buf[nr]);
-            if (tile[r] < nt) st_tagged(part + (size_t)(ta + tile[r]) * 128 * cprH + lane, lut_strip(buf[r]), tag);
+            if (tile[r] < nt) st_tagged(part + (size_t)(ta + tile[r]) * tstride + lane, lut_strip(buf[r]), tag);
         }
         if (tile[kLutRing - 1] >= nt) break;
     }
+    return true;
 }
 
 // Workgroup whose down range holds the last unit of output tile td in the
@@ -747,6 +754,91 @@ __device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k,
     return true;
 }
 
+// Output rows [16 sl, 16 sl + 16) for the table-lookup down, by the whole
+// workgroup (H / 16 such slices spread over all workgroups, so each reads a
+// 16th of a tile's partials: one 128-byte line per (rank, chunk)).  Lane l
+// takes row 16 sl + l % 16 of the partials p = 4 (v + 8 q) + l / 16 (wave v,
+// p = rank cprI + chunk, every load of a wave in flight together; polls after
+// the first reload only the words still missing) and weights them by
+// fj[rank][l % 16] = w_j s_j[row] (gate weight times row scale, in LDS, filled
+// by the caller before the barrier below).  The four lanes of a row, then the
+// waves in order, are added; wave 0 adds the shared output, writes the rows
+// and counts the slice on the layer-done counter.  Returns false on a failed
+// wait (the same on every wave).
+constexpr int kSliceRows = 16;
+template <int NB>
+__device__ __forceinline__ bool combine_slice_lut(int sl, int s, unsigned tag, int k, int tilesH, int cprI, int H,
+                                                  bool shared_on, const uint64_t *part_d, const uint64_t *ysh,
+                                                  float *out, const float *fj, unsigned *sync, int *bcast, int wave,
+                                                  int lane) {
+    float *jr = (float *)(dec_lds + kLutX + 512 + MOE_MAX_K * kSliceRows * 4);   // [kPW][16] the waves' sums
+    const int rr = lane & (kSliceRows - 1), pq = lane >> 4;
+    const int r = sl * kSliceRows + rr, td = r / kTileRows;
+    const int np = k * cprI;
+    float acc = 0.f;
+    long spins = 0;
+    bool ok = true;
+    lds_sync();                              // fj is complete
+    for (int p0 = 4 * wave + pq; __any(p0 < np) && ok; p0 += NB * 4 * kPW) {
+        uint64_t v[NB];
+        const uint64_t *pa[NB];
+        int jq[NB];
+#pragma unroll
+        for (int q = 0; q < NB; q++) {
+            const int p = min(p0 + q * 4 * kPW, np - 1);
+            jq[q] = p / cprI;
+            pa[q] = part_d + (((size_t)jq[q] * tilesH + td) * cprI + (p - jq[q] * cprI)) * 64 + (r & 63);
+            v[q] = ld_tagged(pa[q]);
+        }
+        for (;;) {
+            bool all = true;
+#pragma unroll
+            for (int q = 0; q < NB; q++) all = all && tag_ok(v[q], tag);
+            if (__all(all)) break;
+            if (!poll_more(sync, spins)) { ok = false; break; }
+#pragma unroll
+            for (int q = 0; q < NB; q++)
+                if (!tag_ok(v[q], tag)) v[q] = ld_tagged(pa[q]);
+        }
+        if (!ok) break;
+#pragma unroll
+        for (int q = 0; q < NB; q++)
+            if (p0 + q * 4 * kPW < np) acc = fmaf(fj[jq[q] * kSliceRows + rr], tag_val(v[q]), acc);
+    }
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    if (lane < kSliceRows) jr[wave * kSliceRows + lane] = acc;
+    if (!ok && lane == 0) *bcast = 0;
+    lds_sync();
+    if (!*bcast) return false;
+    if (wave == 0) {
+        float o = 0.f;
+#pragma unroll
+        for (int v = 0; v < kPW; v++) o += jr[v * kSliceRows + rr];
+        bool oks = true;
+        if (shared_on) {
+            uint64_t vs;
+            for (;;) {
+                vs = ld_tagged(ysh + r);
+                if (__all(tag_ok(vs, tag))) break;
+                if (!poll_more(sync, spins)) { oks = false; break; }
+            }
+            o += tag_val(vs);
+        }
+        if (oks) {
+            if (lane < kSliceRows) out[(size_t)s * H + r] = o;
+            // counted at once: nothing in this launch reads the outputs
+            if (lane == 0)
+                __hip_atomic_fetch_add(sync + kLayerDone + (sl % kLayerCopies) * kLine, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        } else if (lane == 0) {
+            *bcast = 0;
+        }
+    }
+    lds_sync();
+    return *bcast != 0;
+}
+
 struct DecArgs {
     const DecLayer *layers;  // [nL] in device memory
     int nL, T, H, I, k, E_max, G;
@@ -758,14 +850,16 @@ struct DecArgs {
     unsigned *sync;          // counters
     uint64_t *z;             // [E_max] tagged logits
     uint16_t *hh;            // [k][I] fp16 h per rank
+    uint64_t *hq;            // [k][I] tagged fp32 h per rank (down by table lookup)
     float *hs;               // [I] shared h
     uint64_t *ysh;           // [H] tagged shared y
     uint64_t *part_gu;       // [k*tilesI][slots_gu][128] tagged
     uint64_t *part_d;        // [k*tilesH][slots_d][64] tagged
     int slots_gu, slots_d;
     int slots_red_gu, slots_red_d;   // tiles one workgroup's range can touch (LDS sum slots)
-    int lut;                 // gate/up by table lookup: 1, else 0 (part_gu then has
-                             // H / 128 slots per tile, one per chunk)
+    int lut;                 // kLutGateUp | kLutDown: the phases done by table lookup
+                             // (part_gu, part_d then have one slot per chunk of
+                             // H, I)
     unsigned long long *stamps;   // optional phase timestamps [steps][G][kDecStamps], or null
     int stamp_steps;
 };
@@ -814,7 +908,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // fixed during the launch): the chosen experts' loads can start right
         // after top-k
         for (int e = threadIdx.x; e < E; e += kPW * 64) recs_all[e] = (uint64_t)lay.records[e];
-        if (s > 0 && !wg_wait<kLayerCopies>(sync, sync + kLayerDone, (unsigned)s * tilesH, bcast)) return;
+        // output units per step: 64-row tiles, or 16-row slices (down by table lookup)
+        if (s > 0 && !wg_wait<kLayerCopies>(sync, sync + kLayerDone,
+                                            (unsigned)s * ((a.lut & kLutDown) ? H / kSliceRows : tilesH), bcast))
+            return;
         if (s == 0) lds_sync();
         mark(kStampLayerWait);
 
@@ -850,7 +947,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     const int cu = c + u * kPiece;
-                    if (cu < H && a.lut) {
+                    if (cu < H && (a.lut & kLutGateUp)) {
                         *(float4 *)(lds + kLutX + 4 * cu) = xv[u];   // fp32, for the table builds
                     } else if (cu < H) {
                         xl[cu / 2] = pack_f16x2(xv[u].x, xv[u].y);
@@ -1079,7 +1176,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         lds_sync();
         mark(kStampRouted);
 
-        if (a.lut) {
+        if (a.lut & kLutGateUp) {
             // ---- gate/up by table lookup over this workgroup's range of the
             // (rank, matrix, chunk, tile) space, one segment (fixed rank,
             // matrix and chunk) at a time; each tile's sum over the chunk goes
@@ -1096,9 +1193,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 const int c = seg % cprH, m = (seg / cprH) & 1, j = seg / (2 * cprH);
                 const uint8_t *rec = (const uint8_t *)recs[j];
                 const int ta = ua - seg * tilesI;
-                stream_gateup_lut((const u32x4 *)(rec + a.off.codes[m]), (const u32x4 *)(rec + a.off.cb[m]), cprH, c,
-                                  ta, ub - ua, a.part_gu + ((size_t)j * tilesI * cprH + c) * 128 + m * 64, tag, wave,
-                                  lane);
+                stream_lut((const u32x4 *)(rec + a.off.codes[m]), (const u32x4 *)(rec + a.off.cb[m]), cprH, c,
+                           kLutX + 4 * kChunkCols * c, ta, ub - ua,
+                           a.part_gu + ((size_t)j * tilesI * cprH + c) * 128 + m * 64, 128 * cprH, tag, wave, lane,
+                           [] { return true; });
                 ua = ub;
             }
             lds_sync();
@@ -1118,22 +1216,34 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 float gs[2] = {0.f, 0.f}, us[2] = {0.f, 0.f};
                 for (int s0 = wave; s0 < cprH && okj; s0 += 4 * kPW) {
                     uint64_t vg[2][4], vu[2][4];
+                    const uint64_t *pp[2][4];
                     long spins = 0;
+#pragma unroll
+                    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            const long tau = w + (long)G * (p0 + min(tt, tn - 1));
+                            const int sl = min(s0 + q * kPW, cprH - 1);
+                            pp[tt][q] = a.part_gu + ((size_t)tau * cprH + sl) * 128 + lane;
+                            vg[tt][q] = ld_tagged(pp[tt][q]);
+                            vu[tt][q] = ld_tagged(pp[tt][q] + 64);
+                        }
+                    // later polls reload only the words still missing
                     for (;;) {
                         bool ok = true;
 #pragma unroll
                         for (int tt = 0; tt < 2; tt++)
 #pragma unroll
-                            for (int q = 0; q < 4; q++) {
-                                const long tau = w + (long)G * (p0 + min(tt, tn - 1));
-                                const int sl = min(s0 + q * kPW, cprH - 1);
-                                const uint64_t *pp = a.part_gu + ((size_t)tau * cprH + sl) * 128 + lane;
-                                vg[tt][q] = ld_tagged(pp);
-                                vu[tt][q] = ld_tagged(pp + 64);
-                                ok = ok && tag_ok(vg[tt][q], tag) && tag_ok(vu[tt][q], tag);
-                            }
+                            for (int q = 0; q < 4; q++) ok = ok && tag_ok(vg[tt][q], tag) && tag_ok(vu[tt][q], tag);
                         if (__all(ok)) break;
                         if (!poll_more(sync, spins)) { okj = false; break; }
+#pragma unroll
+                        for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+                            for (int q = 0; q < 4; q++) {
+                                if (!tag_ok(vg[tt][q], tag)) vg[tt][q] = ld_tagged(pp[tt][q]);
+                                if (!tag_ok(vu[tt][q], tag)) vu[tt][q] = ld_tagged(pp[tt][q] + 64);
+                            }
                     }
                     if (!okj) break;
 #pragma unroll
@@ -1164,23 +1274,34 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     }
                     g *= (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
                     uu *= (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
-                    const _Float16 hf = (_Float16)(g / (1.f + __expf(-g)) * uu);
-                    st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
+                    const float hv = g / (1.f + __expf(-g)) * uu;
+                    if (a.lut & kLutDown) {
+                        st_tagged(a.hq + (size_t)j * I + r, hv, tag);   // read per chunk by down
+                    } else {
+                        const _Float16 hf = (_Float16)hv;
+                        st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
+                    }
                 }
                 lds_sync();
             }
             if (lane == 0 && !okj) *bcast = 0;
-            wait_vm_all();
-            __syncthreads();
-            if (!*bcast) return;
-            if (threadIdx.x == 0)
+            if (a.lut & kLutDown) {
+                // h is tagged: no wait for the stores, no counter
+                lds_sync();
+                if (!*bcast) return;
+            } else {
+                wait_vm_all();
+                __syncthreads();
+                if (!*bcast) return;
+            }
+            if (threadIdx.x == 0 && !(a.lut & kLutDown))
                 for (long tau = w; tau < (long)k * tilesI; tau += G)
                     __hip_atomic_fetch_add(h_ready + (tau / tilesI) * kLine, 1u, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
         }
         // ---- gate/up over this workgroup's range of (rank, tile, chunk), one
         // expert segment at a time (a range spans at most two experts)
-        for (long ea = a.lut ? gu1 : gu0; ea < gu1;) {
+        for (long ea = (a.lut & kLutGateUp) ? gu1 : gu0; ea < gu1;) {
             const int j = (int)(ea / ((long)tilesI * cprH));
             const long eb = min(gu1, (long)(j + 1) * tilesI * cprH);
             const uint8_t *rec = (const uint8_t *)recs[j];
@@ -1310,6 +1431,76 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         }
 
         mark(kStampSharedDown);
+        if (a.lut & kLutDown) {
+            // ---- down by table lookup over this workgroup's range of the
+            // (rank, chunk of I, tile of H) space, one segment (fixed rank
+            // and chunk) at a time; each tile's sum over the chunk goes out
+            // as a tagged partial (slot = chunk).  A segment's table needs
+            // only its chunk's 128 values of the rank's h, polled as tagged
+            // words (no counter, no wait for the whole h).  Where every
+            // segment has a workgroup of its own, each takes one whole
+            // segment (one table build).
+            // (32-bit index math: the host allows this path only where
+            // nLd * G fits an int)
+            float *fj = (float *)(lds + kLutX + 512);   // [k][16] w_j s_j[row] of slice w (combined below)
+            const int nSl = H / kSliceRows;
+            auto fill_fj = [&](int sl) {
+                for (int i = threadIdx.x; i < k * kSliceRows; i += kPW * 64) {
+                    const int j = i / kSliceRows;
+                    fj[i] = sw[j] * (float)((const _Float16 *)((const uint8_t *)recs[j] +
+                                                               a.off.scales[2]))[sl * kSliceRows + i % kSliceRows];
+                }
+            };
+            if (w < nSl) fill_fj(w);
+            const int nLd = k * cprI * tilesH;
+            const int GaD = min(k * cprI, G);
+            const int l1 = w + 1 >= GaD ? nLd : nLd * (w + 1) / GaD;
+            for (int ua = w >= GaD ? nLd : nLd * w / GaD; ua < l1;) {
+                const int seg = ua / tilesH;
+                const int ub = min(l1, (seg + 1) * tilesH);
+                const int c = seg % cprI, j = seg / cprI;
+                const uint8_t *rec = (const uint8_t *)recs[j];
+                const uint64_t *hsrc = a.hq + (size_t)j * I + kChunkCols * c;
+                const bool ok = stream_lut(
+                    (const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]), cprI, c, kLutX,
+                    ua - seg * tilesH, ub - ua, a.part_d + ((size_t)j * tilesH * cprI + c) * 64, 64 * cprI, tag, wave,
+                    lane, [&] {
+                        // the chunk's h, as fp32 where the build reads x
+                        if (wave == 0) {
+                            uint64_t v0, v1;
+                            long spins = 0;
+                            bool okh = true;
+                            for (;;) {
+                                v0 = ld_tagged(hsrc + 2 * lane);
+                                v1 = ld_tagged(hsrc + 2 * lane + 1);
+                                if (__all(tag_ok(v0, tag) && tag_ok(v1, tag))) break;
+                                if (!poll_more(sync, spins)) { okh = false; break; }
+                            }
+                            *(float2 *)(lds + kLutX + 8 * lane) = make_float2(tag_val(v0), tag_val(v1));
+                            if (lane == 0) bcast[1] = okh;   // its own word: others may still read bcast[0]
+                        }
+                        lds_sync();
+                        mark(kStampDownStaged);
+                        return bcast[1] != 0;
+                    });
+                if (!ok) return;
+                ua = ub;
+            }
+            lds_sync();
+            mark(kStampDownLoop);
+            // ---- output slices w, w + G, ... (whole workgroup each)
+            for (int sl = w; sl < nSl; sl += G) {
+                if (sl != w) {
+                    lds_sync();
+                    fill_fj(sl);
+                }
+                if (!combine_slice_lut<8>(sl, s, tag, k, tilesH, cprI, H, shared_on, a.part_d, a.ysh, a.out, fj, sync,
+                                          bcast, wave, lane))
+                    return;
+            }
+            mark(kStampDownDone);
+            continue;
+        }
         // ---- down over this workgroup's range of (rank, tile of H, chunk),
         // one expert segment at a time: tagged partials per touched tile
         for (long ea = d0; ea < d1;) {
@@ -1450,11 +1641,16 @@ hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
     o->slots_red_d = max_tiles_per_range((long)k * tilesH, cprI, G);
     // Table lookup: a table costs about as much as streaming 4096 rows' groups
     // by gathers, so it pays when every table serves many more rows than that
-    // (by default I >= 8192 rows per gate/up matrix); x (fp32) must fit in LDS
-    // beside the table.
-    const bool lut_fits = lds_at_zero && H <= kLutMaxH && (long)k * 2 * cprH * tilesI * G < (1L << 31);
-    o->lut = lut_fits && (lut_mode == 1 || (lut_mode < 0 && I >= 2 * kCbRows)) ? 1 : 0;
-    if (o->lut) o->slots_gu = cprH;
+    // (by default where I >= 8192: a gate/up table serves I rows; a down
+    // table serves H rows, and by then the join that precedes down is
+    // already per chunk); gate/up's x (fp32) must fit in LDS beside the table.
+    const bool want = lut_mode > 0 || (lut_mode < 0 && I >= 2 * kCbRows);
+    const bool gu_fits = lds_at_zero && H <= kLutMaxH && (long)k * 2 * cprH * tilesI * G < (1L << 31);
+    // down by table lookup takes its h, per chunk, from gate/up's table-lookup joins
+    const bool d_fits = gu_fits && (long)k * cprI * tilesH * G < (1L << 31);
+    o->lut = (want && gu_fits ? kLutGateUp : 0) | (want && lut_mode != 2 && d_fits ? kLutDown : 0);
+    if (o->lut & kLutGateUp) o->slots_gu = cprH;
+    if (o->lut & kLutDown) o->slots_d = cprI;
     o->sync_words = kHReady + (size_t)(k + 1) * kLine;
     // LDS: both phases' layouts must fit below the routing tail
     const long red_gu = 2L * kCbRows * 16 + ((H * 2 + 255) & ~255) + (long)o->slots_red_gu * kPW * 128 * 4;
@@ -1493,6 +1689,7 @@ hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s) {
     a.sync = d.sync;
     a.z = d.z;
     a.hh = d.hh;
+    a.hq = d.hq;
     a.hs = d.hs;
     a.ysh = d.ysh;
     a.part_gu = d.part_gu;

@@ -286,6 +286,7 @@ struct DecodeWs {
     DecLayer *layers;
     uint64_t *z, *ysh, *part_gu, *part_d;
     uint16_t *hh;
+    uint64_t *hq;
     float *hs;
     unsigned long long *stamps;
     int stamp_steps;
@@ -300,11 +301,14 @@ int decode_stamp_steps() {
     return e ? std::max(0, atoi(e)) : 0;
 }
 
-// MOE_DECODE_LUT=0 or 1 forces the gate/up method of the decode kernel
-// (codebook gathers or table lookup); unset, the shape decides.
+// MOE_DECODE_LUT forces the decode kernel's methods: 0 codebook gathers, 1
+// table lookup for gate/up and down, 2 table lookup for gate/up only; unset,
+// the shape decides.
 int decode_lut_mode() {
     const char *e = getenv("MOE_DECODE_LUT");
-    return e && *e ? (atoi(e) ? 1 : 0) : -1;
+    if (!e || !*e) return -1;
+    const int v = atoi(e);
+    return v == 2 ? 2 : (v ? 1 : 0);
 }
 
 int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *D) {
@@ -334,6 +338,7 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
     D->ysh = c.take<uint64_t>((size_t)H);
     D->part_gu = c.take<uint64_t>((size_t)k * (I / 64) * D->slots_gu * 128);
     D->part_d = c.take<uint64_t>((size_t)k * (H / 64) * D->slots_d * 64);
+    D->hq = (D->lut & kLutDown) ? c.take<uint64_t>((size_t)k * I) : nullptr;
     D->clear_words = c.pos / 4;
     D->layers = c.take<DecLayer>(kDecMaxLayers);
     D->hh = c.take<uint16_t>((size_t)k * I);
@@ -387,6 +392,7 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
     d.layer_buf = D.layers;
     d.z = D.z;
     d.hh = D.hh;
+    d.hq = D.hq;
     d.hs = D.hs;
     d.ysh = D.ysh;
     d.part_gu = D.part_gu;
@@ -433,15 +439,23 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
     return MOE_OK;
 }
 
-int moe_decode_gate_up_method(const moe_layer *layers, int32_t n_layers, int32_t *method) {
+static int decode_method(const moe_layer *layers, int32_t n_layers, int32_t *method, int bit) {
     if (!layers || n_layers < 1 || !method) return fail(MOE_E_INVAL, "layers or method is NULL, or n_layers < 1");
     if (!dims_ok(layers[0].H, layers[0].I) || layers[0].router.k < 1)
         return fail(MOE_E_INVAL, "invalid layer shape");
     DecodeWs D;
     int rc = carve_decode(nullptr, layers, n_layers, &D);
     if (rc) return rc;
-    *method = D.lut;
+    *method = (D.lut & bit) ? 1 : 0;
     return MOE_OK;
+}
+
+int moe_decode_gate_up_method(const moe_layer *layers, int32_t n_layers, int32_t *method) {
+    return decode_method(layers, n_layers, method, kLutGateUp);
+}
+
+int moe_decode_down_method(const moe_layer *layers, int32_t n_layers, int32_t *method) {
+    return decode_method(layers, n_layers, method, kLutDown);
 }
 
 int moe_decode_status(const void *ws, int32_t *timed_out) {

@@ -103,6 +103,9 @@ struct DecLayer {
     int32_t E, k, score_fn, pad;
 };
 
+// Phases of the decode kernel done by table lookup (bits of DecodeLaunch::lut).
+constexpr int kLutGateUp = 1, kLutDown = 2;
+
 struct DecodeLaunch {
     DecLayer layers[kDecMaxLayers];
     int nL, T, H, I, k, E_max, G, has_shared;
@@ -116,10 +119,11 @@ struct DecodeLaunch {
     DecLayer *layer_buf;     // [kDecMaxLayers] device copy of the descriptors
     uint64_t *z, *ysh, *part_gu, *part_d;   // step-tagged exchange buffers
     uint16_t *hh;
+    uint64_t *hq;            // tagged fp32 h (down by table lookup), zeroed before the launch
     float *hs;
     int slots_gu, slots_d;
     int slots_red_gu, slots_red_d;
-    int lut;                 // gate/up by table lookup (decode_plan decides)
+    int lut;                 // kLutGateUp | kLutDown: phases by table lookup (decode_plan decides)
     unsigned long long *stamps;   // phase timestamps (profiling aid), or null
     int stamp_steps;
 };
@@ -128,12 +132,13 @@ struct DecodePlanOut {
     int G;                        // persistent workgroups (one per CU)
     int slots_gu, slots_d;        // most contributors to one tile's partial sums
     int slots_red_gu, slots_red_d;   // most tiles one workgroup touches per phase
-    int lut;                      // gate/up by table lookup: 1, by codebook gathers: 0
+    int lut;                      // kLutGateUp | kLutDown: the phases done by table lookup
     size_t sync_words;
     bool lds_ok;
 };
 // lut_mode: -1 = choose by shape, 0 = codebook gathers, 1 = table lookup
-// (o->lut = 0 if the shape does not allow it).
+// for gate/up and down, 2 = table lookup for gate/up only (a phase whose
+// shape does not allow it uses gathers).
 hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o);
 hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s);
 

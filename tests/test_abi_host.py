@@ -144,8 +144,9 @@ def test_hbm_read_validation(L):
     assert L.moe_hbm_read(ctypes.c_void_p(4096), 24, sink, None) == _lib.MOE_E_INVAL   # not a multiple of 16
 
 
-def test_decode_gate_up_method_rejects_bad_arguments(L):
+@pytest.mark.parametrize("fn", ["moe_decode_gate_up_method", "moe_decode_down_method"])
+def test_decode_method_queries_reject_bad_arguments(L, fn):
     m = ctypes.c_int32(-1)
-    assert L.moe_decode_gate_up_method(None, 1, ctypes.byref(m)) == -1
-    assert L.moe_decode_gate_up_method(None, 0, None) == -1
+    assert getattr(L, fn)(None, 1, ctypes.byref(m)) == -1
+    assert getattr(L, fn)(None, 0, None) == -1
     assert m.value == -1

@@ -129,15 +129,17 @@ def test_layer_parity_real_shapes(moe, name, T):
     torch.cuda.empty_cache()
 
 
-def _check_decode(moe, cfg, layers=None, sample=None, method=None):
+def _check_decode(moe, cfg, layers=None, sample=None, method=None, down=None):
     """Persistent decode kernel (one launch for all tokens x layers) against
     the oracle, layer call by layer call; also run-to-run determinism, the
-    device-side wait flag and (if given) the gate/up method in use."""
+    device-side wait flag and (if given) the gate/up and down methods in use."""
     from routed_expert_streaming_amd.device_workload import DeviceWorkload
     log(f"decode {cfg.name}: {cfg.tokens} tokens x {cfg.layers} layers, uploading")
     dw = DeviceWorkload(cfg)
     if method is not None:
         assert moe.decode_gate_up_method(dw.layers) == method
+    if down is not None:
+        assert moe.decode_down_method(dw.layers) == down
     x = dw.inputs()
     ws = torch.empty(moe.decode_workspace_bytes(dw.layers), dtype=torch.uint8, device="cuda")
     out, idx = moe.decode_forward(dw.layers, x, ws=ws)
@@ -181,20 +183,27 @@ def test_decode_forward_k3_shape_fewer_experts_per_token(moe, k):
 
 def test_decode_forward_mixtral_full_size(moe):
     # the configuration bench.py times: all 32 layers, 8 resident experts each
-    # (gate/up by table lookup, the default at I = 14336)
-    _check_decode(moe, synth.get_config("mixtral", tokens=2), method="lookup")
+    # (gate/up and down by table lookup, the default at I = 14336)
+    _check_decode(moe, synth.get_config("mixtral", tokens=2), method="lookup", down="lookup")
 
 
 def test_decode_forward_mixtral_gathers(moe, monkeypatch):
-    # the same shape with gate/up by codebook gathers
+    # the same shape with gate/up and down by codebook gathers
     monkeypatch.setenv("MOE_DECODE_LUT", "0")
-    _check_decode(moe, synth.get_config("mixtral", tokens=1, layers=4), method="gathers")
+    _check_decode(moe, synth.get_config("mixtral", tokens=1, layers=4), method="gathers", down="gathers")
+
+
+def test_decode_forward_mixtral_lookup_gate_up_only(moe, monkeypatch):
+    # gate/up by table lookup, down by codebook gathers
+    monkeypatch.setenv("MOE_DECODE_LUT", "2")
+    _check_decode(moe, synth.get_config("mixtral", tokens=1, layers=4), method="lookup", down="gathers")
 
 
 def test_decode_forward_lut_default_small(moe):
     # table lookup chosen by the shape (I = 8192), not forced: 16 tiles per
     # workgroup, 8 workgroups per segment, several tokens and layers
-    _check_decode(moe, synth.get_config("mixtral", H=1024, I=8192, E=4, tokens=3, layers=3), method="lookup")
+    _check_decode(moe, synth.get_config("mixtral", H=1024, I=8192, E=4, tokens=3, layers=3), method="lookup",
+                  down="lookup")
 
 
 def test_decode_forward_lut_straddling_segments(moe, monkeypatch):
@@ -202,13 +211,23 @@ def test_decode_forward_lut_straddling_segments(moe, monkeypatch):
     # 4.5 tiles per workgroup, so ranges straddle segments (matrices, chunk
     # groups, experts) and most waves have no tile
     monkeypatch.setenv("MOE_DECODE_LUT", "1")
-    _check_decode(moe, synth.get_config("mixtral", H=2048, I=3072, k=3, tokens=2, layers=2), method="lookup")
+    _check_decode(moe, synth.get_config("mixtral", H=2048, I=3072, k=3, tokens=2, layers=2), method="lookup",
+                  down="lookup")
+
+
+def test_decode_forward_lut_down_straddling_segments(moe):
+    # down by table lookup with more (rank, chunk) segments (8 x 64) than
+    # workgroups: 8 tiles per workgroup, so most ranges span two segments
+    # and each combine polls 512 partials per row over several round trips
+    _check_decode(moe, synth.get_config("mixtral", H=256, I=8192, E=16, k=8, tokens=2, layers=2), method="lookup",
+                  down="lookup")
 
 
 def test_decode_forward_lut_shared_sigmoid(moe, monkeypatch):
     # forced table lookup with a shared expert, sigmoid top-8 and Zipf bias
     monkeypatch.setenv("MOE_DECODE_LUT", "1")
-    _check_decode(moe, synth.get_config("kimi_linear", H=2048, I=2048, E=64, tokens=2, layers=2), method="lookup")
+    _check_decode(moe, synth.get_config("kimi_linear", H=2048, I=2048, E=64, tokens=2, layers=2), method="lookup",
+                  down="lookup")
 
 
 def _streamed_setup(moe, cfg, capacity, pageable=False):
