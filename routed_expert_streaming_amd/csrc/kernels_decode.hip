@@ -20,7 +20,12 @@
 //   down             the (rank, 64-row tile of H, chunk) space likewise,
 //                    after the rank's h is complete; the last contributor of
 //                    an output tile combines sum_j w_j y_j + shared in fixed
-//                    (rank, contributor) order and counts the tile as done
+//                    (rank, contributor) order and counts the tile as done.
+//                    Where gate/up and down go by table lookup (many rows per
+//                    codebook), down's space is (rank, chunk, tile), each
+//                    segment waits only for its chunk of h (tagged words),
+//                    and 16-row output slices over all workgroups combine
+//                    the per-chunk partials
 // The next step's routing starts when every output tile of this step is done.
 // Counters only grow within a launch (targets are multiples of the step
 // index), are zeroed before the launch, and every wait is bounded: on
@@ -1442,16 +1447,16 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // segment (one table build).
             // (32-bit index math: the host allows this path only where
             // nLd * G fits an int)
-            float *fj = (float *)(lds + kLutX + 512);   // [k][16] w_j s_j[row] of slice w (combined below)
+            // fj [k][16] (k 16 <= 512: one entry per thread): w_j s_j[row] of slice w, combined below
+            float *fj = (float *)(lds + kLutX + 512);
             const int nSl = H / kSliceRows;
-            auto fill_fj = [&](int sl) {
-                for (int i = threadIdx.x; i < k * kSliceRows; i += kPW * 64) {
-                    const int j = i / kSliceRows;
-                    fj[i] = sw[j] * (float)((const _Float16 *)((const uint8_t *)recs[j] +
-                                                               a.off.scales[2]))[sl * kSliceRows + i % kSliceRows];
-                }
+            auto scale_of = [&](int sl) -> _Float16 {
+                const int j = threadIdx.x / kSliceRows;
+                return ((const _Float16 *)((const uint8_t *)recs[j] + a.off.scales[2]))[sl * kSliceRows +
+                                                                                        threadIdx.x % kSliceRows];
             };
-            if (w < nSl) fill_fj(w);
+            const bool fj_entry = threadIdx.x < k * kSliceRows;
+            bool fj_done = w >= nSl;
             const int nLd = k * cprI * tilesH;
             const int GaD = min(k * cprI, G);
             const int l1 = w + 1 >= GaD ? nLd : nLd * (w + 1) / GaD;
@@ -1465,6 +1470,11 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     (const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]), cprI, c, kLutX,
                     ua - seg * tilesH, ub - ua, a.part_d + ((size_t)j * tilesH * cprI + c) * 64, 64 * cprI, tag, wave,
                     lane, [&] {
+                        // the first segment also loads slice w's row scales: issued here,
+                        // after the A fragments and the code rings, stored after the poll
+                        const bool fill = !fj_done && fj_entry;
+                        _Float16 sv = (_Float16)0.f;
+                        if (fill) sv = scale_of(w);
                         // the chunk's h, as fp32 where the build reads x
                         if (wave == 0) {
                             uint64_t v0, v1;
@@ -1479,6 +1489,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                             *(float2 *)(lds + kLutX + 8 * lane) = make_float2(tag_val(v0), tag_val(v1));
                             if (lane == 0) bcast[1] = okh;   // its own word: others may still read bcast[0]
                         }
+                        if (fill) fj[threadIdx.x] = sw[threadIdx.x / kSliceRows] * (float)sv;
+                        fj_done = true;
                         lds_sync();
                         mark(kStampDownStaged);
                         return bcast[1] != 0;
@@ -1490,9 +1502,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             mark(kStampDownLoop);
             // ---- output slices w, w + G, ... (whole workgroup each)
             for (int sl = w; sl < nSl; sl += G) {
-                if (sl != w) {
-                    lds_sync();
-                    fill_fj(sl);
+                if (sl != w || !fj_done) {
+                    if (sl != w) lds_sync();
+                    if (fj_entry) fj[threadIdx.x] = sw[threadIdx.x / kSliceRows] * (float)scale_of(sl);
+                    fj_done = true;
                 }
                 if (!combine_slice_lut<8>(sl, s, tag, k, tilesH, cprI, H, shared_on, a.part_d, a.ysh, a.out, fj, sync,
                                           bcast, wave, lane))
