@@ -223,6 +223,14 @@ def test_decode_forward_lut_down_straddling_segments(moe):
                   down="lookup")
 
 
+def test_decode_forward_lut_forced_k3_shape(moe, monkeypatch):
+    # forced table lookup at the K3 slice shape (H 5120, I 2048, top-16 of
+    # 768, shared expert): 320 output slices for 256 workgroups, so some
+    # workgroups combine two slices
+    monkeypatch.setenv("MOE_DECODE_LUT", "1")
+    _check_decode(moe, synth.get_config("k3_slice", tokens=1, layers=2), method="lookup", down="lookup")
+
+
 def test_decode_forward_lut_shared_sigmoid(moe, monkeypatch):
     # forced table lookup with a shared expert, sigmoid top-8 and Zipf bias
     monkeypatch.setenv("MOE_DECODE_LUT", "1")
