@@ -648,7 +648,8 @@ __device__ __forceinline__ int lut_next_tile(unsigned *ctr, int lane) {
 }
 template <class Pre>
 __device__ __forceinline__ bool stream_lut(const u32x4 *codes, const u32x4 *cb, int cpr, int c, int xo, int ta, int nt,
-                                           uint64_t *part, int tstride, unsigned tag, int wave, int lane, Pre pre) {
+                                           uint64_t *part, int tstride, unsigned tag, int wave, int lane, Pre pre,
+                                           unsigned long long *built = nullptr) {
     gu32x4 *gb = (gu32x4 *)codes;
     unsigned *ctr = (unsigned *)(dec_lds + kDecCtr);
     // the A fragments first: the build waits for them alone, tile by tile,
@@ -675,6 +676,7 @@ __device__ __forceinline__ bool stream_lut(const u32x4 *codes, const u32x4 *cb, 
     if (threadIdx.x == 0) *ctr = kPW * (kLutRing - 1);
     lut_build(A, xo, wave);
     lds_sync();
+    if (built && threadIdx.x == 0) *built = wall_clock64();   // profiling stamp: the table is ready
     // a wave's tiles only grow, so once one is past the segment, all later ones are
     for (;;) {
 #pragma unroll
@@ -1201,7 +1203,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 stream_lut((const u32x4 *)(rec + a.off.codes[m]), (const u32x4 *)(rec + a.off.cb[m]), cprH, c,
                            kLutX + 4 * kChunkCols * c, ta, ub - ua,
                            a.part_gu + ((size_t)j * tilesI * cprH + c) * 128 + m * 64, 128 * cprH, tag, wave, lane,
-                           [] { return true; });
+                           [] { return true; }, stamp ? stamp + kStampGuStaged : nullptr);
                 ua = ub;
             }
             lds_sync();

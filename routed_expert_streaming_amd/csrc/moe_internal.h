@@ -85,7 +85,7 @@ enum DecStamp {
     kStampStart,        // step begins
     kStampLayerWait,    // previous step's outputs all written
     kStampRouted,       // top-k known
-    kStampGuStaged,     // gate/up codebooks and x in LDS (last segment)
+    kStampGuStaged,     // gate/up codebooks and x in LDS, or its lookup table built (last segment)
     kStampGuLoop,       // gate/up streaming done (last segment)
     kStampGuDone,       // gate/up partials joined
     kStampSharedDown,   // shared-expert down rows done
