@@ -144,6 +144,25 @@ __device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
 __device__ __forceinline__ bool tag_ok(uint64_t v, unsigned tag) { return (unsigned)(v >> 32) == tag; }
 __device__ __forceinline__ float tag_val(uint64_t v) { return __uint_as_float((unsigned)v); }
 
+// Row-pair words of the table-lookup phases' partials: rows l and l + 32 of
+// a tile in one 64-bit word, each as the top 24 bits of its fp32 value
+// (rounded to nearest: 15 mantissa bits, relative error <= 2^-16), with a
+// 16-bit step tag, (step mod 65535) + 1, in bits 48..63, so a tile's
+// partial is 32 words where it was 64.  Every word of these buffers is
+// rewritten each step, so consecutive steps' tags always differ.
+__device__ __forceinline__ unsigned tag16(int s) { return (unsigned)(s % 65535) + 1u; }
+__device__ __forceinline__ uint64_t f24(float v) { return (uint64_t)((__float_as_uint(v) + 0x80u) >> 8); }
+// lane l < 32 stores rows l and l + 32 (the value of lane l + 32 comes across)
+__device__ __forceinline__ void st_pair(uint64_t *p, float v, unsigned tag, int lane) {
+    const float hi = __shfl_down(v, 32, 64);
+    if (lane < 32) st_x(p + lane, f24(v) | (f24(hi) << 24) | ((uint64_t)tag << 48));
+}
+__device__ __forceinline__ bool pair_ok(uint64_t v, unsigned tag) { return (unsigned)(v >> 48) == tag; }
+// the value of row lane (0..63) from the word of rows lane % 32, lane % 32 + 32
+__device__ __forceinline__ float pair_val(uint64_t v, int lane) {
+    return __uint_as_float((unsigned)(lane < 32 ? v : v >> 24) << 8);
+}
+
 // Wave-level bound on a poll loop: false (and the error flag set) after too
 // many polls, or once another workgroup has failed.
 __device__ __forceinline__ bool poll_more(unsigned *sync, long &spins) {
@@ -633,8 +652,8 @@ __device__ __forceinline__ void lut_build(const f16x4 (&A)[kLutCbTiles], int xo,
 // at cb, cpr chunks per row tile) of one expert, chunk c, row tiles
 // [ta, ta + nt).  One table build, then the waves stream the tiles through
 // register rings (no barriers) and store each tile's sum over the chunk as a
-// tagged partial at part + tstride * tile (the caller's part points at the
-// segment's slot).  Wave v's first kLutRing - 1 tiles are v, v + kPW, ...;
+// row-pair partial at part + tstride * tile (the caller's part points at the
+// segment's slot; tag: tag16 of the step).  Wave v's first kLutRing - 1 tiles are v, v + kPW, ...;
 // after that each wave takes the next tile from a workgroup counter in LDS,
 // so waves that run ahead take more tiles.  A tile is always summed whole by
 // one wave, so the result does not depend on which.  pre() runs once the
@@ -684,7 +703,7 @@ __device__ __forceinline__ bool stream_lut(const u32x4 *codes, const u32x4 *cb, 
             const int nr = (r + kLutRing - 1) % kLutRing;
             tile[nr] = lut_next_tile(ctr, lane);
             load_codes(gb, unit_addr(tile[nr]), lane, buf[nr]);
-            if (tile[r] < nt) st_tagged(part + (size_t)(ta + tile[r]) * tstride + lane, lut_strip(buf[r]), tag);
+            if (tile[r] < nt) st_pair(part + (size_t)(ta + tile[r]) * tstride, lut_strip(buf[r]), tag, lane);
         }
         if (tile[kLutRing - 1] >= nt) break;
     }
@@ -782,6 +801,7 @@ __device__ __forceinline__ bool combine_slice_lut(int sl, int s, unsigned tag, i
     const int rr = lane & (kSliceRows - 1), pq = lane >> 4;
     const int r = sl * kSliceRows + rr, td = r / kTileRows;
     const int np = k * cprI;
+    const unsigned t16 = tag16(s);
     float acc = 0.f;
     long spins = 0;
     bool ok = true;
@@ -794,23 +814,23 @@ __device__ __forceinline__ bool combine_slice_lut(int sl, int s, unsigned tag, i
         for (int q = 0; q < NB; q++) {
             const int p = min(p0 + q * 4 * kPW, np - 1);
             jq[q] = p / cprI;
-            pa[q] = part_d + (((size_t)jq[q] * tilesH + td) * cprI + (p - jq[q] * cprI)) * 64 + (r & 63);
+            pa[q] = part_d + (((size_t)jq[q] * tilesH + td) * cprI + (p - jq[q] * cprI)) * 32 + (r & 31);
             v[q] = ld_tagged(pa[q]);
         }
         for (;;) {
             bool all = true;
 #pragma unroll
-            for (int q = 0; q < NB; q++) all = all && tag_ok(v[q], tag);
+            for (int q = 0; q < NB; q++) all = all && pair_ok(v[q], t16);
             if (__all(all)) break;
             if (!poll_more(sync, spins)) { ok = false; break; }
 #pragma unroll
             for (int q = 0; q < NB; q++)
-                if (!tag_ok(v[q], tag)) v[q] = ld_tagged(pa[q]);
+                if (!pair_ok(v[q], t16)) v[q] = ld_tagged(pa[q]);
         }
         if (!ok) break;
 #pragma unroll
         for (int q = 0; q < NB; q++)
-            if (p0 + q * 4 * kPW < np) acc = fmaf(fj[jq[q] * kSliceRows + rr], tag_val(v[q]), acc);
+            if (p0 + q * 4 * kPW < np) acc = fmaf(fj[jq[q] * kSliceRows + rr], pair_val(v[q], r & 63), acc);
     }
     acc += __shfl_xor(acc, 16, 64);
     acc += __shfl_xor(acc, 32, 64);
@@ -1202,7 +1222,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 const int ta = ua - seg * tilesI;
                 stream_lut((const u32x4 *)(rec + a.off.codes[m]), (const u32x4 *)(rec + a.off.cb[m]), cprH, c,
                            kLutX + 4 * kChunkCols * c, ta, ub - ua,
-                           a.part_gu + ((size_t)j * tilesI * cprH + c) * 128 + m * 64, 128 * cprH, tag, wave, lane,
+                           a.part_gu + ((size_t)j * tilesI * cprH + c) * 64 + m * 32, 64 * cprH, tag16(s), wave, lane,
                            [] { return true; }, stamp ? stamp + kStampGuStaged : nullptr);
                 ua = ub;
             }
@@ -1215,6 +1235,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // and wave tt adds them in wave order for tile tt, scales, and
             // writes fp16 SiLU(g) * u.
             bool okj = true;
+            const unsigned t16 = tag16(s);
             const long nTau = (long)k * tilesI;
             const int nT = w < nTau ? (int)((nTau - 1 - w) / G) + 1 : 0;
             float *jred = (float *)lds;     // [2][kPW][128], table area (free now)
@@ -1231,9 +1252,9 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                         for (int q = 0; q < 4; q++) {
                             const long tau = w + (long)G * (p0 + min(tt, tn - 1));
                             const int sl = min(s0 + q * kPW, cprH - 1);
-                            pp[tt][q] = a.part_gu + ((size_t)tau * cprH + sl) * 128 + lane;
+                            pp[tt][q] = a.part_gu + ((size_t)tau * cprH + sl) * 64 + (lane & 31);
                             vg[tt][q] = ld_tagged(pp[tt][q]);
-                            vu[tt][q] = ld_tagged(pp[tt][q] + 64);
+                            vu[tt][q] = ld_tagged(pp[tt][q] + 32);
                         }
                     // later polls reload only the words still missing
                     for (;;) {
@@ -1241,15 +1262,15 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
                         for (int tt = 0; tt < 2; tt++)
 #pragma unroll
-                            for (int q = 0; q < 4; q++) ok = ok && tag_ok(vg[tt][q], tag) && tag_ok(vu[tt][q], tag);
+                            for (int q = 0; q < 4; q++) ok = ok && pair_ok(vg[tt][q], t16) && pair_ok(vu[tt][q], t16);
                         if (__all(ok)) break;
                         if (!poll_more(sync, spins)) { okj = false; break; }
 #pragma unroll
                         for (int tt = 0; tt < 2; tt++)
 #pragma unroll
                             for (int q = 0; q < 4; q++) {
-                                if (!tag_ok(vg[tt][q], tag)) vg[tt][q] = ld_tagged(pp[tt][q]);
-                                if (!tag_ok(vu[tt][q], tag)) vu[tt][q] = ld_tagged(pp[tt][q] + 64);
+                                if (!pair_ok(vg[tt][q], t16)) vg[tt][q] = ld_tagged(pp[tt][q]);
+                                if (!pair_ok(vu[tt][q], t16)) vu[tt][q] = ld_tagged(pp[tt][q] + 32);
                             }
                     }
                     if (!okj) break;
@@ -1258,8 +1279,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
                         for (int q = 0; q < 4; q++)
                             if (s0 + q * kPW < cprH) {
-                                gs[tt] += tag_val(vg[tt][q]);
-                                us[tt] += tag_val(vu[tt][q]);
+                                gs[tt] += pair_val(vg[tt][q], lane);
+                                us[tt] += pair_val(vu[tt][q], lane);
                             }
                 }
 #pragma unroll
@@ -1470,7 +1491,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 const uint64_t *hsrc = a.hq + (size_t)j * I + kChunkCols * c;
                 const bool ok = stream_lut(
                     (const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]), cprI, c, kLutX,
-                    ua - seg * tilesH, ub - ua, a.part_d + ((size_t)j * tilesH * cprI + c) * 64, 64 * cprI, tag, wave,
+                    ua - seg * tilesH, ub - ua, a.part_d + ((size_t)j * tilesH * cprI + c) * 32, 32 * cprI, tag16(s), wave,
                     lane, [&] {
                         // the first segment also loads slice w's row scales: issued here,
                         // after the A fragments and the code rings, stored after the poll
