@@ -880,8 +880,8 @@ struct DecArgs {
     uint64_t *hq;            // [k][I] tagged fp32 h per rank (down by table lookup)
     float *hs;               // [I] shared h
     uint64_t *ysh;           // [H] tagged shared y
-    uint64_t *part_gu;       // [k*tilesI][slots_gu][128] tagged
-    uint64_t *part_d;        // [k*tilesH][slots_d][64] tagged
+    uint64_t *part_gu;       // [k*tilesI][slots_gu][128] tagged ([64] row pairs by table lookup)
+    uint64_t *part_d;        // [k*tilesH][slots_d][64] tagged ([32] row pairs by table lookup)
     int slots_gu, slots_d;
     int slots_red_gu, slots_red_d;   // tiles one workgroup's range can touch (LDS sum slots)
     int lut;                 // kLutGateUp | kLutDown: the phases done by table lookup

@@ -336,8 +336,9 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
     D->sync = c.take<unsigned>(D->sync_words);
     D->z = c.take<uint64_t>((size_t)E_max);
     D->ysh = c.take<uint64_t>((size_t)H);
-    D->part_gu = c.take<uint64_t>((size_t)k * (I / 64) * D->slots_gu * 128);
-    D->part_d = c.take<uint64_t>((size_t)k * (H / 64) * D->slots_d * 64);
+    // table-lookup partials pack two rows per word: half the words per tile
+    D->part_gu = c.take<uint64_t>((size_t)k * (I / 64) * D->slots_gu * ((D->lut & kLutGateUp) ? 64 : 128));
+    D->part_d = c.take<uint64_t>((size_t)k * (H / 64) * D->slots_d * ((D->lut & kLutDown) ? 32 : 64));
     D->hq = (D->lut & kLutDown) ? c.take<uint64_t>((size_t)k * I) : nullptr;
     D->clear_words = c.pos / 4;
     D->layers = c.take<DecLayer>(kDecMaxLayers);
