@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # valid for the kernel source they were taken on: reported as null once that
 # source has changed.
 DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
-                  "sha256_prefix": "f3a318bb4930694a", "bytes_per_launch": 5272241673}
+                  "sha256_prefix": "b0ab1ff55c2638e5", "bytes_per_launch": 5272291208}
 
 
 def measured_traffic():

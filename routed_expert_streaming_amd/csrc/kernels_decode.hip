@@ -1207,8 +1207,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // ---- gate/up by table lookup over this workgroup's range of the
             // (rank, matrix, chunk, tile) space, one segment (fixed rank,
             // matrix and chunk) at a time; each tile's sum over the chunk goes
-            // out as a tagged partial (slot = chunk; gate in words 0..63, up
-            // in 64..127)
+            // out as a row-pair partial (slot = chunk; gate in words 0..31, up
+            // in 32..63)
             // (32-bit index math: the host allows this path only where
             // nL * G fits an int)
             const int nL = k * 2 * cprH * tilesI;
@@ -1233,7 +1233,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // loads in flight together: one round trip once the partials have
             // landed) and sums them in slot order; the waves' sums meet in LDS,
             // and wave tt adds them in wave order for tile tt, scales, and
-            // writes fp16 SiLU(g) * u.
+            // writes SiLU(g) * u: fp16 for a gather down, else fp32 as
+            // step-tagged words (down by table lookup polls them per chunk).
             bool okj = true;
             const unsigned t16 = tag16(s);
             const long nTau = (long)k * tilesI;
@@ -1463,7 +1464,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // ---- down by table lookup over this workgroup's range of the
             // (rank, chunk of I, tile of H) space, one segment (fixed rank
             // and chunk) at a time; each tile's sum over the chunk goes out
-            // as a tagged partial (slot = chunk).  A segment's table needs
+            // as a row-pair partial (slot = chunk, 32 words).  A segment's table needs
             // only its chunk's 128 values of the rank's h, polled as tagged
             // words (no counter, no wait for the whole h).  Where every
             // segment has a workgroup of its own, each takes one whole
