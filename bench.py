@@ -121,7 +121,7 @@ def cpu_baseline(cfg, x_np, sample_tokens: int, one_thread_tokens: int = 1):
 
     import oracle
     import synth
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = len(os.sched_getaffinity(0))        # every CPU this process may run on
     oracle.set_threads(threads)
     wl = synth.Workload(cfg)
     # inputs of the oracle: records of the experts its own router selects
@@ -160,8 +160,11 @@ def cpu_baseline(cfg, x_np, sample_tokens: int, one_thread_tokens: int = 1):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64, help="timed decode tokens")
-    ap.add_argument("--warmup", type=int, default=2, help="untimed decode tokens")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 64 decode tokens; 64 batched calls; k3_slice: all 256 tokens "
+                         "of the workload, from a cold cache)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before them (default 2; k3_slice: 0, the cold start is the workload)")
     ap.add_argument("--config", default="mixtral", choices=["mixtral", "kimi_linear", "batched", "k3_slice"],
                     help="mixtral / kimi_linear: resident decode; batched: one 256-token grouped layer call "
                          "per step; k3_slice: streamed decode through the HBM slot cache (cold start)")
@@ -177,6 +180,10 @@ def main() -> int:
                     help="only run a plain device copy of MIB MiB three times (reference for the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 256 if args.config == "k3_slice" and not args.sweep else 64
+    if args.warmup is None:
+        args.warmup = 0 if args.config == "k3_slice" and not args.sweep else 2
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
               "see the sharding design notes.", file=sys.stderr)
@@ -237,6 +244,9 @@ def main() -> int:
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
+    if moe.decode_status(ws):
+        log("decode kernel hit its wait limit during warm-up: outputs invalid")
+        return 3
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -248,6 +258,9 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if moe.decode_status(ws):      # sticky over every launch since the warm-up check
+        log("decode kernel hit its wait limit in the timed steps: outputs invalid")
+        return 3
 
     tok_s = args.steps / elapsed
     bytes_tok = synth.expert_bytes_per_token(cfg)
@@ -281,6 +294,7 @@ def main() -> int:
                                    "table lookup" if m == "lookup" else "codebook gathers"
                                    for m in (moe.decode_gate_up_method(dw.layers), moe.decode_down_method(dw.layers))),
                      "algorithmic_bytes_per_launch": bytes_tok},
+        "decode_status": "ok (no wait limit reached in any launch)",
         "device": torch.cuda.get_device_name(0),
         "commit": git_commit(),
     }
@@ -292,6 +306,20 @@ def main() -> int:
         record["cpu_baseline"] = cpu_baseline(cfg, x.cpu().numpy(), args.cpu_sample_tokens)
     print(json.dumps(record), flush=True)
     return 0
+
+
+def teardown():
+    """After main() has returned (its tensors, caches and host tiers are
+    gone): wait for the device and release torch's cached device memory while
+    the runtime is whole, so that nothing is left to free at interpreter
+    exit."""
+    import gc
+    gc.collect()
+    if "torch" in sys.modules:
+        import torch
+        if torch.cuda.is_available() and torch.cuda.is_initialized():
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
 
 
 def bench_batched(args, cfg) -> int:
@@ -358,18 +386,22 @@ def _streamed_run(moe, cfg, layers, x, hp, tables, cap, warmup, steps):
     out = torch.empty((warmup + steps, cfg.layers, cfg.H), dtype=torch.float32, device="cuda")
     copy_stream = torch.cuda.Stream()
 
+    idx = torch.empty((warmup + steps, cfg.layers, cfg.k), dtype=torch.int32, device="cuda")
+
     def token(t):
         for L in range(cfg.layers):
             moe.layer_forward_streamed(layers[L], cache, L, None, x[t, L][None], copy_stream, ws=ws,
-                                       out=out[t, L][None], host_table=tables[L])
+                                       out=out[t, L][None], idx=idx[t, L][None], host_table=tables[L])
 
     for t in range(warmup):
         token(t)
     torch.cuda.synchronize()
     st0 = cache.stats()
     t_start = time.perf_counter()
+    ends = []
     for i in range(steps):
         token(warmup + i)
+        ends.append(time.perf_counter())   # each layer call waits for its routing, so this is near the GPU's end
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     st = cache.stats()
@@ -379,7 +411,8 @@ def _streamed_run(moe, cfg, layers, x, hp, tables, cap, warmup, steps):
     keys = np.array([r[0] for r in tr], dtype=np.uint32)
     hits = np.array([r[1] for r in tr], dtype=np.int32)
     misses_timed = (st["lookups"] - st0["lookups"]) - (st["hits"] - st0["hits"])
-    return {"elapsed": elapsed, "tok_s": steps / elapsed, "keys": keys, "hits": hits,
+    return {"elapsed": elapsed, "tok_s": steps / elapsed, "keys": keys, "hits": hits, "trace": tr,
+            "token_end_s": [e - t_start for e in ends], "idx": idx.cpu().numpy(),
             "timed_lookups": st["lookups"] - st0["lookups"], "timed_hits": st["hits"] - st0["hits"],
             "misses_timed": misses_timed}
 
@@ -421,30 +454,59 @@ def _cold_tier(cfg, hp):
 
 
 def bench_streamed(args, cfg) -> int:
-    """K3-scale slice: 8 layers x 768 experts in pinned host memory, a 25%
-    HBM slot cache (1536 slots) starting cold; one step = one token."""
+    """K3-scale slice as the workload defines it: 8 layers x 768 experts in
+    host memory, a 25% HBM slot cache (1536 slots) starting cold, 256 tokens
+    one at a time; by default every token is timed (the cold start is part of
+    the workload).  Reports tok/s over all timed tokens and over the second
+    half, the hit rate over all tokens and over the second half, the misses'
+    H2D rate, and whether the cache's whole trace equals the oracle's LRU
+    over the oracle's own routing (bit for bit)."""
+    import numpy as np
+
+    import oracle
     import synth
     n_tok = args.warmup + args.steps
-    if n_tok > cfg.tokens:
-        cfg = cfg.replace(tokens=n_tok)
+    cfg = cfg.replace(tokens=n_tok)
     moe, dw, x, hp, tables = _streamed_setup(cfg)
     cap = cfg.cache_capacity
     r = _streamed_run(moe, cfg, dw.layers, x, hp, tables, cap, args.warmup, args.steps)
     hits = r["hits"]
     per_tok = cfg.layers * cfg.k
-    half = (cfg.tokens // 2) * per_tok
+    half_tok = n_tok // 2
+    half = half_tok * per_tok
     tok_s = r["tok_s"]
+    ends = np.asarray(r["token_end_s"])
+    h0 = max(0, half_tok - args.warmup)               # first timed token of the second half
+    t_half0 = ends[h0 - 1] if h0 > 0 else 0.0
+    tok_s_second = (len(ends) - h0) / (ends[-1] - t_half0) if len(ends) > h0 else None
     hbm_bytes = synth.expert_bytes_per_token(cfg)
+    # the oracle's routing of every (token, layer) and its LRU over those keys
+    t0 = time.time()
+    x64 = x.cpu().numpy().astype(np.float64)
+    oidx = np.zeros((n_tok * cfg.layers, cfg.k), np.int32)
+    for L in range(cfg.layers):
+        oidx[L::cfg.layers] = oracle.route(dw.wl.router(L), dw.wl.bias(L), x64[:, L, :], cfg.k, cfg.score)[0]
+    key, ohit, oslot, oev = oracle.stream_trace(oidx, cfg.layers, cfg.E, cap)
+    tr = r["trace"]
+    trace_ok = (len(tr) == len(key) and [q[0] for q in tr] == key.tolist() and [q[1] for q in tr] == ohit.tolist()
+                and [q[2] for q in tr] == oslot.tolist()
+                and [(-1 if q[3] is None else q[3]) for q in tr] == oev.tolist())
+    routing_ok = bool(np.array_equal(np.sort(r["idx"].reshape(-1, cfg.k), 1), np.sort(oidx, 1)))
+    log(f"oracle routing and LRU trace in {time.time() - t0:.1f} s: trace equal {trace_ok}, routing equal "
+        f"{routing_ok}")
     peak = h2d_peak()
     rec = {"metric": "streamed MoE decode tok/s on 1 MI355X (HBM LRU slot cache, misses over PCIe)",
            "value": round(tok_s, 3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(r["elapsed"] * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32 accumulate, fp16 x RVQ-3bit weights", "data": "synthetic",
            "config": {"workload": f"k3_slice streamed decode: {cfg.layers} layers x {cfg.E} experts, H {cfg.H}, "
-                                  f"I {cfg.I}, top-{cfg.k} sigmoid + shared, Zipf bias, cache {cap} slots",
-                      "tokens": cfg.tokens},
+                                  f"I {cfg.I}, top-{cfg.k} sigmoid + shared, Zipf bias, cache {cap} slots, cold start",
+                      "tokens_decoded": n_tok, "tokens_timed": args.steps},
+           "tok_s_second_half": round(tok_s_second, 3) if tok_s_second else None,
            "hit_rate_all": round(float(hits.mean()), 4),
            "hit_rate_second_half": round(float(hits[half:].mean()), 4) if len(hits) > half else None,
+           "second_half_tokens": [half_tok, n_tok - 1],
+           "trace_equals_oracle": bool(trace_ok), "routing_equals_oracle": routing_ok,
            "misses_per_token_timed": round(r["misses_timed"] / args.steps, 2),
            "h2d_gbs": round(r["misses_timed"] * hp.stride / r["elapsed"] / 1e9, 2),
            "hbm_expert_gbs": round(hbm_bytes * tok_s / 1e9, 1),
@@ -453,7 +515,7 @@ def bench_streamed(args, cfg) -> int:
            "h2d_frac_of_pinned_peak": round(r["misses_timed"] * hp.stride / r["elapsed"] / 1e9 / peak, 4),
            "commit": git_commit()}
     print(json.dumps(rec), flush=True)
-    return 0
+    return 0 if trace_ok and routing_ok else 1
 
 
 def bench_sweep_capacity(args, cfg) -> int:
@@ -735,7 +797,5 @@ def bench_sweep_k(args, cfg) -> int:
 
 if __name__ == "__main__":
     rc = main()
-    # a successful run ends normally: leaving through SystemExit reorders the
-    # runtime's teardown so that rocprofv3 loses its results
-    if rc:
-        sys.exit(rc)
+    teardown()
+    sys.exit(rc)

@@ -65,6 +65,13 @@
  *  inside a tile, byte p of row l's 48-byte strip is at
  *  (p/16)*1024 + l*16 + p%16, and strip byte 3g+m is byte m (little-endian)
  *  of group 16j+g's code pair.
+ *  Numerics: products and sums are fp32; activations (x, and the SwiGLU
+ *  intermediate h) are rounded to fp16 for the GEMVs only after a
+ *  power-of-two scaling of their block, undone exactly after the fp32 sums,
+ *  so any finite fp32 activation is accepted.  The table-lookup decode
+ *  methods also store C[c] . x_q (8 terms) in fp16: codebook entries must be
+ *  below 16 in magnitude (RVQ codebooks are unit-scale; the row scales carry
+ *  the magnitude).
  * Shared expert (optional, always on, weight 1): dense bf16
  *   gate [I, H] | up [I, H] | down [H, I], row-major.
  */
@@ -230,10 +237,13 @@ int moe_decode_gate_up_method(const moe_layer *layers, int32_t n_layers, int32_t
  *   layers [host] as for moe_decode_forward;  method: 0 or 1 */
 int moe_decode_down_method(const moe_layer *layers, int32_t n_layers, int32_t *method);
 
-/* Whether the last moe_decode_forward that used this workspace hit its
+/* Whether any moe_decode_forward on this workspace since the previous
+ * moe_decode_status call (or since the workspace's first use) hit its
  * device-side wait limit (a dependency between workgroups did not resolve
- * within a few seconds; every wave then leaves the kernel and the outputs of
- * that call are invalid).  Synchronises with the device (reads one word).
+ * within a few seconds; every wave of that launch then leaves the kernel and
+ * the outputs of that call are invalid).  The status is sticky across
+ * launches and is reset by this call once read.  Synchronises the device
+ * (hipDeviceSynchronize), then reads one word.
  *   ws [dev] the workspace passed to moe_decode_forward;  timed_out: 0 or 1 */
 int moe_decode_status(const void *ws, int32_t *timed_out);
 

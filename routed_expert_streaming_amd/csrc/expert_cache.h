@@ -65,5 +65,7 @@ int cache_release(moe_cache *c, int32_t slot, hipStream_t s);
 // through the next bounce buffer, which host threads fill after its previous
 // copy has completed (the runtime's own staging of pageable copies reaches a
 // fraction of the link rate).
-hipError_t cache_copy_in(moe_cache *c, int32_t s, const void *src, hipStream_t ps);
+// *enqueued tells whether the copy into the slot was enqueued (then, even on
+// an error, the slot's previous contents are gone).
+hipError_t cache_copy_in(moe_cache *c, int32_t s, const void *src, hipStream_t ps, bool *enqueued);
 }  // namespace moe

@@ -119,9 +119,14 @@ void CopyPool::copy(void *dst, const void *src, size_t bytes) {
     done_.wait(l, [&] { return pending_ == 0; });
 }
 
-hipError_t cache_copy_in(moe_cache *c, int32_t s, const void *src, hipStream_t ps) {
+hipError_t cache_copy_in(moe_cache *c, int32_t s, const void *src, hipStream_t ps, bool *enqueued) {
     char *dst = c->pool + (size_t)s * c->slot_bytes;
-    if (page_locked(src)) return hipMemcpyAsync(dst, src, c->slot_bytes, hipMemcpyHostToDevice, ps);
+    *enqueued = false;
+    if (page_locked(src)) {
+        const hipError_t e = hipMemcpyAsync(dst, src, c->slot_bytes, hipMemcpyHostToDevice, ps);
+        *enqueued = e == hipSuccess;
+        return e;
+    }
     hipError_t e = hipSuccess;
     if (!c->copier) {
         for (int b = 0; e == hipSuccess && b < kBounce; b++) {
@@ -139,9 +144,18 @@ hipError_t cache_copy_in(moe_cache *c, int32_t s, const void *src, hipStream_t p
     c->bounce_used[b] = false;
     c->copier->copy(c->bounce[b], src, c->slot_bytes);
     e = hipMemcpyAsync(dst, c->bounce[b], c->slot_bytes, hipMemcpyHostToDevice, ps);
-    if (e == hipSuccess) e = hipEventRecord(c->bounce_done[b], ps);
-    c->bounce_used[b] = e == hipSuccess;
-    return e;
+    if (e != hipSuccess) return e;
+    *enqueued = true;
+    e = hipEventRecord(c->bounce_done[b], ps);
+    if (e != hipSuccess) {
+        // the buffer's transfer is in flight but cannot be waited on: drain
+        // the copy stream so that the buffer can be refilled safely
+        (void)hipStreamSynchronize(ps);
+        c->bounce_used[b] = false;
+        return e;
+    }
+    c->bounce_used[b] = true;
+    return hipSuccess;
 }
 }  // namespace moe
 
@@ -199,8 +213,18 @@ int expert_cache_insert(moe_cache *c, uint32_t key, const void *host_src, void *
     hipError_t e = hipSuccess;
     if (c->used[s]) e = hipStreamWaitEvent(cs, c->last_use[s], 0);      // readers of the victim first
     if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(last_use)");
-    e = moe::cache_copy_in(c, s, host_src, cs);
-    if (e != hipSuccess) return hip_fail(e, "copy into slot");    // nothing enqueued: cache unchanged
+    bool enqueued = false;
+    e = moe::cache_copy_in(c, s, host_src, cs, &enqueued);
+    if (e != hipSuccess) {
+        if (enqueued) {
+            // the slot's bytes are being overwritten: the victim it held is
+            // gone, so forget it and leave the slot free
+            c->core.drop_slot(s);
+            c->filled[s] = 0;
+        }
+        // otherwise nothing was enqueued: the cache is unchanged
+        return hip_fail(e, "copy into slot");
+    }
     e = hipEventRecord(c->ready[s], cs);
     if (e != hipSuccess) {
         // the copy is in flight but cannot be waited on: the slot no longer

@@ -13,7 +13,9 @@
 // Numerics: logits, accumulation and the combine are fp32.  The RVQ GEMVs
 // multiply the exact fp16 codebook entries by the input rounded to fp16
 // (v_dot2_f32_f16: exact products, fp32 accumulation); the SwiGLU
-// intermediate is rounded to fp16 before the down GEMV.
+// intermediate is kept in fp32 and rounded to fp16 when the down GEMV stages
+// it.  Each rounding to fp16 follows a power-of-two range scaling of its
+// block (range_exp), undone exactly after the fp32 sums.
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
@@ -252,34 +254,40 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
     }
 }
 
-// x -> fp16 pairs (one dword per two consecutive elements)
-__global__ __launch_bounds__(256) void k_pack_x(const void *__restrict__ x, int x_dtype, int T, int H,
-                                                int64_t x_stride, uint32_t *__restrict__ xh) {
+// x -> fp16 pairs (one dword per two consecutive elements), one workgroup
+// per token: the token's values are scaled by 2^-xexp[t] (xexp from the
+// largest |x_t|, range_exp) so that no pair overflows fp16; the gate/up sums
+// are scaled back by 2^xexp[t].
+__global__ __launch_bounds__(256) void k_pack_x(const void *__restrict__ x, int x_dtype, int H, int64_t x_stride,
+                                                uint32_t *__restrict__ xh, int32_t *__restrict__ xexp) {
+    __shared__ float wm[4];
+    const int t = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    auto val = [&](int c) -> float {
+        if (x_dtype == MOE_DTYPE_F32) return ((const float *)x + (size_t)t * x_stride)[c];
+        return bf16_to_f32(((const uint16_t *)x + (size_t)t * x_stride)[c]);
+    };
+    float m = 0.f;
+    for (int c = threadIdx.x; c < H; c += 256) m = fmaxf(m, fabsf(val(c)));
+    m = wave_max(m);
+    if (lane == 0) wm[wave] = m;
+    __syncthreads();
+    const int e = range_exp(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])));
     const int hp = H / 2;
-    const size_t n = (size_t)T * hp;
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const size_t t = i / hp, c = (i % hp) * 2;
-        float a, b;
-        if (x_dtype == MOE_DTYPE_F32) {
-            const float *xr = (const float *)x + t * x_stride;
-            a = xr[c]; b = xr[c + 1];
-        } else {
-            const uint16_t *xr = (const uint16_t *)x + t * x_stride;
-            a = bf16_to_f32(xr[c]); b = bf16_to_f32(xr[c + 1]);
-        }
-        xh[i] = pack_f16x2(a, b);
-    }
+    for (int p = threadIdx.x; p < hp; p += 256)
+        xh[(size_t)t * hp + p] = pack_f16x2(ldexpf(val(2 * p), -e), ldexpf(val(2 * p + 1), -e));
+    if (threadIdx.x == 0) xexp[t] = e;
 }
 
 // ------------------------------------------------------------- RVQ GEMVs
 // Gate/up: one workgroup per (item, 64-row tile); both codebooks staged in
 // LDS (128 KiB); lane = row, waves split the 128-column chunks; the input's
-// fp16 pairs are wave-uniform (scalar loads).  Output: fp16 SiLU(g) * u.
+// fp16 pairs are wave-uniform (scalar loads).  Output: fp32 SiLU(g) * u.
 constexpr int kGuWaves = 8;
 
 __global__ __launch_bounds__(kGuWaves * 64) void k_rvq_gateup(RecSrc src, RecOffsets off, int H, int I,
                                                               const uint32_t *__restrict__ xh,
-                                                              uint16_t *__restrict__ hh) {
+                                                              const int32_t *__restrict__ xexp,
+                                                              float *__restrict__ hh) {
     extern __shared__ __align__(16) char lds[];
     char *cbg = lds, *cbu = lds + kCbRows * 16;
     float *red = (float *)(lds + 2 * kCbRows * 16);      // [kGuWaves][2][64]
@@ -338,49 +346,66 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_rvq_gateup(RecSrc src, RecOff
         const int r = tile * kTileRows + lane;
         const _Float16 sg = ((const _Float16 *)(rec + off.scales[0]))[r];
         const _Float16 su = ((const _Float16 *)(rec + off.scales[1]))[r];
-        g *= (float)sg;
-        u *= (float)su;
-        const float h = g / (1.f + __expf(-g)) * u;
-        const _Float16 hf = (_Float16)h;
-        hh[(size_t)item * I + r] = __builtin_bit_cast(uint16_t, hf);
+        const int xe = xexp[t];
+        g = ldexpf(g, xe) * (float)sg;
+        u = ldexpf(u, xe) * (float)su;
+        hh[(size_t)item * I + r] = g / (1.f + __expf(-g)) * u;
     }
 }
 
 // Down: one workgroup per (item, 64-row tile of H, K-slice); down codebook in
-// LDS (64 KiB); writes s_d[r] * partial dot into ypart[item][ks][r].
+// LDS (64 KiB), then the slice's h (fp32) as fp16 pairs scaled by 2^-e (e
+// from the slice's largest |h|, range_exp); writes s_d[r] * 2^e * partial dot
+// into ypart[item][ks][r].
 constexpr int kDnWaves = 4;
 
 __global__ __launch_bounds__(kDnWaves * 64) void k_rvq_down(RecSrc src, RecOffsets off, int H, int I, int KS,
-                                                            const uint16_t *__restrict__ hh,
+                                                            const float *__restrict__ hh,
                                                             float *__restrict__ ypart) {
     extern __shared__ __align__(16) char lds[];
     char *cbd = lds;
     float *red = (float *)(lds + kCbRows * 16);           // [kDnWaves][64]
+    float *wm = red + kDnWaves * 64;                      // [kDnWaves]
+    uint32_t *xl = (uint32_t *)(wm + kDnWaves);           // the slice's h pairs
     const int tiles = H / kTileRows;
     const int ks = blockIdx.x % KS;
     const int tile = (blockIdx.x / KS) % tiles;
     const int local = blockIdx.x / (KS * tiles);
     int item;
     const uint8_t *rec = resolve_record(src, local, item);
-    {
-        const u32x4 *d = (const u32x4 *)(rec + off.cb[2]);
-        for (int i = threadIdx.x; i < kCbRows; i += kDnWaves * 64) ((u32x4 *)cbd)[i] = d[i];
-    }
-    __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int cpr = I / kChunkCols;
     const int c0 = (int)((int64_t)cpr * ks / KS), c1 = (int)((int64_t)cpr * (ks + 1) / KS);
+    const float *h = hh + (size_t)item * I + c0 * kChunkCols;
+    const int np = (c1 - c0) * kChunkCols / 2;
     const u32x4 *codes = (const u32x4 *)(rec + off.codes[2]) + (size_t)tile * cpr * kTileVec;
-    const uint32_t *x = (const uint32_t *)(hh + (size_t)item * I);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     int c = c0 + wave;
     uint32_t d[12];
-    if (c < c1) load_strip(codes + (size_t)c * kTileVec, lane, d);
+    if (c < c1) load_strip(codes + (size_t)c * kTileVec, lane, d);   // in flight during the staging
+    float m = 0.f;
+    {
+        const u32x4 *cbsrc = (const u32x4 *)(rec + off.cb[2]);
+        for (int i = threadIdx.x; i < kCbRows; i += kDnWaves * 64) ((u32x4 *)cbd)[i] = cbsrc[i];
+        for (int p = threadIdx.x; p < np; p += kDnWaves * 64) {
+            const float2 v = *(const float2 *)(h + 2 * p);
+            m = fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y)));
+        }
+        m = wave_max(m);
+        if (lane == 0) wm[wave] = m;
+    }
+    __syncthreads();
+    const int e = range_exp(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])));
+    for (int p = threadIdx.x; p < np; p += kDnWaves * 64) {
+        const float2 v = *(const float2 *)(h + 2 * p);
+        xl[p] = pack_f16x2(ldexpf(v.x, -e), ldexpf(v.y, -e));
+    }
+    __syncthreads();
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     while (c < c1) {
         const int cn = c + kDnWaves;
         uint32_t nd[12];
         if (cn < c1) load_strip(codes + (size_t)cn * kTileVec, lane, nd);
-        strip_dot<0>(d, cbd, x + c * 64, acc);
+        strip_dot<0>(d, cbd, xl + (c - c0) * 64, acc);
         if (cn < c1) {
 #pragma unroll
             for (int i = 0; i < 12; i++) d[i] = nd[i];
@@ -395,7 +420,7 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_rvq_down(RecSrc src, RecOffse
         for (int wv = 0; wv < kDnWaves; wv++) y += red[wv * 64 + lane];
         const int r = tile * kTileRows + lane;
         const _Float16 sd = ((const _Float16 *)(rec + off.scales[2]))[r];
-        ypart[((size_t)item * KS + ks) * H + r] = y * (float)sd;
+        ypart[((size_t)item * KS + ks) * H + r] = ldexpf(y, e) * (float)sd;
     }
 }
 
@@ -519,7 +544,12 @@ __global__ __launch_bounds__(256) void k_dense_down(const uint16_t *__restrict__
 }
 
 size_t gateup_lds() { return 2 * kCbRows * 16 + kGuWaves * 2 * 64 * sizeof(float); }
-size_t down_lds() { return kCbRows * 16 + kDnWaves * 64 * sizeof(float); }
+// codebook, wave sums, wave maxima, and the largest K-slice's h pairs
+size_t down_lds(int I, int KS) {
+    const int cpr = I / kChunkCols;
+    return kCbRows * 16 + (kDnWaves * 64 + kDnWaves) * sizeof(float) + (size_t)((cpr + KS - 1) / KS) * kChunkCols * 2;
+}
+constexpr int kMaxLds = 160 * 1024;
 
 }  // namespace
 
@@ -560,16 +590,15 @@ hipError_t launch_topk(const float *z, int E, int k, int score_fn, int T, int32_
     return hipGetLastError();
 }
 
-hipError_t launch_pack_x(const void *x, int x_dtype, int T, int H, int64_t x_stride, uint32_t *xh,
+hipError_t launch_pack_x(const void *x, int x_dtype, int T, int H, int64_t x_stride, uint32_t *xh, int32_t *xexp,
                          hipStream_t s) {
-    const size_t n = (size_t)T * H / 2;
-    const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
-    k_pack_x<<<grid, 256, 0, s>>>(x, x_dtype, T, H, x_stride, xh);
+    if (T == 0) return hipSuccess;
+    k_pack_x<<<T, 256, 0, s>>>(x, x_dtype, H, x_stride, xh, xexp);
     return hipGetLastError();
 }
 
 hipError_t launch_rvq_gateup(const RecSrc &src, const RecOffsets &off, int H, int I, int n_items,
-                             const uint32_t *xh, uint16_t *hh, hipStream_t s) {
+                             const uint32_t *xh, const int32_t *xexp, float *hh, hipStream_t s) {
     if (n_items == 0) return hipSuccess;
     static bool attr = false;
     if (!attr) {
@@ -579,7 +608,7 @@ hipError_t launch_rvq_gateup(const RecSrc &src, const RecOffsets &off, int H, in
         attr = true;
     }
     const int grid = n_items * (I / kTileRows);
-    k_rvq_gateup<<<grid, kGuWaves * 64, gateup_lds(), s>>>(src, off, H, I, xh, hh);
+    k_rvq_gateup<<<grid, kGuWaves * 64, gateup_lds(), s>>>(src, off, H, I, xh, xexp, hh);
     return hipGetLastError();
 }
 
@@ -593,17 +622,19 @@ int down_splits(int H, int I, int n_items) {
 }
 
 hipError_t launch_rvq_down(const RecSrc &src, const RecOffsets &off, int H, int I, int n_items, int KS,
-                           const uint16_t *hh, float *ypart, hipStream_t s) {
+                           const float *hh, float *ypart, hipStream_t s) {
     if (n_items == 0) return hipSuccess;
+    const size_t lds = down_lds(I, KS);
+    if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_rvq_down, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)down_lds());
+        hipError_t e =
+            hipFuncSetAttribute((const void *)k_rvq_down, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
         if (e != hipSuccess) return e;
         attr = true;
     }
     const int grid = n_items * (H / kTileRows) * KS;
-    k_rvq_down<<<grid, kDnWaves * 64, down_lds(), s>>>(src, off, H, I, KS, hh, ypart);
+    k_rvq_down<<<grid, kDnWaves * 64, lds, s>>>(src, off, H, I, KS, hh, ypart);
     return hipGetLastError();
 }
 

@@ -46,9 +46,20 @@ constexpr int kDecLdsBytes = 160 * 1024;
 // not contend with adders of another): the error flag, kLayerCopies
 // layer-done counters (output tile td adds to copy td % kLayerCopies; a
 // waiter sums them), then h_ready[j] for j = 0..k (k: the shared expert).
+// Word kErr is this launch's abort flag (zeroed before every launch, polled
+// by every wait); word kStatus, on the same line, keeps kStatusFailed from a
+// failed launch until the host reads and resets it, so a failure is seen
+// even when later launches on the workspace succeed.
 constexpr int kLine = 64;          // words per counter line
 constexpr int kLayerCopies = 8;
-enum SyncIdx { kErr = 0, kLayerDone = kLine, kHReady = kLine * (1 + kLayerCopies) };
+enum SyncIdx { kErr = 0, kStatus = 1, kLayerDone = kLine, kHReady = kLine * (1 + kLayerCopies) };
+
+// Mark this launch as failed: every wait then leaves, and the sticky status
+// records it.
+__device__ __forceinline__ void set_error(unsigned *sync) {
+    __hip_atomic_store(sync + kStatus, (unsigned)kDecodeStatusFailed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(sync + kErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Cross-workgroup data (logits, packed x, partial sums, h, shared-expert
 // vectors) is written and read with agent-scope relaxed atomic accesses,
@@ -114,7 +125,7 @@ __device__ __forceinline__ bool wg_wait(unsigned *sync, const unsigned *p, unsig
             if (err) { ok = 0; break; }
             __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
-                __hip_atomic_store(sync + kErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                set_error(sync);
                 ok = 0;
                 break;
             }
@@ -167,7 +178,7 @@ __device__ __forceinline__ float pair_val(uint64_t v, int lane) {
 // many polls, or once another workgroup has failed.
 __device__ __forceinline__ bool poll_more(unsigned *sync, long &spins) {
     if (++spins > kSpinLimit) {
-        __hip_atomic_store(sync + kErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        set_error(sync);
         return false;
     }
     if ((spins & 31) == 0 && ld_cnt(sync + kErr)) return false;
@@ -338,6 +349,7 @@ constexpr int kDecCtr = kDecLdsBytes - 4;   // the lookup phase's tile counter (
 constexpr int kRingGU = 3;      // code buffers per wave (2 units in flight ahead)
 constexpr int kShRows = 8;      // shared-expert rows per load group
 constexpr int kTopkScratch = 2048;   // LDS bytes (codebook area, free while routing): top-k staging
+constexpr int kXStage = 16 * 1024;   // LDS bytes (codebook area, free while routing): fp32 x for the gathers
 constexpr int kTopkGroups = 8;       // first-level groups of the top-k
 // zkey [MOE_MAX_E], candidates [kTopkGroups * MOE_MAX_K], logits in rank order [MOE_MAX_K], count
 constexpr int kTopkCount = kTopkScratch + 8 * (MOE_MAX_E + kTopkGroups * MOE_MAX_K) + 4 * MOE_MAX_K;
@@ -466,9 +478,9 @@ __device__ __forceinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *us
 // The first loads are issued before waiting for the expert's h (counter
 // h_ready >= h_target) and staging it with the codebook.  Returns 0 if the
 // wait failed.
-__device__ __forceinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_src, const uint32_t *h_src, unsigned *sync,
-                                        const unsigned *h_ready, unsigned h_target, int *bcast, int H, int I, int cpr,
-                                        int la, int lb, int t0, int nslots, int wave, int lane,
+__device__ __forceinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_src, const float *h_src, unsigned *sync,
+                                        const unsigned *h_ready, unsigned h_target, int *bcast, float *wmax, int &he,
+                                        int H, int I, int cpr, int la, int lb, int t0, int nslots, int wave, int lane,
                                         unsigned long long *stamp) {
     const DecLds L = dec_lds_layout(H, I);
     char *cb = dec_lds;
@@ -483,7 +495,43 @@ __device__ __forceinline__ int stream_down(const u32x4 *dsec, const u32x4 *cbd_s
     stage_lds<kLdsPlain>(cb, cbd_src, kCbRows * 16, wave, lane);
     for (int i = threadIdx.x; i < nslots * kPW * 64; i += kPW * 64) red[i] = 0.f;
     if (!wg_wait(sync, h_ready, h_target, bcast)) return 0;
-    stage_lds<kLdsCoherent>((char *)xl, h_src, I * 2, wave, lane);
+    // h (fp32, written by other workgroups) into LDS as fp16 pairs scaled by
+    // 2^-he (he from the largest |h|, the same in every workgroup); the
+    // partial sums are scaled back by 2^he.  Up to 4 pairs per thread stay
+    // in registers; a larger I reloads the rest for the conversion.
+    {
+        const uint64_t *hp = (const uint64_t *)h_src;
+        const int np = I / 2;
+        constexpr int kReg = 4, kStride = kPW * 64;
+        uint64_t hv[kReg];
+        float m = 0.f;
+        auto mag = [](uint64_t v) {
+            return fmaxf(fabsf(__uint_as_float((uint32_t)v)), fabsf(__uint_as_float((uint32_t)(v >> 32))));
+        };
+#pragma unroll
+        for (int i = 0; i < kReg; i++) {
+            const int p = threadIdx.x + i * kStride;
+            hv[i] = p < np ? ld_x(hp + p) : 0;
+            m = fmaxf(m, mag(hv[i]));
+        }
+        for (int p = threadIdx.x + kReg * kStride; p < np; p += kStride) m = fmaxf(m, mag(ld_x(hp + p)));
+        m = wave_max(m);
+        if (lane == 0) wmax[wave] = m;
+        lds_sync();
+        m = wmax[0];
+#pragma unroll
+        for (int v = 1; v < kPW; v++) m = fmaxf(m, wmax[v]);
+        he = __builtin_amdgcn_readfirstlane(range_exp(m));
+        auto pack = [&](uint64_t v) {
+            return pack_f16x2(ldexpf(__uint_as_float((uint32_t)v), -he), ldexpf(__uint_as_float((uint32_t)(v >> 32)), -he));
+        };
+#pragma unroll
+        for (int i = 0; i < kReg; i++) {
+            const int p = threadIdx.x + i * kStride;
+            if (p < np) xl[p] = pack(hv[i]);
+        }
+        for (int p = threadIdx.x + kReg * kStride; p < np; p += kStride) xl[p] = pack(ld_x(hp + p));
+    }
     wait_vm_all();
     __syncthreads();
     if (stamp && threadIdx.x == 0) stamp[kStampDownStaged] = wall_clock64();
@@ -601,16 +649,27 @@ __device__ __forceinline__ int fresh_lane() {
 
 // The table of one chunk from the A fragments; the chunk's 128 x values
 // (fp32) are at LDS byte xo.
-__device__ __forceinline__ void lut_build(const f16x4 (&A)[kLutCbTiles], int xo, int wave) {
+// Returns the chunk's exponent e: the table holds C[c].(x_q 2^-e) (range
+// scaling, so that no entry overflows fp16), and each sum over the chunk is
+// scaled back by 2^e.  Every wave reads all 128 values, so all find the same e.
+__device__ __forceinline__ int lut_build(const f16x4 (&A)[kLutCbTiles], int xo, int wave) {
     const int lane = fresh_lane();
     const int n = lane & 15, g = lane >> 4;
     const bool valid = (g >> 1) == (n >> 3);
     const f16x4 z4 = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
     f16x4 bh[2], bl[2];
+    float4 xr[2];
+    float m = 0.f;
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
-        const float4 xv =
-            *(const float4 *)(dec_lds + xo + 4 * (64 * hf + 8 * (n & 7) + 4 * (g & 1)));
+        xr[hf] = *(const float4 *)(dec_lds + xo + 4 * (64 * hf + 8 * (n & 7) + 4 * (g & 1)));
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(xr[hf].x), fabsf(xr[hf].y)), fmaxf(fabsf(xr[hf].z), fabsf(xr[hf].w))));
+    }
+    const int e = __builtin_amdgcn_readfirstlane(range_exp(wave_max(m)));
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+        const float4 xv = make_float4(ldexpf(xr[hf].x, -e), ldexpf(xr[hf].y, -e), ldexpf(xr[hf].z, -e),
+                                      ldexpf(xr[hf].w, -e));
         bh[hf].x = (_Float16)xv.x; bh[hf].y = (_Float16)xv.y; bh[hf].z = (_Float16)xv.z; bh[hf].w = (_Float16)xv.w;
         bl[hf].x = (_Float16)(xv.x - (float)bh[hf].x);
         bl[hf].y = (_Float16)(xv.y - (float)bh[hf].y);
@@ -646,6 +705,7 @@ __device__ __forceinline__ void lut_build(const f16x4 (&A)[kLutCbTiles], int xo,
                 *(f16x4 *)(dst + hf * 8 * kLutRowB + 64 * (t + u)) = o;
             }
     }
+    return e;
 }
 
 // One segment of a table-lookup space: one matrix (codes at codes, codebook
@@ -693,7 +753,7 @@ __device__ __forceinline__ bool stream_lut(const u32x4 *codes, const u32x4 *cb, 
     if (!pre()) return false;
     lds_sync();                    // the previous table's readers and counter users are done
     if (threadIdx.x == 0) *ctr = kPW * (kLutRing - 1);
-    lut_build(A, xo, wave);
+    const int e = lut_build(A, xo, wave);
     lds_sync();
     if (built && threadIdx.x == 0) *built = wall_clock64();   // profiling stamp: the table is ready
     // a wave's tiles only grow, so once one is past the segment, all later ones are
@@ -703,7 +763,8 @@ __device__ __forceinline__ bool stream_lut(const u32x4 *codes, const u32x4 *cb, 
             const int nr = (r + kLutRing - 1) % kLutRing;
             tile[nr] = lut_next_tile(ctr, lane);
             load_codes(gb, unit_addr(tile[nr]), lane, buf[nr]);
-            if (tile[r] < nt) st_pair(part + (size_t)(ta + tile[r]) * tstride, lut_strip(buf[r]), tag, lane);
+            if (tile[r] < nt)
+                st_pair(part + (size_t)(ta + tile[r]) * tstride, ldexpf(lut_strip(buf[r]), e), tag, lane);
         }
         if (tile[kLutRing - 1] >= nt) break;
     }
@@ -876,7 +937,7 @@ struct DecArgs {
     RecOffsets off;
     unsigned *sync;          // counters
     uint64_t *z;             // [E_max] tagged logits
-    uint16_t *hh;            // [k][I] fp16 h per rank
+    float *hh;               // [k][I] fp32 h per rank (gather down)
     uint64_t *hq;            // [k][I] tagged fp32 h per rank (down by table lookup)
     float *hs;               // [I] shared h
     uint64_t *ysh;           // [H] tagged shared y
@@ -901,6 +962,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
     int *bcast = (int *)(sw + MOE_MAX_K);                       // [4]
     float *red = (float *)(bcast + 4);                          // [kPW] router partials
     uint64_t *recs = (uint64_t *)(red + kPW);                   // [MOE_MAX_K] records of the chosen experts
+    float *lmax = (float *)(recs + MOE_MAX_K);                  // [kPW] the waves' largest magnitudes
     uint64_t *recs_all = (uint64_t *)(lds + kDecRecs);          // [E] until top-k
 
     const int G = a.G, w = blockIdx.x;
@@ -918,6 +980,21 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
     const int shI0 = (int)range_start(I, G, w), shI1 = (int)range_start(I, G, w + 1);
     const int shH0 = (int)range_start(H, G, w), shH1 = (int)range_start(H, G, w + 1);
     const unsigned sh_gu_contrib = (unsigned)min(G, I);          // workgroups with shared gate/up rows
+    // Whether this workgroup uses a step's routing result.  Which workgroups
+    // own gate/up units, joins, down units or output units depends only on
+    // the shape (workgroup w owns some of an n-unit space iff w < min(n, G)),
+    // never on the experts chosen.  A workgroup that owns none of them skips
+    // the logit poll: every workgroup that polls the step-tagged logits of
+    // step s owns work that the step-(s+1) layer-done barrier waits for, so
+    // no poller can still be reading step s's logits when they are retagged.
+    const bool routed = [&] {
+        const bool lg = a.lut & kLutGateUp, ld = a.lut & kLutDown;
+        const long gu_units = lg ? (long)k * 2 * cprH * tilesI : nGU;
+        const long join_units = lg ? (long)k * tilesI : 0;       // gather joins: owners of gate/up units
+        const long d_units = ld ? (long)k * cprI : nD;           // table-lookup down: (rank, chunk) segments
+        const long out_units = ld ? (long)(H / kSliceRows) : 0;  // gather combines: owners of down units
+        return w == 0 || w < gu_units || w < join_units || w < d_units || w < out_units;
+    }();
 
     unsigned long long *stamp = nullptr;
     auto mark = [&](int i) {
@@ -957,8 +1034,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // them in increasing m, the order of the row loop below (pieces past
         // H add fma(0, 0), as there)
         float acc_w = 0.f;
+        int xe = 0;                 // gather gate/up: x enters as fp16 pairs scaled by 2^-xe
         {
-            uint32_t *xl = (uint32_t *)(lds + LL.x_gu);
+            float *xst = (float *)(lds + kXStage);   // gathers: fp32 x, packed below once xe is known
+            float xm = 0.f;
             const bool row_w = w < nE;
             const float *wr = lay.W + (size_t)(row_w ? w : 0) * H;
             const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -977,8 +1056,9 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     if (cu < H && (a.lut & kLutGateUp)) {
                         *(float4 *)(lds + kLutX + 4 * cu) = xv[u];   // fp32, for the table builds
                     } else if (cu < H) {
-                        xl[cu / 2] = pack_f16x2(xv[u].x, xv[u].y);
-                        xl[cu / 2 + 1] = pack_f16x2(xv[u].z, xv[u].w);
+                        *(float4 *)(xst + cu) = xv[u];
+                        xm = fmaxf(xm, fmaxf(fmaxf(fabsf(xv[u].x), fabsf(xv[u].y)),
+                                             fmaxf(fabsf(xv[u].z), fabsf(xv[u].w))));
                     }
                     acc_w = fmaf(wv[u].x, xv[u].x, acc_w);
                     acc_w = fmaf(wv[u].y, xv[u].y, acc_w);
@@ -986,6 +1066,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     acc_w = fmaf(wv[u].w, xv[u].w, acc_w);
                 }
             }
+            xm = wave_max(xm);
+            if (lane == 0) lmax[wave] = xm;    // read after the logit poll's barrier
         }
 
         // ---- route: logits of rows e = w, w + G, ... (tagged, no counter)
@@ -1092,7 +1174,9 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // comparison orders by logit, then by lower id
         uint64_t *zkey = (uint64_t *)(lds + kTopkScratch);    // [E rounded up to 32]
         float *sz = (float *)(zkey + MOE_MAX_E + kTopkGroups * MOE_MAX_K);   // [MOE_MAX_K] logits in rank order
-        if (wave == 0) {
+        if (wave == 0 && !routed) {
+            if (lane == 0) *bcast = 1;
+        } else if (wave == 0) {
             long spins = 0;
             bool okw = true;
             for (;;) {
@@ -1118,6 +1202,20 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         }
         lds_sync();
         if (!*bcast) return;
+        if (!(a.lut & kLutGateUp)) {
+            // x as fp16 pairs for the gathers, scaled by 2^-xe (xe from the
+            // largest |x|, the same in every workgroup)
+            float m = lmax[0];
+#pragma unroll
+            for (int v = 1; v < kPW; v++) m = fmaxf(m, lmax[v]);
+            xe = __builtin_amdgcn_readfirstlane(range_exp(m));
+            const float *xst = (const float *)(lds + kXStage);
+            uint32_t *xl = (uint32_t *)(lds + LL.x_gu);
+            for (int p = threadIdx.x; p < H / 2; p += kPW * 64) {
+                const float2 v = *(const float2 *)(xst + 2 * p);
+                xl[p] = pack_f16x2(ldexpf(v.x, -xe), ldexpf(v.y, -xe));
+            }
+        }
         if (sh_rows) {
             shared_finish(shI0, 1);
             for (int r0 = shI0 + kShRows; r0 < shI1; r0 += kShRows) {
@@ -1127,7 +1225,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 shared_finish(r0, 0);
             }
         }
-        {
+        if (routed) {
             // Exact top-k by counting: a key's rank is the number of keys
             // above it (keys are unique: logit bits above the inverted id).
             // For E > 64 in two levels: each key is first ranked within its
@@ -1180,7 +1278,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             }
         }
         lds_sync();
-        if (wave == 0 && lane < lay.k) {
+        if (routed && wave == 0 && lane < lay.k) {
             const float zmax = sz[0];
             float sum = 0.f, mine = 0.f;
             for (int r = 0; r < lay.k; r++) {
@@ -1307,8 +1405,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     if (a.lut & kLutDown) {
                         st_tagged(a.hq + (size_t)j * I + r, hv, tag);   // read per chunk by down
                     } else {
-                        const _Float16 hf = (_Float16)hv;
-                        st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
+                        st_x(a.hh + (size_t)j * I + r, hv);
                     }
                 }
                 lds_sync();
@@ -1394,10 +1491,9 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                             uu += tag_val(vu[q]);
                         }
                 }
-                g *= sg;
-                uu *= su;
-                const _Float16 hf = (_Float16)(g / (1.f + __expf(-g)) * uu);
-                st_x(a.hh + (size_t)j * I + r, __builtin_bit_cast(uint16_t, hf));
+                g = ldexpf(g, xe) * sg;
+                uu = ldexpf(uu, xe) * su;
+                st_x(a.hh + (size_t)j * I + r, g / (1.f + __expf(-g)) * uu);
             }
             if (lane == 0 && !okj) *bcast = 0;
             wait_vm_all();
@@ -1545,9 +1641,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             const long eb = min(d1, (long)(j + 1) * tilesH * cprI);
             const uint8_t *rec = (const uint8_t *)recs[j];
             const long base = (long)j * tilesH * cprI;
+            int he = 0;
             if (!stream_down((const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]),
-                             (const uint32_t *)(a.hh + (size_t)j * I), sync, h_ready + j * kLine, (unsigned)(s + 1) * tilesI,
-                             bcast, H, I, cprI, (int)(ea - base), (int)(eb - base), (int)(ea / cprI - base / cprI),
+                             a.hh + (size_t)j * I, sync, h_ready + j * kLine, (unsigned)(s + 1) * tilesI, bcast, lmax,
+                             he, H, I, cprI, (int)(ea - base), (int)(eb - base), (int)(ea / cprI - base / cprI),
                              a.slots_red_d, wave, lane, stamp))
                 return;
             lds_sync();
@@ -1560,7 +1657,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
                 for (int q = 0; q < kPW; q++) y += red_d[(v * kPW + q) * 64 + lane];
                 const int r = (int)(tau % tilesH) * kTileRows + lane;
-                y *= (float)((const _Float16 *)(rec + a.off.scales[2]))[r];
+                y = ldexpf(y, he) * (float)((const _Float16 *)(rec + a.off.scales[2]))[r];
                 st_tagged(a.part_d + ((size_t)tau * a.slots_d + (w - range_owner(nD, G, tau * cprI))) * 64 + lane, y,
                           tag);
             }
@@ -1612,8 +1709,17 @@ __global__ void k_store_layers(LayerPack pack, DecLayer *dst) {
         if (l < pack.n) dst[l] = pack.layers[l];
 }
 
-__global__ void k_fill_u32(unsigned *p, size_t n) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+// Zeroes the counters and tagged buffers before a launch, except the sticky
+// status word, which keeps kDecodeStatusFailed and is set to
+// kDecodeStatusClean if it holds neither value (a workspace's first use).
+__global__ void k_decode_clear(unsigned *p, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        if (i != (size_t)kStatus) {
+            p[i] = 0;
+        } else if (p[i] != (unsigned)kDecodeStatusFailed) {
+            p[i] = (unsigned)kDecodeStatusClean;
+        }
+    }
 }
 
 size_t decode_lds() { return kDecLdsBytes; }
@@ -1693,14 +1799,15 @@ hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
     const long red_gu = 2L * kCbRows * 16 + ((H * 2 + 255) & ~255) + (long)o->slots_red_gu * kPW * 128 * 4;
     const long red_d = (long)kCbRows * 16 + ((I * 2 + 255) & ~255) + (long)o->slots_red_d * kPW * 64 * 4;
     // the shared expert's fp32 h is staged below the record pointers
-    o->lds_ok = red_gu <= kDecTail && red_d <= kDecTail && (long)I * 4 + kPW * kShRows * 4 <= kDecRecs;
+    o->lds_ok = red_gu <= kDecTail && red_d <= kDecTail && (long)I * 4 + kPW * kShRows * 4 <= kDecRecs &&
+                ((o->lut & kLutGateUp) || kXStage + (long)H * 4 <= 2L * kCbRows * 16);
     return hipSuccess;
 }
 
 hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s) {
     const int tilesI = d.I / kTileRows, tilesH = d.H / kTileRows;
     const unsigned fill_blocks = (unsigned)std::min<size_t>(1024, (d.clear_words + 255) / 256);
-    k_fill_u32<<<fill_blocks, 256, 0, s>>>(d.sync, d.clear_words);
+    k_decode_clear<<<fill_blocks, 256, 0, s>>>(d.sync, d.clear_words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     DecArgs a{};

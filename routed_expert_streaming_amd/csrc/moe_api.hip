@@ -96,7 +96,8 @@ LayerWs carve_layer(void *ws, int H, int I, int E, int k, int T, bool shared) {
     L.idx = c.take<int32_t>((size_t)T * k);
     L.w = c.take<float>((size_t)T * k);
     L.xh = c.take<uint32_t>((size_t)T * H / 2);
-    L.hh = c.take<uint16_t>((size_t)items * I);
+    L.xexp = c.take<int32_t>((size_t)T);
+    L.hh = c.take<float>((size_t)items * I);
     L.ypart = c.take<float>((size_t)items * KS * H);
     L.hs = shared ? c.take<float>((size_t)T * I) : nullptr;
     L.ysh = shared ? c.take<float>((size_t)T * H) : nullptr;
@@ -165,9 +166,9 @@ int run_experts(const moe_layer *L, const LayerWs &ws, const RecSrc &src, const 
     const int H = L->H, I = L->I, items = T * k;
     const RecOffsets off = offsets_of(H, I);
     const int KS = down_splits(H, I, items);
-    HIPCHK(launch_pack_x(x, x_dtype, T, H, H, ws.xh, s), "pack_x launch");
+    HIPCHK(launch_pack_x(x, x_dtype, T, H, H, ws.xh, ws.xexp, s), "pack_x launch");
     if (L->shared) HIPCHK(launch_dense_gateup(L->shared, H, I, x, x_dtype, H, T, ws.hs, s), "shared gate/up launch");
-    HIPCHK(launch_rvq_gateup(src, off, H, I, items, ws.xh, ws.hh, s), "rvq gate/up launch");
+    HIPCHK(launch_rvq_gateup(src, off, H, I, items, ws.xh, ws.xexp, ws.hh, s), "rvq gate/up launch");
     HIPCHK(launch_rvq_down(src, off, H, I, items, KS, ws.hh, ws.ypart, s), "rvq down launch");
     if (L->shared) HIPCHK(launch_dense_down(L->shared, H, I, ws.hs, T, ws.ysh, s), "shared down launch");
     HIPCHK(launch_combine(ws.ypart, k, KS, H, w, L->shared ? ws.ysh : nullptr, out, H, T, 0, s), "combine launch");
@@ -242,8 +243,8 @@ int moe_expert_ffn_rvq(const void *record, int32_t H, int32_t I, const float *x,
     src.n_local = 1;
     const RecOffsets off = offsets_of(H, I);
     const int KS = down_splits(H, I, T);
-    HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, T, H, H, L.xh, s), "pack_x launch");
-    HIPCHK(launch_rvq_gateup(src, off, H, I, T, L.xh, L.hh, s), "rvq gate/up launch");
+    HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, T, H, H, L.xh, L.xexp, s), "pack_x launch");
+    HIPCHK(launch_rvq_gateup(src, off, H, I, T, L.xh, L.xexp, L.hh, s), "rvq gate/up launch");
     HIPCHK(launch_rvq_down(src, off, H, I, T, KS, L.hh, L.ypart, s), "rvq down launch");
     HIPCHK(launch_combine(L.ypart, 1, KS, H, gate_w, nullptr, y, H, T, accumulate, s), "combine launch");
     return MOE_OK;
@@ -285,7 +286,7 @@ struct DecodeWs {
     unsigned *sync;
     DecLayer *layers;
     uint64_t *z, *ysh, *part_gu, *part_d;
-    uint16_t *hh;
+    float *hh;
     uint64_t *hq;
     float *hs;
     unsigned long long *stamps;
@@ -331,8 +332,9 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
     D->lut = P.lut;
     D->sync_words = P.sync_words;
     Carver c(ws);
-    // zeroed before every launch: the counters (word 0 is the error flag
-    // that moe_decode_status reads), then the step-tagged buffers
+    // zeroed before every launch: the counters (word 0 is the launch's
+    // abort flag; word 1, the sticky status that moe_decode_status reads, is
+    // kept), then the step-tagged buffers
     D->sync = c.take<unsigned>(D->sync_words);
     D->z = c.take<uint64_t>((size_t)E_max);
     D->ysh = c.take<uint64_t>((size_t)H);
@@ -342,7 +344,7 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
     D->hq = (D->lut & kLutDown) ? c.take<uint64_t>((size_t)k * I) : nullptr;
     D->clear_words = c.pos / 4;
     D->layers = c.take<DecLayer>(kDecMaxLayers);
-    D->hh = c.take<uint16_t>((size_t)k * I);
+    D->hh = c.take<float>((size_t)k * I);
     D->hs = c.take<float>((size_t)I);
     D->stamp_steps = decode_stamp_steps();
     D->stamps = D->stamp_steps ? c.take<unsigned long long>((size_t)D->stamp_steps * D->G * kDecStamps) : nullptr;
@@ -461,9 +463,17 @@ int moe_decode_down_method(const moe_layer *layers, int32_t n_layers, int32_t *m
 
 int moe_decode_status(const void *ws, int32_t *timed_out) {
     if (!ws || !timed_out) return fail(MOE_E_INVAL, "ws and timed_out must be non-NULL");
-    unsigned flag = 0;
-    HIPCHK(hipMemcpy(&flag, ws, sizeof flag, hipMemcpyDeviceToHost), "read decode status");
-    *timed_out = flag != 0;
+    // the sticky status is 32-bit word 1 of the workspace (the counters
+    // come first); the device is idle once hipDeviceSynchronize returns
+    unsigned *word = (unsigned *)ws + 1;
+    unsigned v = 0;
+    HIPCHK(hipDeviceSynchronize(), "synchronise before reading the decode status");
+    HIPCHK(hipMemcpy(&v, word, sizeof v, hipMemcpyDeviceToHost), "read decode status");
+    *timed_out = v == kDecodeStatusFailed;
+    if (*timed_out) {
+        const unsigned clean = kDecodeStatusClean;
+        HIPCHK(hipMemcpy(word, &clean, sizeof clean, hipMemcpyHostToDevice), "reset decode status");
+    }
     return MOE_OK;
 }
 
@@ -553,7 +563,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         HIPCHK(launch_topk(za, ah.L->router.E, ah.k, ah.L->router.score_fn, 1, ia, wa, cs), "look-ahead top-k");
         HIPCHK(hipMemcpyAsync(h_ahead, ia, ah.k * sizeof(int32_t), hipMemcpyDeviceToHost, cs), "look-ahead ids");
     }
-    HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, 1, H, H, W.xh, cs), "pack_x");
+    HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, 1, H, H, W.xh, W.xexp, cs), "pack_x");
     if (L->shared) {
         HIPCHK(launch_dense_gateup(L->shared, H, I, x, MOE_DTYPE_F32, H, 1, W.hs, cs), "shared gate/up");
         HIPCHK(launch_dense_down(L->shared, H, I, W.hs, 1, W.ysh, cs), "shared down");
@@ -600,7 +610,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         hits.n_local++;
     }
     if (hits.n_local) {
-        HIPCHK(launch_rvq_gateup(hits, off, H, I, hits.n_local, W.xh, W.hh, cs), "rvq gate/up (hits)");
+        HIPCHK(launch_rvq_gateup(hits, off, H, I, hits.n_local, W.xh, W.xexp, W.hh, cs), "rvq gate/up (hits)");
         HIPCHK(launch_rvq_down(hits, off, H, I, hits.n_local, KS, W.hh, W.ypart, cs), "rvq down (hits)");
     }
     // file tier: the misses' records into host slots (read while the hit
@@ -631,9 +641,10 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         const int32_t s = slot_of[j];
         if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "copy waits for slot readers");
         const void *src = tier.t ? (const void *)src_of[j] : experts_host[c->h_idx[j]];
+        bool enqueued = false;   // the key is committed either way: a failed copy drops its slot
         hipError_t e = tier.t ? hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, src, c->slot_bytes,
                                                hipMemcpyHostToDevice, ps)
-                              : cache_copy_in(c, s, src, ps);
+                              : cache_copy_in(c, s, src, ps, &enqueued);
         if (e == hipSuccess && tier.t) {
             const int trc = tier_copied(tier.t, src_of[j], ps);
             if (trc) {
@@ -654,7 +665,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         one.n_local = 1;
         one.list[0] = c->pool + (size_t)s * c->slot_bytes;
         one.rank[0] = (uint8_t)j;
-        HIPCHK(launch_rvq_gateup(one, off, H, I, 1, W.xh, W.hh, cs), "rvq gate/up (miss)");
+        HIPCHK(launch_rvq_gateup(one, off, H, I, 1, W.xh, W.xexp, W.hh, cs), "rvq gate/up (miss)");
         HIPCHK(launch_rvq_down(one, off, H, I, 1, KS, W.hh, W.ypart, cs), "rvq down (miss)");
     }
     HIPCHK(launch_combine(W.ypart, k, KS, H, W.w, L->shared ? W.ysh : nullptr, out, H, 1, 0, cs), "combine");
@@ -683,7 +694,8 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         if (!inserted) continue;
         c->filled[s] = 0;
         if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "look-ahead copy waits for slot readers");
-        hipError_t e = cache_copy_in(c, s, ah.host[pred[j]], ps);
+        bool enqueued = false;
+        hipError_t e = cache_copy_in(c, s, ah.host[pred[j]], ps, &enqueued);
         if (e == hipSuccess) e = hipEventRecord(c->ready[s], ps);
         if (e != hipSuccess) {
             c->core.drop_slot(s);

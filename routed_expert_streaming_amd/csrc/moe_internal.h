@@ -41,8 +41,9 @@ struct LayerWs {
     float *z;          // [T, E] router logits
     int32_t *idx;      // [T, k]
     float *w;          // [T, k]
-    uint32_t *xh;      // [T, H/2] x as fp16 pairs
-    uint16_t *hh;      // [T*k, I] SwiGLU intermediate as fp16
+    uint32_t *xh;      // [T, H/2] x as fp16 pairs, scaled by 2^-xexp[t]
+    int32_t *xexp;     // [T] range exponent of each token's x
+    float *hh;         // [T*k, I] SwiGLU intermediate (fp32)
     float *ypart;      // [T*k, KS, H] down partial sums (scaled)
     float *hs;         // [T, I] shared-expert intermediate (fp32)
     float *ysh;        // [T, H] shared-expert output
@@ -60,13 +61,13 @@ constexpr int kRouteMaxSlices = 16;
 int route_blocked_slices(int E, int H, int T);
 hipError_t launch_route_blocked(const float *W, const float *bias, int E, int H, const void *x, int x_dtype, int T,
                                 float *part, float *z, hipStream_t s);
-hipError_t launch_pack_x(const void *x, int x_dtype, int T, int H, int64_t x_stride, uint32_t *xh,
+hipError_t launch_pack_x(const void *x, int x_dtype, int T, int H, int64_t x_stride, uint32_t *xh, int32_t *xexp,
                          hipStream_t s);
 // n_local_total = T * src.n_local local items in the launch
 hipError_t launch_rvq_gateup(const RecSrc &src, const RecOffsets &off, int H, int I, int n_local_total,
-                             const uint32_t *xh, uint16_t *hh, hipStream_t s);
+                             const uint32_t *xh, const int32_t *xexp, float *hh, hipStream_t s);
 hipError_t launch_rvq_down(const RecSrc &src, const RecOffsets &off, int H, int I, int n_local_total,
-                           int KS, const uint16_t *hh, float *ypart, hipStream_t s);
+                           int KS, const float *hh, float *ypart, hipStream_t s);
 hipError_t launch_combine(const float *ypart, int k, int KS, int H, const float *w, const float *ysh,
                           float *out, int64_t out_stride, int T, int accumulate, hipStream_t s);
 hipError_t launch_dense_gateup(const uint16_t *shared, int H, int I, const void *x, int x_dtype,
@@ -118,7 +119,7 @@ struct DecodeLaunch {
                              // (the counters and every step-tagged buffer)
     DecLayer *layer_buf;     // [kDecMaxLayers] device copy of the descriptors
     uint64_t *z, *ysh, *part_gu, *part_d;   // step-tagged exchange buffers
-    uint16_t *hh;
+    float *hh;               // [k][I] fp32 h (gather down)
     uint64_t *hq;            // tagged fp32 h (down by table lookup), zeroed before the launch
     float *hs;
     int slots_gu, slots_d;
@@ -127,6 +128,9 @@ struct DecodeLaunch {
     unsigned long long *stamps;   // phase timestamps (profiling aid), or null
     int stamp_steps;
 };
+
+// Values of the decode workspace's sticky status word (32-bit word 1).
+constexpr unsigned kDecodeStatusClean = 0x600D600Du, kDecodeStatusFailed = 0xBAD0BAD0u;
 
 struct DecodePlanOut {
     int G;                        // persistent workgroups (one per CU)

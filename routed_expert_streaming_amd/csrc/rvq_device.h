@@ -31,6 +31,27 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Power-of-two range scaling before a rounding to fp16 (largest finite value
+// 65504): for a block whose largest magnitude is amax, e such that
+// amax * 2^-e lies in [2^kRangeExp, 2^(kRangeExp + 1)).  The scaled values
+// then stay below 2^8, and a sum of 8 of them times codebook entries below
+// 16 in magnitude stays below 2^15.  Scaling by 2^-e before the rounding and
+// by 2^e after the fp32 sum is exact (ldexp), so only the fp16 rounding
+// itself remains, at the same relative size as for unscaled inputs.
+constexpr int kRangeExp = 7;
+__device__ __forceinline__ int range_exp(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    if (!(amax > 0.f) || b >= 0x7F800000u) return 0;   // zero, NaN, inf: no scaling
+    const int p = (int)(b >> 23) - 127;                 // floor(log2 amax); -127 for subnormals
+    return min(max(p - kRangeExp, -120), 120);
+}
+
 // Local item -> (global item, record).
 __device__ __forceinline__ const uint8_t *resolve_record(const RecSrc &s, int local, int &item) {
     const int t = local / s.n_local, l = local % s.n_local;

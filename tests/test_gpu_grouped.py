@@ -68,7 +68,7 @@ def test_grouped_k3_shape_with_shared(moe):
     _check(moe, cfg)
 
 
-def test_grouped_full_batched_layer_sampled(moe):
-    # the full 256-token, 384-expert layer; sampled tokens are checked one by one
+def test_grouped_full_batched_layer(moe):
+    # the full 256-token, 384-expert layer; every token is checked on its own
     cfg = synth.CONFIGS["batched"]
-    _check(moe, cfg, sample=[0, 1, 37, 100, 128, 201, 254, 255])
+    _check(moe, cfg)

@@ -181,10 +181,55 @@ def test_decode_forward_k3_shape_fewer_experts_per_token(moe, k):
     _check_decode(moe, synth.get_config("k3_slice", tokens=2, layers=2, k=k))
 
 
-def test_decode_forward_mixtral_full_size(moe):
-    # the configuration bench.py times: all 32 layers, 8 resident experts each
-    # (gate/up and down by table lookup, the default at I = 14336)
-    _check_decode(moe, synth.get_config("mixtral", tokens=2), method="lookup", down="lookup")
+def _check_decode_all(moe, cfg, method=None, down=None):
+    """The whole decode of a configuration (every token x every layer, one
+    launch) against the oracle, every layer call; each layer's records are
+    generated once, for the experts some token selects."""
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    log(f"decode {cfg.name}: all {cfg.tokens} tokens x {cfg.layers} layers, uploading")
+    dw = DeviceWorkload(cfg)
+    if method is not None:
+        assert moe.decode_gate_up_method(dw.layers) == method
+    if down is not None:
+        assert moe.decode_down_method(dw.layers) == down
+    x = dw.inputs()
+    ws = torch.empty(moe.decode_workspace_bytes(dw.layers), dtype=torch.uint8, device="cuda")
+    out, idx = moe.decode_forward(dw.layers, x, ws=ws)
+    torch.cuda.synchronize()
+    assert not moe.decode_status(ws), "device-side wait limit reached"
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    oracle.set_threads(16)
+    x64 = x.cpu().numpy().astype(np.float64)
+    empty = np.zeros(1, np.uint8)
+    rs = []
+    for L in range(cfg.layers):
+        W, b = dw.wl.router(L), dw.wl.bias(L)
+        ridx, _, _ = oracle.route(W, b, x64[:, L], cfg.k, cfg.score)
+        assert same_sets(idx[:, L], ridx), f"routing differs at layer {L}"
+        need = set(int(e) for e in ridx.reshape(-1))
+        recs = [dw.wl.record(L, e) if e in need else empty for e in range(cfg.E)]
+        ref, _, _ = oracle.layer(W, b, cfg.k, cfg.score, recs, dw.wl.shared(L), cfg.H, cfg.I, x64[:, L])
+        for t in range(cfg.tokens):
+            r = rel_l2(out[t, L], ref[t])
+            rs.append(r)
+            assert r <= RTOL_F32_PATH, f"token {t} layer {L}: rel_l2 {r:.3e}"
+        if L % 4 == 3:
+            log(f"  layers 0..{L} checked, worst rel_l2 so far {max(rs):.3e}")
+    log(f"  {len(rs)} layer calls checked: worst rel_l2 {max(rs):.3e}, median {np.median(rs):.3e}")
+
+
+def test_decode_forward_mixtral_all_tokens(moe):
+    # the configuration bench.py times, whole: all 64 tokens x 32 layers of 8
+    # resident experts (gate/up and down by table lookup, the default at
+    # I = 14336) in one launch; all 2048 layer calls against the oracle
+    _check_decode_all(moe, synth.CONFIGS["mixtral"], method="lookup", down="lookup")
+
+
+def test_decode_forward_kimi_linear_all_tokens(moe):
+    # the Kimi-Linear-class decode, whole: 128 tokens x 27 layers of 256
+    # experts + the shared expert, sigmoid top-8 with the Zipf bias (codebook
+    # gathers at I = 1024); all 3456 layer calls against the oracle
+    _check_decode_all(moe, synth.CONFIGS["kimi_linear"], method="gathers", down="gathers")
 
 
 def test_decode_forward_mixtral_gathers(moe, monkeypatch):
@@ -435,3 +480,119 @@ def test_streamed_file_tier(moe, tmp_path):
     log(f"file tier: {st}, HBM misses {len(misses)} of {len(cache.trace())}")
     tier.close()
     cache.close()
+
+
+# ---------------------------------------------------------------- routing edges
+@pytest.mark.parametrize("k,score", [(1, "softmax"), (1, "sigmoid"), (8, "softmax"), (8, "sigmoid")])
+def test_routing_edge_k(moe, k, score):
+    # k = 1 (the weight is exactly 1) and k = E (every expert; softmax-renorm
+    # is the full softmax): router, layer and decode kernels against the
+    # oracle on the Tiny shape (8 experts); for k = 1 the router is redrawn
+    # until every token's top-1 margin is at least 1e-3
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    cfg = synth.get_config("tiny", k=k, score=score)
+    dw = DeviceWorkload(cfg)
+    x = dw.inputs()[:, 0, :].contiguous()
+    idx, w = moe.route_topk(dw.layers[0].router, x)
+    x64 = x.cpu().numpy().astype(np.float64)
+    ridx, rw, z = oracle.route(dw.wl.router(0), None, x64, k, score)
+    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    if k == 1:
+        assert np.array_equal(idx, ridx)
+        assert np.all(w == 1.0)
+    else:
+        assert np.array_equal(np.sort(idx, 1), np.tile(np.arange(cfg.E), (cfg.tokens, 1)))
+        full = np.exp(z - z.max(1, keepdims=True)) if score == "softmax" else 1.0 / (1.0 + np.exp(-z))
+        full = full / full.sum(1, keepdims=True)
+        np.testing.assert_allclose(weights_by_expert(idx, w), full, rtol=2e-6, atol=1e-7)
+        np.testing.assert_allclose(weights_by_expert(ridx, rw), full, rtol=1e-12)
+    assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-6)
+    out, lidx, _ = moe.layer_forward(dw.layers[0], x)
+    ref, _, _ = _oracle_layer(dw, 0, x64)
+    assert same_sets(lidx.cpu().numpy(), ridx)
+    r = rel_l2(out.cpu().numpy(), ref)
+    log(f"k={k} {score}: layer rel_l2 {r:.3e}")
+    assert r <= RTOL_F32_PATH
+    _check_decode(moe, cfg)
+
+
+# ----------------------------------------------------------------- fp16 range
+def _scaled_layers(dw, sx, outlier_cols, so):
+    """Layers whose experts see x * 2^sx (columns outlier_cols a further
+    2^so) while the logits stay those of the unscaled input: the router
+    weights are scaled by the inverse powers of two, so every fp32 product
+    of the logit sums is the unscaled one exactly."""
+    from routed_expert_streaming_amd import Layer, Router
+    cfg = dw.cfg
+    col = np.full(cfg.H, 2.0 ** sx)
+    col[outlier_cols] *= 2.0 ** so
+    layers, Ws = [], []
+    for i, L in enumerate(dw.layer_ids):
+        W = (dw.wl.router(L).astype(np.float64) / col).astype(np.float32)
+        Ws.append(W)
+        base = dw.layers[i]
+        r = Router(torch.from_numpy(W).cuda(), cfg.k, cfg.score, base.router.bias)
+        layers.append(Layer(cfg.H, cfg.I, r, shared=base.shared, record_ptrs=base.record_ptrs))
+    return layers, Ws, torch.from_numpy(col.astype(np.float32)).cuda()
+
+
+@pytest.mark.parametrize("name,lut", [("mixtral", None), ("mixtral", "0"), ("mixtral", "2"), ("k3_slice", None)])
+def test_decode_fp16_range(moe, monkeypatch, name, lut):
+    # activations far beyond fp16's range (|x| up to ~2^22, so |h| and the
+    # table entries C[c].x_q would overflow 65504 without range scaling):
+    # every decode method must stay finite and match the oracle
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    if lut is not None:
+        monkeypatch.setenv("MOE_DECODE_LUT", lut)
+    cfg = synth.get_config(name, tokens=2, layers=2)
+    dw = DeviceWorkload(cfg)
+    layers, Ws, col = _scaled_layers(dw, 15, np.arange(5, cfg.H, 97), 5)
+    x = (dw.inputs() * col).contiguous()
+    assert x.abs().max().item() > 65504.0 * 16
+    out, idx = moe.decode_forward(layers, x)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    oracle.set_threads(16)
+    x64 = x.cpu().numpy().astype(np.float64)
+    empty = np.zeros(1, np.uint8)
+    worst = 0.0
+    for t in range(cfg.tokens):
+        for L in range(cfg.layers):
+            ridx, _, _ = oracle.route(Ws[L], dw.wl.bias(L), x64[t, L][None], cfg.k, cfg.score)
+            need = set(int(e) for e in ridx[0])
+            recs = [dw.wl.record(L, e) if e in need else empty for e in range(cfg.E)]
+            ref, ridx, _ = oracle.layer(Ws[L], dw.wl.bias(L), cfg.k, cfg.score, recs, dw.wl.shared(L), cfg.H, cfg.I,
+                                        x64[t, L][None])
+            assert same_sets(idx[t, L][None], ridx)
+            r = rel_l2(out[t, L], ref[0])
+            worst = max(worst, r)
+            assert r <= RTOL_F32_PATH, f"token {t} layer {L}: rel_l2 {r:.3e}"
+    log(f"{name} decode (MOE_DECODE_LUT={lut}) with |x| up to {np.abs(x64).max():.3g}: worst rel_l2 {worst:.3e}")
+
+
+@pytest.mark.parametrize("name,T", [("k3_slice", 2), ("mixtral", 1)])
+def test_layer_fp16_range(moe, name, T):
+    # the multi-kernel layer path (also the streamed path's kernels) with the
+    # same out-of-range activations
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    cfg = synth.get_config(name, tokens=T, layers=1)
+    dw = DeviceWorkload(cfg, layers=[0])
+    layers, Ws, col = _scaled_layers(dw, 15, np.arange(3, cfg.H, 89), 5)
+    x = (dw.inputs()[:, 0, :] * col).contiguous()
+    out, idx, _ = moe.layer_forward(layers[0], x)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    x64 = x.cpu().numpy().astype(np.float64)
+    ridx, _, _ = oracle.route(Ws[0], dw.wl.bias(0), x64, cfg.k, cfg.score)
+    need = set(int(e) for e in ridx.reshape(-1))
+    empty = np.zeros(1, np.uint8)
+    recs = [dw.wl.record(0, e) if e in need else empty for e in range(cfg.E)]
+    oracle.set_threads(16)
+    ref, ridx, _ = oracle.layer(Ws[0], dw.wl.bias(0), cfg.k, cfg.score, recs, dw.wl.shared(0), cfg.H, cfg.I, x64)
+    assert same_sets(idx.cpu().numpy(), ridx)
+    for t in range(T):
+        r = rel_l2(out[t], ref[t])
+        log(f"{name} layer token {t} with |x| up to {np.abs(x64).max():.3g}: rel_l2 {r:.3e}")
+        assert r <= RTOL_F32_PATH
