@@ -244,8 +244,33 @@ int moe_decode_down_method(const moe_layer *layers, int32_t n_layers, int32_t *m
  * the outputs of that call are invalid).  The status is sticky across
  * launches and is reset by this call once read.  Synchronises the device
  * (hipDeviceSynchronize), then reads one word.
- *   ws [dev] the workspace passed to moe_decode_forward;  timed_out: 0 or 1 */
+ *   ws [dev] the workspace passed to moe_decode_forward, or NULL for the
+ *            current device's scratch array of moe_decode_forward_noalloc;
+ *   timed_out: 0 or 1 */
 int moe_decode_status(const void *ws, int32_t *timed_out);
+
+/* Bytes of the device scratch array that moe_decode_forward_noalloc uses
+ * (one per device, held from the library's load until the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/* moe_decode_forward without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The decode's workspace (counters and the
+ * step-tagged exchange buffers, cleared by a kernel at each launch) is a
+ * file-scope device array of MOE_NOALLOC_SCRATCH_BYTES in the library, one
+ * copy per device, whose address is looked up on the first call on each
+ * device; nothing is allocated (no hipMalloc, hipFree or allocating library
+ * call).  Outputs equal moe_decode_forward's bit for bit.  The caller still
+ * passes x, out and idx_out as for moe_decode_forward.  Every call on a
+ * device shares that device's array: calls that overlap on one device (on
+ * different streams or host threads) race and give invalid results.  The
+ * wait-limit status is read with moe_decode_status(NULL, ...).
+ * MOE_E_SPACE if these layers need more workspace than
+ * MOE_NOALLOC_SCRATCH_BYTES (moe_decode_workspace_bytes tells; the Mixtral-,
+ * Kimi-Linear- and K3-shaped decodes need at most 12 MB); other errors as
+ * for moe_decode_forward. */
+int moe_decode_forward_noalloc(const moe_layer *layers, int32_t n_layers, const float *x, int32_t T,
+                               float *out, int32_t *idx_out, void *hip_stream);
 
 /* Workspace bytes that moe_layer_forward_grouped needs for T tokens. */
 size_t moe_grouped_workspace_bytes(const moe_layer *L, int32_t T);

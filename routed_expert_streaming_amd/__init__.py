@@ -4,6 +4,7 @@ Python face of libmoe (include/moe.h): torch supplies device memory and
 streams; every computation runs in the library's HIP kernels.  Names follow
 the C ABI: route_topk, expert_ffn_rvq, layer_forward, decode_forward,
 layer_forward_grouped, ExpertCache (expert_cache_*), layer_forward_streamed,
+decode_forward_noalloc,
 lru_stack_distances, HostTier (moe_host_tier_*), hbm_read.
 """
 from __future__ import annotations
@@ -223,9 +224,33 @@ def decode_down_method(layers: Sequence[Layer]) -> str:
     return "lookup" if m.value else "gathers"
 
 
-def decode_status(ws: torch.Tensor) -> bool:
-    """True if the last decode_forward on this workspace hit its device-side
-    wait limit (its outputs are then invalid).  Synchronises."""
+NOALLOC_SCRATCH_BYTES = _lib.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def decode_forward_noalloc(layers: Sequence[Layer], x: torch.Tensor, stream=None,
+                           out: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                           want_idx: bool = True):
+    """decode_forward with the library's own device scratch array as the
+    workspace (moe_decode_forward_noalloc: nothing is allocated by the
+    library; calls that overlap on one device race)."""
+    _need(x.dim() == 3 and x.dtype == torch.float32 and x.is_contiguous(), "x must be contiguous fp32 [T, L, H]")
+    T, nL, H = x.shape
+    _need(nL == len(layers), "x's layer dimension must match len(layers)")
+    arr = _layer_array(layers)
+    k = layers[0].router.k
+    out = out if out is not None else torch.empty_like(x)
+    if want_idx and idx is None:
+        idx = torch.empty((T, nL, k), dtype=torch.int32, device=x.device)
+    check(lib().moe_decode_forward_noalloc(arr, nL, _ptr(x), T, _ptr(out), _ptr(idx if want_idx else None),
+                                           _stream(stream)), "moe_decode_forward_noalloc")
+    return out, (idx if want_idx else None)
+
+
+def decode_status(ws: Optional[torch.Tensor]) -> bool:
+    """True if any decode_forward on this workspace (ws = None: any
+    decode_forward_noalloc on the current device) since the previous call hit
+    its device-side wait limit (those outputs are invalid); resets the
+    status.  Synchronises."""
     flag = ctypes.c_int32()
     check(lib().moe_decode_status(_ptr(ws), ctypes.byref(flag)), "moe_decode_status")
     return bool(flag.value)

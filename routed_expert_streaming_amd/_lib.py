@@ -20,6 +20,7 @@ MOE_OK, MOE_E_INVAL, MOE_E_HIP, MOE_E_SPACE, MOE_E_STATE, MOE_E_NOMEM = 0, -1, -
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_MAX_K, MOE_MAX_E = 32, 1024
+MOE_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 MOE_NO_KEY = 0xFFFFFFFF
 
 
@@ -54,6 +55,7 @@ SIGNATURES = {
     "moe_decode_workspace_bytes": (SZ, [ctypes.POINTER(MoeLayer), I32]),
     "moe_decode_forward": (ctypes.c_int, [ctypes.POINTER(MoeLayer), I32, P, I32, P, P, P, SZ, P]),
     "moe_decode_status": (ctypes.c_int, [P, ctypes.POINTER(I32)]),
+    "moe_decode_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeLayer), I32, P, I32, P, P, P]),
     "moe_decode_gate_up_method": (ctypes.c_int, [P, I32, ctypes.POINTER(I32)]),
     "moe_decode_down_method": (ctypes.c_int, [P, I32, ctypes.POINTER(I32)]),
     "moe_grouped_workspace_bytes": (SZ, [ctypes.POINTER(MoeLayer), I32]),

@@ -1756,16 +1756,24 @@ static int max_tiles_per_range(long n_tiles, int cpr, int G) {
 }
 
 hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
-    static int G = 0;
-    static bool lds_at_zero = false;   // no static LDS: dynamic LDS starts at byte 0
+    // per device: the persistent grid and whether dynamic LDS starts at byte 0
+    // (no static LDS)
+    constexpr int kMaxDev = 64;
+    static int Gdev[kMaxDev] = {};
+    static bool lds_zero_dev[kMaxDev] = {};
+    int dev = 0;
+    hipError_t ed = hipGetDevice(&dev);
+    if (ed != hipSuccess) return ed;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    int &G = Gdev[dev];
+    bool &lds_at_zero = lds_zero_dev[dev];
     if (G == 0) {
         hipFuncAttributes fa;
         hipError_t ea = hipFuncGetAttributes(&fa, (const void *)k_decode_persistent);
         if (ea != hipSuccess) return ea;
         lds_at_zero = fa.sharedSizeBytes == 0;
-        int dev = 0, cus = 0, per = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        int cus = 0, per = 0;
+        hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
             e = hipFuncSetAttribute((const void *)k_decode_persistent, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     (int)decode_lds());
@@ -1795,12 +1803,14 @@ hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
     if (o->lut & kLutGateUp) o->slots_gu = cprH;
     if (o->lut & kLutDown) o->slots_d = cprI;
     o->sync_words = kHReady + (size_t)(k + 1) * kLine;
-    // LDS: both phases' layouts must fit below the routing tail
+    // LDS: the gathers' layouts of the phases done by gathers must fit below
+    // the routing tail (a table-lookup phase uses the table area instead)
     const long red_gu = 2L * kCbRows * 16 + ((H * 2 + 255) & ~255) + (long)o->slots_red_gu * kPW * 128 * 4;
     const long red_d = (long)kCbRows * 16 + ((I * 2 + 255) & ~255) + (long)o->slots_red_d * kPW * 64 * 4;
+    const bool gu_ok = (o->lut & kLutGateUp) || (red_gu <= kDecTail && kXStage + (long)H * 4 <= 2L * kCbRows * 16);
+    const bool d_ok = (o->lut & kLutDown) || red_d <= kDecTail;
     // the shared expert's fp32 h is staged below the record pointers
-    o->lds_ok = red_gu <= kDecTail && red_d <= kDecTail && (long)I * 4 + kPW * kShRows * 4 <= kDecRecs &&
-                ((o->lut & kLutGateUp) || kXStage + (long)H * 4 <= 2L * kCbRows * 16);
+    o->lds_ok = gu_ok && d_ok && (long)I * 4 + kPW * kShRows * 4 <= kDecRecs;
     return hipSuccess;
 }
 

@@ -281,6 +281,8 @@ int moe_layer_forward(const moe_layer *L, const void *x, int32_t x_dtype, int32_
     return run_experts(L, W, src, x, x_dtype, T, k, w, out, s);
 }
 
+}  // extern "C"
+
 namespace {
 struct DecodeWs {
     unsigned *sync;
@@ -312,7 +314,7 @@ int decode_lut_mode() {
     return v == 2 ? 2 : (v ? 1 : 0);
 }
 
-int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *D) {
+int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *D, bool stamps = true) {
     const int H = layers[0].H, I = layers[0].I, k = layers[0].router.k;
     int E_max = 1;
     bool shared = false;
@@ -346,7 +348,7 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
     D->layers = c.take<DecLayer>(kDecMaxLayers);
     D->hh = c.take<float>((size_t)k * I);
     D->hs = c.take<float>((size_t)I);
-    D->stamp_steps = decode_stamp_steps();
+    D->stamp_steps = stamps ? decode_stamp_steps() : 0;
     D->stamps = D->stamp_steps ? c.take<unsigned long long>((size_t)D->stamp_steps * D->G * kDecStamps) : nullptr;
     D->bytes = (size_t)align_up((int64_t)c.pos, 256);
     (void)shared;
@@ -354,18 +356,8 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
 }
 }  // namespace
 
-size_t moe_decode_workspace_bytes(const moe_layer *layers, int32_t n_layers) {
-    if (!layers || n_layers < 1 || !dims_ok(layers[0].H, layers[0].I) || layers[0].router.k < 1) {
-        fail(MOE_E_INVAL, "decode workspace: invalid layers, n_layers or shapes");
-        return 0;
-    }
-    DecodeWs D;
-    if (carve_decode(nullptr, layers, n_layers, &D)) return 0;
-    return D.bytes;
-}
-
-int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x, int32_t T, float *out,
-                       int32_t *idx_out, void *ws, size_t ws_bytes, void *hip_stream) {
+namespace moe {
+int decode_check_args(const moe_layer *layers, int32_t n_layers, const float *x, int32_t T, const float *out) {
     if (!layers || n_layers < 1) return fail(MOE_E_INVAL, "layers is NULL or n_layers < 1");
     for (int l = 0; l < n_layers; l++) {
         int rc = check_layer(&layers[l], true);
@@ -376,13 +368,27 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
     }
     if (T < 0) return fail(MOE_E_INVAL, "T=%d < 0", T);
     if (T == 0) return MOE_OK;
-    if (!x || !out || !ws) return fail(MOE_E_INVAL, "x, out and ws must be non-NULL");
+    if (!x || !out) return fail(MOE_E_INVAL, "x and out must be non-NULL");
+    return MOE_OK;
+}
+
+int decode_ws_bytes(const moe_layer *layers, int32_t n_layers, bool stamps, size_t *bytes) {
+    if (!layers || n_layers < 1 || !dims_ok(layers[0].H, layers[0].I) || layers[0].router.k < 1)
+        return fail(MOE_E_INVAL, "decode workspace: invalid layers, n_layers or shapes");
     DecodeWs D;
-    int rc = carve_decode(ws, layers, n_layers, &D);
+    int rc = carve_decode(nullptr, layers, n_layers, &D, stamps);
+    if (rc) return rc;
+    *bytes = D.bytes;
+    return MOE_OK;
+}
+
+int decode_forward_impl(const moe_layer *layers, int32_t n_layers, const float *x, int32_t T, float *out,
+                        int32_t *idx_out, void *ws, size_t ws_bytes, bool stamps, hipStream_t s) {
+    DecodeWs D;
+    int rc = carve_decode(ws, layers, n_layers, &D, stamps);
     if (rc) return rc;
     if (ws_bytes < D.bytes) return fail(MOE_E_SPACE, "workspace %zu < %zu bytes", ws_bytes, D.bytes);
     const int H = layers[0].H, I = layers[0].I, k = layers[0].router.k;
-    hipStream_t s = (hipStream_t)hip_stream;
     DecodeLaunch d{};
     d.H = H;
     d.I = I;
@@ -441,6 +447,22 @@ int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x
     }
     return MOE_OK;
 }
+}  // namespace moe
+
+extern "C" {
+
+size_t moe_decode_workspace_bytes(const moe_layer *layers, int32_t n_layers) {
+    size_t n = 0;
+    return decode_ws_bytes(layers, n_layers, true, &n) == MOE_OK ? n : 0;
+}
+
+int moe_decode_forward(const moe_layer *layers, int32_t n_layers, const float *x, int32_t T, float *out,
+                       int32_t *idx_out, void *ws, size_t ws_bytes, void *hip_stream) {
+    int rc = decode_check_args(layers, n_layers, x, T, out);
+    if (rc || T == 0) return rc;
+    if (!ws) return fail(MOE_E_INVAL, "ws must be non-NULL");
+    return decode_forward_impl(layers, n_layers, x, T, out, idx_out, ws, ws_bytes, true, (hipStream_t)hip_stream);
+}
 
 static int decode_method(const moe_layer *layers, int32_t n_layers, int32_t *method, int bit) {
     if (!layers || n_layers < 1 || !method) return fail(MOE_E_INVAL, "layers or method is NULL, or n_layers < 1");
@@ -462,7 +484,14 @@ int moe_decode_down_method(const moe_layer *layers, int32_t n_layers, int32_t *m
 }
 
 int moe_decode_status(const void *ws, int32_t *timed_out) {
-    if (!ws || !timed_out) return fail(MOE_E_INVAL, "ws and timed_out must be non-NULL");
+    if (!timed_out) return fail(MOE_E_INVAL, "timed_out must be non-NULL");
+    if (!ws) {
+        // the current device's scratch array of moe_decode_forward_noalloc
+        void *p = nullptr;
+        int rc = decode_noalloc_scratch(&p);
+        if (rc) return rc;
+        ws = p;
+    }
     // the sticky status is 32-bit word 1 of the workspace (the counters
     // come first); the device is idle once hipDeviceSynchronize returns
     unsigned *word = (unsigned *)ws + 1;

@@ -146,6 +146,17 @@ struct DecodePlanOut {
 hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o);
 hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s);
 
+// The decode driver behind moe_decode_forward and moe_decode_forward_noalloc
+// (moe_api.hip): argument checks (MOE_OK also for T = 0), the workspace size
+// (with or without the optional profiling stamps), and the launches.
+int decode_check_args(const moe_layer *layers, int32_t n_layers, const float *x, int32_t T, const float *out);
+int decode_ws_bytes(const moe_layer *layers, int32_t n_layers, bool stamps, size_t *bytes);
+int decode_forward_impl(const moe_layer *layers, int32_t n_layers, const float *x, int32_t T, float *out,
+                        int32_t *idx_out, void *ws, size_t ws_bytes, bool stamps, hipStream_t s);
+// Device address of the current device's no-alloc scratch array
+// (decode_noalloc.hip).
+int decode_noalloc_scratch(void **out);
+
 // ---- batched path (kernels_grouped.hip) --------------------------------------
 hipError_t launch_group(const int32_t *idx, int n_pairs, int E, int32_t *perm, int32_t *inv, int32_t *counts,
                         int32_t *offsets, hipStream_t s);
