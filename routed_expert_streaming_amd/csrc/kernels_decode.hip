@@ -39,6 +39,7 @@ namespace moe {
 namespace {
 
 constexpr int kPW = 8;                 // waves per workgroup
+constexpr int kXcds = 8;               // accelerator complex dies (each with its own L2) of an MI355X
 constexpr long kSpinLimit = 1L << 24;  // x ~0.1 us per poll: a few seconds
 constexpr int kDecLdsBytes = 160 * 1024;
 
@@ -347,7 +348,9 @@ constexpr int kDecRecs = kDecTail - 8 * MOE_MAX_E;   // the layer's record point
 
 constexpr int kDecCtr = kDecLdsBytes - 4;   // the lookup phase's tile counter (unused end of the tail)
 constexpr int kRingGU = 3;      // code buffers per wave (2 units in flight ahead)
-constexpr int kShRows = 8;      // shared-expert rows per load group
+constexpr int kShRows = 8;      // shared-expert rows per load group (gate/up)
+constexpr int kShDR = 3;        // shared-expert down rows per wave in flight
+constexpr int kShCP = 4;        // 512-column passes of those rows in flight (I <= 2048 in one)
 constexpr int kTopkScratch = 2048;   // LDS bytes (codebook area, free while routing): top-k staging
 constexpr int kXStage = 16 * 1024;   // LDS bytes (codebook area, free while routing): fp32 x for the gathers
 constexpr int kTopkGroups = 8;       // first-level groups of the top-k
@@ -424,10 +427,12 @@ __device__ __forceinline__ void d_unit(const uint32_t (&d)[12], const char *cb, 
 // loads past the wave's last unit re-read that unit (their buffers are never
 // consumed), so every load of the ring stays in flight while older units are
 // computed.
+// count_at: if not null, this wave adds 1 there once the staging has waited
+// for all of its memory operations (stores issued before the call included).
 __device__ __forceinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *usec, const u32x4 *cbg_src,
                                            const u32x4 *cbu_src, int H, int I,
                                            int cpr, int la, int lb, int t0, int nslots, int wave, int lane,
-                                           unsigned long long *stamp) {
+                                           unsigned long long *stamp, unsigned *count_at) {
     const DecLds L = dec_lds_layout(H, I);
     char *cbg = dec_lds, *cbu = dec_lds + kCbRows * 16;
     uint32_t *xl = (uint32_t *)(dec_lds + L.x_gu);
@@ -441,6 +446,7 @@ __device__ __forceinline__ void stream_gateup(const u32x4 *gsec, const u32x4 *us
     uint32_t bg[kRingGU][12], bu[kRingGU][12];
     for (int i = threadIdx.x; i < nslots * kPW * 128; i += kPW * 64) red[i] = 0.f;
     wait_lds_barrier<0>();
+    if (count_at && lane == 0) __hip_atomic_fetch_add(count_at, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     lds_barrier();
     // first ring stages, issued after the codebooks have landed (issued
     // together, the chip-wide burst of code loads delays the codebooks); a
@@ -965,7 +971,14 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
     float *lmax = (float *)(recs + MOE_MAX_K);                  // [kPW] the waves' largest magnitudes
     uint64_t *recs_all = (uint64_t *)(lds + kDecRecs);          // [E] until top-k
 
-    const int G = a.G, w = blockIdx.x;
+    // XCD-major work index: workgroup b runs on XCD b % 8 (the dispatcher
+    // deals workgroups round-robin over the 8 XCDs), so with w as below the 32
+    // workgroups of one XCD take a contiguous slice of every phase's unit
+    // space: one XCD streams the tiles of one (expert, matrix) and its L2
+    // fetches that codebook and that chunk of x once, instead of every XCD
+    // fetching every codebook.
+    const int G = a.G;
+    const int w = G % kXcds == 0 ? (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds) : (int)blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int H = a.H, I = a.I, k = a.k;
     const int tilesI = I / kTileRows, tilesH = H / kTileRows;
@@ -1035,6 +1048,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // H add fma(0, 0), as there)
         float acc_w = 0.f;
         int xe = 0;                 // gather gate/up: x enters as fp16 pairs scaled by 2^-xe
+        // thread 0: the bias of logit row w, loaded together with x and the row
+        const float bias_w = threadIdx.x == 0 && lay.bias && w < nE ? lay.bias[w] : 0.f;
         {
             float *xst = (float *)(lds + kXStage);   // gathers: fp32 x, packed below once xe is known
             float xm = 0.f;
@@ -1074,6 +1089,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         if (w < nE) {
             for (int e = w; e < E; e += G) {
                 const float *wr = lay.W + (size_t)e * H;
+                // thread 0: this row's bias, in flight with the row's loads
+                const float be = threadIdx.x == 0 && lay.bias ? (e == w ? bias_w : lay.bias[e]) : 0.f;
                 float acc = e == w ? acc_w : 0.f;
                 for (int c0 = threadIdx.x * 4; c0 < H && e != w; c0 += 2 * kPW * 64 * 4) {
                     // two chunks' loads in flight together
@@ -1098,7 +1115,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 if (threadIdx.x == 0) {
                     float z = 0.f;
                     for (int v = 0; v < kPW; v++) z += red[v];
-                    st_tagged(a.z + e, z + (lay.bias ? lay.bias[e] : 0.f), tag);
+                    st_tagged(a.z + e, z + be, tag);
                 }
             }
         }
@@ -1292,14 +1309,22 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             recs[lane] = recs_all[e];
             if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = e;
         }
-        // wave 1 wrote every shared row: once its stores are done (long since,
-        // by now), count them
-        if (sh_rows && wave == 1) {
-            wait_vm_all();
-            if (lane == 0) __hip_atomic_fetch_add(h_ready + k * kLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
         lds_sync();
         mark(kStampRouted);
+        // wave 1 wrote every shared row of this workgroup: it counts them once
+        // its stores are done, at the first point after routing where it
+        // waits for its memory operations anyway (gathers: the codebook
+        // staging) or, at the latest, before this workgroup's first wait on
+        // another workgroup (the joins), so the count never waits on them
+        bool sh_counted = !(sh_rows && wave == 1);
+        auto count_shared = [&] {
+            if (!sh_counted) {
+                wait_vm_all();
+                if (lane == 0)
+                    __hip_atomic_fetch_add(h_ready + k * kLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sh_counted = true;
+            }
+        };
 
         if (a.lut & kLutGateUp) {
             // ---- gate/up by table lookup over this workgroup's range of the
@@ -1326,6 +1351,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             }
             lds_sync();
             mark(kStampGuLoop);
+            count_shared();
             // joins: tiles tau = w + G i of all ranks' k * tilesI tiles, two at
             // a time.  Wave v polls slots v, v + kPW, ... of both tiles (all its
             // loads in flight together: one round trip once the partials have
@@ -1435,7 +1461,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             stream_gateup((const u32x4 *)(rec + a.off.codes[0]), (const u32x4 *)(rec + a.off.codes[1]),
                           (const u32x4 *)(rec + a.off.cb[0]), (const u32x4 *)(rec + a.off.cb[1]), H, I, cprH,
                           (int)(ea - base), (int)(eb - base), (int)(ea / cprH - base / cprH), a.slots_red_gu, wave,
-                          lane, stamp);
+                          lane, stamp, sh_counted ? nullptr : h_ready + k * kLine);
+            sh_counted = true;
             lds_sync();
             mark(kStampGuLoop);
             // one tagged partial per touched tile (wave v: tiles v, v + kPW,
@@ -1505,54 +1532,75 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         }
 
         mark(kStampGuDone);
-        // ---- shared down rows (after the whole shared h is ready), tagged;
-        // kShRows rows at a time with every thread on 8 columns of each, as
-        // for gate/up
+        // ---- shared down rows, tagged: wave v takes the workgroup's rows
+        // shH0 + v, shH0 + v + kPW, ..., kShDR at a time, lane l columns
+        // 8 l + 512 m.  A wave issues its rows' weight loads, then waits for
+        // the whole shared h (its own poll of the counter), then loads h
+        // (coherent loads) and sums: no workgroup barrier, and the weights'
+        // round trip overlaps the wait.
+        count_shared();
         if (shared_on && shH1 > shH0) {
-            if (!wg_wait(sync, h_ready + k * kLine, (unsigned)(s + 1) * sh_gu_contrib, bcast)) return;
-            float *hl = (float *)lds;                                   // [I]
-            float *shred = hl + I;                                      // [kPW][kShRows]
-            for (int b = wave; b * 64 < I; b += kPW) dma_block(hl + b * 64, a.hs + b * 64, lane);
-            wait_vm_all();
-            __syncthreads();
             const uint16_t *wd0 = lay.shared + 2 * (size_t)I * H;
-            for (int r0 = shH0; r0 < shH1; r0 += kShRows) {
-                const int nr = min(kShRows, shH1 - r0);
-                float acc[kShRows];
+            const unsigned h_target = (unsigned)(s + 1) * sh_gu_contrib;
+            bool h_seen = false, oks = true;
+            for (int rb = shH0 + wave; rb < shH1 && oks; rb += kPW * kShDR) {
+                float acc[kShDR];
 #pragma unroll
-                for (int q = 0; q < kShRows; q++) acc[q] = 0.f;
-                for (int c = threadIdx.x * 8; c < I; c += kPW * 64 * 8) {
-                    uint4 dv[kShRows];
+                for (int d = 0; d < kShDR; d++) acc[d] = 0.f;
+                for (int c0 = 0; c0 < I && oks; c0 += 512 * kShCP) {
+                    uint4 wv[kShDR][kShCP];
 #pragma unroll
-                    for (int q = 0; q < kShRows; q++)
-                        dv[q] = *(const uint4 *)(wd0 + (size_t)min(r0 + q, shH1 - 1) * I + c);
-                    float hv[8];
+                    for (int d = 0; d < kShDR; d++)
 #pragma unroll
-                    for (int i = 0; i < 8; i++) hv[i] = hl[c + i];
+                        for (int p = 0; p < kShCP; p++) {
+                            const int r = rb + d * kPW, c = c0 + 512 * p + 8 * lane;
+                            wv[d][p] = r < shH1 && c < I ? *(const uint4 *)(wd0 + (size_t)r * I + c)
+                                                         : make_uint4(0u, 0u, 0u, 0u);
+                        }
+                    if (!h_seen) {
+                        long spins = 0;
+                        while (ld_cnt(h_ready + k * kLine) < h_target)
+                            if (!poll_more(sync, spins)) { oks = false; break; }
+                        h_seen = true;
+                    }
+                    if (!oks) break;
+                    uint64_t hv[kShCP][4];
 #pragma unroll
-                    for (int q = 0; q < kShRows; q++) {
-                        const uint32_t dq[4] = {dv[q].x, dv[q].y, dv[q].z, dv[q].w};
+                    for (int p = 0; p < kShCP; p++) {
+                        const int c = c0 + 512 * p + 8 * lane;
 #pragma unroll
-                        for (int i = 0; i < 4; i++) {
-                            acc[q] = fmaf(__uint_as_float(dq[i] << 16), hv[2 * i], acc[q]);
-                            acc[q] = fmaf(__uint_as_float(dq[i] & 0xFFFF0000u), hv[2 * i + 1], acc[q]);
+                        for (int q = 0; q < 4; q++)
+                            hv[p][q] = c < I ? ld_x((const uint64_t *)(a.hs + c) + q) : 0u;
+                    }
+#pragma unroll
+                    for (int p = 0; p < kShCP; p++) {
+                        float hf[8];
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            hf[2 * q] = __uint_as_float((uint32_t)hv[p][q]);
+                            hf[2 * q + 1] = __uint_as_float((uint32_t)(hv[p][q] >> 32));
+                        }
+#pragma unroll
+                        for (int d = 0; d < kShDR; d++) {
+                            const uint32_t dq[4] = {wv[d][p].x, wv[d][p].y, wv[d][p].z, wv[d][p].w};
+#pragma unroll
+                            for (int i = 0; i < 4; i++) {
+                                acc[d] = fmaf(__uint_as_float(dq[i] << 16), hf[2 * i], acc[d]);
+                                acc[d] = fmaf(__uint_as_float(dq[i] & 0xFFFF0000u), hf[2 * i + 1], acc[d]);
+                            }
                         }
                     }
                 }
 #pragma unroll
-                for (int q = 0; q < kShRows; q++) acc[q] = wave_sum(acc[q]);
-                if (lane == 0) {
-#pragma unroll
-                    for (int q = 0; q < kShRows; q++) shred[wave * kShRows + q] = acc[q];
+                for (int d = 0; d < kShDR; d++) {
+                    const float y = wave_sum(acc[d]);
+                    const int r = rb + d * kPW;
+                    if (oks && lane == 0 && r < shH1) st_tagged(a.ysh + r, y, tag);
                 }
-                lds_sync();
-                if (threadIdx.x < nr) {
-                    float y = 0.f;
-                    for (int v = 0; v < kPW; v++) y += shred[v * kShRows + threadIdx.x];
-                    st_tagged(a.ysh + r0 + threadIdx.x, y, tag);
-                }
-                lds_sync();
             }
+            if (!oks && lane == 0) *bcast = 0;
+            lds_sync();
+            if (!*bcast) return;
         }
 
         mark(kStampSharedDown);
@@ -1809,8 +1857,7 @@ hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
     const long red_d = (long)kCbRows * 16 + ((I * 2 + 255) & ~255) + (long)o->slots_red_d * kPW * 64 * 4;
     const bool gu_ok = (o->lut & kLutGateUp) || (red_gu <= kDecTail && kXStage + (long)H * 4 <= 2L * kCbRows * 16);
     const bool d_ok = (o->lut & kLutDown) || red_d <= kDecTail;
-    // the shared expert's fp32 h is staged below the record pointers
-    o->lds_ok = gu_ok && d_ok && (long)I * 4 + kPW * kShRows * 4 <= kDecRecs;
+    o->lds_ok = gu_ok && d_ok;
     return hipSuccess;
 }
 
