@@ -194,7 +194,6 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
                                                        int32_t *__restrict__ idx, float *__restrict__ w) {
     __shared__ __align__(16) uint64_t key[MOE_MAX_E];              // padded to a multiple of 32 with zeros
     __shared__ __align__(16) uint64_t cand[kTopkLvl * MOE_MAX_K];  // zeros past the candidates
-    __shared__ int ncand;
     __shared__ int sidx[MOE_MAX_K];
     __shared__ float sz[MOE_MAX_K];
     const int t = blockIdx.x;
@@ -202,7 +201,6 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
     for (int e = threadIdx.x; e < Ep; e += kTopkThreads)
         key[e] = e < E ? (uint64_t)topk_order_key(z[(size_t)t * E + e]) << 32 | (0xFFFFFFFFu - (uint32_t)e) : 0u;
     for (int i = threadIdx.x; i < kTopkLvl * MOE_MAX_K; i += kTopkThreads) cand[i] = 0u;
-    if (threadIdx.x == 0) ncand = 0;
     __syncthreads();
     const bool two = E > 64;
     const int gsz = two ? ((E + kTopkLvl - 1) / kTopkLvl + 31) & ~31 : Ep;
@@ -227,15 +225,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
         const int g0 = e / gsz * gsz;
         const int rank = count_above(key, g0, min(Ep, g0 + gsz), ke);
         if (rank < k) {
-            if (two) cand[atomicAdd(&ncand, 1)] = ke;
+            if (two) cand[e / gsz * k + rank] = ke;   // a slot of its own: (group, local rank)
             else place(rank, ke);
         }
     }
     if (two) {
         __syncthreads();
-        const int nc = ncand;
+        // the groups' candidates, zeros where a group had fewer than k keys
+        const int nc = (E + gsz - 1) / gsz * k;
         for (int c = threadIdx.x; c < nc; c += kTopkThreads) {
             const uint64_t ke = cand[c];
+            if (!ke) continue;
             const int rank = count_above(cand, 0, (nc + 31) & ~31, ke);
             if (rank < k) place(rank, ke);
         }

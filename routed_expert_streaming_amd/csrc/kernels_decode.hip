@@ -354,8 +354,8 @@ constexpr int kShCP = 4;        // 512-column passes of those rows in flight (I 
 constexpr int kTopkScratch = 2048;   // LDS bytes (codebook area, free while routing): top-k staging
 constexpr int kXStage = 16 * 1024;   // LDS bytes (codebook area, free while routing): fp32 x for the gathers
 constexpr int kTopkGroups = 8;       // first-level groups of the top-k
-// zkey [MOE_MAX_E], candidates [kTopkGroups * MOE_MAX_K], logits in rank order [MOE_MAX_K], count
-constexpr int kTopkCount = kTopkScratch + 8 * (MOE_MAX_E + kTopkGroups * MOE_MAX_K) + 4 * MOE_MAX_K;
+// zkey [MOE_MAX_E], candidates [kTopkGroups * MOE_MAX_K] (slot group * k + local rank), logits in
+// rank order [MOE_MAX_K]
 
 // Order-preserving key of a float (larger float, larger key; -0 and +0 one
 // key, as they compare equal) and back.
@@ -1037,7 +1037,6 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // the top-k's candidate list and count (LDS free since the last step ended)
             uint64_t *cand0 = (uint64_t *)(lds + kTopkScratch) + MOE_MAX_E;
             for (int i = threadIdx.x; i < kTopkGroups * MOE_MAX_K; i += kPW * 64) cand0[i] = 0u;
-            if (threadIdx.x == 0) *(unsigned *)(lds + kTopkCount) = 0u;
         }
 
         // ---- x as fp16 pairs into LDS (every workgroup, for gate/up), in
@@ -1248,13 +1247,12 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // For E > 64 in two levels: each key is first ranked within its
             // group (E split into kTopkGroups ranges of whole 32-key blocks);
             // keys of local rank < k are candidates (every global top-k key is
-            // one) and are ranked among themselves, so the result does not
-            // depend on the order in which they were appended.
+            // one), each in the slot (group, local rank), and are ranked among
+            // themselves.
             const int kk = __builtin_amdgcn_readfirstlane(lay.k);
             const bool two = E > 64;
             const int gsz = two ? ((E + kTopkGroups - 1) / kTopkGroups + 31) & ~31 : (E + 31) & ~31;
             uint64_t *cand = zkey + MOE_MAX_E;                  // [kTopkGroups * MOE_MAX_K], zeroed while routing began
-            unsigned *ncand = (unsigned *)(lds + kTopkCount);
             // rank of key ke among the keys at list[q0, q1) (q0, q1 multiples of 32)
             auto count_above = [&](const uint64_t *list, int q0, int q1, uint64_t ke) {
                 int r[4] = {0, 0, 0, 0};
@@ -1280,15 +1278,18 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 const int g0 = e / gsz * gsz;
                 const int rank = count_above(zkey, g0, min((E + 31) & ~31, g0 + gsz), ke);
                 if (rank < kk) {
-                    if (two) cand[__hip_atomic_fetch_add(ncand, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)] = ke;
+                    if (two) cand[e / gsz * kk + rank] = ke;   // a slot of its own: (group, local rank)
                     else place(rank, ke);
                 }
             }
             if (two) {
                 lds_sync();
-                const int nc = (int)*ncand;
+                // the groups' candidates, zeros where a group had fewer than k keys
+                // (zero is below every real key)
+                const int nc = (E + gsz - 1) / gsz * kk;
                 for (int c = threadIdx.x; c < nc; c += kPW * 64) {
                     const uint64_t ke = cand[c];
+                    if (!ke) continue;
                     const int rank = count_above(cand, 0, (nc + 31) & ~31, ke);
                     if (rank < kk) place(rank, ke);
                 }
