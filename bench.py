@@ -29,21 +29,24 @@ HBM_PEAK_GBS = 8000.0
 
 # HBM bytes per decode launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # (each scaled by the same counter on a 1 GiB device copy; the runs and the
-# factors are in profiles/k_decode_persistent_mixtral_hbm_counters.txt),
+# factors are in profiles/k_decode_persistent_<workload>_hbm_counters.txt),
 # valid for the kernel source they were taken on: reported as null once that
 # source has changed.
 DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
-                  "sha256_prefix": "b0ab1ff55c2638e5", "bytes_per_launch": 5272291208}
+                  "sha256_prefix": "acd43d9a0157f209",
+                  "bytes_per_launch": {"mixtral": 5057639682, "kimi_linear": 1253679471}}
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     import hashlib
     try:
         with open(os.path.join(ROOT, DECODE_TRAFFIC["kernel_source"]), "rb") as f:
             digest = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    return DECODE_TRAFFIC["bytes_per_launch"] if digest.startswith(DECODE_TRAFFIC["sha256_prefix"]) else None
+    if not digest.startswith(DECODE_TRAFFIC["sha256_prefix"]):
+        return None
+    return DECODE_TRAFFIC["bytes_per_launch"].get(workload)
 
 
 def log(msg: str) -> None:
@@ -288,7 +291,7 @@ def main() -> int:
         "tok_s_blocks": block_rates(step_ms, 1.0),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if cfg.name == "mixtral" else None,
+                     "traffic": measured_traffic(cfg.name),
                      "kernel": "k_decode_persistent (route, top-k, RVQ gate/up by %s, RVQ down by %s, combine; "
                                "all layers of one token per launch)" % tuple(
                                    "table lookup" if m == "lookup" else "codebook gathers"
