@@ -1690,6 +1690,12 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             const long eb = min(d1, (long)(j + 1) * tilesH * cprI);
             const uint8_t *rec = (const uint8_t *)recs[j];
             const long base = (long)j * tilesH * cprI;
+            const long tA = ea / cprI;
+            const int nt = (int)((eb - 1) / cprI - tA) + 1;
+            const _Float16 *dscale = (const _Float16 *)(rec + a.off.scales[2]);
+            // the row scales of this wave's first tile, loaded before the
+            // loop: the partial stores after it wait for no load
+            const float sc0 = wave < nt ? (float)dscale[(int)((tA + wave) % tilesH) * kTileRows + lane] : 0.f;
             int he = 0;
             if (!stream_down((const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]),
                              a.hh + (size_t)j * I, sync, h_ready + j * kLine, (unsigned)(s + 1) * tilesI, bcast, lmax,
@@ -1698,15 +1704,13 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 return;
             lds_sync();
             mark(kStampDownLoop);
-            const long tA = ea / cprI;
-            const int nt = (int)((eb - 1) / cprI - tA) + 1;
             for (int v = wave; v < nt; v += kPW) {
                 const long tau = tA + v;
                 float y = 0.f;
 #pragma unroll
                 for (int q = 0; q < kPW; q++) y += red_d[(v * kPW + q) * 64 + lane];
                 const int r = (int)(tau % tilesH) * kTileRows + lane;
-                y = ldexpf(y, he) * (float)((const _Float16 *)(rec + a.off.scales[2]))[r];
+                y = ldexpf(y, he) * (v == wave ? sc0 : (float)dscale[r]);
                 st_tagged(a.part_d + ((size_t)tau * a.slots_d + (w - range_owner(nD, G, tau * cprI))) * 64 + lane, y,
                           tag);
             }
