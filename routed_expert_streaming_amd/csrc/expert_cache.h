@@ -45,6 +45,8 @@ struct moe_cache {
     std::vector<uint8_t> filled;          // slot has had a copy enqueued
     std::vector<uint8_t> used;            // last_use has been recorded
     int32_t *h_idx = nullptr;             // pinned staging for the router's expert ids
+    hipEvent_t idx_ev = nullptr;          // recorded after the ids' copy to h_idx
+    hipEvent_t ahead_ev = nullptr;        // recorded after the look-ahead ids' copy
     int device = 0;
     // records in pageable host memory go through pinned bounce buffers
     // (allocated on first use) filled by host threads
@@ -68,4 +70,6 @@ int cache_release(moe_cache *c, int32_t slot, hipStream_t s);
 // *enqueued tells whether the copy into the slot was enqueued (then, even on
 // an error, the slot's previous contents are gone).
 hipError_t cache_copy_in(moe_cache *c, int32_t s, const void *src, hipStream_t ps, bool *enqueued);
+// Whether host memory at p is page-locked (a copy from it needs no staging).
+bool host_page_locked(const void *p);
 }  // namespace moe

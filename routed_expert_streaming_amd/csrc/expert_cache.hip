@@ -50,6 +50,9 @@ void destroy_events(moe_cache *c) {
     c->last_use.clear();
     if (c->h_idx) (void)hipHostFree(c->h_idx);
     c->h_idx = nullptr;
+    if (c->idx_ev) (void)hipEventDestroy(c->idx_ev);
+    if (c->ahead_ev) (void)hipEventDestroy(c->ahead_ev);
+    c->idx_ev = c->ahead_ev = nullptr;
     for (int b = 0; b < moe::kBounce; b++) {
         if (c->bounce_used[b]) (void)hipEventSynchronize(c->bounce_done[b]);
         if (c->bounce_done[b]) (void)hipEventDestroy(c->bounce_done[b]);
@@ -73,6 +76,8 @@ bool page_locked(const void *p) {
 }  // namespace
 
 namespace moe {
+bool host_page_locked(const void *p) { return page_locked(p); }
+
 CopyPool::CopyPool(int n) : n_((size_t)n) {
     th_.reserve(n_);
     for (int i = 0; i < n; i++) th_.emplace_back(&CopyPool::worker, this, i);
@@ -181,6 +186,8 @@ int expert_cache_create(int32_t capacity, uint64_t slot_bytes, void *pool_dev, m
         if (e == hipSuccess) e = hipEventCreateWithFlags(&c->last_use[s], hipEventDisableTiming);
     }
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_idx, 2 * MOE_MAX_K * sizeof(int32_t), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->idx_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ahead_ev, hipEventDisableTiming);
     if (e != hipSuccess) {
         destroy_events(c);
         delete c;

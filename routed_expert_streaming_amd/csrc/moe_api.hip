@@ -581,23 +581,26 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     const RecOffsets off = offsets_of(H, I);
     const int KS = down_splits(H, I, k);
 
-    // route, then everything that does not depend on the choice
+    // route; the host waits only for the expert ids, while the work that does
+    // not depend on the choice (x packing, the shared expert) runs on
     HIPCHK(launch_route_logits(L->router.weight, L->router.bias, E, H, x, MOE_DTYPE_F32, 1, W.z, cs), "route logits");
     HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, 1, idx, W.w, cs), "top-k");
     HIPCHK(hipMemcpyAsync(c->h_idx, idx, k * sizeof(int32_t), hipMemcpyDeviceToHost, cs), "idx to host");
+    HIPCHK(hipEventRecord(c->idx_ev, cs), "ids copied");
     if (ah.L) {
         // the next layer's router on this layer's input: a prediction only
         HIPCHK(launch_route_logits(ah.L->router.weight, ah.L->router.bias, ah.L->router.E, H, x, MOE_DTYPE_F32, 1, za,
                                    cs), "look-ahead logits");
         HIPCHK(launch_topk(za, ah.L->router.E, ah.k, ah.L->router.score_fn, 1, ia, wa, cs), "look-ahead top-k");
         HIPCHK(hipMemcpyAsync(h_ahead, ia, ah.k * sizeof(int32_t), hipMemcpyDeviceToHost, cs), "look-ahead ids");
+        HIPCHK(hipEventRecord(c->ahead_ev, cs), "look-ahead ids copied");
     }
     HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, 1, H, H, W.xh, W.xexp, cs), "pack_x");
     if (L->shared) {
         HIPCHK(launch_dense_gateup(L->shared, H, I, x, MOE_DTYPE_F32, H, 1, W.hs, cs), "shared gate/up");
         HIPCHK(launch_dense_down(L->shared, H, I, W.hs, 1, W.ysh, cs), "shared down");
     }
-    HIPCHK(hipStreamSynchronize(cs), "wait for routing");
+    HIPCHK(hipEventSynchronize(c->idx_ev), "wait for the expert ids");
 
     // cache bookkeeping in ascending expert id (get-or-insert, the LRU order
     // the trace records); the copies of misses are enqueued after the hit
@@ -663,10 +666,21 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         for (int q = 0; q < nm; q++) src_of[mj[q]] = ptrs[q];
     }
     // each miss: copy into its slot after the slot's previous readers, then
-    // its expert after the copy lands
-    for (int n = 0; n < k; n++) {
-        const int j = order[n];
-        if (hit[j]) continue;
+    // its expert after the copy lands.  Records in page-locked memory go
+    // first (ascending id), then pageable ones (ascending id): the host
+    // threads stage a pageable record while the copy engine moves the
+    // page-locked ones.  (The cache's operations were all done above, in
+    // ascending id; only the copies' order differs.)
+    int morder[MOE_MAX_K], nmiss = 0;
+    for (int pass = 0; pass < 2; pass++)
+        for (int n = 0; n < k; n++) {
+            const int j = order[n];
+            if (hit[j]) continue;
+            const bool locked = tier.t || host_page_locked(experts_host[c->h_idx[j]]);
+            if (locked == (pass == 0)) morder[nmiss++] = j;
+        }
+    for (int n = 0; n < nmiss; n++) {
+        const int j = morder[n];
         const int32_t s = slot_of[j];
         if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "copy waits for slot readers");
         const void *src = tier.t ? (const void *)src_of[j] : experts_host[c->h_idx[j]];
@@ -707,6 +721,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     // touched in the LRU; the absent ones are copied now, behind this layer's
     // misses on the copy stream, so they land while this layer computes.  A
     // victim slot's copy still waits for that slot's last readers.
+    HIPCHK(hipEventSynchronize(c->ahead_ev), "wait for the look-ahead ids");
     int pred[MOE_MAX_K];
     const int En = ah.L->router.E;
     for (int j = 0; j < ah.k; j++) {
