@@ -1,5 +1,5 @@
 // HIP side of the expert-slot cache: the slot pool, per-slot ready events
-// (copy landed) and last-use events (write-after-read guard for evictions).
+// (copy landed) and readers' events (write-after-read guard for evictions).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,9 +41,16 @@ struct moe_cache {
     char *pool = nullptr;                 // caller-owned device pool
     uint64_t slot_bytes = 0;
     std::vector<hipEvent_t> ready;        // recorded on the copy stream after a slot's copy
-    std::vector<hipEvent_t> last_use;     // recorded on a compute stream after the slot's readers
     std::vector<uint8_t> filled;          // slot has had a copy enqueued
-    std::vector<uint8_t> used;            // last_use has been recorded
+    // Readers' events: one event is recorded on a compute stream after the
+    // readers of a whole batch of slots (one release call), and every slot of
+    // the batch refers to it; an event no slot refers to any more is free for
+    // reuse (re-recording it then cannot delay a copy that waits for an older
+    // recording, since no slot waits for that one).
+    std::vector<hipEvent_t> use_ev;
+    std::vector<int32_t> use_refs;        // slots referring to each event
+    std::vector<int32_t> use_free;        // events with no referring slot
+    std::vector<int32_t> slot_use;        // per slot: its readers' event, or -1
     int32_t *h_idx = nullptr;             // pinned staging for the router's expert ids
     hipEvent_t idx_ev = nullptr;          // recorded after the ids' copy to h_idx
     hipEvent_t ahead_ev = nullptr;        // recorded after the look-ahead ids' copy
@@ -62,6 +69,11 @@ struct moe_cache {
 namespace moe {
 int cache_wait(moe_cache *c, int32_t slot, hipStream_t s);
 int cache_release(moe_cache *c, int32_t slot, hipStream_t s);
+// Records one event on s after the readers of n distinct slots and makes it
+// their readers' event.
+int cache_release_many(moe_cache *c, const int32_t *slots, int n, hipStream_t s);
+// Makes stream s wait for the readers of slot s_ (if any were recorded).
+hipError_t cache_wait_readers(moe_cache *c, int32_t slot, hipStream_t s);
 // Enqueue the copy of one record (slot_bytes at src, host memory) into slot
 // s on stream ps: straight from page-locked memory; from pageable memory
 // through the next bounce buffer, which host threads fill after its previous

@@ -28,13 +28,43 @@ int cache_wait(moe_cache *c, int32_t slot, hipStream_t s) {
     return MOE_OK;
 }
 
-int cache_release(moe_cache *c, int32_t slot, hipStream_t s) {
+int cache_release_many(moe_cache *c, const int32_t *slots, int n, hipStream_t s) {
     if (!c) return fail(MOE_E_INVAL, "cache is NULL");
-    if (slot < 0 || slot >= c->core.capacity()) return fail(MOE_E_STATE, "slot %d out of range", slot);
-    hipError_t e = hipEventRecord(c->last_use[slot], s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(last_use)");
-    c->used[slot] = 1;
+    for (int i = 0; i < n; i++)
+        if (slots[i] < 0 || slots[i] >= c->core.capacity()) return fail(MOE_E_STATE, "slot %d out of range", slots[i]);
+    if (n <= 0) return MOE_OK;
+    int32_t ev;
+    if (!c->use_free.empty()) {
+        ev = c->use_free.back();
+        c->use_free.pop_back();
+    } else {
+        hipEvent_t h = nullptr;
+        hipError_t e = hipEventCreateWithFlags(&h, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags(readers)");
+        ev = (int32_t)c->use_ev.size();
+        c->use_ev.push_back(h);
+        c->use_refs.push_back(0);
+    }
+    hipError_t e = hipEventRecord(c->use_ev[ev], s);
+    if (e != hipSuccess) {
+        c->use_free.push_back(ev);
+        return hip_fail(e, "hipEventRecord(readers)");
+    }
+    for (int i = 0; i < n; i++) {
+        int32_t &u = c->slot_use[slots[i]];
+        if (u == ev) continue;               // the slot appears twice in the batch
+        if (u >= 0 && --c->use_refs[u] == 0) c->use_free.push_back(u);
+        u = ev;
+        c->use_refs[ev]++;
+    }
     return MOE_OK;
+}
+
+int cache_release(moe_cache *c, int32_t slot, hipStream_t s) { return cache_release_many(c, &slot, 1, s); }
+
+hipError_t cache_wait_readers(moe_cache *c, int32_t slot, hipStream_t s) {
+    const int32_t u = c->slot_use[slot];
+    return u >= 0 ? hipStreamWaitEvent(s, c->use_ev[u], 0) : hipSuccess;
 }
 }  // namespace moe
 
@@ -44,10 +74,10 @@ namespace {
 void destroy_events(moe_cache *c) {
     for (hipEvent_t e : c->ready)
         if (e) (void)hipEventDestroy(e);
-    for (hipEvent_t e : c->last_use)
+    for (hipEvent_t e : c->use_ev)
         if (e) (void)hipEventDestroy(e);
     c->ready.clear();
-    c->last_use.clear();
+    c->use_ev.clear();
     if (c->h_idx) (void)hipHostFree(c->h_idx);
     c->h_idx = nullptr;
     if (c->idx_ev) (void)hipEventDestroy(c->idx_ev);
@@ -177,13 +207,11 @@ int expert_cache_create(int32_t capacity, uint64_t slot_bytes, void *pool_dev, m
     c->pool = (char *)pool_dev;
     c->slot_bytes = slot_bytes;
     c->ready.assign(capacity, nullptr);
-    c->last_use.assign(capacity, nullptr);
+    c->slot_use.assign(capacity, -1);
     c->filled.assign(capacity, 0);
-    c->used.assign(capacity, 0);
     hipError_t e = hipGetDevice(&c->device);
     for (int s = 0; e == hipSuccess && s < capacity; s++) {
         e = hipEventCreateWithFlags(&c->ready[s], hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&c->last_use[s], hipEventDisableTiming);
     }
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_idx, 2 * MOE_MAX_K * sizeof(int32_t), hipHostMallocDefault);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->idx_ev, hipEventDisableTiming);
@@ -218,8 +246,8 @@ int expert_cache_insert(moe_cache *c, uint32_t key, const void *host_src, void *
     if (s < 0) return fail(MOE_E_STATE, "key %u is already cached", key);
     hipStream_t cs = (hipStream_t)copy_stream;
     hipError_t e = hipSuccess;
-    if (c->used[s]) e = hipStreamWaitEvent(cs, c->last_use[s], 0);      // readers of the victim first
-    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(last_use)");
+    e = cache_wait_readers(c, s, cs);      // readers of the victim first
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(readers)");
     bool enqueued = false;
     e = moe::cache_copy_in(c, s, host_src, cs, &enqueued);
     if (e != hipSuccess) {

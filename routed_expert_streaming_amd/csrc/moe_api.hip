@@ -682,7 +682,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     for (int n = 0; n < nmiss; n++) {
         const int j = morder[n];
         const int32_t s = slot_of[j];
-        if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "copy waits for slot readers");
+        HIPCHK(cache_wait_readers(c, s, ps), "copy waits for slot readers");
         const void *src = tier.t ? (const void *)src_of[j] : experts_host[c->h_idx[j]];
         bool enqueued = false;   // the key is committed either way: a failed copy drops its slot
         hipError_t e = tier.t ? hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, src, c->slot_bytes,
@@ -712,10 +712,8 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         HIPCHK(launch_rvq_down(one, off, H, I, 1, KS, W.hh, W.ypart, cs), "rvq down (miss)");
     }
     HIPCHK(launch_combine(W.ypart, k, KS, H, W.w, L->shared ? W.ysh : nullptr, out, H, 1, 0, cs), "combine");
-    for (int j = 0; j < k; j++) {
-        rc = cache_release(c, slot_of[j], cs);
-        if (rc) return rc;
-    }
+    rc = cache_release_many(c, slot_of, k, cs);
+    if (rc) return rc;
     if (!ah.L) return MOE_OK;
     // look-ahead: the predicted keys of the next layer (ascending id) are
     // touched in the LRU; the absent ones are copied now, behind this layer's
@@ -737,7 +735,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         const int32_t s = c->core.touch_ahead(key, &victim, &inserted);
         if (!inserted) continue;
         c->filled[s] = 0;
-        if (c->used[s]) HIPCHK(hipStreamWaitEvent(ps, c->last_use[s], 0), "look-ahead copy waits for slot readers");
+        HIPCHK(cache_wait_readers(c, s, ps), "look-ahead copy waits for slot readers");
         bool enqueued = false;
         hipError_t e = cache_copy_in(c, s, ah.host[pred[j]], ps, &enqueued);
         if (e == hipSuccess) e = hipEventRecord(c->ready[s], ps);
