@@ -23,7 +23,11 @@ int cache_wait(moe_cache *c, int32_t slot, hipStream_t s) {
     if (!c) return fail(MOE_E_INVAL, "cache is NULL");
     if (slot < 0 || slot >= c->core.capacity()) return fail(MOE_E_STATE, "slot %d out of range", slot);
     if (!c->filled[slot]) return fail(MOE_E_STATE, "slot %d has never been filled", slot);
-    hipError_t e = hipStreamWaitEvent(s, c->ready[slot], 0);
+    // a copy that has landed already needs no wait on the stream
+    hipError_t e = hipEventQuery(c->ready[slot]);
+    if (e == hipSuccess) return MOE_OK;
+    if (e != hipErrorNotReady) return hip_fail(e, "hipEventQuery(ready)");
+    e = hipStreamWaitEvent(s, c->ready[slot], 0);
     if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(ready)");
     return MOE_OK;
 }
@@ -64,7 +68,12 @@ int cache_release(moe_cache *c, int32_t slot, hipStream_t s) { return cache_rele
 
 hipError_t cache_wait_readers(moe_cache *c, int32_t slot, hipStream_t s) {
     const int32_t u = c->slot_use[slot];
-    return u >= 0 ? hipStreamWaitEvent(s, c->use_ev[u], 0) : hipSuccess;
+    if (u < 0) return hipSuccess;
+    // readers long done (the usual case for an LRU victim): no wait enqueued
+    const hipError_t q = hipEventQuery(c->use_ev[u]);
+    if (q == hipSuccess) return hipSuccess;
+    if (q != hipErrorNotReady) return q;
+    return hipStreamWaitEvent(s, c->use_ev[u], 0);
 }
 }  // namespace moe
 

@@ -629,58 +629,23 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         slot_of[j] = s;
     }
 
-    // hit experts run at once
-    RecSrc hits{};
-    hits.k = k;
-    for (int n = 0; n < k; n++) {
-        const int j = order[n];
-        if (!hit[j]) continue;
-        rc = cache_wait(c, slot_of[j], cs);
-        if (rc) return rc;
-        hits.list[hits.n_local] = c->pool + (size_t)slot_of[j] * c->slot_bytes;
-        hits.rank[hits.n_local] = (uint8_t)j;
-        hits.n_local++;
-    }
-    if (hits.n_local) {
-        HIPCHK(launch_rvq_gateup(hits, off, H, I, hits.n_local, W.xh, W.xexp, W.hh, cs), "rvq gate/up (hits)");
-        HIPCHK(launch_rvq_down(hits, off, H, I, hits.n_local, KS, W.hh, W.ypart, cs), "rvq down (hits)");
-    }
-    // file tier: the misses' records into host slots (read while the hit
-    // experts compute)
-    const char *src_of[MOE_MAX_K] = {};
-    if (tier.t) {
-        int64_t recs[MOE_MAX_K];
-        int nm = 0, mj[MOE_MAX_K];
-        for (int n = 0; n < k; n++) {
-            const int j = order[n];
-            if (hit[j]) continue;
-            mj[nm] = j;
-            recs[nm++] = tier.record0 + c->h_idx[j];
-        }
-        const char *ptrs[MOE_MAX_K];
-        rc = tier_fetch(tier.t, recs, nm, ptrs);
-        if (rc) {
-            for (int q = 0; q < nm; q++) c->core.drop_slot(slot_of[mj[q]]);   // never filled
-            return rc;
-        }
-        for (int q = 0; q < nm; q++) src_of[mj[q]] = ptrs[q];
-    }
-    // each miss: copy into its slot after the slot's previous readers, then
-    // its expert after the copy lands.  Records in page-locked memory go
-    // first (ascending id), then pageable ones (ascending id): the host
-    // threads stage a pageable record while the copy engine moves the
-    // page-locked ones.  (The cache's operations were all done above, in
-    // ascending id; only the copies' order differs.)
-    int morder[MOE_MAX_K], nmiss = 0;
+    // misses in copy order: records in page-locked memory first (ascending
+    // id), then pageable ones (ascending id), so the host threads stage a
+    // pageable record while the copy engine moves the page-locked ones.  (The
+    // cache's operations were all done above, in ascending id; only the
+    // copies' order differs.)
+    int morder[MOE_MAX_K], nmiss = 0, nlocked = 0;
     for (int pass = 0; pass < 2; pass++)
         for (int n = 0; n < k; n++) {
             const int j = order[n];
             if (hit[j]) continue;
             const bool locked = tier.t || host_page_locked(experts_host[c->h_idx[j]]);
             if (locked == (pass == 0)) morder[nmiss++] = j;
+            if (locked && pass == 0) nlocked++;
         }
-    for (int n = 0; n < nmiss; n++) {
-        const int j = morder[n];
+    const char *src_of[MOE_MAX_K] = {};
+    // a miss's copy into its slot, after the slot's previous readers
+    auto copy_miss = [&](int j) -> int {
         const int32_t s = slot_of[j];
         HIPCHK(cache_wait_readers(c, s, ps), "copy waits for slot readers");
         const void *src = tier.t ? (const void *)src_of[j] : experts_host[c->h_idx[j]];
@@ -701,8 +666,13 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
             return hip_fail(e, "expert copy");
         }
         c->filled[s] = 1;
-        rc = cache_wait(c, s, cs);
-        if (rc) return rc;
+        return MOE_OK;
+    };
+    // a miss's expert, once its copy has landed
+    auto run_miss = [&](int j) -> int {
+        const int32_t s = slot_of[j];
+        int r = cache_wait(c, s, cs);
+        if (r) return r;
         RecSrc one{};
         one.k = k;
         one.n_local = 1;
@@ -710,6 +680,56 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         one.rank[0] = (uint8_t)j;
         HIPCHK(launch_rvq_gateup(one, off, H, I, 1, W.xh, W.xexp, W.hh, cs), "rvq gate/up (miss)");
         HIPCHK(launch_rvq_down(one, off, H, I, 1, KS, W.hh, W.ypart, cs), "rvq down (miss)");
+        return MOE_OK;
+    };
+    // the hit experts, all at once
+    auto run_hits = [&]() -> int {
+        RecSrc hits{};
+        hits.k = k;
+        for (int n = 0; n < k; n++) {
+            const int j = order[n];
+            if (!hit[j]) continue;
+            int r = cache_wait(c, slot_of[j], cs);
+            if (r) return r;
+            hits.list[hits.n_local] = c->pool + (size_t)slot_of[j] * c->slot_bytes;
+            hits.rank[hits.n_local] = (uint8_t)j;
+            hits.n_local++;
+        }
+        if (hits.n_local) {
+            HIPCHK(launch_rvq_gateup(hits, off, H, I, hits.n_local, W.xh, W.xexp, W.hh, cs), "rvq gate/up (hits)");
+            HIPCHK(launch_rvq_down(hits, off, H, I, hits.n_local, KS, W.hh, W.ypart, cs), "rvq down (hits)");
+        }
+        return MOE_OK;
+    };
+    if (!tier.t) {
+        // page-locked misses' copies first (the copy engine starts at once),
+        // then the hit experts, then the misses' experts
+        for (int n = 0; n < nlocked; n++)
+            if ((rc = copy_miss(morder[n]))) return rc;
+        if ((rc = run_hits())) return rc;
+        for (int n = 0; n < nlocked; n++)
+            if ((rc = run_miss(morder[n]))) return rc;
+        for (int n = nlocked; n < nmiss; n++) {
+            if ((rc = copy_miss(morder[n]))) return rc;
+            if ((rc = run_miss(morder[n]))) return rc;
+        }
+    } else {
+        // file tier: the hit experts run while the misses' records are read
+        // into host slots
+        if ((rc = run_hits())) return rc;
+        int64_t recs[MOE_MAX_K];
+        for (int n = 0; n < nmiss; n++) recs[n] = tier.record0 + c->h_idx[morder[n]];
+        const char *ptrs[MOE_MAX_K];
+        rc = tier_fetch(tier.t, recs, nmiss, ptrs);
+        if (rc) {
+            for (int n = 0; n < nmiss; n++) c->core.drop_slot(slot_of[morder[n]]);   // never filled
+            return rc;
+        }
+        for (int n = 0; n < nmiss; n++) src_of[morder[n]] = ptrs[n];
+        for (int n = 0; n < nmiss; n++) {
+            if ((rc = copy_miss(morder[n]))) return rc;
+            if ((rc = run_miss(morder[n]))) return rc;
+        }
     }
     HIPCHK(launch_combine(W.ypart, k, KS, H, W.w, L->shared ? W.ysh : nullptr, out, H, 1, 0, cs), "combine");
     rc = cache_release_many(c, slot_of, k, cs);
