@@ -32,6 +32,8 @@
 // timeout the kernel sets an error flag and all waves leave.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "rvq_device.h"
 
@@ -1127,23 +1129,25 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // further groups with all waves after the poll.
         const bool sh_rows = shared_on && shI1 > shI0;
         float *shred = (float *)lds;   // [kPW][2 * kShRows], codebook area (free until gate/up)
-        auto shared_partials = [&](int r0, int t, int nthr) {
+        // (NR rows per group: 4 where a workgroup has at most 4 rows)
+        auto shared_partials = [&](auto nr_tag, int r0, int t, int nthr) {
+            constexpr int NR = decltype(nr_tag)::value;
             const uint16_t *wg0 = lay.shared, *wu0 = lay.shared + (size_t)I * H;
-            float g[kShRows], u[kShRows];
+            float g[NR], u[NR];
 #pragma unroll
-            for (int q = 0; q < kShRows; q++) g[q] = u[q] = 0.f;
+            for (int q = 0; q < NR; q++) g[q] = u[q] = 0.f;
             for (int c = t * 8; c < H; c += nthr * 8) {
                 const float4 xa = *(const float4 *)(xs + c), xb = *(const float4 *)(xs + c + 4);
-                uint4 gv[kShRows], uv[kShRows];
+                uint4 gv[NR], uv[NR];
 #pragma unroll
-                for (int q = 0; q < kShRows; q++) {
+                for (int q = 0; q < NR; q++) {
                     const size_t o = (size_t)min(r0 + q, shI1 - 1) * H + c;
                     gv[q] = *(const uint4 *)(wg0 + o);
                     uv[q] = *(const uint4 *)(wu0 + o);
                 }
                 const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-                for (int q = 0; q < kShRows; q++) {
+                for (int q = 0; q < NR; q++) {
                     const uint32_t gq[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
                     const uint32_t uq[4] = {uv[q].x, uv[q].y, uv[q].z, uv[q].w};
 #pragma unroll
@@ -1156,13 +1160,13 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 }
             }
 #pragma unroll
-            for (int q = 0; q < kShRows; q++) {
+            for (int q = 0; q < NR; q++) {
                 g[q] = wave_sum(g[q]);
                 u[q] = wave_sum(u[q]);
             }
             if (lane == 0) {
 #pragma unroll
-                for (int q = 0; q < kShRows; q++) {
+                for (int q = 0; q < NR; q++) {
                     shred[wave * 2 * kShRows + q] = g[q];
                     shred[wave * 2 * kShRows + kShRows + q] = u[q];
                 }
@@ -1214,7 +1218,11 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             }
             if (lane == 0) *bcast = okw;
         } else if (sh_rows) {
-            shared_partials(shI0, (int)threadIdx.x - 64, (kPW - 1) * 64);
+            if (shI1 - shI0 <= 4)
+                shared_partials(std::integral_constant<int, 4>{}, shI0, (int)threadIdx.x - 64, (kPW - 1) * 64);
+            else
+                shared_partials(std::integral_constant<int, kShRows>{}, shI0, (int)threadIdx.x - 64,
+                                (kPW - 1) * 64);
         }
         lds_sync();
         if (!*bcast) return;
@@ -1236,7 +1244,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             shared_finish(shI0, 1);
             for (int r0 = shI0 + kShRows; r0 < shI1; r0 += kShRows) {
                 lds_sync();
-                shared_partials(r0, threadIdx.x, kPW * 64);
+                shared_partials(std::integral_constant<int, kShRows>{}, r0, threadIdx.x, kPW * 64);
                 lds_sync();
                 shared_finish(r0, 0);
             }
