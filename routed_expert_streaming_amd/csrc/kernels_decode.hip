@@ -1326,6 +1326,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // staging) or, at the latest, before this workgroup's first wait on
         // another workgroup (the joins), so the count never waits on them
         bool sh_counted = !(sh_rows && wave == 1);
+        // the shared h counter, loaded after the gate/up loop (its round trip
+        // overlaps the joins): where it already shows every row, the shared
+        // down needs no poll of its own
+        unsigned sh_early = 0;
         auto count_shared = [&] {
             if (!sh_counted) {
                 wait_vm_all();
@@ -1361,6 +1365,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             lds_sync();
             mark(kStampGuLoop);
             count_shared();
+            if (shared_on) sh_early = ld_cnt(h_ready + k * kLine);
             // joins: tiles tau = w + G i of all ranks' k * tilesI tiles, two at
             // a time.  Wave v polls slots v, v + kPW, ... of both tiles (all its
             // loads in flight together: one round trip once the partials have
@@ -1474,6 +1479,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             sh_counted = true;
             lds_sync();
             mark(kStampGuLoop);
+            if (shared_on) sh_early = ld_cnt(h_ready + k * kLine);
             // one tagged partial per touched tile (wave v: tiles v, v + kPW,
             // ...); the workgroup owning a tile's last unit joins it (one
             // wave per tile) into fp16 SiLU(g) * u once every contributor's
@@ -1544,9 +1550,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // ---- shared down rows, tagged: wave v takes the workgroup's rows
         // shH0 + v, shH0 + v + kPW, ..., kShDR at a time, lane l columns
         // 8 l + 512 m.  A wave issues its rows' weight loads, then waits for
-        // the whole shared h (its own poll of the counter), then loads h
-        // (coherent loads) and sums: no workgroup barrier, and the weights'
-        // round trip overlaps the wait.
+        // the whole shared h (its own poll of the counter, unless the value
+        // loaded after gate/up already showed it), then loads h (coherent
+        // loads) and sums: no workgroup barrier, and the weights' round trip
+        // overlaps the wait.
         count_shared();
         if (shared_on && shH1 > shH0) {
             const uint16_t *wd0 = lay.shared + 2 * (size_t)I * H;
@@ -1566,12 +1573,12 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                             wv[d][p] = r < shH1 && c < I ? *(const uint4 *)(wd0 + (size_t)r * I + c)
                                                          : make_uint4(0u, 0u, 0u, 0u);
                         }
-                    if (!h_seen) {
+                    if (!h_seen && sh_early < h_target) {
                         long spins = 0;
                         while (ld_cnt(h_ready + k * kLine) < h_target)
                             if (!poll_more(sync, spins)) { oks = false; break; }
-                        h_seen = true;
                     }
+                    h_seen = true;
                     if (!oks) break;
                     uint64_t hv[kShCP][4];
 #pragma unroll
