@@ -46,16 +46,16 @@ constexpr long kSpinLimit = 1L << 24;  // x ~0.1 us per poll: a few seconds
 constexpr int kDecLdsBytes = 160 * 1024;
 
 // Counter words, each on its own 256-byte line (pollers of one counter do
-// not contend with adders of another): the error flag, kLayerCopies
-// layer-done counters (output tile td adds to copy td % kLayerCopies; a
-// waiter sums them), then h_ready[j] for j = 0..k (k: the shared expert).
+// not contend with adders of another): the error flag, up to kLayerCopiesMax
+// layer-done counters (the kernel's LC of them: output unit u adds to copy
+// u % LC; a waiter sums them), then h_ready[j] for j = 0..k (k: the shared expert).
 // Word kErr is this launch's abort flag (zeroed before every launch, polled
 // by every wait); word kStatus, on the same line, keeps kStatusFailed from a
 // failed launch until the host reads and resets it, so a failure is seen
 // even when later launches on the workspace succeed.
 constexpr int kLine = 64;          // words per counter line
-constexpr int kLayerCopies = 8;
-enum SyncIdx { kErr = 0, kStatus = 1, kLayerDone = kLine, kHReady = kLine * (1 + kLayerCopies) };
+constexpr int kLayerCopiesMax = 16;
+enum SyncIdx { kErr = 0, kStatus = 1, kLayerDone = kLine, kHReady = kLine * (1 + kLayerCopiesMax) };
 
 // Mark this launch as failed: every wait then leaves, and the sticky status
 // records it.
@@ -861,7 +861,7 @@ __device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k,
 // and counts the slice on the layer-done counter.  Returns false on a failed
 // wait (the same on every wave).
 constexpr int kSliceRows = 16;
-template <int NB>
+template <int NB, int LC>
 __device__ __forceinline__ bool combine_slice_lut(int sl, int s, unsigned tag, int k, int tilesH, int cprI, int H,
                                                   bool shared_on, const uint64_t *part_d, const uint64_t *ysh,
                                                   float *out, const float *fj, unsigned *sync, int *bcast, int wave,
@@ -925,7 +925,7 @@ __device__ __forceinline__ bool combine_slice_lut(int sl, int s, unsigned tag, i
             if (lane < kSliceRows) out[(size_t)s * H + r] = o;
             // counted at once: nothing in this launch reads the outputs
             if (lane == 0)
-                __hip_atomic_fetch_add(sync + kLayerDone + (sl % kLayerCopies) * kLine, 1u, __ATOMIC_RELAXED,
+                __hip_atomic_fetch_add(sync + kLayerDone + (sl % LC) * kLine, 1u, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
         } else if (lane == 0) {
             *bcast = 0;
@@ -960,6 +960,9 @@ struct DecArgs {
     int stamp_steps;
 };
 
+// LC: layer-done counter copies (8 where a step has few output units, 16
+// where it has many: fewer adders per copy, more words per wait)
+template <int LC>
 __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_decode_persistent(DecArgs a) {
     char *lds = dec_lds;
     const DecLds LL = dec_lds_layout(a.H, a.I);
@@ -1028,8 +1031,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // after top-k
         for (int e = threadIdx.x; e < E; e += kPW * 64) recs_all[e] = (uint64_t)lay.records[e];
         // output units per step: 64-row tiles, or 16-row slices (down by table lookup)
-        if (s > 0 && !wg_wait<kLayerCopies>(sync, sync + kLayerDone,
-                                            (unsigned)s * ((a.lut & kLutDown) ? H / kSliceRows : tilesH), bcast))
+        if (s > 0 && !wg_wait<LC>(sync, sync + kLayerDone,
+                                 (unsigned)s * ((a.lut & kLutDown) ? H / kSliceRows : tilesH), bcast))
             return;
         if (s == 0) lds_sync();
         mark(kStampLayerWait);
@@ -1691,7 +1694,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     if (fj_entry) fj[threadIdx.x] = sw[threadIdx.x / kSliceRows] * (float)scale_of(sl);
                     fj_done = true;
                 }
-                if (!combine_slice_lut<8>(sl, s, tag, k, tilesH, cprI, H, shared_on, a.part_d, a.ysh, a.out, fj, sync,
+                if (!combine_slice_lut<8, LC>(sl, s, tag, k, tilesH, cprI, H, shared_on, a.part_d, a.ysh, a.out, fj, sync,
                                           bcast, wave, lane))
                     return;
             }
@@ -1752,7 +1755,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 // counted at once: nothing in this launch reads the outputs, and
                 // the partials it read are consumed (their values are used)
                 if (okc && lane == 0)
-                    __hip_atomic_fetch_add(sync + kLayerDone + (td % kLayerCopies) * kLine, 1u, __ATOMIC_RELAXED,
+                    __hip_atomic_fetch_add(sync + kLayerDone + (td % LC) * kLine, 1u, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
             }
             if (lane == 0 && !okc) *bcast = 0;
@@ -1837,20 +1840,23 @@ hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
     bool &lds_at_zero = lds_zero_dev[dev];
     if (G == 0) {
         hipFuncAttributes fa;
-        hipError_t ea = hipFuncGetAttributes(&fa, (const void *)k_decode_persistent);
-        if (ea != hipSuccess) return ea;
-        lds_at_zero = fa.sharedSizeBytes == 0;
-        int cus = 0, per = 0;
+        const void *fns[2] = {(const void *)k_decode_persistent<8>, (const void *)k_decode_persistent<16>};
+        int cus = 0, per_min = 1 << 30;
         hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void *)k_decode_persistent, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)decode_lds());
-        if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void *)k_decode_persistent, kPW * 64,
-                                                             decode_lds());
+        lds_at_zero = true;
+        for (const void *fn : fns) {
+            hipFuncAttributes fa;
+            if (e == hipSuccess) e = hipFuncGetAttributes(&fa, fn);
+            if (e == hipSuccess) lds_at_zero = lds_at_zero && fa.sharedSizeBytes == 0;
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_lds());
+            int per = 0;
+            if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kPW * 64, decode_lds());
+            per_min = std::min(per_min, per);
+        }
         if (e != hipSuccess) return e;
-        if (per < 1) return hipErrorInvalidConfiguration;
-        G = cus * per;
+        if (per_min < 1) return hipErrorInvalidConfiguration;
+        G = cus * per_min;
     }
     const int tilesI = I / kTileRows, tilesH = H / kTileRows, cprH = H / kChunkCols, cprI = I / kChunkCols;
     o->G = G;
@@ -1923,10 +1929,10 @@ hipError_t launch_decode_persistent(const DecodeLaunch &d, hipStream_t s) {
     a.stamps = d.stamps;
     a.stamp_steps = d.stamp_steps;
     (void)tilesI;
-    (void)tilesH;
     void *args[] = {&a};
-    return hipLaunchCooperativeKernel((const void *)k_decode_persistent, dim3(d.G), dim3(kPW * 64), args,
-                                      (unsigned)decode_lds(), s);
+    const int out_units = (d.lut & kLutDown) ? d.H / kSliceRows : tilesH;   // output units per step
+    const void *fn = out_units >= 128 ? (const void *)k_decode_persistent<16> : (const void *)k_decode_persistent<8>;
+    return hipLaunchCooperativeKernel(fn, dim3(d.G), dim3(kPW * 64), args, (unsigned)decode_lds(), s);
 }
 
 }  // namespace moe
