@@ -57,6 +57,7 @@ def lib():
         L.oracle_layer.argtypes = [P, P, I32, I32, I32, P, P, I32, I32, P, I32, P, P, P]
         L.oracle_lru.argtypes = [P, I64, I32, P, P, P]
         L.oracle_stream_trace.argtypes = [P, I64, I32, I32, I32, I32, I32, P, P, P, P]
+        L.oracle_two_tier.argtypes = [P, I64, I32, I32, P, P, P, P, P, P, P]
         L.oracle_set_threads.argtypes = [I32]
         L.oracle_get_threads.restype = I32
         _lib = L
@@ -184,6 +185,22 @@ def lru(keys, capacity: int):
     ev = np.zeros(n, np.int64)
     _check(lib().oracle_lru(_p(keys), n, capacity, _p(hit), _p(slot), _p(ev)), "lru")
     return hit, slot, ev
+
+
+def two_tier(keys, c1: int, c2: int):
+    """Two exclusive LRU tiers (upper c1 slots, lower c2 slots) over a key
+    sequence.  Returns a dict of arrays: hit1, slot1, ev1 (upper tier, as
+    lru), hit2 (-1 upper hit, 0 absent below, 1 found below), slot2 (lower
+    slot it was found in, -1), dslot and dev (lower slot the upper victim went
+    to, key that left the lower tier for it; -1 if none)."""
+    keys = _c(keys, np.int64)
+    n = keys.size
+    out = {"hit1": np.zeros(n, np.int32), "slot1": np.zeros(n, np.int32), "ev1": np.zeros(n, np.int64),
+           "hit2": np.zeros(n, np.int32), "slot2": np.zeros(n, np.int32), "dslot": np.zeros(n, np.int32),
+           "dev": np.zeros(n, np.int64)}
+    _check(lib().oracle_two_tier(_p(keys), n, c1, c2, _p(out["hit1"]), _p(out["slot1"]), _p(out["ev1"]),
+                                 _p(out["hit2"]), _p(out["slot2"]), _p(out["dslot"]), _p(out["dev"])), "two_tier")
+    return out
 
 
 def stream_trace(idx, nlayers: int, E: int, capacity: int, layer0: int = 0):

@@ -508,3 +508,152 @@ int oracle_stream_trace(const int32_t *idx, int64_t steps, int nlayers, int laye
     free(sorted);
     return oracle_lru(key, steps * k, capacity, hit, slot, evicted);
 }
+
+/* --------------------------------------------- two tiers, exclusive LRU */
+
+/* One LRU level with explicit slots: key_of[s] (-1 free), recency order as
+ * a doubly linked list (most recent at the head).  Used by the two-tier
+ * model below; written out on its own so that a freed slot is visible. */
+typedef struct {
+    int cap;
+    int64_t *key_of;
+    int *prev, *next;
+    int head, tail;
+} level_t;
+
+static int level_init(level_t *L, int cap)
+{
+    L->cap = cap;
+    L->key_of = malloc(sizeof(int64_t) * (cap > 0 ? cap : 1));
+    L->prev = malloc(sizeof(int) * (cap > 0 ? cap : 1));
+    L->next = malloc(sizeof(int) * (cap > 0 ? cap : 1));
+    L->head = L->tail = -1;
+    if (!L->key_of || !L->prev || !L->next)
+        return -2;
+    for (int s = 0; s < cap; s++)
+        L->key_of[s] = -1;
+    return 0;
+}
+
+static void level_free(level_t *L)
+{
+    free(L->key_of);
+    free(L->prev);
+    free(L->next);
+}
+
+static int level_find(const level_t *L, int64_t key)
+{
+    for (int s = L->head; s != -1; s = L->next[s])
+        if (L->key_of[s] == key)
+            return s;
+    return -1;
+}
+
+static void level_unlink(level_t *L, int s)
+{
+    if (L->prev[s] != -1)
+        L->next[L->prev[s]] = L->next[s];
+    else
+        L->head = L->next[s];
+    if (L->next[s] != -1)
+        L->prev[L->next[s]] = L->prev[s];
+    else
+        L->tail = L->prev[s];
+}
+
+static void level_push_head(level_t *L, int s)
+{
+    L->prev[s] = -1;
+    L->next[s] = L->head;
+    if (L->head != -1)
+        L->prev[L->head] = s;
+    L->head = s;
+    if (L->tail == -1)
+        L->tail = s;
+}
+
+/* Put key at the head: the lowest free slot, else the tail key's slot (that
+ * key is evicted: *evicted, else -1).  Returns the slot. */
+static int level_insert(level_t *L, int64_t key, int64_t *evicted)
+{
+    int s = -1;
+    *evicted = -1;
+    for (int f = 0; f < L->cap; f++)
+        if (L->key_of[f] == -1) {
+            s = f;
+            break;
+        }
+    if (s < 0) {
+        s = L->tail;
+        *evicted = L->key_of[s];
+        level_unlink(L, s);
+    }
+    L->key_of[s] = key;
+    level_push_head(L, s);
+    return s;
+}
+
+/* Two exclusive LRU tiers: an upper tier of c1 slots (the HBM cache) and a
+ * lower tier of c2 slots (host memory) in front of a backing store (the
+ * file).  Each key is looked up in the upper tier; a hit moves it to the
+ * upper tier's head.  On a miss the key is looked up in the lower tier: if
+ * there, it leaves the lower tier (its slot becomes free) and its record is
+ * the source of the copy, else the record comes from the backing store.  The
+ * key is then inserted in the upper tier like oracle_lru (lowest free slot,
+ * else the upper tier's least recently used key is evicted), and an evicted
+ * key moves down: it is inserted at the lower tier's head (lowest free slot,
+ * else the lower tier's least recently used key leaves both tiers).  WISP
+ * "통찰" (each lookup goes to the fastest tier that holds the expert; LRU
+ * promotes the experts in use) read as an exclusive hierarchy: a record is in
+ * at most one tier, the upper tier's victims fill the lower one.
+ * Per key i:
+ *   hit1, slot1, ev1: the upper tier, as oracle_lru;
+ *   hit2: -1 (no lower lookup: upper hit), 0 absent, 1 found there;
+ *   slot2: the lower slot the key was found in, else -1;
+ *   dslot, dev: the lower slot the upper tier's evicted key went to and the
+ *   key that left the lower tier for it (-1 if none). */
+int oracle_two_tier(const int64_t *keys, int64_t n, int c1, int c2,
+                    int32_t *hit1, int32_t *slot1, int64_t *ev1,
+                    int32_t *hit2, int32_t *slot2, int32_t *dslot, int64_t *dev)
+{
+    if (c1 < 1 || c2 < 1)
+        return -1;
+    level_t up, lo;
+    int rc = level_init(&up, c1);
+    if (!rc)
+        rc = level_init(&lo, c2);
+    if (rc) {
+        level_free(&up);
+        return rc;
+    }
+    for (int64_t i = 0; i < n; i++) {
+        hit2[i] = -1;
+        slot2[i] = -1;
+        dslot[i] = -1;
+        dev[i] = -1;
+        ev1[i] = -1;
+        int s = level_find(&up, keys[i]);
+        if (s >= 0) {
+            hit1[i] = 1;
+            level_unlink(&up, s);
+            level_push_head(&up, s);
+            slot1[i] = s;
+            continue;
+        }
+        hit1[i] = 0;
+        int h = level_find(&lo, keys[i]);
+        hit2[i] = h >= 0;
+        if (h >= 0) {
+            slot2[i] = h;
+            level_unlink(&lo, h);
+            lo.key_of[h] = -1;
+        }
+        slot1[i] = level_insert(&up, keys[i], &ev1[i]);
+        if (ev1[i] != -1)
+            dslot[i] = level_insert(&lo, ev1[i], &dev[i]);
+    }
+    level_free(&up);
+    level_free(&lo);
+    return 0;
+}
