@@ -662,8 +662,11 @@ def bench_sweep_tiers(args, cfg) -> int:
     """Three tiers (WISP: VRAM, then RAM, then NVMe): the first two layers of
     the K3 slice (1536 records, 18.5 GB) in a file read with O_DIRECT, behind
     a pinned host pool and the HBM slot cache, both cold.  Runs: host pool of
-    25% of the records, and of only k records (nearly every HBM miss read
-    from the file).  The file is written, synced, used, and removed."""
+    25% of the records kept inclusive (every HBM miss passes through it), of
+    only k records (nearly every HBM miss read from the file), and 25% kept as
+    the HBM cache's exclusive lower tier (it holds the HBM cache's evicted
+    records; its pool has MOE_MAX_K more pages for records in transit).  The
+    file is written, synced, used, and removed."""
     import numpy as np
     import torch
 
@@ -691,10 +694,11 @@ def bench_sweep_tiers(args, cfg) -> int:
         copy_stream = torch.cuda.Stream()
         hbm_slots = n_rec // 4
         runs = []
-        for ram_slots in (n_rec // 4, ck.k):
+        for ram_slots, exclusive in ((n_rec // 4, False), (ck.k, False), (n_rec // 4, True)):
             pool = torch.empty(hbm_slots * stride, dtype=torch.uint8, device="cuda")
             cache = moe.ExpertCache(hbm_slots, stride, pool)
-            tier = moe.HostTier(path, stride, n_rec, ram_slots, io_threads=args.io_threads)
+            tier = moe.HostTier(path, stride, n_rec, ram_slots + (moe.MOE_MAX_K if exclusive else 0),
+                                io_threads=args.io_threads, exclusive=exclusive)
 
             def token(t):
                 for L in range(ck.layers):
@@ -713,14 +717,17 @@ def bench_sweep_tiers(args, cfg) -> int:
             c1, s1 = cache.stats(), tier.stats()
             dc = {q: c1[q] - c0[q] for q in c1}
             dt = {q: s1[q] - s0[q] for q in s1}
-            runs.append({"hbm_slots": hbm_slots, "host_slots": ram_slots, "tok_s": round(args.steps / elapsed, 3),
+            runs.append({"hbm_slots": hbm_slots, "host_slots": ram_slots,
+                         "host_policy": "exclusive" if exclusive else "inclusive",
+                         "tok_s": round(args.steps / elapsed, 3),
                          "layers_per_token": ck.layers,
                          "hbm_hit_rate": round(dc["hits"] / max(1, dc["lookups"]), 4),
                          "host_hit_rate": round(dt["hits"] / max(1, dt["lookups"]), 4),
                          "file_reads_per_token": round(dt["reads"] / args.steps, 2),
                          "file_read_gbs": round(dt["read_bytes"] / max(1, dt["read_ns"]), 2),
-                         "file_gb_per_token": round(dt["read_bytes"] / args.steps / 1e9, 3)})
-            log(f"host slots {ram_slots}: {runs[-1]}")
+                         "file_gb_per_token": round(dt["read_bytes"] / args.steps / 1e9, 3),
+                         "demotions_per_token": round(dt["demotions"] / args.steps, 2)})
+            log(f"host slots {ram_slots} ({runs[-1]['host_policy']}): {runs[-1]}")
             tier.close()
             cache.close()
             del pool

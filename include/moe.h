@@ -142,6 +142,9 @@ typedef struct moe_trace_rec {
     uint32_t key;       /* layer_id * E + expert                                  */
     int32_t hit;        /* 1 = hit, 0 = miss; look-ahead touches (not lookups):   */
                         /* 2 = inserted ahead, 3 = already present (moved to MRU) */
+                        /* exclusive host tier: 4 = lookup found nothing (nothing */
+                        /* inserted, slot -1), 5 = the HBM cache's evicted key    */
+                        /* moved in                                               */
     int32_t slot;       /* slot holding the key after the lookup                  */
     uint32_t evicted;   /* key evicted by this miss, or MOE_NO_KEY                */
 } moe_trace_rec;
@@ -413,6 +416,26 @@ typedef struct moe_host_tier moe_host_tier;
  * O_DIRECT or is shorter than n_records records. */
 int moe_host_tier_create(const char *path, uint64_t record_bytes, int64_t n_records, int32_t slots,
                          void *pinned_pool, int32_t io_threads, moe_host_tier **out);
+/* The same file tier as an exclusive lower tier of the HBM cache (WISP
+ * "통찰": each lookup goes to the fastest tier that holds the expert, read as
+ * a hierarchy where a record sits in one tier at a time).  In
+ * moe_layer_forward_streamed_tiered, per key of the layer in ascending expert
+ * id: an HBM miss looks the key up here; a key found here leaves this tier
+ * and its slot is the copy's source, else the record is read from the file
+ * into a transit page; the key is inserted in the HBM cache, and the key the
+ * HBM cache evicts (if its slot was filled) moves here, at the most recent
+ * end, its bytes copied device-to-host from its HBM slot on the copy stream
+ * before the slot is overwritten (this tier evicts its own least recently
+ * used key if full).  The two tiers then hold the c1 + c2 most recently used
+ * keys, as one LRU of their combined size would (the oracle's two_tier
+ * model).  Keys are the HBM cache's keys (layer_id * E + e), so record0 must
+ * equal layer_id * E.  The pool holds `slots` records: slots - MOE_MAX_K are
+ * the LRU's capacity, MOE_MAX_K are transit pages for one layer call's
+ * copies.  MOE_E_INVAL as moe_host_tier_create, or if slots <= MOE_MAX_K. */
+int moe_host_tier_create_exclusive(const char *path, uint64_t record_bytes, int64_t n_records, int32_t slots,
+                                   void *pinned_pool, int32_t io_threads, moe_host_tier **out);
+/* Keys moved into an exclusive host tier from the HBM cache since creation. */
+int moe_host_tier_demotions(moe_host_tier *t, int64_t *demotions);
 /* Waits for the copies still reading the pool, closes the file. */
 void moe_host_tier_destroy(moe_host_tier *t);
 /* Counters since creation: lookups and hits of the host slots, records read

@@ -16,7 +16,7 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_E_INVAL, MOE_NO_KEY, MOE_SCORE_SIGMOID,
+from ._lib import (MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_E_INVAL, MOE_MAX_K, MOE_NO_KEY, MOE_SCORE_SIGMOID,
                    MOE_SCORE_SOFTMAX, MoeError, MoeLayer, MoeRecordLayout, MoeRouter,
                    MoeTraceRec, check, lib)
 
@@ -367,15 +367,22 @@ def lru_hits_at(dist, capacities: Sequence[int]) -> List[int]:
 class HostTier:
     """Expert records in a file (moe_host_tier_*): O_DIRECT reads into a
     pinned pool of `slots` records kept as LRU, the source of the HBM
-    cache's misses in layer_forward_streamed(..., tier=(this, record0))."""
+    cache's misses in layer_forward_streamed(..., tier=(this, record0)).
+    exclusive=True makes it the HBM cache's exclusive lower tier
+    (moe_host_tier_create_exclusive): it holds the HBM cache's evicted
+    records, slots - MOE_MAX_K of them, and the pool has MOE_MAX_K more
+    pages for records in transit."""
 
-    def __init__(self, path: str, record_bytes: int, n_records: int, slots: int, io_threads: int = 8):
+    def __init__(self, path: str, record_bytes: int, n_records: int, slots: int, io_threads: int = 8,
+                 exclusive: bool = False):
         self.pool = torch.empty(slots * record_bytes + 4096, dtype=torch.uint8, pin_memory=True)
         base = (self.pool.data_ptr() + 4095) & ~4095
         h = ctypes.c_void_p()
-        check(lib().moe_host_tier_create(path.encode(), record_bytes, n_records, slots, base, io_threads,
-                                         ctypes.byref(h)), "moe_host_tier_create")
+        fn = lib().moe_host_tier_create_exclusive if exclusive else lib().moe_host_tier_create
+        check(fn(path.encode(), record_bytes, n_records, slots, base, io_threads, ctypes.byref(h)),
+              "moe_host_tier_create_exclusive" if exclusive else "moe_host_tier_create")
         self.handle = h
+        self.exclusive = exclusive
 
     def close(self):
         if self.handle:
@@ -391,7 +398,11 @@ class HostTier:
     def stats(self):
         v = [ctypes.c_int64() for _ in range(5)]
         check(lib().moe_host_tier_stats(self.handle, *[ctypes.byref(x) for x in v]), "moe_host_tier_stats")
-        return dict(zip(("lookups", "hits", "reads", "read_bytes", "read_ns"), [x.value for x in v]))
+        d = dict(zip(("lookups", "hits", "reads", "read_bytes", "read_ns"), [x.value for x in v]))
+        dm = ctypes.c_int64()
+        check(lib().moe_host_tier_demotions(self.handle, ctypes.byref(dm)), "moe_host_tier_demotions")
+        d["demotions"] = dm.value
+        return d
 
     def trace(self):
         """List of (key, hit, slot, evicted or None); keys are record indices."""

@@ -75,6 +75,8 @@ SIGNATURES = {
     "expert_cache_stats_ahead": (ctypes.c_int, [P, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                                 ctypes.POINTER(I64), ctypes.POINTER(I64)]),
     "moe_host_tier_create": (ctypes.c_int, [ctypes.c_char_p, U64, I64, I32, P, I32, ctypes.POINTER(P)]),
+    "moe_host_tier_create_exclusive": (ctypes.c_int, [ctypes.c_char_p, U64, I64, I32, P, I32, ctypes.POINTER(P)]),
+    "moe_host_tier_demotions": (ctypes.c_int, [P, ctypes.POINTER(I64)]),
     "moe_host_tier_destroy": (None, [P]),
     "moe_host_tier_stats": (ctypes.c_int, [P, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64),
                                            ctypes.POINTER(I64), ctypes.POINTER(I64)]),

@@ -91,6 +91,18 @@ int LruCore::touch_ahead(uint32_t key, uint32_t *victim, bool *inserted) {
     return s;
 }
 
+int LruCore::probe(uint32_t key) {
+    const int s = lookup(key);
+    if (s < 0) trace_.push_back({key, kTraceAbsent, -1, kNoKey});
+    return s;
+}
+
+int LruCore::insert_kind(uint32_t key, int32_t kind, uint32_t *victim) {
+    const int s = plan_insert(key, victim);
+    if (s >= 0) insert_at(key, s, *victim, kind);
+    return s;
+}
+
 void LruCore::drop_slot(int slot) {
     const uint32_t k = key_of_[slot];
     if (k == kNoKey) return;

@@ -25,6 +25,8 @@ enum TraceKind : int32_t {
     kTraceHit = 1,           // lookup hit; the key moved to MRU
     kTraceAheadInsert = 2,   // look-ahead: key absent, inserted ahead of its lookup
     kTraceAheadPresent = 3,  // look-ahead: key present, moved to MRU
+    kTraceAbsent = 4,        // lower tier of two: lookup found nothing, nothing inserted
+    kTraceDemote = 5,        // lower tier of two: the upper tier's victim inserted
 };
 
 struct CacheTraceRec {
@@ -60,6 +62,15 @@ public:
     // Either way the LRU order changes as it would for a lookup of the key,
     // but the lookup and hit counters do not.
     int touch_ahead(uint32_t key, uint32_t *victim, bool *inserted);
+
+    // Lookup that also records a miss (kTraceAbsent, slot -1) and inserts
+    // nothing: the lower tier of two exclusive tiers, whose keys arrive only
+    // by demotion.  A hit moves the key to MRU as lookup() does.
+    int probe(uint32_t key);
+
+    // Insert an absent key (kind: the trace record's kind) at the slot and
+    // with the victim plan_insert gives; returns the slot, -1 if present.
+    int insert_kind(uint32_t key, int32_t kind, uint32_t *victim);
 
     // Forget whatever key a slot holds (the slot becomes free).
     void drop_slot(int slot);

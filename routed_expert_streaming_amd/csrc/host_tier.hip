@@ -43,6 +43,48 @@ bool read_record(int fd, char *dst, uint64_t bytes, int64_t index) {
 }
 }  // namespace
 
+// Records recs[q] into dst[q] (q < nt), spread over the I/O threads; on a
+// failed read returns an error with *bad = its index.
+int read_parallel(moe_host_tier *t, const int64_t *recs, char *const *dst, int nt, int *bad) {
+    if (!nt) return MOE_OK;
+    const auto t0 = std::chrono::steady_clock::now();
+    bool ok[MOE_MAX_K];
+    int err[MOE_MAX_K];
+    const int nthr = std::min(nt, t->io_threads);
+    auto worker = [&](int w) {
+        for (int q = w; q < nt; q += nthr) {
+            errno = 0;
+            ok[q] = read_record(t->fd, t->bounce[w], t->record_bytes, recs[q]);
+            err[q] = ok[q] ? 0 : (errno ? errno : EIO);
+            if (ok[q]) memcpy(dst[q], t->bounce[w], t->record_bytes);
+        }
+    };
+    if (nthr <= 1) {
+        worker(0);
+    } else {
+        std::thread th[MOE_MAX_K];
+        int started = 0;
+        try {
+            for (int w = 1; w < nthr; w++, started++) th[w] = std::thread(worker, w);
+        } catch (...) {
+        }
+        worker(0);
+        for (int w = 1; w <= started; w++) th[w].join();
+        for (int w = started + 1; w < nthr; w++) worker(w);   // threads that could not start
+    }
+    t->read_ns += (int64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0)
+                      .count();
+    for (int q = 0; q < nt; q++) {
+        if (!ok[q]) {
+            *bad = q;
+            return fail(MOE_E_HIP, "read of record %lld failed: %s", (long long)recs[q], strerror(err[q]));
+        }
+        t->reads++;
+        t->read_bytes += (int64_t)t->record_bytes;
+    }
+    return MOE_OK;
+}
+
 int tier_fetch(moe_host_tier *t, const int64_t *recs, int n, const char **ptrs) {
     if (n > t->core.capacity())
         return fail(MOE_E_INVAL, "%d records requested at once from a host tier of %d slots", n, t->core.capacity());
@@ -69,64 +111,60 @@ int tier_fetch(moe_host_tier *t, const int64_t *recs, int n, const char **ptrs) 
         ptrs[i] = t->pool + (size_t)slot[i] * t->record_bytes;
     }
     // the reads of this batch, spread over the I/O threads
+    int64_t rr[MOE_MAX_K];
+    char *dst[MOE_MAX_K];
     int todo[MOE_MAX_K], nt = 0;
     for (int i = 0; i < n; i++)
-        if (need[i]) todo[nt++] = i;
-    if (!nt) return MOE_OK;
-    const auto t0 = std::chrono::steady_clock::now();
-    bool ok[MOE_MAX_K];
-    int err[MOE_MAX_K];
-    const int nthr = std::min(nt, t->io_threads);
-    auto worker = [&](int w) {
-        for (int q = w; q < nt; q += nthr) {
-            const int i = todo[q];
-            errno = 0;
-            ok[q] = read_record(t->fd, t->bounce[w], t->record_bytes, recs[i]);
-            err[q] = ok[q] ? 0 : (errno ? errno : EIO);
-            if (ok[q]) memcpy((char *)ptrs[i], t->bounce[w], t->record_bytes);
+        if (need[i]) {
+            todo[nt] = i;
+            rr[nt] = recs[i];
+            dst[nt++] = (char *)ptrs[i];
         }
-    };
-    if (nthr <= 1) {
-        worker(0);
-    } else {
-        std::thread th[MOE_MAX_K];
-        int started = 0;
-        try {
-            for (int w = 1; w < nthr; w++, started++) th[w] = std::thread(worker, w);
-        } catch (...) {
-        }
-        worker(0);
-        for (int w = 1; w <= started; w++) th[w].join();
-        for (int w = started + 1; w < nthr; w++) worker(w);   // threads that could not start
-    }
-    t->read_ns += (int64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0)
-                      .count();
-    for (int q = 0; q < nt; q++) {
-        if (!ok[q]) {
-            t->core.drop_slot(slot[todo[q]]);
-            return fail(MOE_E_HIP, "read of record %lld failed: %s", (long long)recs[todo[q]], strerror(err[q]));
-        }
-        t->reads++;
-        t->read_bytes += (int64_t)t->record_bytes;
-    }
-    return MOE_OK;
+    int bad = -1;
+    const int rc = read_parallel(t, rr, dst, nt, &bad);
+    if (rc) t->core.drop_slot(slot[todo[bad]]);
+    return rc;
 }
 
 int tier_copied(moe_host_tier *t, const char *src, hipStream_t copy_stream) {
-    const int32_t s = (int32_t)((src - t->pool) / (ptrdiff_t)t->record_bytes);
-    hipError_t e = hipEventRecord(t->copied[s], copy_stream);
-    if (e != hipSuccess) return hip_fail(e, "record a host slot's copy");
-    t->pending[s] = 1;
+    return tier_page_copied(t, (int32_t)((src - t->pool) / (ptrdiff_t)t->record_bytes), copy_stream);
+}
+
+int tier_page_copied(moe_host_tier *t, int32_t page, hipStream_t copy_stream) {
+    hipError_t e = hipEventRecord(t->copied[page], copy_stream);
+    if (e != hipSuccess) return hip_fail(e, "record a host page's copy");
+    t->pending[page] = 1;
     return MOE_OK;
+}
+
+int tier_take_page(moe_host_tier *t, bool cpu_write, hipStream_t copy_stream, int32_t *page) {
+    if (t->free_pages.empty()) return fail(MOE_E_STATE, "exclusive host tier: no free page");
+    const int32_t p = t->free_pages.back();
+    if (t->pending[p]) {
+        hipError_t e = hipEventQuery(t->copied[p]);
+        if (e == hipErrorNotReady)
+            e = cpu_write ? hipEventSynchronize(t->copied[p]) : hipStreamWaitEvent(copy_stream, t->copied[p], 0);
+        if (e != hipSuccess) return hip_fail(e, "wait for a host page's last copy");
+        if (cpu_write) t->pending[p] = 0;
+    }
+    t->free_pages.pop_back();
+    *page = p;
+    return MOE_OK;
+}
+
+int tier_read_pages(moe_host_tier *t, const int64_t *recs, const int32_t *pages, int n) {
+    char *dst[MOE_MAX_K];
+    for (int q = 0; q < n; q++) dst[q] = tier_page(t, pages[q]);
+    int bad = -1;
+    return read_parallel(t, recs, dst, n, &bad);
 }
 }  // namespace moe
 
 using namespace moe;
 
-extern "C" {
-
-int moe_host_tier_create(const char *path, uint64_t record_bytes, int64_t n_records, int32_t slots,
-                         void *pinned_pool, int32_t io_threads, moe_host_tier **out) {
+namespace {
+int create_tier(const char *path, uint64_t record_bytes, int64_t n_records, int32_t slots, void *pinned_pool,
+                int32_t io_threads, bool exclusive, moe_host_tier **out) {
     if (!out) return fail(MOE_E_INVAL, "out is NULL");
     *out = nullptr;
     if (!path || !pinned_pool) return fail(MOE_E_INVAL, "path and pinned_pool must be non-NULL");
@@ -135,6 +173,8 @@ int moe_host_tier_create(const char *path, uint64_t record_bytes, int64_t n_reco
     if ((uintptr_t)pinned_pool % 4096) return fail(MOE_E_INVAL, "pinned_pool must be 4096-byte aligned");
     if (n_records < 1 || n_records > (int64_t)kNoKey) return fail(MOE_E_INVAL, "n_records=%lld", (long long)n_records);
     if (slots < 1) return fail(MOE_E_INVAL, "slots=%d < 1", slots);
+    if (exclusive && slots <= MOE_MAX_K)
+        return fail(MOE_E_INVAL, "an exclusive host tier needs more than %d slots (got %d)", MOE_MAX_K, slots);
     if (io_threads < 1 || io_threads > MOE_MAX_K) return fail(MOE_E_INVAL, "io_threads must be in 1..%d", MOE_MAX_K);
     const int fd = open(path, O_RDONLY | O_DIRECT);
     if (fd < 0) return fail(MOE_E_INVAL, "open(%s, O_DIRECT): %s", path, strerror(errno));
@@ -144,7 +184,7 @@ int moe_host_tier_create(const char *path, uint64_t record_bytes, int64_t n_reco
         return fail(MOE_E_INVAL, "%s holds fewer than %lld records of %llu bytes", path, (long long)n_records,
                     (unsigned long long)record_bytes);
     }
-    moe_host_tier *t = new (std::nothrow) moe_host_tier(slots);
+    moe_host_tier *t = new (std::nothrow) moe_host_tier(exclusive ? slots - MOE_MAX_K : slots);
     if (!t) {
         close(fd);
         return fail(MOE_E_NOMEM, "host allocation failed");
@@ -154,6 +194,11 @@ int moe_host_tier_create(const char *path, uint64_t record_bytes, int64_t n_reco
     t->n_records = n_records;
     t->pool = (char *)pinned_pool;
     t->io_threads = io_threads;
+    t->exclusive = exclusive;
+    t->page_of.resize(t->core.capacity());
+    for (int i = 0; i < t->core.capacity(); i++) t->page_of[i] = exclusive ? -1 : i;
+    if (exclusive)
+        for (int p = slots - 1; p >= 0; p--) t->free_pages.push_back(p);   // lowest page taken first
     t->copied.assign(slots, nullptr);
     t->pending.assign(slots, 0);
     t->bounce.assign(io_threads, nullptr);
@@ -166,11 +211,31 @@ int moe_host_tier_create(const char *path, uint64_t record_bytes, int64_t n_reco
     }
     hipError_t e = hipSuccess;
     for (int s = 0; e == hipSuccess && s < slots; s++) e = hipEventCreateWithFlags(&t->copied[s], hipEventDisableTiming);
+    if (e == hipSuccess && exclusive) e = hipStreamCreateWithFlags(&t->down, hipStreamNonBlocking);
     if (e != hipSuccess) {
         moe_host_tier_destroy(t);
         return hip_fail(e, "hipEventCreate");
     }
     *out = t;
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_host_tier_create(const char *path, uint64_t record_bytes, int64_t n_records, int32_t slots,
+                         void *pinned_pool, int32_t io_threads, moe_host_tier **out) {
+    return create_tier(path, record_bytes, n_records, slots, pinned_pool, io_threads, false, out);
+}
+
+int moe_host_tier_create_exclusive(const char *path, uint64_t record_bytes, int64_t n_records, int32_t slots,
+                                   void *pinned_pool, int32_t io_threads, moe_host_tier **out) {
+    return create_tier(path, record_bytes, n_records, slots, pinned_pool, io_threads, true, out);
+}
+
+int moe_host_tier_demotions(moe_host_tier *t, int64_t *demotions) {
+    if (!t || !demotions) return fail(MOE_E_INVAL, "host tier and demotions must be non-NULL");
+    *demotions = t->demotions;
     return MOE_OK;
 }
 
@@ -182,6 +247,7 @@ void moe_host_tier_destroy(moe_host_tier *t) {
         (void)hipEventDestroy(t->copied[s]);
     }
     for (char *b : t->bounce) free(b);
+    if (t->down) (void)hipStreamDestroy(t->down);
     if (t->fd >= 0) close(t->fd);
     delete t;
 }

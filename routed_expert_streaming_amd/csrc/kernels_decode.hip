@@ -1839,7 +1839,6 @@ hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
     int &G = Gdev[dev];
     bool &lds_at_zero = lds_zero_dev[dev];
     if (G == 0) {
-        hipFuncAttributes fa;
         const void *fns[2] = {(const void *)k_decode_persistent<8>, (const void *)k_decode_persistent<16>};
         int cus = 0, per_min = 1 << 30;
         hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

@@ -615,16 +615,45 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     std::sort(order, order + k, [&](int a, int b) { return c->h_idx[a] < c->h_idx[b]; });
     int32_t slot_of[MOE_MAX_K];
     bool hit[MOE_MAX_K];
+    // exclusive host tier: per miss, the page its record comes from (-1: the
+    // file) and the page the HBM cache's evicted key moves to (-1: none)
+    moe_host_tier *X = tier.t && tier.t->exclusive ? tier.t : nullptr;
+    int32_t spage[MOE_MAX_K], vpage[MOE_MAX_K];
+    int32_t transit[MOE_MAX_K];
+    int ntransit = 0;
     for (int n = 0; n < k; n++) {
         const int j = order[n];
         const uint32_t key = layer_id * (uint32_t)E + (uint32_t)c->h_idx[j];
         int32_t s = c->core.lookup(key);
         hit[j] = s >= 0;
+        spage[j] = vpage[j] = -1;
         if (s < 0) {
+            if (X) {
+                // the lower tier: a key found there leaves it (its page is in
+                // transit until this call's copies are enqueued)
+                const int32_t h = X->core.probe(key);
+                if (h >= 0) {
+                    spage[j] = transit[ntransit++] = X->page_of[h];
+                    X->page_of[h] = -1;
+                    X->core.drop_slot(h);
+                }
+            }
             uint32_t victim = kNoKey;
             s = c->core.plan_insert(key, &victim);
+            const bool demote = X && victim != kNoKey && c->filled[s];
             c->core.commit_insert(key, s, victim);
             c->filled[s] = 0;                 // until its copy is enqueued below
+            if (demote) {
+                // the evicted key moves down, at the lower tier's most recent end
+                uint32_t gone = kNoKey;
+                const int32_t hv = X->core.insert_kind(victim, kTraceDemote, &gone);
+                if (gone == kNoKey) {
+                    rc = tier_take_page(X, false, X->down, &X->page_of[hv]);
+                    if (rc) return rc;
+                }
+                vpage[j] = X->page_of[hv];     // a key that left the tier leaves its page to this one
+                X->demotions++;
+            }
         }
         slot_of[j] = s;
     }
@@ -644,17 +673,42 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
             if (locked && pass == 0) nlocked++;
         }
     const char *src_of[MOE_MAX_K] = {};
-    // a miss's copy into its slot, after the slot's previous readers
+    // a miss's copy into its slot, after the slot's previous readers (and,
+    // with an exclusive host tier, after the slot's old record has been
+    // copied down to its page)
     auto copy_miss = [&](int j) -> int {
         const int32_t s = slot_of[j];
         HIPCHK(cache_wait_readers(c, s, ps), "copy waits for slot readers");
+        // an event not yet complete: stream st waits for it
+        auto after = [&](hipStream_t st, hipEvent_t ev) {
+            hipError_t q = hipEventQuery(ev);
+            return q == hipErrorNotReady ? hipStreamWaitEvent(st, ev, 0) : q;
+        };
+        if (vpage[j] >= 0) {
+            // the evicted record goes down on the tier's own stream (the link
+            // carries it while the copy stream moves records up), after the
+            // slot's record landed and the page's last copy; the copy up into
+            // the slot waits for it
+            const int32_t vp = vpage[j];
+            HIPCHK(after(X->down, c->ready[s]), "demotion waits for the slot's record");
+            if (X->pending[vp]) HIPCHK(after(X->down, X->copied[vp]), "demotion waits for the page");
+            HIPCHK(hipMemcpyAsync(tier_page(X, vp), c->pool + (size_t)s * c->slot_bytes, c->slot_bytes,
+                                  hipMemcpyDeviceToHost, X->down), "demotion copy");
+            int r = tier_page_copied(X, vp, X->down);
+            if (r) return r;
+            HIPCHK(hipStreamWaitEvent(ps, X->copied[vp], 0), "copy up waits for the copy down");
+        }
+        if (X && X->pending[(int32_t)((src_of[j] - X->pool) / (ptrdiff_t)X->record_bytes)])
+            HIPCHK(after(ps, X->copied[(int32_t)((src_of[j] - X->pool) / (ptrdiff_t)X->record_bytes)]),
+                   "copy up waits for its page");
         const void *src = tier.t ? (const void *)src_of[j] : experts_host[c->h_idx[j]];
         bool enqueued = false;   // the key is committed either way: a failed copy drops its slot
         hipError_t e = tier.t ? hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, src, c->slot_bytes,
                                                hipMemcpyHostToDevice, ps)
                               : cache_copy_in(c, s, src, ps, &enqueued);
         if (e == hipSuccess && tier.t) {
-            const int trc = tier_copied(tier.t, src_of[j], ps);
+            const int trc = X ? tier_page_copied(X, (int32_t)((src_of[j] - X->pool) / (ptrdiff_t)X->record_bytes), ps)
+                              : tier_copied(tier.t, src_of[j], ps);
             if (trc) {
                 c->core.drop_slot(s);
                 return trc;
@@ -713,6 +767,36 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
             if ((rc = copy_miss(morder[n]))) return rc;
             if ((rc = run_miss(morder[n]))) return rc;
         }
+    } else if (X) {
+        // exclusive host tier: the hit experts run while the records found in
+        // neither tier are read from the file into transit pages; then the
+        // misses' copies (down, then up) in ascending id
+        if ((rc = run_hits())) return rc;
+        int64_t recs[MOE_MAX_K];
+        int32_t pages[MOE_MAX_K];
+        int nr = 0;
+        for (int n = 0; n < nmiss; n++) {
+            const int j = morder[n];
+            if (spage[j] >= 0) continue;
+            rc = tier_take_page(X, true, ps, &spage[j]);
+            if (rc) return rc;
+            transit[ntransit++] = spage[j];
+            recs[nr] = tier.record0 + c->h_idx[j];
+            pages[nr++] = spage[j];
+        }
+        rc = tier_read_pages(X, recs, pages, nr);
+        if (rc) {
+            for (int n = 0; n < nmiss; n++) c->core.drop_slot(slot_of[morder[n]]);   // never filled
+            return rc;
+        }
+        for (int n = 0; n < nmiss; n++) src_of[morder[n]] = tier_page(X, spage[morder[n]]);
+        for (int n = 0; n < nmiss; n++) {
+            if ((rc = copy_miss(morder[n]))) return rc;
+            if ((rc = run_miss(morder[n]))) return rc;
+        }
+        // the transit pages are free again once their copies are done (each
+        // page's event says when)
+        for (int q = 0; q < ntransit; q++) X->free_pages.push_back(transit[q]);
     } else {
         // file tier: the hit experts run while the misses' records are read
         // into host slots
@@ -788,6 +872,10 @@ int moe_layer_forward_streamed_tiered(const moe_layer *L, moe_cache *c, uint32_t
     if (L && tier->core.capacity() < L->router.k)
         return fail(MOE_E_INVAL, "host tier has %d slots, below k = %d", tier->core.capacity(), L->router.k);
     if (record0 < 0) return fail(MOE_E_INVAL, "record0=%lld < 0", (long long)record0);
+    if (tier->exclusive && L && (int64_t)layer_id * L->router.E != record0)
+        return fail(MOE_E_INVAL, "an exclusive host tier keys records like the HBM cache: record0 must be "
+                                 "layer_id * E = %lld (got %lld)", (long long)layer_id * L->router.E,
+                    (long long)record0);
     Tier tr;
     tr.t = tier;
     tr.record0 = record0;

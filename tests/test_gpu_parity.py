@@ -482,6 +482,69 @@ def test_streamed_file_tier(moe, tmp_path):
     cache.close()
 
 
+def test_streamed_file_tier_exclusive(moe, tmp_path):
+    # The file tier as the HBM cache's exclusive lower tier: an HBM miss is
+    # looked up in host memory (a key found there leaves it), else read from
+    # the file; the key the HBM cache evicts moves down, copied device to
+    # host from its slot.  Outputs equal the resident path's bit for bit (a
+    # record that went down and came back up carries the right bytes); the
+    # HBM trace and the host tier's operation string equal the oracle's
+    # two-tier model over the lookups in order; together the tiers hit
+    # exactly where one LRU of their combined size hits.
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload, write_record_file
+    cfg = synth.get_config("tiny", tokens=8, layers=3, E=16)
+    path = str(tmp_path / "records.bin")
+    stride = write_record_file(cfg, path, list(range(cfg.layers)))
+    dw = DeviceWorkload(cfg)
+    x = dw.inputs()
+    hbm_slots, lower = 4, 6
+    pool = torch.empty(hbm_slots * stride, dtype=torch.uint8, device="cuda")
+    cache = moe.ExpertCache(hbm_slots, stride, pool)
+    tier = moe.HostTier(path, stride, cfg.layers * cfg.E, lower + moe.MOE_MAX_K, io_threads=3, exclusive=True)
+    copy_stream = torch.cuda.Stream()
+    ws = torch.empty(moe.streamed_workspace_bytes(dw.layers[0]), dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoeError):   # keys shared with the HBM cache: record0 = layer * E
+        moe.layer_forward_streamed(dw.layers[1], cache, 1, None, x[0, 1][None].contiguous(), copy_stream, ws=ws,
+                                   tier=(tier, 0))
+    outs = []
+    for t in range(cfg.tokens):
+        for L in range(cfg.layers):
+            o = moe.layer_forward_streamed(dw.layers[L], cache, L, None, x[t, L][None].contiguous(), copy_stream,
+                                           ws=ws, tier=(tier, L * cfg.E))
+            outs.append(o.clone())
+    torch.cuda.synchronize()
+    for n, o in enumerate(outs):
+        t, L = divmod(n, cfg.layers)
+        ro, _, _ = moe.layer_forward(dw.layers[L], x[t, L][None].contiguous())
+        assert torch.equal(o[0], ro[0]), f"exclusive file tier != resident at token {t} layer {L}"
+    ctr = cache.trace()
+    keys = np.array([r[0] for r in ctr], np.int64)
+    m = oracle.two_tier(keys, hbm_slots, lower)
+    assert [r[1] for r in ctr] == m["hit1"].tolist()
+    assert [r[2] for r in ctr] == m["slot1"].tolist()
+    assert [(-1 if r[3] is None else r[3]) for r in ctr] == m["ev1"].tolist()
+    want = []
+    for i in range(len(keys)):
+        if m["hit1"][i]:
+            continue
+        want.append((int(keys[i]), 1 if m["hit2"][i] else 4, int(m["slot2"][i]), -1))
+        if m["ev1"][i] != -1:
+            want.append((int(m["ev1"][i]), 5, int(m["dslot"][i]), int(m["dev"][i])))
+    got = [(r[0], r[1], r[2], -1 if r[3] is None else r[3]) for r in tier.trace()]
+    assert got == want
+    both, _, _ = oracle.lru(keys, hbm_slots + lower)
+    assert (((m["hit1"] == 1) | (m["hit2"] == 1)).astype(np.int32)).tolist() == both.tolist()
+    st = tier.stats()
+    n_miss = int((m["hit1"] == 0).sum())
+    n_low = int((m["hit2"] == 1).sum())
+    assert n_low > 0, "the run should find evicted records in host memory"
+    assert st["lookups"] == n_miss and st["hits"] == n_low and st["reads"] == n_miss - n_low
+    assert st["demotions"] == int((m["ev1"] != -1).sum())
+    log(f"exclusive file tier: {st}, HBM misses {n_miss} of {len(keys)}, found below {n_low}")
+    tier.close()
+    cache.close()
+
+
 # ---------------------------------------------------------------- routing edges
 @pytest.mark.parametrize("k,score", [(1, "softmax"), (1, "sigmoid"), (8, "softmax"), (8, "sigmoid")])
 def test_routing_edge_k(moe, k, score):
