@@ -574,8 +574,10 @@ def bench_sweep_ahead(args, cfg) -> int:
     """Look-ahead reads (WARP's pre-read router) on the chained K3 slice: each
     layer reads the rescaled residual stream of the previous layers' outputs,
     so the next layer's router applied to this layer's input is a prediction.
-    Cold 25% cache; runs without look-ahead and with k_ahead = k and k/2;
-    outputs must be identical bit for bit."""
+    Cold 25% cache; runs without look-ahead, with k_ahead = k and k/2, and
+    with k_ahead = k and a confidence threshold (only predictions whose
+    renormalised weight is at least 1/k, or 1.5/k, are read ahead); outputs
+    must be identical bit for bit."""
     import numpy as np
     import torch
 
@@ -588,7 +590,7 @@ def bench_sweep_ahead(args, cfg) -> int:
     ws = torch.empty(moe.streamed_workspace_bytes(dw.layers[0]), dtype=torch.uint8, device="cuda")
     copy_stream = torch.cuda.Stream()
     runs, ref_out = [], None
-    for k_ahead in (0, cfg.k, cfg.k // 2):
+    for k_ahead, min_w in ((0, 0.0), (cfg.k, 0.0), (cfg.k // 2, 0.0), (cfg.k, 1.0 / cfg.k), (cfg.k, 1.5 / cfg.k)):
         pool = torch.empty(cap * hp.stride, dtype=torch.uint8, device="cuda")
         cache = moe.ExpertCache(cap, hp.stride, pool)
         out = torch.empty((n_tok, cfg.layers, cfg.H), dtype=torch.float32, device="cuda")
@@ -600,7 +602,7 @@ def bench_sweep_ahead(args, cfg) -> int:
             for L in range(cfg.layers):
                 ahead = None
                 if k_ahead and L + 1 < cfg.layers:
-                    ahead = (dw.layers[L + 1], L + 1, tables[L + 1], k_ahead)
+                    ahead = (dw.layers[L + 1], L + 1, tables[L + 1], k_ahead, min_w)
                 moe.layer_forward_streamed(dw.layers[L], cache, L, None, xin, copy_stream, ws=ws,
                                            out=out[t, L][None], host_table=tables[L], ahead=ahead)
                 xin = chain_next_input(h, out[t, L], scale)
@@ -619,7 +621,7 @@ def bench_sweep_ahead(args, cfg) -> int:
         cache.close()
         del pool
         # prediction quality from the operation string: per (t, L) k lookups,
-        # then k_ahead touches of layer L + 1 (not after the last layer)
+        # then up to k_ahead touches of layer L + 1 (not after the last layer)
         pos, inter, npred = 0, 0, 0
         pending = None
         for t in range(n_tok):
@@ -631,12 +633,15 @@ def bench_sweep_ahead(args, cfg) -> int:
                     npred += len(pending)
                     pending = None
                 if k_ahead and L + 1 < cfg.layers:
-                    pending = set(r[0] for r in tr[pos:pos + k_ahead])
-                    pos += k_ahead
+                    n_pred = 0
+                    while pos + n_pred < len(tr) and tr[pos + n_pred][1] in (2, 3):
+                        n_pred += 1
+                    pending = set(r[0] for r in tr[pos:pos + n_pred])
+                    pos += n_pred
         if ref_out is None:
             ref_out = out
         d = {k2: st[k2] - st0[k2] for k2 in st}
-        runs.append({"k_ahead": k_ahead, "tok_s": round(args.steps / elapsed, 3),
+        runs.append({"k_ahead": k_ahead, "min_weight": round(min_w, 4), "tok_s": round(args.steps / elapsed, 3),
                      "hit_rate_timed": round(d["hits"] / max(1, d["lookups"]), 4),
                      "demand_misses_per_token": round((d["lookups"] - d["hits"]) / args.steps, 2),
                      "ahead_copies_per_token": round(d["ahead_inserted"] / args.steps, 2),
@@ -645,7 +650,7 @@ def bench_sweep_ahead(args, cfg) -> int:
                      "h2d_gb_per_token": round((d["inserts"]) * hp.stride / args.steps / 1e9, 3),
                      "prediction_precision": round(inter / npred, 4) if npred else None,
                      "outputs_identical": bool(torch.equal(out, ref_out))})
-        log(f"k_ahead={k_ahead}: {runs[-1]}")
+        log(f"k_ahead={k_ahead} min_weight={min_w:.4f}: {runs[-1]}")
     ok = all(u["outputs_identical"] for u in runs)
     rec = {"metric": "chained streamed decode tok/s with and without look-ahead reads (one MI355X)",
            "value": runs[1]["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -390,10 +390,14 @@ int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_
  * LRU key if full) and copied from next_experts_host[e] on copy_stream behind
  * this layer's miss copies; its copy waits for the victim slot's last
  * readers.  Outputs are those of moe_layer_forward_streamed bit for bit: the
- * prediction changes only which copies happen and when.
+ * prediction changes only which copies happen and when.  Only predictions
+ * whose weight, the next router's score renormalised over its k_ahead
+ * choices as the gate weights are, is at least min_weight are touched (a
+ * confidence threshold: 0 touches all k_ahead; 1/k_ahead keeps those above
+ * the mean).
  *   next [host] the next layer (its records are not read; H must match)
  *   next_experts_host [host] array of E_next [pinned] record pointers
- *   k_ahead in 1..min(E_next, MOE_MAX_K, capacity)
+ *   k_ahead in 1..min(E_next, MOE_MAX_K, capacity); min_weight in [0, 1]
  * MOE_E_INVAL on a NULL next or bad arguments, as well as the conditions of
  * moe_layer_forward_streamed.  ws: moe_streamed_workspace_bytes(L, T). */
 int moe_layer_forward_streamed_ahead(const moe_layer *L, moe_cache *c, uint32_t layer_id,
@@ -401,7 +405,7 @@ int moe_layer_forward_streamed_ahead(const moe_layer *L, moe_cache *c, uint32_t 
                                      float *out, int32_t *idx_out, void *ws, size_t ws_bytes,
                                      void *compute_stream, void *copy_stream, const moe_layer *next,
                                      uint32_t next_layer_id, const void *const *next_experts_host,
-                                     int32_t k_ahead);
+                                     int32_t k_ahead, float min_weight);
 
 /* ---- third tier: expert records in a file ------------------------------- */
 typedef struct moe_host_tier moe_host_tier;

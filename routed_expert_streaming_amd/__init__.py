@@ -424,8 +424,9 @@ def layer_forward_streamed(layer: Layer, cache: ExpertCache, layer_id: int, expe
                            idx: Optional[torch.Tensor] = None, host_table=None, ahead=None, tier=None):
     """One decode step of one layer fed from the slot cache.  experts_host:
     E pinned host addresses of the layer's records (or a prebuilt ctypes
-    array).  ahead = (next_layer, next_layer_id, next_host_table, k_ahead)
-    adds the look-ahead read of moe_layer_forward_streamed_ahead; tier =
+    array).  ahead = (next_layer, next_layer_id, next_host_table, k_ahead[,
+    min_weight]) adds the look-ahead read of moe_layer_forward_streamed_ahead
+    (predictions with a smaller weight are not read ahead); tier =
     (HostTier, record0) takes the misses from the file tier instead
     (moe_layer_forward_streamed_tiered)."""
     _need(x.dim() == 2 and x.shape[0] == 1 and x.dtype == torch.float32, "x must be fp32 [1, H]")
@@ -448,11 +449,13 @@ def layer_forward_streamed(layer: Layer, cache: ExpertCache, layer_id: int, expe
                                                _ptr(idx), _ptr(ws), ws.numel(), _stream(stream),
                                                _stream(copy_stream)), "moe_layer_forward_streamed")
         return out
-    nxt, nxt_id, nxt_host, k_ahead = ahead
+    nxt, nxt_id, nxt_host, k_ahead = ahead[:4]
+    min_weight = float(ahead[4]) if len(ahead) > 4 else 0.0
     ns = nxt.struct()
     ntable = nxt_host if not isinstance(nxt_host, (list, tuple)) else (ctypes.c_void_p * len(nxt_host))(*nxt_host)
     check(lib().moe_layer_forward_streamed_ahead(ctypes.byref(s), cache.handle, layer_id, table, _ptr(x), 1,
                                                  _ptr(out), _ptr(idx), _ptr(ws), ws.numel(), _stream(stream),
-                                                 _stream(copy_stream), ctypes.byref(ns), nxt_id, ntable, k_ahead),
+                                                 _stream(copy_stream), ctypes.byref(ns), nxt_id, ntable, k_ahead,
+                                                 min_weight),
           "moe_layer_forward_streamed_ahead")
     return out

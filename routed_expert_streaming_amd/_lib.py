@@ -84,7 +84,8 @@ SIGNATURES = {
     "moe_layer_forward_streamed_tiered": (ctypes.c_int, [ctypes.POINTER(MoeLayer), P, U32, P, I64, P, I32, P, P, P,
                                                          SZ, P, P]),
     "moe_layer_forward_streamed_ahead": (ctypes.c_int, [ctypes.POINTER(MoeLayer), P, U32, P, P, I32, P, P,
-                                                        P, SZ, P, P, ctypes.POINTER(MoeLayer), U32, P, I32]),
+                                                        P, SZ, P, P, ctypes.POINTER(MoeLayer), U32, P, I32,
+                                                        ctypes.c_float]),
     "moe_streamed_workspace_bytes": (SZ, [ctypes.POINTER(MoeLayer), I32]),
     "moe_layer_forward_streamed": (ctypes.c_int, [ctypes.POINTER(MoeLayer), P, U32, P, P, I32, P, P,
                                                   P, SZ, P, P]),

@@ -51,7 +51,8 @@ struct moe_cache {
     std::vector<int32_t> use_refs;        // slots referring to each event
     std::vector<int32_t> use_free;        // events with no referring slot
     std::vector<int32_t> slot_use;        // per slot: its readers' event, or -1
-    int32_t *h_idx = nullptr;             // pinned staging for the router's expert ids
+    int32_t *h_idx = nullptr;             // pinned staging: the router's expert ids, the look-ahead ids and
+                                          // (bits of) the look-ahead weights, MOE_MAX_K each
     hipEvent_t idx_ev = nullptr;          // recorded after the ids' copy to h_idx
     hipEvent_t ahead_ev = nullptr;        // recorded after the look-ahead ids' copy
     int device = 0;

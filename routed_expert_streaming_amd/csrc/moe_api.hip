@@ -523,6 +523,7 @@ struct Ahead {
     uint32_t layer_id = 0;
     const void *const *host = nullptr;
     int k = 0;
+    float min_weight = 0.f;                // predictions with a smaller weight are not read ahead
 };
 struct Tier {
     moe_host_tier *t = nullptr;            // file tier, or null: records from experts_host
@@ -577,6 +578,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         wa = ca.take<float>(MOE_MAX_K);
     }
     int32_t *h_ahead = c->h_idx + MOE_MAX_K;
+    float *h_ahead_w = (float *)(c->h_idx + 2 * MOE_MAX_K);
     int32_t *idx = idx_out ? idx_out : W.idx;
     const RecOffsets off = offsets_of(H, I);
     const int KS = down_splits(H, I, k);
@@ -593,6 +595,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
                                    cs), "look-ahead logits");
         HIPCHK(launch_topk(za, ah.L->router.E, ah.k, ah.L->router.score_fn, 1, ia, wa, cs), "look-ahead top-k");
         HIPCHK(hipMemcpyAsync(h_ahead, ia, ah.k * sizeof(int32_t), hipMemcpyDeviceToHost, cs), "look-ahead ids");
+        HIPCHK(hipMemcpyAsync(h_ahead_w, wa, ah.k * sizeof(float), hipMemcpyDeviceToHost, cs), "look-ahead weights");
         HIPCHK(hipEventRecord(c->ahead_ev, cs), "look-ahead ids copied");
     }
     HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, 1, H, H, W.xh, W.xexp, cs), "pack_x");
@@ -824,15 +827,19 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     // misses on the copy stream, so they land while this layer computes.  A
     // victim slot's copy still waits for that slot's last readers.
     HIPCHK(hipEventSynchronize(c->ahead_ev), "wait for the look-ahead ids");
-    int pred[MOE_MAX_K];
+    // the predictions whose weight (renormalised over the k_ahead predicted)
+    // is at least min_weight, in ascending id
+    int pred[MOE_MAX_K], np = 0;
     const int En = ah.L->router.E;
     for (int j = 0; j < ah.k; j++) {
-        pred[j] = h_ahead[j];
-        if (pred[j] < 0 || pred[j] >= En) return fail(MOE_E_HIP, "look-ahead router produced expert id %d", pred[j]);
-        if (!ah.host[pred[j]]) return fail(MOE_E_INVAL, "next layer's experts_host[%d] is NULL", pred[j]);
+        const int e = h_ahead[j];
+        if (e < 0 || e >= En) return fail(MOE_E_HIP, "look-ahead router produced expert id %d", e);
+        if (!(h_ahead_w[j] >= ah.min_weight)) continue;
+        if (!ah.host[e]) return fail(MOE_E_INVAL, "next layer's experts_host[%d] is NULL", e);
+        pred[np++] = e;
     }
-    std::sort(pred, pred + ah.k);
-    for (int j = 0; j < ah.k; j++) {
+    std::sort(pred, pred + np);
+    for (int j = 0; j < np; j++) {
         const uint32_t key = ah.layer_id * (uint32_t)En + (uint32_t)pred[j];
         uint32_t victim = kNoKey;
         bool inserted = false;
@@ -887,13 +894,15 @@ int moe_layer_forward_streamed_ahead(const moe_layer *L, moe_cache *c, uint32_t 
                                      const void *const *experts_host, const float *x, int32_t T, float *out,
                                      int32_t *idx_out, void *ws, size_t ws_bytes, void *compute_stream,
                                      void *copy_stream, const moe_layer *next, uint32_t next_layer_id,
-                                     const void *const *next_experts_host, int32_t k_ahead) {
+                                     const void *const *next_experts_host, int32_t k_ahead, float min_weight) {
     if (!next) return fail(MOE_E_INVAL, "next layer is NULL (use moe_layer_forward_streamed)");
+    if (!(min_weight >= 0.f && min_weight <= 1.f)) return fail(MOE_E_INVAL, "min_weight must be in [0, 1]");
     Ahead ah;
     ah.L = next;
     ah.layer_id = next_layer_id;
     ah.host = next_experts_host;
     ah.k = k_ahead;
+    ah.min_weight = min_weight;
     return streamed_impl(L, c, layer_id, experts_host, x, T, out, idx_out, ws, ws_bytes, compute_stream, copy_stream,
                          ah);
 }

@@ -352,16 +352,20 @@ def test_streamed_rejects_capacity_below_k(moe):
     cache.close()
 
 
-def test_streamed_lookahead_chained(moe):
+@pytest.mark.parametrize("threshold", [False, True])
+def test_streamed_lookahead_chained(moe, threshold):
     # Chained decode (each layer reads the rescaled residual stream, so the
     # next layer's router applied to this layer's input predicts something):
     # the look-ahead changes which copies happen and when, never the outputs;
     # the cache trace (lookups and look-ahead touches) replays exactly through
     # the oracle's LRU; actual and predicted expert sets match the oracle's
-    # routers wherever the top-k boundary is not a near-tie.
+    # routers wherever the top-k boundary is not a near-tie.  With a
+    # confidence threshold (min_weight = 1 / k_ahead) only the predictions of
+    # at least that renormalised weight are touched.
     from routed_expert_streaming_amd.device_workload import chain_next_input
     cfg = synth.get_config("k3_slice", tokens=4, layers=3, E=48)
     capacity, k_ahead = 40, cfg.k
+    min_w = 1.0 / k_ahead if threshold else 0.0
     dw, hp, cache = _streamed_setup(moe, cfg, capacity)
     pool2 = torch.empty(capacity * hp.stride, dtype=torch.uint8, device="cuda")
     cache_plain = moe.ExpertCache(capacity, hp.stride, pool2)
@@ -383,7 +387,7 @@ def test_streamed_lookahead_chained(moe):
                 else:
                     ahead = None
                     if mode == "ahead" and L + 1 < cfg.layers:
-                        ahead = (dw.layers[L + 1], L + 1, tables[L + 1], k_ahead)
+                        ahead = (dw.layers[L + 1], L + 1, tables[L + 1], k_ahead, min_w)
                     c = cache if mode == "ahead" else cache_plain
                     o = moe.layer_forward_streamed(dw.layers[L], c, L, None, xin, copy_stream, ws=ws,
                                                    host_table=tables[L], ahead=ahead)
@@ -420,13 +424,17 @@ def test_streamed_lookahead_chained(moe):
                 assert sorted(r[0] - L * cfg.E for r in look) == sorted(ridx[0].tolist())
                 checked += 1
             if L + 1 < cfg.layers:
-                pred = tr[pos:pos + k_ahead]
-                pos += k_ahead
-                assert all(r[1] in (2, 3) for r in pred)
-                pidx, _, zp = oracle.route(dw.wl.router(L + 1), dw.wl.bias(L + 1), x64, k_ahead, cfg.score)
+                n_pred = 0
+                while pos + n_pred < len(tr) and tr[pos + n_pred][1] in (2, 3):
+                    n_pred += 1
+                pred = tr[pos:pos + n_pred]
+                pos += n_pred
+                pidx, pw, zp = oracle.route(dw.wl.router(L + 1), dw.wl.bias(L + 1), x64, k_ahead, cfg.score)
                 zs = np.sort(zp[0])[::-1]
-                if zs[k_ahead - 1] - zs[k_ahead] > 1e-4:
-                    assert sorted(r[0] - (L + 1) * cfg.E for r in pred) == sorted(pidx[0].tolist())
+                margin_ok = zs[k_ahead - 1] - zs[k_ahead] > 1e-4 and np.all(np.abs(pw[0] - min_w) > 1e-5)
+                if margin_ok:
+                    want = sorted(int(e) for e, w in zip(pidx[0], pw[0]) if w >= min_w)
+                    assert sorted(r[0] - (L + 1) * cfg.E for r in pred) == want
                     checked += 1
     assert pos == len(tr) and checked >= len(out_a)
     st = cache.stats()
