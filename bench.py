@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0
 # valid for the kernel source they were taken on: reported as null once that
 # source has changed.
 DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
-                  "sha256_prefix": "dacfb8a96550b634",
-                  "bytes_per_launch": {"mixtral": 5057005375, "kimi_linear": 1240357724}}
+                  "sha256_prefix": "fab0db0257a2ef41",
+                  "bytes_per_launch": {"mixtral": 5057644555, "kimi_linear": 1235807045}}
 
 
 def measured_traffic(workload: str):
