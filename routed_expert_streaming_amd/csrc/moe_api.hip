@@ -624,6 +624,17 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     int32_t spage[MOE_MAX_K], vpage[MOE_MAX_K];
     int32_t transit[MOE_MAX_K];
     int ntransit = 0;
+    // pages in transit are free again when this call returns, on every path
+    // (a page's event says when its last copy is done)
+    struct TransitBack {
+        moe_host_tier *X;
+        const int32_t *pages;
+        const int *n;
+        ~TransitBack() {
+            if (X)
+                for (int q = 0; q < *n; q++) X->free_pages.push_back(pages[q]);
+        }
+    } transit_back{X, transit, &ntransit};
     for (int n = 0; n < k; n++) {
         const int j = order[n];
         const uint32_t key = layer_id * (uint32_t)E + (uint32_t)c->h_idx[j];
@@ -652,7 +663,10 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
                 const int32_t hv = X->core.insert_kind(victim, kTraceDemote, &gone);
                 if (gone == kNoKey) {
                     rc = tier_take_page(X, false, X->down, &X->page_of[hv]);
-                    if (rc) return rc;
+                    if (rc) {
+                        X->core.drop_slot(hv);      // no page: the key is not kept
+                        return rc;
+                    }
                 }
                 vpage[j] = X->page_of[hv];     // a key that left the tier leaves its page to this one
                 X->demotions++;
@@ -797,9 +811,6 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
             if ((rc = copy_miss(morder[n]))) return rc;
             if ((rc = run_miss(morder[n]))) return rc;
         }
-        // the transit pages are free again once their copies are done (each
-        // page's event says when)
-        for (int q = 0; q < ntransit; q++) X->free_pages.push_back(transit[q]);
     } else {
         // file tier: the hit experts run while the misses' records are read
         // into host slots
