@@ -175,6 +175,21 @@ def test_decode_forward_k3_shape_shared(moe):
     _check_decode(moe, synth.get_config("k3_slice", tokens=2, layers=2), method="gathers")
 
 
+def test_decode_forward_more_layers_than_one_launch(moe):
+    # 45 layers: more than one launch carries (40), so the decode runs one
+    # launch per (token, layer group); every layer call against the oracle
+    _check_decode(moe, synth.get_config("tiny", tokens=2, layers=45))
+
+
+def test_decode_forward_no_tokens(moe):
+    # T = 0: nothing to decode, no launch, no error
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    dw = DeviceWorkload(synth.get_config("tiny", tokens=1))
+    x = torch.empty((0, 1, dw.cfg.H), dtype=torch.float32, device="cuda")
+    out, idx = moe.decode_forward(dw.layers, x)
+    assert out.shape[0] == 0 and idx.shape[0] == 0
+
+
 @pytest.mark.parametrize("k", [4, 8])
 def test_decode_forward_k3_shape_fewer_experts_per_token(moe, k):
     # num_experts_per_token below the K3 default of 16 (the k sweep's settings)
