@@ -21,6 +21,12 @@
 // K-step s uses group 4*(l/16)+s in lane block l/16 (a fixed permutation of
 // K, applied to A and B alike).  The weight row scale is applied to the fp32
 // accumulator.
+//
+// A workgroup multiplies by one matrix of one expert (gate, up or down): its
+// LDS is one codebook plus the A ring (76 KB), so two workgroups share a CU
+// and one's codebook staging and epilogue overlap the other's gathers.  Gate
+// and up go to fp32 buffers and a separate elementwise kernel forms
+// h = bf16(SiLU(gate) * up) for the down GEMM.
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
@@ -32,10 +38,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kNwGateUp = 16;       // waves per workgroup (gate/up)
-constexpr int kTwGateUp = 1;        // 16-row tiles per wave unit (gate/up)
-constexpr int kNwDown = 16;         // waves per workgroup (down)
-constexpr int kTwDown = 2;          // 16-row tiles per wave unit (down)
+constexpr int kNw = 8;              // waves per workgroup
+constexpr int kTw = 2;              // 16-row tiles per wave unit
 
 __device__ __forceinline__ uint32_t bf16_pair_from_f16_pair(uint32_t a) {
     const f16x2 h = __builtin_bit_cast(f16x2, a);
@@ -141,11 +145,12 @@ struct GroupedArgs {
     // operands
     const uint16_t *a;          // A rows: x bf16 [T, K] (gate/up) or h bf16 [positions, K] (down)
     int a_by_token;             // 1: A row of position p = token of p; 0: A row = p
-    uint16_t *hout;             // gate/up: h bf16 [positions, N]
-    float *yout;                // down: y fp32 [positions, N] (scaled)
+    float *yout;                // y fp32 [positions, N] (scaled by the row scale) of matrix mat
     int N, K;                   // weight matrix rows (outputs) and columns (reduction)
-    int splits;                 // workgroups per expert (row ranges)
-    int mat;                    // RVQ matrix: 0 = gate (+up), 2 = down
+    int splits;                 // workgroups per expert and matrix (row ranges)
+    int mat;                    // first RVQ matrix: 0 = gate, 1 = up, 2 = down
+    int mats;                   // matrices mat .. mat+mats-1, each by workgroups of its own
+    size_t ymat_stride;         // elements between the outputs of consecutive matrices
     int xcd_group;              // 1: place each expert's workgroups on one XCD (expert count % 8 == 0)
 };
 
@@ -250,8 +255,8 @@ __global__ __launch_bounds__(256) void k_dense_mm(const uint16_t *__restrict__ A
 // codes).  All waves of a workgroup sweep the 128-column chunks together:
 //  - the A operand (16 token rows x 128 columns, 4 KB per chunk) goes
 //    through a 3-slot ring in LDS, copied once per workgroup instead of once
-//    per wave (each wave copies 1/8 of a chunk two chunks ahead), with one
-//    workgroup barrier per chunk;
+//    per wave (the first four waves copy it, one 16-byte piece per lane, two
+//    chunks ahead), with one workgroup barrier per chunk;
 //  - each wave keeps its own codes in a 3-deep register ring (loads past the
 //    last chunk re-read it and tiles past the last row re-use the last tile,
 //    so the steady state has no branches around its loads);
@@ -282,30 +287,24 @@ __device__ __forceinline__ RvqQuadOff rvq_quad_off(int g4) {
 
 template <int TW>
 struct RvqStage {
-    // per tile (gate or down; up): the 8-byte load in [0], [1], the 4-byte one in [2]
-    uint32_t c0[TW][3], c1[TW][3];
+    // per tile: the 8-byte load in [0], [1], the 4-byte one in [2]
+    uint32_t c0[TW][3];
 };
 
-// Codes of chunk j through buffer loads: rs0/rs1 describe the code sections
-// of the two matrices (reads past a section's end return zero), qoff[t] the
-// lane's byte offsets of its two loads of tile t in chunk 0, and the chunk's
-// offset goes in the scalar offset.  Streaming (nt) loads.
-template <bool GATEUP, int TW>
-__device__ __forceinline__ void rvq_load(RvqStage<TW> &st, __amdgpu_buffer_rsrc_t rs0, __amdgpu_buffer_rsrc_t rs1,
-                                         const uint32_t (&qoff)[TW][2], int j) {
+// Codes of chunk j through buffer loads: rs describes the matrix's code
+// section (reads past its end return zero), qoff[t] the lane's byte offsets
+// of its two loads of tile t in chunk 0, and the chunk's offset goes in the
+// scalar offset.  Streaming (nt) loads.
+template <int TW>
+__device__ __forceinline__ void rvq_load(RvqStage<TW> &st, __amdgpu_buffer_rsrc_t rs, const uint32_t (&qoff)[TW][2],
+                                         int j) {
     const int soff = j * kTileBytes;
 #pragma unroll
     for (int t = 0; t < TW; t++) {
-        const auto q0 = __builtin_amdgcn_raw_buffer_load_b64(rs0, (int)qoff[t][0], soff, kBufNt);
+        const auto q0 = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)qoff[t][0], soff, kBufNt);
         st.c0[t][0] = q0[0];
         st.c0[t][1] = q0[1];
-        st.c0[t][2] = __builtin_amdgcn_raw_buffer_load_b32(rs0, (int)qoff[t][1], soff, kBufNt);
-        if constexpr (GATEUP) {
-            const auto q1 = __builtin_amdgcn_raw_buffer_load_b64(rs1, (int)qoff[t][0], soff, kBufNt);
-            st.c1[t][0] = q1[0];
-            st.c1[t][1] = q1[1];
-            st.c1[t][2] = __builtin_amdgcn_raw_buffer_load_b32(rs1, (int)qoff[t][1], soff, kBufNt);
-        }
+        st.c0[t][2] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)qoff[t][1], soff, kBufNt);
     }
 }
 
@@ -317,38 +316,28 @@ __device__ __forceinline__ void rvq_dwords(const uint32_t (&c)[3], bool odd, uin
     d2 = odd ? c[1] : c[2];
 }
 
-// Gathered B fragments of one K-step: C[a] and C[b] per tile and matrix.
-template <bool GATEUP, int TW>
+// Gathered B fragments of one K-step: C[a] and C[b] per tile.
+template <int TW>
 struct RvqGather {
-    bf16x8 b[TW][GATEUP ? 2 : 1][2];
+    bf16x8 b[TW][2];
 };
 
-template <bool GATEUP, int TW, int S>
-__device__ __forceinline__ void rvq_gather(const RvqStage<TW> &st, bool odd, const char *cb0, const char *cb1,
-                                           RvqGather<GATEUP, TW> &g) {
+template <int TW, int S>
+__device__ __forceinline__ void rvq_gather(const RvqStage<TW> &st, bool odd, const char *cb, RvqGather<TW> &g) {
 #pragma unroll
     for (int t = 0; t < TW; t++) {
         uint32_t d0, d1, d2;
         rvq_dwords(st.c0[t], odd, d0, d1, d2);
-        group_rows(cb0, quad_code<S>(d0, d1, d2), g.b[t][0][0], g.b[t][0][1]);
-        if constexpr (GATEUP) {
-            rvq_dwords(st.c1[t], odd, d0, d1, d2);
-            group_rows(cb1, quad_code<S>(d0, d1, d2), g.b[t][1][0], g.b[t][1][1]);
-        }
+        group_rows(cb, quad_code<S>(d0, d1, d2), g.b[t][0], g.b[t][1]);
     }
 }
 
-template <bool GATEUP, int TW>
-__device__ __forceinline__ void rvq_mfma(const bf16x8 &a, const RvqGather<GATEUP, TW> &g, f32x4 (&acc0)[TW],
-                                         f32x4 (&acc1)[TW]) {
+template <int TW>
+__device__ __forceinline__ void rvq_mfma(const bf16x8 &a, const RvqGather<TW> &g, f32x4 (&acc)[TW]) {
 #pragma unroll
     for (int t = 0; t < TW; t++) {
-        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][0][0], acc0[t], 0, 0, 0);
-        acc0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][0][1], acc0[t], 0, 0, 0);
-        if constexpr (GATEUP) {
-            acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][1][0], acc1[t], 0, 0, 0);
-            acc1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][1][1], acc1[t], 0, 0, 0);
-        }
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][0], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g.b[t][1], acc[t], 0, 0, 0);
     }
 }
 
@@ -362,10 +351,10 @@ __device__ __forceinline__ void lds_wait_barrier() {
 
 // The A ring.  Token m's 16-byte piece q (columns 8q..8q+7 of the chunk)
 // sits at m*256 + (q ^ m)*16 of a slot, so the 16 lanes of one lane block
-// (16 tokens, one piece each) read 16 different bank groups.  Thread i of
-// the workgroup copies piece (i % 256) to slot byte 16 (i % 256); beyond 256
-// threads the copies repeat, which keeps the copy free of branches.
+// (16 tokens, one piece each) read 16 different bank groups.  Thread i < 256
+// of the workgroup copies piece i to slot byte 16 i.
 struct ARing {
+    bool copy;                  // this wave copies (waves 0-3; wave-uniform)
     char *base;                 // slot 0
     const uint16_t *src;        // the lane's token row + its piece (columns 8q..)
     uint32_t wr;                // byte offset of the lane's piece in a slot
@@ -383,46 +372,44 @@ __device__ __forceinline__ void a_store(const ARing &r, int slot, const u32x4 &v
 // chunk's gathers and areg the A piece of chunk j+1 (copied here into the
 // ring); areg leaves with chunk j+2's piece, fill with chunk j+2's codes
 // and, with NEXT, g with K-step 0 of the next chunk (nxt).
-template <bool GATEUP, int TW, bool NEXT, int R>
+template <int TW, bool NEXT, int R>
 __device__ __forceinline__ void rvq_chunk(const RvqStage<TW> &cur, const RvqStage<TW> &nxt, RvqStage<TW> &fill,
-                                          __amdgpu_buffer_rsrc_t rs0, __amdgpu_buffer_rsrc_t rs1,
-                                          const uint32_t (&qoff)[TW][2], bool odd,
-                                          int j, int cpr, const ARing &ar, u32x4 &areg,
-                                          const char *cb0, const char *cb1, RvqGather<GATEUP, TW> &g,
-                                          f32x4 (&acc0)[TW], f32x4 (&acc1)[TW]) {
-    constexpr int kG = TW * (GATEUP ? 2 : 1) * 2;   // gathers per K-step
+                                          __amdgpu_buffer_rsrc_t rs, const uint32_t (&qoff)[TW][2], bool odd,
+                                          int j, int cpr, const ARing &ar, u32x4 &areg, const char *cb,
+                                          RvqGather<TW> &g, f32x4 (&acc)[TW]) {
+    constexpr int kG = TW * 2;   // gathers per K-step
     static_assert(kG <= 15, "lgkmcnt range");
-    a_store(ar, (R + 1) % kARing, areg);
+    if (ar.copy) a_store(ar, (R + 1) % kARing, areg);
     bf16x8 a[4];
     const char *slot = ar.base + R * kASlot;
 #pragma unroll
     for (int s = 0; s < 4; s++) a[s] = *(const bf16x8 *)(slot + ar.rd[s]);
-    areg = a_fetch(ar, min(j + 2, cpr - 1));
-    rvq_load<GATEUP, TW>(fill, rs0, rs1, qoff, min(j + 2, cpr - 1));
+    if (ar.copy) areg = a_fetch(ar, min(j + 2, cpr - 1));
+    rvq_load<TW>(fill, rs, qoff, min(j + 2, cpr - 1));
     __builtin_amdgcn_sched_barrier(0);
-    RvqGather<GATEUP, TW> g1, g2;
-    rvq_gather<GATEUP, TW, 1>(cur, odd, cb0, cb1, g1);
+    RvqGather<TW> g1, g2;
+    rvq_gather<TW, 1>(cur, odd, cb, g1);
     __builtin_amdgcn_sched_barrier(0);
     // the A copy of chunk j+1 (issued before the K-step 1 gathers) is done
     lds_wait_barrier<kG>();
     __builtin_amdgcn_sched_barrier(0);
-    rvq_mfma<GATEUP, TW>(a[0], g, acc0, acc1);
+    rvq_mfma<TW>(a[0], g, acc);
     __builtin_amdgcn_sched_barrier(0);
-    rvq_gather<GATEUP, TW, 2>(cur, odd, cb0, cb1, g2);
+    rvq_gather<TW, 2>(cur, odd, cb, g2);
     __builtin_amdgcn_sched_barrier(0);
-    rvq_mfma<GATEUP, TW>(a[1], g1, acc0, acc1);
+    rvq_mfma<TW>(a[1], g1, acc);
     __builtin_amdgcn_sched_barrier(0);
-    rvq_gather<GATEUP, TW, 3>(cur, odd, cb0, cb1, g1);
+    rvq_gather<TW, 3>(cur, odd, cb, g1);
     __builtin_amdgcn_sched_barrier(0);
-    rvq_mfma<GATEUP, TW>(a[2], g2, acc0, acc1);
+    rvq_mfma<TW>(a[2], g2, acc);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) rvq_gather<GATEUP, TW, 0>(nxt, odd, cb0, cb1, g);
+    if constexpr (NEXT) rvq_gather<TW, 0>(nxt, odd, cb, g);
     __builtin_amdgcn_sched_barrier(0);
-    rvq_mfma<GATEUP, TW>(a[3], g1, acc0, acc1);
+    rvq_mfma<TW>(a[3], g1, acc);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool GATEUP, int TW, int NW>
+template <int TW, int NW>
 __global__ __launch_bounds__(NW * 64) void k_grouped_rvq(GroupedArgs g) {
     static_assert(NW >= 4, "the A copy needs 256 lanes");
     extern __shared__ __align__(16) char lds[];
@@ -430,28 +417,30 @@ __global__ __launch_bounds__(NW * 64) void k_grouped_rvq(GroupedArgs g) {
     // expert count is a multiple of 8, the row ranges of one expert all go to
     // one XCD (consecutive there), so its codebooks and A rows come from HBM
     // once and from that XCD's L2 after.
-    int slot, split;
+    // An expert's units are its matrices' row ranges (matrix-major).
+    const int units = g.mats * g.splits;
+    int slot, unit;
     if (g.xcd_group) {
         const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
-        slot = (idx / g.splits) * 8 + xcd;
-        split = idx % g.splits;
+        slot = (idx / units) * 8 + xcd;
+        unit = idx % units;
     } else {
-        slot = blockIdx.x / g.splits;
-        split = blockIdx.x % g.splits;
+        slot = blockIdx.x / units;
+        unit = blockIdx.x % units;
     }
+    const int split = unit % g.splits, m = unit / g.splits;
+    const int mat = g.mat + m;
+    float *const yout = g.yout + m * g.ymat_stride;
     const int cnt = g.counts[slot], pos0 = g.offsets[slot];
     if (cnt == 0) return;                 // uniform across the workgroup
     const uint8_t *rec = (const uint8_t *)g.table[slot];
-    char *cb0 = lds, *cb1 = lds + kCbRows * 16;
-    char *aring = lds + (GATEUP ? 2 : 1) * kCbRows * 16;
+    char *cb = lds, *aring = lds + kCbRows * 16;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    // codebooks into LDS with direct copies (all in flight at once), then bf16
-    stage_lds_waves<kLdsPlain, NW>(cb0, rec + g.off.cb[g.mat], kCbRows * 16, wave, lane);
-    if constexpr (GATEUP) stage_lds_waves<kLdsPlain, NW>(cb1, rec + g.off.cb[1], kCbRows * 16, wave, lane);
+    // the codebook into LDS with direct copies (all in flight at once), then bf16
+    stage_lds_waves<kLdsPlain, NW>(cb, rec + g.off.cb[mat], kCbRows * 16, wave, lane);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    codebook_to_bf16(cb0);
-    if constexpr (GATEUP) codebook_to_bf16(cb1);
+    codebook_to_bf16(cb);
     const int col = lane & 15, g4 = lane >> 4;
     const RvqQuadOff qo = rvq_quad_off(g4);
     const bool odd = (g4 & 1) != 0;
@@ -461,17 +450,15 @@ __global__ __launch_bounds__(NW * 64) void k_grouped_rvq(GroupedArgs g) {
     const int tgroups = (tiles + TW - 1) / TW;
     const int rounds = (tgroups + NW - 1) / NW;
     const int cpr = g.K / kChunkCols;
-    const int code_bytes = g.N / 64 * cpr * kTileBytes;   // one matrix's code section
-    const __amdgpu_buffer_rsrc_t rs0 =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(rec + g.off.codes[g.mat]), 0, code_bytes, kBufWord3);
-    const __amdgpu_buffer_rsrc_t rs1 =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(rec + g.off.codes[1]), 0, code_bytes, kBufWord3);
-    const _Float16 *sc0 = (const _Float16 *)(rec + g.off.scales[g.mat]);
-    const _Float16 *sc1 = (const _Float16 *)(rec + g.off.scales[1]);
+    const int code_bytes = g.N / 64 * cpr * kTileBytes;   // the matrix's code section
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(rec + g.off.codes[mat]), 0, code_bytes, kBufWord3);
+    const _Float16 *sc = (const _Float16 *)(rec + g.off.scales[mat]);
     const int passes = (cnt + 15) / 16;
     ARing ar;
+    ar.copy = wave < 4;
     ar.base = aring;
-    const int apiece = (wave * 64 + lane) & 255;   // A piece this lane copies: token apiece/16, piece apiece%16
+    const int apiece = (wave * 64 + lane) & 255;   // A piece a copying lane copies: token apiece/16, piece apiece%16
     ar.wr = apiece * 16;
 #pragma unroll
     for (int s = 0; s < 4; s++) ar.rd[s] = col * 256 + (((4 * g4 + s) ^ col) & 15) * 16;
@@ -501,64 +488,64 @@ __global__ __launch_bounds__(NW * 64) void k_grouped_rvq(GroupedArgs g) {
             const uint16_t *row = g.a + (size_t)(g.a_by_token ? g.perm[p] / g.k : p) * g.K;
             ar.src = row + (((lane & 15) ^ mloc) & 15) * 8;
         }
-        f32x4 acc0[TW], acc1[TW];
+        f32x4 acc[TW];
 #pragma unroll
-        for (int t = 0; t < TW; t++) {
-            acc0[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            acc1[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
+        for (int t = 0; t < TW; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
         // prologue: every wave is past the previous unit's last A reads (and
         // the codebook conversion) before slot 0 is rewritten
-        u32x4 areg = a_fetch(ar, 0);
+        u32x4 areg = {0u, 0u, 0u, 0u};
+        if (ar.copy) areg = a_fetch(ar, 0);
         lds_wait_barrier<0>();
-        a_store(ar, 0, areg);
-        areg = a_fetch(ar, min(1, cpr - 1));
+        if (ar.copy) {
+            a_store(ar, 0, areg);
+            areg = a_fetch(ar, min(1, cpr - 1));
+        }
         RvqStage<TW> st[3];
-        rvq_load<GATEUP, TW>(st[0], rs0, rs1, qoff, 0);
-        rvq_load<GATEUP, TW>(st[1], rs0, rs1, qoff, min(1, cpr - 1));
-        RvqGather<GATEUP, TW> g0;
-        rvq_gather<GATEUP, TW, 0>(st[0], odd, cb0, cb1, g0);
+        rvq_load<TW>(st[0], rs, qoff, 0);
+        rvq_load<TW>(st[1], rs, qoff, min(1, cpr - 1));
+        RvqGather<TW> g0;
+        rvq_gather<TW, 0>(st[0], odd, cb, g0);
         lds_wait_barrier<0>();
         int j = 0;
         for (; j + 3 <= cpr; j += 3) {
-            rvq_chunk<GATEUP, TW, true, 0>(st[0], st[1], st[2], rs0, rs1, qoff, odd, j, cpr, ar, areg, cb0, cb1, g0,
-                                           acc0, acc1);
-            rvq_chunk<GATEUP, TW, true, 1>(st[1], st[2], st[0], rs0, rs1, qoff, odd, j + 1, cpr, ar, areg, cb0, cb1,
-                                           g0, acc0, acc1);
-            rvq_chunk<GATEUP, TW, true, 2>(st[2], st[0], st[1], rs0, rs1, qoff, odd, j + 2, cpr, ar, areg, cb0, cb1,
-                                           g0, acc0, acc1);
+            rvq_chunk<TW, true, 0>(st[0], st[1], st[2], rs, qoff, odd, j, cpr, ar, areg, cb, g0, acc);
+            rvq_chunk<TW, true, 1>(st[1], st[2], st[0], rs, qoff, odd, j + 1, cpr, ar, areg, cb, g0, acc);
+            rvq_chunk<TW, true, 2>(st[2], st[0], st[1], rs, qoff, odd, j + 2, cpr, ar, areg, cb, g0, acc);
         }
         // the last cpr - j (< 3) chunks are already in st[0], st[1]
         if (j + 2 == cpr) {
-            rvq_chunk<GATEUP, TW, true, 0>(st[0], st[1], st[2], rs0, rs1, qoff, odd, j, cpr, ar, areg, cb0, cb1, g0,
-                                           acc0, acc1);
-            rvq_chunk<GATEUP, TW, false, 1>(st[1], st[2], st[0], rs0, rs1, qoff, odd, j + 1, cpr, ar, areg, cb0, cb1,
-                                            g0, acc0, acc1);
+            rvq_chunk<TW, true, 0>(st[0], st[1], st[2], rs, qoff, odd, j, cpr, ar, areg, cb, g0, acc);
+            rvq_chunk<TW, false, 1>(st[1], st[2], st[0], rs, qoff, odd, j + 1, cpr, ar, areg, cb, g0, acc);
         } else if (j + 1 == cpr) {
-            rvq_chunk<GATEUP, TW, false, 0>(st[0], st[1], st[2], rs0, rs1, qoff, odd, j, cpr, ar, areg, cb0, cb1, g0,
-                                            acc0, acc1);
+            rvq_chunk<TW, false, 0>(st[0], st[1], st[2], rs, qoff, odd, j, cpr, ar, areg, cb, g0, acc);
         }
         if (!active) continue;
         // epilogue: lane holds D[4*g4 + i][col] of each tile
 #pragma unroll
         for (int t = 0; t < TW; t++) {
             if (t >= ntw) continue;
-            const float s0v = (float)sc0[n[t]];
-            const float s1v = GATEUP ? (float)sc1[n[t]] : 1.f;
+            const float sv = (float)sc[n[t]];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int mm = pass * 16 + 4 * g4 + i;
                 if (mm >= cnt) continue;
-                const size_t p = (size_t)(pos0 + mm);
-                if constexpr (GATEUP) {
-                    const float gg = acc0[t][i] * s0v, uu = acc1[t][i] * s1v;
-                    const __bf16 h = (__bf16)(gg / (1.f + __expf(-gg)) * uu);
-                    g.hout[p * g.N + n[t]] = __builtin_bit_cast(uint16_t, h);
-                } else {
-                    g.yout[p * g.N + n[t]] = acc0[t][i] * s0v;
-                }
+                yout[(size_t)(pos0 + mm) * g.N + n[t]] = acc[t][i] * sv;
             }
         }
+    }
+}
+
+// h = bf16(SiLU(g) * u) from the fp32 gate and up outputs, 4 per thread
+__global__ __launch_bounds__(256) void k_silu_mul(const float4 *__restrict__ gv, const float4 *__restrict__ uv,
+                                                  size_t n4, uint2 *__restrict__ h) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+        const float4 a = gv[i], b = uv[i];
+        const float gg[4] = {a.x, a.y, a.z, a.w}, uu[4] = {b.x, b.y, b.z, b.w};
+        uint16_t r[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            r[j] = __builtin_bit_cast(uint16_t, (__bf16)(gg[j] / (1.f + __expf(-gg[j])) * uu[j]));
+        h[i] = make_uint2(r[0] | (uint32_t)r[1] << 16, r[2] | (uint32_t)r[3] << 16);
     }
 }
 
@@ -600,10 +587,9 @@ static int pick_splits(int N, int TW, int NW) {
     return 1;
 }
 
-constexpr int kLdsGateUp = 2 * kCbRows * 16 + kARing * kASlot;
-constexpr int kLdsDown = kCbRows * 16 + kARing * kASlot;
+constexpr int kLdsRvq = kCbRows * 16 + kARing * kASlot;   // 76 KB: two workgroups per CU
 
-hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, int E, int H, int I,
+hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, int E, int H, int I, int n_pairs,
                               const int32_t *counts, const int32_t *offsets, const int32_t *perm, int k,
                               const uint16_t *xb, uint16_t *hbuf, float *ybuf, hipStream_t s) {
     GroupedArgs g{};
@@ -613,38 +599,43 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
     g.offsets = offsets;
     g.perm = perm;
     g.k = k;
-    // gate/up: N = I rows, K = H
-    g.a = xb;
-    g.a_by_token = 1;
-    g.hout = hbuf;
-    g.N = I;
-    g.K = H;
-    g.splits = pick_splits(I, kTwGateUp, kNwGateUp);
-    g.mat = 0;
     g.xcd_group = E % 8 == 0;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_grouped_rvq<true, kTwGateUp, kNwGateUp>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsGateUp);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void *)k_grouped_rvq<false, kTwDown, kNwDown>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDown);
+        const hipError_t e = hipFuncSetAttribute((const void *)k_grouped_rvq<kTw, kNw>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsRvq);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    k_grouped_rvq<true, kTwGateUp, kNwGateUp><<<E * g.splits, kNwGateUp * 64, kLdsGateUp, s>>>(g);
+    // gate and up (N = I rows, K = H, A = x rows by token), each by its own
+    // workgroups: gate into ybuf[0, pairs*I), up into ybuf[pairs*I, 2*pairs*I)
+    g.a = xb;
+    g.a_by_token = 1;
+    g.N = I;
+    g.K = H;
+    g.mat = 0;
+    g.mats = 2;
+    g.ymat_stride = (size_t)n_pairs * I;
+    g.yout = ybuf;
+    g.splits = pick_splits(I, kTw, kNw);
+    k_grouped_rvq<kTw, kNw><<<E * 2 * g.splits, kNw * 64, kLdsRvq, s>>>(g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // h = bf16(SiLU(gate) * up)
+    const size_t n4 = (size_t)n_pairs * I / 4;
+    const int grid = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+    k_silu_mul<<<grid, 256, 0, s>>>((const float4 *)ybuf, (const float4 *)(ybuf + g.ymat_stride), n4, (uint2 *)hbuf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     // down: N = H rows, K = I; A = h rows by position
     g.a = hbuf;
     g.a_by_token = 0;
-    g.hout = nullptr;
-    g.yout = ybuf;
     g.N = H;
     g.K = I;
-    g.splits = pick_splits(H, kTwDown, kNwDown);
     g.mat = 2;
-    k_grouped_rvq<false, kTwDown, kNwDown><<<E * g.splits, kNwDown * 64, kLdsDown, s>>>(g);
+    g.mats = 1;
+    g.ymat_stride = 0;
+    g.splits = pick_splits(H, kTw, kNw);
+    k_grouped_rvq<kTw, kNw><<<E * g.splits, kNw * 64, kLdsRvq, s>>>(g);
     return hipGetLastError();
 }
 

@@ -128,7 +128,7 @@ GroupedWs carve_grouped(void *ws, int H, int I, int E, int k, int T, bool shared
     G.offsets = c.take<int32_t>((size_t)E + 1);
     G.xb = c.take<uint16_t>((size_t)T * H);
     G.hbuf = c.take<uint16_t>(pairs * I);
-    G.ybuf = c.take<float>(pairs * H);
+    G.ybuf = c.take<float>(pairs * std::max(H, 2 * I));   // y, or gate and up before it
     G.hs = shared ? c.take<uint16_t>((size_t)T * I) : nullptr;
     G.ysh = shared ? c.take<float>((size_t)T * H) : nullptr;
     G.bytes = (size_t)align_up((int64_t)c.pos, 256);
@@ -944,7 +944,7 @@ int moe_layer_forward_grouped(const moe_layer *L, const void *x, int32_t x_dtype
     HIPCHK(launch_group(idx, T * k, E, W.perm, W.inv, W.counts, W.offsets, s), "group");
     HIPCHK(launch_to_bf16(x, x_dtype, (size_t)T * H, W.xb, s), "x to bf16");
     if (L->shared) HIPCHK(launch_grouped_dense(L->shared, H, I, T, W.xb, W.hs, W.ysh, s), "shared expert");
-    HIPCHK(launch_grouped_rvq(L->records, offsets_of(H, I), E, H, I, W.counts, W.offsets, W.perm, k, W.xb, W.hbuf,
+    HIPCHK(launch_grouped_rvq(L->records, offsets_of(H, I), E, H, I, T * k, W.counts, W.offsets, W.perm, k, W.xb, W.hbuf,
                               W.ybuf, s), "grouped RVQ GEMMs");
     HIPCHK(launch_grouped_combine(W.ybuf, W.inv, w, k, H, T, L->shared ? W.ysh : nullptr, out, s), "combine");
     return MOE_OK;

@@ -161,7 +161,7 @@ int decode_noalloc_scratch(void **out);
 hipError_t launch_group(const int32_t *idx, int n_pairs, int E, int32_t *perm, int32_t *inv, int32_t *counts,
                         int32_t *offsets, hipStream_t s);
 hipError_t launch_to_bf16(const void *x, int x_dtype, size_t n, uint16_t *xb, hipStream_t s);
-hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, int E, int H, int I,
+hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, int E, int H, int I, int n_pairs,
                               const int32_t *counts, const int32_t *offsets, const int32_t *perm, int k,
                               const uint16_t *xb, uint16_t *hbuf, float *ybuf, hipStream_t s);
 hipError_t launch_grouped_dense(const uint16_t *shared, int H, int I, int T, const uint16_t *xb, uint16_t *hs,
