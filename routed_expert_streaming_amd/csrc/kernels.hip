@@ -564,7 +564,7 @@ hipError_t launch_route_logits(const float *W, const float *bias, int E, int H, 
 int route_blocked_slices(int E, int H, int T) {
     const int tiles = ((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE);
     const int steps = H / kRbK;
-    int ks = (256 + tiles - 1) / tiles;
+    int ks = (512 + tiles - 1) / tiles;   // about two workgroups per CU
     return std::max(1, std::min(ks, std::min(steps, kRouteMaxSlices)));
 }
 

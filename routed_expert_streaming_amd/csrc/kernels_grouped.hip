@@ -78,45 +78,69 @@ __device__ __forceinline__ uint32_t quad_code(uint32_t d0, uint32_t d1, uint32_t
 }
 
 // ------------------------------------------------------------------ group
-// One workgroup: histogram of expert ids, exclusive scan, scatter, then a
-// per-expert insertion sort so every segment lists its pairs in ascending
-// pair index (deterministic).
+// One workgroup: histogram of expert ids, exclusive scan (one wave), scatter,
+// then a per-expert insertion sort so every segment lists its pairs in
+// ascending pair index (deterministic).  Up to kGroupLdsPairs pairs are
+// scattered and sorted in LDS and written out once; more are sorted in place
+// in global memory.
+constexpr int kGroupLdsPairs = 12288;
+
 __global__ __launch_bounds__(1024) void k_group(const int32_t *__restrict__ idx, int n_pairs, int E,
                                                 int32_t *__restrict__ perm, int32_t *__restrict__ inv,
                                                 int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
     __shared__ int cnt[MOE_MAX_E + 1];
     __shared__ int off[MOE_MAX_E + 1];
     __shared__ int fill[MOE_MAX_E];
+    __shared__ int sperm[kGroupLdsPairs];
+    const bool in_lds = n_pairs <= kGroupLdsPairs;
+    int *P = in_lds ? sperm : perm;
     for (int e = threadIdx.x; e <= E; e += blockDim.x) { cnt[e] = 0; fill[e < E ? e : 0] = 0; }
     __syncthreads();
     for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) atomicAdd(&cnt[idx[p]], 1);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int s = 0;
-        for (int e = 0; e < E; e++) { off[e] = s; s += cnt[e]; }
-        off[E] = s;
+    if (threadIdx.x < 64) {
+        // lane l sums experts [l*per, (l+1)*per); a shuffle scan gives the bases
+        const int lane = threadIdx.x, per = (E + 63) / 64;
+        const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
+        int local = 0;
+        for (int e = e0; e < e1; e++) local += cnt[e];
+        int incl = local;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
+        }
+        int base = incl - local;
+        for (int e = e0; e < e1; e++) {
+            off[e] = base;
+            base += cnt[e];
+        }
+        if (lane == 63) off[E] = incl;
     }
     __syncthreads();
     for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
         const int e = idx[p];
-        perm[off[e] + atomicAdd(&fill[e], 1)] = p;
+        P[off[e] + atomicAdd(&fill[e], 1)] = p;
     }
     __syncthreads();
     __threadfence_block();
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         const int b = off[e], n = cnt[e];
         for (int i = 1; i < n; i++) {
-            const int v = perm[b + i];
+            const int v = P[b + i];
             int j = i - 1;
-            while (j >= 0 && perm[b + j] > v) { perm[b + j + 1] = perm[b + j]; j--; }
-            perm[b + j + 1] = v;
+            while (j >= 0 && P[b + j] > v) { P[b + j + 1] = P[b + j]; j--; }
+            P[b + j + 1] = v;
         }
         counts[e] = n;
         offsets[e] = b;
     }
     if (threadIdx.x == 0) offsets[E] = off[E];
     __syncthreads();
-    for (int q = threadIdx.x; q < n_pairs; q += blockDim.x) inv[perm[q]] = q;
+    for (int q = threadIdx.x; q < n_pairs; q += blockDim.x) {
+        const int p = P[q];
+        if (in_lds) perm[q] = p;
+        inv[p] = q;
+    }
 }
 
 // x (fp32 or bf16) -> bf16 [T, H]
@@ -161,15 +185,18 @@ struct GroupedArgs {
 // through LDS in stages of 64 columns, double-buffered, the next stage's
 // operands loaded into registers while this stage is multiplied.  Rows are
 // padded to 144 bytes in LDS so the 16 lanes of a fragment read hit 16
-// different bank groups.  Gate/up: two weight matrices, epilogue
-// h = bf16(SiLU(g) * u); down: fp32 output.  Token rows past T are clamped
-// on load and never written.
+// different bank groups.  K may be split over gridDim.z slices (contiguous
+// stage ranges) so that a few-token GEMM still has several workgroups per CU
+// in flight; each slice then writes fp32 partial sums, part[z][b][t][n] (b:
+// gate, up) or part[z][t][n].  Gate/up with one slice writes
+// h = bf16(SiLU(g) * u) directly.  Token rows past T are clamped on load and
+// never written.
 constexpr int kDnN = 64, kDnM = 32, kDnK = 64, kDnRow = 144;
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void k_dense_mm(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W0,
                                                   const uint16_t *__restrict__ W1, int T, int N, int K,
-                                                  uint16_t *__restrict__ hout, float *__restrict__ yout) {
+                                                  uint16_t *__restrict__ hout, float *__restrict__ part) {
     constexpr int NB = GATEUP ? 2 : 1;
     constexpr int kStage = (kDnM + NB * kDnN) * kDnRow;
     __shared__ __align__(16) char lds[2 * kStage];
@@ -208,13 +235,14 @@ __global__ __launch_bounds__(256) void k_dense_mm(const uint16_t *__restrict__ A
     for (int b = 0; b < NB; b++)
 #pragma unroll
         for (int j = 0; j < 2; j++) acc[b][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    const int stages = K / kDnK;
-    fetch(0);
+    const int stages = K / kDnK, z = blockIdx.z, ks = gridDim.z;
+    const int st_begin = z * stages / ks, st_end = (z + 1) * stages / ks;
+    fetch(st_begin * kDnK);
     stash(0);
     __syncthreads();
-    for (int st = 0; st < stages; st++) {
-        const int cur = st & 1;
-        if (st + 1 < stages) fetch((st + 1) * kDnK);
+    for (int st = st_begin; st < st_end; st++) {
+        const int cur = (st - st_begin) & 1;
+        if (st + 1 < st_end) fetch((st + 1) * kDnK);
         const char *L = lds + cur * kStage;
 #pragma unroll
         for (int kk = 0; kk < kDnK / 32; kk++) {
@@ -228,7 +256,7 @@ __global__ __launch_bounds__(256) void k_dense_mm(const uint16_t *__restrict__ A
                     acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[b][j], 0, 0, 0);
                 }
         }
-        if (st + 1 < stages) stash(cur ^ 1);
+        if (st + 1 < st_end) stash(cur ^ 1);
         __syncthreads();
     }
     // lane holds D[token 4*g4 + i][row col] of each 16 x 16 tile
@@ -239,14 +267,28 @@ __global__ __launch_bounds__(256) void k_dense_mm(const uint16_t *__restrict__ A
         for (int i = 0; i < 4; i++) {
             const int t = m0 + wm + 4 * g4 + i;
             if (t >= T) continue;
-            if constexpr (GATEUP) {
+            if (GATEUP && ks == 1) {
                 const float g = acc[0][j][i], u = acc[NB - 1][j][i];
                 const __bf16 h = (__bf16)(g / (1.f + __expf(-g)) * u);
                 hout[(size_t)t * N + n] = __builtin_bit_cast(uint16_t, h);
             } else {
-                yout[(size_t)t * N + n] = acc[0][j][i];
+#pragma unroll
+                for (int b = 0; b < NB; b++) part[(((size_t)z * NB + b) * T + t) * N + n] = acc[b][j][i];
             }
         }
+    }
+}
+
+// h[t][n] = bf16(SiLU(sum_z g_z) * sum_z u_z), slices added in order
+__global__ __launch_bounds__(256) void k_dense_silu_reduce(const float *__restrict__ part, int ks, size_t tn,
+                                                           uint16_t *__restrict__ h) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < tn; i += (size_t)gridDim.x * blockDim.x) {
+        float g = 0.f, u = 0.f;
+        for (int z = 0; z < ks; z++) {
+            g += part[(2 * (size_t)z) * tn + i];
+            u += part[(2 * (size_t)z + 1) * tn + i];
+        }
+        h[i] = __builtin_bit_cast(uint16_t, (__bf16)(g / (1.f + __expf(-g)) * u));
     }
 }
 
@@ -549,20 +591,56 @@ __global__ __launch_bounds__(256) void k_silu_mul(const float4 *__restrict__ gv,
     }
 }
 
-// out[t, c] = sum_j w[t, j] * y[inv[t*k+j], c] + ysh[t, c]
-__global__ __launch_bounds__(256) void k_grouped_combine(const float *__restrict__ y, const int32_t *__restrict__ inv,
-                                                         const float *__restrict__ w, int k, int H, int T,
-                                                         const float *__restrict__ ysh, float *__restrict__ out) {
-    const size_t n = (size_t)T * H;
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const size_t t = i / H, c = i % H;
-        float acc = 0.f;
-        for (int j = 0; j < k; j++) acc = fmaf(w[t * k + j], y[(size_t)inv[t * k + j] * H + c], acc);
-        if (ysh) acc += ysh[i];
-        out[i] = acc;
+// out[t, c] = sum_j w[t, j] * y[inv[t*k+j], c] + sum_z ysh[z, t, c], the
+// ranks and the shared expert's slices in order.  Workgroup row blockIdx.y takes tokens blockIdx.y + i * gridDim.y; a
+// thread takes V consecutive columns (V = 4 with 16-byte aligned rows).
+template <int V>
+__device__ __forceinline__ void load_v(const float *p, float (&v)[V]) {
+    if constexpr (V == 4) {
+        const float4 q = *(const float4 *)p;
+        v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; i++) v[i] = p[i];
     }
 }
 
+template <int V>
+__global__ __launch_bounds__(256) void k_grouped_combine(const float *__restrict__ y, const int32_t *__restrict__ inv,
+                                                         const float *__restrict__ w, int k, int H, int T,
+                                                         const float *__restrict__ ysh, int nsh,
+                                                         float *__restrict__ out) {
+    const int c = (blockIdx.x * blockDim.x + threadIdx.x) * V;
+    if (c >= H) return;
+    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        float acc[V] = {};
+        for (int j = 0; j < k; j++) {
+            const float wj = w[(size_t)t * k + j];
+            float v[V];
+            load_v<V>(y + (size_t)inv[(size_t)t * k + j] * H + c, v);
+#pragma unroll
+            for (int i = 0; i < V; i++) acc[i] = fmaf(wj, v[i], acc[i]);
+        }
+        if (nsh > 0) {
+            float sh[V] = {};
+            for (int z = 0; z < nsh; z++) {
+                float v[V];
+                load_v<V>(ysh + ((size_t)z * T + t) * H + c, v);
+#pragma unroll
+                for (int i = 0; i < V; i++) sh[i] += v[i];
+            }
+#pragma unroll
+            for (int i = 0; i < V; i++) acc[i] += sh[i];
+        }
+        float *o = out + (size_t)t * H + c;
+        if constexpr (V == 4) {
+            *(float4 *)o = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; i++) o[i] = acc[i];
+        }
+    }
+}
 
 }  // namespace
 
@@ -639,24 +717,49 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
     return hipGetLastError();
 }
 
+int dense_splits(int N, int T, int K) {
+    const int tiles = (N / kDnN) * ((T + kDnM - 1) / kDnM);
+    const int ks = (1024 + tiles - 1) / tiles;   // about four workgroups per CU
+    return std::max(1, std::min(ks, std::min(K / kDnK, 8)));
+}
+
+size_t dense_part_floats(int H, int I, int T) {
+    const int kg = dense_splits(I, T, H), kd = dense_splits(H, T, I);
+    return std::max(kg > 1 ? (size_t)kg * 2 * T * I : 0, (size_t)kd * T * H);
+}
+
 hipError_t launch_grouped_dense(const uint16_t *shared, int H, int I, int T, const uint16_t *xb, uint16_t *hs,
-                                float *ysh, hipStream_t s) {
+                                float *part, int *nsh, hipStream_t s) {
+    *nsh = 0;
     if (T <= 0) return hipSuccess;
     if (I % kDnN || H % kDnN || H % kDnK || I % kDnK) return hipErrorInvalidValue;
     const uint16_t *wg = shared, *wu = shared + (size_t)I * H, *wd = shared + 2 * (size_t)I * H;
     const int mt = (T + kDnM - 1) / kDnM;
-    k_dense_mm<true><<<dim3(I / kDnN, mt), 256, 0, s>>>(xb, wg, wu, T, I, H, hs, nullptr);
+    const int kg = dense_splits(I, T, H), kd = dense_splits(H, T, I);
+    k_dense_mm<true><<<dim3(I / kDnN, mt, kg), 256, 0, s>>>(xb, wg, wu, T, I, H, hs, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_dense_mm<false><<<dim3(H / kDnN, mt), 256, 0, s>>>(hs, wd, nullptr, T, H, I, nullptr, ysh);
+    if (kg > 1) {
+        const size_t tn = (size_t)T * I;
+        k_dense_silu_reduce<<<(int)std::min<size_t>((tn + 255) / 256, 4096), 256, 0, s>>>(part, kg, tn, hs);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // down partials (kd slices of [T, H]) are added by the combine
+    k_dense_mm<false><<<dim3(H / kDnN, mt, kd), 256, 0, s>>>(hs, wd, nullptr, T, H, I, nullptr, part);
+    *nsh = kd;
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_combine(const float *ybuf, const int32_t *inv, const float *w, int k, int H, int T,
-                                  const float *ysh, float *out, hipStream_t s) {
-    const size_t n = (size_t)T * H;
-    const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
-    k_grouped_combine<<<grid, 256, 0, s>>>(ybuf, inv, w, k, H, T, ysh, out);
+                                  const float *ysh, int nsh, float *out, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    const dim3 block(256);
+    const int rows = std::min(T, 65535);
+    // y and ysh rows are 16-byte aligned (workspace, H % 128 == 0); out is the caller's
+    if (H % 4 == 0 && (uintptr_t)out % 16 == 0)
+        k_grouped_combine<4><<<dim3((H / 4 + 255) / 256, rows), block, 0, s>>>(ybuf, inv, w, k, H, T, ysh, nsh, out);
+    else
+        k_grouped_combine<1><<<dim3((H + 255) / 256, rows), block, 0, s>>>(ybuf, inv, w, k, H, T, ysh, nsh, out);
     return hipGetLastError();
 }
 

@@ -119,7 +119,7 @@ GroupedWs carve_grouped(void *ws, int H, int I, int E, int k, int T, bool shared
     GroupedWs G;
     const size_t pairs = (size_t)T * k;
     G.z = c.take<float>((size_t)T * E);
-    G.zpart = c.take<float>((size_t)kRouteMaxSlices * T * E);
+    G.zpart = c.take<float>((size_t)route_blocked_slices(E, H, T) * T * E);
     G.idx = c.take<int32_t>(pairs);
     G.w = c.take<float>(pairs);
     G.perm = c.take<int32_t>(pairs);
@@ -130,7 +130,7 @@ GroupedWs carve_grouped(void *ws, int H, int I, int E, int k, int T, bool shared
     G.hbuf = c.take<uint16_t>(pairs * I);
     G.ybuf = c.take<float>(pairs * std::max(H, 2 * I));   // y, or gate and up before it
     G.hs = shared ? c.take<uint16_t>((size_t)T * I) : nullptr;
-    G.ysh = shared ? c.take<float>((size_t)T * H) : nullptr;
+    G.ysh = shared ? c.take<float>(dense_part_floats(H, I, T)) : nullptr;   // shared expert's partial sums
     G.bytes = (size_t)align_up((int64_t)c.pos, 256);
     return G;
 }
@@ -943,10 +943,11 @@ int moe_layer_forward_grouped(const moe_layer *L, const void *x, int32_t x_dtype
     HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, T, idx, w, s), "top-k");
     HIPCHK(launch_group(idx, T * k, E, W.perm, W.inv, W.counts, W.offsets, s), "group");
     HIPCHK(launch_to_bf16(x, x_dtype, (size_t)T * H, W.xb, s), "x to bf16");
-    if (L->shared) HIPCHK(launch_grouped_dense(L->shared, H, I, T, W.xb, W.hs, W.ysh, s), "shared expert");
+    int nsh = 0;
+    if (L->shared) HIPCHK(launch_grouped_dense(L->shared, H, I, T, W.xb, W.hs, W.ysh, &nsh, s), "shared expert");
     HIPCHK(launch_grouped_rvq(L->records, offsets_of(H, I), E, H, I, T * k, W.counts, W.offsets, W.perm, k, W.xb, W.hbuf,
                               W.ybuf, s), "grouped RVQ GEMMs");
-    HIPCHK(launch_grouped_combine(W.ybuf, W.inv, w, k, H, T, L->shared ? W.ysh : nullptr, out, s), "combine");
+    HIPCHK(launch_grouped_combine(W.ybuf, W.inv, w, k, H, T, W.ysh, nsh, out, s), "combine");
     return MOE_OK;
 }
 

@@ -57,7 +57,7 @@ hipError_t launch_topk(const float *z, int E, int k, int score_fn, int T, int32_
                        hipStream_t s);
 // Many-token router logits: H-sliced partial sums (part: route_blocked_slices
 // x T x E floats) reduced in slice order into z.  H % 64 == 0.
-constexpr int kRouteMaxSlices = 16;
+constexpr int kRouteMaxSlices = 64;
 int route_blocked_slices(int E, int H, int T);
 hipError_t launch_route_blocked(const float *W, const float *bias, int E, int H, const void *x, int x_dtype, int T,
                                 float *part, float *z, hipStream_t s);
@@ -164,9 +164,15 @@ hipError_t launch_to_bf16(const void *x, int x_dtype, size_t n, uint16_t *xb, hi
 hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, int E, int H, int I, int n_pairs,
                               const int32_t *counts, const int32_t *offsets, const int32_t *perm, int k,
                               const uint16_t *xb, uint16_t *hbuf, float *ybuf, hipStream_t s);
+// Shared expert over all T tokens (dense bf16 GEMMs, K split into slices when
+// few tokens leave the CUs idle): part holds dense_part_floats(H, I, T)
+// floats; the down GEMM's *nsh slices of [T, H] partial sums stay in part for
+// the combine to add.
+int dense_splits(int N, int T, int K);
+size_t dense_part_floats(int H, int I, int T);
 hipError_t launch_grouped_dense(const uint16_t *shared, int H, int I, int T, const uint16_t *xb, uint16_t *hs,
-                                float *ysh, hipStream_t s);
+                                float *part, int *nsh, hipStream_t s);
 hipError_t launch_grouped_combine(const float *ybuf, const int32_t *inv, const float *w, int k, int H, int T,
-                                  const float *ysh, float *out, hipStream_t s);
+                                  const float *ysh, int nsh, float *out, hipStream_t s);
 
 }  // namespace moe

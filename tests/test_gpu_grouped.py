@@ -72,3 +72,12 @@ def test_grouped_full_batched_layer(moe):
     # the full 256-token, 384-expert layer; every token is checked on its own
     cfg = synth.CONFIGS["batched"]
     _check(moe, cfg)
+
+
+def test_grouped_many_pairs(moe):
+    # 1600 tokens x top-8 = 12,800 (token, rank) pairs: more than the grouping
+    # kernel sorts in LDS, so its segments are sorted in global memory; ~200
+    # tokens per expert (13 passes of 16)
+    cfg = synth.get_config("batched", tokens=1600, E=64, k=8, H=512, I=256, shared=True)
+    counts = _check(moe, cfg, sample=list(range(0, 1600, 7)) + [1599])
+    assert counts.sum() == 12800
