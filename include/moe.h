@@ -280,10 +280,11 @@ size_t moe_grouped_workspace_bytes(const moe_layer *L, int32_t T);
 
 /* Batched layer (many tokens, WASTE "실무자에게 남는 질문은 ...": one image
  * is 256 prompt positions, each through every MoE layer): route all tokens,
- * group (token, rank) pairs per expert, then a bf16-input grouped GEMM on
- * matrix cores with fp32 accumulation, weights dequantised from the RVQ
- * codes into LDS tiles, SiLU * up, down GEMM, fixed-order combine plus the
- * shared expert.  x [dev] [T, H] bf16 (MOE_DTYPE_BF16) or fp32; out [T, H] fp32.
+ * group (token, rank) pairs per expert, then per expert and matrix a
+ * bf16-input GEMM on matrix cores with fp32 accumulation whose weight
+ * operand is the codebook rows the RVQ codes pick (the codebook in LDS, no
+ * dequantised matrix), SiLU(gate) * up, the down GEMM, and a fixed-order
+ * combine plus the shared expert.  x [dev] [T, H] bf16 (MOE_DTYPE_BF16) or fp32; out [T, H] fp32.
  * Accuracy: relative L2 <= 1e-2 against an fp64 evaluation. */
 int moe_layer_forward_grouped(const moe_layer *L, const void *x, int32_t x_dtype,
                               int32_t T, float *out, int32_t *idx_out, float *w_out,
