@@ -111,7 +111,13 @@ class HostRecordPool:
     """Expert records of several layers in host memory (the cold tier of
     streamed decode): page-locked chunks of at most ``chunk_bytes`` up to
     ``pin_limit`` bytes in total, the remainder (if any) in pageable memory.
-    ``pinned_records`` says how many records are page-locked."""
+    ``pinned_records`` says how many records are page-locked.  Records are
+    laid out expert-major (expert e of every layer, then e + 1), so a pin
+    budget below the whole pool leaves every layer the same share of
+    page-locked records (expert ids carry no popularity order): each layer's
+    misses then mostly include page-locked ones, whose transfers run while
+    the host stages the pageable ones.  Layer-major order would leave whole
+    layers pageable, whose first miss waits for its staging."""
 
     def __init__(self, cfg: synth.MoEConfig, layers: Sequence[int], experts: Optional[int] = None,
                  chunk_bytes: int = 4 << 30, pin_limit: int = 52 << 30):
@@ -120,7 +126,7 @@ class HostRecordPool:
         self.stride = wl.layout.padded
         E = cfg.E if experts is None else experts
         per_chunk = max(1, chunk_bytes // self.stride)
-        keys = [(L, e) for L in layers for e in range(E)]
+        keys = [(L, e) for e in range(E) for L in layers]
         self.chunks: List = []
         self.addr = {}
         self.pinned_records = 0
