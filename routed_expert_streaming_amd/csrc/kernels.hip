@@ -178,7 +178,9 @@ __global__ __launch_bounds__(256) void k_route_reduce(const float *__restrict__ 
 // eighths of the experts first (whole 32-key blocks); the keys of local rank
 // below k (every global top-k key is one) are then ranked among themselves.
 // Weights: softmax over the selected logits, or sigmoid scores renormalised,
-// summed in rank order.
+// summed in rank order.  With idx_host / w_host (page-locked host memory) the
+// kernel also writes the ids and weights there, visible to the host once the
+// kernel has completed (no separate device-to-host copy).
 constexpr int kTopkThreads = 256, kTopkLvl = 8;
 __device__ __forceinline__ uint32_t topk_order_key(float f) {
     f = f == f ? f : -INFINITY;
@@ -191,7 +193,8 @@ __device__ __forceinline__ float topk_key_value(uint32_t k) {
 }
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__ z, int E, int k, int score_fn,
-                                                       int32_t *__restrict__ idx, float *__restrict__ w) {
+                                                       int32_t *__restrict__ idx, float *__restrict__ w,
+                                                       int32_t *__restrict__ idx_host, float *__restrict__ w_host) {
     __shared__ __align__(16) uint64_t key[MOE_MAX_E];              // padded to a multiple of 32 with zeros
     __shared__ __align__(16) uint64_t cand[kTopkLvl * MOE_MAX_K];  // zeros past the candidates
     __shared__ int sidx[MOE_MAX_K];
@@ -251,6 +254,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
         }
         idx[(size_t)t * k + threadIdx.x] = sidx[threadIdx.x];
         w[(size_t)t * k + threadIdx.x] = mine / sum;
+        if (idx_host) idx_host[(size_t)t * k + threadIdx.x] = sidx[threadIdx.x];
+        if (w_host) w_host[(size_t)t * k + threadIdx.x] = mine / sum;
     }
 }
 
@@ -585,8 +590,8 @@ hipError_t launch_route_blocked(const float *W, const float *bias, int E, int H,
 }
 
 hipError_t launch_topk(const float *z, int E, int k, int score_fn, int T, int32_t *idx, float *w,
-                       hipStream_t s) {
-    k_topk<<<T, kTopkThreads, 0, s>>>(z, E, k, score_fn, idx, w);
+                       hipStream_t s, int32_t *idx_host, float *w_host) {
+    k_topk<<<T, kTopkThreads, 0, s>>>(z, E, k, score_fn, idx, w, idx_host, w_host);
     return hipGetLastError();
 }
 

@@ -586,17 +586,15 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     // route; the host waits only for the expert ids, while the work that does
     // not depend on the choice (x packing, the shared expert) runs on
     HIPCHK(launch_route_logits(L->router.weight, L->router.bias, E, H, x, MOE_DTYPE_F32, 1, W.z, cs), "route logits");
-    HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, 1, idx, W.w, cs), "top-k");
-    HIPCHK(hipMemcpyAsync(c->h_idx, idx, k * sizeof(int32_t), hipMemcpyDeviceToHost, cs), "idx to host");
-    HIPCHK(hipEventRecord(c->idx_ev, cs), "ids copied");
+    HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, 1, idx, W.w, cs, c->h_idx), "top-k");   // ids to the host too
+    HIPCHK(hipEventRecord(c->idx_ev, cs), "ids written");
     if (ah.L) {
         // the next layer's router on this layer's input: a prediction only
         HIPCHK(launch_route_logits(ah.L->router.weight, ah.L->router.bias, ah.L->router.E, H, x, MOE_DTYPE_F32, 1, za,
                                    cs), "look-ahead logits");
-        HIPCHK(launch_topk(za, ah.L->router.E, ah.k, ah.L->router.score_fn, 1, ia, wa, cs), "look-ahead top-k");
-        HIPCHK(hipMemcpyAsync(h_ahead, ia, ah.k * sizeof(int32_t), hipMemcpyDeviceToHost, cs), "look-ahead ids");
-        HIPCHK(hipMemcpyAsync(h_ahead_w, wa, ah.k * sizeof(float), hipMemcpyDeviceToHost, cs), "look-ahead weights");
-        HIPCHK(hipEventRecord(c->ahead_ev, cs), "look-ahead ids copied");
+        HIPCHK(launch_topk(za, ah.L->router.E, ah.k, ah.L->router.score_fn, 1, ia, wa, cs, h_ahead, h_ahead_w),
+               "look-ahead top-k");
+        HIPCHK(hipEventRecord(c->ahead_ev, cs), "look-ahead ids written");
     }
     HIPCHK(launch_pack_x(x, MOE_DTYPE_F32, 1, H, H, W.xh, W.xexp, cs), "pack_x");
     if (L->shared) {
