@@ -364,12 +364,14 @@ size_t moe_streamed_workspace_bytes(const moe_layer *L, int32_t T);
 /* One layer fed from the cache (WISP "더블 버퍼 비동기 파이프라인"; WASTE
  * "병목은 ...": reads overlap arithmetic; WARP "WARP의 캐시 설정에서 드러나는
  * 역설": refuse to run below the floor).  T must be 1 (decode).  Routes on
- * compute_stream, copies the k expert ids to the host (one sync), looks the
- * keys layer_id * E + e up in ascending expert id, inserts each miss
- * (copy on copy_stream from experts_host[e]), runs the hit experts at once
- * and each miss expert after its copy lands, then combines in fixed rank
- * order with the shared expert.  Output equals moe_layer_forward's bit for
- * bit.  MOE_E_INVAL if the cache capacity is below k or its slot size below
+ * compute_stream (the top-k kernel writes the k expert ids to page-locked
+ * host memory; one sync), looks the keys layer_id * E + e up in ascending
+ * expert id, inserts each miss (copied from experts_host[e], alternately on
+ * copy_stream and on a second copy stream the cache owns; copy_stream then
+ * waits for the second, so it completes after every copy of the call), runs
+ * the hit experts at once and each miss expert after its copy lands, then
+ * combines in fixed rank order with the shared expert.  Output equals
+ * moe_layer_forward's bit for bit.  MOE_E_INVAL if the cache capacity is below k or its slot size below
  * the record size.
  *   experts_host [host] array of E [pinned] record pointers
  *   x [dev] [1, H] fp32;  out [dev] [1, H] fp32;  idx_out [dev] [1, k] or NULL */

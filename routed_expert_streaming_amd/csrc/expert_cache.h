@@ -40,7 +40,7 @@ struct moe_cache {
     moe::LruCore core;
     char *pool = nullptr;                 // caller-owned device pool
     uint64_t slot_bytes = 0;
-    std::vector<hipEvent_t> ready;        // recorded on the copy stream after a slot's copy
+    std::vector<hipEvent_t> ready;        // recorded on a copy stream after a slot's copy
     std::vector<uint8_t> filled;          // slot has had a copy enqueued
     // Readers' events: one event is recorded on a compute stream after the
     // readers of a whole batch of slots (one release call), and every slot of
@@ -53,13 +53,20 @@ struct moe_cache {
     std::vector<int32_t> slot_use;        // per slot: its readers' event, or -1
     int32_t *h_idx = nullptr;             // pinned staging: the router's expert ids, the look-ahead ids and
                                           // (bits of) the look-ahead weights, MOE_MAX_K each
-    hipEvent_t idx_ev = nullptr;          // recorded after the ids' copy to h_idx
-    hipEvent_t ahead_ev = nullptr;        // recorded after the look-ahead ids' copy
+    hipEvent_t idx_ev = nullptr;          // recorded after the top-k that writes the ids to h_idx
+    hipEvent_t ahead_ev = nullptr;        // recorded after the look-ahead top-k
+    // A second copy stream of the cache's own: a streamed layer alternates its
+    // misses' copies between the caller's copy stream and this one, so that
+    // one copy's start-up overlaps the other's transfer; the caller's copy
+    // stream then waits for this one (ps2_done), so it still completes after
+    // every copy of the call.
+    hipStream_t ps2 = nullptr;
+    hipEvent_t ps2_done = nullptr;
     int device = 0;
     // records in pageable host memory go through pinned bounce buffers
     // (allocated on first use) filled by host threads
     char *bounce[moe::kBounce] = {};
-    hipEvent_t bounce_done[moe::kBounce] = {};   // recorded on the copy stream after the buffer's copy
+    hipEvent_t bounce_done[moe::kBounce] = {};   // recorded on a copy stream after the buffer's copy
     bool bounce_used[moe::kBounce] = {};
     int bounce_next = 0;
     moe::CopyPool *copier = nullptr;

@@ -81,6 +81,7 @@ using namespace moe;
 
 namespace {
 void destroy_events(moe_cache *c) {
+    if (c->ps2) (void)hipStreamSynchronize(c->ps2);   // its copies record the events below
     for (hipEvent_t e : c->ready)
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->use_ev)
@@ -92,6 +93,10 @@ void destroy_events(moe_cache *c) {
     if (c->idx_ev) (void)hipEventDestroy(c->idx_ev);
     if (c->ahead_ev) (void)hipEventDestroy(c->ahead_ev);
     c->idx_ev = c->ahead_ev = nullptr;
+    if (c->ps2) (void)hipStreamDestroy(c->ps2);
+    if (c->ps2_done) (void)hipEventDestroy(c->ps2_done);
+    c->ps2 = nullptr;
+    c->ps2_done = nullptr;
     for (int b = 0; b < moe::kBounce; b++) {
         if (c->bounce_used[b]) (void)hipEventSynchronize(c->bounce_done[b]);
         if (c->bounce_done[b]) (void)hipEventDestroy(c->bounce_done[b]);
@@ -225,6 +230,8 @@ int expert_cache_create(int32_t capacity, uint64_t slot_bytes, void *pool_dev, m
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_idx, 3 * MOE_MAX_K * sizeof(int32_t), hipHostMallocDefault);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->idx_ev, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ahead_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->ps2, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ps2_done, hipEventDisableTiming);
     if (e != hipSuccess) {
         destroy_events(c);
         delete c;

@@ -688,17 +688,19 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
             if (locked && pass == 0) nlocked++;
         }
     const char *src_of[MOE_MAX_K] = {};
-    // a miss's copy into its slot, after the slot's previous readers (and,
-    // with an exclusive host tier, after the slot's old record has been
-    // copied down to its page)
-    auto copy_miss = [&](int j) -> int {
+    // an event not yet complete: stream st waits for it
+    auto after = [&](hipStream_t st, hipEvent_t ev) {
+        hipError_t q = hipEventQuery(ev);
+        return q == hipErrorNotReady ? hipStreamWaitEvent(st, ev, 0) : q;
+    };
+    // a miss's copy into its slot on copy stream ps (or the cache's second
+    // one), after the slot's previous copy (which may have been on the other
+    // stream) and readers (and, with an exclusive host tier, after the slot's
+    // old record has been copied down to its page)
+    auto copy_miss = [&](int j, hipStream_t ps) -> int {
         const int32_t s = slot_of[j];
+        HIPCHK(after(ps, c->ready[s]), "copy waits for the slot's previous copy");
         HIPCHK(cache_wait_readers(c, s, ps), "copy waits for slot readers");
-        // an event not yet complete: stream st waits for it
-        auto after = [&](hipStream_t st, hipEvent_t ev) {
-            hipError_t q = hipEventQuery(ev);
-            return q == hipErrorNotReady ? hipStreamWaitEvent(st, ev, 0) : q;
-        };
         if (vpage[j] >= 0) {
             // the evicted record goes down on the tier's own stream (the link
             // carries it while the copy stream moves records up), after the
@@ -772,15 +774,22 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     };
     if (!tier.t) {
         // page-locked misses' copies first (the copy engine starts at once),
-        // then the hit experts, then the misses' experts
+        // then the hit experts, then the misses' experts.  The copies
+        // alternate between the two copy streams; the caller's then waits for
+        // the cache's own.
+        auto copy_ps = [&](int n) { return n % 2 ? c->ps2 : ps; };
         for (int n = 0; n < nlocked; n++)
-            if ((rc = copy_miss(morder[n]))) return rc;
+            if ((rc = copy_miss(morder[n], copy_ps(n)))) return rc;
         if ((rc = run_hits())) return rc;
         for (int n = 0; n < nlocked; n++)
             if ((rc = run_miss(morder[n]))) return rc;
         for (int n = nlocked; n < nmiss; n++) {
-            if ((rc = copy_miss(morder[n]))) return rc;
+            if ((rc = copy_miss(morder[n], copy_ps(n)))) return rc;
             if ((rc = run_miss(morder[n]))) return rc;
+        }
+        if (nmiss > 1) {
+            HIPCHK(hipEventRecord(c->ps2_done, c->ps2), "second copy stream done");
+            HIPCHK(hipStreamWaitEvent(ps, c->ps2_done, 0), "copy stream waits for the second");
         }
     } else if (X) {
         // exclusive host tier: the hit experts run while the records found in
@@ -806,7 +815,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         }
         for (int n = 0; n < nmiss; n++) src_of[morder[n]] = tier_page(X, spage[morder[n]]);
         for (int n = 0; n < nmiss; n++) {
-            if ((rc = copy_miss(morder[n]))) return rc;
+            if ((rc = copy_miss(morder[n], ps))) return rc;
             if ((rc = run_miss(morder[n]))) return rc;
         }
     } else {
@@ -823,7 +832,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         }
         for (int n = 0; n < nmiss; n++) src_of[morder[n]] = ptrs[n];
         for (int n = 0; n < nmiss; n++) {
-            if ((rc = copy_miss(morder[n]))) return rc;
+            if ((rc = copy_miss(morder[n], ps))) return rc;
             if ((rc = run_miss(morder[n]))) return rc;
         }
     }
