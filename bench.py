@@ -27,26 +27,33 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per decode launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-# (each scaled by the same counter on a 1 GiB device copy; the runs and the
-# factors are in profiles/k_decode_persistent_<workload>_hbm_counters.txt),
-# valid for the kernel source they were taken on: reported as null once that
-# source has changed.
-DECODE_TRAFFIC = {"kernel_source": "routed_expert_streaming_amd/csrc/kernels_decode.hip",
-                  "sha256_prefix": "fab0db0257a2ef41",
-                  "bytes_per_launch": {"mixtral": 5057644555, "kimi_linear": 1235807045}}
+# HBM bytes per launch (decode) or per layer call (batched: every kernel of the
+# call) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (each scaled by the same
+# counter on a 1 GiB device copy; the runs and the factors are in
+# profiles/k_decode_persistent_<workload>_hbm_counters.txt and
+# profiles/k_grouped_rvq_batched_counters.txt), valid for the kernel sources
+# they were taken on: reported as null once any of them has changed.
+TRAFFIC = {
+    "decode": {"sources": {"routed_expert_streaming_amd/csrc/kernels_decode.hip": "fab0db0257a2ef41"},
+               "bytes": {"mixtral": 5057644555, "kimi_linear": 1235807045}},
+    "batched": {"sources": {"routed_expert_streaming_amd/csrc/kernels_grouped.hip": "613c8e21cf66bf46",
+                            "routed_expert_streaming_amd/csrc/kernels.hip": "e982d601c873d008"},
+                "bytes": {"batched": 5475616797}},
+}
 
 
-def measured_traffic(workload: str):
+def measured_traffic(kind: str, workload: str):
     import hashlib
-    try:
-        with open(os.path.join(ROOT, DECODE_TRAFFIC["kernel_source"]), "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
-    except OSError:
-        return None
-    if not digest.startswith(DECODE_TRAFFIC["sha256_prefix"]):
-        return None
-    return DECODE_TRAFFIC["bytes_per_launch"].get(workload)
+    entry = TRAFFIC[kind]
+    for path, prefix in entry["sources"].items():
+        try:
+            with open(os.path.join(ROOT, path), "rb") as f:
+                digest = hashlib.sha256(f.read()).hexdigest()
+        except OSError:
+            return None
+        if not digest.startswith(prefix):
+            return None
+    return entry["bytes"].get(workload)
 
 
 def log(msg: str) -> None:
@@ -291,7 +298,7 @@ def main() -> int:
         "tok_s_blocks": block_rates(step_ms, 1.0),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(cfg.name),
+                     "traffic": measured_traffic("decode", cfg.name),
                      "kernel": "k_decode_persistent (route, top-k, RVQ gate/up by %s, RVQ down by %s, combine; "
                                "all layers of one token per launch)" % tuple(
                                    "table lookup" if m == "lookup" else "codebook gathers"
@@ -365,7 +372,8 @@ def bench_batched(args, cfg) -> int:
            "data": "synthetic", "config": {"workload": f"batched layer: T {cfg.tokens}, H {cfg.H}, I {cfg.I}, "
                                                         f"{cfg.E} experts, top-{cfg.k} + shared"},
            "roofline": {"bound": "hbm", "achieved": round(nbytes / mean_s / 1e9, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(nbytes / mean_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                        "unit": "GB/s", "frac": round(nbytes / mean_s / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic("batched", cfg.name),
                         "kernel": "batched layer call", "algorithmic_bytes_per_launch": nbytes},
            "mfma": {"flops_per_call": flops, "achieved_tflops": round(flops / mean_s / 1e12, 2),
                     "peak_tflops": 2500.0, "utilisation": round(flops / mean_s / 1e12 / 2500.0, 4)},
