@@ -739,20 +739,25 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         c->filled[s] = 1;
         return MOE_OK;
     };
-    // a miss's expert, once its copy has landed
-    auto run_miss = [&](int j) -> int {
-        const int32_t s = slot_of[j];
-        int r = cache_wait(c, s, cs);
-        if (r) return r;
-        RecSrc one{};
-        one.k = k;
-        one.n_local = 1;
-        one.list[0] = c->pool + (size_t)s * c->slot_bytes;
-        one.rank[0] = (uint8_t)j;
-        HIPCHK(launch_rvq_gateup(one, off, H, I, 1, W.xh, W.xexp, W.hh, cs), "rvq gate/up (miss)");
-        HIPCHK(launch_rvq_down(one, off, H, I, 1, KS, W.hh, W.ypart, cs), "rvq down (miss)");
+    // misses' experts js[0..nj), once their copies have landed, in one launch
+    // each for gate/up and down (an expert's result does not depend on which
+    // others share the launch)
+    auto run_misses = [&](const int *js, int nj) -> int {
+        RecSrc src{};
+        src.k = k;
+        src.n_local = nj;
+        for (int q = 0; q < nj; q++) {
+            const int32_t s = slot_of[js[q]];
+            int r = cache_wait(c, s, cs);
+            if (r) return r;
+            src.list[q] = c->pool + (size_t)s * c->slot_bytes;
+            src.rank[q] = (uint8_t)js[q];
+        }
+        HIPCHK(launch_rvq_gateup(src, off, H, I, nj, W.xh, W.xexp, W.hh, cs), "rvq gate/up (misses)");
+        HIPCHK(launch_rvq_down(src, off, H, I, nj, KS, W.hh, W.ypart, cs), "rvq down (misses)");
         return MOE_OK;
     };
+    auto run_miss = [&](int j) { return run_misses(&j, 1); };
     // the hit experts, all at once
     auto run_hits = [&]() -> int {
         RecSrc hits{};
@@ -775,17 +780,20 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     if (!tier.t) {
         // page-locked misses' copies first (the copy engine starts at once),
         // then the hit experts, then the misses' experts.  The copies
-        // alternate between the two copy streams; the caller's then waits for
-        // the cache's own.
+        // alternate between the two copy streams (the caller's then waits for
+        // the cache's own), so consecutive misses n, n+1 land together: their
+        // experts run as one pair.
         auto copy_ps = [&](int n) { return n % 2 ? c->ps2 : ps; };
         for (int n = 0; n < nlocked; n++)
             if ((rc = copy_miss(morder[n], copy_ps(n)))) return rc;
         if ((rc = run_hits())) return rc;
-        for (int n = 0; n < nlocked; n++)
-            if ((rc = run_miss(morder[n]))) return rc;
-        for (int n = nlocked; n < nmiss; n++) {
-            if ((rc = copy_miss(morder[n], copy_ps(n)))) return rc;
-            if ((rc = run_miss(morder[n]))) return rc;
+        for (int n = 0; n < nlocked; n += 2)
+            if ((rc = run_misses(morder + n, std::min(2, nlocked - n)))) return rc;
+        for (int n = nlocked; n < nmiss; n += 2) {
+            const int nj = std::min(2, nmiss - n);
+            for (int q = 0; q < nj; q++)
+                if ((rc = copy_miss(morder[n + q], copy_ps(n + q)))) return rc;
+            if ((rc = run_misses(morder + n, nj))) return rc;
         }
         if (nmiss > 1) {
             HIPCHK(hipEventRecord(c->ps2_done, c->ps2), "second copy stream done");
