@@ -284,88 +284,72 @@ __global__ __launch_bounds__(256) void k_pack_x(const void *__restrict__ x, int 
 }
 
 // ------------------------------------------------------------- RVQ GEMVs
-// Gate/up: one workgroup per (item, 64-row tile); both codebooks staged in
-// LDS (128 KiB); lane = row, waves split the 128-column chunks; the input's
-// fp16 pairs are wave-uniform (scalar loads).  Output: fp32 SiLU(g) * u.
+// Gate/up: one workgroup per (item, 64-row tile, matrix): gate and up are
+// separate workgroups, each with its matrix's codebook staged in LDS (64 KiB,
+// so two workgroups share a CU); lane = row, waves split the 128-column
+// chunks; the input's fp16 pairs are wave-uniform (scalar loads).  Output:
+// the scaled fp32 gate and up, gu[item][0][r] and gu[item][1][r]; the down
+// kernel forms SiLU(g) * u from them.
 constexpr int kGuWaves = 8;
 
 __global__ __launch_bounds__(kGuWaves * 64) void k_rvq_gateup(RecSrc src, RecOffsets off, int H, int I,
                                                               const uint32_t *__restrict__ xh,
                                                               const int32_t *__restrict__ xexp,
-                                                              float *__restrict__ hh) {
+                                                              float *__restrict__ gu) {
     extern __shared__ __align__(16) char lds[];
-    char *cbg = lds, *cbu = lds + kCbRows * 16;
-    float *red = (float *)(lds + 2 * kCbRows * 16);      // [kGuWaves][2][64]
+    char *cb = lds;
+    float *red = (float *)(lds + kCbRows * 16);      // [kGuWaves][64]
     const int tiles = I / kTileRows;
-    const int local = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int mat = blockIdx.x & 1, tile = (blockIdx.x >> 1) % tiles, local = (blockIdx.x >> 1) / tiles;
     int item;
     const uint8_t *rec = resolve_record(src, local, item);
     const int t = item / src.k;
     {
-        const u32x4 *g = (const u32x4 *)(rec + off.cb[0]);
-        const u32x4 *u = (const u32x4 *)(rec + off.cb[1]);
-        for (int i = threadIdx.x; i < kCbRows; i += kGuWaves * 64) {
-            ((u32x4 *)cbg)[i] = g[i];
-            ((u32x4 *)cbu)[i] = u[i];
-        }
+        const u32x4 *g = (const u32x4 *)(rec + off.cb[mat]);
+        for (int i = threadIdx.x; i < kCbRows; i += kGuWaves * 64) ((u32x4 *)cb)[i] = g[i];
     }
     __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int cpr = H / kChunkCols;
-    const u32x4 *gcodes = (const u32x4 *)(rec + off.codes[0]) + (size_t)tile * cpr * kTileVec;
-    const u32x4 *ucodes = (const u32x4 *)(rec + off.codes[1]) + (size_t)tile * cpr * kTileVec;
+    const u32x4 *codes = (const u32x4 *)(rec + off.codes[mat]) + (size_t)tile * cpr * kTileVec;
     const uint32_t *x = xh + (size_t)t * (H / 2);
-    float ag[4] = {0.f, 0.f, 0.f, 0.f}, au[4] = {0.f, 0.f, 0.f, 0.f};
+    float ag[4] = {0.f, 0.f, 0.f, 0.f};
     int c = wave;
-    uint32_t dg[12], du[12];
-    if (c < cpr) {
-        load_strip(gcodes + (size_t)c * kTileVec, lane, dg);
-        load_strip(ucodes + (size_t)c * kTileVec, lane, du);
-    }
+    uint32_t dg[12];
+    if (c < cpr) load_strip(codes + (size_t)c * kTileVec, lane, dg);
     while (c < cpr) {
         const int cn = c + kGuWaves;
-        uint32_t ng[12], nu[12];
-        if (cn < cpr) {
-            load_strip(gcodes + (size_t)cn * kTileVec, lane, ng);
-            load_strip(ucodes + (size_t)cn * kTileVec, lane, nu);
-        }
-        const uint32_t *xp = x + c * 64;
-        strip_dot<0>(dg, cbg, xp, ag);
-        strip_dot<0>(du, cbu, xp, au);
+        uint32_t ng[12];
+        if (cn < cpr) load_strip(codes + (size_t)cn * kTileVec, lane, ng);
+        strip_dot<0>(dg, cb, x + c * 64, ag);
         if (cn < cpr) {
 #pragma unroll
-            for (int i = 0; i < 12; i++) { dg[i] = ng[i]; du[i] = nu[i]; }
+            for (int i = 0; i < 12; i++) dg[i] = ng[i];
         }
         c = cn;
     }
-    red[(wave * 2 + 0) * 64 + lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
-    red[(wave * 2 + 1) * 64 + lane] = (au[0] + au[1]) + (au[2] + au[3]);
+    red[wave * 64 + lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
     __syncthreads();
     if (wave == 0) {
-        float g = 0.f, u = 0.f;
+        float g = 0.f;
 #pragma unroll
-        for (int wv = 0; wv < kGuWaves; wv++) {
-            g += red[(wv * 2 + 0) * 64 + lane];
-            u += red[(wv * 2 + 1) * 64 + lane];
-        }
+        for (int wv = 0; wv < kGuWaves; wv++) g += red[wv * 64 + lane];
         const int r = tile * kTileRows + lane;
-        const _Float16 sg = ((const _Float16 *)(rec + off.scales[0]))[r];
-        const _Float16 su = ((const _Float16 *)(rec + off.scales[1]))[r];
-        const int xe = xexp[t];
-        g = ldexpf(g, xe) * (float)sg;
-        u = ldexpf(u, xe) * (float)su;
-        hh[(size_t)item * I + r] = g / (1.f + __expf(-g)) * u;
+        const _Float16 sg = ((const _Float16 *)(rec + off.scales[mat]))[r];
+        gu[((size_t)item * 2 + mat) * I + r] = ldexpf(g, xexp[t]) * (float)sg;
     }
 }
 
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + __expf(-g)) * u; }
+
 // Down: one workgroup per (item, 64-row tile of H, K-slice); down codebook in
-// LDS (64 KiB), then the slice's h (fp32) as fp16 pairs scaled by 2^-e (e
-// from the slice's largest |h|, range_exp); writes s_d[r] * 2^e * partial dot
-// into ypart[item][ks][r].
+// LDS (64 KiB), then the slice's h = SiLU(g) * u (fp32, from the gate/up
+// outputs) as fp16 pairs scaled by 2^-e (e from the slice's largest |h|,
+// range_exp); writes s_d[r] * 2^e * partial dot into ypart[item][ks][r].
 constexpr int kDnWaves = 4;
 
 __global__ __launch_bounds__(kDnWaves * 64) void k_rvq_down(RecSrc src, RecOffsets off, int H, int I, int KS,
-                                                            const float *__restrict__ hh,
+                                                            const float *__restrict__ gu,
                                                             float *__restrict__ ypart) {
     extern __shared__ __align__(16) char lds[];
     char *cbd = lds;
@@ -381,7 +365,7 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_rvq_down(RecSrc src, RecOffse
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int cpr = I / kChunkCols;
     const int c0 = (int)((int64_t)cpr * ks / KS), c1 = (int)((int64_t)cpr * (ks + 1) / KS);
-    const float *h = hh + (size_t)item * I + c0 * kChunkCols;
+    const float *hg = gu + (size_t)item * 2 * I + c0 * kChunkCols, *hu = hg + I;
     const int np = (c1 - c0) * kChunkCols / 2;
     const u32x4 *codes = (const u32x4 *)(rec + off.codes[2]) + (size_t)tile * cpr * kTileVec;
     int c = c0 + wave;
@@ -392,8 +376,8 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_rvq_down(RecSrc src, RecOffse
         const u32x4 *cbsrc = (const u32x4 *)(rec + off.cb[2]);
         for (int i = threadIdx.x; i < kCbRows; i += kDnWaves * 64) ((u32x4 *)cbd)[i] = cbsrc[i];
         for (int p = threadIdx.x; p < np; p += kDnWaves * 64) {
-            const float2 v = *(const float2 *)(h + 2 * p);
-            m = fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y)));
+            const float2 g = *(const float2 *)(hg + 2 * p), u = *(const float2 *)(hu + 2 * p);
+            m = fmaxf(m, fmaxf(fabsf(silu_mul(g.x, u.x)), fabsf(silu_mul(g.y, u.y))));
         }
         m = wave_max(m);
         if (lane == 0) wm[wave] = m;
@@ -401,8 +385,8 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_rvq_down(RecSrc src, RecOffse
     __syncthreads();
     const int e = range_exp(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])));
     for (int p = threadIdx.x; p < np; p += kDnWaves * 64) {
-        const float2 v = *(const float2 *)(h + 2 * p);
-        xl[p] = pack_f16x2(ldexpf(v.x, -e), ldexpf(v.y, -e));
+        const float2 g = *(const float2 *)(hg + 2 * p), u = *(const float2 *)(hu + 2 * p);
+        xl[p] = pack_f16x2(ldexpf(silu_mul(g.x, u.x), -e), ldexpf(silu_mul(g.y, u.y), -e));
     }
     __syncthreads();
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -548,7 +532,7 @@ __global__ __launch_bounds__(256) void k_dense_down(const uint16_t *__restrict__
     }
 }
 
-size_t gateup_lds() { return 2 * kCbRows * 16 + kGuWaves * 2 * 64 * sizeof(float); }
+size_t gateup_lds() { return kCbRows * 16 + kGuWaves * 64 * sizeof(float); }
 // codebook, wave sums, wave maxima, and the largest K-slice's h pairs
 size_t down_lds(int I, int KS) {
     const int cpr = I / kChunkCols;
@@ -603,7 +587,7 @@ hipError_t launch_pack_x(const void *x, int x_dtype, int T, int H, int64_t x_str
 }
 
 hipError_t launch_rvq_gateup(const RecSrc &src, const RecOffsets &off, int H, int I, int n_items,
-                             const uint32_t *xh, const int32_t *xexp, float *hh, hipStream_t s) {
+                             const uint32_t *xh, const int32_t *xexp, float *gu, hipStream_t s) {
     if (n_items == 0) return hipSuccess;
     static bool attr = false;
     if (!attr) {
@@ -612,8 +596,8 @@ hipError_t launch_rvq_gateup(const RecSrc &src, const RecOffsets &off, int H, in
         if (e != hipSuccess) return e;
         attr = true;
     }
-    const int grid = n_items * (I / kTileRows);
-    k_rvq_gateup<<<grid, kGuWaves * 64, gateup_lds(), s>>>(src, off, H, I, xh, xexp, hh);
+    const int grid = n_items * (I / kTileRows) * 2;
+    k_rvq_gateup<<<grid, kGuWaves * 64, gateup_lds(), s>>>(src, off, H, I, xh, xexp, gu);
     return hipGetLastError();
 }
 
@@ -627,7 +611,7 @@ int down_splits(int H, int I, int n_items) {
 }
 
 hipError_t launch_rvq_down(const RecSrc &src, const RecOffsets &off, int H, int I, int n_items, int KS,
-                           const float *hh, float *ypart, hipStream_t s) {
+                           const float *gu, float *ypart, hipStream_t s) {
     if (n_items == 0) return hipSuccess;
     const size_t lds = down_lds(I, KS);
     if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
@@ -639,7 +623,7 @@ hipError_t launch_rvq_down(const RecSrc &src, const RecOffsets &off, int H, int 
         attr = true;
     }
     const int grid = n_items * (H / kTileRows) * KS;
-    k_rvq_down<<<grid, kDnWaves * 64, lds, s>>>(src, off, H, I, KS, hh, ypart);
+    k_rvq_down<<<grid, kDnWaves * 64, lds, s>>>(src, off, H, I, KS, gu, ypart);
     return hipGetLastError();
 }
 

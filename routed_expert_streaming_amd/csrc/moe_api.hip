@@ -97,7 +97,7 @@ LayerWs carve_layer(void *ws, int H, int I, int E, int k, int T, bool shared) {
     L.w = c.take<float>((size_t)T * k);
     L.xh = c.take<uint32_t>((size_t)T * H / 2);
     L.xexp = c.take<int32_t>((size_t)T);
-    L.hh = c.take<float>((size_t)items * I);
+    L.hh = c.take<float>((size_t)items * 2 * I);   // gate and up per item
     L.ypart = c.take<float>((size_t)items * KS * H);
     L.hs = shared ? c.take<float>((size_t)T * I) : nullptr;
     L.ysh = shared ? c.take<float>((size_t)T * H) : nullptr;

@@ -43,7 +43,7 @@ struct LayerWs {
     float *w;          // [T, k]
     uint32_t *xh;      // [T, H/2] x as fp16 pairs, scaled by 2^-xexp[t]
     int32_t *xexp;     // [T] range exponent of each token's x
-    float *hh;         // [T*k, I] SwiGLU intermediate (fp32)
+    float *hh;         // [T*k, 2, I] gate and up outputs (fp32); the down kernel forms SiLU(g) * u
     float *ypart;      // [T*k, KS, H] down partial sums (scaled)
     float *hs;         // [T, I] shared-expert intermediate (fp32)
     float *ysh;        // [T, H] shared-expert output
@@ -67,9 +67,9 @@ hipError_t launch_pack_x(const void *x, int x_dtype, int T, int H, int64_t x_str
                          hipStream_t s);
 // n_local_total = T * src.n_local local items in the launch
 hipError_t launch_rvq_gateup(const RecSrc &src, const RecOffsets &off, int H, int I, int n_local_total,
-                             const uint32_t *xh, const int32_t *xexp, float *hh, hipStream_t s);
+                             const uint32_t *xh, const int32_t *xexp, float *gu, hipStream_t s);
 hipError_t launch_rvq_down(const RecSrc &src, const RecOffsets &off, int H, int I, int n_local_total,
-                           int KS, const float *hh, float *ypart, hipStream_t s);
+                           int KS, const float *gu, float *ypart, hipStream_t s);
 hipError_t launch_combine(const float *ypart, int k, int KS, int H, const float *w, const float *ysh,
                           float *out, int64_t out_stride, int T, int accumulate, hipStream_t s);
 hipError_t launch_dense_gateup(const uint16_t *shared, int H, int I, const void *x, int x_dtype,
