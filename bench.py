@@ -37,8 +37,8 @@ TRAFFIC = {
     "decode": {"sources": {"routed_expert_streaming_amd/csrc/kernels_decode.hip": "fab0db0257a2ef41"},
                "bytes": {"mixtral": 5057644555, "kimi_linear": 1235807045}},
     "batched": {"sources": {"routed_expert_streaming_amd/csrc/kernels_grouped.hip": "613c8e21cf66bf46",
-                            "routed_expert_streaming_amd/csrc/kernels.hip": "e982d601c873d008"},
-                "bytes": {"batched": 5475616797}},
+                            "routed_expert_streaming_amd/csrc/kernels.hip": "d84fc65f26f96ba2"},
+                "bytes": {"batched": 5475445409}},
 }
 
 
