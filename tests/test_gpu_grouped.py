@@ -81,3 +81,21 @@ def test_grouped_many_pairs(moe):
     cfg = synth.get_config("batched", tokens=1600, E=64, k=8, H=512, I=256, shared=True)
     counts = _check(moe, cfg, sample=list(range(0, 1600, 7)) + [1599])
     assert counts.sum() == 12800
+
+
+def test_grouped_unaligned_out(moe):
+    # an output that is not 16-byte aligned takes the combine's one-column
+    # path; it must give the same bits as the aligned four-column path
+    from routed_expert_streaming_amd.device_workload import DeviceWorkload
+    cfg = synth.get_config("batched", tokens=48, E=64)
+    dw = DeviceWorkload(cfg, layers=[0])
+    x = dw.inputs()
+    x = (x[:, 0, :] if x.dim() == 3 else x).contiguous().to(torch.bfloat16)
+    ref, idx_a, _ = moe.layer_forward_grouped(dw.layers[0], x)
+    buf = torch.empty(cfg.tokens * cfg.H + 1, dtype=torch.float32, device="cuda")
+    out = buf[1:].view(cfg.tokens, cfg.H)
+    assert out.data_ptr() % 16 != 0
+    got, idx_b, _ = moe.layer_forward_grouped(dw.layers[0], x, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, idx_b)
+    assert torch.equal(got, ref)
