@@ -369,10 +369,11 @@ size_t moe_streamed_workspace_bytes(const moe_layer *L, int32_t T);
  * expert id, inserts each miss (copied from experts_host[e], alternately on
  * copy_stream and on a second copy stream the cache owns; copy_stream then
  * waits for the second, so it completes after every copy of the call), runs
- * the hit experts at once and each miss expert after its copy lands, then
- * combines in fixed rank order with the shared expert.  Output equals
- * moe_layer_forward's bit for bit.  MOE_E_INVAL if the cache capacity is below k or its slot size below
- * the record size.
+ * the hit experts at once and the miss experts (two per launch, one from
+ * each copy stream) once their copies have landed, then combines in fixed
+ * rank order with the shared expert.  Output equals moe_layer_forward's bit
+ * for bit.  MOE_E_INVAL if the cache capacity is below k or its slot size
+ * below the record size.
  *   experts_host [host] array of E [pinned] record pointers
  *   x [dev] [1, H] fp32;  out [dev] [1, H] fp32;  idx_out [dev] [1, k] or NULL */
 int moe_layer_forward_streamed(const moe_layer *L, moe_cache *c, uint32_t layer_id,
