@@ -170,7 +170,7 @@ hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, i
 // few tokens leave the CUs idle): part holds dense_part_floats(H, I, T)
 // floats; the down GEMM's *nsh slices of [T, H] partial sums stay in part for
 // the combine to add.
-int dense_splits(int N, int T, int K);
+int dense_splits(int N, int T, int K, int M);
 size_t dense_part_floats(int H, int I, int T);
 hipError_t launch_grouped_dense(const uint16_t *shared, int H, int I, int T, const uint16_t *xb, uint16_t *hs,
                                 float *part, int *nsh, hipStream_t s);
