@@ -78,25 +78,41 @@ __device__ __forceinline__ uint32_t quad_code(uint32_t d0, uint32_t d1, uint32_t
 }
 
 // ------------------------------------------------------------------ group
-// One workgroup: histogram of expert ids, exclusive scan (one wave), scatter,
-// then a per-expert insertion sort so every segment lists its pairs in
-// ascending pair index (deterministic).  Up to kGroupLdsPairs pairs are
-// scattered and sorted in LDS and written out once; more are sorted in place
-// in global memory.
+// One workgroup: histogram of expert ids, exclusive scan (one wave), then
+// every pair's position in its expert's segment, so that each segment lists
+// its pairs in ascending pair index (deterministic).  Pair p is token p / k's
+// rank p % k, and a token's k experts differ, so p's position in expert e's
+// segment is the number of earlier tokens that chose e: with a bitmap of the
+// tokens per expert in LDS (up to kGroupBitWords words), a popcount.  Larger
+// cases scatter, then sort each segment by insertion (in LDS up to
+// kGroupLdsPairs pairs, else in global memory).
 constexpr int kGroupLdsPairs = 12288;
+constexpr int kGroupBitWords = 8192;
 
-__global__ __launch_bounds__(1024) void k_group(const int32_t *__restrict__ idx, int n_pairs, int E,
+__global__ __launch_bounds__(1024) void k_group(const int32_t *__restrict__ idx, int n_pairs, int k, int E,
                                                 int32_t *__restrict__ perm, int32_t *__restrict__ inv,
                                                 int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
     __shared__ int cnt[MOE_MAX_E + 1];
     __shared__ int off[MOE_MAX_E + 1];
     __shared__ int fill[MOE_MAX_E];
     __shared__ int sperm[kGroupLdsPairs];
+    __shared__ uint32_t bits[kGroupBitWords];
+    const int T = n_pairs / k, nw = (T + 31) / 32;   // tokens, bitmap words per expert
+    const bool by_bits = (long)E * nw <= kGroupBitWords;
     const bool in_lds = n_pairs <= kGroupLdsPairs;
     int *P = in_lds ? sperm : perm;
     for (int e = threadIdx.x; e <= E; e += blockDim.x) { cnt[e] = 0; fill[e < E ? e : 0] = 0; }
+    if (by_bits)
+        for (int i = threadIdx.x; i < E * nw; i += blockDim.x) bits[i] = 0u;
     __syncthreads();
-    for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) atomicAdd(&cnt[idx[p]], 1);
+    for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
+        const int e = idx[p];
+        atomicAdd(&cnt[e], 1);
+        if (by_bits) {
+            const int t = p / k;
+            atomicOr(&bits[e * nw + (t >> 5)], 1u << (t & 31));
+        }
+    }
     __syncthreads();
     if (threadIdx.x < 64) {
         // lane l sums experts [l*per, (l+1)*per); a shuffle scan gives the bases
@@ -117,6 +133,23 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t *__restrict__ idx,
         if (lane == 63) off[E] = incl;
     }
     __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        counts[e] = cnt[e];
+        offsets[e] = off[e];
+    }
+    if (threadIdx.x == 0) offsets[E] = off[E];
+    if (by_bits) {
+        for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
+            const int e = idx[p], t = p / k;
+            const uint32_t *row = bits + e * nw;
+            int rank = __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
+            for (int i = 0; i < (t >> 5); i++) rank += __popc(row[i]);
+            const int q = off[e] + rank;
+            perm[q] = p;
+            inv[p] = q;
+        }
+        return;
+    }
     for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
         const int e = idx[p];
         P[off[e] + atomicAdd(&fill[e], 1)] = p;
@@ -131,10 +164,7 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t *__restrict__ idx,
             while (j >= 0 && P[b + j] > v) { P[b + j + 1] = P[b + j]; j--; }
             P[b + j + 1] = v;
         }
-        counts[e] = n;
-        offsets[e] = b;
     }
-    if (threadIdx.x == 0) offsets[E] = off[E];
     __syncthreads();
     for (int q = threadIdx.x; q < n_pairs; q += blockDim.x) {
         const int p = P[q];
@@ -662,9 +692,9 @@ __global__ __launch_bounds__(256) void k_grouped_combine(const float *__restrict
 
 }  // namespace
 
-hipError_t launch_group(const int32_t *idx, int n_pairs, int E, int32_t *perm, int32_t *inv, int32_t *counts,
-                        int32_t *offsets, hipStream_t s) {
-    k_group<<<1, 1024, 0, s>>>(idx, n_pairs, E, perm, inv, counts, offsets);
+hipError_t launch_group(const int32_t *idx, int n_pairs, int k, int E, int32_t *perm, int32_t *inv,
+                        int32_t *counts, int32_t *offsets, hipStream_t s) {
+    k_group<<<1, 1024, 0, s>>>(idx, n_pairs, k, E, perm, inv, counts, offsets);
     return hipGetLastError();
 }
 

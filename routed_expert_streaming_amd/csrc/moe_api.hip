@@ -956,7 +956,7 @@ int moe_layer_forward_grouped(const moe_layer *L, const void *x, int32_t x_dtype
     HIPCHK(launch_route_blocked(L->router.weight, L->router.bias, E, H, x, x_dtype, T, W.zpart, W.z, s),
            "route logits");
     HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, T, idx, w, s), "top-k");
-    HIPCHK(launch_group(idx, T * k, E, W.perm, W.inv, W.counts, W.offsets, s), "group");
+    HIPCHK(launch_group(idx, T * k, k, E, W.perm, W.inv, W.counts, W.offsets, s), "group");
     HIPCHK(launch_to_bf16(x, x_dtype, (size_t)T * H, W.xb, s), "x to bf16");
     int nsh = 0;
     if (L->shared) HIPCHK(launch_grouped_dense(L->shared, H, I, T, W.xb, W.hs, W.ysh, &nsh, s), "shared expert");

@@ -160,8 +160,9 @@ int decode_forward_impl(const moe_layer *layers, int32_t n_layers, const float *
 int decode_noalloc_scratch(void **out);
 
 // ---- batched path (kernels_grouped.hip) --------------------------------------
-hipError_t launch_group(const int32_t *idx, int n_pairs, int E, int32_t *perm, int32_t *inv, int32_t *counts,
-                        int32_t *offsets, hipStream_t s);
+// idx: T * k expert ids, a token's k ids distinct (top-k)
+hipError_t launch_group(const int32_t *idx, int n_pairs, int k, int E, int32_t *perm, int32_t *inv,
+                        int32_t *counts, int32_t *offsets, hipStream_t s);
 hipError_t launch_to_bf16(const void *x, int x_dtype, size_t n, uint16_t *xb, hipStream_t s);
 hipError_t launch_grouped_rvq(const void *const *table, const RecOffsets &off, int E, int H, int I, int n_pairs,
                               const int32_t *counts, const int32_t *offsets, const int32_t *perm, int k,

@@ -75,12 +75,22 @@ def test_grouped_full_batched_layer(moe):
 
 
 def test_grouped_many_pairs(moe):
-    # 1600 tokens x top-8 = 12,800 (token, rank) pairs: more than the grouping
-    # kernel sorts in LDS, so its segments are sorted in global memory; ~200
+    # 1600 tokens x top-8 = 12,800 (token, rank) pairs over 64 experts: the
+    # grouping ranks pairs by per-expert token bitmaps (64 x 50 words); ~200
     # tokens per expert (13 passes of 16)
     cfg = synth.get_config("batched", tokens=1600, E=64, k=8, H=512, I=256, shared=True)
     counts = _check(moe, cfg, sample=list(range(0, 1600, 7)) + [1599])
     assert counts.sum() == 12800
+
+
+@pytest.mark.parametrize("tokens,k", [(300, 2), (1600, 8)])
+def test_grouped_many_experts(moe, tokens, k):
+    # 1024 experts: the token bitmaps would exceed the grouping kernel's LDS
+    # budget, so it scatters and sorts each segment by insertion: in LDS for
+    # 600 pairs, in global memory for 12,800
+    cfg = synth.get_config("batched", tokens=tokens, E=1024, k=k, H=256, I=128, shared=False)
+    counts = _check(moe, cfg, sample=list(range(0, tokens, 11)) + [tokens - 1])
+    assert counts.sum() == tokens * k
 
 
 def test_grouped_unaligned_out(moe):
