@@ -165,7 +165,16 @@ __global__ __launch_bounds__(256) void k_route_reduce(const float *__restrict__ 
     const size_t n = (size_t)T * E;
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
         float s = 0.f;
-        for (int ks = 0; ks < KS; ks++) s += part[ks * n + i];
+        // eight slices' loads in flight at a time, added in slice order
+        int ks = 0;
+        for (; ks + 8 <= KS; ks += 8) {
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; q++) v[q] = part[(ks + q) * n + i];
+#pragma unroll
+            for (int q = 0; q < 8; q++) s += v[q];
+        }
+        for (; ks < KS; ks++) s += part[ks * n + i];
         z[i] = s + (bias ? bias[i % E] : 0.f);
     }
 }
@@ -553,7 +562,7 @@ hipError_t launch_route_logits(const float *W, const float *bias, int E, int H, 
 int route_blocked_slices(int E, int H, int T) {
     const int tiles = ((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE);
     const int steps = H / kRbK;
-    int ks = (512 + tiles - 1) / tiles;   // about two workgroups per CU
+    int ks = (1024 + tiles - 1) / tiles;   // about four workgroups per CU
     return std::max(1, std::min(ks, std::min(steps, kRouteMaxSlices)));
 }
 
