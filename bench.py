@@ -36,9 +36,9 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC = {
     "decode": {"sources": {"routed_expert_streaming_amd/csrc/kernels_decode.hip": "fab0db0257a2ef41"},
                "bytes": {"mixtral": 5057644555, "kimi_linear": 1235807045}},
-    "batched": {"sources": {"routed_expert_streaming_amd/csrc/kernels_grouped.hip": "613c8e21cf66bf46",
-                            "routed_expert_streaming_amd/csrc/kernels.hip": "d84fc65f26f96ba2"},
-                "bytes": {"batched": 5475445409}},
+    "batched": {"sources": {"routed_expert_streaming_amd/csrc/kernels_grouped.hip": "19f8b9070b2243fe",
+                            "routed_expert_streaming_amd/csrc/kernels.hip": "12a44aa153794c79"},
+                "bytes": {"batched": 5525670840}},
 }
 
 
