@@ -783,7 +783,25 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         // alternate between the two copy streams (the caller's then waits for
         // the cache's own), so consecutive misses n, n+1 land together: their
         // experts run as one pair.
-        auto copy_ps = [&](int n) { return n % 2 ? c->ps2 : ps; };
+        // on every path out of this branch (an error included) the caller's
+        // copy stream waits for the second one once that one has a copy
+        struct Join {
+            moe_cache *c;
+            hipStream_t ps;
+            bool used = false;
+            hipError_t run() {
+                if (!used) return hipSuccess;
+                used = false;
+                hipError_t e = hipEventRecord(c->ps2_done, c->ps2);
+                return e == hipSuccess ? hipStreamWaitEvent(ps, c->ps2_done, 0) : e;
+            }
+            ~Join() { (void)run(); }
+        } join{c, ps};
+        auto copy_ps = [&](int n) {
+            if (n % 2 == 0) return ps;
+            join.used = true;
+            return c->ps2;
+        };
         for (int n = 0; n < nlocked; n++)
             if ((rc = copy_miss(morder[n], copy_ps(n)))) return rc;
         if ((rc = run_hits())) return rc;
@@ -795,10 +813,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
                 if ((rc = copy_miss(morder[n + q], copy_ps(n + q)))) return rc;
             if ((rc = run_misses(morder + n, nj))) return rc;
         }
-        if (nmiss > 1) {
-            HIPCHK(hipEventRecord(c->ps2_done, c->ps2), "second copy stream done");
-            HIPCHK(hipStreamWaitEvent(ps, c->ps2_done, 0), "copy stream waits for the second");
-        }
+        HIPCHK(join.run(), "copy stream waits for the second");
     } else if (X) {
         // exclusive host tier: the hit experts run while the records found in
         // neither tier are read from the file into transit pages; then the
