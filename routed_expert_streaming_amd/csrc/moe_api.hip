@@ -757,7 +757,6 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         HIPCHK(launch_rvq_down(src, off, H, I, nj, KS, W.hh, W.ypart, cs), "rvq down (misses)");
         return MOE_OK;
     };
-    auto run_miss = [&](int j) { return run_misses(&j, 1); };
     // the hit experts, all at once
     auto run_hits = [&]() -> int {
         RecSrc hits{};
@@ -777,31 +776,44 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         }
         return MOE_OK;
     };
+    // The misses' copies alternate between the caller's copy stream and the
+    // cache's own (copy n on the second when n is odd), so consecutive misses
+    // n, n+1 land together and their experts run as one pair.  On every path
+    // out of the miss loops (an error included) the caller's copy stream
+    // waits for the second one once that one has a copy.
+    struct Join {
+        moe_cache *c;
+        hipStream_t ps;
+        bool used = false;
+        hipError_t run() {
+            if (!used) return hipSuccess;
+            used = false;
+            hipError_t e = hipEventRecord(c->ps2_done, c->ps2);
+            return e == hipSuccess ? hipStreamWaitEvent(ps, c->ps2_done, 0) : e;
+        }
+        ~Join() { (void)run(); }
+    } join{c, ps};
+    auto copy_ps = [&](int n) {
+        if (n % 2 == 0) return ps;
+        join.used = true;
+        return c->ps2;
+    };
+    // misses morder[0..nmiss) copied and run in pairs
+    auto copy_run_pairs = [&]() -> int {
+        for (int n = 0; n < nmiss; n += 2) {
+            const int nj = std::min(2, nmiss - n);
+            for (int q = 0; q < nj; q++) {
+                const int r = copy_miss(morder[n + q], copy_ps(n + q));
+                if (r) return r;
+            }
+            const int r = run_misses(morder + n, nj);
+            if (r) return r;
+        }
+        return MOE_OK;
+    };
     if (!tier.t) {
         // page-locked misses' copies first (the copy engine starts at once),
-        // then the hit experts, then the misses' experts.  The copies
-        // alternate between the two copy streams (the caller's then waits for
-        // the cache's own), so consecutive misses n, n+1 land together: their
-        // experts run as one pair.
-        // on every path out of this branch (an error included) the caller's
-        // copy stream waits for the second one once that one has a copy
-        struct Join {
-            moe_cache *c;
-            hipStream_t ps;
-            bool used = false;
-            hipError_t run() {
-                if (!used) return hipSuccess;
-                used = false;
-                hipError_t e = hipEventRecord(c->ps2_done, c->ps2);
-                return e == hipSuccess ? hipStreamWaitEvent(ps, c->ps2_done, 0) : e;
-            }
-            ~Join() { (void)run(); }
-        } join{c, ps};
-        auto copy_ps = [&](int n) {
-            if (n % 2 == 0) return ps;
-            join.used = true;
-            return c->ps2;
-        };
+        // then the hit experts, then the misses' experts
         for (int n = 0; n < nlocked; n++)
             if ((rc = copy_miss(morder[n], copy_ps(n)))) return rc;
         if ((rc = run_hits())) return rc;
@@ -837,10 +849,8 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
             return rc;
         }
         for (int n = 0; n < nmiss; n++) src_of[morder[n]] = tier_page(X, spage[morder[n]]);
-        for (int n = 0; n < nmiss; n++) {
-            if ((rc = copy_miss(morder[n], ps))) return rc;
-            if ((rc = run_miss(morder[n]))) return rc;
-        }
+        if ((rc = copy_run_pairs())) return rc;
+        HIPCHK(join.run(), "copy stream waits for the second");
     } else {
         // file tier: the hit experts run while the misses' records are read
         // into host slots
@@ -854,10 +864,8 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
             return rc;
         }
         for (int n = 0; n < nmiss; n++) src_of[morder[n]] = ptrs[n];
-        for (int n = 0; n < nmiss; n++) {
-            if ((rc = copy_miss(morder[n], ps))) return rc;
-            if ((rc = run_miss(morder[n]))) return rc;
-        }
+        if ((rc = copy_run_pairs())) return rc;
+        HIPCHK(join.run(), "copy stream waits for the second");
     }
     HIPCHK(launch_combine(W.ypart, k, KS, H, W.w, L->shared ? W.ysh : nullptr, out, H, 1, 0, cs), "combine");
     rc = cache_release_many(c, slot_of, k, cs);
