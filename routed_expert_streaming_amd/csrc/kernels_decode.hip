@@ -192,16 +192,18 @@ __device__ __forceinline__ bool poll_more(unsigned *sync, long &spins) {
 // A space of n units is split over Ga = min(G, n) active workgroups into
 // contiguous, non-empty ranges [start(w), start(w+1)); workgroups w >= Ga get
 // nothing.  Non-empty ranges keep the contributors of any unit interval
-// contiguous in w.
-__device__ __forceinline__ int active_of(long n, int G) { return (int)(n < G ? n : G); }
-__device__ __forceinline__ long range_start(long n, int G, int w) {
+// contiguous in w.  32-bit arithmetic: every space here has n * (G + 1) <
+// 2^31 (the plan checks it), so the products cannot overflow (a 64-bit
+// division is a long instruction sequence, and these sit on phases' tails).
+__device__ __forceinline__ int active_of(int n, int G) { return n < G ? n : G; }
+__device__ __forceinline__ int range_start(int n, int G, int w) {
     const int Ga = active_of(n, G);
-    return w >= Ga ? n : n * w / Ga;
+    return w >= Ga ? n : (int)((unsigned)(n * w) / (unsigned)Ga);
 }
 // workgroup owning unit u
-__device__ __forceinline__ int range_owner(long n, int G, long u) {
+__device__ __forceinline__ int range_owner(int n, int G, int u) {
     const int Ga = active_of(n, G);
-    return (int)(((u + 1) * Ga + n - 1) / n - 1);
+    return (int)((unsigned)((u + 1) * Ga + n - 1) / (unsigned)n) - 1;
 }
 
 // One strip (64 rows x 128 columns, 16 groups of 8 columns) of codes against
@@ -781,8 +783,8 @@ __device__ __forceinline__ bool stream_lut(const u32x4 *codes, const u32x4 *cb, 
 
 // Workgroup whose down range holds the last unit of output tile td in the
 // last rank: it combines the tile.
-__device__ __forceinline__ int combiner_of(int td, int k, int tilesH, int cprI, long nD, int G) {
-    return range_owner(nD, G, ((long)(k - 1) * tilesH + td + 1) * cprI - 1);
+__device__ __forceinline__ int combiner_of(int td, int k, int tilesH, int cprI, int nD, int G) {
+    return range_owner(nD, G, ((k - 1) * tilesH + td + 1) * cprI - 1);
 }
 
 // Output tile td, by one wave: out = sum_j w_j * sum_slots y_j + shared, in
@@ -792,7 +794,7 @@ __device__ __forceinline__ int combiner_of(int td, int k, int tilesH, int cprI, 
 // of up to RG ranks needs one round trip once the last partial lands.
 // Returns false on a failed wait.
 template <int RG>
-__device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k, int tilesH, int cprI, long nD,
+__device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k, int tilesH, int cprI, int nD,
                                              int G, int H, bool shared_on, const uint64_t *part_d, int slots_d,
                                              const uint64_t *ysh, float *out, const float *sw, unsigned *sync,
                                              int lane) {
@@ -808,7 +810,7 @@ __device__ __forceinline__ bool combine_tile(int td, int s, unsigned tag, int k,
         int cmax = 0;
 #pragma unroll
         for (int jj = 0; jj < RG; jj++) {
-            const long t = (long)min(j0 + jj, k - 1) * tilesH + td;
+            const int t = min(j0 + jj, k - 1) * tilesH + td;
             cj[jj] = range_owner(nD, G, (t + 1) * cprI - 1) - range_owner(nD, G, t * cprI) + 1;
             pj[jj] = part_d + (size_t)t * slots_d * 64 + lane;
             cmax = max(cmax, cj[jj]);
@@ -988,15 +990,15 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
     const int H = a.H, I = a.I, k = a.k;
     const int tilesI = I / kTileRows, tilesH = H / kTileRows;
     const int cprH = H / kChunkCols, cprI = I / kChunkCols;
-    const long nGU = (long)k * tilesI * cprH, nD = (long)k * tilesH * cprI;
-    const long gu0 = range_start(nGU, G, w), gu1 = range_start(nGU, G, w + 1);
-    const long d0 = range_start(nD, G, w), d1 = range_start(nD, G, w + 1);
+    const int nGU = k * tilesI * cprH, nD = k * tilesH * cprI;
+    const int gu0 = range_start(nGU, G, w), gu1 = range_start(nGU, G, w + 1);
+    const int d0 = range_start(nD, G, w), d1 = range_start(nD, G, w + 1);
     unsigned *sync = a.sync;
     unsigned *h_ready = sync + kHReady;                          // [k+1], kLine apart
     const int steps = a.T * a.nL;
     // shared-expert row ranges
-    const int shI0 = (int)range_start(I, G, w), shI1 = (int)range_start(I, G, w + 1);
-    const int shH0 = (int)range_start(H, G, w), shH1 = (int)range_start(H, G, w + 1);
+    const int shI0 = range_start(I, G, w), shI1 = range_start(I, G, w + 1);
+    const int shH0 = range_start(H, G, w), shH1 = range_start(H, G, w + 1);
     const unsigned sh_gu_contrib = (unsigned)min(G, I);          // workgroups with shared gate/up rows
     // Whether this workgroup uses a step's routing result.  Which workgroups
     // own gate/up units, joins, down units or output units depends only on
@@ -1378,8 +1380,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // step-tagged words (down by table lookup polls them per chunk).
             bool okj = true;
             const unsigned t16 = tag16(s);
-            const long nTau = (long)k * tilesI;
-            const int nT = w < nTau ? (int)((nTau - 1 - w) / G) + 1 : 0;
+            const int nTau = k * tilesI;
+            const int nT = w < nTau ? (nTau - 1 - w) / G + 1 : 0;
             float *jred = (float *)lds;     // [2][kPW][128], table area (free now)
             for (int p0 = 0; p0 < nT; p0 += 2) {
                 const int tn = min(2, nT - p0);
@@ -1392,7 +1394,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                     for (int tt = 0; tt < 2; tt++)
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
-                            const long tau = w + (long)G * (p0 + min(tt, tn - 1));
+                            const int tau = w + G * (p0 + min(tt, tn - 1));
                             const int sl = min(s0 + q * kPW, cprH - 1);
                             pp[tt][q] = a.part_gu + ((size_t)tau * cprH + sl) * 64 + (lane & 31);
                             vg[tt][q] = ld_tagged(pp[tt][q]);
@@ -1432,7 +1434,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 }
                 lds_sync();
                 if (wave < tn) {
-                    const long tau = w + (long)G * (p0 + wave);
+                    const int tau = w + G * (p0 + wave);
                     const int j = (int)(tau / tilesI);
                     const uint8_t *rec = (const uint8_t *)recs[j];
                     const int r = (int)(tau % tilesI) * kTileRows + lane;
@@ -1464,20 +1466,20 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 if (!*bcast) return;
             }
             if (threadIdx.x == 0 && !(a.lut & kLutDown))
-                for (long tau = w; tau < (long)k * tilesI; tau += G)
+                for (int tau = w; tau < k * tilesI; tau += G)
                     __hip_atomic_fetch_add(h_ready + (tau / tilesI) * kLine, 1u, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
         }
         // ---- gate/up over this workgroup's range of (rank, tile, chunk), one
         // expert segment at a time (a range spans at most two experts)
-        for (long ea = (a.lut & kLutGateUp) ? gu1 : gu0; ea < gu1;) {
-            const int j = (int)(ea / ((long)tilesI * cprH));
-            const long eb = min(gu1, (long)(j + 1) * tilesI * cprH);
+        for (int ea = (a.lut & kLutGateUp) ? gu1 : gu0; ea < gu1;) {
+            const int j = ea / (tilesI * cprH);
+            const int eb = min(gu1, (j + 1) * tilesI * cprH);
             const uint8_t *rec = (const uint8_t *)recs[j];
-            const long base = (long)j * tilesI * cprH;       // expert-local units
+            const int base = j * tilesI * cprH;              // expert-local units
             stream_gateup((const u32x4 *)(rec + a.off.codes[0]), (const u32x4 *)(rec + a.off.codes[1]),
                           (const u32x4 *)(rec + a.off.cb[0]), (const u32x4 *)(rec + a.off.cb[1]), H, I, cprH,
-                          (int)(ea - base), (int)(eb - base), (int)(ea / cprH - base / cprH), a.slots_red_gu, wave,
+                          ea - base, eb - base, ea / cprH - base / cprH, a.slots_red_gu, wave,
                           lane, stamp, sh_counted ? nullptr : h_ready + k * kLine);
             sh_counted = true;
             lds_sync();
@@ -1487,10 +1489,10 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             // ...); the workgroup owning a tile's last unit joins it (one
             // wave per tile) into fp16 SiLU(g) * u once every contributor's
             // partial of this step is there
-            const long tA = ea / cprH;
-            const int nt = (int)((eb - 1) / cprH - tA) + 1;
+            const int tA = ea / cprH;
+            const int nt = (eb - 1) / cprH - tA + 1;
             for (int v = wave; v < nt; v += kPW) {
-                const long tau = tA + v;
+                const int tau = tA + v;
                 const int slot = w - range_owner(nGU, G, tau * cprH);
                 float g = 0.f, uu = 0.f;
 #pragma unroll
@@ -1505,11 +1507,11 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             int nj = 0;
             bool okj = true;
             for (int v = 0; v < nt; v++) {
-                const long tau = tA + v;
+                const int tau = tA + v;
                 if (range_owner(nGU, G, (tau + 1) * cprH - 1) != w) continue;
                 if (nj++ % kPW != wave) continue;
                 const int first = range_owner(nGU, G, tau * cprH), ncontrib = w - first + 1;
-                const int r = (int)(tau % tilesI) * kTileRows + lane;
+                const int r = tau % tilesI * kTileRows + lane;
                 const float sg = (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
                 const float su = (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
                 const uint64_t *pp = a.part_gu + (size_t)tau * a.slots_gu * 128 + lane;
@@ -1703,31 +1705,31 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         }
         // ---- down over this workgroup's range of (rank, tile of H, chunk),
         // one expert segment at a time: tagged partials per touched tile
-        for (long ea = d0; ea < d1;) {
-            const int j = (int)(ea / ((long)tilesH * cprI));
-            const long eb = min(d1, (long)(j + 1) * tilesH * cprI);
+        for (int ea = d0; ea < d1;) {
+            const int j = ea / (tilesH * cprI);
+            const int eb = min(d1, (j + 1) * tilesH * cprI);
             const uint8_t *rec = (const uint8_t *)recs[j];
-            const long base = (long)j * tilesH * cprI;
-            const long tA = ea / cprI;
-            const int nt = (int)((eb - 1) / cprI - tA) + 1;
+            const int base = j * tilesH * cprI;
+            const int tA = ea / cprI;
+            const int nt = (eb - 1) / cprI - tA + 1;
             const _Float16 *dscale = (const _Float16 *)(rec + a.off.scales[2]);
             // the row scales of this wave's first tile, loaded before the
             // loop: the partial stores after it wait for no load
-            const float sc0 = wave < nt ? (float)dscale[(int)((tA + wave) % tilesH) * kTileRows + lane] : 0.f;
+            const float sc0 = wave < nt ? (float)dscale[(tA + wave) % tilesH * kTileRows + lane] : 0.f;
             int he = 0;
             if (!stream_down((const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]),
                              a.hh + (size_t)j * I, sync, h_ready + j * kLine, (unsigned)(s + 1) * tilesI, bcast, lmax,
-                             he, H, I, cprI, (int)(ea - base), (int)(eb - base), (int)(ea / cprI - base / cprI),
+                             he, H, I, cprI, ea - base, eb - base, ea / cprI - base / cprI,
                              a.slots_red_d, wave, lane, stamp))
                 return;
             lds_sync();
             mark(kStampDownLoop);
             for (int v = wave; v < nt; v += kPW) {
-                const long tau = tA + v;
+                const int tau = tA + v;
                 float y = 0.f;
 #pragma unroll
                 for (int q = 0; q < kPW; q++) y += red_d[(v * kPW + q) * 64 + lane];
-                const int r = (int)(tau % tilesH) * kTileRows + lane;
+                const int r = tau % tilesH * kTileRows + lane;
                 y = ldexpf(y, he) * (v == wave ? sc0 : (float)dscale[r]);
                 st_tagged(a.part_d + ((size_t)tau * a.slots_d + (w - range_owner(nD, G, tau * cprI))) * 64 + lane, y,
                           tag);
@@ -1742,9 +1744,9 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             int nc = 0;
             bool okc = true;
             // candidates: the last rank's tiles that this workgroup's range touches
-            const long lb0 = (long)(k - 1) * tilesH * cprI;
-            const int tdA = d1 > lb0 ? (int)((max(d0, lb0) - lb0) / cprI) : tilesH;
-            const int tdB = d1 > lb0 ? (int)((d1 - 1 - lb0) / cprI) : -1;
+            const int lb0 = (k - 1) * tilesH * cprI;
+            const int tdA = d1 > lb0 ? (max(d0, lb0) - lb0) / cprI : tilesH;
+            const int tdB = d1 > lb0 ? (d1 - 1 - lb0) / cprI : -1;
             for (int td = tdA; td <= tdB; td++) {
                 if (combiner_of(td, k, tilesH, cprI, nD, G) != w) continue;
                 if (nc++ % kPW != wave || !okc) continue;
@@ -1883,6 +1885,10 @@ hipError_t decode_plan(int H, int I, int k, int lut_mode, DecodePlanOut *o) {
     const bool gu_ok = (o->lut & kLutGateUp) || (red_gu <= kDecTail && kXStage + (long)H * 4 <= 2L * kCbRows * 16);
     const bool d_ok = (o->lut & kLutDown) || red_d <= kDecTail;
     o->lds_ok = gu_ok && d_ok;
+    // the kernel's work-range arithmetic is 32-bit: n * (G + 1) < 2^31 for
+    // every unit space it splits
+    const long lim = (1L << 31) / (G + 1);
+    o->units_ok = (long)k * tilesI * cprH < lim && (long)k * tilesH * cprI < lim && I < lim && H < lim;
     return hipSuccess;
 }
 

@@ -326,6 +326,7 @@ int carve_decode(void *ws, const moe_layer *layers, int32_t n_layers, DecodeWs *
     hipError_t e = decode_plan(H, I, k, decode_lut_mode(), &P);
     if (e != hipSuccess) return hip_fail(e, "decode plan");
     if (!P.lds_ok) return fail(MOE_E_INVAL, "decode kernel: H=%d, I=%d do not fit its LDS layout", H, I);
+    if (!P.units_ok) return fail(MOE_E_INVAL, "decode kernel: k=%d, H=%d, I=%d exceed its work-range arithmetic", k, H, I);
     D->G = P.G;
     D->slots_gu = P.slots_gu;
     D->slots_d = P.slots_d;

@@ -141,6 +141,7 @@ struct DecodePlanOut {
     int lut;                      // kLutGateUp | kLutDown: the phases done by table lookup
     size_t sync_words;
     bool lds_ok;
+    bool units_ok;   // the unit spaces fit the kernel's 32-bit range arithmetic
 };
 // lut_mode: -1 = choose by shape, 0 = codebook gathers, 1 = table lookup
 // for gate/up and down, 2 = table lookup for gate/up only (a phase whose
