@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void k_route_reduce(const float *__restrict__ 
             for (int q = 0; q < 8; q++) s += v[q];
         }
         for (; ks < KS; ks++) s += part[ks * n + i];
-        z[i] = s + (bias ? bias[i % E] : 0.f);
+        z[i] = s + (bias ? bias[n <= 0xFFFFFFFFu ? (unsigned)i % (unsigned)E : i % E] : 0.f);
     }
 }
 
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_rvq_down(RecSrc src, RecOffse
     const uint8_t *rec = resolve_record(src, local, item);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int cpr = I / kChunkCols;
-    const int c0 = (int)((int64_t)cpr * ks / KS), c1 = (int)((int64_t)cpr * (ks + 1) / KS);
+    const int c0 = cpr * ks / KS, c1 = cpr * (ks + 1) / KS;   // 32-bit: cpr * KS is small
     const float *hg = gu + (size_t)item * 2 * I + c0 * kChunkCols, *hu = hg + I;
     const int np = (c1 - c0) * kChunkCols / 2;
     const u32x4 *codes = (const u32x4 *)(rec + off.codes[2]) + (size_t)tile * cpr * kTileVec;
@@ -429,7 +429,17 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ypart
                                                  int accumulate) {
     const size_t n = (size_t)T * H;
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const size_t t = i / H, c = i % H;
+        // 32-bit index division where the index fits (a 64-bit one is a long
+        // instruction sequence); the branch is uniform
+        size_t t, c;
+        if (n <= 0xFFFFFFFFu) {
+            const unsigned u = (unsigned)i;
+            t = u / (unsigned)H;
+            c = u - (unsigned)t * (unsigned)H;
+        } else {
+            t = i / H;
+            c = i % H;
+        }
         float acc = 0.f;
         for (int j = 0; j < k; j++) {
             const size_t item = t * k + j;
