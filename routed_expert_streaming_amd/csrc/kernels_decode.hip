@@ -1245,15 +1245,6 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 xl[p] = pack_f16x2(ldexpf(v.x, -xe), ldexpf(v.y, -xe));
             }
         }
-        if (sh_rows) {
-            shared_finish(shI0, 1);
-            for (int r0 = shI0 + kShRows; r0 < shI1; r0 += kShRows) {
-                lds_sync();
-                shared_partials(std::integral_constant<int, kShRows>{}, r0, threadIdx.x, kPW * 64);
-                lds_sync();
-                shared_finish(r0, 0);
-            }
-        }
         if (routed) {
             // Exact top-k by counting: a key's rank is the number of keys
             // above it (keys are unique: logit bits above the inverted id).
@@ -1324,6 +1315,19 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = e;
         }
         lds_sync();
+        // the shared rows' SiLU(g) * u, stored after the top-k: a wave's
+        // stores hold its later vector-memory waits (which the top-k's
+        // register reuse brings in), and the shared down reads these rows
+        // only after the gate/up phase
+        if (sh_rows) {
+            shared_finish(shI0, 1);
+            for (int r0 = shI0 + kShRows; r0 < shI1; r0 += kShRows) {
+                lds_sync();
+                shared_partials(std::integral_constant<int, kShRows>{}, r0, threadIdx.x, kPW * 64);
+                lds_sync();
+                shared_finish(r0, 0);
+            }
+        }
         mark(kStampRouted);
         // wave 1 wrote every shared row of this workgroup: it counts them once
         // its stores are done, at the first point after routing where it
