@@ -1288,31 +1288,46 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             }
             if (two) {
                 lds_sync();
-                // the groups' candidates, zeros where a group had fewer than k keys
-                // (zero is below every real key)
+                // the groups' candidates, zeros where a group had fewer than k
+                // keys (zero is below every real key; the candidate area is
+                // zeroed up to its end, kTopkGroups * MOE_MAX_K >= ncp).  Each
+                // candidate is ranked by P threads (every thread of the
+                // workgroup takes part), each counting a P-th of the list; the
+                // P counts are added across their lanes.
                 const int nc = (E + gsz - 1) / gsz * kk;
-                for (int c = threadIdx.x; c < nc; c += kPW * 64) {
-                    const uint64_t ke = cand[c];
-                    if (!ke) continue;
-                    const int rank = count_above(cand, 0, (nc + 31) & ~31, ke);
-                    if (rank < kk) place(rank, ke);
+                int ncp = 32;
+                while (ncp < nc) ncp <<= 1;
+                const int P = max(1, kPW * 64 / ncp), len = ncp / P;
+                const int c = threadIdx.x / P, q0 = (threadIdx.x % P) * len;
+                const uint64_t ke = c < nc ? cand[c] : 0u;
+                int rank = 0;
+                for (int q = q0; q < q0 + len; q += 2) {
+                    const u32x4 tw = *(const u32x4 *)(cand + q);
+                    rank += ((uint64_t)tw.y << 32 | tw.x) > ke;
+                    rank += ((uint64_t)tw.w << 32 | tw.z) > ke;
                 }
+                for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o, 64);
+                if (threadIdx.x % P == 0 && ke && rank < kk) place(rank, ke);
             }
         }
         lds_sync();
-        if (routed && wave == 0 && lane < lay.k) {
+        if (routed && wave == 0) {
+            // lane r < k scores rank r; the sum runs in rank order
+            const int kk = __builtin_amdgcn_readfirstlane(lay.k);
             const float zmax = sz[0];
-            float sum = 0.f, mine = 0.f;
-            for (int r = 0; r < lay.k; r++) {
-                const float z = sz[r];
-                const float sc = lay.score_fn == MOE_SCORE_SOFTMAX ? __expf(z - zmax) : 1.f / (1.f + __expf(-z));
-                sum += sc;
-                if (r == lane) mine = sc;
+            float sc = 0.f;
+            if (lane < kk) {
+                const float z = sz[lane];
+                sc = lay.score_fn == MOE_SCORE_SOFTMAX ? __expf(z - zmax) : 1.f / (1.f + __expf(-z));
             }
-            const int e = sidx[lane];
-            sw[lane] = mine / sum;
-            recs[lane] = recs_all[e];
-            if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = e;
+            float sum = 0.f;
+            for (int r = 0; r < kk; r++) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), r));
+            if (lane < kk) {
+                const int e = sidx[lane];
+                sw[lane] = sc / sum;
+                recs[lane] = recs_all[e];
+                if (w == 0 && a.idx_out) a.idx_out[(size_t)s * k + lane] = e;
+            }
         }
         lds_sync();
         // the shared rows' SiLU(g) * u, stored after the top-k: a wave's
