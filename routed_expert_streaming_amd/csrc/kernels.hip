@@ -293,6 +293,22 @@ __global__ __launch_bounds__(256) void k_pack_x(const void *__restrict__ x, int 
 }
 
 // ------------------------------------------------------------- RVQ GEMVs
+// Copies a codebook (kCbRows rows of 16 bytes) from global memory into LDS
+// with NT threads, every load of a thread issued before its first LDS store.
+// (Loads through a generic pointer cannot be moved past an LDS store, so a
+// plain copy loop runs one memory round trip per row a thread copies.)
+template <int NT>
+__device__ __forceinline__ void stage_codebook(char *dst, const uint8_t *src) {
+    gu32x4 *g = (gu32x4 *)src;
+    constexpr int kPer = kCbRows / NT;
+    static_assert(kPer * NT == kCbRows && kPer <= 16, "codebook staging layout");
+    u32x4 v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; i++) v[i] = g[threadIdx.x + i * NT];
+#pragma unroll
+    for (int i = 0; i < kPer; i++) ((u32x4 *)dst)[threadIdx.x + i * NT] = v[i];
+}
+
 // Gate/up: one workgroup per (item, 64-row tile, matrix): gate and up are
 // separate workgroups, each with its matrix's codebook staged in LDS (64 KiB,
 // so two workgroups share a CU); lane = row, waves split the 128-column
@@ -313,29 +329,30 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_rvq_gateup(RecSrc src, RecOff
     int item;
     const uint8_t *rec = resolve_record(src, local, item);
     const int t = item / src.k;
-    {
-        const u32x4 *g = (const u32x4 *)(rec + off.cb[mat]);
-        for (int i = threadIdx.x; i < kCbRows; i += kGuWaves * 64) ((u32x4 *)cb)[i] = g[i];
-    }
-    __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int cpr = H / kChunkCols;
     const u32x4 *codes = (const u32x4 *)(rec + off.codes[mat]) + (size_t)tile * cpr * kTileVec;
+    // a wave's first two strips are in flight during the codebook staging,
+    // and each strip's dots run with the next two strips' loads in flight
+    int c = wave;
+    uint32_t dg[12], ng[12];
+    if (c < cpr) load_strip(codes + (size_t)c * kTileVec, lane, dg);
+    if (c + kGuWaves < cpr) load_strip(codes + (size_t)(c + kGuWaves) * kTileVec, lane, ng);
+    stage_codebook<kGuWaves * 64>(cb, rec + off.cb[mat]);
+    __syncthreads();
     const uint32_t *x = xh + (size_t)t * (H / 2);
     float ag[4] = {0.f, 0.f, 0.f, 0.f};
-    int c = wave;
-    uint32_t dg[12];
-    if (c < cpr) load_strip(codes + (size_t)c * kTileVec, lane, dg);
     while (c < cpr) {
-        const int cn = c + kGuWaves;
-        uint32_t ng[12];
-        if (cn < cpr) load_strip(codes + (size_t)cn * kTileVec, lane, ng);
+        const int cn = c + 2 * kGuWaves;
+        uint32_t nn[12];
+        if (cn < cpr) load_strip(codes + (size_t)cn * kTileVec, lane, nn);
         strip_dot<0>(dg, cb, x + c * 64, ag);
-        if (cn < cpr) {
 #pragma unroll
-            for (int i = 0; i < 12; i++) dg[i] = ng[i];
+        for (int i = 0; i < 12; i++) {
+            dg[i] = ng[i];
+            ng[i] = nn[i];
         }
-        c = cn;
+        c += kGuWaves;
     }
     red[wave * 64 + lane] = (ag[0] + ag[1]) + (ag[2] + ag[3]);
     __syncthreads();
@@ -377,38 +394,63 @@ __global__ __launch_bounds__(kDnWaves * 64) void k_rvq_down(RecSrc src, RecOffse
     const float *hg = gu + (size_t)item * 2 * I + c0 * kChunkCols, *hu = hg + I;
     const int np = (c1 - c0) * kChunkCols / 2;
     const u32x4 *codes = (const u32x4 *)(rec + off.codes[2]) + (size_t)tile * cpr * kTileVec;
+    // a wave's first two strips are in flight during the staging, and each
+    // strip's dots run with the next two strips' loads in flight
     int c = c0 + wave;
-    uint32_t d[12];
-    if (c < c1) load_strip(codes + (size_t)c * kTileVec, lane, d);   // in flight during the staging
-    float m = 0.f;
-    {
-        const u32x4 *cbsrc = (const u32x4 *)(rec + off.cb[2]);
-        for (int i = threadIdx.x; i < kCbRows; i += kDnWaves * 64) ((u32x4 *)cbd)[i] = cbsrc[i];
-        for (int p = threadIdx.x; p < np; p += kDnWaves * 64) {
-            const float2 g = *(const float2 *)(hg + 2 * p), u = *(const float2 *)(hu + 2 * p);
-            m = fmaxf(m, fmaxf(fabsf(silu_mul(g.x, u.x)), fabsf(silu_mul(g.y, u.y))));
-        }
-        m = wave_max(m);
-        if (lane == 0) wm[wave] = m;
+    uint32_t d[12], nd[12];
+    if (c < c1) load_strip(codes + (size_t)c * kTileVec, lane, d);
+    if (c + kDnWaves < c1) load_strip(codes + (size_t)(c + kDnWaves) * kTileVec, lane, nd);
+    // the slice's gate and up values: up to kHReg pairs per thread stay in
+    // registers (loaded with the codebook, all in flight together); a longer
+    // slice reloads the rest for the packing
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(1))) const f2v gf2;
+    gf2 *hg2 = (gf2 *)hg, *hu2 = (gf2 *)hu;
+    constexpr int kHReg = 4, kNT = kDnWaves * 64;
+    f2v gr[kHReg], ur[kHReg];
+#pragma unroll
+    for (int i = 0; i < kHReg; i++) {
+        const int p = threadIdx.x + i * kNT;
+        const f2v z = {0.f, 0.f};
+        gr[i] = p < np ? hg2[p] : z;
+        ur[i] = p < np ? hu2[p] : z;
     }
+    stage_codebook<kNT>(cbd, rec + off.cb[2]);
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < kHReg; i++)
+        if (threadIdx.x + i * kNT < np)
+            m = fmaxf(m, fmaxf(fabsf(silu_mul(gr[i].x, ur[i].x)), fabsf(silu_mul(gr[i].y, ur[i].y))));
+    for (int p = threadIdx.x + kHReg * kNT; p < np; p += kNT) {
+        const f2v g = hg2[p], u = hu2[p];
+        m = fmaxf(m, fmaxf(fabsf(silu_mul(g.x, u.x)), fabsf(silu_mul(g.y, u.y))));
+    }
+    m = wave_max(m);
+    if (lane == 0) wm[wave] = m;
     __syncthreads();
     const int e = range_exp(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])));
-    for (int p = threadIdx.x; p < np; p += kDnWaves * 64) {
-        const float2 g = *(const float2 *)(hg + 2 * p), u = *(const float2 *)(hu + 2 * p);
+#pragma unroll
+    for (int i = 0; i < kHReg; i++) {
+        const int p = threadIdx.x + i * kNT;
+        if (p < np) xl[p] = pack_f16x2(ldexpf(silu_mul(gr[i].x, ur[i].x), -e), ldexpf(silu_mul(gr[i].y, ur[i].y), -e));
+    }
+    for (int p = threadIdx.x + kHReg * kNT; p < np; p += kNT) {
+        const f2v g = hg2[p], u = hu2[p];
         xl[p] = pack_f16x2(ldexpf(silu_mul(g.x, u.x), -e), ldexpf(silu_mul(g.y, u.y), -e));
     }
     __syncthreads();
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     while (c < c1) {
-        const int cn = c + kDnWaves;
-        uint32_t nd[12];
-        if (cn < c1) load_strip(codes + (size_t)cn * kTileVec, lane, nd);
+        const int cn = c + 2 * kDnWaves;
+        uint32_t nn[12];
+        if (cn < c1) load_strip(codes + (size_t)cn * kTileVec, lane, nn);
         strip_dot<0>(d, cbd, xl + (c - c0) * 64, acc);
-        if (cn < c1) {
 #pragma unroll
-            for (int i = 0; i < 12; i++) d[i] = nd[i];
+        for (int i = 0; i < 12; i++) {
+            d[i] = nd[i];
+            nd[i] = nn[i];
         }
-        c = cn;
+        c += kDnWaves;
     }
     red[wave * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();

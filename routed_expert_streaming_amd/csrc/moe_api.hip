@@ -752,7 +752,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
             int r = cache_wait(c, s, cs);
             if (r) return r;
             src.list[q] = c->pool + (size_t)s * c->slot_bytes;
-            src.rank[q] = (uint8_t)js[q];
+            src.rank[q] = js[q];
         }
         HIPCHK(launch_rvq_gateup(src, off, H, I, nj, W.xh, W.xexp, W.hh, cs), "rvq gate/up (misses)");
         HIPCHK(launch_rvq_down(src, off, H, I, nj, KS, W.hh, W.ypart, cs), "rvq down (misses)");
@@ -768,7 +768,7 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
             int r = cache_wait(c, slot_of[j], cs);
             if (r) return r;
             hits.list[hits.n_local] = c->pool + (size_t)slot_of[j] * c->slot_bytes;
-            hits.rank[hits.n_local] = (uint8_t)j;
+            hits.rank[hits.n_local] = j;
             hits.n_local++;
         }
         if (hits.n_local) {

@@ -24,7 +24,7 @@ struct RecSrc {
     const void *const *table;      // [dev] record pointer per expert, or nullptr
     const int32_t *idx;            // [dev] expert id per global item (table mode)
     const void *list[MOE_MAX_K];   // list mode: record pointer of local item l
-    uint8_t rank[MOE_MAX_K];       // list mode: rank of local item l
+    int32_t rank[MOE_MAX_K];       // list mode: rank of local item l (32-bit: read by scalar loads)
     int32_t k;                     // ranks per token
     int32_t n_local;               // local items per token in this launch
 };

@@ -54,7 +54,10 @@ __device__ __forceinline__ int range_exp(float amax) {
 
 // Local item -> (global item, record).
 __device__ __forceinline__ const uint8_t *resolve_record(const RecSrc &s, int local, int &item) {
-    const int t = local / s.n_local, l = local % s.n_local;
+    // uniform across the workgroup: scalar loads of the argument arrays
+    // (a vector load of the argument segment is a memory round trip)
+    const int t = __builtin_amdgcn_readfirstlane(local / s.n_local);
+    const int l = __builtin_amdgcn_readfirstlane(local % s.n_local);
     if (s.table) {
         item = t * s.k + l;
         return (const uint8_t *)s.table[s.idx[item]];
