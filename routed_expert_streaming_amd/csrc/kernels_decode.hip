@@ -189,6 +189,24 @@ __device__ __forceinline__ bool poll_more(unsigned *sync, long &spins) {
     return true;
 }
 
+// Loads of weights and record fields through pointers held in memory (the
+// layer table, record pointers) as global-memory loads: through a generic
+// pointer they would be flat loads, which also count against the LDS wait
+// counter and cannot be reordered with LDS accesses.
+typedef float g_f32x4 __attribute__((ext_vector_type(4)));
+template <class T>
+__device__ __forceinline__ T gld(const T *p) {
+    return *(__attribute__((address_space(1))) const T *)p;
+}
+__device__ __forceinline__ float4 gld4(const float *p) {
+    const g_f32x4 v = *(__attribute__((address_space(1))) const g_f32x4 *)p;
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 gldu4(const void *p) {
+    const u32x4 v = *(gu32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // A space of n units is split over Ga = min(G, n) active workgroups into
 // contiguous, non-empty ranges [start(w), start(w+1)); workgroups w >= Ga get
 // nothing.  Non-empty ranges keep the contributors of any unit interval
@@ -1031,7 +1049,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         // the layer's record pointers, loaded while waiting (the table is
         // fixed during the launch): the chosen experts' loads can start right
         // after top-k
-        for (int e = threadIdx.x; e < E; e += kPW * 64) recs_all[e] = (uint64_t)lay.records[e];
+        for (int e = threadIdx.x; e < E; e += kPW * 64) recs_all[e] = gld((const uint64_t *)lay.records + e);
         // output units per step: 64-row tiles, or 16-row slices (down by table lookup)
         if (s > 0 && !wg_wait<LC>(sync, sync + kLayerDone,
                                  (unsigned)s * ((a.lut & kLutDown) ? H / kSliceRows : tilesH), bcast))
@@ -1055,7 +1073,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
         float acc_w = 0.f;
         int xe = 0;                 // gather gate/up: x enters as fp16 pairs scaled by 2^-xe
         // thread 0: the bias of logit row w, loaded together with x and the row
-        const float bias_w = threadIdx.x == 0 && lay.bias && w < nE ? lay.bias[w] : 0.f;
+        const float bias_w = threadIdx.x == 0 && lay.bias && w < nE ? gld(lay.bias + w) : 0.f;
         {
             float *xst = (float *)(lds + kXStage);   // gathers: fp32 x, packed below once xe is known
             float xm = 0.f;
@@ -1068,8 +1086,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     const int cu = c + u * kPiece;
-                    xv[u] = cu < H ? *(const float4 *)(xs + cu) : zero4;
-                    wv[u] = cu < H && row_w ? *(const float4 *)(wr + cu) : zero4;
+                    xv[u] = cu < H ? gld4(xs + cu) : zero4;
+                    wv[u] = cu < H && row_w ? gld4(wr + cu) : zero4;
                 }
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
@@ -1096,15 +1114,15 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             for (int e = w; e < E; e += G) {
                 const float *wr = lay.W + (size_t)e * H;
                 // thread 0: this row's bias, in flight with the row's loads
-                const float be = threadIdx.x == 0 && lay.bias ? (e == w ? bias_w : lay.bias[e]) : 0.f;
+                const float be = threadIdx.x == 0 && lay.bias ? (e == w ? bias_w : gld(lay.bias + e)) : 0.f;
                 float acc = e == w ? acc_w : 0.f;
                 for (int c0 = threadIdx.x * 4; c0 < H && e != w; c0 += 2 * kPW * 64 * 4) {
                     // two chunks' loads in flight together
                     const int c1 = c0 + kPW * 64 * 4;
-                    const float4 w0 = *(const float4 *)(wr + c0), x0 = *(const float4 *)(xs + c0);
+                    const float4 w0 = gld4(wr + c0), x0 = gld4(xs + c0);
                     const bool two = c1 < H;
-                    const float4 w1 = two ? *(const float4 *)(wr + c1) : make_float4(0.f, 0.f, 0.f, 0.f);
-                    const float4 x1 = two ? *(const float4 *)(xs + c1) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const float4 w1 = two ? gld4(wr + c1) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const float4 x1 = two ? gld4(xs + c1) : make_float4(0.f, 0.f, 0.f, 0.f);
                     acc = fmaf(w0.x, x0.x, acc);
                     acc = fmaf(w0.y, x0.y, acc);
                     acc = fmaf(w0.z, x0.z, acc);
@@ -1142,13 +1160,13 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
             for (int q = 0; q < NR; q++) g[q] = u[q] = 0.f;
             for (int c = t * 8; c < H; c += nthr * 8) {
-                const float4 xa = *(const float4 *)(xs + c), xb = *(const float4 *)(xs + c + 4);
+                const float4 xa = gld4(xs + c), xb = gld4(xs + c + 4);
                 uint4 gv[NR], uv[NR];
 #pragma unroll
                 for (int q = 0; q < NR; q++) {
                     const size_t o = (size_t)min(r0 + q, shI1 - 1) * H + c;
-                    gv[q] = *(const uint4 *)(wg0 + o);
-                    uv[q] = *(const uint4 *)(wu0 + o);
+                    gv[q] = gldu4(wg0 + o);
+                    uv[q] = gldu4(wu0 + o);
                 }
                 const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
@@ -1463,8 +1481,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                         g += jred[(wave * kPW + v) * 128 + lane];
                         uu += jred[(wave * kPW + v) * 128 + 64 + lane];
                     }
-                    g *= (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
-                    uu *= (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
+                    g *= (float)gld((const _Float16 *)(rec + a.off.scales[0]) + r);
+                    uu *= (float)gld((const _Float16 *)(rec + a.off.scales[1]) + r);
                     const float hv = g / (1.f + __expf(-g)) * uu;
                     if (a.lut & kLutDown) {
                         st_tagged(a.hq + (size_t)j * I + r, hv, tag);   // read per chunk by down
@@ -1531,8 +1549,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
                 if (nj++ % kPW != wave) continue;
                 const int first = range_owner(nGU, G, tau * cprH), ncontrib = w - first + 1;
                 const int r = tau % tilesI * kTileRows + lane;
-                const float sg = (float)((const _Float16 *)(rec + a.off.scales[0]))[r];
-                const float su = (float)((const _Float16 *)(rec + a.off.scales[1]))[r];
+                const float sg = (float)gld((const _Float16 *)(rec + a.off.scales[0]) + r);
+                const float su = (float)gld((const _Float16 *)(rec + a.off.scales[1]) + r);
                 const uint64_t *pp = a.part_gu + (size_t)tau * a.slots_gu * 128 + lane;
                 float g = 0.f, uu = 0.f;
                 long spins = 0;
@@ -1594,7 +1612,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
                         for (int p = 0; p < kShCP; p++) {
                             const int r = rb + d * kPW, c = c0 + 512 * p + 8 * lane;
-                            wv[d][p] = r < shH1 && c < I ? *(const uint4 *)(wd0 + (size_t)r * I + c)
+                            wv[d][p] = r < shH1 && c < I ? gldu4(wd0 + (size_t)r * I + c)
                                                          : make_uint4(0u, 0u, 0u, 0u);
                         }
                     if (!h_seen && sh_early < h_target) {
@@ -1660,8 +1678,8 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             const int nSl = H / kSliceRows;
             auto scale_of = [&](int sl) -> _Float16 {
                 const int j = threadIdx.x / kSliceRows;
-                return ((const _Float16 *)((const uint8_t *)recs[j] + a.off.scales[2]))[sl * kSliceRows +
-                                                                                        threadIdx.x % kSliceRows];
+                return gld((const _Float16 *)((const uint8_t *)recs[j] + a.off.scales[2]) + sl * kSliceRows +
+                           threadIdx.x % kSliceRows);
             };
             const bool fj_entry = threadIdx.x < k * kSliceRows;
             bool fj_done = w >= nSl;
@@ -1734,7 +1752,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
             const _Float16 *dscale = (const _Float16 *)(rec + a.off.scales[2]);
             // the row scales of this wave's first tile, loaded before the
             // loop: the partial stores after it wait for no load
-            const float sc0 = wave < nt ? (float)dscale[(tA + wave) % tilesH * kTileRows + lane] : 0.f;
+            const float sc0 = wave < nt ? (float)gld(dscale + (tA + wave) % tilesH * kTileRows + lane) : 0.f;
             int he = 0;
             if (!stream_down((const u32x4 *)(rec + a.off.codes[2]), (const u32x4 *)(rec + a.off.cb[2]),
                              a.hh + (size_t)j * I, sync, h_ready + j * kLine, (unsigned)(s + 1) * tilesI, bcast, lmax,
@@ -1749,7 +1767,7 @@ __global__ __launch_bounds__(kPW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
                 for (int q = 0; q < kPW; q++) y += red_d[(v * kPW + q) * 64 + lane];
                 const int r = tau % tilesH * kTileRows + lane;
-                y = ldexpf(y, he) * (v == wave ? sc0 : (float)dscale[r]);
+                y = ldexpf(y, he) * (v == wave ? sc0 : (float)gld(dscale + r));
                 st_tagged(a.part_d + ((size_t)tau * a.slots_d + (w - range_owner(nD, G, tau * cprI))) * 64 + lane, y,
                           tag);
             }
