@@ -34,11 +34,11 @@ HBM_PEAK_GBS = 8000.0
 # profiles/k_grouped_rvq_batched_counters.txt), valid for the kernel sources
 # they were taken on: reported as null once any of them has changed.
 TRAFFIC = {
-    "decode": {"sources": {"routed_expert_streaming_amd/csrc/kernels_decode.hip": "ecf3dc42207f7e5f"},
-               "bytes": {"mixtral": 5057227629, "kimi_linear": 1248273440}},
+    "decode": {"sources": {"routed_expert_streaming_amd/csrc/kernels_decode.hip": "7156988d9f0198fa"},
+               "bytes": {"mixtral": 5051719539, "kimi_linear": 1235223982}},
     "batched": {"sources": {"routed_expert_streaming_amd/csrc/kernels_grouped.hip": "19f8b9070b2243fe",
-                            "routed_expert_streaming_amd/csrc/kernels.hip": "e752dac27ab2b67f"},
-                "bytes": {"batched": 5525649473}},
+                            "routed_expert_streaming_amd/csrc/kernels.hip": "6521b2c3e86917ef"},
+                "bytes": {"batched": 5526878369}},
 }
 
 
