@@ -34,6 +34,7 @@ private:
     bool stop_ = false;
 };
 constexpr int kBounce = 4;   // pinned bounce buffers per cache
+constexpr int kIdsFlag = 3 * MOE_MAX_K;   // word of moe_cache::h_idx holding the ids' sequence flag
 }  // namespace moe
 
 struct moe_cache {
@@ -52,7 +53,9 @@ struct moe_cache {
     std::vector<int32_t> use_free;        // events with no referring slot
     std::vector<int32_t> slot_use;        // per slot: its readers' event, or -1
     int32_t *h_idx = nullptr;             // pinned staging: the router's expert ids, the look-ahead ids and
-                                          // (bits of) the look-ahead weights, MOE_MAX_K each
+                                          // (bits of) the look-ahead weights, MOE_MAX_K each, then the
+                                          // ids' sequence flag (word kIdsFlag)
+    uint32_t ids_seq = 0;                 // the last sequence number the top-k was asked to write
     hipEvent_t idx_ev = nullptr;          // recorded after the top-k that writes the ids to h_idx
     hipEvent_t ahead_ev = nullptr;        // recorded after the look-ahead top-k
     // A second copy stream of the cache's own: a streamed layer alternates its

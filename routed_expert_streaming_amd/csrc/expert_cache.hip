@@ -227,7 +227,8 @@ int expert_cache_create(int32_t capacity, uint64_t slot_bytes, void *pool_dev, m
     for (int s = 0; e == hipSuccess && s < capacity; s++) {
         e = hipEventCreateWithFlags(&c->ready[s], hipEventDisableTiming);
     }
-    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_idx, 3 * MOE_MAX_K * sizeof(int32_t), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_idx, (kIdsFlag + 1) * sizeof(int32_t), hipHostMallocDefault);
+    if (e == hipSuccess) c->h_idx[kIdsFlag] = 0;   // no sequence number yet (they start at 1)
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->idx_ev, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ahead_ev, hipEventDisableTiming);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->ps2, hipStreamNonBlocking);

@@ -203,7 +203,8 @@ __device__ __forceinline__ float topk_key_value(uint32_t k) {
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__ z, int E, int k, int score_fn,
                                                        int32_t *__restrict__ idx, float *__restrict__ w,
-                                                       int32_t *__restrict__ idx_host, float *__restrict__ w_host) {
+                                                       int32_t *__restrict__ idx_host, float *__restrict__ w_host,
+                                                       uint32_t *flag_host, uint32_t seq) {
     __shared__ __align__(16) uint64_t key[MOE_MAX_E];              // padded to a multiple of 32 with zeros
     __shared__ __align__(16) uint64_t cand[kTopkLvl * MOE_MAX_K];  // zeros past the candidates
     __shared__ int sidx[MOE_MAX_K];
@@ -265,6 +266,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
         w[(size_t)t * k + threadIdx.x] = mine / sum;
         if (idx_host) idx_host[(size_t)t * k + threadIdx.x] = sidx[threadIdx.x];
         if (w_host) w_host[(size_t)t * k + threadIdx.x] = mine / sum;
+    }
+    // then seq to flag_host: the host can read the ids as soon as it sees it,
+    // before the kernel's completion is signalled.  Every id and weight was
+    // written by wave 0 (k <= 32), whose stores the system-scope fence orders
+    // before the flag's.
+    if (flag_host && t == 0 && threadIdx.x == 0) {
+        __threadfence_system();
+        __hip_atomic_store(flag_host, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
@@ -635,8 +644,8 @@ hipError_t launch_route_blocked(const float *W, const float *bias, int E, int H,
 }
 
 hipError_t launch_topk(const float *z, int E, int k, int score_fn, int T, int32_t *idx, float *w,
-                       hipStream_t s, int32_t *idx_host, float *w_host) {
-    k_topk<<<T, kTopkThreads, 0, s>>>(z, E, k, score_fn, idx, w, idx_host, w_host);
+                       hipStream_t s, int32_t *idx_host, float *w_host, uint32_t *flag_host, uint32_t seq) {
+    k_topk<<<T, kTopkThreads, 0, s>>>(z, E, k, score_fn, idx, w, idx_host, w_host, flag_host, seq);
     return hipGetLastError();
 }
 

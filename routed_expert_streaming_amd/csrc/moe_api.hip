@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -587,7 +588,10 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
     // route; the host waits only for the expert ids, while the work that does
     // not depend on the choice (x packing, the shared expert) runs on
     HIPCHK(launch_route_logits(L->router.weight, L->router.bias, E, H, x, MOE_DTYPE_F32, 1, W.z, cs), "route logits");
-    HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, 1, idx, W.w, cs, c->h_idx), "top-k");   // ids to the host too
+    // ids to the host too, with a sequence flag after them (1, 2, ..., skipping 0)
+    const uint32_t seq = ++c->ids_seq ? c->ids_seq : ++c->ids_seq;
+    uint32_t *ids_flag = (uint32_t *)(c->h_idx + kIdsFlag);
+    HIPCHK(launch_topk(W.z, E, k, L->router.score_fn, 1, idx, W.w, cs, c->h_idx, nullptr, ids_flag, seq), "top-k");
     HIPCHK(hipEventRecord(c->idx_ev, cs), "ids written");
     if (ah.L) {
         // the next layer's router on this layer's input: a prediction only
@@ -602,7 +606,19 @@ int streamed_impl(const moe_layer *L, moe_cache *c, uint32_t layer_id, const voi
         HIPCHK(launch_dense_gateup(L->shared, H, I, x, MOE_DTYPE_F32, H, 1, W.hs, cs), "shared gate/up");
         HIPCHK(launch_dense_down(L->shared, H, I, W.hs, 1, W.ysh, cs), "shared down");
     }
-    HIPCHK(hipEventSynchronize(c->idx_ev), "wait for the expert ids");
+    // the ids are readable once the flag shows this call's sequence number
+    // (written by the top-k after them, before its completion is signalled);
+    // past a bound (the stream may still be busy with earlier work) the
+    // event's wait takes over, which also reports a failed launch
+    {
+        const auto t0 = std::chrono::steady_clock::now();
+        bool seen = false;
+        for (int n = 0;; n++) {
+            if (__atomic_load_n(ids_flag, __ATOMIC_ACQUIRE) == seq) { seen = true; break; }
+            if ((n & 255) == 255 && std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(2)) break;
+        }
+        if (!seen) HIPCHK(hipEventSynchronize(c->idx_ev), "wait for the expert ids");
+    }
 
     // cache bookkeeping in ascending expert id (get-or-insert, the LRU order
     // the trace records); the copies of misses are enqueued after the hit

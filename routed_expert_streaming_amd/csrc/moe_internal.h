@@ -54,9 +54,11 @@ struct LayerWs {
 hipError_t launch_route_logits(const float *W, const float *bias, int E, int H, const void *x,
                                int x_dtype, int T, float *z, hipStream_t s);
 // idx_host / w_host (optional, page-locked host memory): the ids and weights
-// are written there too, visible once the kernel has completed.
+// are written there too, visible once the kernel has completed, or (token 0)
+// as soon as seq appears in *flag_host (optional, page-locked host memory).
 hipError_t launch_topk(const float *z, int E, int k, int score_fn, int T, int32_t *idx, float *w,
-                       hipStream_t s, int32_t *idx_host = nullptr, float *w_host = nullptr);
+                       hipStream_t s, int32_t *idx_host = nullptr, float *w_host = nullptr,
+                       uint32_t *flag_host = nullptr, uint32_t seq = 0);
 // Many-token router logits: H-sliced partial sums (part: route_blocked_slices
 // x T x E floats) reduced in slice order into z.  H % 64 == 0.
 constexpr int kRouteMaxSlices = 64;
