@@ -245,27 +245,43 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
     if (two) {
         __syncthreads();
         // the groups' candidates, zeros where a group had fewer than k keys
+        // (the candidate area is zeroed to its end, kTopkLvl * MOE_MAX_K >=
+        // ncp).  Each candidate is ranked by P threads, each counting a P-th
+        // of the list; the P counts are added across their lanes.
         const int nc = (E + gsz - 1) / gsz * k;
-        for (int c = threadIdx.x; c < nc; c += kTopkThreads) {
-            const uint64_t ke = cand[c];
-            if (!ke) continue;
-            const int rank = count_above(cand, 0, (nc + 31) & ~31, ke);
-            if (rank < k) place(rank, ke);
+        int ncp = 32;
+        while (ncp < nc) ncp <<= 1;
+        const int P = max(1, kTopkThreads / ncp), len = ncp / P;
+        const int c = threadIdx.x / P, q0 = (threadIdx.x % P) * len;
+        const uint64_t ke = c < nc ? cand[c] : 0u;
+        int r4[4] = {0, 0, 0, 0};
+#pragma unroll 4
+        for (int q = q0; q < q0 + len; q += 4) {   // len is a multiple of 4: four loads in flight
+            const uint64_t k0 = cand[q], k1 = cand[q + 1], k2 = cand[q + 2], k3 = cand[q + 3];
+            r4[0] += k0 > ke;
+            r4[1] += k1 > ke;
+            r4[2] += k2 > ke;
+            r4[3] += k3 > ke;
         }
+        int rank = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o, 64);
+        if (threadIdx.x % P == 0 && ke && rank < k) place(rank, ke);
     }
     __syncthreads();
-    if (threadIdx.x < k) {
+    if (threadIdx.x < 64) {
+        // lane r < k scores rank r; the sum runs in rank order
+        const int lane = threadIdx.x;
         const float zmax = sz[0];
-        float sum = 0.f, mine = 0.f;
-        for (int r = 0; r < k; r++) {
-            const float s = score_fn == MOE_SCORE_SOFTMAX ? __expf(sz[r] - zmax) : 1.f / (1.f + __expf(-sz[r]));
-            sum += s;
-            if (r == (int)threadIdx.x) mine = s;
+        float sc = 0.f;
+        if (lane < k) sc = score_fn == MOE_SCORE_SOFTMAX ? __expf(sz[lane] - zmax) : 1.f / (1.f + __expf(-sz[lane]));
+        float sum = 0.f;
+        for (int r = 0; r < k; r++) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), r));
+        if (lane < k) {
+            idx[(size_t)t * k + lane] = sidx[lane];
+            w[(size_t)t * k + lane] = sc / sum;
+            if (idx_host) idx_host[(size_t)t * k + lane] = sidx[lane];
+            if (w_host) w_host[(size_t)t * k + lane] = sc / sum;
         }
-        idx[(size_t)t * k + threadIdx.x] = sidx[threadIdx.x];
-        w[(size_t)t * k + threadIdx.x] = mine / sum;
-        if (idx_host) idx_host[(size_t)t * k + threadIdx.x] = sidx[threadIdx.x];
-        if (w_host) w_host[(size_t)t * k + threadIdx.x] = mine / sum;
     }
     // then seq to flag_host: the host can read the ids as soon as it sees it,
     // before the kernel's completion is signalled.  Every id and weight was
