@@ -37,8 +37,8 @@ TRAFFIC = {
     "decode": {"sources": {"routed_expert_streaming_amd/csrc/kernels_decode.hip": "7156988d9f0198fa"},
                "bytes": {"mixtral": 5051719539, "kimi_linear": 1235223982}},
     "batched": {"sources": {"routed_expert_streaming_amd/csrc/kernels_grouped.hip": "19f8b9070b2243fe",
-                            "routed_expert_streaming_amd/csrc/kernels.hip": "6521b2c3e86917ef"},
-                "bytes": {"batched": 5526878369}},
+                            "routed_expert_streaming_amd/csrc/kernels.hip": "4a1aa007b71fe287"},
+                "bytes": {"batched": 5525163723}},
 }
 
 
