@@ -195,8 +195,8 @@ def main() -> int:
     if args.warmup is None:
         args.warmup = 0 if args.config == "k3_slice" and not args.sweep else 2
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
-              "see the sharding design notes.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path "
+              "(the layer would shard its experts across GPUs; not implemented).", file=sys.stderr)
         return 2
 
     import numpy as np
